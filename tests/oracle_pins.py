@@ -1,0 +1,496 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError if
+the oracle disagrees with a closed form, a special case, a brute-force count,
+a library routine or a value printed on the pages. The same functions run
+against deliberately broken copies of the oracle in ``test_oracle_pins.py`` to
+show that a plausible mistake anywhere in it fails at least one pin.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import datagen
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as fh:
+        return json.load(fh)
+
+
+def _mat(o, seed, n, k, codes=None):
+    c = datagen.codes(seed, n, k) if codes is None else np.asarray(codes, np.uint8)
+    s = datagen.scales(seed + 1, n, k)
+    return c, o.pack(c), s
+
+
+def _f16(v):
+    return np.asarray(v, dtype=np.float64).astype(np.float16)
+
+
+# --------------------------------------------------------------------------
+# binary16 conversion: reduces to numpy's IEEE conversions (library routine)
+# --------------------------------------------------------------------------
+
+def pin_h2d_every_pattern(o):
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = h.view(np.float16).astype(np.float64)
+    got = o.h2d(h)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def pin_d2h_round_to_nearest_even(o):
+    # every midpoint between consecutive finite binary16 values (ties), their
+    # binary64 neighbours, plus random values over the whole range
+    h = np.arange(0, 0x7BFF, dtype=np.uint16)
+    lo = h.view(np.float16).astype(np.float64)
+    hi = (h + 1).view(np.float16).astype(np.float64)
+    mid = (lo + hi) / 2
+    cand = np.concatenate([mid, np.nextafter(mid, 0), np.nextafter(mid, np.inf), lo,
+                           [65504.0, 65519.99, 65520.0, 1e6, 0.0, 2.0 ** -25, 2.0 ** -26,
+                            3 * 2.0 ** -26]])
+    rng = np.random.default_rng(11)
+    cand = np.concatenate([cand, rng.normal(0, 1, 20000), rng.uniform(-7e4, 7e4, 20000),
+                           rng.uniform(-1e-4, 1e-4, 20000)])
+    cand = np.concatenate([cand, -cand])
+    got = o.d2h(cand).view(np.uint16)
+    with np.errstate(over="ignore"):
+        ref = cand.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref), np.flatnonzero(got != ref)[:10]
+    # ties go to the even mantissa: 1 + 2^-11 -> 1, 1 + 3*2^-11 -> 1 + 2^-9
+    assert o.d2h(np.array([1 + 2.0 ** -11]))[0] == 1.0
+    assert o.d2h(np.array([1 + 3 * 2.0 ** -11]))[0] == 1 + 2.0 ** -9
+
+
+# --------------------------------------------------------------------------
+# packing: closed forms of "element i of a word lives in bits 4i..4i+3"
+# (Zero TVM Documentation, "Q4F16 quantization format")
+# --------------------------------------------------------------------------
+
+def pin_pack_closed_form(o):
+    assert o.pack(np.array([[0, 1, 2, 3, 4, 5, 6, 7]], np.uint8))[0, 0] == 0x76543210
+    assert o.pack(np.array([[15, 0, 0, 0, 0, 0, 0, 0]], np.uint8))[0, 0] == 0x0000000F
+    assert o.pack(np.array([[0, 0, 0, 0, 0, 0, 0, 15]], np.uint8))[0, 0] == 0xF0000000
+    w = o.pack(np.array([[1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 0]], np.uint8))
+    assert list(w[0]) == [0x87654321, 0x0FEDCBA9]
+
+
+def pin_unpack_inverts_pack(o):
+    c = datagen.codes(5, 7, 96)
+    assert np.array_equal(o.unpack(o.pack(c)), c)
+    w = np.array([[0x76543210, 0xFEDCBA98]], np.uint32)
+    assert list(o.unpack(w)[0]) == list(range(16))
+
+
+def pin_shapes_match_page_table(o):
+    g = _golden("phi3_q4f16_shapes.json")
+    for name, t in g["tensors"].items():
+        words, groups = t["q_weight"][1], t["q_scale"][1]
+        k = words * 8
+        assert groups * 32 == k, name
+        c = datagen.codes(3, 2, k)
+        assert o.pack(c).shape == (2, words), name
+    u = _golden("int4_matmul_uniforms.json")
+    assert u["input_dim"] // 8 == u["K_groups"]
+    assert u["input_dim"] // u["group_size"] == u["scale_stride"]
+    c = datagen.codes(4, 1, u["input_dim"])
+    assert o.pack(c).shape[1] == u["K_groups"]
+    t = _golden("tvm_matmul_structure.json")
+    assert t["threads"] * t["iterations"] * t["codes_per_word"] == t["dot_length"]
+    assert o.pack(datagen.codes(6, 1, t["dot_length"])).shape[1] == t["threads"] * t["iterations"]
+
+
+# --------------------------------------------------------------------------
+# matvec pins
+# --------------------------------------------------------------------------
+
+def pin_one_hot_reproduces_column(o):
+    """x = e_k gives y[n] = (q[n][k] - 7) * S[n][k // 32] exactly, for every k
+    (every nibble position of every word and every group)."""
+    n, k = 6, 96
+    codes, W, S = _mat(o, 21, n, k)
+    Sd = S.astype(np.float64)
+    for kk in range(k):
+        x = np.zeros(k, np.float16)
+        x[kk] = 1.0
+        y = o.gemv(W, S, x)
+        expect = (codes[:, kk].astype(np.float64) - 7.0) * Sd[:, kk // 32]
+        assert np.array_equal(y, expect), kk
+
+
+def pin_all_sevens_zero(o):
+    n, k = 9, 128
+    _, W, S = _mat(o, 22, n, k, codes=np.full((n, k), 7, np.uint8))
+    x = datagen.activations(23, 1, k)[0]
+    assert np.array_equal(o.gemv(W, S, x), np.zeros(n))
+
+
+def pin_scale_linearity(o):
+    n, k = 11, 160
+    _, W, S = _mat(o, 24, n, k)
+    x = datagen.activations(25, 1, k)[0]
+    y1 = o.gemv(W, S, x)
+    y2 = o.gemv(W, (S.astype(np.float64) * 2).astype(np.float16), x)
+    assert np.array_equal(y2, 2 * y1)
+
+
+def pin_x_linearity(o):
+    n, k = 8, 64
+    _, W, S = _mat(o, 26, n, k)
+    r = np.random.default_rng(27)
+    x1 = (r.integers(-64, 64, k) / 64.0).astype(np.float16)
+    x2 = (r.integers(-64, 64, k) / 64.0).astype(np.float16)
+    x3 = (x1.astype(np.float64) + x2.astype(np.float64)).astype(np.float16)
+    assert np.array_equal(x3.astype(np.float64), x1.astype(np.float64) + x2.astype(np.float64))
+    y = o.gemv(W, S, x1) + o.gemv(W, S, x2)
+    assert np.allclose(o.gemv(W, S, x3), y, rtol=0, atol=1e-12)
+
+
+def pin_all_fifteen_closed_form(o):
+    """codes all 15 -> y[n] = 8 * sum_g S[n][g] * sum_{k in g} x[k]."""
+    n, k = 5, 256
+    _, W, S = _mat(o, 28, n, k, codes=np.full((n, k), 15, np.uint8))
+    x = datagen.activations(29, 1, k)[0]
+    gs = x.astype(np.float64).reshape(k // 32, 32).sum(axis=1)
+    expect = 8.0 * (S.astype(np.float64) * gs[None, :]).sum(axis=1)
+    assert np.allclose(o.gemv(W, S, x), expect, rtol=1e-13, atol=1e-13)
+
+
+def pin_brute_force_every_code_every_position(o):
+    """Row n holds code (n + k) % 16 at column k, so across 16 rows every code
+    value sits at every nibble position of every word; exact rational sums."""
+    n, k = 16, 64
+    codes = (np.arange(n)[:, None] + np.arange(k)[None, :]) % 16
+    codes = codes.astype(np.uint8)
+    _, W, S = _mat(o, 30, n, k, codes=codes)
+    x = datagen.activations(31, 1, k)[0]
+    y = o.gemv(W, S, x)
+    xf = [Fraction(float(v)) for v in x]
+    for r in range(n):
+        acc = Fraction(0)
+        for c in range(k):
+            acc += (int(codes[r, c]) - 7) * Fraction(float(S[r, c // 32])) * xf[c]
+        assert abs(Fraction(y[r]) - acc) <= Fraction(1, 2 ** 40) * (1 + abs(acc)), r
+
+
+def pin_matvec_equals_library_matmul(o):
+    """Against numpy's float64 matmul of the matrix dequantised from the codes
+    (ragged sizes, several groups)."""
+    n, k = 37, 224
+    codes, W, S = _mat(o, 32, n, k)
+    x = datagen.activations(33, 1, k)[0]
+    dense = (codes.astype(np.float64) - 7.0) * np.repeat(S.astype(np.float64), 32, axis=1)
+    assert np.allclose(o.dequant(W, S), dense, rtol=0, atol=0)
+    assert np.allclose(o.gemv(W, S, x), dense @ x.astype(np.float64), rtol=1e-12, atol=1e-12)
+    rows = np.array([36, 0, 17])
+    assert np.array_equal(o.gemv_rows(W, S, x, rows), o.gemv(W, S, x)[rows])
+
+
+def pin_batched(o):
+    n, k, m = 13, 96, 5
+    codes, W, S = _mat(o, 34, n, k)
+    X = datagen.activations(35, m, k)
+    dense = (codes.astype(np.float64) - 7.0) * np.repeat(S.astype(np.float64), 32, axis=1)
+    Y = o.gemv_batched(W, S, X)
+    assert Y.shape == (m, n)
+    assert np.allclose(Y, X.astype(np.float64) @ dense.T, rtol=1e-12, atol=1e-12)
+    same = np.repeat(X[:1], 4, axis=0)
+    Ys = o.gemv_batched(W, S, same)
+    assert all(np.array_equal(Ys[0], Ys[i]) for i in range(4))
+
+
+# --------------------------------------------------------------------------
+# add + RMSNorm pins (shaders 2 and 7)
+# --------------------------------------------------------------------------
+
+def pin_rmsnorm_constant_input(o):
+    d = 64
+    for c in (0.5, 3.0, -2.0, 0.0078125):
+        r = np.full(d, c, np.float16)
+        g = np.ones(d, np.float16)
+        res, out = o.add_rmsnorm(None, r, g, eps=1e-5)
+        assert np.array_equal(res[0].view(np.uint16), r.view(np.uint16))
+        expect = c / math.sqrt(c * c + 1e-5)
+        assert np.allclose(out[0], expect, rtol=1e-14, atol=0)
+
+
+def pin_rmsnorm_one_nonzero(o):
+    """r = [c, 0, ..., 0] has mean square c^2 / D, so out[0] = c / sqrt(c^2/D + eps)."""
+    for d in (8, 100):
+        c = 0.25
+        r = np.zeros(d, np.float16)
+        r[0] = c
+        g = _f16(np.linspace(0.5, 1.5, d))
+        _, out = o.add_rmsnorm(None, r, g, eps=1e-5)
+        expect = c / math.sqrt(c * c / d + 1e-5) * float(g[0])
+        assert np.allclose(out[0, 0], expect, rtol=1e-14)
+        assert np.all(out[0, 1:] == 0)
+
+
+def pin_rmsnorm_unit_rms(o):
+    d = 48
+    r = np.where(np.arange(d) % 2 == 0, 1.0, -1.0).astype(np.float16)
+    g = datagen.gammas(36, 1, d)[0]
+    _, out = o.add_rmsnorm(None, r, g, eps=0.0)
+    assert np.array_equal(out[0], r.astype(np.float64) * g.astype(np.float64))
+
+
+def pin_rmsnorm_scale_invariance(o):
+    d = 96
+    r = datagen.activations(37, 1, d)[0]
+    g = datagen.gammas(38, 1, d)[0]
+    r2 = (r.astype(np.float64) * 2).astype(np.float16)
+    _, a = o.add_rmsnorm(None, r, g, eps=0.0)
+    _, b = o.add_rmsnorm(None, r2, g, eps=0.0)
+    assert np.allclose(a, b, rtol=1e-14, atol=1e-14)
+
+
+def pin_add_residual_rounding(o):
+    d = 4
+    g = np.ones(d, np.float16)
+    a = np.array([1.0, 1.0, 0.0, 2.0], np.float16)
+    r = np.array([2.0 ** -11, 3 * 2.0 ** -11, 0.75, 2.0 ** -10], np.float16)
+    res, _ = o.add_rmsnorm(a, r, g)
+    # ties round to even; an exact sum is kept as is
+    assert list(res[0].astype(np.float64)) == [1.0, 1 + 2.0 ** -9, 0.75, 2.0]
+    # a == 0 leaves the residual bit-identical
+    rr = datagen.activations(39, 1, 64)[0]
+    res2, _ = o.add_rmsnorm(np.zeros(64, np.float16), rr, np.ones(64, np.float16))
+    assert np.array_equal(res2[0].view(np.uint16), rr.view(np.uint16))
+
+
+def pin_add_then_norm(o):
+    """out is RMSNorm of the stored (rounded) residual: with a = r the residual
+    doubles exactly and the norm is that of r (eps = 0)."""
+    d = 32
+    r = datagen.activations(40, 1, d)[0]
+    g = datagen.gammas(41, 1, d)[0]
+    res, out = o.add_rmsnorm(r, r, g, eps=0.0)
+    assert np.array_equal(res[0].astype(np.float64), 2 * r.astype(np.float64))
+    _, ref = o.add_rmsnorm(None, r, g, eps=0.0)
+    assert np.allclose(out, ref, rtol=1e-14, atol=1e-15)
+
+
+def pin_eps_inside_sqrt(o):
+    c = 2.0 ** -8
+    r = np.array([c], np.float16)
+    _, out = o.add_rmsnorm(None, r, np.ones(1, np.float16), eps=1e-5)
+    assert np.allclose(out[0, 0], c / math.sqrt(c * c + 1e-5), rtol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# split-SiLU-multiply pins (RESEARCH.md, "1. Dispatch profile")
+# --------------------------------------------------------------------------
+
+def _gu(gate, up):
+    return np.concatenate([np.asarray(gate, np.float16), np.asarray(up, np.float16)])
+
+
+def pin_silu_special_values(o):
+    out = o.silu_mul(_gu([0.0, 20.0, -30.0, 0.0], [5.0, 1.0, 1.0, 0.0]))[0]
+    assert out[0] == 0.0 and out[3] == 0.0
+    assert abs(out[1] - 20.0) < 20.0 * 3e-9          # 20 * sigmoid(20)
+    assert -3e-12 < out[2] < -2.7e-12                 # -30 * sigmoid(-30)
+    # tiny gate: silu(z) = z/2 + z^2/4 + O(z^4)
+    z = 2.0 ** -12
+    t = o.silu_mul(_gu([z], [1.0]))[0, 0]
+    assert abs(t - (z / 2 + z * z / 4)) < 1e-15
+
+
+def pin_silu_odd_identity(o):
+    """silu(z) - silu(-z) = z for every z."""
+    g = datagen.normal_f16(42, 256, 0.0, 4.0)
+    pos = o.silu_mul(_gu(g, np.ones_like(g)))[0]
+    neg = o.silu_mul(_gu(-g, np.ones_like(g)))[0]
+    assert np.allclose(pos - neg, g.astype(np.float64), rtol=0, atol=1e-14)
+
+
+def pin_silu_gate_first(o):
+    """The first half of [gate | up] is the gate: gate 20, up 1 gives ~20 (the
+    other order would give silu(1) * 20 ~ 14.6); up scales linearly."""
+    out = o.silu_mul(_gu([20.0, 1.0], [1.0, 20.0]))[0]
+    assert abs(out[0] - 20.0) < 1e-6
+    assert abs(out[1] - 20.0 / (1 + math.exp(-1.0))) < 1e-12
+    g = datagen.normal_f16(43, 64)
+    u = datagen.normal_f16(44, 64)
+    a = o.silu_mul(_gu(g, u))[0]
+    b = o.silu_mul(_gu(g, (u.astype(np.float64) * 2).astype(np.float16)))[0]
+    assert np.array_equal(b, 2 * a)
+
+
+# --------------------------------------------------------------------------
+# MoE pins (BENCH.md, "MoE chunked prefill"; "MoE Phase B")
+# --------------------------------------------------------------------------
+
+def _experts(o, seed, e, n, k, codes_fn=None):
+    W = np.empty((e, n, k // 8), np.uint32)
+    S = np.empty((e, n, k // 32), np.float16)
+    for i in range(e):
+        c = datagen.codes(seed + 2 * i, n, k) if codes_fn is None else codes_fn(i)
+        W[i] = o.pack(c)
+        S[i] = datagen.scales(seed + 2 * i + 1, n, k)
+    return W, S
+
+
+def pin_moe_one_hot_routing_is_dense_chain(o):
+    e, d, f, t, topk = 6, 64, 32, 3, 3
+    Wg, Sg = _experts(o, 50, e, 2 * f, d)
+    Wd, Sd = _experts(o, 80, e, d, f)
+    ids = np.array([[4, 1, 2], [0, 5, 3], [2, 3, 4]], np.int32)
+    x = datagen.activations(51, t, d)
+    u = o.moe_stage(Wg, Sg, ids, None, x, d, 0, 2 * f, d, epi_silu=True)
+    u16 = u.astype(np.float16)
+    for slot in range(topk):
+        w = np.zeros((t, topk), np.float16)
+        w[:, slot] = 1.0
+        y = o.moe_stage(Wd, Sd, ids, w, u16, topk * f, f, d, f, epi_silu=False)
+        for i in range(t):
+            ex = ids[i, slot]
+            gu = o.gemv(Wg[ex], Sg[ex], x[i]).astype(np.float16)
+            uu = o.silu_mul(gu)[0].astype(np.float16)
+            dn = o.gemv(Wd[ex], Sd[ex], uu)
+            assert np.array_equal(y[i], dn), (slot, i)
+
+
+def pin_moe_slot_permutation(o):
+    e, d, f, t, topk = 5, 32, 32, 2, 4
+    Wd, Sd = _experts(o, 90, e, d, f)
+    ids, w = datagen.routing(91, t, e, topk)
+    u = datagen.activations(92, t * topk, f).reshape(t, topk, f)
+    y = o.moe_stage(Wd, Sd, ids, w, u, topk * f, f, d, f, epi_silu=False)
+    p = np.array([2, 0, 3, 1])
+    y2 = o.moe_stage(Wd, Sd, ids[:, p], w[:, p], np.ascontiguousarray(u[:, p]), topk * f, f,
+                     d, f, epi_silu=False)
+    assert np.allclose(y, y2, rtol=1e-13, atol=1e-13)
+
+
+def pin_moe_identical_experts(o):
+    e, d, f, t, topk = 4, 32, 32, 3, 3
+    c = datagen.codes(93, d, f)
+    Wd, Sd = _experts(o, 94, e, d, f, codes_fn=lambda i: c)
+    Sd[:] = Sd[0]
+    ids, w = datagen.routing(95, t, e, topk)
+    xa = datagen.activations(96, t, f)
+    u = np.repeat(xa[:, None, :], topk, axis=1)      # same activation in every slot
+    y = o.moe_stage(Wd, Sd, ids, w, u, topk * f, f, d, f, epi_silu=False)
+    for i in range(t):
+        dense = o.gemv(Wd[0], Sd[0], xa[i])
+        assert np.allclose(y[i], w[i].astype(np.float64).sum() * dense, rtol=1e-13, atol=1e-13)
+
+
+def pin_moe_per_slot_outputs(o):
+    e, d, n, t, topk = 5, 64, 48, 2, 3
+    W, S = _experts(o, 97, e, n, d)
+    ids, _ = datagen.routing(98, t, e, topk)
+    x = datagen.activations(99, t * topk, d)
+    y = o.moe_stage(W, S, ids, None, x, topk * d, d, n, d, epi_silu=False)
+    for i in range(t):
+        for s in range(topk):
+            ex = ids[i, s]
+            assert np.array_equal(y[i, s], o.gemv(W[ex], S[ex], x[i * topk + s]))
+
+
+# --------------------------------------------------------------------------
+# stack pins (decode loop with attention := V slice)
+# --------------------------------------------------------------------------
+
+DIMS = (64, 96, 192, 128, 64)          # d, f, n_qkv, v_off, dv
+
+
+def _layer_mats(o, seed, zero_o_down=False):
+    d, f, nq, _, dv = DIMS
+    seven = lambda n, k: np.full((n, k), 7, np.uint8)
+    mats = []
+    for j, (n, k) in enumerate([(nq, d), (d, dv), (2 * f, d), (d, f)]):
+        codes = seven(n, k) if (zero_o_down and j in (1, 3)) else datagen.codes(seed + j, n, k)
+        mats += [o.pack(codes), datagen.scales(seed + 10 + j, n, k)]
+    return mats
+
+
+def pin_stack_identity_layers(o):
+    """O and down codes all 7: both residual adds add zero, so r is unchanged
+    and h is RMSNorm(r) with the next layer's gamma."""
+    d = DIMS[0]
+    L = 3
+    layers = [_layer_mats(o, 100 + 20 * i, zero_o_down=True) for i in range(L)]
+    gi = datagen.gammas(160, L, d)
+    gp = datagen.gammas(161, L, d)
+    gf = datagen.gammas(162, 1, d)[0]
+    r0 = datagen.activations(163, 1, d)[0]
+    h0 = datagen.activations(164, 1, d)[0]
+    r, h, h64, tr, th = o.stack(DIMS, layers, gi, gp, gf, r0, h0, trace=True)
+    assert np.array_equal(r.view(np.uint16), r0.view(np.uint16))
+    for li in range(L):
+        g_next = gi[li + 1] if li + 1 < L else gf
+        _, ref = o.add_rmsnorm(None, r0, g_next)
+        assert np.array_equal(th[li].view(np.uint16), ref[0].astype(np.float16).view(np.uint16))
+    _, ref = o.add_rmsnorm(None, r0, gf)
+    assert np.array_equal(h64, ref[0])
+
+
+def pin_stack_only_v_slice_matters(o):
+    """Rows of the QKV matrix outside the V slice do not change the result."""
+    d, f, nq, v_off, dv = DIMS
+    lay = _layer_mats(o, 200)
+    lay2 = list(lay)
+    codes = o.unpack(lay[0])
+    codes[:v_off] = (codes[:v_off] + 5) % 16
+    lay2[0] = o.pack(codes)
+    gp, gn = datagen.gammas(201, 2, d)
+    r0 = datagen.activations(202, 1, d)[0]
+    h0 = datagen.activations(203, 1, d)[0]
+    a = o.layer(DIMS, lay, gp, gn, r0, h0)
+    b = o.layer(DIMS, lay2, gp, gn, r0, h0)
+    assert np.array_equal(a[2], b[2])
+    codes[v_off] = (codes[v_off] + 3) % 16          # a V row does change it
+    lay2[0] = o.pack(codes)
+    c = o.layer(DIMS, lay2, gp, gn, r0, h0)
+    assert not np.array_equal(a[2], c[2])
+
+
+def pin_layer_is_composition(o):
+    """One layer equals the chain of single ops with f16 stores between them."""
+    d, f, nq, v_off, dv = DIMS
+    Wq, Sq, Wo, So, Wg, Sg, Wd, Sd = _layer_mats(o, 300)
+    gp, gn = datagen.gammas(301, 2, d)
+    r0 = datagen.activations(302, 1, d)[0]
+    h0 = datagen.activations(303, 1, d)[0]
+    r2, h2, h64 = o.layer(DIMS, [Wq, Sq, Wo, So, Wg, Sg, Wd, Sd], gp, gn, r0, h0)
+    qkv = o.gemv(Wq, Sq, h0).astype(np.float16)
+    oo = o.gemv(Wo, So, qkv[v_off:v_off + dv]).astype(np.float16)
+    r1, h1 = o.add_rmsnorm(oo, r0, gp)
+    gu = o.gemv(Wg, Sg, h1[0].astype(np.float16)).astype(np.float16)
+    u = o.silu_mul(gu)[0].astype(np.float16)
+    dn = o.gemv(Wd, Sd, u).astype(np.float16)
+    rr, hh = o.add_rmsnorm(dn, r1[0], gn)
+    assert np.array_equal(rr[0].view(np.uint16), r2.view(np.uint16))
+    assert np.array_equal(hh[0], h64)
+
+
+def pin_stack_is_layer_sequence(o):
+    d = DIMS[0]
+    L = 2
+    layers = [_layer_mats(o, 400 + 20 * i) for i in range(L)]
+    gi = datagen.gammas(460, L, d)
+    gp = datagen.gammas(461, L, d)
+    gf = datagen.gammas(462, 1, d)[0]
+    r0 = datagen.activations(463, 1, d)[0]
+    h0 = datagen.activations(464, 1, d)[0]
+    r, h, h64 = o.stack(DIMS, layers, gi, gp, gf, r0, h0)
+    ra, ha, _ = o.layer(DIMS, layers[0], gp[0], gi[1], r0, h0)
+    rb, hb, hb64 = o.layer(DIMS, layers[1], gp[1], gf, ra, ha)
+    assert np.array_equal(r.view(np.uint16), rb.view(np.uint16))
+    assert np.array_equal(h64, hb64)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
