@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of the int4 (q4f16_1) decode path on one MI355X.
+
+Workload (one "step" = one decode token): a Phi-3-mini-shaped 32-layer stack at
+batch 1 -- per layer QKV 9216x3072 -> O 3072x3072 (input: the V slice, i.e.
+single-position attention) -> add+RMSNorm -> gate_up 16384x3072 + SiLU-multiply
+-> down 3072x8192 -> add+RMSNorm, all weights int4 group-32 (2,038,431,744 bytes
+per token), eps 1e-5, gammas ~N(1, 0.1). Each token consumes the previous
+token's output: token i+1 starts from residual = h_i and normalised state =
+h_i (a unit-RMS vector, as an embedding row would be after the input norm), so
+the timed steps form one dependency chain while the residual stream restarts
+every token, as it does in decode. Weights
+(synthetic, seeded) are resident in HBM before timing starts; 2.04 GB per token
+streams past the 256 MB Infinity Cache by itself.
+
+Printed: one JSON line with the effective weight bandwidth (GB/s), the
+microseconds per token, the roofline of the dominant kernel (measured with HIP
+events on the stream it runs on) and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import datagen  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "effective weight GB/s (% of HBM peak) and µs/token for int4 dequant-GEMV decode stack"
+
+PHI3 = dict(d=3072, f=8192, n_qkv=9216, v_off=6144, dv=3072, layers=32, eps=1e-5)
+BPW = 0.5625  # bytes per int4 weight: 4 bits + one f16 scale per 32 weights
+
+
+def layer_shapes(p):
+    return [(p["n_qkv"], p["d"]), (p["d"], p["dv"]), (2 * p["f"], p["d"]), (p["d"], p["f"])]
+
+
+def stack_weight_bytes(p, n_layers=None):
+    n_layers = p["layers"] if n_layers is None else n_layers
+    return int(n_layers * sum(n * k * BPW for n, k in layer_shapes(p)))
+
+
+def stack_seed(layer, j):
+    """Seed of matrix j (0..7: W/S of QKV, O, gate_up, down) of one layer."""
+    return datagen.SEED_BASE + 3_000_000 + 16 * layer + j
+
+
+def host_layer(p, layer):
+    """Packed words and scales of one layer, as host arrays (for the oracle)."""
+    mats = []
+    for j, (n, k) in enumerate(layer_shapes(p)):
+        mats.append(datagen.words(stack_seed(layer, 2 * j), n, k))
+        mats.append(datagen.scales(stack_seed(layer, 2 * j + 1), n, k))
+    return mats
+
+
+def host_state(p, n_layers):
+    d = p["d"]
+    base = datagen.SEED_BASE + 3_900_000
+    gi = datagen.gammas(base + 1, n_layers, d)
+    gp = datagen.gammas(base + 2, n_layers, d)
+    gf = datagen.gammas(base + 3, 1, d)[0]
+    r0 = datagen.activations(base + 4, 1, d)[0]
+    h0 = datagen.activations(base + 5, 1, d)[0]
+    return gi, gp, gf, r0, h0
+
+
+def build_stack(q4, torch, p, n_layers=None, device="cuda"):
+    """Upload a seeded stack. Returns (q4.Stack, device state dict)."""
+    n_layers = p["layers"] if n_layers is None else n_layers
+    layers = []
+    for L in range(n_layers):
+        mats = host_layer(p, L)
+        layers.append([torch.from_numpy(m.view(np.int32) if m.dtype == np.uint32 else m)
+                       .to(device) for m in mats])
+    gi, gp, gf, r0, h0 = host_state(p, n_layers)
+    g = [torch.from_numpy(a).to(device) for a in (gi, gp, gf)]
+    stack = q4.Stack(layers, g[0], g[1], g[2], p["d"], p["f"], p["n_qkv"], p["v_off"], p["dv"],
+                     p["eps"])
+    st = dict(r0=torch.from_numpy(r0).to(device), h0=torch.from_numpy(h0).to(device),
+              gammas=g, host=(gi, gp, gf, r0, h0))
+    return stack, st
+
+
+def time_dominant_kernel(q4, torch, stack, st, p, reps=3):
+    """The gate_up matvec as the stack runs it (RMSNorm prologue, SiLU-multiply
+    epilogue; the largest matrix of a layer), launched over the 32 layers'
+    gate_up weights back to back (a 906 MB rotation), each launch bracketed by
+    HIP events on the stream it runs on. A device-side sleep queued first keeps
+    the stream busy while the launches are enqueued, so the events see the
+    kernels back to back rather than host launch latency."""
+    d, f = p["d"], p["f"]
+    x = st["r0"]
+    gamma = st["gammas"][1][0]
+    y = torch.empty(f, dtype=torch.float16, device="cuda")
+    n = len(stack.layers)
+    durs = []
+    for _ in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        torch.cuda._sleep(20_000_000)
+        for L in range(n):
+            ev[L].record()
+            Wg, Sg = stack.layers[L][4], stack.layers[L][5]
+            q4.gemv_ex(Wg, Sg, x, y=y, kind=q4.EPI_SILU_MUL, norm_gamma=gamma, eps=p["eps"])
+        ev[n].record()
+        torch.cuda.synchronize()
+        durs += [ev[L].elapsed_time(ev[L + 1]) * 1e3 for L in range(n)]
+    us = float(np.mean(durs))
+    bytes_per_launch = 2 * f * d * BPW
+    return us, bytes_per_launch
+
+
+def verify_one_token(q4, torch, stack, st, p, o, layers_checked=(0, 1)):
+    """Teacher-forced check of single layers of one token against the oracle."""
+    d = p["d"]
+    n = len(stack.layers)
+    trace = torch.empty((n, 2, d), dtype=torch.float16, device="cuda")
+    r_out = torch.empty(d, dtype=torch.float16, device="cuda")
+    h_out = torch.empty(d, dtype=torch.float16, device="cuda")
+    stack.decode(st["r0"], st["h0"], r_out, h_out, trace=trace)
+    torch.cuda.synchronize()
+    tr = trace.cpu().numpy()
+    gi, gp, gf, r0, h0 = st["host"]
+    worst = 0.0
+    dims = (p["d"], p["f"], p["n_qkv"], p["v_off"], p["dv"])
+    for L in layers_checked:
+        r_in, h_in = (r0, h0) if L == 0 else (tr[L - 1, 0], tr[L - 1, 1])
+        g_next = gi[L + 1] if L + 1 < n else gf
+        _, _, h64 = o.layer(dims, host_layer(p, L), gp[L], g_next, r_in, h_in, eps=p["eps"])
+        err = np.abs(tr[L, 1].astype(np.float64) - h64)
+        tol = 1e-2 + 5e-3 * np.abs(h64)
+        if not np.all(err <= tol):
+            raise SystemExit("parity check failed at layer %d (max abs err %.3g)" % (L, err.max()))
+        worst = max(worst, float(err.max()))
+    return worst
+
+
+def cpu_baseline(p, o, seconds=10.0):
+    """The oracle (single-threaded C, binary64) on whole decode layers of the same
+    stack, chained, until about `seconds` of CPU time has been spent."""
+    gi, gp, gf, r0, h0 = host_state(p, p["layers"])
+    dims = (p["d"], p["f"], p["n_qkv"], p["v_off"], p["dv"])
+    r, h = r0, h0
+    done, spent = 0, 0.0
+    while spent < seconds and done < p["layers"]:
+        mats = host_layer(p, done)
+        t0 = time.perf_counter()
+        r, h, _ = o.layer(dims, mats, gp[done], gi[done + 1] if done + 1 < p["layers"] else gf,
+                          r, h, eps=p["eps"])
+        spent += time.perf_counter() - t0
+        done += 1
+    gbs = stack_weight_bytes(p, done) / spent / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "%d of 32 decode layers of one token (%.1f MB of int4 weights), "
+                      "single-threaded C oracle in binary64, %.1f s" % (
+                          done, stack_weight_bytes(p, done) / 1e6, spent)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the int4 decode path is built and timed on a single "
+              "MI355X (multi-GPU sharding is a design note, not part of this build); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import int4_weight_only_q4_amd as q4
+
+    q4.lib()
+    assert torch.cuda.is_available(), "no GPU"
+    p = PHI3
+    print("building the %d-layer stack (%.3f GB of int4 weights)..." % (
+        p["layers"], stack_weight_bytes(p) / 1e9), file=sys.stderr, flush=True)
+    stack, st = build_stack(q4, torch, p)
+    torch.cuda.synchronize()
+
+    import oracle
+    o = oracle.load()
+    worst = verify_one_token(q4, torch, stack, st, p, o)
+    print("parity (teacher-forced layers 0,1): max abs err %.3g" % worst, file=sys.stderr,
+          flush=True)
+
+    d = p["d"]
+    r_out = torch.empty(d, dtype=torch.float16, device="cuda")
+    hs = [st["h0"].clone(), torch.empty(d, dtype=torch.float16, device="cuda")]
+    stack.decode(st["r0"], st["h0"], r_out, hs[0])      # first token from the seeded state
+
+    def run(i0, count):
+        # token i+1 starts from (residual, normalised) = (h_i, h_i)
+        for i in range(i0, i0 + count):
+            a, b = i & 1, (i + 1) & 1
+            stack.decode(hs[a], hs[a], r_out, hs[b])
+
+    run(0, args.warmup)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    run(args.warmup, args.steps)
+    e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1e3 / args.steps
+    gpu_ms = e0.elapsed_time(e1) / args.steps
+    ms = max(wall_ms, gpu_ms)
+    h_last = hs[(args.warmup + args.steps) & 1].float()
+    if not torch.isfinite(h_last).all() or float(h_last.abs().max()) == 0.0:
+        raise SystemExit("timed output is not finite / all zero")
+
+    wb = stack_weight_bytes(p)
+    gbs = wb / (ms * 1e-3) / 1e9
+    dom_us, dom_bytes = time_dominant_kernel(q4, torch, stack, st, p)
+    dom_gbs = dom_bytes / (dom_us * 1e-6) / 1e9
+
+    rec = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "Phi-3-mini-shaped 32-layer int4 (q4f16_1) decode stack, batch 1",
+            "layers": p["layers"], "d": p["d"], "ffn": p["f"], "qkv_rows": p["n_qkv"],
+            "weight_bytes_per_token": wb,
+            "us_per_token": round(ms * 1e3, 2),
+            "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "gpu_event_ms_per_token": round(gpu_ms, 6),
+            "wall_ms_per_token": round(wall_ms, 6),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "gate_up 16384x3072 matvec, RMSNorm prologue + SiLU-multiply epilogue",
+            "achieved": round(dom_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+            "us_per_launch": round(dom_us, 3),
+            "bytes_per_launch": int(dom_bytes),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(p, o, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -51,6 +51,21 @@ def codes(seed: int, n: int, k: int) -> np.ndarray:
     return _rng(seed).integers(0, 16, size=(n, k), dtype=np.uint8)
 
 
+def words(seed: int, n: int, k: int) -> np.ndarray:
+    """Uniform random 32-bit words ``uint32[n][k // 8]``.
+
+    Every 4-bit field of a uniform random word is an independent uniform code in
+    [0, 15], whatever the field order, so these words are a draw of ``n * k``
+    uniform codes already in packed form. Used for the large workloads, where
+    drawing one byte per code would dominate the set-up time.
+    """
+    if k % 8:
+        raise ValueError(f"K={k} is not a multiple of 8")
+    count = n * (k // 8)
+    raw = _rng(seed).bit_generator.random_raw((count + 1) // 2).astype("<u8")
+    return raw.view("<u4")[:count].reshape(n, k // 8).copy()
+
+
 def scales(seed: int, n: int, k: int) -> np.ndarray:
     """One binary16 scale per 32-element K-group: ``float16[n][k // 32]``."""
     if k % GROUP:

@@ -1,0 +1,231 @@
+/*
+ * q4.h -- C ABI of libq4, an MI355X (gfx950) library for the single-token
+ * decode matmul over q4f16_1 group-quantised int4 weights, with the
+ * dequantisation fused into the matmul.
+ *
+ * Weight format (Zero TVM Documentation, "Q4F16 quantization format"):
+ *   packed  uint32 [N][K/8]   eight 4-bit codes per word; element k = 8j + i of
+ *                             a row lives in word j, bits 4i..4i+3
+ *   scales  binary16 [N][K/32] one scale per 32 consecutive K elements
+ *   value   w[n][k] = (code - 7) * scale[n][k/32]
+ * y = W x: weights are stored by output row (the "NT" matmul of RESEARCH.md,
+ * "1. Dispatch profile", and shader 5 of "WGSL Kernel Roles").
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers on the current HIP device, owned
+ *     by the caller; the library never frees them. binary16 values are passed
+ *     as uint16_t bit patterns.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the call returns without synchronising. Argument errors are detected on
+ *     the host before anything is enqueued and returned synchronously; nothing
+ *     is launched then. Kernel faults surface at the caller's next
+ *     synchronisation.
+ *   - Shapes: K must be a multiple of 32 and at most Q4_MAX_K; dimensions are
+ *     positive. Alignment: packed weights and the activation input of a matvec
+ *     16 bytes (row strides of batched / MoE activations multiples of 8
+ *     elements); every other binary16 vector 2 bytes. Tensors from a device
+ *     allocator satisfy this.
+ *   - Outputs must not overlap any input of the same call (Q4_EALIAS). This
+ *     includes the residual rule of the ping-pong buffers (Zero TVM
+ *     Documentation, "Ping-pong residual buffers"): res_out != res_in.
+ *   - Accumulation is f32; results are rounded to binary16 (nearest even).
+ *     Results are bit-identical from run to run for the same arguments on the
+ *     same device (fixed reduction order, no floating-point atomics).
+ *   - Entry points that need scratch memory (fused add+RMSNorm, MoE, stack)
+ *     use a library-owned workspace allocated once per (device, stream) on first
+ *     use and kept until the process ends; concurrent calls on distinct streams
+ *     do not share it. The first such call on a stream allocates, so warm up
+ *     before capturing a HIP graph.
+ */
+#ifndef Q4_H
+#define Q4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum q4_status {
+    Q4_OK = 0,
+    Q4_EINVAL = 1, /* NULL pointer, non-positive dimension, unknown mode      */
+    Q4_ESHAPE = 2, /* K % 32 != 0, odd row count for a SiLU split, ...       */
+    Q4_EALIGN = 3, /* pointer not aligned as stated above                    */
+    Q4_EALIAS = 4, /* an output overlaps an input                            */
+    Q4_ERANGE = 5, /* a size beyond a supported maximum                      */
+    Q4_EHIP = 6    /* HIP runtime error (allocation, launch)                 */
+} q4_status;
+
+/* Largest supported reduction length (the activation vector is staged in LDS). */
+#define Q4_MAX_K 24576
+
+/* A hipStream_t. */
+typedef void *q4_stream;
+
+/* Library version string. */
+const char *q4_version(void);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char *q4_last_error(void);
+
+/* Number of bytes one int4 weight occupies in this format (0.5625 = 4.5 bits):
+ * K/8 * 4 + K/32 * 2 bytes per row of K weights. Host-only helper. */
+double q4_bytes_per_weight(void);
+
+/* ---------------------------------------------------------------------------
+ * q4_pack -- "Q4F16 quantization format": codes u8[N][K] with values 0..15 ->
+ * packed u32[N][K/8], code of element 8j+i into bits 4i..4i+3 of word j.
+ * Codes above 15 are not checked on the device; only their low 4 bits are used.
+ * Alignment: packed 16 bytes; codes any.
+ */
+q4_status q4_pack(const uint8_t *codes, uint32_t *packed, int64_t N, int64_t K,
+                  q4_stream stream);
+
+/* q4_unpack -- inverse of q4_pack (u32[N][K/8] -> u8[N][K]); a test hook. */
+q4_status q4_unpack(const uint32_t *packed, uint8_t *codes, int64_t N, int64_t K,
+                    q4_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * q4_gemv -- the decode matmul ("WGSL Kernel Roles", shader 5 "int4 Matmul";
+ * RESEARCH.md "Matmul Shader Analysis"):
+ *   y[n] = f16( sum_k (code[n][k] - 7) * S[n][k/32] * x[k] ),  f32 accumulation
+ * W u32[N][K/8], S f16[N][K/32], x f16[K], y f16[N].
+ */
+q4_status q4_gemv(const uint32_t *W, const uint16_t *S, const uint16_t *x, uint16_t *y,
+                  int64_t N, int64_t K, q4_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * q4_gemv_batched -- M activation rows sharing one weight read (BENCH.md,
+ * "Falsifiability result: batched M-dim matmul"):
+ *   y[m*ldy + n] = f16( sum_k w[n][k] * x[m*ldx + k] ),  m = 0..M-1
+ * ldx >= K, ldy >= N (elements). 1 <= M <= Q4_MAX_M.
+ */
+#define Q4_MAX_M 64
+q4_status q4_gemv_batched(const uint32_t *W, const uint16_t *S, const uint16_t *x,
+                          int64_t ldx, uint16_t *y, int64_t ldy, int64_t N, int64_t K,
+                          int64_t M, q4_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * q4_moe_gemv -- one expert stage of a MoE layer (BENCH.md, "MoE chunked
+ * prefill (2026-08-13)": every (token, slot) runs its own expert's matmul; the
+ * slot outputs are combined by routing weight; "MoE Phase B": grouping the
+ * (token, slot) rows by expert so each expert's weights are read once).
+ *   W u32[E][N][K/8], S f16[E][N][K/32]   expert weights, stacked
+ *   ids i32[T][TOPK]                       expert of (token t, slot s), 0 <= id < E
+ *   x                                      activation of (t, s) starts at
+ *                                          x + t*ldx + s*x_slot_stride (f16[K]);
+ *                                          x_slot_stride = 0 shares one row per token
+ *   v(t, s) = W[ids[t][s]] . x(t, s)       (f32)
+ * Modes:
+ *   epi_silu != 0, route_w == NULL : y f16[T][TOPK][N/2] =
+ *        f16( silu(f16(v[:N/2])) * f16(v[N/2:]) )   (gate_up stage; N even)
+ *   epi_silu == 0, route_w == NULL : y f16[T][TOPK][N] = f16(v)
+ *   epi_silu == 0, route_w f16[T][TOPK] : y f16[T][N] =
+ *        f16( sum_s route_w[t][s] * v(t, s) )       (down stage + combine)
+ * epi_silu together with route_w is Q4_EINVAL. Each distinct expert's weights
+ * are streamed once per call for all (t, s) that chose it. Ids are validated on
+ * the device; an out-of-range id contributes zeros. T*TOPK <= Q4_MAX_PAIRS.
+ */
+#define Q4_MAX_PAIRS 4096
+q4_status q4_moe_gemv(const uint32_t *W, const uint16_t *S, const int32_t *ids,
+                      const uint16_t *route_w, const uint16_t *x, int64_t ldx,
+                      int64_t x_slot_stride, uint16_t *y, int64_t E, int64_t N, int64_t K,
+                      int64_t T, int64_t TOPK, int epi_silu, q4_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * q4_add_rmsnorm -- fused residual add + RMSNorm ("WGSL Kernel Roles", shaders 2
+ * and 7; "Ping-pong residual buffers"), for M rows of length D:
+ *   res_out = f16(a + res_in)          (a == NULL: res_out = res_in)
+ *   out     = f16( res_out / sqrt(mean(res_out^2) + eps) * gamma )
+ * a, res_in, out, res_out f16[M][D]; gamma f16[D]. res_out must not overlap
+ * res_in; out must not overlap a or res_in. D <= Q4_MAX_K.
+ */
+q4_status q4_add_rmsnorm(const uint16_t *a, const uint16_t *res_in, const uint16_t *gamma,
+                         uint16_t *out, uint16_t *res_out, int64_t D, int64_t M, float eps,
+                         q4_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * q4_silu_mul -- split-SiLU-multiply (RESEARCH.md, "1. Dispatch profile": gate
+ * split + SiLU + elementwise multiply; shader 6 "Fused FFN": gate and up share
+ * one row-concatenated matrix, gate first):
+ *   out[m][i] = f16( silu(gu[m][i]) * gu[m][F + i] ),  silu(z) = z / (1 + e^-z)
+ * gu f16[M][2F], out f16[M][F].
+ */
+q4_status q4_silu_mul(const uint16_t *gu, uint16_t *out, int64_t F, int64_t M,
+                      q4_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * q4_gemv_ex -- q4_gemv with a fused prologue and/or epilogue. The results are
+ * bit-identical to the unfused sequence of calls named below.
+ *   prologue (norm_gamma != NULL): x is a residual f16[K]; the matvec input is
+ *                        q4_add_rmsnorm(NULL, x, norm_gamma, h, ., K, 1, eps)'s h,
+ *                        computed inside the matvec (norm_gamma 16-byte aligned).
+ *                        Not combined with Q4_EPI_ADD_RMSNORM.
+ *   Q4_EPI_NONE        : as q4_gemv.
+ *   Q4_EPI_SILU_MUL    : rows [0, N/2) are gate, [N/2, N) are up; y f16[N/2] =
+ *                        q4_silu_mul(q4_gemv(W, S, x)).   N even.
+ *   Q4_EPI_ADD_RMSNORM : t = q4_gemv(W, S, x) (f16[N], not stored);
+ *                        q4_add_rmsnorm(t, res_in, gamma, y, res_out, N, 1, eps).
+ *                        N <= Q4_MAX_K. Runs as the matvec with the residual add
+ *                        in its per-row epilogue followed by a one-workgroup
+ *                        normalisation (no synchronisation inside a kernel).
+ */
+typedef enum q4_epi_kind { Q4_EPI_NONE = 0, Q4_EPI_SILU_MUL = 1, Q4_EPI_ADD_RMSNORM = 2 } q4_epi_kind;
+
+typedef struct q4_epilogue {
+    int kind;                    /* q4_epi_kind                                  */
+    const uint16_t *res_in;      /* ADD_RMSNORM: running residual f16[N]          */
+    const uint16_t *gamma;       /* ADD_RMSNORM: norm weights f16[N]              */
+    uint16_t *res_out;           /* ADD_RMSNORM: new residual f16[N], != res_in   */
+    float eps;                   /* both norms                                    */
+    const uint16_t *norm_gamma;  /* prologue norm weights f16[K], or NULL         */
+} q4_epilogue;
+
+q4_status q4_gemv_ex(const uint32_t *W, const uint16_t *S, const uint16_t *x, uint16_t *y,
+                     int64_t N, int64_t K, const q4_epilogue *epi, q4_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * q4_stack_decode -- one decode token through a stack of decoder layers whose
+ * attention is replaced by the single-position identity on the V slice
+ * (Zero TVM Documentation, "Decode loop": per layer QKV matmul -> attention ->
+ * O matmul -> add+RMSNorm -> gate_up + SiLU*mul -> down -> add+RMSNorm; with one
+ * cached position the softmax weight is 1, so attention returns V).
+ * Per layer L (r, h: residual and normalised hidden state, f16[d]):
+ *   qkv = f16(Wqkv[L] . h)                       Wqkv: n_qkv x d
+ *   o   = f16(Wo[L] . qkv[v_off : v_off + dv])   Wo:   d x dv
+ *   (r, h) = add_rmsnorm(o, r, gamma_post[L])
+ *   u   = silu_mul(f16(Wgu[L] . h))              Wgu:  2f x d
+ *   dn  = f16(Wdn[L] . u)                        Wdn:  d x f
+ *   (r, h) = add_rmsnorm(dn, r, L+1 < n_layers ? gamma_in[L+1] : gamma_final)
+ * The descriptor holds HOST arrays of n_layers DEVICE pointers per matrix, and
+ * device pointers to gamma_in f16[n_layers][d], gamma_post f16[n_layers][d],
+ * gamma_final f16[d]. r_in/h_in are read, r_out/h_out written (f16[d]); inputs
+ * and outputs must not overlap. trace (may be NULL) receives the state after
+ * every layer: f16[n_layers][2][d] as (r, h) pairs.
+ */
+typedef struct q4_stack_desc {
+    int64_t n_layers, d, f, n_qkv, v_off, dv;
+    float eps;
+    const uint32_t *const *Wqkv;
+    const uint16_t *const *Sqkv;
+    const uint32_t *const *Wo;
+    const uint16_t *const *So;
+    const uint32_t *const *Wgu;
+    const uint16_t *const *Sgu;
+    const uint32_t *const *Wdn;
+    const uint16_t *const *Sdn;
+    const uint16_t *gamma_in;
+    const uint16_t *gamma_post;
+    const uint16_t *gamma_final;
+} q4_stack_desc;
+
+q4_status q4_stack_decode(const q4_stack_desc *desc, const uint16_t *r_in,
+                          const uint16_t *h_in, uint16_t *r_out, uint16_t *h_out,
+                          uint16_t *trace, q4_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4_H */

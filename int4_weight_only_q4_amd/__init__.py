@@ -1,0 +1,260 @@
+"""Python binding of libq4, the gfx950 int4 (q4f16_1) decode-matmul library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/q4.h``. PyTorch provides device
+memory and streams. There is no CPU fallback: if ``libq4.so`` has not been
+built, ``lib()`` raises.
+
+Tensor conventions (all on the current CUDA/HIP device):
+  packed weights  int32  [N, K/8]   (the uint32 words, viewed as int32)
+  scales          float16 [N, K/32]
+  activations     float16
+Calls enqueue on ``stream`` (default: torch's current stream) and return
+without synchronising.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libq4.so")
+
+Q4_OK, Q4_EINVAL, Q4_ESHAPE, Q4_EALIGN, Q4_EALIAS, Q4_ERANGE, Q4_EHIP = range(7)
+EPI_NONE, EPI_SILU_MUL, EPI_ADD_RMSNORM = 0, 1, 2
+MAX_K = 24576
+MAX_M = 64
+MAX_PAIRS = 4096
+
+#: Bytes per int4 weight in this format: 4 bits + one f16 scale per 32 weights.
+BYTES_PER_WEIGHT = 0.5 + 2.0 / 32.0
+
+ABI_SYMBOLS = (
+    "q4_version", "q4_last_error", "q4_bytes_per_weight", "q4_pack", "q4_unpack", "q4_gemv",
+    "q4_gemv_batched", "q4_moe_gemv", "q4_add_rmsnorm", "q4_silu_mul", "q4_gemv_ex",
+    "q4_stack_decode",
+)
+
+
+class Q4Error(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__("libq4 status %d: %s" % (status, message))
+        self.status = status
+
+
+class Epilogue(C.Structure):
+    _fields_ = [("kind", C.c_int), ("res_in", C.c_void_p), ("gamma", C.c_void_p),
+                ("res_out", C.c_void_p), ("eps", C.c_float), ("norm_gamma", C.c_void_p)]
+
+
+class StackDesc(C.Structure):
+    _fields_ = [("n_layers", C.c_int64), ("d", C.c_int64), ("f", C.c_int64),
+                ("n_qkv", C.c_int64), ("v_off", C.c_int64), ("dv", C.c_int64),
+                ("eps", C.c_float),
+                ("Wqkv", C.c_void_p), ("Sqkv", C.c_void_p), ("Wo", C.c_void_p),
+                ("So", C.c_void_p), ("Wgu", C.c_void_p), ("Sgu", C.c_void_p),
+                ("Wdn", C.c_void_p), ("Sdn", C.c_void_p),
+                ("gamma_in", C.c_void_p), ("gamma_post", C.c_void_p),
+                ("gamma_final", C.c_void_p)]
+
+
+_P, _I = C.c_void_p, C.c_int64
+_SIGS = {
+    "q4_version": (C.c_char_p, []),
+    "q4_last_error": (C.c_char_p, []),
+    "q4_bytes_per_weight": (C.c_double, []),
+    "q4_pack": (C.c_int, [_P, _P, _I, _I, _P]),
+    "q4_unpack": (C.c_int, [_P, _P, _I, _I, _P]),
+    "q4_gemv": (C.c_int, [_P, _P, _P, _P, _I, _I, _P]),
+    "q4_gemv_batched": (C.c_int, [_P, _P, _P, _I, _P, _I, _I, _I, _I, _P]),
+    "q4_moe_gemv": (C.c_int, [_P, _P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _I, C.c_int, _P]),
+    "q4_add_rmsnorm": (C.c_int, [_P, _P, _P, _P, _P, _I, _I, C.c_float, _P]),
+    "q4_silu_mul": (C.c_int, [_P, _P, _I, _I, _P]),
+    "q4_gemv_ex": (C.c_int, [_P, _P, _P, _P, _I, _I, C.POINTER(Epilogue), _P]),
+    "q4_stack_decode": (C.c_int, [C.POINTER(StackDesc), _P, _P, _P, _P, _P, _P]),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded libq4 (raises if it has not been built).
+
+    torch is imported first so that libq4 binds to the HIP runtime torch has
+    loaded (both carry the soname libamdhip64.so.7); loading libq4 first would
+    bring a second HIP runtime into the process.
+    """
+    global _lib
+    if _lib is None:
+        import torch  # noqa: F401  (loads the process's HIP runtime)
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libq4.so is not built (run __graft_entry__.build() or "
+                              "python -m int4_weight_only_q4_amd._build)")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def version() -> str:
+    return lib().q4_version().decode()
+
+
+def _check(status):
+    if status != Q4_OK:
+        raise Q4Error(status, lib().q4_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _need(t, dtype, name):
+    import torch
+    if t is None:
+        raise ValueError("%s is required" % name)
+    if t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous %s CUDA tensor" % (name, dtype))
+    return t
+
+
+def pack(codes, out=None, stream=None):
+    """codes uint8 [N, K] (values 0..15) -> packed int32 [N, K/8]."""
+    import torch
+    _need(codes, torch.uint8, "codes")
+    n, k = codes.shape
+    if out is None:
+        out = torch.empty((n, k // 8), dtype=torch.int32, device=codes.device)
+    _check(lib().q4_pack(_ptr(codes), _ptr(out), n, k, _stream(stream)))
+    return out
+
+
+def unpack(packed, k=None, out=None, stream=None):
+    import torch
+    _need(packed, torch.int32, "packed")
+    n = packed.shape[0]
+    k = packed.shape[1] * 8 if k is None else k
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.uint8, device=packed.device)
+    _check(lib().q4_unpack(_ptr(packed), _ptr(out), n, k, _stream(stream)))
+    return out
+
+
+def gemv(W, S, x, y=None, stream=None):
+    """y[N] = f16(W . x) with W packed int32 [N, K/8], S f16 [N, K/32], x f16 [K]."""
+    import torch
+    n, k = W.shape[0], W.shape[1] * 8
+    if y is None:
+        y = torch.empty(n, dtype=torch.float16, device=W.device)
+    _check(lib().q4_gemv(_ptr(W), _ptr(S), _ptr(x), _ptr(y), n, k, _stream(stream)))
+    return y
+
+
+def gemv_ex(W, S, x, y=None, kind=EPI_NONE, res_in=None, gamma=None, res_out=None, eps=1e-5,
+            norm_gamma=None, stream=None):
+    """q4_gemv with a fused prologue / epilogue (see include/q4.h)."""
+    import torch
+    n, k = W.shape[0], W.shape[1] * 8
+    if y is None:
+        y = torch.empty(n // 2 if kind == EPI_SILU_MUL else n, dtype=torch.float16,
+                        device=W.device)
+    epi = Epilogue(kind, _ptr(res_in), _ptr(gamma), _ptr(res_out), eps, _ptr(norm_gamma))
+    _check(lib().q4_gemv_ex(_ptr(W), _ptr(S), _ptr(x), _ptr(y), n, k, C.byref(epi),
+                            _stream(stream)))
+    return y
+
+
+def gemv_batched(W, S, x, y=None, stream=None):
+    """x f16 [M, ldx >= K] -> y f16 [M, N]; rows share one weight read."""
+    import torch
+    n, k = W.shape[0], W.shape[1] * 8
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float16, device=W.device)
+    _check(lib().q4_gemv_batched(_ptr(W), _ptr(S), _ptr(x), x.stride(0), _ptr(y), y.stride(0),
+                                 n, k, m, _stream(stream)))
+    return y
+
+
+def moe_gemv(W, S, ids, x, ldx, x_slot_stride, route_w=None, epi_silu=False, y=None,
+             stream=None):
+    """One MoE expert stage. W int32 [E, N, K/8], S f16 [E, N, K/32], ids int32 [T, TOPK]."""
+    import torch
+    e, n, k = W.shape[0], W.shape[1], W.shape[2] * 8
+    t, topk = ids.shape
+    if y is None:
+        if route_w is not None:
+            shape = (t, n)
+        else:
+            shape = (t, topk, n // 2 if epi_silu else n)
+        y = torch.empty(shape, dtype=torch.float16, device=W.device)
+    _check(lib().q4_moe_gemv(_ptr(W), _ptr(S), _ptr(ids), _ptr(route_w), _ptr(x), ldx,
+                             x_slot_stride, _ptr(y), e, n, k, t, topk, int(bool(epi_silu)),
+                             _stream(stream)))
+    return y
+
+
+def add_rmsnorm(a, res_in, gamma, out=None, res_out=None, eps=1e-5, stream=None):
+    """res_out = f16(a + res_in); out = f16(RMSNorm(res_out) * gamma). Rows of length D."""
+    import torch
+    d = res_in.shape[-1]
+    m = res_in.numel() // d
+    if out is None:
+        out = torch.empty_like(res_in)
+    if res_out is None:
+        res_out = torch.empty_like(res_in)
+    _check(lib().q4_add_rmsnorm(_ptr(a), _ptr(res_in), _ptr(gamma), _ptr(out), _ptr(res_out),
+                                d, m, eps, _stream(stream)))
+    return out, res_out
+
+
+def silu_mul(gu, out=None, stream=None):
+    """gu f16 [M, 2F] = [gate | up] -> f16 [M, F]."""
+    import torch
+    f2 = gu.shape[-1]
+    m = gu.numel() // f2
+    if out is None:
+        out = torch.empty(gu.shape[:-1] + (f2 // 2,), dtype=torch.float16, device=gu.device)
+    _check(lib().q4_silu_mul(_ptr(gu), _ptr(out), f2 // 2, m, _stream(stream)))
+    return out
+
+
+class Stack:
+    """Holds a q4_stack_desc for a list of layers.
+
+    layers: list of (Wqkv, Sqkv, Wo, So, Wgu, Sgu, Wdn, Sdn) device tensors;
+    gamma_in, gamma_post: f16 [L, d]; gamma_final: f16 [d].
+    """
+
+    def __init__(self, layers, gamma_in, gamma_post, gamma_final, d, f, n_qkv, v_off, dv,
+                 eps=1e-5):
+        self.layers = layers
+        self.gammas = (gamma_in, gamma_post, gamma_final)
+        n = len(layers)
+        self._arrays = []
+        cols = []
+        for j in range(8):
+            arr = (C.c_void_p * n)(*[lay[j].data_ptr() for lay in layers])
+            self._arrays.append(arr)
+            cols.append(C.cast(arr, C.c_void_p))
+        self.desc = StackDesc(n, d, f, n_qkv, v_off, dv, eps, *cols, gamma_in.data_ptr(),
+                              gamma_post.data_ptr(), gamma_final.data_ptr())
+        self.d = d
+        self.n_layers = n
+
+    def decode(self, r_in, h_in, r_out, h_out, trace=None, stream=None):
+        _check(lib().q4_stack_decode(C.byref(self.desc), _ptr(r_in), _ptr(h_in), _ptr(r_out),
+                                     _ptr(h_out), _ptr(trace), _stream(stream)))
+
+
+def stack_decode(stack: Stack, r_in, h_in, r_out, h_out, trace=None, stream=None):
+    stack.decode(r_in, h_in, r_out, h_out, trace, stream)

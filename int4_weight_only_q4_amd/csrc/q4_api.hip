@@ -1,0 +1,458 @@
+// C ABI of libq4: argument validation on the host, workspace management and
+// dispatch to the gfx950 kernels. Every check happens before anything is
+// enqueued, so an error return means nothing was launched.
+#include <cstdarg>
+#include <cstdio>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "q4_common.h"
+
+namespace q4 {
+
+namespace {
+thread_local char g_err[512] = "";
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, std::pair<void *, size_t>> g_ws;
+}  // namespace
+
+q4_status fail(q4_status st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+q4_status check_launch(const char *what)
+{
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(Q4_EHIP, "launch of %s failed: %s", what, hipGetErrorString(e));
+    return Q4_OK;
+}
+
+void *workspace(hipStream_t stream, size_t bytes)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        fail(Q4_EHIP, "hipGetDevice failed");
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    auto &e = g_ws[{dev, stream}];
+    if (e.first && e.second >= bytes)
+        return e.first;
+    if (e.first) {
+        // growing: the old buffer may still be in use by work on this stream
+        if (hipStreamSynchronize(stream) != hipSuccess || hipFree(e.first) != hipSuccess) {
+            fail(Q4_EHIP, "releasing the workspace failed");
+            return nullptr;
+        }
+        e = {nullptr, 0};
+    }
+    size_t nb = bytes < (size_t)(1 << 20) ? (size_t)(1 << 20) : bytes;
+    void *p = nullptr;
+    if (hipMalloc(&p, nb) != hipSuccess) {
+        fail(Q4_EHIP, "hipMalloc of a %zu-byte workspace failed", nb);
+        return nullptr;
+    }
+    if (hipMemset(p, 0, kCounterBytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        hipFree(p);
+        fail(Q4_EHIP, "clearing the workspace counters failed");
+        return nullptr;
+    }
+    e = {p, nb};
+    return p;
+}
+
+}  // namespace q4
+
+using namespace q4;
+
+namespace {
+
+inline hipStream_t as_stream(q4_stream s) { return reinterpret_cast<hipStream_t>(s); }
+
+q4_status check_matrix(const uint32_t *W, const uint16_t *S, int64_t N, int64_t K)
+{
+    if (!W || !S)
+        return fail(Q4_EINVAL, "NULL weight or scale pointer");
+    if (N <= 0 || K <= 0)
+        return fail(Q4_EINVAL, "non-positive shape N=%lld K=%lld", (long long)N, (long long)K);
+    if (K % 32)
+        return fail(Q4_ESHAPE, "K=%lld is not a multiple of 32", (long long)K);
+    if (K > Q4_MAX_K)
+        return fail(Q4_ERANGE, "K=%lld exceeds Q4_MAX_K=%d", (long long)K, Q4_MAX_K);
+    if (N > (1ll << 30))
+        return fail(Q4_ERANGE, "N=%lld is too large", (long long)N);
+    if (!aligned(W, 16))
+        return fail(Q4_EALIGN, "packed weights must be 16-byte aligned");
+    if (!aligned(S, 2))
+        return fail(Q4_EALIGN, "scales must be 2-byte aligned");
+    return Q4_OK;
+}
+
+inline size_t wbytes(int64_t N, int64_t K) { return (size_t)N * (size_t)K / 2; }
+inline size_t sbytes(int64_t N, int64_t K) { return (size_t)N * (size_t)K / 16; }
+
+q4_status check_gemv_args(const uint32_t *W, const uint16_t *S, const uint16_t *x, uint16_t *y,
+                          int64_t N, int64_t K, int64_t ny)
+{
+    q4_status st = check_matrix(W, S, N, K);
+    if (st != Q4_OK)
+        return st;
+    if (!x || !y)
+        return fail(Q4_EINVAL, "NULL activation or output pointer");
+    if (!aligned(x, 16))
+        return fail(Q4_EALIGN, "the activation vector must be 16-byte aligned");
+    if (!aligned(y, 2))
+        return fail(Q4_EALIGN, "the output must be 2-byte aligned");
+    const size_t yb = (size_t)ny * 2;
+    if (overlaps(y, yb, W, wbytes(N, K)) || overlaps(y, yb, S, sbytes(N, K)) ||
+        overlaps(y, yb, x, (size_t)K * 2))
+        return fail(Q4_EALIAS, "the output overlaps an input");
+    return Q4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *q4_version(void) { return "libq4 0.1 (gfx950)"; }
+
+const char *q4_last_error(void) { return g_err; }
+
+double q4_bytes_per_weight(void) { return 4.0 / 8.0 + 2.0 / 32.0; }
+
+q4_status q4_pack(const uint8_t *codes, uint32_t *packed, int64_t N, int64_t K, q4_stream stream)
+{
+    if (!codes || !packed)
+        return fail(Q4_EINVAL, "NULL pointer");
+    if (N <= 0 || K <= 0)
+        return fail(Q4_EINVAL, "non-positive shape");
+    if (K % 32)
+        return fail(Q4_ESHAPE, "K=%lld is not a multiple of 32", (long long)K);
+    if (!aligned(packed, 16))
+        return fail(Q4_EALIGN, "packed weights must be 16-byte aligned");
+    if (overlaps(codes, (size_t)N * K, packed, wbytes(N, K)))
+        return fail(Q4_EALIAS, "codes and packed words overlap");
+    return launch_pack(codes, packed, N * K / 8, as_stream(stream));
+}
+
+q4_status q4_unpack(const uint32_t *packed, uint8_t *codes, int64_t N, int64_t K, q4_stream stream)
+{
+    if (!codes || !packed)
+        return fail(Q4_EINVAL, "NULL pointer");
+    if (N <= 0 || K <= 0)
+        return fail(Q4_EINVAL, "non-positive shape");
+    if (K % 32)
+        return fail(Q4_ESHAPE, "K=%lld is not a multiple of 32", (long long)K);
+    if (!aligned(packed, 4))
+        return fail(Q4_EALIGN, "packed weights must be 4-byte aligned");
+    if (overlaps(codes, (size_t)N * K, packed, wbytes(N, K)))
+        return fail(Q4_EALIAS, "codes and packed words overlap");
+    return launch_unpack(packed, codes, N * K / 8, as_stream(stream));
+}
+
+q4_status q4_gemv(const uint32_t *W, const uint16_t *S, const uint16_t *x, uint16_t *y, int64_t N,
+                  int64_t K, q4_stream stream)
+{
+    q4_status st = check_gemv_args(W, S, x, y, N, K, N);
+    if (st != Q4_OK)
+        return st;
+    return launch_gemv(W, S, x, y, (int)N, (int)K, EpiArgs{}, as_stream(stream));
+}
+
+q4_status q4_gemv_ex(const uint32_t *W, const uint16_t *S, const uint16_t *x, uint16_t *y,
+                     int64_t N, int64_t K, const q4_epilogue *epi, q4_stream stream)
+{
+    EpiArgs e;
+    if (epi) {
+        e.kind = epi->kind;
+        e.norm_gamma = epi->norm_gamma;
+        e.eps = epi->eps;
+    }
+    if (e.norm_gamma) {
+        if (e.kind == Q4_EPI_ADD_RMSNORM)
+            return fail(Q4_EINVAL, "a normalising prologue is not combined with add+RMSNorm");
+        if (!aligned(e.norm_gamma, 16))
+            return fail(Q4_EALIGN, "norm_gamma must be 16-byte aligned");
+        if (!(e.eps >= 0.f))
+            return fail(Q4_EINVAL, "eps must be non-negative");
+    }
+    if (e.kind != Q4_EPI_NONE && e.kind != Q4_EPI_SILU_MUL && e.kind != Q4_EPI_ADD_RMSNORM)
+        return fail(Q4_EINVAL, "unknown epilogue kind %d", e.kind);
+    if (e.kind == Q4_EPI_SILU_MUL && (N % 2))
+        return fail(Q4_ESHAPE, "SiLU-multiply needs an even row count, N=%lld", (long long)N);
+    const int64_t ny = e.kind == Q4_EPI_SILU_MUL ? N / 2 : N;
+    q4_status st = check_gemv_args(W, S, x, y, N, K, ny);
+    if (st != Q4_OK)
+        return st;
+    if (e.kind == Q4_EPI_ADD_RMSNORM) {
+        e.res_in = epi->res_in;
+        e.gamma = epi->gamma;
+        e.res_out = epi->res_out;
+        e.eps = epi->eps;
+        if (!e.res_in || !e.gamma || !e.res_out)
+            return fail(Q4_EINVAL, "add+RMSNorm epilogue needs res_in, gamma and res_out");
+        if (N > Q4_MAX_K)
+            return fail(Q4_ERANGE, "add+RMSNorm epilogue over N=%lld > Q4_MAX_K rows",
+                        (long long)N);
+        if (!aligned(e.res_in, 2) || !aligned(e.gamma, 2) || !aligned(e.res_out, 2))
+            return fail(Q4_EALIGN, "epilogue vectors must be 2-byte aligned");
+        const size_t vb = (size_t)N * 2;
+        if (overlaps(e.res_out, vb, e.res_in, vb))
+            return fail(Q4_EALIAS, "res_out overlaps res_in (use two residual buffers)");
+        if (overlaps(e.res_out, vb, y, vb) || overlaps(y, vb, e.res_in, vb) ||
+            overlaps(y, vb, e.gamma, vb) || overlaps(e.res_out, vb, e.gamma, vb) ||
+            overlaps(e.res_out, vb, x, (size_t)K * 2) || overlaps(e.res_out, vb, W, wbytes(N, K)) ||
+            overlaps(e.res_out, vb, S, sbytes(N, K)))
+            return fail(Q4_EALIAS, "an epilogue output overlaps an input or another output");
+        if (!(e.eps >= 0.f))
+            return fail(Q4_EINVAL, "eps must be non-negative");
+    }
+    return launch_gemv(W, S, x, y, (int)N, (int)K, e, as_stream(stream));
+}
+
+q4_status q4_gemv_batched(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
+                          uint16_t *y, int64_t ldy, int64_t N, int64_t K, int64_t M,
+                          q4_stream stream)
+{
+    q4_status st = check_matrix(W, S, N, K);
+    if (st != Q4_OK)
+        return st;
+    if (!x || !y)
+        return fail(Q4_EINVAL, "NULL activation or output pointer");
+    if (M < 1 || M > Q4_MAX_M)
+        return fail(Q4_ERANGE, "M=%lld outside [1, %d]", (long long)M, Q4_MAX_M);
+    if (ldx < K || ldy < N)
+        return fail(Q4_EINVAL, "leading dimensions too small (ldx=%lld, ldy=%lld)",
+                    (long long)ldx, (long long)ldy);
+    if (!aligned(x, 16) || ldx % 8)
+        return fail(Q4_EALIGN, "activation rows must be 16-byte aligned (ldx %% 8 == 0)");
+    if (!aligned(y, 2))
+        return fail(Q4_EALIGN, "the output must be 2-byte aligned");
+    const size_t yb = ((size_t)(M - 1) * ldy + N) * 2, xb = ((size_t)(M - 1) * ldx + K) * 2;
+    if (overlaps(y, yb, W, wbytes(N, K)) || overlaps(y, yb, S, sbytes(N, K)) ||
+        overlaps(y, yb, x, xb))
+        return fail(Q4_EALIAS, "the output overlaps an input");
+    return launch_gemv_batched(W, S, x, ldx, y, ldy, (int)N, (int)K, (int)M, as_stream(stream));
+}
+
+q4_status q4_moe_gemv(const uint32_t *W, const uint16_t *S, const int32_t *ids,
+                      const uint16_t *route_w, const uint16_t *x, int64_t ldx,
+                      int64_t x_slot_stride, uint16_t *y, int64_t E, int64_t N, int64_t K,
+                      int64_t T, int64_t TOPK, int epi_silu, q4_stream stream)
+{
+    if (E <= 0 || T <= 0 || TOPK <= 0)
+        return fail(Q4_EINVAL, "non-positive E, T or TOPK");
+    q4_status st = check_matrix(W, S, N, K);
+    if (st != Q4_OK)
+        return st;
+    if (!ids || !x || !y)
+        return fail(Q4_EINVAL, "NULL ids, activation or output pointer");
+    if (epi_silu && route_w)
+        return fail(Q4_EINVAL, "the SiLU epilogue and the routing combine are separate stages");
+    if (epi_silu && (N % 2))
+        return fail(Q4_ESHAPE, "SiLU-multiply needs an even row count, N=%lld", (long long)N);
+    if (T * TOPK > Q4_MAX_PAIRS)
+        return fail(Q4_ERANGE, "T*TOPK=%lld exceeds Q4_MAX_PAIRS=%d", (long long)(T * TOPK),
+                    Q4_MAX_PAIRS);
+    if ((int64_t)E * N > (1ll << 31))
+        return fail(Q4_ERANGE, "E*N is too large");
+    if (x_slot_stride < 0 || ldx < 0)
+        return fail(Q4_EINVAL, "negative stride");
+    if (!aligned(x, 16) || ldx % 8 || x_slot_stride % 8)
+        return fail(Q4_EALIGN, "activation rows must be 16-byte aligned (strides %% 8 == 0)");
+    if (!aligned(ids, 4) || (route_w && !aligned(route_w, 2)) || !aligned(y, 2))
+        return fail(Q4_EALIGN, "misaligned ids, routing weights or output");
+    const int64_t P = T * TOPK;
+    const size_t yb = (route_w ? (size_t)T * N : (size_t)P * (epi_silu ? N / 2 : N)) * 2;
+    const size_t xb = ((size_t)(T - 1) * ldx + (size_t)(TOPK - 1) * x_slot_stride + K) * 2;
+    if (overlaps(y, yb, W, wbytes(E * N, K)) || overlaps(y, yb, S, sbytes(E * N, K)) ||
+        overlaps(y, yb, x, xb) || overlaps(y, yb, ids, (size_t)P * 4) ||
+        (route_w && overlaps(y, yb, route_w, (size_t)P * 2)))
+        return fail(Q4_EALIAS, "the output overlaps an input");
+    return launch_moe(W, S, ids, route_w, x, ldx, x_slot_stride, y, (int)E, (int)N, (int)K, (int)T,
+                      (int)TOPK, epi_silu, as_stream(stream));
+}
+
+q4_status q4_add_rmsnorm(const uint16_t *a, const uint16_t *res_in, const uint16_t *gamma,
+                         uint16_t *out, uint16_t *res_out, int64_t D, int64_t M, float eps,
+                         q4_stream stream)
+{
+    if (!res_in || !gamma || !out || !res_out)
+        return fail(Q4_EINVAL, "NULL pointer");
+    if (D <= 0 || M <= 0)
+        return fail(Q4_EINVAL, "non-positive shape");
+    if (D > Q4_MAX_K || M > (1 << 20))
+        return fail(Q4_ERANGE, "D=%lld or M=%lld too large", (long long)D, (long long)M);
+    if (!(eps >= 0.f))
+        return fail(Q4_EINVAL, "eps must be non-negative");
+    if ((a && !aligned(a, 2)) || !aligned(res_in, 2) || !aligned(gamma, 2) || !aligned(out, 2) ||
+        !aligned(res_out, 2))
+        return fail(Q4_EALIGN, "binary16 vectors must be 2-byte aligned");
+    const size_t b = (size_t)D * M * 2;
+    if (overlaps(res_out, b, res_in, b))
+        return fail(Q4_EALIAS, "res_out overlaps res_in (use two residual buffers)");
+    if (overlaps(out, b, res_in, b) || overlaps(out, b, res_out, b) || overlaps(out, b, a, b) ||
+        overlaps(res_out, b, a, b) || overlaps(out, b, gamma, (size_t)D * 2) ||
+        overlaps(res_out, b, gamma, (size_t)D * 2))
+        return fail(Q4_EALIAS, "an output overlaps an input or the other output");
+    return launch_add_rmsnorm(a, res_in, gamma, out, res_out, (int)D, (int)M, eps,
+                              as_stream(stream));
+}
+
+q4_status q4_silu_mul(const uint16_t *gu, uint16_t *out, int64_t F, int64_t M, q4_stream stream)
+{
+    if (!gu || !out)
+        return fail(Q4_EINVAL, "NULL pointer");
+    if (F <= 0 || M <= 0)
+        return fail(Q4_EINVAL, "non-positive shape");
+    if (F * M > (1ll << 31))
+        return fail(Q4_ERANGE, "F*M too large");
+    if (!aligned(gu, 2) || !aligned(out, 2))
+        return fail(Q4_EALIGN, "binary16 vectors must be 2-byte aligned");
+    if (overlaps(out, (size_t)F * M * 2, gu, (size_t)F * M * 4))
+        return fail(Q4_EALIAS, "the output overlaps the input");
+    return launch_silu_mul(gu, out, (int)F, (int)M, as_stream(stream));
+}
+
+q4_status q4_stack_decode(const q4_stack_desc *d, const uint16_t *r_in, const uint16_t *h_in,
+                          uint16_t *r_out, uint16_t *h_out, uint16_t *trace, q4_stream stream)
+{
+    if (!d)
+        return fail(Q4_EINVAL, "NULL descriptor");
+    if (d->n_layers <= 0 || d->d <= 0 || d->f <= 0 || d->n_qkv <= 0 || d->dv <= 0 || d->v_off < 0)
+        return fail(Q4_EINVAL, "non-positive stack dimension");
+    if (d->v_off + d->dv > d->n_qkv)
+        return fail(Q4_ESHAPE, "V slice [%lld, %lld) outside the QKV rows", (long long)d->v_off,
+                    (long long)(d->v_off + d->dv));
+    if (d->v_off % 8)
+        return fail(Q4_EALIGN, "v_off must be a multiple of 8 (16-byte aligned slice)");
+    if (!d->Wqkv || !d->Sqkv || !d->Wo || !d->So || !d->Wgu || !d->Sgu || !d->Wdn || !d->Sdn ||
+        !d->gamma_in || !d->gamma_post || !d->gamma_final)
+        return fail(Q4_EINVAL, "NULL pointer in the stack descriptor");
+    if (!r_in || !h_in || !r_out || !h_out)
+        return fail(Q4_EINVAL, "NULL state pointer");
+    if (!(d->eps >= 0.f))
+        return fail(Q4_EINVAL, "eps must be non-negative");
+    const int64_t D = d->d, F = d->f;
+    if (!aligned(h_in, 16) || !aligned(r_in, 2) || !aligned(r_out, 2) || !aligned(h_out, 2) ||
+        (trace && !aligned(trace, 2)))
+        return fail(Q4_EALIGN, "h_in must be 16-byte aligned, other state vectors 2-byte");
+    if (!aligned(d->gamma_in, 16) || !aligned(d->gamma_post, 16) || !aligned(d->gamma_final, 2))
+        return fail(Q4_EALIGN, "gamma_in / gamma_post must be 16-byte aligned");
+    const size_t vb = (size_t)D * 2;
+    const void *ins[2] = {r_in, h_in};
+    const void *outs[2] = {r_out, h_out};
+    for (const void *o : outs) {
+        for (const void *i : ins)
+            if (overlaps(o, vb, i, vb))
+                return fail(Q4_EALIAS, "stack outputs overlap its inputs");
+        if (trace && overlaps(o, vb, trace, (size_t)d->n_layers * 2 * vb))
+            return fail(Q4_EALIAS, "stack outputs overlap the trace");
+    }
+    if (overlaps(r_out, vb, h_out, vb))
+        return fail(Q4_EALIAS, "r_out overlaps h_out");
+    for (int64_t L = 0; L < d->n_layers; ++L) {
+        q4_status st;
+        if ((st = check_matrix(d->Wqkv[L], d->Sqkv[L], d->n_qkv, D)) != Q4_OK ||
+            (st = check_matrix(d->Wo[L], d->So[L], D, d->dv)) != Q4_OK ||
+            (st = check_matrix(d->Wgu[L], d->Sgu[L], 2 * F, D)) != Q4_OK ||
+            (st = check_matrix(d->Wdn[L], d->Sdn[L], D, F)) != Q4_OK)
+            return st;
+    }
+
+    // Per layer four matvecs and no synchronisation between workgroups: the
+    // residual add happens row by row in the O / down epilogues, and the
+    // RMSNorm that follows it is recomputed by every workgroup of the next
+    // matvec while it stages its activation (bit-identical to q4_add_rmsnorm).
+    // workspace: header | qkv | r1 | u | rA | rB   (256-byte aligned pieces)
+    auto al = [](size_t b) { return (b + 255) / 256 * 256; };
+    const size_t q_b = al((size_t)d->n_qkv * 2), v_b = al(vb), u_b = al((size_t)F * 2);
+    const size_t total = kWsHeader + q_b + 3 * v_b + u_b;
+    hipStream_t st = as_stream(stream);
+    char *ws = static_cast<char *>(workspace(st, total));
+    if (!ws)
+        return Q4_EHIP;
+    uint16_t *qkv = reinterpret_cast<uint16_t *>(ws + kWsHeader);
+    char *p = ws + kWsHeader + q_b;
+    uint16_t *r1 = reinterpret_cast<uint16_t *>(p);
+    uint16_t *u = reinterpret_cast<uint16_t *>(p + v_b);
+    uint16_t *rp[2] = {reinterpret_cast<uint16_t *>(p + v_b + u_b),
+                       reinterpret_cast<uint16_t *>(p + 2 * v_b + u_b)};
+
+    const uint16_t *rc = r_in;
+    for (int64_t L = 0; L < d->n_layers; ++L) {
+        const bool last = L + 1 == d->n_layers;
+        uint16_t *r2 = last ? r_out : rp[L & 1];
+        const uint16_t *g_next = last ? d->gamma_final : d->gamma_in + (L + 1) * D;
+        q4_status s;
+        GemvOp qk;
+        qk.W = d->Wqkv[L];
+        qk.S = d->Sqkv[L];
+        qk.N = (int)d->n_qkv;
+        qk.K = (int)D;
+        if (L == 0) {
+            qk.x = h_in;
+        } else {  // h = RMSNorm(r) * gamma_in[L], recomputed in the prologue
+            qk.norm_src = rc;
+            qk.norm_gamma = d->gamma_in + L * D;
+            qk.norm_eps = d->eps;
+        }
+        qk.epi = GemvOp::NONE;
+        qk.y = qkv;
+        if ((s = launch_gemv_op(qk, st)) != Q4_OK)
+            return s;
+        GemvOp o;
+        o.W = d->Wo[L];
+        o.S = d->So[L];
+        o.N = (int)D;
+        o.K = (int)d->dv;
+        o.x = qkv + d->v_off;
+        o.epi = GemvOp::RESID;
+        o.res_in = rc;
+        o.res_out = r1;
+        if ((s = launch_gemv_op(o, st)) != Q4_OK)
+            return s;
+        GemvOp gu;
+        gu.W = d->Wgu[L];
+        gu.S = d->Sgu[L];
+        gu.N = (int)(2 * F);
+        gu.K = (int)D;
+        gu.norm_src = r1;
+        gu.norm_gamma = d->gamma_post + L * D;
+        gu.norm_eps = d->eps;
+        gu.epi = GemvOp::SILU;
+        gu.y = u;
+        if ((s = launch_gemv_op(gu, st)) != Q4_OK)
+            return s;
+        GemvOp dn;
+        dn.W = d->Wdn[L];
+        dn.S = d->Sdn[L];
+        dn.N = (int)D;
+        dn.K = (int)F;
+        dn.x = u;
+        dn.epi = GemvOp::RESID;
+        dn.res_in = r1;
+        dn.res_out = r2;
+        if ((s = launch_gemv_op(dn, st)) != Q4_OK)
+            return s;
+        if (trace) {
+            uint16_t *tr = trace + (2 * L) * D;
+            Q4_HIP(hipMemcpyAsync(tr, r2, vb, hipMemcpyDeviceToDevice, st));
+            if ((s = launch_add_rmsnorm(nullptr, r2, g_next, tr + D, nullptr, (int)D, 1, d->eps,
+                                        st)) != Q4_OK)
+                return s;
+        }
+        rc = r2;
+    }
+    return launch_add_rmsnorm(nullptr, r_out, d->gamma_final, h_out, nullptr, (int)D, 1, d->eps,
+                              st);
+}
+
+}  // extern "C"

@@ -1,0 +1,149 @@
+// Internal helpers of libq4 (gfx950). Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "q4.h"
+
+namespace q4 {
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+
+// Records a message for q4_last_error() on this thread and returns st.
+q4_status fail(q4_status st, const char *fmt, ...);
+
+// Wraps a HIP call made by an entry point.
+#define Q4_HIP(call)                                                                      \
+    do {                                                                                  \
+        hipError_t e_ = (call);                                                           \
+        if (e_ != hipSuccess)                                                             \
+            return ::q4::fail(Q4_EHIP, "%s failed: %s", #call, hipGetErrorString(e_));    \
+    } while (0)
+
+// Launch check: hipGetLastError after a kernel launch.
+q4_status check_launch(const char *what);
+
+// Library-owned scratch for one (device, stream): at least `bytes` bytes. Its
+// first kWsHeader bytes are reserved (zero-initialised counters); callers place
+// their own data after them. Returns nullptr (and sets the error) on failure.
+constexpr size_t kCounterBytes = 256;
+constexpr size_t kWsHeader = kCounterBytes;
+void *workspace(hipStream_t stream, size_t bytes);
+
+inline bool overlaps(const void *a, size_t an, const void *b, size_t bn)
+{
+    if (!a || !b || an == 0 || bn == 0)
+        return false;
+    auto pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + bn && pb < pa + an;
+}
+
+inline bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Kernel launchers shared between entry points (defined in q4_gemv.hip etc.).
+struct EpiArgs {
+    int kind = Q4_EPI_NONE;
+    const uint16_t *res_in = nullptr;
+    const uint16_t *gamma = nullptr;
+    uint16_t *res_out = nullptr;
+    float eps = 0.f;
+    const uint16_t *norm_gamma = nullptr;  // prologue: normalise x first
+};
+
+q4_status launch_gemv(const uint32_t *W, const uint16_t *S, const uint16_t *x, uint16_t *y,
+                      int N, int K, const EpiArgs &epi, hipStream_t stream);
+
+// One matvec with an optional RMSNorm prologue and a per-row epilogue; no
+// synchronisation between workgroups is ever needed.
+//   prologue: x (16-byte aligned), or, when norm_src is set, the activation
+//             f16(RMSNorm(norm_src) * norm_gamma) (both length K, 16-byte
+//             aligned), computed by every workgroup with the canonical
+//             summation order of q4_add_rmsnorm (bit-identical to it)
+//   epilogue: NONE  y[n] = f16(acc)
+//             SILU  y[i] = f16(silu(f16(acc_i)) * f16(acc_{N/2+i}))
+//             RESID res_out[n] = f16(f16(acc) + res_in[n])
+struct GemvOp {
+    enum { NONE = 0, SILU = 1, RESID = 2 };
+    const uint32_t *W = nullptr;
+    const uint16_t *S = nullptr;
+    int N = 0, K = 0;
+    const uint16_t *x = nullptr;
+    const uint16_t *norm_src = nullptr;
+    const uint16_t *norm_gamma = nullptr;
+    float norm_eps = 0.f;
+    int epi = NONE;
+    uint16_t *y = nullptr;
+    const uint16_t *res_in = nullptr;
+    uint16_t *res_out = nullptr;
+};
+q4_status launch_gemv_op(const GemvOp &op, hipStream_t stream);
+q4_status launch_gemv_batched(const uint32_t *W, const uint16_t *S, const uint16_t *x,
+                              int64_t ldx, uint16_t *y, int64_t ldy, int N, int K, int M,
+                              hipStream_t stream);
+q4_status launch_add_rmsnorm(const uint16_t *a, const uint16_t *res_in, const uint16_t *gamma,
+                             uint16_t *out, uint16_t *res_out, int D, int M, float eps,
+                             hipStream_t stream);
+q4_status launch_silu_mul(const uint16_t *gu, uint16_t *out, int F, int M, hipStream_t stream);
+q4_status launch_pack(const uint8_t *codes, uint32_t *packed, int64_t words, hipStream_t stream);
+q4_status launch_unpack(const uint32_t *packed, uint8_t *codes, int64_t words, hipStream_t stream);
+q4_status launch_moe(const uint32_t *W, const uint16_t *S, const int32_t *ids,
+                     const uint16_t *route_w, const uint16_t *x, int64_t ldx,
+                     int64_t x_slot_stride, uint16_t *y, int E, int N, int K, int T, int TOPK,
+                     int epi_silu, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Device side
+// ---------------------------------------------------------------------------
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+// Round an f32 value to binary16, nearest even (the default mode of
+// v_cvt_f16_f32). The empty asm makes the f32 value opaque, so the compiler
+// cannot fuse a preceding multiply into a single-rounding v_fma_mix*_f16 in
+// some kernels and not in others: every path rounds the same f32 value.
+__device__ __forceinline__ uint16_t f2h(float f)
+{
+    asm volatile("" : "+v"(f));
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+__device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+
+// silu(g) * u in f32, g and u already binary16 values. One definition for every
+// kernel, so fused and unfused paths give identical bits.
+__device__ __forceinline__ float silu_mul_f(float g, float u)
+{
+    float s = g / (1.0f + __expf(-g));
+    return s * u;
+}
+
+// Canonical order of an RMSNorm's sum of squares over a row of D values:
+// thread t visits the 8-element chunks c = t, t + 256, ... ([8c, 8c + 8) cut at
+// D), elements in order, ss = fmaf(v, v, ss); then block_sum_256. Every kernel
+// that normalises (standalone or as a matvec prologue) follows it, so their
+// results are bit-identical.
+
+// Block-wide sum over 256 threads in a fixed order: xor-butterfly inside each
+// wave, then the four wave totals added in wave order. `red` is 4 floats of LDS.
+__device__ __forceinline__ float block_sum_256(float v, float *red)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        v += __shfl_xor(v, off, 64);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0)
+        red[wave] = v;
+    __syncthreads();
+    float t = ((red[0] + red[1]) + red[2]) + red[3];
+    __syncthreads();
+    return t;
+}
+
+}  // namespace q4

@@ -1,0 +1,104 @@
+// Device routines shared by the int4 matvec kernels of libq4 (gfx950).
+//
+// Format (Zero TVM Documentation, "Q4F16 quantization format"): eight 4-bit
+// codes per uint32, element i of a word in bits 4i..4i+3, one binary16 scale
+// per 32-element group, value (code - 7) * scale.
+//
+// Unpack without conversions (see group_dot): codes are masked straight into
+// subnormal binary16 pairs that v_dot2_f32_f16 multiplies exactly. The
+// activation is staged with each 8-element chunk stored as the pairs (x0,x4)
+// (x1,x5) (x2,x6) (x3,x7), which line up with the masks, and with 7 * (group
+// sum) beside it.
+#pragma once
+
+#include "q4_common.h"
+
+namespace q4 {
+
+// Sum over one group (four words, 32 codes) of (c - 7) * x.
+//
+// A code c kept in mantissa bits 0..3 of a binary16 whose exponent field is
+// zero is the exact subnormal c * 2^-24; kept in bits 4..7 it is c * 2^-20. So
+// for a word w, (w & 0x000F000F) holds the codes of elements 0 and 4 as such a
+// pair, (w & 0x00F000F0) those of 1 and 5, and the same masks on w >> 8 those
+// of 2, 6 and 3, 7: one shift and four ANDs per word, no conversion. The
+// activation chunk is staged as the matching pairs (x0,x4) (x1,x5) (x2,x6)
+// (x3,x7). v_dot2_f32_f16 multiplies exactly (f16 denormals are kept) and
+// accumulates in f32; lo gathers the 2^-24-scaled pairs, hi the 2^-20-scaled
+// ones, and sum (c - 7) x = 2^24 lo + 2^20 hi - 7 sum(x), with c7 = 7 sum(x)
+// staged beside the activation. A one-hot x therefore gives (c - 7) exactly.
+__device__ __forceinline__ float group_dot(uint4 wv, const uint4 *xp, float c7)
+{
+    const uint32_t m0 = 0x000F000Fu, m1 = 0x00F000F0u;
+    float lo = 0.f, hi = 0.f;
+    const uint32_t w[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint4 xq = xp[q];
+        const uint32_t t = w[q] >> 8;
+        lo = __builtin_amdgcn_fdot2(as_h2(w[q] & m0), as_h2(xq.x), lo, false);
+        hi = __builtin_amdgcn_fdot2(as_h2(w[q] & m1), as_h2(xq.y), hi, false);
+        lo = __builtin_amdgcn_fdot2(as_h2(t & m0), as_h2(xq.z), lo, false);
+        hi = __builtin_amdgcn_fdot2(as_h2(t & m1), as_h2(xq.w), hi, false);
+    }
+    return fmaf(0x1p24f, lo, fmaf(0x1p20f, hi, -c7));
+}
+
+// Stage x[K] (K % 32 == 0) into LDS: xs[K/8] pair-interleaved chunks and
+// cs[K/32] = 7 * group sums. Must be called by all 256 threads.
+__device__ __forceinline__ void stage_activation(const uint16_t *__restrict__ x, int K, uint4 *xs, float *cs)
+{
+    const int chunks = K >> 3;
+    for (int base = 0; base < chunks; base += 256) {
+        const int c = base + threadIdx.x;
+        float sum = 0.f;
+        if (c < chunks) {
+            const uint4 v = reinterpret_cast<const uint4 *>(x)[c];
+            uint4 p;
+            p.x = (v.x & 0xFFFFu) | (v.z << 16);
+            p.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
+            p.z = (v.y & 0xFFFFu) | (v.w << 16);
+            p.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
+            xs[c] = p;
+            sum = ((h2f(v.x & 0xFFFF) + h2f(v.x >> 16)) + (h2f(v.y & 0xFFFF) + h2f(v.y >> 16))) +
+                  ((h2f(v.z & 0xFFFF) + h2f(v.z >> 16)) + (h2f(v.w & 0xFFFF) + h2f(v.w >> 16)));
+        }
+        sum += __shfl_xor(sum, 1, 64);
+        sum += __shfl_xor(sum, 2, 64);
+        if (c < chunks && (c & 3) == 0)
+            cs[c >> 2] = 7.f * sum;
+    }
+}
+
+// The 8 binary16 values of a chunk, in order, as floats.
+__device__ __forceinline__ void chunk_to_float(uint4 v, float f[8])
+{
+    f[0] = h2f(v.x & 0xFFFF); f[1] = h2f(v.x >> 16);
+    f[2] = h2f(v.y & 0xFFFF); f[3] = h2f(v.y >> 16);
+    f[4] = h2f(v.z & 0xFFFF); f[5] = h2f(v.z >> 16);
+    f[6] = h2f(v.w & 0xFFFF); f[7] = h2f(v.w >> 16);
+}
+
+// Write one staged chunk (thread-held, chunk index c of a K-vector) into LDS in
+// the pair-interleaved order, and 7 * (group sum) for every 4th chunk. All
+// 256 threads must call it together (for every j), since it shuffles.
+__device__ __forceinline__ void put_chunk(uint4 v, int c, bool valid, uint4 *xs, float *cs)
+{
+    float sum = 0.f;
+    if (valid) {
+        uint4 p;
+        p.x = (v.x & 0xFFFFu) | (v.z << 16);
+        p.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
+        p.z = (v.y & 0xFFFFu) | (v.w << 16);
+        p.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
+        xs[c] = p;
+        sum = ((h2f(v.x & 0xFFFF) + h2f(v.x >> 16)) + (h2f(v.y & 0xFFFF) + h2f(v.y >> 16))) +
+              ((h2f(v.z & 0xFFFF) + h2f(v.z >> 16)) + (h2f(v.w & 0xFFFF) + h2f(v.w >> 16)));
+    }
+    sum += __shfl_xor(sum, 1, 64);
+    sum += __shfl_xor(sum, 2, 64);
+    if (valid && (c & 3) == 0)
+        cs[c >> 2] = 7.f * sum;
+}
+
+}  // namespace q4

@@ -1,0 +1,466 @@
+// Dequantising int4 x f16 matvec for gfx950 (single token, M = 1), with the
+// SiLU-multiply and add+RMSNorm epilogues.
+//
+// What is computed follows the Zero TVM Documentation ("Q4F16 quantization
+// format"; "WGSL Kernel Roles", shaders 5, 6 and 7): y[n] = sum_k (q - 7) * s * x.
+// How it is computed is designed for CDNA4 rather than taken from the pages'
+// WGSL:
+//  * One quantisation group (32 codes = four uint32 = 16 bytes) is one 128-bit
+//    load per lane. A row is spread over LPR consecutive lanes (a "segment"),
+//    lane j taking groups j, j + LPR, ...; one wave covers 64 / LPR rows, so a
+//    wave-wide load instruction reads LPR * 16 contiguous bytes of each row.
+//  * Every weight and scale load of a lane is issued before the activation is
+//    staged, so the whole tile is in flight at once.
+//  * The activation vector is staged once per workgroup in LDS, with each
+//    8-element chunk stored as the pairs (x0,x4) (x1,x5) (x2,x6) (x3,x7) that
+//    line up with the in-register nibble unpack, plus 7 * (group sum).
+//  * Nibble unpack without conversions (q4_dequant.h): codes are masked into
+//    exact subnormal binary16 pairs for v_dot2_f32_f16 (1 shift + 4 ANDs +
+//    4 dot2 per word), and the group's sum of (c - 7) x is applied with its
+//    scale in f32. A one-hot x therefore reproduces (c - 7) * s exactly.
+//  * The LPR partial sums of a row are combined with an xor butterfly in a
+//    fixed order, so results are identical run to run.
+#include "q4_dequant.h"
+
+namespace q4 {
+namespace {
+
+constexpr int kWaves = 4;  // 256 threads per workgroup
+
+enum { PRO_X = 0, PRO_NORM = 1 };
+enum { EPI_NONE_ = 0, EPI_SILU = 1, EPI_RESID = 2 };
+
+struct GemvParams {
+    const uint4 *W;     // [N][G] groups of 16 bytes
+    const uint16_t *S;  // [N][G]
+    int N, G;
+    // prologue: PRO_X reads x; PRO_NORM stages f16(RMSNorm(src) * gamma)
+    const uint16_t *x;  // [K], 16-byte aligned (PRO_X) or the residual (PRO_NORM)
+    const uint16_t *pro_gamma;
+    float pro_eps;
+    // epilogue
+    uint16_t *y;              // NONE: [N]; SILU: [N/2]
+    const uint16_t *res_in;   // RESID: res_out[n] = f16(f16(y[n]) + res_in[n])
+    uint16_t *res_out;
+};
+
+template <int LPR, int NG, int RPS, int EPI, int PRO>
+__global__ __launch_bounds__(256) void k_gemv(GemvParams a)
+{
+    constexpr int SPW = 64 / LPR;             // segments (rows) per wave
+    constexpr int RB = kWaves * SPW * RPS;    // rows per workgroup
+    constexpr int XCH = (LPR * NG + 63) / 64; // activation chunks (8 values) per thread
+    extern __shared__ uint4 smem[];
+    __shared__ float red[4];
+    __shared__ float vals[EPI == EPI_SILU ? RB : 1];
+
+    const int G = a.G;
+    const int K = G * 32;
+    const int chunks = K >> 3;
+    uint4 *xs = smem;
+    float *cs = reinterpret_cast<float *>(smem + chunks);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int seg = lane / LPR, j = lane % LPR;
+    const int half = a.N >> 1;
+
+    // 0. this thread's activation chunks (issued first: waiting for them must
+    //    not wait for the weight loads behind them)
+    uint4 xr[XCH];
+    uint4 gr[PRO == PRO_NORM ? XCH : 1];
+#pragma unroll
+    for (int q = 0; q < XCH; ++q) {
+        const int c = tid + 256 * q;
+        if (c < chunks) {
+            xr[q] = reinterpret_cast<const uint4 *>(a.x)[c];
+            if (PRO == PRO_NORM)
+                gr[q] = reinterpret_cast<const uint4 *>(a.pro_gamma)[c];
+        }
+    }
+
+    int row[RPS], li[RPS];
+    bool ok[RPS];
+#pragma unroll
+    for (int r = 0; r < RPS; ++r) {
+        li[r] = (wave * SPW + seg) * RPS + r;
+        int rr;
+        if (EPI == EPI_SILU) {
+            const int gi = blockIdx.x * (RB / 2) + (li[r] % (RB / 2));
+            ok[r] = gi < half;
+            rr = li[r] < RB / 2 ? gi : half + gi;
+        } else {
+            rr = blockIdx.x * RB + li[r];
+            ok[r] = rr < a.N;
+        }
+        row[r] = ok[r] ? rr : 0;
+    }
+
+    // 1. weight and scale loads, in the order they are consumed (group-major)
+    uint4 wv[NG][RPS];
+    uint16_t sv[NG][RPS];
+#pragma unroll
+    for (int i = 0; i < NG; ++i)
+#pragma unroll
+        for (int r = 0; r < RPS; ++r) {
+            const int g = j + LPR * i;
+            if (g < G) {
+                const size_t off = (size_t)row[r] * G + g;
+                wv[i][r] = a.W[off];
+                sv[i][r] = a.S[off];
+            } else {
+                wv[i][r] = make_uint4(0, 0, 0, 0);
+                sv[i][r] = 0;
+            }
+        }
+
+    // 2. activation into LDS (after an RMSNorm of the residual for PRO_NORM)
+    if (PRO == PRO_NORM) {
+        float ss = 0.f;
+#pragma unroll
+        for (int q = 0; q < XCH; ++q)
+            if (tid + 256 * q < chunks) {
+                float f[8];
+                chunk_to_float(xr[q], f);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    ss = fmaf(f[e], f[e], ss);
+            }
+        ss = block_sum_256(ss, red);
+        const float inv = 1.0f / sqrtf(ss / (float)K + a.pro_eps);
+#pragma unroll
+        for (int q = 0; q < XCH; ++q)
+            if (tid + 256 * q < chunks) {
+                float f[8], g8[8];
+                chunk_to_float(xr[q], f);
+                chunk_to_float(gr[q], g8);
+                uint32_t h[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    h[e] = f2h(f[e] * inv * g8[e]);
+                xr[q] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                                   h[6] | (h[7] << 16));
+            }
+    }
+#pragma unroll
+    for (int q = 0; q < XCH; ++q) {
+        const int c = tid + 256 * q;
+        put_chunk(xr[q], c, c < chunks, xs, cs);
+    }
+    __syncthreads();
+
+    // 3. dequantise and accumulate, in load order
+    float acc[RPS];
+#pragma unroll
+    for (int r = 0; r < RPS; ++r)
+        acc[r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+        const int g = j + LPR * i;
+        if (g < G) {
+            const uint4 *xp = xs + g * 4;
+            const float c7 = cs[g];
+#pragma unroll
+            for (int r = 0; r < RPS; ++r)
+                acc[r] = fmaf(h2f(sv[i][r]), group_dot(wv[i][r], xp, c7), acc[r]);
+        }
+    }
+
+    // 4. combine the LPR lanes of each row
+#pragma unroll
+    for (int r = 0; r < RPS; ++r)
+#pragma unroll
+        for (int off = LPR / 2; off > 0; off >>= 1)
+            acc[r] += __shfl_xor(acc[r], off, 64);
+
+    // 5. epilogue
+    if (EPI == EPI_NONE_) {
+        if (j == 0)
+#pragma unroll
+            for (int r = 0; r < RPS; ++r)
+                if (ok[r])
+                    a.y[row[r]] = f2h(acc[r]);
+    } else if (EPI == EPI_SILU) {
+        if (j == 0)
+#pragma unroll
+            for (int r = 0; r < RPS; ++r)
+                vals[li[r]] = h2f(f2h(acc[r]));  // as stored by an unfused matvec
+        __syncthreads();
+        if (tid < RB / 2) {
+            const int gi = blockIdx.x * (RB / 2) + tid;
+            if (gi < half)
+                a.y[gi] = f2h(silu_mul_f(vals[tid], vals[tid + RB / 2]));
+        }
+    } else {  // EPI_RESID: the residual add of an add+RMSNorm, row by row
+        if (j == 0)
+#pragma unroll
+            for (int r = 0; r < RPS; ++r)
+                if (ok[r]) {
+                    const float t = h2f(f2h(acc[r]));  // as stored by an unfused matvec
+                    a.res_out[row[r]] = f2h(t + h2f(a.res_in[row[r]]));
+                }
+    }
+}
+
+struct Cfg {
+    int lpr, ng;
+};
+
+int max_ng(int lpr) { return lpr == 64 ? 12 : 8; }
+
+Cfg choose_cfg(int G)
+{
+    Cfg best{0, 0};
+    int best_waste = 1 << 30;
+    for (int lpr : {64, 32, 16, 8}) {
+        const int ng = (G + lpr - 1) / lpr;
+        if (ng > max_ng(lpr))
+            continue;
+        const int waste = ng * lpr - G;
+        if (waste < best_waste) {
+            best_waste = waste;
+            best = {lpr, ng};
+        }
+    }
+    return best;
+}
+
+template <int LPR, int NG, int EPI, int PRO>
+q4_status run_gemv(const GemvParams &p, hipStream_t st)
+{
+    constexpr int RPS = NG <= 2 ? 4 : (NG <= 4 ? 2 : 1);
+    constexpr int RB = kWaves * (64 / LPR) * RPS;
+    const int rows = EPI == EPI_SILU ? p.N / 2 : p.N;
+    const int rb = EPI == EPI_SILU ? RB / 2 : RB;
+    const int blocks = (rows + rb - 1) / rb;
+    const size_t lds = (size_t)p.G * 32 * 2 + (size_t)p.G * 4;
+    hipLaunchKernelGGL((k_gemv<LPR, NG, RPS, EPI, PRO>), dim3(blocks), dim3(256), lds, st, p);
+    return check_launch("k_gemv");
+}
+
+template <int LPR, int EPI, int PRO>
+q4_status dispatch_ng(int ng, const GemvParams &p, hipStream_t st)
+{
+    switch (ng) {
+    case 1: return run_gemv<LPR, 1, EPI, PRO>(p, st);
+    case 2: return run_gemv<LPR, 2, EPI, PRO>(p, st);
+    case 3: return run_gemv<LPR, 3, EPI, PRO>(p, st);
+    case 4: return run_gemv<LPR, 4, EPI, PRO>(p, st);
+    case 5: return run_gemv<LPR, 5, EPI, PRO>(p, st);
+    case 6: return run_gemv<LPR, 6, EPI, PRO>(p, st);
+    case 7: return run_gemv<LPR, 7, EPI, PRO>(p, st);
+    case 8: return run_gemv<LPR, 8, EPI, PRO>(p, st);
+    default: break;
+    }
+    if constexpr (LPR == 64) {
+        switch (ng) {
+        case 9: return run_gemv<64, 9, EPI, PRO>(p, st);
+        case 10: return run_gemv<64, 10, EPI, PRO>(p, st);
+        case 11: return run_gemv<64, 11, EPI, PRO>(p, st);
+        case 12: return run_gemv<64, 12, EPI, PRO>(p, st);
+        default: break;
+        }
+    }
+    return fail(Q4_ERANGE, "no matvec configuration for %d groups per lane", ng);
+}
+
+template <int EPI, int PRO>
+q4_status dispatch_lpr(const Cfg &c, const GemvParams &p, hipStream_t st)
+{
+    switch (c.lpr) {
+    case 64: return dispatch_ng<64, EPI, PRO>(c.ng, p, st);
+    case 32: return dispatch_ng<32, EPI, PRO>(c.ng, p, st);
+    case 16: return dispatch_ng<16, EPI, PRO>(c.ng, p, st);
+    case 8: return dispatch_ng<8, EPI, PRO>(c.ng, p, st);
+    default: return fail(Q4_ERANGE, "no matvec configuration for K = %d", p.G * 32);
+    }
+}
+
+}  // namespace
+
+q4_status launch_gemv_op(const GemvOp &op, hipStream_t stream)
+{
+    GemvParams p{};
+    p.W = reinterpret_cast<const uint4 *>(op.W);
+    p.S = op.S;
+    p.N = op.N;
+    p.G = op.K / 32;
+    p.x = op.norm_src ? op.norm_src : op.x;
+    p.pro_gamma = op.norm_gamma;
+    p.pro_eps = op.norm_eps;
+    p.y = op.y;
+    p.res_in = op.res_in;
+    p.res_out = op.res_out;
+    const Cfg c = choose_cfg(p.G);
+    const bool norm = op.norm_src != nullptr;
+    switch (op.epi) {
+    case GemvOp::NONE:
+        return norm ? dispatch_lpr<EPI_NONE_, PRO_NORM>(c, p, stream)
+                    : dispatch_lpr<EPI_NONE_, PRO_X>(c, p, stream);
+    case GemvOp::SILU:
+        return norm ? dispatch_lpr<EPI_SILU, PRO_NORM>(c, p, stream)
+                    : dispatch_lpr<EPI_SILU, PRO_X>(c, p, stream);
+    case GemvOp::RESID:
+        if (norm)
+            return fail(Q4_EINVAL, "internal: normalising prologue with a residual epilogue");
+        return dispatch_lpr<EPI_RESID, PRO_X>(c, p, stream);
+    default:
+        return fail(Q4_EINVAL, "internal: unknown matvec epilogue %d", op.epi);
+    }
+}
+
+q4_status launch_gemv(const uint32_t *W, const uint16_t *S, const uint16_t *x, uint16_t *y,
+                      int N, int K, const EpiArgs &epi, hipStream_t stream)
+{
+    GemvOp op;
+    op.W = W;
+    op.S = S;
+    op.N = N;
+    op.K = K;
+    if (epi.norm_gamma) {
+        op.norm_src = x;
+        op.norm_gamma = epi.norm_gamma;
+        op.norm_eps = epi.eps;
+    } else {
+        op.x = x;
+    }
+    switch (epi.kind) {
+    case Q4_EPI_NONE:
+        op.epi = GemvOp::NONE;
+        op.y = y;
+        return launch_gemv_op(op, stream);
+    case Q4_EPI_SILU_MUL:
+        op.epi = GemvOp::SILU;
+        op.y = y;
+        return launch_gemv_op(op, stream);
+    case Q4_EPI_ADD_RMSNORM: {
+        // residual rows in the matvec's epilogue, then one workgroup normalises
+        // the stored row: no synchronisation between workgroups of a kernel
+        op.epi = GemvOp::RESID;
+        op.res_in = epi.res_in;
+        op.res_out = epi.res_out;
+        q4_status st = launch_gemv_op(op, stream);
+        if (st != Q4_OK)
+            return st;
+        return launch_add_rmsnorm(nullptr, epi.res_out, epi.gamma, y, nullptr, N, 1, epi.eps,
+                                  stream);
+    }
+    default:
+        return fail(Q4_EINVAL, "unknown epilogue kind %d", epi.kind);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Batched matvec (M activation rows share each weight load). First version:
+// VALU dot2 path; each wave owns one row, weights stay in registers for all
+// M rows, activations are staged in LDS MB rows at a time.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kBatchNG = 12;  // groups per lane (LPR = 64): K <= 24576
+
+template <int MB>
+__global__ __launch_bounds__(256) void k_gemv_batched(const uint4 *__restrict__ W,
+                                                      const uint16_t *__restrict__ S,
+                                                      const uint16_t *__restrict__ x, int64_t ldx,
+                                                      uint16_t *__restrict__ y, int64_t ldy, int N,
+                                                      int G, int M)
+{
+    extern __shared__ uint4 smem[];
+    const int K = G * 32;
+    const int stride = (K >> 3) + ((G + 3) >> 2);  // uint4 per staged row
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = blockIdx.x * kWaves + wave;
+    const bool ok = row < N;
+    const int rrow = ok ? row : 0;
+    const int ng = (G + 63) >> 6;
+
+    uint4 wv[kBatchNG];
+    float sv[kBatchNG];
+#pragma unroll
+    for (int i = 0; i < kBatchNG; ++i) {
+        const int g = lane + 64 * i;
+        if (i < ng && g < G) {
+            const size_t off = (size_t)rrow * G + g;
+            wv[i] = W[off];
+            sv[i] = h2f(S[off]);
+        } else {
+            wv[i] = make_uint4(0, 0, 0, 0);
+            sv[i] = 0.f;
+        }
+    }
+
+    for (int m0 = 0; m0 < M; m0 += MB) {
+        const int mb = min(MB, M - m0);
+        __syncthreads();
+        for (int m = 0; m < mb; ++m) {
+            uint4 *xs = smem + m * stride;
+            stage_activation(x + (int64_t)(m0 + m) * ldx, K, xs,
+                             reinterpret_cast<float *>(xs + (K >> 3)));
+        }
+        __syncthreads();
+        float acc[MB];
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+            acc[m] = 0.f;
+#pragma unroll
+        for (int i = 0; i < kBatchNG; ++i) {
+            const int g = lane + 64 * i;
+            if (i < ng && g < G) {
+#pragma unroll
+                for (int m = 0; m < MB; ++m) {
+                    if (m < mb) {
+                        const uint4 *xs = smem + m * stride;
+                        const float *cs = reinterpret_cast<const float *>(xs + (K >> 3));
+                        acc[m] = fmaf(sv[i], group_dot(wv[i], xs + g * 4, cs[g]), acc[m]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1)
+                acc[m] += __shfl_xor(acc[m], off, 64);
+            if (lane == 0 && ok && m < mb)
+                y[(int64_t)(m0 + m) * ldy + row] = f2h(acc[m]);
+        }
+    }
+}
+
+}  // namespace
+
+q4_status launch_gemv_batched(const uint32_t *W, const uint16_t *S, const uint16_t *x,
+                              int64_t ldx, uint16_t *y, int64_t ldy, int N, int K, int M,
+                              hipStream_t stream)
+{
+    const int G = K / 32;
+    const size_t row_bytes = ((size_t)(K >> 3) + (size_t)((G + 3) >> 2)) * 16;
+    const size_t budget = 60 * 1024;
+    int mb = 8;
+    while (mb > 1 && (size_t)mb * row_bytes > budget)
+        mb >>= 1;
+    const int blocks = (N + kWaves - 1) / kWaves;
+    const size_t lds = (size_t)mb * row_bytes;
+    const uint4 *W4 = reinterpret_cast<const uint4 *>(W);
+    switch (mb) {
+    case 8:
+        hipLaunchKernelGGL(k_gemv_batched<8>, dim3(blocks), dim3(256), lds, stream, W4, S, x, ldx,
+                           y, ldy, N, G, M);
+        break;
+    case 4:
+        hipLaunchKernelGGL(k_gemv_batched<4>, dim3(blocks), dim3(256), lds, stream, W4, S, x, ldx,
+                           y, ldy, N, G, M);
+        break;
+    case 2:
+        hipLaunchKernelGGL(k_gemv_batched<2>, dim3(blocks), dim3(256), lds, stream, W4, S, x, ldx,
+                           y, ldy, N, G, M);
+        break;
+    default:
+        hipLaunchKernelGGL(k_gemv_batched<1>, dim3(blocks), dim3(256), lds, stream, W4, S, x, ldx,
+                           y, ldy, N, G, M);
+        break;
+    }
+    return check_launch("k_gemv_batched");
+}
+
+}  // namespace q4

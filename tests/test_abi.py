@@ -1,0 +1,171 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+* libq4.so loads and exports every function declared in include/q4.h.
+* Argument validation returns the documented status before anything is
+  enqueued: these calls use fake (never dereferenced) pointer values.
+* The byte accounting of the format matches the pages' figures.
+"""
+import ctypes as C
+import json
+import os
+import re
+
+import pytest
+
+import int4_weight_only_q4_amd as q4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q4_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert declared_functions() == sorted(q4.ABI_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = q4.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert "gfx950" in q4.version()
+
+
+def test_bytes_per_weight():
+    assert q4.lib().q4_bytes_per_weight() == 0.5625 == q4.BYTES_PER_WEIGHT
+
+
+def test_per_token_bytes_match_bandwidth_ceiling_passage():
+    """Zero TVM Documentation, 'The memory-bandwidth ceiling': the q4 shape table
+    summed over 32 layers plus the LM head (and one embedding row) is ~2.09 GB
+    per token, ~5.2 ms at 400 GB/s, ~191 tok/s."""
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "phi3_q4f16_shapes.json")))
+    t = g["tensors"]
+
+    def tensor_bytes(name, rows=None):
+        n, words = t[name]["q_weight"]
+        k = words * 8
+        return (rows if rows is not None else n) * k * q4.BYTES_PER_WEIGHT
+
+    layer = sum(tensor_bytes(x) for x in ("qkv_proj", "o_proj", "gate_up", "down"))
+    total = g["layers"] * layer + tensor_bytes("lm_head") + tensor_bytes("embedding", rows=1)
+    assert abs(total / 1e9 - g["bytes_per_token_GB_approx"]) < 0.005
+    assert abs(total / (g["bus_GB_per_s"] * 1e9) * 1e3 - g["ms_per_token_approx"]) < 0.05
+    assert abs(g["bus_GB_per_s"] * 1e9 / total - g["tok_per_s_ceiling_approx"]) < 1.0
+    assert g["layers"] * layer == 2_038_431_744      # the 32-layer stack without LM head
+
+
+def test_density_matches_mlc_build():
+    """MLC-COMPILE.md: a q4f16_1 build reports 4.503 bits/param; the quantised
+    weights cost exactly 4.5 bits each, the rest being unquantised tensors."""
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "mlc_density.json")))
+    bits = q4.BYTES_PER_WEIGHT * 8
+    assert bits == 4.5 and 0 <= g["bits_per_param"] - bits < 0.01
+
+
+# ---------------------------------------------------------------------------
+# validation: fake device pointers, never dereferenced
+# ---------------------------------------------------------------------------
+A = 0x7F0000000000  # 16-byte aligned fake addresses, far apart
+B = A + 0x10000000
+X = A + 0x20000000
+Y = A + 0x30000000
+R = A + 0x40000000
+
+
+def status(fn, *args):
+    return getattr(q4.lib(), fn)(*args)
+
+
+def test_gemv_validation():
+    assert status("q4_gemv", None, B, X, Y, 16, 64, None) == q4.Q4_EINVAL
+    assert status("q4_gemv", A, B, X, Y, 0, 64, None) == q4.Q4_EINVAL
+    assert status("q4_gemv", A, B, X, Y, 16, 48, None) == q4.Q4_ESHAPE
+    assert status("q4_gemv", A, B, X, Y, 16, q4.MAX_K + 32, None) == q4.Q4_ERANGE
+    assert status("q4_gemv", A + 4, B, X, Y, 16, 64, None) == q4.Q4_EALIGN
+    assert status("q4_gemv", A, B, X + 2, Y, 16, 64, None) == q4.Q4_EALIGN
+    # output inside the weights / the activation
+    assert status("q4_gemv", A, B, X, A + 64, 16, 64, None) == q4.Q4_EALIAS
+    assert status("q4_gemv", A, B, X, X + 8, 16, 64, None) == q4.Q4_EALIAS
+    assert "overlaps" in q4.lib().q4_last_error().decode()
+
+
+def test_gemv_ex_validation():
+    ep = q4.Epilogue(7, None, None, None, 1e-5)
+    assert status("q4_gemv_ex", A, B, X, Y, 16, 64, C.byref(ep), None) == q4.Q4_EINVAL
+    ep = q4.Epilogue(q4.EPI_SILU_MUL, None, None, None, 1e-5)
+    assert status("q4_gemv_ex", A, B, X, Y, 15, 64, C.byref(ep), None) == q4.Q4_ESHAPE
+    ep = q4.Epilogue(q4.EPI_ADD_RMSNORM, R, None, R + 4096, 1e-5)
+    assert status("q4_gemv_ex", A, B, X, Y, 16, 64, C.byref(ep), None) == q4.Q4_EINVAL
+    # the ping-pong rule: res_out may not overlap res_in
+    ep = q4.Epilogue(q4.EPI_ADD_RMSNORM, R, R + 8192, R + 16, 1e-5)
+    assert status("q4_gemv_ex", A, B, X, Y, 16, 64, C.byref(ep), None) == q4.Q4_EALIAS
+    ep = q4.Epilogue(q4.EPI_ADD_RMSNORM, R, R + 8192, R + 4096, -1.0)
+    assert status("q4_gemv_ex", A, B, X, Y, 16, 64, C.byref(ep), None) == q4.Q4_EINVAL
+    # a normalising prologue: aligned gamma, not together with add+RMSNorm
+    ep = q4.Epilogue(q4.EPI_ADD_RMSNORM, R, R + 8192, R + 4096, 1e-5, R + 16384)
+    assert status("q4_gemv_ex", A, B, X, Y, 16, 64, C.byref(ep), None) == q4.Q4_EINVAL
+    ep = q4.Epilogue(q4.EPI_SILU_MUL, None, None, None, 1e-5, R + 2)
+    assert status("q4_gemv_ex", A, B, X, Y, 16, 64, C.byref(ep), None) == q4.Q4_EALIGN
+
+
+def test_batched_validation():
+    assert status("q4_gemv_batched", A, B, X, 64, Y, 16, 16, 64, 0, None) == q4.Q4_ERANGE
+    assert status("q4_gemv_batched", A, B, X, 64, Y, 16, 16, 64, q4.MAX_M + 1, None) == q4.Q4_ERANGE
+    assert status("q4_gemv_batched", A, B, X, 60, Y, 16, 16, 64, 2, None) == q4.Q4_EINVAL
+    assert status("q4_gemv_batched", A, B, X, 68, Y, 16, 16, 64, 2, None) == q4.Q4_EALIGN
+    assert status("q4_gemv_batched", A, B, X, 64, X + 64, 16, 16, 64, 2, None) == q4.Q4_EALIAS
+
+
+def test_moe_validation():
+    args = [A, B, R, None, X, 64, 0, Y, 8, 16, 64, 2, 4, 1, None]
+    bad = list(args); bad[3] = R + 4096   # SiLU epilogue together with a routing combine
+    assert status("q4_moe_gemv", *bad) == q4.Q4_EINVAL
+    bad = list(args); bad[9] = 15          # odd N with SiLU
+    assert status("q4_moe_gemv", *bad) == q4.Q4_ESHAPE
+    bad = list(args); bad[12] = 5000; bad[13] = 1   # too many (token, slot) pairs
+    assert status("q4_moe_gemv", *bad) == q4.Q4_ERANGE
+    bad = list(args); bad[6] = 4          # slot stride breaks 16-byte alignment
+    assert status("q4_moe_gemv", *bad) == q4.Q4_EALIGN
+    bad = list(args); bad[7] = R          # output over the ids
+    assert status("q4_moe_gemv", *bad) == q4.Q4_EALIAS
+
+
+def test_norm_and_silu_validation():
+    assert status("q4_add_rmsnorm", None, R, B, Y, R, 64, 1, 1e-5, None) == q4.Q4_EALIAS
+    assert status("q4_add_rmsnorm", None, R, None, Y, X, 64, 1, 1e-5, None) == q4.Q4_EINVAL
+    assert status("q4_add_rmsnorm", None, R, B, R + 64, X, 64, 1, 1e-5, None) == q4.Q4_EALIAS
+    assert status("q4_silu_mul", X, X + 64, 64, 1, None) == q4.Q4_EALIAS
+    assert status("q4_silu_mul", X, Y, 0, 1, None) == q4.Q4_EINVAL
+
+
+def test_stack_validation():
+    arr = (C.c_void_p * 1)(A)
+    sarr = (C.c_void_p * 1)(B)
+    ptr = C.cast(arr, C.c_void_p)
+    sptr = C.cast(sarr, C.c_void_p)
+    d = q4.StackDesc(1, 64, 64, 192, 128, 64, 1e-5, ptr, sptr, ptr, sptr, ptr, sptr, ptr, sptr,
+                     R, R + 4096, R + 8192)
+    st = q4.lib().q4_stack_decode
+    assert st(None, X, X + 4096, Y, Y + 4096, None, None) == q4.Q4_EINVAL
+    # outputs over inputs
+    assert st(C.byref(d), X, X + 4096, X, Y + 4096, None, None) == q4.Q4_EALIAS
+    d.v_off = 160
+    assert st(C.byref(d), X, X + 4096, Y, Y + 4096, None, None) == q4.Q4_ESHAPE
+    d.v_off = 124
+    d.dv = 64
+    assert st(C.byref(d), X, X + 4096, Y, Y + 4096, None, None) == q4.Q4_EALIGN
+    d.v_off = 128
+    d.d = 48
+    assert st(C.byref(d), X, X + 4096, Y, Y + 4096, None, None) == q4.Q4_ESHAPE
+
+
+def test_pack_validation():
+    assert status("q4_pack", None, A, 4, 64, None) == q4.Q4_EINVAL
+    assert status("q4_pack", X, A, 4, 40, None) == q4.Q4_ESHAPE
+    assert status("q4_pack", X, A + 4, 4, 64, None) == q4.Q4_EALIGN
+    assert status("q4_pack", X, X + 16, 4, 64, None) == q4.Q4_EALIAS

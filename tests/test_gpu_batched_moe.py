@@ -1,0 +1,181 @@
+"""GPU parity of q4_gemv_batched and q4_moe_gemv against the oracle.
+
+Batched: the Qwen3-4B matrices at batch 8 (8 independent activation rows),
+ragged and larger M, identical rows giving identical outputs.
+MoE: 128 experts with gate_up 1536 x 2048 and down 2048 x 768, top-8 routing at
+token batches 1, 4 and 16 (both stages, combined by routing weight), plus
+small cases with repeated experts and an out-of-range id.
+"""
+import numpy as np
+import pytest
+
+import datagen
+import oracle
+from gpu_common import assert_within, bits, dev_tensor, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def o():
+    return oracle.load()
+
+
+@pytest.fixture(scope="module")
+def q4():
+    import int4_weight_only_q4_amd as m
+    m.lib()
+    return m
+
+
+def sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+BATCHED = [
+    ("qwen3_qkv", 6144, 2560, 8),
+    ("qwen3_o", 2560, 4096, 8),
+    ("qwen3_gate_up", 19456, 2560, 8),
+    ("qwen3_down", 2560, 9728, 8),
+    ("phi3_o_m1", 3072, 3072, 1),
+    ("ragged_m13", 37, 96, 13),
+    ("m64", 300, 512, 64),
+    ("m3_kmax", 33, 24576, 3),
+]
+
+
+@pytest.mark.parametrize("name,n,k,m", BATCHED, ids=[b[0] for b in BATCHED])
+def test_batched_vs_oracle(o, q4, name, n, k, m):
+    seed = 900 + n + m
+    codes = datagen.codes(seed, n, k)
+    W, S = o.pack(codes), datagen.scales(seed + 1, n, k)
+    X = datagen.activations(seed + 2, m, k)
+    Y = q4.gemv_batched(dev_tensor(W), dev_tensor(S), dev_tensor(X))
+    sync()
+    assert_within(host(Y), o.gemv_batched(W, S, X), name)
+
+
+def test_batched_lm_head_sampled(o, q4):
+    n, k, m = 151936, 2560, 8
+    codes = datagen.codes(datagen.seed_for(4, 60), n, k)
+    W, S = o.pack(codes), datagen.scales(datagen.seed_for(4, 61), n, k)
+    X = datagen.activations(datagen.seed_for(4, 62), m, k)
+    Y = host(q4.gemv_batched(dev_tensor(W), dev_tensor(S), dev_tensor(X)))
+    sync()
+    rows = np.unique(np.random.default_rng(9).integers(0, n, 512))
+    for i in range(m):
+        assert_within(Y[i, rows], o.gemv_rows(W, S, X[i], rows), "lm head row %d" % i)
+
+
+def test_batched_identical_rows(o, q4):
+    n, k = 2560, 9728
+    codes = datagen.codes(71, n, k)
+    W, S = o.pack(codes), datagen.scales(72, n, k)
+    x = datagen.activations(73, 1, k)
+    X = np.repeat(x, 8, axis=0)
+    Y = q4.gemv_batched(dev_tensor(W), dev_tensor(S), dev_tensor(X))
+    sync()
+    b = bits(Y)
+    assert all(np.array_equal(b[0], b[i]) for i in range(8))
+
+
+def test_batched_strided_rows(o, q4):
+    import torch
+    n, k, m = 96, 256, 5
+    codes = datagen.codes(81, n, k)
+    W, S = o.pack(codes), datagen.scales(82, n, k)
+    X = datagen.activations(83, m, k)
+    big = torch.zeros((m, k + 64), dtype=torch.float16, device="cuda")
+    big[:, :k] = dev_tensor(X)
+    out = torch.full((m, n + 8), 7.0, dtype=torch.float16, device="cuda")
+    q4.gemv_batched(dev_tensor(W), dev_tensor(S), big[:, :k], y=out[:, :n])
+    sync()
+    h = host(out)
+    assert np.all(h[:, n:] == np.float16(7.0))
+    assert_within(h[:, :n], o.gemv_batched(W, S, X), "strided")
+
+
+# ---------------------------------------------------------------------------
+# MoE
+# ---------------------------------------------------------------------------
+
+def experts(o, seed, e, n, k):
+    W = np.empty((e, n, k // 8), np.uint32)
+    S = np.empty((e, n, k // 32), np.float16)
+    for i in range(e):
+        W[i] = o.pack(datagen.codes(seed + 2 * i, n, k))
+        S[i] = datagen.scales(seed + 2 * i + 1, n, k)
+    return W, S
+
+
+@pytest.fixture(scope="module")
+def moe128(o):
+    """128 experts: gate_up 1536 x 2048, down 2048 x 768 (hidden 2048, ffn 768)."""
+    Wg, Sg = experts(o, datagen.seed_for(5, 0), 128, 1536, 2048)
+    Wd, Sd = experts(o, datagen.seed_for(5, 1000), 128, 2048, 768)
+    return Wg, Sg, Wd, Sd, [dev_tensor(a) for a in (Wg, Sg, Wd, Sd)]
+
+
+@pytest.mark.parametrize("t", [1, 4, 16])
+def test_moe_layer_128_experts(o, q4, moe128, t):
+    Wg, Sg, Wd, Sd, (Wgd, Sgd, Wdd, Sdd) = moe128
+    topk, hidden, f = 8, 2048, 768
+    ids, rw = datagen.routing(datagen.seed_for(5, 2000 + t), t, 128, topk)
+    x = datagen.activations(datagen.seed_for(5, 3000 + t), t, hidden)
+    idsd, rwd, xd = dev_tensor(ids), dev_tensor(rw), dev_tensor(x)
+    u = q4.moe_gemv(Wgd, Sgd, idsd, xd, ldx=hidden, x_slot_stride=0, epi_silu=True)
+    y = q4.moe_gemv(Wdd, Sdd, idsd, u, ldx=topk * f, x_slot_stride=f, route_w=rwd)
+    sync()
+    u_ref = o.moe_stage(Wg, Sg, ids, None, x, hidden, 0, 2 * f, hidden, epi_silu=True)
+    assert_within(host(u), u_ref, "gate_up stage")
+    # the down stage is checked from the GPU's own stored u (teacher forcing)
+    uh = host(u)
+    y_ref = o.moe_stage(Wd, Sd, ids, rw, uh, topk * f, f, hidden, f, epi_silu=False)
+    assert_within(host(y), y_ref, "down stage + combine")
+
+
+def test_moe_per_slot_mode_and_repeated_experts(o, q4):
+    e, n, k, t, topk = 6, 96, 128, 5, 4
+    W, S = experts(o, 1234, e, n, k)
+    ids = np.array([[0, 1, 2, 3], [3, 2, 1, 0], [5, 5, 5, 5], [4, 0, 4, 0], [1, 1, 2, 2]],
+                   np.int32)
+    x = datagen.activations(1240, t * topk, k)
+    y = q4.moe_gemv(dev_tensor(W), dev_tensor(S), dev_tensor(ids), dev_tensor(x),
+                    ldx=topk * k, x_slot_stride=k)
+    sync()
+    ref = o.moe_stage(W, S, ids, None, x, topk * k, k, n, k, epi_silu=False)
+    assert_within(host(y), ref, "per-slot")
+
+
+def test_moe_out_of_range_id_contributes_zero(o, q4):
+    e, n, k, t, topk = 4, 64, 64, 2, 3
+    W, S = experts(o, 1300, e, n, k)
+    ids = np.array([[0, 7, 1], [-1, 2, 3]], np.int32)
+    rw = np.array([[0.5, 0.25, 0.25], [0.125, 0.5, 0.375]], np.float16)
+    x = datagen.activations(1301, t * topk, k)
+    y = q4.moe_gemv(dev_tensor(W), dev_tensor(S), dev_tensor(ids), dev_tensor(x),
+                    ldx=topk * k, x_slot_stride=k, route_w=dev_tensor(rw))
+    yp = q4.moe_gemv(dev_tensor(W), dev_tensor(S), dev_tensor(ids), dev_tensor(x),
+                     ldx=topk * k, x_slot_stride=k)
+    sync()
+    ok = np.where((ids >= 0) & (ids < e), ids, 0)
+    w_eff = np.where((ids >= 0) & (ids < e), rw, np.float16(0))
+    ref = o.moe_stage(W, S, ok.astype(np.int32), w_eff, x, topk * k, k, n, k, epi_silu=False)
+    assert_within(host(y), ref, "combine with invalid ids")
+    yp = host(yp)
+    assert np.all(yp[0, 1] == 0) and np.all(yp[1, 0] == 0)
+
+
+def test_moe_deterministic(o, q4, moe128):
+    _, _, _, _, (Wgd, Sgd, Wdd, Sdd) = moe128
+    ids, rw = datagen.routing(77, 16, 128, 8)
+    x = datagen.activations(78, 16, 2048)
+    idsd, rwd, xd = dev_tensor(ids), dev_tensor(rw), dev_tensor(x)
+    outs = []
+    for _ in range(2):
+        u = q4.moe_gemv(Wgd, Sgd, idsd, xd, ldx=2048, x_slot_stride=0, epi_silu=True)
+        y = q4.moe_gemv(Wdd, Sdd, idsd, u, ldx=8 * 768, x_slot_stride=768, route_w=rwd)
+        outs.append(bits(y))
+    sync()
+    assert np.array_equal(outs[0], outs[1])
