@@ -95,9 +95,9 @@ def time_dominant_kernel(q4, torch, stack, st, p, reps=3):
     """The gate_up matvec as the stack runs it (RMSNorm prologue, SiLU-multiply
     epilogue; the largest matrix of a layer), launched over the 32 layers'
     gate_up weights back to back (a 906 MB rotation), each launch bracketed by
-    HIP events on the stream it runs on. A device-side sleep queued first keeps
-    the stream busy while the launches are enqueued, so the events see the
-    kernels back to back rather than host launch latency."""
+    its own pair of HIP events on the stream it runs on. A device-side sleep
+    queued first keeps the stream busy while the launches are enqueued, so the
+    events see the kernels back to back rather than host launch latency."""
     d, f = p["d"], p["f"]
     x = st["r0"]
     gamma = st["gammas"][1][0]
@@ -105,15 +105,16 @@ def time_dominant_kernel(q4, torch, stack, st, p, reps=3):
     n = len(stack.layers)
     durs = []
     for _ in range(reps):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        e0 = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        e1 = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
         torch.cuda._sleep(20_000_000)
         for L in range(n):
-            ev[L].record()
+            e0[L].record()
             Wg, Sg = stack.layers[L][4], stack.layers[L][5]
             q4.gemv_ex(Wg, Sg, x, y=y, kind=q4.EPI_SILU_MUL, norm_gamma=gamma, eps=p["eps"])
-        ev[n].record()
+            e1[L].record()
         torch.cuda.synchronize()
-        durs += [ev[L].elapsed_time(ev[L + 1]) * 1e3 for L in range(n)]
+        durs += [e0[L].elapsed_time(e1[L]) * 1e3 for L in range(n)]
     us = float(np.mean(durs))
     bytes_per_launch = 2 * f * d * BPW
     return us, bytes_per_launch

@@ -203,6 +203,12 @@ q4_status q4_gemv_ex(const uint32_t *W, const uint16_t *S, const uint16_t *x, ui
  * gamma_final f16[d]. r_in/h_in are read, r_out/h_out written (f16[d]); inputs
  * and outputs must not overlap. trace (may be NULL) receives the state after
  * every layer: f16[n_layers][2][d] as (r, h) pairs.
+ * mode: Q4_STACK_AUTO and Q4_STACK_MULTI run four matvec launches per layer
+ * (the faster path on gfx950 at the shapes measured); Q4_STACK_PERSISTENT runs
+ * every layer in one cooperative launch and requires that the shapes and
+ * buffers allow it (V slice last in the QKV rows; r_out, h_out, trace 16-byte
+ * aligned; a phase's slice per CU within the kernel's register budget),
+ * Q4_ERANGE otherwise. Both paths give bit-identical results.
  */
 typedef struct q4_stack_desc {
     int64_t n_layers, d, f, n_qkv, v_off, dv;
@@ -218,11 +224,20 @@ typedef struct q4_stack_desc {
     const uint16_t *gamma_in;
     const uint16_t *gamma_post;
     const uint16_t *gamma_final;
+    int mode; /* q4_stack_mode */
 } q4_stack_desc;
+
+typedef enum q4_stack_mode { Q4_STACK_AUTO = 0, Q4_STACK_MULTI = 1, Q4_STACK_PERSISTENT = 2 } q4_stack_mode;
 
 q4_status q4_stack_decode(const q4_stack_desc *desc, const uint16_t *r_in,
                           const uint16_t *h_in, uint16_t *r_out, uint16_t *h_out,
                           uint16_t *trace, q4_stream stream);
+
+/* q4_stack_status -- synchronises `stream` and reports whether a persistent
+ * q4_stack_decode on it gave up waiting for data (every wait inside the kernel
+ * is bounded; a timeout makes the kernel finish with undefined outputs and is
+ * reported here as Q4_EHIP, once). Q4_OK otherwise. */
+q4_status q4_stack_status(q4_stream stream);
 
 #ifdef __cplusplus
 }

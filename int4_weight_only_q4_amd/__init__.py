@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(PKG, "libq4.so")
 
 Q4_OK, Q4_EINVAL, Q4_ESHAPE, Q4_EALIGN, Q4_EALIAS, Q4_ERANGE, Q4_EHIP = range(7)
 EPI_NONE, EPI_SILU_MUL, EPI_ADD_RMSNORM = 0, 1, 2
+STACK_AUTO, STACK_MULTI, STACK_PERSISTENT = 0, 1, 2
 MAX_K = 24576
 MAX_M = 64
 MAX_PAIRS = 4096
@@ -32,7 +33,7 @@ BYTES_PER_WEIGHT = 0.5 + 2.0 / 32.0
 ABI_SYMBOLS = (
     "q4_version", "q4_last_error", "q4_bytes_per_weight", "q4_pack", "q4_unpack", "q4_gemv",
     "q4_gemv_batched", "q4_moe_gemv", "q4_add_rmsnorm", "q4_silu_mul", "q4_gemv_ex",
-    "q4_stack_decode",
+    "q4_stack_decode", "q4_stack_status",
 )
 
 
@@ -55,7 +56,7 @@ class StackDesc(C.Structure):
                 ("So", C.c_void_p), ("Wgu", C.c_void_p), ("Sgu", C.c_void_p),
                 ("Wdn", C.c_void_p), ("Sdn", C.c_void_p),
                 ("gamma_in", C.c_void_p), ("gamma_post", C.c_void_p),
-                ("gamma_final", C.c_void_p)]
+                ("gamma_final", C.c_void_p), ("mode", C.c_int)]
 
 
 _P, _I = C.c_void_p, C.c_int64
@@ -72,6 +73,7 @@ _SIGS = {
     "q4_silu_mul": (C.c_int, [_P, _P, _I, _I, _P]),
     "q4_gemv_ex": (C.c_int, [_P, _P, _P, _P, _I, _I, C.POINTER(Epilogue), _P]),
     "q4_stack_decode": (C.c_int, [C.POINTER(StackDesc), _P, _P, _P, _P, _P, _P]),
+    "q4_stack_status": (C.c_int, [_P]),
 }
 
 _lib = None
@@ -236,7 +238,7 @@ class Stack:
     """
 
     def __init__(self, layers, gamma_in, gamma_post, gamma_final, d, f, n_qkv, v_off, dv,
-                 eps=1e-5):
+                 eps=1e-5, mode=STACK_AUTO):
         self.layers = layers
         self.gammas = (gamma_in, gamma_post, gamma_final)
         n = len(layers)
@@ -247,13 +249,21 @@ class Stack:
             self._arrays.append(arr)
             cols.append(C.cast(arr, C.c_void_p))
         self.desc = StackDesc(n, d, f, n_qkv, v_off, dv, eps, *cols, gamma_in.data_ptr(),
-                              gamma_post.data_ptr(), gamma_final.data_ptr())
+                              gamma_post.data_ptr(), gamma_final.data_ptr(), mode)
         self.d = d
         self.n_layers = n
 
     def decode(self, r_in, h_in, r_out, h_out, trace=None, stream=None):
         _check(lib().q4_stack_decode(C.byref(self.desc), _ptr(r_in), _ptr(h_in), _ptr(r_out),
                                      _ptr(h_out), _ptr(trace), _stream(stream)))
+
+    def set_mode(self, mode):
+        self.desc.mode = mode
+
+
+def stack_status(stream=None):
+    """Synchronise and raise if a persistent stack kernel timed out waiting."""
+    _check(lib().q4_stack_status(_stream(stream)))
 
 
 def stack_decode(stack: Stack, r_in, h_in, r_out, h_out, trace=None, stream=None):

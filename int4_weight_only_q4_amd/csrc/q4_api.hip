@@ -8,6 +8,9 @@
 #include <utility>
 
 #include "q4_common.h"
+#include "q4_stack.h"
+#include <cstring>
+#include <vector>
 
 namespace q4 {
 
@@ -114,6 +117,266 @@ q4_status check_gemv_args(const uint32_t *W, const uint16_t *S, const uint16_t *
     if (overlaps(y, yb, W, wbytes(N, K)) || overlaps(y, yb, S, sbytes(N, K)) ||
         overlaps(y, yb, x, (size_t)K * 2))
         return fail(Q4_EALIAS, "the output overlaps an input");
+    return Q4_OK;
+}
+
+
+// ---------------------------------------------------------------------------
+// Decode stack: multi-kernel path (four matvec launches per layer)
+// ---------------------------------------------------------------------------
+q4_status stack_multi(const q4_stack_desc *d, const uint16_t *r_in, const uint16_t *h_in,
+                      uint16_t *r_out, uint16_t *h_out, uint16_t *trace, hipStream_t st)
+{
+    const int64_t D = d->d, F = d->f;
+    const size_t vb = (size_t)D * 2;
+    // Per layer four matvecs and no synchronisation between workgroups: the
+    // residual add happens row by row in the O / down epilogues, and the
+    // RMSNorm that follows it is recomputed by every workgroup of the next
+    // matvec while it stages its activation (bit-identical to q4_add_rmsnorm).
+    // workspace: header | qkv | r1 | u | rA | rB   (256-byte aligned pieces)
+    auto al = [](size_t b) { return (b + 255) / 256 * 256; };
+    const size_t q_b = al((size_t)d->n_qkv * 2), v_b = al(vb), u_b = al((size_t)F * 2);
+    const size_t total = kWsHeader + q_b + 3 * v_b + u_b;
+    char *ws = static_cast<char *>(workspace(st, total));
+    if (!ws)
+        return Q4_EHIP;
+    uint16_t *qkv = reinterpret_cast<uint16_t *>(ws + kWsHeader);
+    char *p = ws + kWsHeader + q_b;
+    uint16_t *r1 = reinterpret_cast<uint16_t *>(p);
+    uint16_t *u = reinterpret_cast<uint16_t *>(p + v_b);
+    uint16_t *rp[2] = {reinterpret_cast<uint16_t *>(p + v_b + u_b),
+                       reinterpret_cast<uint16_t *>(p + 2 * v_b + u_b)};
+
+    const uint16_t *rc = r_in;
+    for (int64_t L = 0; L < d->n_layers; ++L) {
+        const bool last = L + 1 == d->n_layers;
+        uint16_t *r2 = last ? r_out : rp[L & 1];
+        const uint16_t *g_next = last ? d->gamma_final : d->gamma_in + (L + 1) * D;
+        q4_status s;
+        GemvOp qk;
+        qk.W = d->Wqkv[L];
+        qk.S = d->Sqkv[L];
+        qk.N = (int)d->n_qkv;
+        qk.K = (int)D;
+        if (L == 0) {
+            qk.x = h_in;
+        } else {  // h = RMSNorm(r) * gamma_in[L], recomputed in the prologue
+            qk.norm_src = rc;
+            qk.norm_gamma = d->gamma_in + L * D;
+            qk.norm_eps = d->eps;
+        }
+        qk.epi = GemvOp::NONE;
+        qk.y = qkv;
+        if ((s = launch_gemv_op(qk, st)) != Q4_OK)
+            return s;
+        GemvOp o;
+        o.W = d->Wo[L];
+        o.S = d->So[L];
+        o.N = (int)D;
+        o.K = (int)d->dv;
+        o.x = qkv + d->v_off;
+        o.epi = GemvOp::RESID;
+        o.res_in = rc;
+        o.res_out = r1;
+        if ((s = launch_gemv_op(o, st)) != Q4_OK)
+            return s;
+        GemvOp gu;
+        gu.W = d->Wgu[L];
+        gu.S = d->Sgu[L];
+        gu.N = (int)(2 * F);
+        gu.K = (int)D;
+        gu.norm_src = r1;
+        gu.norm_gamma = d->gamma_post + L * D;
+        gu.norm_eps = d->eps;
+        gu.epi = GemvOp::SILU;
+        gu.y = u;
+        if ((s = launch_gemv_op(gu, st)) != Q4_OK)
+            return s;
+        GemvOp dn;
+        dn.W = d->Wdn[L];
+        dn.S = d->Sdn[L];
+        dn.N = (int)D;
+        dn.K = (int)F;
+        dn.x = u;
+        dn.epi = GemvOp::RESID;
+        dn.res_in = r1;
+        dn.res_out = r2;
+        if ((s = launch_gemv_op(dn, st)) != Q4_OK)
+            return s;
+        if (trace) {
+            uint16_t *tr = trace + (2 * L) * D;
+            Q4_HIP(hipMemcpyAsync(tr, r2, vb, hipMemcpyDeviceToDevice, st));
+            if ((s = launch_add_rmsnorm(nullptr, r2, g_next, tr + D, nullptr, (int)D, 1, d->eps,
+                                        st)) != Q4_OK)
+                return s;
+        }
+        rc = r2;
+    }
+    return launch_add_rmsnorm(nullptr, r_out, d->gamma_final, h_out, nullptr, (int)D, 1, d->eps,
+                              st);
+}
+
+
+// ---------------------------------------------------------------------------
+// Decode stack: persistent path (one cooperative launch per token)
+// ---------------------------------------------------------------------------
+struct StackState {
+    char *mem = nullptr;
+    size_t bytes = 0;
+    uint32_t epoch = 0;                 // tag of the next call's first phase
+    std::vector<const void *> table;    // host copy of the uploaded pointer tables
+    size_t off_tab = 0, off_v = 0, off_r1 = 0, off_u = 0, off_r2 = 0, off_qkv = 0;
+};
+std::mutex g_stack_mu;
+std::map<std::pair<int, hipStream_t>, StackState> g_stack;
+
+q4_status stack_persistent(const q4_stack_desc *d, const uint16_t *r_in, const uint16_t *h_in,
+                           uint16_t *r_out, uint16_t *h_out, uint16_t *trace, hipStream_t st,
+                           bool *ran)
+{
+    *ran = false;
+    const int L = (int)d->n_layers, D = (int)d->d, F = (int)d->f, NQ = (int)d->n_qkv;
+    const int DV = (int)d->dv, VOFF = (int)d->v_off;
+    if (VOFF + DV != NQ)
+        return fail(Q4_OK, "the V slice is not the last rows of the QKV matrix");
+    if (!aligned(r_out, 16) || !aligned(h_out, 16) || (trace && !aligned(trace, 16)))
+        return fail(Q4_OK, "r_out, h_out and trace must be 16-byte aligned");
+    int dev = 0;
+    Q4_HIP(hipGetDevice(&dev));
+    int coop = 0, nb = 0;
+    Q4_HIP(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev));
+    Q4_HIP(hipDeviceGetAttribute(&nb, hipDeviceAttributeMultiprocessorCount, dev));
+    if (!coop)
+        return fail(Q4_OK, "cooperative launch is not supported");
+    auto per = [&](int n) { return (n + nb - 1) / nb; };
+    const int kmax = std::max(D, std::max(DV, F));
+    int stmax = std::max(std::max(per(DV) * (D / 32), per(VOFF) * (D / 32)),
+                         std::max(per(D) * (DV / 32),
+                                  std::max(2 * per(F) * (D / 32), per(D) * (F / 32))));
+    // the compute lanes hold the weights of a phase, kStackNch groups per lane
+    if (stmax > kStackNch * kStackCompute)
+        return fail(Q4_OK, "a phase slice of %d groups exceeds the kernel's %d", stmax,
+                    kStackNch * kStackCompute);
+    // LDS carve-up: staged activation (+ 7 * group sums) for K = kmax and for
+    // the O phase, per-chunk partials, the residual of a norm, SiLU row values
+    // and this workgroup's residual rows
+    auto a16 = [](size_t b) { return (b + 15) / 16 * 16; };
+    size_t lds = 0;
+    auto carve = [&](size_t bytes) {
+        const size_t o = lds;
+        lds += a16(bytes);
+        return (int)o;
+    };
+    const int lds_xs = carve((size_t)kmax * 2), lds_cs = carve((size_t)kmax / 8);
+    const int lds_xo = carve((size_t)DV * 2), lds_co = carve((size_t)DV / 8);
+    const int lds_st = carve((size_t)stmax * 8), lds_raw = carve((size_t)D * 2);
+    const int lds_rowv = carve((size_t)2 * per(F) * 4), lds_lres = carve((size_t)per(D) * 4);
+    int max_lds = 0;
+    Q4_HIP(hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev));
+    if (lds + 64 > (size_t)max_lds)
+        return fail(Q4_OK, "the persistent kernel would need %zu bytes of LDS", lds);
+    Q4_HIP(hipFuncSetAttribute(stack_kernel(), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)lds));
+    int occ = 0;
+    Q4_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, stack_kernel(), kStackThreads, lds));
+    if (occ < 1)
+        return fail(Q4_OK, "one workgroup per CU does not fit");
+
+    auto al = [](size_t b) { return (b + 255) / 256 * 256; };
+    StackState *S;
+    {
+        std::lock_guard<std::mutex> lock(g_stack_mu);
+        S = &g_stack[{dev, st}];
+    }
+    const size_t off_tab = 256, tab_b = al((size_t)L * 8 * sizeof(void *));
+    const size_t off_v = off_tab + tab_b, off_r1 = off_v + al((size_t)DV * 4);
+    const size_t off_u = off_r1 + al((size_t)D * 4), off_r2 = off_u + al((size_t)F * 4);
+    const size_t off_fl = off_r2 + al((size_t)D * 4), off_qkv = off_fl + al((size_t)4 * nb * 4);
+    const size_t total = off_qkv + al((size_t)NQ * 2);
+    if (!S->mem || S->bytes < total || S->off_v != off_v || S->off_r1 != off_r1 ||
+        S->off_u != off_u || S->off_r2 != off_r2) {
+        if (S->mem) {
+            Q4_HIP(hipStreamSynchronize(st));
+            Q4_HIP(hipFree(S->mem));
+            S->mem = nullptr;
+        }
+        void *m = nullptr;
+        Q4_HIP(hipMalloc(&m, total));
+        // tags 0xFFFF never match a phase: every buffer starts out stale
+        Q4_HIP(hipMemset(m, 0, 256));
+        Q4_HIP(hipMemset(static_cast<char *>(m) + off_v, 0xFF, off_qkv - off_v));
+        Q4_HIP(hipDeviceSynchronize());
+        S->mem = static_cast<char *>(m);
+        S->bytes = total;
+        S->table.clear();
+        S->off_tab = off_tab;
+        S->off_v = off_v;
+        S->off_r1 = off_r1;
+        S->off_u = off_u;
+        S->off_r2 = off_r2;
+        S->off_qkv = off_qkv;
+    }
+    // device pointer tables [L][4] of weights, then scales (uploaded when they change)
+    std::vector<const void *> tab((size_t)L * 8);
+    for (int l = 0; l < L; ++l) {
+        tab[l * 4 + 0] = d->Wqkv[l];
+        tab[l * 4 + 1] = d->Wo[l];
+        tab[l * 4 + 2] = d->Wgu[l];
+        tab[l * 4 + 3] = d->Wdn[l];
+        tab[(size_t)L * 4 + l * 4 + 0] = d->Sqkv[l];
+        tab[(size_t)L * 4 + l * 4 + 1] = d->So[l];
+        tab[(size_t)L * 4 + l * 4 + 2] = d->Sgu[l];
+        tab[(size_t)L * 4 + l * 4 + 3] = d->Sdn[l];
+    }
+    if (tab != S->table) {
+        Q4_HIP(hipStreamSynchronize(st));
+        Q4_HIP(hipMemcpy(S->mem + off_tab, tab.data(), tab.size() * sizeof(void *),
+                         hipMemcpyHostToDevice));
+        S->table = tab;
+    }
+
+    StackParams p{};
+    p.n_layers = L;
+    p.d = D;
+    p.f = F;
+    p.n_qkv = NQ;
+    p.v_off = VOFF;
+    p.dv = DV;
+    p.eps = d->eps;
+    p.W = reinterpret_cast<const uint32_t *const *>(S->mem + off_tab);
+    p.S = reinterpret_cast<const uint16_t *const *>(S->mem + off_tab + (size_t)L * 4 * sizeof(void *));
+    p.gamma_in = d->gamma_in;
+    p.gamma_post = d->gamma_post;
+    p.gamma_final = d->gamma_final;
+    p.r_in = r_in;
+    p.h_in = h_in;
+    p.r_out = r_out;
+    p.h_out = h_out;
+    p.trace = trace;
+    p.qkv = reinterpret_cast<uint16_t *>(S->mem + off_qkv);
+    p.vbuf = reinterpret_cast<uint32_t *>(S->mem + off_v);
+    p.r1buf = reinterpret_cast<uint32_t *>(S->mem + off_r1);
+    p.ubuf = reinterpret_cast<uint32_t *>(S->mem + off_u);
+    p.r2buf = reinterpret_cast<uint32_t *>(S->mem + off_r2);
+    p.flags = reinterpret_cast<uint32_t *>(S->mem + off_fl);
+    p.epoch0 = S->epoch;
+    S->epoch = (uint32_t)((S->epoch + 4ull * L) % 0xFFFFu);
+    p.err = reinterpret_cast<unsigned *>(S->mem);
+    p.lds_xs = lds_xs;
+    p.lds_cs = lds_cs;
+    p.lds_xo = lds_xo;
+    p.lds_co = lds_co;
+    p.lds_st = lds_st;
+    p.lds_raw = lds_raw;
+    p.lds_rowv = lds_rowv;
+    p.lds_lres = lds_lres;
+    matvec_layout(D / 32, &p.lpr_d, &p.ng_d);
+    matvec_layout(DV / 32, &p.lpr_v, &p.ng_v);
+    matvec_layout(F / 32, &p.lpr_f, &p.ng_f);
+    void *args[] = {&p};
+    Q4_HIP(hipLaunchCooperativeKernel(stack_kernel(), dim3(nb), dim3(kStackThreads), args, (unsigned)lds,
+                                      st));
+    *ran = true;
     return Q4_OK;
 }
 
@@ -367,92 +630,43 @@ q4_status q4_stack_decode(const q4_stack_desc *d, const uint16_t *r_in, const ui
             return st;
     }
 
-    // Per layer four matvecs and no synchronisation between workgroups: the
-    // residual add happens row by row in the O / down epilogues, and the
-    // RMSNorm that follows it is recomputed by every workgroup of the next
-    // matvec while it stages its activation (bit-identical to q4_add_rmsnorm).
-    // workspace: header | qkv | r1 | u | rA | rB   (256-byte aligned pieces)
-    auto al = [](size_t b) { return (b + 255) / 256 * 256; };
-    const size_t q_b = al((size_t)d->n_qkv * 2), v_b = al(vb), u_b = al((size_t)F * 2);
-    const size_t total = kWsHeader + q_b + 3 * v_b + u_b;
+    const int mode = d->mode;
+    if (mode != Q4_STACK_AUTO && mode != Q4_STACK_MULTI && mode != Q4_STACK_PERSISTENT)
+        return fail(Q4_EINVAL, "unknown stack mode %d", mode);
     hipStream_t st = as_stream(stream);
-    char *ws = static_cast<char *>(workspace(st, total));
-    if (!ws)
-        return Q4_EHIP;
-    uint16_t *qkv = reinterpret_cast<uint16_t *>(ws + kWsHeader);
-    char *p = ws + kWsHeader + q_b;
-    uint16_t *r1 = reinterpret_cast<uint16_t *>(p);
-    uint16_t *u = reinterpret_cast<uint16_t *>(p + v_b);
-    uint16_t *rp[2] = {reinterpret_cast<uint16_t *>(p + v_b + u_b),
-                       reinterpret_cast<uint16_t *>(p + 2 * v_b + u_b)};
-
-    const uint16_t *rc = r_in;
-    for (int64_t L = 0; L < d->n_layers; ++L) {
-        const bool last = L + 1 == d->n_layers;
-        uint16_t *r2 = last ? r_out : rp[L & 1];
-        const uint16_t *g_next = last ? d->gamma_final : d->gamma_in + (L + 1) * D;
-        q4_status s;
-        GemvOp qk;
-        qk.W = d->Wqkv[L];
-        qk.S = d->Sqkv[L];
-        qk.N = (int)d->n_qkv;
-        qk.K = (int)D;
-        if (L == 0) {
-            qk.x = h_in;
-        } else {  // h = RMSNorm(r) * gamma_in[L], recomputed in the prologue
-            qk.norm_src = rc;
-            qk.norm_gamma = d->gamma_in + L * D;
-            qk.norm_eps = d->eps;
-        }
-        qk.epi = GemvOp::NONE;
-        qk.y = qkv;
-        if ((s = launch_gemv_op(qk, st)) != Q4_OK)
+    if (mode == Q4_STACK_PERSISTENT) {
+        bool ran = false;
+        q4_status s = stack_persistent(d, r_in, h_in, r_out, h_out, trace, st, &ran);
+        if (s != Q4_OK || ran)
             return s;
-        GemvOp o;
-        o.W = d->Wo[L];
-        o.S = d->So[L];
-        o.N = (int)D;
-        o.K = (int)d->dv;
-        o.x = qkv + d->v_off;
-        o.epi = GemvOp::RESID;
-        o.res_in = rc;
-        o.res_out = r1;
-        if ((s = launch_gemv_op(o, st)) != Q4_OK)
-            return s;
-        GemvOp gu;
-        gu.W = d->Wgu[L];
-        gu.S = d->Sgu[L];
-        gu.N = (int)(2 * F);
-        gu.K = (int)D;
-        gu.norm_src = r1;
-        gu.norm_gamma = d->gamma_post + L * D;
-        gu.norm_eps = d->eps;
-        gu.epi = GemvOp::SILU;
-        gu.y = u;
-        if ((s = launch_gemv_op(gu, st)) != Q4_OK)
-            return s;
-        GemvOp dn;
-        dn.W = d->Wdn[L];
-        dn.S = d->Sdn[L];
-        dn.N = (int)D;
-        dn.K = (int)F;
-        dn.x = u;
-        dn.epi = GemvOp::RESID;
-        dn.res_in = r1;
-        dn.res_out = r2;
-        if ((s = launch_gemv_op(dn, st)) != Q4_OK)
-            return s;
-        if (trace) {
-            uint16_t *tr = trace + (2 * L) * D;
-            Q4_HIP(hipMemcpyAsync(tr, r2, vb, hipMemcpyDeviceToDevice, st));
-            if ((s = launch_add_rmsnorm(nullptr, r2, g_next, tr + D, nullptr, (int)D, 1, d->eps,
-                                        st)) != Q4_OK)
-                return s;
-        }
-        rc = r2;
+        char why[sizeof(g_err)];
+        memcpy(why, g_err, sizeof(why));
+        return fail(Q4_ERANGE, "the persistent stack kernel cannot run here: %s", why);
     }
-    return launch_add_rmsnorm(nullptr, r_out, d->gamma_final, h_out, nullptr, (int)D, 1, d->eps,
-                              st);
+    return stack_multi(d, r_in, h_in, r_out, h_out, trace, st);
+}
+
+q4_status q4_stack_status(q4_stream stream)
+{
+    hipStream_t st = as_stream(stream);
+    Q4_HIP(hipStreamSynchronize(st));
+    int dev = 0;
+    Q4_HIP(hipGetDevice(&dev));
+    unsigned *err = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_stack_mu);
+        auto it = g_stack.find({dev, st});
+        if (it == g_stack.end())
+            return Q4_OK;
+        err = reinterpret_cast<unsigned *>(it->second.mem);
+    }
+    unsigned h = 0;
+    Q4_HIP(hipMemcpy(&h, err, sizeof(h), hipMemcpyDeviceToHost));
+    if (!h)
+        return Q4_OK;
+    const unsigned zero = 0;
+    Q4_HIP(hipMemcpy(err, &zero, sizeof(zero), hipMemcpyHostToDevice));
+    return fail(Q4_EHIP, "a persistent decode-stack kernel timed out waiting for data");
 }
 
 }  // extern "C"

@@ -15,6 +15,28 @@
 
 namespace q4 {
 
+// Weight and scale loads. Weights are read once per token, so they use
+// non-temporal loads (they do not displace the activation or the published
+// vectors in the caches), through global (not flat) addressing so that they
+// count only against the vector-memory counter. A scale is returned in a
+// 32-bit register of its own: two 16-bit scales packed into one register make
+// the compiler wait for the first load before it can issue the next, which
+// serialises the whole load sequence.
+typedef uint32_t q4_v4u32 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const q4_v4u32 q4_global_v4u32;
+typedef __attribute__((address_space(1))) const uint16_t q4_global_u16;
+
+__device__ __forceinline__ uint4 load_weights(const uint4 *p)
+{
+    const q4_v4u32 v = __builtin_nontemporal_load((q4_global_v4u32 *)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint32_t load_scale(const uint16_t *p)
+{
+    return __builtin_nontemporal_load((q4_global_u16 *)p);
+}
+
 // Sum over one group (four words, 32 codes) of (c - 7) * x.
 //
 // A code c kept in mantissa bits 0..3 of a binary16 whose exponent field is

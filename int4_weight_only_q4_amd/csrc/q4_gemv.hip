@@ -21,6 +21,7 @@
 //  * The LPR partial sums of a row are combined with an xor butterfly in a
 //    fixed order, so results are identical run to run.
 #include "q4_dequant.h"
+#include "q4_stack.h"
 
 namespace q4 {
 namespace {
@@ -97,20 +98,18 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams a)
 
     // 1. weight and scale loads, in the order they are consumed (group-major)
     uint4 wv[NG][RPS];
-    uint16_t sv[NG][RPS];
+    uint32_t sv[NG][RPS];
+    // (branch-free: a lane past the last group re-reads group G - 1, which the
+    // accumulation skips; a conditional load would let the compiler convert the
+    // scale inside the branch and wait for it there)
 #pragma unroll
     for (int i = 0; i < NG; ++i)
 #pragma unroll
         for (int r = 0; r < RPS; ++r) {
-            const int g = j + LPR * i;
-            if (g < G) {
-                const size_t off = (size_t)row[r] * G + g;
-                wv[i][r] = a.W[off];
-                sv[i][r] = a.S[off];
-            } else {
-                wv[i][r] = make_uint4(0, 0, 0, 0);
-                sv[i][r] = 0;
-            }
+            const int g = min(j + LPR * i, G - 1);
+            const size_t off = (size_t)row[r] * G + g;
+            wv[i][r] = load_weights(a.W + off);
+            sv[i][r] = load_scale(a.S + off);
         }
 
     // 2. activation into LDS (after an RMSNorm of the residual for PRO_NORM)
@@ -277,6 +276,13 @@ q4_status dispatch_lpr(const Cfg &c, const GemvParams &p, hipStream_t st)
 
 }  // namespace
 
+void matvec_layout(int G, int *lpr, int *ng)
+{
+    const Cfg c = choose_cfg(G);
+    *lpr = c.lpr;
+    *ng = c.ng;
+}
+
 q4_status launch_gemv_op(const GemvOp &op, hipStream_t stream)
 {
     GemvParams p{};
@@ -375,18 +381,13 @@ __global__ __launch_bounds__(256) void k_gemv_batched(const uint4 *__restrict__ 
     const int ng = (G + 63) >> 6;
 
     uint4 wv[kBatchNG];
-    float sv[kBatchNG];
+    uint32_t sv[kBatchNG];
 #pragma unroll
     for (int i = 0; i < kBatchNG; ++i) {
-        const int g = lane + 64 * i;
-        if (i < ng && g < G) {
-            const size_t off = (size_t)rrow * G + g;
-            wv[i] = W[off];
-            sv[i] = h2f(S[off]);
-        } else {
-            wv[i] = make_uint4(0, 0, 0, 0);
-            sv[i] = 0.f;
-        }
+        // branch-free (see k_gemv): lanes past the last group re-read group G - 1
+        const size_t off = (size_t)rrow * G + min(lane + 64 * i, G - 1);
+        wv[i] = load_weights(W + off);
+        sv[i] = load_scale(S + off);
     }
 
     for (int m0 = 0; m0 < M; m0 += MB) {
@@ -411,7 +412,7 @@ __global__ __launch_bounds__(256) void k_gemv_batched(const uint4 *__restrict__ 
                     if (m < mb) {
                         const uint4 *xs = smem + m * stride;
                         const float *cs = reinterpret_cast<const float *>(xs + (K >> 3));
-                        acc[m] = fmaf(sv[i], group_dot(wv[i], xs + g * 4, cs[g]), acc[m]);
+                        acc[m] = fmaf(h2f(sv[i]), group_dot(wv[i], xs + g * 4, cs[g]), acc[m]);
                     }
                 }
             }

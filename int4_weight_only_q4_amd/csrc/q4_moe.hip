@@ -136,18 +136,15 @@ __global__ __launch_bounds__(256) void k_moe_gemv(const uint4 *__restrict__ Wall
     const uint4 *W = Wall + (size_t)e * N * G;
     const uint16_t *S = Sall + (size_t)e * N * G;
     uint4 wv[NGMAX];
-    float sv[NGMAX];
+    uint32_t sv[NGMAX];
 #pragma unroll
     for (int i = 0; i < NGMAX; ++i) {
-        const int g = j + LPR * i;
-        if (i < ng && g < G) {
-            const size_t off = (size_t)row * G + g;
-            wv[i] = W[off];
-            sv[i] = h2f(S[off]);
-        } else {
-            wv[i] = make_uint4(0, 0, 0, 0);
-            sv[i] = 0.f;
-        }
+        // branch-free: lanes past the last group re-read group G - 1, which the
+        // accumulation skips (a conditional load would make the compiler wait
+        // for each scale inside its branch)
+        const size_t off = (size_t)row * G + min(j + LPR * i, G - 1);
+        wv[i] = load_weights(W + off);
+        sv[i] = load_scale(S + off);
     }
 
     for (int q0 = p0; q0 < p1; q0 += MB) {
@@ -174,7 +171,7 @@ __global__ __launch_bounds__(256) void k_moe_gemv(const uint4 *__restrict__ Wall
                     if (m < mb) {
                         const uint4 *xs = smem + m * stride;
                         const float *cs = reinterpret_cast<const float *>(xs + (K >> 3));
-                        acc[m] = fmaf(sv[i], group_dot(wv[i], xs + g * 4, cs[g]), acc[m]);
+                        acc[m] = fmaf(h2f(sv[i]), group_dot(wv[i], xs + g * 4, cs[g]), acc[m]);
                     }
             }
         }
