@@ -289,9 +289,10 @@ q4_status stack_persistent(const q4_stack_desc *d, const uint16_t *r_in, const u
         S = &g_stack[{dev, st}];
     }
     const size_t off_tab = 256, tab_b = al((size_t)L * 8 * sizeof(void *));
-    const size_t off_v = off_tab + tab_b, off_r1 = off_v + al((size_t)DV * 4);
-    const size_t off_u = off_r1 + al((size_t)D * 4), off_r2 = off_u + al((size_t)F * 4);
-    const size_t off_fl = off_r2 + al((size_t)D * 4), off_qkv = off_fl + al((size_t)4 * nb * 4);
+    const size_t R = kStackCopies;  // copies of each published vector and flag array
+    const size_t off_v = off_tab + tab_b, off_r1 = off_v + al(R * DV * 4);
+    const size_t off_u = off_r1 + al(R * D * 4), off_r2 = off_u + al(R * F * 4);
+    const size_t off_fl = off_r2 + al(R * D * 4), off_qkv = off_fl + al(4 * R * nb * 4);
     const size_t total = off_qkv + al((size_t)NQ * 2);
     if (!S->mem || S->bytes < total || S->off_v != off_v || S->off_r1 != off_r1 ||
         S->off_u != off_u || S->off_r2 != off_r2) {

@@ -49,14 +49,21 @@ __device__ __forceinline__ uint32_t load_scale(const uint16_t *p)
 // accumulates in f32; lo gathers the 2^-24-scaled pairs, hi the 2^-20-scaled
 // ones, and sum (c - 7) x = 2^24 lo + 2^20 hi - 7 sum(x), with c7 = 7 sum(x)
 // staged beside the activation. A one-hot x therefore gives (c - 7) exactly.
-__device__ __forceinline__ float group_dot(uint4 wv, const uint4 *xp, float c7)
+// Position in the staged activation of quarter q (chunk 4 g + q) of group g.
+// The four 16-byte quarters of a group are rotated by g / 2: lanes that read
+// the same quarter of consecutive groups (64 bytes apart) would otherwise hit
+// the same LDS banks; rotated, 8 such lanes cover 8 distinct 16-byte bank
+// groups.
+__device__ __forceinline__ int staged_index(int g, int q) { return 4 * g + ((q + (g >> 1)) & 3); }
+
+__device__ __forceinline__ float group_dot(uint4 wv, const uint4 *xs, int g, float c7)
 {
     const uint32_t m0 = 0x000F000Fu, m1 = 0x00F000F0u;
     float lo = 0.f, hi = 0.f;
     const uint32_t w[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const uint4 xq = xp[q];
+        const uint4 xq = xs[staged_index(g, q)];
         const uint32_t t = w[q] >> 8;
         lo = __builtin_amdgcn_fdot2(as_h2(w[q] & m0), as_h2(xq.x), lo, false);
         hi = __builtin_amdgcn_fdot2(as_h2(w[q] & m1), as_h2(xq.y), hi, false);
@@ -81,7 +88,7 @@ __device__ __forceinline__ void stage_activation(const uint16_t *__restrict__ x,
             p.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
             p.z = (v.y & 0xFFFFu) | (v.w << 16);
             p.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
-            xs[c] = p;
+            xs[staged_index(c >> 2, c & 3)] = p;
             sum = ((h2f(v.x & 0xFFFF) + h2f(v.x >> 16)) + (h2f(v.y & 0xFFFF) + h2f(v.y >> 16))) +
                   ((h2f(v.z & 0xFFFF) + h2f(v.z >> 16)) + (h2f(v.w & 0xFFFF) + h2f(v.w >> 16)));
         }
@@ -113,7 +120,7 @@ __device__ __forceinline__ void put_chunk(uint4 v, int c, bool valid, uint4 *xs,
         p.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
         p.z = (v.y & 0xFFFFu) | (v.w << 16);
         p.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
-        xs[c] = p;
+        xs[staged_index(c >> 2, c & 3)] = p;
         sum = ((h2f(v.x & 0xFFFF) + h2f(v.x >> 16)) + (h2f(v.y & 0xFFFF) + h2f(v.y >> 16))) +
               ((h2f(v.z & 0xFFFF) + h2f(v.z >> 16)) + (h2f(v.w & 0xFFFF) + h2f(v.w >> 16)));
     }

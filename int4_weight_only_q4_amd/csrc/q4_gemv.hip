@@ -156,11 +156,10 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams a)
     for (int i = 0; i < NG; ++i) {
         const int g = j + LPR * i;
         if (g < G) {
-            const uint4 *xp = xs + g * 4;
             const float c7 = cs[g];
 #pragma unroll
             for (int r = 0; r < RPS; ++r)
-                acc[r] = fmaf(h2f(sv[i][r]), group_dot(wv[i][r], xp, c7), acc[r]);
+                acc[r] = fmaf(h2f(sv[i][r]), group_dot(wv[i][r], xs, g, c7), acc[r]);
         }
     }
 
@@ -412,7 +411,7 @@ __global__ __launch_bounds__(256) void k_gemv_batched(const uint4 *__restrict__ 
                     if (m < mb) {
                         const uint4 *xs = smem + m * stride;
                         const float *cs = reinterpret_cast<const float *>(xs + (K >> 3));
-                        acc[m] = fmaf(h2f(sv[i]), group_dot(wv[i], xs + g * 4, cs[g]), acc[m]);
+                        acc[m] = fmaf(h2f(sv[i]), group_dot(wv[i], xs, g, cs[g]), acc[m]);
                     }
                 }
             }

@@ -171,7 +171,7 @@ __global__ __launch_bounds__(256) void k_moe_gemv(const uint4 *__restrict__ Wall
                     if (m < mb) {
                         const uint4 *xs = smem + m * stride;
                         const float *cs = reinterpret_cast<const float *>(xs + (K >> 3));
-                        acc[m] = fmaf(h2f(sv[i]), group_dot(wv[i], xs + g * 4, cs[g]), acc[m]);
+                        acc[m] = fmaf(h2f(sv[i]), group_dot(wv[i], xs, g, cs[g]), acc[m]);
                     }
             }
         }

@@ -12,6 +12,8 @@ namespace q4 {
 constexpr int kStackThreads = 1024;
 constexpr int kStackCompute = 768;
 constexpr int kStackNch = 8;
+// Copies of every published vector and flag array (one per XCD).
+constexpr int kStackCopies = 8;
 
 struct StackParams {
     int n_layers, d, f, n_qkv, v_off, dv;
@@ -22,8 +24,8 @@ struct StackParams {
     const uint16_t *r_in, *h_in;
     uint16_t *r_out, *h_out, *trace;
     uint16_t *qkv;                           // plain [n_qkv]
-    uint32_t *vbuf, *r1buf, *ubuf, *r2buf;   // tagged [dv], [d], [f], [d]
-    uint32_t *flags;                         // [4][workgroups] phase flags (V, r1, u, r2)
+    uint32_t *vbuf, *r1buf, *ubuf, *r2buf;   // tagged [copies][dv], [d], [f], [d]
+    uint32_t *flags;                         // [4][copies][workgroups] (V, r1, u, r2)
     uint32_t epoch0;                         // tag of the first phase of this call
     unsigned *err;                           // set on a wait timeout
     int lds_xs, lds_cs, lds_xo, lds_co, lds_st, lds_raw, lds_rowv, lds_lres;  // LDS byte offsets

@@ -50,23 +50,40 @@ constexpr int kStagers = kThreads - kCompute;  // waves 12..15: cross-workgroup 
 static_assert(kStagers == 256, "the staging lanes replay the 256-lane canonical order");
 constexpr unsigned kSpinLimit = 1u << 21;  // polls before giving up
 
-__device__ __forceinline__ void publish(uint32_t *buf, int i, uint16_t v, uint32_t tag)
+// Every published vector (and its flag array) exists in kCopies copies, one per
+// group of workgroups (blockIdx mod kCopies, i.e. per XCD under the round-robin
+// dispatch of workgroups to XCDs): a producer writes all copies, a consumer
+// reads its own, so each copy is read by nb / kCopies workgroups and no few
+// memory channels serve the whole chip's reads.
+constexpr int kCopies = kStackCopies;
+
+__device__ __forceinline__ int my_copy() { return (int)(blockIdx.x % kCopies); }
+
+// Element i of a published vector of length len, all copies.
+__device__ __forceinline__ void publish(uint32_t *buf, int len, int i, uint16_t v, uint32_t tag)
 {
-    __hip_atomic_store(buf + i, (uint32_t)v | (tag << 16), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t w = (uint32_t)v | (tag << 16);
+#pragma unroll
+    for (int c = 0; c < kCopies; ++c)
+        __hip_atomic_store(buf + (size_t)c * len + i, w, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One flag word per workgroup and phase kind, written after its data.
-__device__ __forceinline__ void publish_flag(uint32_t *flags, int b, uint32_t tag)
+// One flag word per workgroup and phase kind (all copies), written after its
+// data. flags: [kCopies][nb].
+__device__ __forceinline__ void publish_flag(uint32_t *flags, int nb, int b, uint32_t tag)
 {
-    __hip_atomic_store(flags + b, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((int)threadIdx.x < kCopies)
+        __hip_atomic_store(flags + (size_t)threadIdx.x * nb + b, tag, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Poller wave: bounded wait until all nb flags carry `tag`.
+// One wave: bounded wait until all nb flags of this workgroup's copy carry `tag`.
 __device__ __forceinline__ void poll_flags(const uint32_t *flags, int nb, uint32_t tag,
                                            unsigned *err)
 {
     const int lane = threadIdx.x & 63;
+    flags += (size_t)my_copy() * nb;
     for (unsigned it = 0;; ++it) {
         bool ok = true;
         for (int i = lane; i < nb; i += 64)
@@ -147,7 +164,7 @@ __device__ __forceinline__ void compute_chunks(const PhaseMap &m, const uint4 (&
     for (int i = 0; i < kStackNch; ++i) {
         const int cl = t + kCompute * i;
         if (cl < total)
-            st[cl] = make_float2(h2f(sv[i]), group_dot(wv[i], xs + g * 4, cs[g]));
+            st[cl] = make_float2(h2f(sv[i]), group_dot(wv[i], xs, g, cs[g]));
         g += step;
         if (g >= m.G)
             g -= m.G;
@@ -191,8 +208,8 @@ __device__ __forceinline__ void load_chunk_words(const uint32_t *buf, int c, uin
         q[k] = __hip_atomic_load(p + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Staging lanes s = 0..255: read chunks c = s + 256 i of a tagged buffer of
-// `chunks` chunks, kReadBatch chunks per lane in flight at a time, re-reading a
+// Staging lanes s = 0..255: read chunks c = s + 256 i of this workgroup's copy
+// of a tagged buffer of `chunks` chunks, kReadBatch chunks per lane in flight at a time, re-reading a
 // chunk until all its words carry `tag` (bounded: on timeout sets *err and
 // goes on). fn(c, valid, value) is called for every i by every lane (so it may
 // shuffle within the wave).
@@ -203,6 +220,7 @@ __device__ __forceinline__ void read_tagged(const uint32_t *buf, int chunks, uin
                                             unsigned *err, F &&fn)
 {
     const int s = threadIdx.x - kCompute;
+    buf += (size_t)my_copy() * chunks * 8;
     for (int base = 0; base < chunks; base += kStagers * kReadBatch) {
         uint64_t q[kReadBatch][4];
 #pragma unroll
@@ -423,8 +441,9 @@ __device__ __forceinline__ void layer_loop(const StackParams &p, const Lds &l)
     const int b = blockIdx.x, nb = gridDim.x;
     const int t = threadIdx.x;
     const int d = p.d, f = p.f;
-    uint32_t *const flag_v = p.flags, *const flag_r1 = p.flags + nb;
-    uint32_t *const flag_u = p.flags + 2 * nb, *const flag_r2 = p.flags + 3 * nb;
+    const int fl = kCopies * nb;  // flags of one phase kind: [kCopies][nb]
+    uint32_t *const flag_v = p.flags, *const flag_r1 = p.flags + fl;
+    uint32_t *const flag_u = p.flags + 2 * fl, *const flag_r2 = p.flags + 3 * fl;
     uint4 wv[kStackNch];  // compute role: this lane's weight chunks of a phase
     uint32_t sv[kStackNch];
 
@@ -460,11 +479,10 @@ __device__ __forceinline__ void layer_loop(const StackParams &p, const Lds &l)
                 const int row = cur.row_of(v);
                 const uint16_t y = f2h(acc);
                 p.qkv[row] = y;
-                publish(p.vbuf, row - p.v_off, y, tg);
+                publish(p.vbuf, p.dv, row - p.v_off, y, tg);
             });
             __syncthreads();
-            if (t == 0)
-                publish_flag(flag_v, b, tg);
+            publish_flag(flag_v, nb, b, tg);
         }
         // ---- Q/K rows (compute role) while the stagers wait for V -----------
         const PhaseMap qk = map_of(p, 1, L, b, nb);
@@ -490,11 +508,10 @@ __device__ __forceinline__ void layer_loop(const StackParams &p, const Lds &l)
             reduce_rows(o, l.st, [&](int v, float acc) {
                 const uint16_t r1 = f2h(h2f(f2h(acc)) + l.lres[v]);
                 l.lres[v] = h2f(r1);
-                publish(p.r1buf, o.row_of(v), r1, tg);
+                publish(p.r1buf, d, o.row_of(v), r1, tg);
             });
             __syncthreads();
-            if (t == 0)
-                publish_flag(flag_r1, b, tg);
+            publish_flag(flag_r1, nb, b, tg);
         }
         // ---- gate_up: RMSNorm prologue, SiLU-multiply epilogue --------------
         const PhaseMap gu = map_of(p, 3, L, b, nb);
@@ -514,10 +531,10 @@ __device__ __forceinline__ void layer_loop(const StackParams &p, const Lds &l)
         {
             const uint32_t tg = phase_tag(p.epoch0, ph + 2);
             for (int i = t; i < gu.nrow; i += kThreads)
-                publish(p.ubuf, gu.row0 + i, f2h(silu_mul_f(l.rowv[i], l.rowv[gu.nrow + i])), tg);
+                publish(p.ubuf, f, gu.row0 + i, f2h(silu_mul_f(l.rowv[i], l.rowv[gu.nrow + i])),
+                        tg);
             __syncthreads();
-            if (t == 0)
-                publish_flag(flag_u, b, tg);
+            publish_flag(flag_u, nb, b, tg);
         }
         // ---- down: residual add in the epilogue -----------------------------
         const PhaseMap dn = map_of(p, 4, L, b, nb);
@@ -535,13 +552,12 @@ __device__ __forceinline__ void layer_loop(const StackParams &p, const Lds &l)
             reduce_rows(dn, l.st, [&](int v, float acc) {
                 const uint16_t r2 = f2h(h2f(f2h(acc)) + l.lres[v]);
                 l.lres[v] = h2f(r2);
-                publish(p.r2buf, dn.row_of(v), r2, tg);
+                publish(p.r2buf, d, dn.row_of(v), r2, tg);
                 if (last)
                     p.r_out[dn.row_of(v)] = r2;
             });
             __syncthreads();
-            if (t == 0)
-                publish_flag(flag_r2, b, tg);
+            publish_flag(flag_r2, nb, b, tg);
         }
         if (!STAGER && !last) {
             cur = map_of(p, 0, L + 1, b, nb);
