@@ -94,10 +94,10 @@ def build_stack(q4, torch, p, n_layers=None, device="cuda"):
 def time_dominant_kernel(q4, torch, stack, st, p, reps=3):
     """The gate_up matvec as the stack runs it (RMSNorm prologue, SiLU-multiply
     epilogue; the largest matrix of a layer), launched over the 32 layers'
-    gate_up weights back to back (a 906 MB rotation), each launch bracketed by
-    its own pair of HIP events on the stream it runs on. A device-side sleep
-    queued first keeps the stream busy while the launches are enqueued, so the
-    events see the kernels back to back rather than host launch latency."""
+    gate_up weights back to back (a 906 MB rotation). Each launch records its
+    own dispatch start and end on HIP events (q4_timer_arm: the kernel's
+    execution on the stream it runs on, as a profiler's kernel trace measures
+    it); the mean over the launches is returned."""
     d, f = p["d"], p["f"]
     x = st["r0"]
     gamma = st["gammas"][1][0]
@@ -105,19 +105,140 @@ def time_dominant_kernel(q4, torch, stack, st, p, reps=3):
     n = len(stack.layers)
     durs = []
     for _ in range(reps):
-        e0 = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-        e1 = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-        torch.cuda._sleep(20_000_000)
+        torch.cuda._sleep(20_000_000)  # keeps the stream busy while launches queue
         for L in range(n):
-            e0[L].record()
-            Wg, Sg = stack.layers[L][4], stack.layers[L][5]
-            q4.gemv_ex(Wg, Sg, x, y=y, kind=q4.EPI_SILU_MUL, norm_gamma=gamma, eps=p["eps"])
-            e1[L].record()
-        torch.cuda.synchronize()
-        durs += [e0[L].elapsed_time(e1[L]) * 1e3 for L in range(n)]
+            q4.timer_arm(L)
+            q4.gemv_ex(stack.layers[L][4], stack.layers[L][5], x, y=y, kind=q4.EPI_SILU_MUL,
+                       norm_gamma=gamma, eps=p["eps"])
+        durs += [q4.timer_read(L) for L in range(n)]
     us = float(np.mean(durs))
     bytes_per_launch = 2 * f * d * BPW
     return us, bytes_per_launch
+
+
+COUNTER_PROFILE = os.path.join(ROOT, "profiles", "traffic_gate_up_phi3.md")
+COPY_BYTES = 256 << 20  # plain device copy used to calibrate the byte counters
+
+
+def kernel_source_hash():
+    """Hash of the sources that define the dominant kernel: counters taken on an
+    older kernel are not reported for the current one."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("q4_gemv.hip", "q4_dequant.h", "q4_common.h"):
+        with open(os.path.join(ROOT, "int4_weight_only_q4_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_workload(q4, torch, stack, st, p):
+    """What the counter runs profile: a plain device copy of COPY_BYTES (three
+    times; it calibrates FETCH_SIZE / WRITE_SIZE), then the dominant kernel over
+    the 32 layers' gate_up weights, launched as time_dominant_kernel does."""
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("copy calibration done", file=sys.stderr, flush=True)
+    x, gamma = st["r0"], st["gammas"][1][0]
+    y = torch.empty(p["f"], dtype=torch.float16, device="cuda")
+    for L in range(len(stack.layers)):
+        q4.gemv_ex(stack.layers[L][4], stack.layers[L][5], x, y=y, kind=q4.EPI_SILU_MUL,
+                   norm_gamma=gamma, eps=p["eps"])
+    torch.cuda.synchronize()
+    print("dominant kernel launches done", file=sys.stderr, flush=True)
+
+
+def _counter_rows(d):
+    """(kernel name, counter value) rows of the rocprofv3 CSV counter output under d."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % d)
+    rows = []
+    for fn in files:
+        with open(fn) as fh:
+            for r in csv.DictReader(fh):
+                rows.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def summarize_counters(fetch_dir, write_dir):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the copy and of the dominant
+    kernel, the copy-calibrated HBM bytes per launch, written to COUNTER_PROFILE."""
+    res = {}
+    for cname, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _counter_rows(d) if r[1] == cname]
+        # the calibration copy is the largest copy dispatch of the run (weight
+        # uploads before it are smaller)
+        copy = sorted(v for k, _, v in rows if "copy" in k.lower())[-3:]
+        dom = [v for k, _, v in rows if "k_gemv<32, 3, 2, 1, 1>" in k]
+        if not copy or not dom:
+            raise SystemExit("%s: missing copy (%d) or dominant-kernel (%d) dispatches" % (
+                cname, len(copy), len(dom)))
+        copy_kib = float(np.median(copy))
+        factor = (COPY_BYTES / 1024.0) / copy_kib
+        res[cname] = dict(copy_kib=round(copy_kib, 1), factor=round(factor, 4),
+                          dominant_kib=round(float(np.mean(dom)), 1), dispatches=len(dom))
+    traffic = 1024.0 * (res["FETCH_SIZE"]["dominant_kib"] * res["FETCH_SIZE"]["factor"] +
+                        res["WRITE_SIZE"]["dominant_kib"] * res["WRITE_SIZE"]["factor"])
+    algo = 2 * PHI3["f"] * PHI3["d"] * BPW
+    rec = dict(kernel="gate_up 16384x3072 matvec (k_gemv<32, 3, 2, 1, 1>)",
+               source_hash=kernel_source_hash(), traffic_bytes_per_launch=int(traffic),
+               algorithmic_bytes_per_launch=int(algo), ratio=round(traffic / algo, 4), **res)
+    cmd = ("export REPO=$PWD && cd /tmp && export TMPDIR=/tmp && timeout -s KILL 150 "
+           "rocprofv3 --pmc {C} "
+           "--output-format csv -d $REPO/gpurun_out/pmc_{c} -o pmc -- "
+           "python3 $REPO/bench.py --counters")
+    text = [
+        "# HBM traffic of the dominant kernel: gate_up 16384x3072 matvec, Phi-3-mini stack",
+        "",
+        "Two counter runs (one counter group each), from the repository root on one MI355X:",
+        "",
+        "```",
+        cmd.format(C="FETCH_SIZE", c="fetch"),
+        cmd.format(C="WRITE_SIZE", c="write"),
+        "python3 bench.py --summarize-counters gpurun_out/pmc_fetch gpurun_out/pmc_write",
+        "```",
+        "",
+        "`bench.py --counters` runs a plain %d MiB device copy three times, then the "
+        "gate_up kernel over the 32 layers' weights (the launch `bench.py` times). Each "
+        "counter is scaled by (copy bytes / what the counter reads for the copy)." % (COPY_BYTES >> 20),
+        "",
+        "| counter | copy KiB | factor | gate_up KiB per dispatch | dispatches |",
+        "|---|---|---|---|---|",
+    ]
+    for cname in ("FETCH_SIZE", "WRITE_SIZE"):
+        r = res[cname]
+        text.append("| %s | %.1f | %.4f | %.1f | %d |" % (cname, r["copy_kib"], r["factor"],
+                                                        r["dominant_kib"], r["dispatches"]))
+    text += ["",
+             "Calibrated HBM bytes per launch: %d (algorithmic: %d, ratio %.3f)." % (
+                 int(traffic), int(algo), traffic / algo),
+             "",
+             "Machine-readable (read by bench.py; ignored once the kernel sources change):",
+             "",
+             json.dumps(rec), ""]
+    with open(COUNTER_PROFILE, "w") as fh:
+        fh.write("\n".join(text))
+    print(json.dumps(rec))
+
+
+def committed_traffic():
+    """Calibrated HBM bytes per launch of the dominant kernel from the committed
+    counter summary, or None if absent or taken on other kernel sources."""
+    try:
+        with open(COUNTER_PROFILE) as fh:
+            for line in fh:
+                if line.startswith("{"):
+                    rec = json.loads(line)
+                    if rec.get("source_hash") == kernel_source_hash():
+                        return int(rec["traffic_bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
 
 
 def verify_one_token(q4, torch, stack, st, p, o, layers_checked=(0, 1)):
@@ -173,7 +294,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--counters", action="store_true",
+                    help="run only the workload of the rocprofv3 counter passes")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the traffic summary from two rocprofv3 --pmc CSV outputs")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: the int4 decode path is built and timed on a single "
               "MI355X (multi-GPU sharding is a design note, not part of this build); "
@@ -190,6 +318,9 @@ def main():
         p["layers"], stack_weight_bytes(p) / 1e9), file=sys.stderr, flush=True)
     stack, st = build_stack(q4, torch, p)
     torch.cuda.synchronize()
+    if args.counters:
+        counter_workload(q4, torch, stack, st, p)
+        return
 
     import oracle
     o = oracle.load()
@@ -260,7 +391,7 @@ def main():
             "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
             "us_per_launch": round(dom_us, 3),
             "bytes_per_launch": int(dom_bytes),
-            "traffic": None,
+            "traffic": committed_traffic(),
         },
     }
     if not args.no_cpu_baseline:

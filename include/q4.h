@@ -239,6 +239,16 @@ q4_status q4_stack_decode(const q4_stack_desc *desc, const uint16_t *r_in,
  * reported here as Q4_EHIP, once). Q4_OK otherwise. */
 q4_status q4_stack_status(q4_stream stream);
 
+/* Measurement hook (not part of the method): q4_timer_arm(slot) makes the next
+ * matvec kernel that this thread launches through libq4 record its dispatch
+ * start and end (the kernel's own execution, as a profiler's kernel trace
+ * sees it) on the slot's library-owned HIP events; q4_timer_read(slot, &us)
+ * waits for that launch and returns its duration in microseconds. slot: 0..63,
+ * per thread. Q4_EINVAL for a bad slot or a slot never armed and launched. A
+ * slot armed while another is armed replaces it. */
+q4_status q4_timer_arm(int slot);
+q4_status q4_timer_read(int slot, float *us);
+
 #ifdef __cplusplus
 }
 #endif

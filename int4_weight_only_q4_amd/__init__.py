@@ -33,7 +33,7 @@ BYTES_PER_WEIGHT = 0.5 + 2.0 / 32.0
 ABI_SYMBOLS = (
     "q4_version", "q4_last_error", "q4_bytes_per_weight", "q4_pack", "q4_unpack", "q4_gemv",
     "q4_gemv_batched", "q4_moe_gemv", "q4_add_rmsnorm", "q4_silu_mul", "q4_gemv_ex",
-    "q4_stack_decode", "q4_stack_status",
+    "q4_stack_decode", "q4_stack_status", "q4_timer_arm", "q4_timer_read",
 )
 
 
@@ -74,6 +74,8 @@ _SIGS = {
     "q4_gemv_ex": (C.c_int, [_P, _P, _P, _P, _I, _I, C.POINTER(Epilogue), _P]),
     "q4_stack_decode": (C.c_int, [C.POINTER(StackDesc), _P, _P, _P, _P, _P, _P]),
     "q4_stack_status": (C.c_int, [_P]),
+    "q4_timer_arm": (C.c_int, [C.c_int]),
+    "q4_timer_read": (C.c_int, [C.c_int, C.POINTER(C.c_float)]),
 }
 
 _lib = None
@@ -264,6 +266,19 @@ class Stack:
 def stack_status(stream=None):
     """Synchronise and raise if a persistent stack kernel timed out waiting."""
     _check(lib().q4_stack_status(_stream(stream)))
+
+
+def timer_arm(slot):
+    """Measurement hook: the next matvec kernel this thread launches records
+    its dispatch start and end on timer `slot` (0..63)."""
+    _check(lib().q4_timer_arm(int(slot)))
+
+
+def timer_read(slot):
+    """Duration in microseconds of the launch timed on `slot` (waits for it)."""
+    us = C.c_float()
+    _check(lib().q4_timer_read(int(slot), C.byref(us)))
+    return float(us.value)
 
 
 def stack_decode(stack: Stack, r_in, h_in, r_out, h_out, trace=None, stream=None):

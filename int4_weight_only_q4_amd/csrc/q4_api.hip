@@ -16,6 +16,15 @@ namespace q4 {
 
 namespace {
 thread_local char g_err[512] = "";
+
+// q4_timer_arm / q4_timer_read state, per thread
+constexpr int kTimerSlots = 64;
+struct TimerSlot {
+    hipEvent_t start = nullptr, stop = nullptr;
+    bool launched = false;
+};
+thread_local TimerSlot g_timers[kTimerSlots];
+thread_local int g_armed = -1;
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, std::pair<void *, size_t>> g_ws;
 }  // namespace
@@ -27,6 +36,18 @@ q4_status fail(q4_status st, const char *fmt, ...)
     vsnprintf(g_err, sizeof(g_err), fmt, ap);
     va_end(ap);
     return st;
+}
+
+bool take_armed_timer(hipEvent_t *start, hipEvent_t *stop)
+{
+    if (g_armed < 0)
+        return false;
+    TimerSlot &t = g_timers[g_armed];
+    g_armed = -1;
+    *start = t.start;
+    *stop = t.stop;
+    t.launched = true;
+    return true;
 }
 
 q4_status check_launch(const char *what)
@@ -388,6 +409,35 @@ extern "C" {
 const char *q4_version(void) { return "libq4 0.1 (gfx950)"; }
 
 const char *q4_last_error(void) { return g_err; }
+
+q4_status q4_timer_arm(int slot)
+{
+    if (slot < 0 || slot >= q4::kTimerSlots)
+        return fail(Q4_EINVAL, "timer slot %d outside 0..%d", slot, q4::kTimerSlots - 1);
+    q4::TimerSlot &t = q4::g_timers[slot];
+    if (!t.start) {
+        Q4_HIP(hipEventCreate(&t.start));
+        Q4_HIP(hipEventCreate(&t.stop));
+    }
+    t.launched = false;
+    q4::g_armed = slot;
+    return Q4_OK;
+}
+
+q4_status q4_timer_read(int slot, float *us)
+{
+    if (slot < 0 || slot >= q4::kTimerSlots || !us)
+        return fail(Q4_EINVAL, "timer slot %d outside 0..%d or NULL output", slot,
+                    q4::kTimerSlots - 1);
+    q4::TimerSlot &t = q4::g_timers[slot];
+    if (!t.launched)
+        return fail(Q4_EINVAL, "timer slot %d was not armed for a launch", slot);
+    Q4_HIP(hipEventSynchronize(t.stop));
+    float ms = 0.f;
+    Q4_HIP(hipEventElapsedTime(&ms, t.start, t.stop));
+    *us = ms * 1e3f;
+    return Q4_OK;
+}
 
 double q4_bytes_per_weight(void) { return 4.0 / 8.0 + 2.0 / 32.0; }
 

@@ -28,6 +28,10 @@ q4_status fail(q4_status st, const char *fmt, ...);
 // Launch check: hipGetLastError after a kernel launch.
 q4_status check_launch(const char *what);
 
+// The events armed by q4_timer_arm for this thread's next matvec launch
+// (disarms them), or false if none is armed.
+bool take_armed_timer(hipEvent_t *start, hipEvent_t *stop);
+
 // Library-owned scratch for one (device, stream): at least `bytes` bytes. Its
 // first kWsHeader bytes are reserved (zero-initialised counters); callers place
 // their own data after them. Returns nullptr (and sets the error) on failure.

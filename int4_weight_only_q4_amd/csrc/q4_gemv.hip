@@ -20,6 +20,8 @@
 //    scale in f32. A one-hot x therefore reproduces (c - 7) * s exactly.
 //  * The LPR partial sums of a row are combined with an xor butterfly in a
 //    fixed order, so results are identical run to run.
+#include <hip/hip_ext.h>
+
 #include "q4_dequant.h"
 #include "q4_stack.h"
 
@@ -231,7 +233,12 @@ q4_status run_gemv(const GemvParams &p, hipStream_t st)
     const int rb = EPI == EPI_SILU ? RB / 2 : RB;
     const int blocks = (rows + rb - 1) / rb;
     const size_t lds = (size_t)p.G * 32 * 2 + (size_t)p.G * 4;
-    hipLaunchKernelGGL((k_gemv<LPR, NG, RPS, EPI, PRO>), dim3(blocks), dim3(256), lds, st, p);
+    hipEvent_t t0, t1;
+    if (take_armed_timer(&t0, &t1))
+        hipExtLaunchKernelGGL((k_gemv<LPR, NG, RPS, EPI, PRO>), dim3(blocks), dim3(256), lds, st,
+                              t0, t1, 0, p);
+    else
+        hipLaunchKernelGGL((k_gemv<LPR, NG, RPS, EPI, PRO>), dim3(blocks), dim3(256), lds, st, p);
     return check_launch("k_gemv");
 }
 

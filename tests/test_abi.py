@@ -169,3 +169,14 @@ def test_pack_validation():
     assert status("q4_pack", X, A, 4, 40, None) == q4.Q4_ESHAPE
     assert status("q4_pack", X, A + 4, 4, 64, None) == q4.Q4_EALIGN
     assert status("q4_pack", X, X + 16, 4, 64, None) == q4.Q4_EALIAS
+
+
+def test_timer_validation():
+    L = q4.lib()
+    assert L.q4_timer_arm(-1) == q4.Q4_EINVAL
+    assert L.q4_timer_arm(64) == q4.Q4_EINVAL
+    us = C.c_float()
+    assert L.q4_timer_read(64, C.byref(us)) == q4.Q4_EINVAL
+    assert L.q4_timer_read(3, None) == q4.Q4_EINVAL
+    # slot 7 was never armed for a launch on this thread
+    assert L.q4_timer_read(7, C.byref(us)) == q4.Q4_EINVAL

@@ -182,3 +182,22 @@ def test_gate_rejects_a_wrong_reference(o, q4, mutant):
     assert within(y, o.gemv(W, S, x))
     bad = oracle_pins.mutant(mutant)
     assert not within(y, bad.gemv(W, S, x))
+
+
+def test_dispatch_timer_measures_the_matvec(o, q4):
+    """q4_timer_arm makes the next matvec record its own start and end: the
+    duration is positive and plausible, the output is unchanged, and a slot is
+    consumed by one launch only."""
+    import torch
+    codes, W, S = make(o, 900, 3072, 3072)
+    x = datagen.activations(902, 1, 3072)[0]
+    Wd, Sd, xd = dev_tensor(W), dev_tensor(S), dev_tensor(x)
+    plain = q4.gemv(Wd, Sd, xd)
+    q4.timer_arm(5)
+    timed = q4.gemv(Wd, Sd, xd)
+    untimed = q4.gemv(Wd, Sd, xd)  # the slot is disarmed after one launch
+    us = q4.timer_read(5)
+    torch.cuda.synchronize()
+    assert 0.1 < us < 10_000
+    assert np.array_equal(bits(plain), bits(timed))
+    assert np.array_equal(bits(plain), bits(untimed))
