@@ -241,6 +241,156 @@ def committed_traffic():
     return None
 
 
+GEMV_TABLE_PROFILE = os.path.join(ROOT, "profiles", "gemv_table_phi3_qwen3_moe.md")
+QWEN3 = dict(qkv=(6144, 2560), o=(2560, 4096), gate_up=(19456, 2560), down=(2560, 9728),
+             lm_head=(151936, 2560))
+
+
+def _rotation(torch, n, k, seed, min_bytes=512 << 20):
+    """Distinct device copies of one seeded n x k matrix, together more than
+    min_bytes, so that cycling through them reads HBM rather than the 256 MB
+    Infinity Cache."""
+    W = torch.from_numpy(datagen.words(seed, n, k).view(np.int32)).cuda()
+    S = torch.from_numpy(datagen.scales(seed + 1, n, k)).cuda()
+    copies = max(2, -(-min_bytes // int(n * k * BPW)))
+    return [(W, S)] + [(W.clone(), S.clone()) for _ in range(copies - 1)]
+
+
+def _time(q4, torch, launch, count, timed_kernels=True):
+    """(us per call back to back, us per matvec kernel from its dispatch events)."""
+    for i in range(4):
+        launch(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(10_000_000)
+    e0.record()
+    for i in range(count):
+        launch(i)
+    e1.record()
+    torch.cuda.synchronize()
+    per_call = e0.elapsed_time(e1) * 1e3 / count
+    per_kernel = None
+    if timed_kernels:
+        n = min(count, 64)
+        torch.cuda._sleep(10_000_000)
+        for i in range(n):
+            q4.timer_arm(i)
+            launch(i)
+        per_kernel = float(np.mean([q4.timer_read(i) for i in range(n)]))
+    return per_call, per_kernel
+
+
+def gemv_table(q4, torch):
+    """Per-GEMV throughput at the single-GEMV, Phi-3-mini, Qwen3-4B (M = 1 and
+    8) and MoE workloads, weights rotated past the Infinity Cache."""
+    rows = []
+    base = datagen.SEED_BASE + 5_000_000
+
+    def add(workload, shape, m, weight_bytes, launch, count=200, note=""):
+        call_us, kern_us = _time(q4, torch, launch, count)
+        us = kern_us if kern_us is not None else call_us
+        gbs = weight_bytes / (us * 1e-6) / 1e9
+        rows.append(dict(workload=workload, shape=shape, m=m, weight_bytes=int(weight_bytes),
+                         us_kernel=round(kern_us, 3) if kern_us is not None else None,
+                         us_per_call=round(call_us, 3), gbs=round(gbs, 1),
+                         pct_peak=round(100 * gbs / HBM_PEAK_GBS, 1), note=note))
+        print("  %-22s %-12s M=%-2d %8.3f us/kernel %8.3f us/call %8.1f GB/s" % (
+            workload, shape, m, us, call_us, gbs), file=sys.stderr, flush=True)
+
+    def gemv_rows(workload, shapes, ms, seed0):
+        for j, (name, (n, k)) in enumerate(shapes):
+            rot = _rotation(torch, n, k, seed0 + 10 * j)
+            wb = n * k * BPW
+            for m in ms:
+                x = torch.from_numpy(datagen.activations(seed0 + 10 * j + 2, m, k)).cuda()
+                y = torch.empty((m, n), dtype=torch.float16, device="cuda")
+                if m == 1:
+                    def launch(i, rot=rot, x=x, y=y):
+                        W, S = rot[i % len(rot)]
+                        q4.gemv(W, S, x[0], y=y[0])
+                else:
+                    def launch(i, rot=rot, x=x, y=y):
+                        W, S = rot[i % len(rot)]
+                        q4.gemv_batched(W, S, x, y=y)
+                add(workload, "%s %dx%d" % (name, n, k), m, wb, launch,
+                    count=max(20, min(200, int(4e9 / wb))))
+            del rot
+            torch.cuda.empty_cache()
+
+    gemv_rows("single GEMV", [("W", (512, 256))], [1], base)
+    gemv_rows("Phi-3-mini layer", [("QKV", (9216, 3072)), ("O", (3072, 3072)),
+                                   ("gate_up", (16384, 3072)), ("down", (3072, 8192))], [1],
+              base + 1000)
+    gemv_rows("Qwen3-4B", list(QWEN3.items()), [1, 8], base + 2000)
+
+    # MoE layer: 128 experts, top-8; gate_up stage (SiLU-multiply) + down stage
+    # with the routing-weighted combine. Two copies of the expert stack are
+    # alternated and the routing is drawn from a pool of 256, so the touched
+    # experts are not hot in cache; GB/s counts the unique experts touched.
+    E, hidden, f, topk = 128, 2048, 768, 8
+    stacks = []
+    for c in range(2):
+        Wg = torch.from_numpy(datagen.words(base + 3000 + c, E * 2 * f, hidden)
+                              .view(np.int32).reshape(E, 2 * f, hidden // 8)).cuda()
+        Sg = torch.from_numpy(datagen.scales(base + 3100 + c, E * 2 * f, hidden)
+                              .reshape(E, 2 * f, hidden // 32)).cuda()
+        Wd = torch.from_numpy(datagen.words(base + 3200 + c, E * hidden, f)
+                              .view(np.int32).reshape(E, hidden, f // 8)).cuda()
+        Sd = torch.from_numpy(datagen.scales(base + 3300 + c, E * hidden, f)
+                              .reshape(E, hidden, f // 32)).cuda()
+        stacks.append((Wg, Sg, Wd, Sd))
+    expert_bytes = (2 * f * hidden + hidden * f) * BPW
+    for t in (1, 4, 16):
+        ids_h, w_h = datagen.routing_pool(base + 4000 + t, 256, t, E, topk)
+        ids = torch.from_numpy(ids_h).cuda()
+        rw = torch.from_numpy(w_h).cuda()
+        x = torch.from_numpy(datagen.activations(base + 4100 + t, t, hidden)).cuda()
+        uniq = float(np.mean([len(np.unique(ids_h[i])) for i in range(len(ids_h))]))
+
+        def launch(i, ids=ids, rw=rw, x=x):
+            Wg, Sg, Wd, Sd = stacks[i & 1]
+            u = q4.moe_gemv(Wg, Sg, ids[i % 256], x, ldx=hidden, x_slot_stride=0, epi_silu=True)
+            q4.moe_gemv(Wd, Sd, ids[i % 256], u, ldx=topk * f, x_slot_stride=f,
+                        route_w=rw[i % 256])
+
+        call_us, _ = _time(q4, torch, launch, 200, timed_kernels=False)
+        wb = uniq * expert_bytes
+        gbs = wb / (call_us * 1e-6) / 1e9
+        rows.append(dict(workload="MoE layer (128 experts, top-8)", shape="T=%d" % t, m=t,
+                         weight_bytes=int(wb), us_kernel=None, us_per_call=round(call_us, 3),
+                         gbs=round(gbs, 1), pct_peak=round(100 * gbs / HBM_PEAK_GBS, 1),
+                         note="%.2f unique experts per layer on average; time of both stages "
+                              "(5 kernels) back to back" % uniq))
+        print("  MoE T=%-2d %8.3f us/layer %8.1f GB/s (unique experts %.2f)" % (
+            t, call_us, gbs, uniq), file=sys.stderr, flush=True)
+    return rows
+
+
+def write_gemv_table(rows):
+    text = ["# Per-GEMV throughput: single GEMV, Phi-3-mini, Qwen3-4B (M = 1, 8) and MoE shapes",
+            "",
+            "Command (from the repository root, on one MI355X): `python3 bench.py --gemv-table`",
+            "",
+            "Weights are seeded synthetic int4 group-32 (codes U{0..15}, scales U[0.005, 0.05]); "
+            "each matrix is cycled through enough distinct device copies to exceed 512 MB, so "
+            "HBM, not the 256 MB Infinity Cache, is measured. `us/kernel` is the matvec "
+            "kernel's own dispatch time (q4_timer_arm events, mean of 64 launches); `us/call` "
+            "is the time per call of 20-200 calls back to back (one event pair, includes "
+            "the gaps between launches). GB/s = weight bytes (0.5625 B per weight) / "
+            "us/kernel (us/call for the MoE layer, which is 5 kernels).",
+            "",
+            "| workload | shape | M | weight bytes | us/kernel | us/call | GB/s | % of 8 TB/s | note |",
+            "|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        text.append("| %s | %s | %d | %d | %s | %.3f | %.1f | %.1f | %s |" % (
+            r["workload"], r["shape"], r["m"], r["weight_bytes"],
+            "%.3f" % r["us_kernel"] if r["us_kernel"] is not None else "",
+            r["us_per_call"], r["gbs"], r["pct_peak"], r["note"]))
+    text.append("")
+    with open(GEMV_TABLE_PROFILE, "w") as fh:
+        fh.write("\n".join(text))
+
+
 def verify_one_token(q4, torch, stack, st, p, o, layers_checked=(0, 1)):
     """Teacher-forced check of single layers of one token against the oracle."""
     d = p["d"]
@@ -294,6 +444,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--gemv-table", action="store_true",
+                    help="measure the per-GEMV table (Phi-3, Qwen3 M=1/8, MoE) and exit")
     ap.add_argument("--counters", action="store_true",
                     help="run only the workload of the rocprofv3 counter passes")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -313,6 +465,11 @@ def main():
 
     q4.lib()
     assert torch.cuda.is_available(), "no GPU"
+    if args.gemv_table:
+        rows = gemv_table(q4, torch)
+        write_gemv_table(rows)
+        print(json.dumps({"gemv_table": rows}), flush=True)
+        return
     p = PHI3
     print("building the %d-layer stack (%.3f GB of int4 weights)..." % (
         p["layers"], stack_weight_bytes(p) / 1e9), file=sys.stderr, flush=True)

@@ -1,6 +1,7 @@
 // Internal helpers of libq4 (gfx950). Not part of the C ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -31,6 +32,18 @@ q4_status check_launch(const char *what);
 // The events armed by q4_timer_arm for this thread's next matvec launch
 // (disarms them), or false if none is armed.
 bool take_armed_timer(hipEvent_t *start, hipEvent_t *stop);
+
+// Launch of a matvec kernel: with the armed timer's events (the dispatch
+// records its own start and end) when q4_timer_arm armed them, plainly
+// otherwise. Wrap a templated kernel name in parentheses.
+#define Q4_LAUNCH_MATVEC(kernel, grid, block, lds, stream, ...)                               \
+    do {                                                                                  \
+        hipEvent_t t0_, t1_;                                                              \
+        if (::q4::take_armed_timer(&t0_, &t1_))                                           \
+            hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, t0_, t1_, 0, __VA_ARGS__); \
+        else                                                                              \
+            hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);            \
+    } while (0)
 
 // Library-owned scratch for one (device, stream): at least `bytes` bytes. Its
 // first kWsHeader bytes are reserved (zero-initialised counters); callers place
@@ -86,6 +99,9 @@ struct GemvOp {
     uint16_t *res_out = nullptr;
 };
 q4_status launch_gemv_op(const GemvOp &op, hipStream_t stream);
+// M >= 2 rows on the matrix cores (q4_mfma.hip)
+q4_status launch_gemv_mfma(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
+                           uint16_t *y, int64_t ldy, int N, int K, int M, hipStream_t stream);
 q4_status launch_gemv_batched(const uint32_t *W, const uint16_t *S, const uint16_t *x,
                               int64_t ldx, uint16_t *y, int64_t ldy, int N, int K, int M,
                               hipStream_t stream);

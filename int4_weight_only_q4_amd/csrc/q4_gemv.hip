@@ -20,8 +20,6 @@
 //    scale in f32. A one-hot x therefore reproduces (c - 7) * s exactly.
 //  * The LPR partial sums of a row are combined with an xor butterfly in a
 //    fixed order, so results are identical run to run.
-#include <hip/hip_ext.h>
-
 #include "q4_dequant.h"
 #include "q4_stack.h"
 
@@ -233,12 +231,7 @@ q4_status run_gemv(const GemvParams &p, hipStream_t st)
     const int rb = EPI == EPI_SILU ? RB / 2 : RB;
     const int blocks = (rows + rb - 1) / rb;
     const size_t lds = (size_t)p.G * 32 * 2 + (size_t)p.G * 4;
-    hipEvent_t t0, t1;
-    if (take_armed_timer(&t0, &t1))
-        hipExtLaunchKernelGGL((k_gemv<LPR, NG, RPS, EPI, PRO>), dim3(blocks), dim3(256), lds, st,
-                              t0, t1, 0, p);
-    else
-        hipLaunchKernelGGL((k_gemv<LPR, NG, RPS, EPI, PRO>), dim3(blocks), dim3(256), lds, st, p);
+    Q4_LAUNCH_MATVEC((k_gemv<LPR, NG, RPS, EPI, PRO>), dim3(blocks), dim3(256), lds, st, p);
     return check_launch("k_gemv");
 }
 
@@ -361,113 +354,15 @@ q4_status launch_gemv(const uint32_t *W, const uint16_t *S, const uint16_t *x, u
     }
 }
 
-// ---------------------------------------------------------------------------
-// Batched matvec (M activation rows share each weight load). First version:
-// VALU dot2 path; each wave owns one row, weights stay in registers for all
-// M rows, activations are staged in LDS MB rows at a time.
-// ---------------------------------------------------------------------------
-namespace {
-
-constexpr int kBatchNG = 12;  // groups per lane (LPR = 64): K <= 24576
-
-template <int MB>
-__global__ __launch_bounds__(256) void k_gemv_batched(const uint4 *__restrict__ W,
-                                                      const uint16_t *__restrict__ S,
-                                                      const uint16_t *__restrict__ x, int64_t ldx,
-                                                      uint16_t *__restrict__ y, int64_t ldy, int N,
-                                                      int G, int M)
-{
-    extern __shared__ uint4 smem[];
-    const int K = G * 32;
-    const int stride = (K >> 3) + ((G + 3) >> 2);  // uint4 per staged row
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int row = blockIdx.x * kWaves + wave;
-    const bool ok = row < N;
-    const int rrow = ok ? row : 0;
-    const int ng = (G + 63) >> 6;
-
-    uint4 wv[kBatchNG];
-    uint32_t sv[kBatchNG];
-#pragma unroll
-    for (int i = 0; i < kBatchNG; ++i) {
-        // branch-free (see k_gemv): lanes past the last group re-read group G - 1
-        const size_t off = (size_t)rrow * G + min(lane + 64 * i, G - 1);
-        wv[i] = load_weights(W + off);
-        sv[i] = load_scale(S + off);
-    }
-
-    for (int m0 = 0; m0 < M; m0 += MB) {
-        const int mb = min(MB, M - m0);
-        __syncthreads();
-        for (int m = 0; m < mb; ++m) {
-            uint4 *xs = smem + m * stride;
-            stage_activation(x + (int64_t)(m0 + m) * ldx, K, xs,
-                             reinterpret_cast<float *>(xs + (K >> 3)));
-        }
-        __syncthreads();
-        float acc[MB];
-#pragma unroll
-        for (int m = 0; m < MB; ++m)
-            acc[m] = 0.f;
-#pragma unroll
-        for (int i = 0; i < kBatchNG; ++i) {
-            const int g = lane + 64 * i;
-            if (i < ng && g < G) {
-#pragma unroll
-                for (int m = 0; m < MB; ++m) {
-                    if (m < mb) {
-                        const uint4 *xs = smem + m * stride;
-                        const float *cs = reinterpret_cast<const float *>(xs + (K >> 3));
-                        acc[m] = fmaf(h2f(sv[i]), group_dot(wv[i], xs, g, cs[g]), acc[m]);
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < MB; ++m) {
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1)
-                acc[m] += __shfl_xor(acc[m], off, 64);
-            if (lane == 0 && ok && m < mb)
-                y[(int64_t)(m0 + m) * ldy + row] = f2h(acc[m]);
-        }
-    }
-}
-
-}  // namespace
-
+// Batched matvec: M = 1 is the matvec above; M >= 2 rows share each weight
+// read on the matrix cores (q4_mfma.hip).
 q4_status launch_gemv_batched(const uint32_t *W, const uint16_t *S, const uint16_t *x,
                               int64_t ldx, uint16_t *y, int64_t ldy, int N, int K, int M,
                               hipStream_t stream)
 {
-    const int G = K / 32;
-    const size_t row_bytes = ((size_t)(K >> 3) + (size_t)((G + 3) >> 2)) * 16;
-    const size_t budget = 60 * 1024;
-    int mb = 8;
-    while (mb > 1 && (size_t)mb * row_bytes > budget)
-        mb >>= 1;
-    const int blocks = (N + kWaves - 1) / kWaves;
-    const size_t lds = (size_t)mb * row_bytes;
-    const uint4 *W4 = reinterpret_cast<const uint4 *>(W);
-    switch (mb) {
-    case 8:
-        hipLaunchKernelGGL(k_gemv_batched<8>, dim3(blocks), dim3(256), lds, stream, W4, S, x, ldx,
-                           y, ldy, N, G, M);
-        break;
-    case 4:
-        hipLaunchKernelGGL(k_gemv_batched<4>, dim3(blocks), dim3(256), lds, stream, W4, S, x, ldx,
-                           y, ldy, N, G, M);
-        break;
-    case 2:
-        hipLaunchKernelGGL(k_gemv_batched<2>, dim3(blocks), dim3(256), lds, stream, W4, S, x, ldx,
-                           y, ldy, N, G, M);
-        break;
-    default:
-        hipLaunchKernelGGL(k_gemv_batched<1>, dim3(blocks), dim3(256), lds, stream, W4, S, x, ldx,
-                           y, ldy, N, G, M);
-        break;
-    }
-    return check_launch("k_gemv_batched");
+    if (M == 1)  // a single row is the bandwidth-bound matvec
+        return launch_gemv(W, S, x, y, N, K, EpiArgs{}, stream);
+    return launch_gemv_mfma(W, S, x, ldx, y, ldy, N, K, M, stream);
 }
 
 }  // namespace q4

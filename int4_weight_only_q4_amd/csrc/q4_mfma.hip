@@ -1,0 +1,244 @@
+// Batched int4 x f16 matvec on the gfx950 matrix cores: M = 2..16 activation
+// rows share one read of the weights (more rows: one launch per 16).
+//
+// What is computed is the group-quantised matvec of the Zero TVM Documentation
+// ("Q4F16 quantization format"; the batched decode of "WGSL Kernel Roles"):
+// y[m][n] = sum_k (q[n][k] - 7) * s[n][k/32] * x[m][k]. At M >= 2 the shared
+// weight read makes it a small dense contraction, so it runs on
+// v_mfma_f32_16x16x32_f16 (one MFMA = 16 activation rows x 16 weight rows x
+// one 32-element quantisation group):
+//  * the B operand is the weights, dequantised to binary16: f16((q - 7) * s).
+//    Codes become exact binary16 integers 1024 + q through the exponent
+//    pattern 0x6400, 1031 is subtracted exactly, and the product with the
+//    scale is rounded once (round to nearest even). Accumulation is f32 in the
+//    matrix core;
+//  * the A operand is the activation, staged once per workgroup in LDS; rows
+//    m >= M of the MFMA tile are never stored;
+//  * a lane (row n = lane % 16, k-block kb = lane / 16) loads one 16-byte
+//    group of its row per step (four consecutive groups per wave and step, 64
+//    bytes contiguous per row), and MFMA t of the step takes word t of that
+//    group: lane (., kb) of both operands then covers k = 32 (g0 + kb) + 8 t +
+//    0..7, so A and B agree on every k and each 16-byte load feeds four MFMAs;
+//  * about three workgroups per CU stay resident: each stages its activation
+//    chunk once and its waves then loop over 16-row tiles, a tile's 8 KB of
+//    weights in flight per wave (an activation staging per tile would queue
+//    behind the other workgroups' weight loads on the CU);
+//  * K is split into chunks of 1024 values (the staged activation);
+//    the f32 partials are summed by a second kernel in a fixed order, so
+//    results are identical run to run.
+#include <algorithm>
+
+#include "q4_dequant.h"
+
+namespace q4 {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;            // 16 weight rows per wave
+constexpr int kRowsPerWg = 16 * kWaves;
+constexpr int kDepth = 8;            // steps (4 groups each) per tile = weight loads in flight
+constexpr int kGroupsPerSplit = 4 * kDepth;  // K chunk per workgroup: 1024 values
+constexpr int kMTile = 16;           // activation rows per launch
+constexpr int kXq = (kMTile * kGroupsPerSplit * 4 + 255) / 256;  // x chunks per thread
+constexpr int kMaxTilesPerWave = 8;  // finished tiles wait in LDS until the loop ends
+
+// The 8 codes of word w as binary16 (q - 7) * s, in element order.
+__device__ __forceinline__ half8 dequant_word(uint32_t w, half2v s2)
+{
+    const half2v c1031 = {(_Float16)1031.0f, (_Float16)1031.0f};
+    half8 b;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t u = w >> (8 * p);
+        const uint32_t bits = (u & 0xFu) | ((u & 0xF0u) << 12) | 0x64006400u;
+        const half2v h = (__builtin_bit_cast(half2v, bits) - c1031) * s2;
+        b[2 * p] = h[0];
+        b[2 * p + 1] = h[1];
+    }
+    return b;
+}
+
+__device__ __forceinline__ uint32_t word(const uint4 &v, int t)
+{
+    return t == 0 ? v.x : (t == 1 ? v.y : (t == 2 ? v.z : v.w));
+}
+
+// grid (P, KS), 256 threads. Split ks covers groups [ks * gc, min(G, (ks + 1) *
+// gc)), gc = kGroupsPerSplit; its activation chunk is staged once, then wave w
+// of workgroup b takes the 16-row tiles b * 4 + w, + 4 P, ... one after
+// another. KS == 1: y written; else
+// f32 partials part[ks][m][n] for the combine kernel.
+__global__ __launch_bounds__(256) void k_gemv_mfma(const uint4 *__restrict__ W,
+                                                   const uint16_t *__restrict__ S,
+                                                   const uint16_t *__restrict__ x, int64_t ldx,
+                                                   uint16_t *__restrict__ y, int64_t ldy,
+                                                   float *__restrict__ part, int N, int G, int M,
+                                                   int gc)
+{
+    extern __shared__ uint4 smem[];
+    const int t = threadIdx.x, l = t & 63, wave = t >> 6;
+    const int ks = blockIdx.y, KS = gridDim.y;
+    const int g0 = ks * gc, gn = min(gc, G - g0);  // groups of this split, >= 1
+    const int xstride = gc * 32 + 8;  // staged row: the chunk plus 16 bytes against bank conflicts
+    // LDS: finished tiles [kWaves][kMaxTilesPerWave][64 lanes] float4, then the activation
+    floatx4 *obuf = reinterpret_cast<floatx4 *>(smem);
+    _Float16 *xs = reinterpret_cast<_Float16 *>(smem + kWaves * kMaxTilesPerWave * 64);
+    const int cpr = gn * 4;           // 16-byte chunks per staged row
+
+    // 1. the activation chunk (all loads issued together, then stored)
+    uint4 xr[kXq];
+#pragma unroll
+    for (int q = 0; q < kXq; ++q) {
+        const int c = min(t + 256 * q, M * cpr - 1);  // branch-free: the tail re-reads
+        const int m = c / cpr, j = c - m * cpr;
+        xr[q] = *reinterpret_cast<const uint4 *>(x + m * ldx + (int64_t)g0 * 32 + 8 * j);
+    }
+#pragma unroll
+    for (int q = 0; q < kXq; ++q) {
+        const int c = min(t + 256 * q, M * cpr - 1);  // the tail rewrites the last chunk
+        const int m = c / cpr, j = c - m * cpr;
+        *reinterpret_cast<uint4 *>(xs + m * xstride + 8 * j) = xr[q];
+    }
+    __syncthreads();
+
+    // 2. this wave's tiles, one after another. A tile's 8 steps of weights
+    //    (16 loads per lane) are issued together and consumed in the same
+    //    iteration; the resident waves of the CU (12 to 16) overlap one
+    //    another's loads. (Loads kept in flight across iterations make the
+    //    compiler copy, and so wait for, them at the loop edge.)
+    const int ntiles = (N + 15) >> 4;
+    const int tstride = gridDim.x * kWaves;
+    const int tile0 = blockIdx.x * kWaves + wave;
+    const int my_tiles = tile0 < ntiles ? (ntiles - 1 - tile0) / tstride + 1 : 0;
+    const int n = l & 15, kb = l >> 4;
+    const int m = l & 15;
+    const bool mok = m < M;
+    for (int j = 0; j < my_tiles; ++j) {
+        const size_t rb = (size_t)min((tile0 + j * tstride) * 16 + n, N - 1) * G + g0;
+        uint4 wq[kDepth];
+        uint32_t sq[kDepth];
+#pragma unroll
+        for (int p = 0; p < kDepth; ++p) {
+            const int gi = min(4 * p + kb, gn - 1);
+            wq[p] = load_weights(W + rb + gi);
+            sq[p] = load_scale(S + rb + gi);
+        }
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < kDepth; ++p) {
+            const int gi = 4 * p + kb;
+            const _Float16 *xa = xs + m * xstride + min(gi, gn - 1) * 32;
+            half8 a[4], b[4];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)  // the four activation reads first
+                a[tt] = mok ? *reinterpret_cast<const half8 *>(xa + 8 * tt) : half8{};
+            const uint16_t s16 = gi < gn ? (uint16_t)sq[p] : (uint16_t)0;
+            const _Float16 sh = __builtin_bit_cast(_Float16, s16);
+            const half2v s2 = {sh, sh};
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+                b[tt] = dequant_word(word(wq[p], tt), s2);
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[tt], b[tt], acc, 0, 0, 0);
+        }
+        // park the finished tile in LDS: a global store here would count
+        // against the next tile's weight loads
+        obuf[(wave * kMaxTilesPerWave + j) * 64 + l] = acc;
+    }
+
+    // 4. write this wave's tiles: lane holds D[4 * (l / 16) + r][l % 16]
+    for (int j = 0; j < my_tiles; ++j) {
+        const floatx4 d = obuf[(wave * kMaxTilesPerWave + j) * 64 + l];
+        const int col = (tile0 + j * tstride) * 16 + n;
+        if (col < N)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int mr = 4 * kb + r;
+                if (mr < M) {
+                    if (KS == 1)
+                        y[mr * ldy + col] = f2h(d[r]);
+                    else
+                        part[((size_t)ks * M + mr) * N + col] = d[r];
+                }
+            }
+    }
+}
+
+// y[m][n] = f16(sum over ks, in order, of part[ks][m][n])
+__global__ __launch_bounds__(256) void k_combine(const float *__restrict__ part, int KS, int M,
+                                                 int N, uint16_t *__restrict__ y, int64_t ldy)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)M * N)
+        return;
+    const int mr = (int)(i / N), col = (int)(i % N);
+    float s = 0.f;
+    for (int k = 0; k < KS; ++k)
+        s += part[((size_t)k * M + mr) * N + col];
+    y[mr * ldy + col] = f2h(s);
+}
+
+int cus()
+{
+    static int n[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (!n[dev]) {
+        int c = 0;
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            c <= 0)
+            c = 256;
+        n[dev] = c;
+    }
+    return n[dev];
+}
+
+}  // namespace
+
+q4_status launch_gemv_mfma(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
+                           uint16_t *y, int64_t ldy, int N, int K, int M, hipStream_t stream)
+{
+    const int G = K / 32;
+    // K splits of kGroupsPerSplit groups (the last may be shorter)
+    const int gc = kGroupsPerSplit;
+    const int KS = (G + gc - 1) / gc;
+    const int ntiles = (N + 15) / 16;
+    // about three resident workgroups per CU, each looping over its tiles (at
+    // most kMaxTilesPerWave per wave)
+    const int P = std::max({1, (ntiles + kWaves * kMaxTilesPerWave - 1) / (kWaves * kMaxTilesPerWave),
+                            std::min((ntiles + kWaves - 1) / kWaves, (3 * cus() + KS - 1) / KS)});
+    float *part = nullptr;
+    for (int m0 = 0; m0 < M; m0 += kMTile) {
+        const int mt = std::min(kMTile, M - m0);
+        const size_t lds = (size_t)kWaves * kMaxTilesPerWave * 64 * 16 +  // finished tiles
+                           (size_t)mt * (gc * 32 + 8) * 2;  // staged rows of this launch
+        if (KS > 1 && !part) {
+            char *ws = static_cast<char *>(
+                workspace(stream, kWsHeader + (size_t)KS * kMTile * N * sizeof(float)));
+            if (!ws)
+                return Q4_EHIP;
+            part = reinterpret_cast<float *>(ws + kWsHeader);
+        }
+        Q4_LAUNCH_MATVEC(k_gemv_mfma, dim3(P, KS), dim3(256), lds, stream,
+                         reinterpret_cast<const uint4 *>(W), S, x + m0 * ldx, ldx, y + m0 * ldy,
+                         ldy, part, N, G, mt, gc);
+        q4_status st = check_launch("k_gemv_mfma");
+        if (st != Q4_OK)
+            return st;
+        if (KS > 1) {
+            const int64_t total = (int64_t)mt * N;
+            hipLaunchKernelGGL(k_combine, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                               stream, part, KS, mt, N, y + m0 * ldy, ldy);
+            if ((st = check_launch("k_combine")) != Q4_OK)
+                return st;
+        }
+    }
+    return Q4_OK;
+}
+
+}  // namespace q4

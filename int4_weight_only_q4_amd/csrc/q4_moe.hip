@@ -236,8 +236,8 @@ q4_status run_moe(int mb, dim3 grid, size_t lds, hipStream_t st, const uint4 *W,
                   int64_t slot_stride, int TOPK, uint16_t *y, float *part, int N, int G)
 {
 #define Q4_MOE_LAUNCH(MBV)                                                                        \
-    hipLaunchKernelGGL((k_moe_gemv<LPR, NGMAX, MBV, MODE>), grid, dim3(256), lds, st, W, S, meta, \
-                       P, x, ldx, slot_stride, TOPK, y, part, N, G)
+    Q4_LAUNCH_MATVEC((k_moe_gemv<LPR, NGMAX, MBV, MODE>), grid, dim3(256), lds, st, W, S, meta, \
+                     P, x, ldx, slot_stride, TOPK, y, part, N, G)
     switch (mb) {
     case 8: Q4_MOE_LAUNCH(8); break;
     case 4: Q4_MOE_LAUNCH(4); break;
