@@ -99,6 +99,14 @@ struct GemvOp {
     uint16_t *res_out = nullptr;
 };
 q4_status launch_gemv_op(const GemvOp &op, hipStream_t stream);
+// MoE expert matvecs on the matrix cores (q4_mfma.hip): meta from the routing
+// kernel, part = f32 scratch of moe_part_bytes(N, K, T * TOPK); mode 0 per-slot
+// outputs, 1 SiLU-multiply of the gate and up halves, 2 routing-weighted combine.
+q4_status launch_moe_mfma(const uint32_t *W, const uint16_t *S, const int32_t *ids,
+                          const int32_t *meta, const uint16_t *route_w, const uint16_t *x,
+                          int64_t ldx, int64_t x_slot_stride, uint16_t *y, float *part, int E,
+                          int N, int K, int T, int TOPK, int mode, hipStream_t stream);
+size_t moe_part_bytes(int N, int K, int P);
 // M >= 2 rows on the matrix cores (q4_mfma.hip)
 q4_status launch_gemv_mfma(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
                            uint16_t *y, int64_t ldy, int N, int K, int M, hipStream_t stream);

@@ -179,3 +179,22 @@ def test_moe_deterministic(o, q4, moe128):
         outs.append(bits(y))
     sync()
     assert np.array_equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("n,k,m", [(3072, 3072, 8), (2560, 9728, 5), (96, 256, 16)])
+def test_batched_one_hot_rows_are_exact(o, q4, n, k, m):
+    """Row m of X is one-hot at column k_m: y[m][n] = f16((q[n][k_m] - 7) *
+    s[n][k_m / 32]) exactly, so the batched path must not round a dequantised
+    weight before it is multiplied (only the final f16 rounding remains)."""
+    seed = 1700 + n + m
+    codes = datagen.codes(seed, n, k)
+    W, S = o.pack(codes), datagen.scales(seed + 1, n, k)
+    ks = np.random.default_rng(seed).integers(0, k, m)
+    X = np.zeros((m, k), np.float16)
+    X[np.arange(m), ks] = 1.0
+    Y = bits(q4.gemv_batched(dev_tensor(W), dev_tensor(S), dev_tensor(X)))
+    sync()
+    for i in range(m):
+        g = ks[i] // 32  # the oracle dequantises the group holding column k_m
+        grp = o.dequant(W[:, 4 * g:4 * g + 4], S[:, g:g + 1])
+        assert np.array_equal(Y[i], o.d2h(grp[:, ks[i] % 32]).view(np.uint16)), i
