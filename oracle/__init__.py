@@ -54,6 +54,8 @@ _SIGS = {
     "q4o_moe_stage": (None, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, C.c_int, _P]),
     "q4o_layer": (None, [_I] * 5 + [_P] * 8 + [_P, _P, C.c_double] + [_P] * 5),
     "q4o_stack": (None, [_I] * 6 + [_P] * 8 + [_P, _P, _P, C.c_double] + [_P] * 5),
+    "q4o_argmax": (C.c_int64, [_P, _I]),
+    "q4o_lm_head": (None, [_P, _P, _P, _I, _I, _I, _I, _P, _P]),
 }
 
 
@@ -150,6 +152,26 @@ class Oracle:
         return y
 
     # -- epilogues -----------------------------------------------------------
+    # -- LM head and greedy sampling ------------------------------------------
+    def argmax(self, v):
+        """Index of the largest value (ties: smallest index; NaN ranks highest)."""
+        v = np.ascontiguousarray(v, dtype=np.float64).ravel()
+        assert v.size >= 1
+        return int(self.lib.q4o_argmax(self._ptr(v), v.size))
+
+    def lm_head(self, W, S, X):
+        """X f16 [M, K] -> (exact logits f64 [M, N], greedy tokens int64 [M])."""
+        W = np.ascontiguousarray(W, dtype=np.uint32)
+        S, X = self._u16(S), self._u16(np.atleast_2d(X))
+        n, k = W.shape[0], W.shape[1] * 8
+        m = X.shape[0]
+        assert X.shape[1] == k
+        logits = np.empty((m, n), np.float64)
+        tokens = np.empty(m, np.int64)
+        self.lib.q4o_lm_head(self._ptr(W), self._ptr(S), self._ptr(X), k, n, k, m,
+                             self._ptr(logits), self._ptr(tokens))
+        return logits, tokens
+
     def add_rmsnorm(self, a, r, gamma, eps=1e-5):
         r = self._u16(np.atleast_2d(r))
         m, d = r.shape

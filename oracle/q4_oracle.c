@@ -30,7 +30,10 @@
  *  - BENCH.md, "MoE chunked prefill (2026-08-13)": each (token, slot) runs its
  *    own expert's matmul and the slot outputs are combined by routing weight.
  *  - Zero TVM Documentation, "Decode loop" and "Ping-pong residual buffers":
- *    the per-layer chain QKV -> attention -> O -> add+norm -> FFN -> add+norm.
+ *    the per-layer chain QKV -> attention -> O -> add+norm -> FFN -> add+norm,
+ *    then the LM head and the argmax of its logits (shader 10, "Argmax
+ *    Sampler"); RESEARCH.md, "Why Fewer Dispatches Matter": the LM head's
+ *    matmul writes f32 logits.
  *
  * Every function here has at least one pin in tests/test_oracle_pins.py
  * (closed forms, special cases, brute force, library routines); none is
@@ -367,4 +370,45 @@ void q4o_stack(int64_t n_layers, int64_t d, int64_t f, int64_t n_qkv, int64_t v_
     }
     free(r2);
     free(h2);
+}
+
+/* ------------------------------------------------------------------------ */
+/* LM head and greedy sampling (Zero TVM Documentation, "Decode loop": the   */
+/* LM-head matmul writes the logits and the argmax picks the next token;     */
+/* shader 10 "Argmax Sampler"; RESEARCH.md, "Why Fewer Dispatches Matter",   */
+/* the per-decode dispatch table and the note below it: the LM head is the   */
+/* f32-output variant of the int4 matmul, kept in f32 for a stable argmax).  */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Index of the largest of n >= 1 values. The pages take the next token as
+ * the argmax of the logits and leave ties and NaN open; read here as: ties go
+ * to the smallest index, -0 equals +0 (IEEE comparison), and a NaN counts as
+ * larger than every number, so the first NaN wins.
+ */
+int64_t q4o_argmax(const double *v, int64_t n)
+{
+    int64_t best = 0;
+    for (int64_t i = 1; i < n; ++i) {
+        if (isnan(v[best]))
+            break;
+        if (isnan(v[i]) || v[i] > v[best])
+            best = i;
+    }
+    return best;
+}
+
+/*
+ * For each of m activation rows x[b*ldx ...]: logits[b][r] = W[r] . x_b in
+ * binary64 (no rounding: the f32 logits of the library are compared against
+ * them) and token[b] = the argmax of those exact logits.
+ */
+void q4o_lm_head(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
+                 int64_t n, int64_t k, int64_t m, double *logits, int64_t *token)
+{
+    for (int64_t b = 0; b < m; ++b) {
+        for (int64_t r = 0; r < n; ++r)
+            logits[b * n + r] = q4o_row_dot(W, S, x + b * ldx, k, r);
+        token[b] = q4o_argmax(logits + b * n, n);
+    }
 }

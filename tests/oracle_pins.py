@@ -493,6 +493,98 @@ def pin_stack_is_layer_sequence(o):
     assert np.array_equal(h64, hb64)
 
 
+# -- LM head and greedy argmax ------------------------------------------------
+# The pages pick the next token as the argmax of the LM head's logits (Zero TVM
+# Documentation, shader 10 "Argmax Sampler") and leave ties and NaN open; the
+# reading pinned here: ties go to the smallest index, -0 equals +0, a NaN ranks
+# above every number (the first NaN wins).
+
+def pin_argmax_special_cases(o):
+    inf, nan = np.inf, np.nan
+    cases = [
+        ([3.0], 0), ([1.0, 2.0, 3.0], 2), ([3.0, 2.0, 1.0], 0),
+        ([2.0, 5.0, 5.0, 1.0], 1),            # tie: the smaller index
+        ([-0.0, 0.0], 0), ([0.0, -0.0], 0),   # -0 == +0
+        ([-inf, -inf, -inf], 0), ([-1.0, -inf], 0), ([1e308, inf], 1),
+        ([-2.0, -1.0, -3.0], 1),
+        ([1.0, nan, 5.0, nan], 1), ([inf, nan], 1), ([nan, inf], 0), ([nan], 0),
+    ]
+    for v, want in cases:
+        assert o.argmax(v) == want, (v, want)
+
+
+def pin_argmax_brute_force(o):
+    """Every sequence of length 1..4 over seven special values against the
+    maximum of the key (rank, -index), rank putting NaN above every number."""
+    import itertools
+    import math
+    vals = [-np.inf, -1.0, -0.0, 0.0, 1.0, np.inf, np.nan]
+
+    def key(v, i):
+        return ((1, 0.0) if math.isnan(v[i]) else (0, v[i]), -i)
+
+    for n in range(1, 5):
+        for v in itertools.product(vals, repeat=n):
+            want = max(range(n), key=lambda i: key(v, i))
+            assert o.argmax(list(v)) == want, (v, want)
+
+
+def pin_argmax_matches_numpy(o):
+    """numpy.argmax is the same definition: the first occurrence of the
+    maximum, a NaN counting as the maximum."""
+    rng = np.random.default_rng(7)
+    for trial in range(40):
+        n = int(rng.integers(1, 3000))
+        v = rng.integers(-4, 5, n).astype(np.float64)  # few levels: many ties
+        if trial % 3 == 0:
+            v[rng.integers(0, n, 2)] = np.nan
+        assert o.argmax(v) == int(np.argmax(v)), trial
+    for seed in range(3):  # f32 logits of the Phi-3 vocabulary size
+        v = np.random.default_rng(seed).standard_normal(32064).astype(np.float32)
+        assert o.argmax(v) == int(np.argmax(v))
+
+
+def pin_lm_head_planted_maximum(o):
+    """All codes 7 (weight 0) except row r0 (codes 15, weight 8 s) and x > 0:
+    every logit is 0 but logit r0 = 8 sum_k s x_k > 0, so the token is r0; a
+    copy of row r0 at a larger index does not change it."""
+    n, k = 96, 256
+    codes = np.full((n, k), 7, np.uint8)
+    r0, r1 = 37, 80
+    codes[r0] = 15
+    codes[r1] = 15
+    W = o.pack(codes)
+    S = datagen.scales(501, n, k)
+    S[r1] = S[r0]
+    x = np.abs(datagen.activations(502, 1, k)).astype(np.float16)
+    logits, tok = o.lm_head(W, S, x)
+    assert tok[0] == r0
+    s = o.h2d(S[r0])
+    xs = o.h2d(x[0])
+    want = sum(8.0 * s[c // 32] * xs[c] for c in range(k))
+    assert logits[0, r0] == logits[0, r1]
+    assert abs(logits[0, r0] - want) <= 1e-12 * abs(want)
+    others = np.delete(logits[0], [r0, r1])
+    assert np.all(others == 0.0)
+
+
+def pin_lm_head_rows_are_matvec_then_argmax(o):
+    """Each row's logits are the matvec of that activation row (one-hot rows
+    give a weight column exactly) and its token is their argmax."""
+    n, k, m = 200, 512, 3
+    _, W, S = _mat(o, 510, n, k)
+    X = datagen.activations(511, m, k)
+    X[1] = 0
+    X[1, 77] = 1.0  # one-hot: logits = column 77 exactly
+    logits, tok = o.lm_head(W, S, X)
+    col = o.dequant(W, S)[:, 77]
+    assert np.array_equal(logits[1], col)
+    for b in range(m):
+        y = o.gemv(W, S, X[b])
+        assert np.array_equal(logits[b], y)
+        assert tok[b] == int(np.argmax(y))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -519,6 +611,12 @@ MUTANTS = [
     ("stack_wrong_v_slice", "qkv + v_off, d, dv", "qkv, d, dv"),
     ("stack_gamma_next_is_current", "gamma_in + (L + 1) * d", "gamma_in + L * d"),
     ("layer_second_norm_uses_first_residual", "q4o_add_rmsnorm(dn, r1, gamma_next", "q4o_add_rmsnorm(dn, r_in, gamma_next"),
+    ("argmax_ties_to_last", "|| v[i] > v[best])", "|| v[i] >= v[best])"),
+    ("argmax_nan_ignored", "if (isnan(v[i]) || v[i] > v[best])", "if (v[i] > v[best])"),
+    ("argmax_is_argmin", "|| v[i] > v[best])", "|| v[i] < v[best])"),
+    ("argmax_skips_first", "int64_t best = 0;\n    for (int64_t i = 1;", "int64_t best = n > 1 ? 1 : 0;\n    for (int64_t i = 2;"),
+    ("lm_head_row_stride_ignored", "q4o_row_dot(W, S, x + b * ldx, k, r);\n        token", "q4o_row_dot(W, S, x, k, r);\n        token"),
+    ("lm_head_token_of_first_row", "token[b] = q4o_argmax(logits + b * n, n);", "token[b] = q4o_argmax(logits, n);"),
 ]
 
 
