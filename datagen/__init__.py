@@ -118,6 +118,27 @@ def routing_pool(seed: int, count: int, t: int, n_experts: int, topk: int):
     return ids, w
 
 
+def logits(seed: int, m: int, n: int, ties: bool = False, special: bool = False) -> np.ndarray:
+    """``m`` rows of ``n`` float32 logits drawn from N(0, 3^2).
+
+    ties: values rounded to multiples of 1/2, so a row's maximum is often shared
+    by several positions. special: each row also gets -0.0, +0.0, -inf and +inf
+    at random positions, and every third row a NaN or two.
+    """
+    r = _rng(seed)
+    v = r.normal(0.0, 3.0, size=(m, n))
+    if ties:
+        v = np.round(v * 2.0) / 2.0
+    v = v.astype(np.float32)
+    if special:
+        for i in range(m):
+            pos = r.integers(0, n, size=4)
+            v[i, pos] = np.array([-0.0, 0.0, -np.inf, np.inf], np.float32)
+            if i % 3 == 2:
+                v[i, r.integers(0, n, size=2)] = np.nan
+    return v
+
+
 def q4_matrix(seed: int, n: int, k: int):
     """Codes and scales of one int4 weight matrix (two seeds derived from ``seed``)."""
     return codes(seed, n, k), scales(seed + 500, n, k)

@@ -186,6 +186,43 @@ q4_status q4_gemv_ex(const uint32_t *W, const uint16_t *S, const uint16_t *x, ui
                      int64_t N, int64_t K, const q4_epilogue *epi, q4_stream stream);
 
 /* ---------------------------------------------------------------------------
+ * LM head and greedy sampling (Zero TVM Documentation, "Decode loop": the LM
+ * head's matmul writes the logits and an argmax picks the next token; shader
+ * 10, "Argmax Sampler"; RESEARCH.md, "Why Fewer Dispatches Matter", the
+ * per-decode dispatch table and the note below it: the LM head is the int4
+ * matmul with f32 outputs, for a stable argmax).
+ *
+ * q4_gemv_f32 -- the matmul with f32 outputs (no rounding to f16):
+ *   y[m*ldy + n] = sum_k w[n][k] * x[m*ldx + k],  f32 accumulation, m < M
+ * W, S as for q4_gemv; x f16 rows (16-byte aligned, ldx % 8 == 0, ldx >= K);
+ * y f32 (4-byte aligned, ldy >= N), caller-owned, must not overlap the inputs.
+ * 1 <= M <= Q4_MAX_M.
+ */
+q4_status q4_gemv_f32(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
+                      float *y, int64_t ldy, int64_t N, int64_t K, int64_t M,
+                      q4_stream stream);
+
+/* q4_argmax -- greedy token of each of M rows of N f32 values v[m*ld ...]:
+ *   index[m] = the smallest n whose v[m*ld + n] is the row's maximum,
+ * where -0 equals +0 and a NaN ranks above every number (the first NaN wins);
+ * the pages leave ties and NaN open. v 4-byte aligned, ld >= N, 1 <= N <
+ * 2^31, 1 <= M <= 65535; index int32[M] (4-byte aligned), caller-owned, must
+ * not overlap v. Deterministic (no atomics).
+ */
+q4_status q4_argmax(const float *v, int64_t ld, int64_t N, int64_t M, int32_t *index,
+                    q4_stream stream);
+
+/* q4_lm_head_argmax -- q4_gemv_f32 into logits (f32, rows of ldl >= N) and
+ * q4_argmax of each row into tokens int32[M], in one call (for M = 1 the
+ * matmul's workgroups hand their rows' best (value, index) to a one-workgroup
+ * reduction; the logits are not read back). Arguments and errors as for the
+ * two calls; logits and tokens must not overlap each other or the inputs.
+ */
+q4_status q4_lm_head_argmax(const uint32_t *W, const uint16_t *S, const uint16_t *x,
+                            int64_t ldx, float *logits, int64_t ldl, int32_t *tokens, int64_t N,
+                            int64_t K, int64_t M, q4_stream stream);
+
+/* ---------------------------------------------------------------------------
  * q4_stack_decode -- one decode token through a stack of decoder layers whose
  * attention is replaced by the single-position identity on the V slice
  * (Zero TVM Documentation, "Decode loop": per layer QKV matmul -> attention ->

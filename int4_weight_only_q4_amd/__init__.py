@@ -33,7 +33,8 @@ BYTES_PER_WEIGHT = 0.5 + 2.0 / 32.0
 ABI_SYMBOLS = (
     "q4_version", "q4_last_error", "q4_bytes_per_weight", "q4_pack", "q4_unpack", "q4_gemv",
     "q4_gemv_batched", "q4_moe_gemv", "q4_add_rmsnorm", "q4_silu_mul", "q4_gemv_ex",
-    "q4_stack_decode", "q4_stack_status", "q4_timer_arm", "q4_timer_read",
+    "q4_stack_decode", "q4_stack_status", "q4_timer_arm", "q4_timer_read", "q4_gemv_f32",
+    "q4_argmax", "q4_lm_head_argmax",
 )
 
 
@@ -76,6 +77,9 @@ _SIGS = {
     "q4_stack_status": (C.c_int, [_P]),
     "q4_timer_arm": (C.c_int, [C.c_int]),
     "q4_timer_read": (C.c_int, [C.c_int, C.POINTER(C.c_float)]),
+    "q4_gemv_f32": (C.c_int, [_P, _P, _P, _I, _P, _I, _I, _I, _I, _P]),
+    "q4_argmax": (C.c_int, [_P, _I, _I, _I, _P, _P]),
+    "q4_lm_head_argmax": (C.c_int, [_P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _P]),
 }
 
 _lib = None
@@ -187,6 +191,54 @@ def gemv_batched(W, S, x, y=None, stream=None):
     _check(lib().q4_gemv_batched(_ptr(W), _ptr(S), _ptr(x), x.stride(0), _ptr(y), y.stride(0),
                                  n, k, m, _stream(stream)))
     return y
+
+
+def _rows(x):
+    """A 1-D activation as one row; returns (2-D view, M, leading dimension)."""
+    x2 = x.unsqueeze(0) if x.dim() == 1 else x
+    return x2, x2.shape[0], x2.stride(0)
+
+
+def gemv_f32(W, S, x, y=None, stream=None):
+    """f32 logits: x f16 [K] or [M, K] -> y f32 [N] or [M, N] (no f16 rounding)."""
+    import torch
+    n, k = W.shape[0], W.shape[1] * 8
+    x2, m, ldx = _rows(x)
+    if y is None:
+        y = torch.empty((m, n) if x.dim() > 1 else (n,), dtype=torch.float32, device=W.device)
+    y2 = y.unsqueeze(0) if y.dim() == 1 else y
+    _check(lib().q4_gemv_f32(_ptr(W), _ptr(S), _ptr(x2), ldx, _ptr(y2), y2.stride(0), n, k, m,
+                             _stream(stream)))
+    return y
+
+
+def argmax(v, index=None, stream=None):
+    """Greedy token of each row of f32 logits v [N] or [M, N] -> int32 [1] or [M]
+    (ties: smallest index; NaN ranks highest)."""
+    import torch
+    v2 = v.unsqueeze(0) if v.dim() == 1 else v
+    m, n = v2.shape
+    if index is None:
+        index = torch.empty(m, dtype=torch.int32, device=v.device)
+    _check(lib().q4_argmax(_ptr(v2), v2.stride(0), n, m, _ptr(index), _stream(stream)))
+    return index
+
+
+def lm_head_argmax(W, S, x, logits=None, tokens=None, stream=None):
+    """LM head with f32 logits and the greedy token of each row:
+    x f16 [K] or [M, K] -> (logits f32 [N] or [M, N], tokens int32 [M])."""
+    import torch
+    n, k = W.shape[0], W.shape[1] * 8
+    x2, m, ldx = _rows(x)
+    if logits is None:
+        logits = torch.empty((m, n) if x.dim() > 1 else (n,), dtype=torch.float32,
+                             device=W.device)
+    if tokens is None:
+        tokens = torch.empty(m, dtype=torch.int32, device=W.device)
+    l2 = logits.unsqueeze(0) if logits.dim() == 1 else logits
+    _check(lib().q4_lm_head_argmax(_ptr(W), _ptr(S), _ptr(x2), ldx, _ptr(l2), l2.stride(0),
+                                   _ptr(tokens), n, k, m, _stream(stream)))
+    return logits, tokens
 
 
 def moe_gemv(W, S, ids, x, ldx, x_slot_stride, route_w=None, epi_silu=False, y=None,

@@ -402,6 +402,46 @@ q4_status stack_persistent(const q4_stack_desc *d, const uint16_t *r_in, const u
     return Q4_OK;
 }
 
+q4_status check_f32_matvec(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
+                           const float *y, int64_t ldy, int64_t N, int64_t K, int64_t M)
+{
+    q4_status st = check_matrix(W, S, N, K);
+    if (st != Q4_OK)
+        return st;
+    if (!x || !y)
+        return fail(Q4_EINVAL, "NULL activation or output pointer");
+    if (M < 1 || M > Q4_MAX_M)
+        return fail(Q4_ERANGE, "M=%lld outside [1, %d]", (long long)M, Q4_MAX_M);
+    if (ldx < K || ldy < N)
+        return fail(Q4_EINVAL, "leading dimensions too small (ldx=%lld, ldy=%lld)",
+                    (long long)ldx, (long long)ldy);
+    if (!aligned(x, 16) || ldx % 8)
+        return fail(Q4_EALIGN, "activation rows must be 16-byte aligned (ldx %% 8 == 0)");
+    if (!aligned(y, 4))
+        return fail(Q4_EALIGN, "the f32 output must be 4-byte aligned");
+    const size_t yb = ((size_t)(M - 1) * ldy + N) * 4, xb = ((size_t)(M - 1) * ldx + K) * 2;
+    if (overlaps(y, yb, W, wbytes(N, K)) || overlaps(y, yb, S, sbytes(N, K)) ||
+        overlaps(y, yb, x, xb))
+        return fail(Q4_EALIAS, "the output overlaps an input");
+    return Q4_OK;
+}
+
+q4_status check_argmax(const float *v, int64_t ld, int64_t N, int64_t M, const int32_t *index)
+{
+    if (!v || !index)
+        return fail(Q4_EINVAL, "NULL logits or index pointer");
+    if (N < 1 || M < 1)
+        return fail(Q4_EINVAL, "non-positive shape N=%lld M=%lld", (long long)N, (long long)M);
+    if (N > 0x7FFFFFFFll || M > 65535)
+        return fail(Q4_ERANGE, "N=%lld or M=%lld too large", (long long)N, (long long)M);
+    if (ld < N)
+        return fail(Q4_EINVAL, "leading dimension ld=%lld < N", (long long)ld);
+    if (!aligned(v, 4) || !aligned(index, 4))
+        return fail(Q4_EALIGN, "logits and index must be 4-byte aligned");
+    if (overlaps(index, (size_t)M * 4, v, ((size_t)(M - 1) * ld + N) * 4))
+        return fail(Q4_EALIAS, "the index output overlaps the logits");
+    return Q4_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -554,6 +594,45 @@ q4_status q4_gemv_batched(const uint32_t *W, const uint16_t *S, const uint16_t *
         overlaps(y, yb, x, xb))
         return fail(Q4_EALIAS, "the output overlaps an input");
     return launch_gemv_batched(W, S, x, ldx, y, ldy, (int)N, (int)K, (int)M, as_stream(stream));
+}
+
+
+q4_status q4_gemv_f32(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
+                      float *y, int64_t ldy, int64_t N, int64_t K, int64_t M, q4_stream stream)
+{
+    q4_status st = check_f32_matvec(W, S, x, ldx, y, ldy, N, K, M);
+    if (st != Q4_OK)
+        return st;
+    return launch_gemv_f32(W, S, x, ldx, y, ldy, (int)N, (int)K, (int)M, as_stream(stream));
+}
+
+q4_status q4_argmax(const float *v, int64_t ld, int64_t N, int64_t M, int32_t *index,
+                    q4_stream stream)
+{
+    q4_status st = check_argmax(v, ld, N, M, index);
+    if (st != Q4_OK)
+        return st;
+    return launch_argmax(v, ld, (int)N, (int)M, index, as_stream(stream));
+}
+
+q4_status q4_lm_head_argmax(const uint32_t *W, const uint16_t *S, const uint16_t *x,
+                            int64_t ldx, float *logits, int64_t ldl, int32_t *tokens, int64_t N,
+                            int64_t K, int64_t M, q4_stream stream)
+{
+    q4_status st = check_f32_matvec(W, S, x, ldx, logits, ldl, N, K, M);
+    if (st != Q4_OK)
+        return st;
+    if (!tokens)
+        return fail(Q4_EINVAL, "NULL token pointer");
+    if (!aligned(tokens, 4))
+        return fail(Q4_EALIGN, "tokens must be 4-byte aligned");
+    const size_t lb = ((size_t)(M - 1) * ldl + N) * 4, tb = (size_t)M * 4;
+    if (overlaps(tokens, tb, logits, lb) || overlaps(tokens, tb, W, wbytes(N, K)) ||
+        overlaps(tokens, tb, S, sbytes(N, K)) ||
+        overlaps(tokens, tb, x, ((size_t)(M - 1) * ldx + K) * 2))
+        return fail(Q4_EALIAS, "tokens overlap another argument");
+    return launch_lm_head_argmax(W, S, x, ldx, logits, ldl, tokens, (int)N, (int)K, (int)M,
+                                 as_stream(stream));
 }
 
 q4_status q4_moe_gemv(const uint32_t *W, const uint16_t *S, const int32_t *ids,

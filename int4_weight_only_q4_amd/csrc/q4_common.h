@@ -84,8 +84,10 @@ q4_status launch_gemv(const uint32_t *W, const uint16_t *S, const uint16_t *x, u
 //   epilogue: NONE  y[n] = f16(acc)
 //             SILU  y[i] = f16(silu(f16(acc_i)) * f16(acc_{N/2+i}))
 //             RESID res_out[n] = f16(f16(acc) + res_in[n])
+//             LOGITS yf[n] = acc (f32); when cand is set, cand[workgroup] =
+//                    the largest argmax_key of the workgroup's rows
 struct GemvOp {
-    enum { NONE = 0, SILU = 1, RESID = 2 };
+    enum { NONE = 0, SILU = 1, RESID = 2, LOGITS = 3 };
     const uint32_t *W = nullptr;
     const uint16_t *S = nullptr;
     int N = 0, K = 0;
@@ -97,8 +99,12 @@ struct GemvOp {
     uint16_t *y = nullptr;
     const uint16_t *res_in = nullptr;
     uint16_t *res_out = nullptr;
+    float *yf = nullptr;
+    unsigned long long *cand = nullptr;
 };
 q4_status launch_gemv_op(const GemvOp &op, hipStream_t stream);
+// Workgroups of one launch_gemv_op for N rows of K (the candidates LOGITS writes).
+int matvec_blocks(int N, int K);
 // MoE expert matvecs on the matrix cores (q4_mfma.hip): meta from the routing
 // kernel, part = f32 scratch of moe_part_bytes(N, K, T * TOPK); mode 0 per-slot
 // outputs, 1 SiLU-multiply of the gate and up halves, 2 routing-weighted combine.
@@ -107,9 +113,19 @@ q4_status launch_moe_mfma(const uint32_t *W, const uint16_t *S, const int32_t *i
                           int64_t ldx, int64_t x_slot_stride, uint16_t *y, float *part, int E,
                           int N, int K, int T, int TOPK, int mode, hipStream_t stream);
 size_t moe_part_bytes(int N, int K, int P);
-// M >= 2 rows on the matrix cores (q4_mfma.hip)
+// M >= 2 rows on the matrix cores (q4_mfma.hip): f16 outputs y, or f32
+// outputs yf when yf is set (y is then ignored)
 q4_status launch_gemv_mfma(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
-                           uint16_t *y, int64_t ldy, int N, int K, int M, hipStream_t stream);
+                           uint16_t *y, float *yf, int64_t ldy, int N, int K, int M,
+                           hipStream_t stream);
+// LM head and greedy argmax (q4_lmhead.hip)
+q4_status launch_gemv_f32(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
+                          float *y, int64_t ldy, int N, int K, int M, hipStream_t stream);
+q4_status launch_argmax(const float *v, int64_t ld, int N, int M, int32_t *index,
+                        hipStream_t stream);
+q4_status launch_lm_head_argmax(const uint32_t *W, const uint16_t *S, const uint16_t *x,
+                                int64_t ldx, float *logits, int64_t ldl, int32_t *tokens, int N,
+                                int K, int M, hipStream_t stream);
 q4_status launch_gemv_batched(const uint32_t *W, const uint16_t *S, const uint16_t *x,
                               int64_t ldx, uint16_t *y, int64_t ldy, int N, int K, int M,
                               hipStream_t stream);
@@ -172,6 +188,36 @@ __device__ __forceinline__ float block_sum_256(float v, float *red)
     float t = ((red[0] + red[1]) + red[2]) + red[3];
     __syncthreads();
     return t;
+}
+
+// Order-preserving 64-bit key of (value, index) for a greedy argmax: a larger
+// value gives a larger key and, between equal values, the smaller index does;
+// -0 equals +0 and a NaN ranks above every number. Key 0 is below every value.
+__device__ __forceinline__ unsigned long long argmax_key(float v, uint32_t idx)
+{
+    uint32_t u = __builtin_bit_cast(uint32_t, v);
+    if (v != v)
+        u = 0xFFFFFFFFu;                       // NaN: above +inf (0xFF800000)
+    else if (v == 0.0f)
+        u = 0x80000000u;                       // either zero
+    else
+        u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((unsigned long long)u << 32) | (0xFFFFFFFFu - idx);
+}
+
+__device__ __forceinline__ int32_t argmax_index(unsigned long long key)
+{
+    return (int32_t)(0xFFFFFFFFu - (uint32_t)key);
+}
+
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long k)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const unsigned long long o = __shfl_xor(k, off, 64);
+        k = o > k ? o : k;
+    }
+    return k;
 }
 
 }  // namespace q4

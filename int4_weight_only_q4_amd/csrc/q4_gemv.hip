@@ -29,7 +29,7 @@ namespace {
 constexpr int kWaves = 4;  // 256 threads per workgroup
 
 enum { PRO_X = 0, PRO_NORM = 1 };
-enum { EPI_NONE_ = 0, EPI_SILU = 1, EPI_RESID = 2 };
+enum { EPI_NONE_ = 0, EPI_SILU = 1, EPI_RESID = 2, EPI_LOGITS = 3 };
 
 struct GemvParams {
     const uint4 *W;     // [N][G] groups of 16 bytes
@@ -43,6 +43,8 @@ struct GemvParams {
     uint16_t *y;              // NONE: [N]; SILU: [N/2]
     const uint16_t *res_in;   // RESID: res_out[n] = f16(f16(y[n]) + res_in[n])
     uint16_t *res_out;
+    float *yf;                 // LOGITS: yf[n] = acc
+    unsigned long long *cand;  // LOGITS: this workgroup's largest argmax_key, or null
 };
 
 template <int LPR, int NG, int RPS, int EPI, int PRO>
@@ -54,6 +56,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams a)
     extern __shared__ uint4 smem[];
     __shared__ float red[4];
     __shared__ float vals[EPI == EPI_SILU ? RB : 1];
+    __shared__ unsigned long long wkey[EPI == EPI_LOGITS ? kWaves : 1];
 
     const int G = a.G;
     const int K = G * 32;
@@ -188,6 +191,29 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams a)
             if (gi < half)
                 a.y[gi] = f2h(silu_mul_f(vals[tid], vals[tid + RB / 2]));
         }
+    } else if (EPI == EPI_LOGITS) {  // f32 logits and this workgroup's argmax candidate
+        unsigned long long key = 0;
+        if (j == 0)
+#pragma unroll
+            for (int r = 0; r < RPS; ++r)
+                if (ok[r]) {
+                    a.yf[row[r]] = acc[r];
+                    const unsigned long long k = argmax_key(acc[r], (uint32_t)row[r]);
+                    key = k > key ? k : key;
+                }
+        if (a.cand) {
+            key = wave_max_u64(key);
+            if (lane == 0)
+                wkey[wave] = key;
+            __syncthreads();
+            if (tid == 0) {
+                unsigned long long m = wkey[0];
+#pragma unroll
+                for (int w = 1; w < kWaves; ++w)
+                    m = wkey[w] > m ? wkey[w] : m;
+                a.cand[blockIdx.x] = m;
+            }
+        }
     } else {  // EPI_RESID: the residual add of an add+RMSNorm, row by row
         if (j == 0)
 #pragma unroll
@@ -204,6 +230,9 @@ struct Cfg {
 };
 
 int max_ng(int lpr) { return lpr == 64 ? 12 : 8; }
+
+// rows (segments) per lane group: fewer groups per lane, more rows per lane
+constexpr int rows_per_segment(int ng) { return ng <= 2 ? 4 : (ng <= 4 ? 2 : 1); }
 
 Cfg choose_cfg(int G)
 {
@@ -225,7 +254,7 @@ Cfg choose_cfg(int G)
 template <int LPR, int NG, int EPI, int PRO>
 q4_status run_gemv(const GemvParams &p, hipStream_t st)
 {
-    constexpr int RPS = NG <= 2 ? 4 : (NG <= 4 ? 2 : 1);
+    constexpr int RPS = rows_per_segment(NG);
     constexpr int RB = kWaves * (64 / LPR) * RPS;
     const int rows = EPI == EPI_SILU ? p.N / 2 : p.N;
     const int rb = EPI == EPI_SILU ? RB / 2 : RB;
@@ -275,6 +304,15 @@ q4_status dispatch_lpr(const Cfg &c, const GemvParams &p, hipStream_t st)
 
 }  // namespace
 
+int matvec_blocks(int N, int K)
+{
+    const Cfg c = choose_cfg(K / 32);
+    if (!c.lpr)
+        return 0;
+    const int rb = kWaves * (64 / c.lpr) * rows_per_segment(c.ng);
+    return (N + rb - 1) / rb;
+}
+
 void matvec_layout(int G, int *lpr, int *ng)
 {
     const Cfg c = choose_cfg(G);
@@ -295,6 +333,8 @@ q4_status launch_gemv_op(const GemvOp &op, hipStream_t stream)
     p.y = op.y;
     p.res_in = op.res_in;
     p.res_out = op.res_out;
+    p.yf = op.yf;
+    p.cand = op.cand;
     const Cfg c = choose_cfg(p.G);
     const bool norm = op.norm_src != nullptr;
     switch (op.epi) {
@@ -308,6 +348,10 @@ q4_status launch_gemv_op(const GemvOp &op, hipStream_t stream)
         if (norm)
             return fail(Q4_EINVAL, "internal: normalising prologue with a residual epilogue");
         return dispatch_lpr<EPI_RESID, PRO_X>(c, p, stream);
+    case GemvOp::LOGITS:
+        if (norm)
+            return fail(Q4_EINVAL, "internal: normalising prologue with the logits epilogue");
+        return dispatch_lpr<EPI_LOGITS, PRO_X>(c, p, stream);
     default:
         return fail(Q4_EINVAL, "internal: unknown matvec epilogue %d", op.epi);
     }
@@ -362,7 +406,7 @@ q4_status launch_gemv_batched(const uint32_t *W, const uint16_t *S, const uint16
 {
     if (M == 1)  // a single row is the bandwidth-bound matvec
         return launch_gemv(W, S, x, y, N, K, EpiArgs{}, stream);
-    return launch_gemv_mfma(W, S, x, ldx, y, ldy, N, K, M, stream);
+    return launch_gemv_mfma(W, S, x, ldx, y, nullptr, ldy, N, K, M, stream);
 }
 
 }  // namespace q4

@@ -36,6 +36,9 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+// native vector (HIP's uint4 is a struct, whose private arrays the compiler
+// keeps in scratch memory instead of registers)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;            // 16 weight rows per wave
 constexpr int kRowsPerWg = 16 * kWaves;
@@ -98,18 +101,18 @@ __device__ __forceinline__ void mfma_rows(const uint4 *__restrict__ W,
     const int cpr = gn * 4;           // 16-byte chunks per staged row
 
     // 1. the activation chunk (all loads issued together, then stored)
-    uint4 xr[kXq];
+    u32x4 xr[kXq];
 #pragma unroll
     for (int q = 0; q < kXq; ++q) {
         const int c = min(t + 256 * q, M * cpr - 1);  // branch-free: the tail re-reads
         const int m = c / cpr, j = c - m * cpr;
-        xr[q] = *reinterpret_cast<const uint4 *>(row_ptr(m) + (int64_t)g0 * 32 + 8 * j);
+        xr[q] = *reinterpret_cast<const u32x4 *>(row_ptr(m) + (int64_t)g0 * 32 + 8 * j);
     }
 #pragma unroll
     for (int q = 0; q < kXq; ++q) {
         const int c = min(t + 256 * q, M * cpr - 1);  // the tail rewrites the last chunk
         const int m = c / cpr, j = c - m * cpr;
-        *reinterpret_cast<uint4 *>(xs + m * xstride + 8 * j) = xr[q];
+        *reinterpret_cast<u32x4 *>(xs + m * xstride + 8 * j) = xr[q];
     }
     __syncthreads();
 
@@ -182,12 +185,13 @@ __device__ __forceinline__ void mfma_rows(const uint4 *__restrict__ W,
 }
 
 // Batched matvec: grid (P, KS), 256 threads; wave w of workgroup b takes the
-// tiles b * 4 + w, + 4 P, ... KS == 1: y written; else f32 partials
-// part[ks][m][n] for k_combine.
+// tiles b * 4 + w, + 4 P, ... KS == 1: the f32 result written to yf when set,
+// else rounded to y; KS > 1: f32 partials part[ks][m][n] for k_combine.
 __global__ __launch_bounds__(256) void k_gemv_mfma(const uint4 *__restrict__ W,
                                                    const uint16_t *__restrict__ S,
                                                    const uint16_t *__restrict__ x, int64_t ldx,
-                                                   uint16_t *__restrict__ y, int64_t ldy,
+                                                   uint16_t *__restrict__ y,
+                                                   float *__restrict__ yf, int64_t ldy,
                                                    float *__restrict__ part, int N, int G, int M,
                                                    int gc)
 {
@@ -196,10 +200,12 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(const uint4 *__restrict__ W,
         W, S, N, G, M, gc, ks, blockIdx.x * kWaves + (threadIdx.x >> 6), gridDim.x * kWaves,
         [&](int m) { return x + m * ldx; },
         [&](int mr, int col, float v) {
-            if (KS == 1)
-                y[mr * ldy + col] = f2h(v);
-            else
+            if (KS > 1)
                 part[((size_t)ks * M + mr) * N + col] = v;
+            else if (yf)
+                yf[mr * ldy + col] = v;
+            else
+                y[mr * ldy + col] = f2h(v);
         });
 }
 
@@ -291,9 +297,11 @@ __global__ __launch_bounds__(256) void k_moe_finish(int mode, const float *__res
     }
 }
 
-// y[m][n] = f16(sum over ks, in order, of part[ks][m][n])
+// sum over ks, in order, of part[ks][m][n]: to yf[m][n] when set, else
+// rounded to y[m][n]
 __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ part, int KS, int M,
-                                                 int N, uint16_t *__restrict__ y, int64_t ldy)
+                                                 int N, uint16_t *__restrict__ y,
+                                                 float *__restrict__ yf, int64_t ldy)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= (int64_t)M * N)
@@ -302,7 +310,10 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ part,
     float s = 0.f;
     for (int k = 0; k < KS; ++k)
         s += part[((size_t)k * M + mr) * N + col];
-    y[mr * ldy + col] = f2h(s);
+    if (yf)
+        yf[mr * ldy + col] = s;
+    else
+        y[mr * ldy + col] = f2h(s);
 }
 
 int cus()
@@ -324,7 +335,8 @@ int cus()
 }  // namespace
 
 q4_status launch_gemv_mfma(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
-                           uint16_t *y, int64_t ldy, int N, int K, int M, hipStream_t stream)
+                           uint16_t *y, float *yf, int64_t ldy, int N, int K, int M,
+                           hipStream_t stream)
 {
     const int G = K / 32;
     // K splits of kGroupsPerSplit groups (the last may be shorter)
@@ -348,15 +360,17 @@ q4_status launch_gemv_mfma(const uint32_t *W, const uint16_t *S, const uint16_t 
             part = reinterpret_cast<float *>(ws + kWsHeader);
         }
         Q4_LAUNCH_MATVEC(k_gemv_mfma, dim3(P, KS), dim3(256), lds, stream,
-                         reinterpret_cast<const uint4 *>(W), S, x + m0 * ldx, ldx, y + m0 * ldy,
-                         ldy, part, N, G, mt, gc);
+                         reinterpret_cast<const uint4 *>(W), S, x + m0 * ldx, ldx,
+                         yf ? nullptr : y + m0 * ldy, yf ? yf + m0 * ldy : nullptr, ldy, part, N,
+                         G, mt, gc);
         q4_status st = check_launch("k_gemv_mfma");
         if (st != Q4_OK)
             return st;
         if (KS > 1) {
             const int64_t total = (int64_t)mt * N;
             hipLaunchKernelGGL(k_combine, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                               stream, part, KS, mt, N, y + m0 * ldy, ldy);
+                               stream, part, KS, mt, N, yf ? nullptr : y + m0 * ldy,
+                               yf ? yf + m0 * ldy : nullptr, ldy);
             if ((st = check_launch("k_combine")) != Q4_OK)
                 return st;
         }

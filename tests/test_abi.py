@@ -180,3 +180,26 @@ def test_timer_validation():
     assert L.q4_timer_read(3, None) == q4.Q4_EINVAL
     # slot 7 was never armed for a launch on this thread
     assert L.q4_timer_read(7, C.byref(us)) == q4.Q4_EINVAL
+
+
+def test_lm_head_validation():
+    # q4_gemv_f32: W, S, x, ldx, y, ldy, N, K, M
+    assert status("q4_gemv_f32", A, B, X, 64, None, 16, 16, 64, 1, None) == q4.Q4_EINVAL
+    assert status("q4_gemv_f32", A, B, X, 64, Y, 16, 16, 64, 0, None) == q4.Q4_ERANGE
+    assert status("q4_gemv_f32", A, B, X, 64, Y, 8, 16, 64, 2, None) == q4.Q4_EINVAL
+    assert status("q4_gemv_f32", A, B, X, 64, Y + 2, 16, 16, 64, 1, None) == q4.Q4_EALIGN
+    assert status("q4_gemv_f32", A, B, X, 64, X + 64, 16, 16, 64, 1, None) == q4.Q4_EALIAS
+    # q4_argmax: v, ld, N, M, index
+    assert status("q4_argmax", None, 16, 16, 1, Y, None) == q4.Q4_EINVAL
+    assert status("q4_argmax", X, 16, 0, 1, Y, None) == q4.Q4_EINVAL
+    assert status("q4_argmax", X, 8, 16, 2, Y, None) == q4.Q4_EINVAL
+    assert status("q4_argmax", X, 1 << 31, 1 << 31, 1, Y, None) == q4.Q4_ERANGE
+    assert status("q4_argmax", X, 16, 16, 65536, Y, None) == q4.Q4_ERANGE
+    assert status("q4_argmax", X + 2, 16, 16, 1, Y, None) == q4.Q4_EALIGN
+    assert status("q4_argmax", X, 16, 16, 1, X + 60, None) == q4.Q4_EALIAS
+    # q4_lm_head_argmax: W, S, x, ldx, logits, ldl, tokens, N, K, M
+    assert status("q4_lm_head_argmax", A, B, X, 64, Y, 16, None, 16, 64, 1, None) == q4.Q4_EINVAL
+    assert status("q4_lm_head_argmax", A, B, X, 64, Y, 16, R + 2, 16, 64, 1, None) == q4.Q4_EALIGN
+    assert status("q4_lm_head_argmax", A, B, X, 64, Y, 16, Y + 32, 16, 64, 1, None) == q4.Q4_EALIAS
+    assert status("q4_lm_head_argmax", A, B, X, 64, Y, 16, X, 16, 64, 1, None) == q4.Q4_EALIAS
+    assert status("q4_lm_head_argmax", A, B, X, 64, Y, 16, R, 16, 48, 1, None) == q4.Q4_ESHAPE
