@@ -286,9 +286,9 @@ def gemv_table(q4, torch):
     rows = []
     base = datagen.SEED_BASE + 5_000_000
 
-    def add(workload, shape, m, weight_bytes, launch, count=200, note=""):
+    def add(workload, shape, m, weight_bytes, launch, count=200, note="", per_call=False):
         call_us, kern_us = _time(q4, torch, launch, count)
-        us = kern_us if kern_us is not None else call_us
+        us = call_us if per_call or kern_us is None else kern_us
         gbs = weight_bytes / (us * 1e-6) / 1e9
         rows.append(dict(workload=workload, shape=shape, m=m, weight_bytes=int(weight_bytes),
                          us_kernel=round(kern_us, 3) if kern_us is not None else None,
@@ -322,6 +322,27 @@ def gemv_table(q4, torch):
                                    ("gate_up", (16384, 3072)), ("down", (3072, 8192))], [1],
               base + 1000)
     gemv_rows("Qwen3-4B", list(QWEN3.items()), [1, 8], base + 2000)
+
+    # LM head with f32 logits and the greedy token (the whole call: matvec and
+    # argmax kernels); the Qwen3-4B head is tied to the embedding matrix
+    for j, (workload, n, k, ms) in enumerate([("Phi-3-mini LM head", 32064, 3072, [1]),
+                                             ("Qwen3-4B LM head", 151936, 2560, [1, 8])]):
+        rot = _rotation(torch, n, k, base + 2500 + 10 * j)
+        wb = n * k * BPW
+        for m in ms:
+            x = torch.from_numpy(datagen.activations(base + 2502 + 10 * j, m, k)).cuda()
+            logits = torch.empty((m, n), dtype=torch.float32, device="cuda")
+            tok = torch.empty(m, dtype=torch.int32, device="cuda")
+
+            def launch(i, rot=rot, x=x, logits=logits, tok=tok, m=m):
+                W, S = rot[i % len(rot)]
+                q4.lm_head_argmax(W, S, x[0] if m == 1 else x, logits=logits[0] if m == 1
+                                  else logits, tokens=tok)
+            add(workload + " + argmax", "%dx%d" % (n, k), m, wb, launch,
+                count=max(20, min(200, int(4e9 / wb))), per_call=True,
+                note="f32 logits; GB/s over the whole call (matvec + argmax)")
+        del rot
+        torch.cuda.empty_cache()
 
     # MoE layer: 128 experts, top-8; gate_up stage (SiLU-multiply) + down stage
     # with the routing-weighted combine. Two copies of the expert stack are
@@ -367,7 +388,8 @@ def gemv_table(q4, torch):
 
 
 def write_gemv_table(rows):
-    text = ["# Per-GEMV throughput: single GEMV, Phi-3-mini, Qwen3-4B (M = 1, 8) and MoE shapes",
+    text = ["# Per-GEMV throughput: single GEMV, Phi-3-mini, Qwen3-4B (M = 1, 8), LM heads with "
+            "argmax, and MoE shapes",
             "",
             "Command (from the repository root, on one MI355X): `python3 bench.py --gemv-table`",
             "",
@@ -377,7 +399,9 @@ def write_gemv_table(rows):
             "kernel's own dispatch time (q4_timer_arm events, mean of 64 launches); `us/call` "
             "is the time per call of 20-200 calls back to back (one event pair, includes "
             "the gaps between launches). GB/s = weight bytes (0.5625 B per weight) / "
-            "us/kernel (us/call for the MoE layer, which is 5 kernels).",
+            "us/kernel, except for the rows that run several kernels per call (the LM head + "
+            "argmax: 2 kernels at M = 1, 4 at M = 8; the MoE layer: 5), where it is weight "
+            "bytes / us/call. For those rows us/kernel is the first matvec kernel alone.",
             "",
             "| workload | shape | M | weight bytes | us/kernel | us/call | GB/s | % of 8 TB/s | note |",
             "|---|---|---|---|---|---|---|---|---|"]

@@ -118,6 +118,15 @@ size_t moe_part_bytes(int N, int K, int P);
 q4_status launch_gemv_mfma(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
                            uint16_t *y, float *yf, int64_t ldy, int N, int K, int M,
                            hipStream_t stream);
+// One matrix-core launch for mt <= 16 activation rows. With mfma_splits(K) > 1
+// it leaves f32 partials part[ks][m][n] (mfma_part_bytes(N, K) bytes) and
+// writes neither y nor yf; otherwise the results go to yf (f32) when set, else
+// to y (f16).
+int mfma_splits(int K);
+size_t mfma_part_bytes(int N, int K);
+q4_status launch_mfma_rows(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
+                           uint16_t *y, float *yf, int64_t ldy, int N, int K, int mt,
+                           float *part, hipStream_t stream);
 // LM head and greedy argmax (q4_lmhead.hip)
 q4_status launch_gemv_f32(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
                           float *y, int64_t ldy, int N, int K, int M, hipStream_t stream);

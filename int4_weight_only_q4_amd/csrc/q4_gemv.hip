@@ -56,7 +56,8 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams a)
     extern __shared__ uint4 smem[];
     __shared__ float red[4];
     __shared__ float vals[EPI == EPI_SILU ? RB : 1];
-    __shared__ unsigned long long wkey[EPI == EPI_LOGITS ? kWaves : 1];
+    __shared__ unsigned long long wkey;  // LOGITS: the workgroup's best key so far
+    __shared__ uint32_t wdone;           // LOGITS: waves that have added theirs
 
     const int G = a.G;
     const int K = G * 32;
@@ -148,6 +149,10 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams a)
         const int c = tid + 256 * q;
         put_chunk(xr[q], c, c < chunks, xs, cs);
     }
+    if (EPI == EPI_LOGITS && tid == 0) {
+        wkey = 0;
+        wdone = 0;
+    }
     __syncthreads();
 
     // 3. dequantise and accumulate, in load order
@@ -202,16 +207,21 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams a)
                     key = k > key ? k : key;
                 }
         if (a.cand) {
-            key = wave_max_u64(key);
-            if (lane == 0)
-                wkey[wave] = key;
-            __syncthreads();
-            if (tid == 0) {
-                unsigned long long m = wkey[0];
+            // only the segment leaders (lanes 0, LPR, 2 LPR, ...) hold rows
 #pragma unroll
-                for (int w = 1; w < kWaves; ++w)
-                    m = wkey[w] > m ? wkey[w] : m;
-                a.cand[blockIdx.x] = m;
+            for (int off = LPR; off < 64; off <<= 1) {
+                const unsigned long long o = __shfl_xor(key, off, 64);
+                key = o > key ? o : key;
+            }
+            // the wave's key into LDS; the last wave to arrive stores the
+            // workgroup's (no barrier: the other waves leave at once)
+            if (lane == 0) {
+                __hip_atomic_fetch_max(&wkey, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                const uint32_t before = __hip_atomic_fetch_add(&wdone, 1u, __ATOMIC_ACQ_REL,
+                                                               __HIP_MEMORY_SCOPE_WORKGROUP);
+                if (before == kWaves - 1)
+                    a.cand[blockIdx.x] =
+                        __hip_atomic_load(&wkey, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
         }
     } else {  // EPI_RESID: the residual add of an add+RMSNorm, row by row

@@ -3,27 +3,25 @@
 //
 // What is computed is the group-quantised matvec of the Zero TVM Documentation
 // ("Q4F16 quantization format"; the batched decode of "WGSL Kernel Roles"):
-// y[m][n] = sum_k (q[n][k] - 7) * s[n][k/32] * x[m][k]. At M >= 2 the shared
-// weight read makes it a small dense contraction, so it runs on
-// v_mfma_f32_16x16x32_f16 (one MFMA = 16 activation rows x 16 weight rows x
-// one 32-element quantisation group):
-//  * the B operand is the weights w = (q - 7) * s, dequantised in registers as
-//    two binary16 vectors hi + lo whose sum is exact (dequant_split), each
-//    multiplied by the activation on the matrix core with f32 accumulation:
-//    no dequantised weight is rounded;
+// y[m][n] = sum_g s[n][g] * sum_{k in g} (q[n][k] - 7) * x[m][k]. At M >= 2
+// the shared weight read makes it a small dense contraction, so the inner sums
+// run on v_mfma_f32_16x16x32_f16, one MFMA per quantisation group of 16
+// weight rows and 16 activation rows:
+//  * the B operand is the codes as the exact binary16 integers q - 7 and the
+//    product with the f16 activation is exact; the group's f32 sum is then
+//    multiplied by the group's scale in f32, as in the single-row matvec. No
+//    dequantised weight is ever rounded to f16;
 //  * the A operand is the activation, staged once per workgroup in LDS; rows
-//    m >= M of the MFMA tile are never stored;
-//  * a lane (row n = lane % 16, k-block kb = lane / 16) loads one 16-byte
+//    m >= M of the MFMA tile repeat row M - 1 and are never stored;
+//  * a lane (row n = lane % 16, lane row kb = lane / 16) loads one 16-byte
 //    group of its row per step (four consecutive groups per wave and step, 64
-//    bytes contiguous per row), and MFMA t of the step takes word t of that
-//    group: lane (., kb) of both operands then covers k = 32 (g0 + kb) + 8 t +
-//    0..7, so A and B agree on every k and each 16-byte load feeds four MFMA
-//    pairs;
+//    bytes contiguous per row); a 4 x 4 transpose across the lane rows
+//    (permlane16/32 swaps) then gives each lane row one word of every group,
+//    which is the B layout of an MFMA covering one group;
 //  * about three workgroups per CU stay resident: each stages its activation
-//    chunk once and its waves then loop over 16-row tiles, a tile's 8 KB of
-//    weights in flight per wave (an activation staging per tile would queue
-//    behind the other workgroups' weight loads on the CU);
-//  * K is split into chunks of 1024 values (the staged activation);
+//    chunk once and its waves then take up to four 16-row tiles each, a
+//    tile's 4 KB of weights in flight per wave;
+//  * K is split into chunks of 512 values (the staged activation);
 //    the f32 partials are summed by a second kernel in a fixed order, so
 //    results are identical run to run.
 #include <algorithm>
@@ -42,49 +40,99 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;            // 16 weight rows per wave
 constexpr int kRowsPerWg = 16 * kWaves;
-constexpr int kDepth = 8;            // steps (4 groups each) of weight loads issued together
-constexpr int kGroupsPerSplit = 32;  // K chunk per workgroup: 1024 values
-constexpr int kBatches = kGroupsPerSplit / (4 * kDepth);  // load batches per tile
+constexpr int kDepth = 4;            // steps (4 groups each) of one tile's weight loads
+constexpr int kGroupsPerSplit = 4 * kDepth;  // K chunk per workgroup: 512 values
 constexpr int kMTile = 16;           // activation rows per launch
 constexpr int kXq = (kMTile * kGroupsPerSplit * 4 + 255) / 256;  // x chunks per thread
-constexpr int kMaxTilesPerWave = 4;  // finished tiles wait in LDS until the loop ends
+constexpr int kMaxTilesPerWave = 4;  // finished tiles wait in LDS until the last is done
 constexpr int kMoePerSlot = 0, kMoeSilu = 1, kMoeCombine = 2;
 
-// The 8 weights of word w, w = (q - 7) * s, as two binary16 vectors whose sum
-// is exact: hi = f16((q - 7) * s) and lo = (q - 7) * s - hi. Codes become
-// exact binary16 integers 1024 + q through the exponent pattern 0x6400 and
-// 1031 is subtracted exactly; the product of a 4-bit integer and a binary16
-// scale has at most 15 significant bits, so its rounding residual has at most
-// 4 and lies on the product's own grid (no finer than 2^-18 for scales above
-// 2^-8): it is exactly representable (as a subnormal if small) and a fused
-// multiply-add with one rounding returns it exactly.
-__device__ __forceinline__ void dequant_split(uint32_t w, half2v s2, half8 &hi, half8 &lo)
+// The 8 codes of word w as the exact binary16 integers q - 7, in the pair
+// order (e0, e4) (e1, e5) (e2, e6) (e3, e7): (w >> 4i) & 0x000F000F puts codes i
+// and i + 4 in the two halves, the exponent pattern 0x6400 makes them 1024 + q
+// and subtracting 1031 is exact. The activation is staged in the same order.
+__device__ __forceinline__ half8 codes_minus7(uint32_t w, uint32_t mask)
 {
     const half2v c1031 = {(_Float16)1031.0f, (_Float16)1031.0f};
+    half8 out;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const uint32_t u = w >> (8 * p);
-        const uint32_t bits = (u & 0xFu) | ((u & 0xF0u) << 12) | 0x64006400u;
+    for (int i = 0; i < 4; ++i) {
+        // (mask & (w >> 4i)) | (~mask & 0x64006400) in one bitfield insert
+        // (mask = 0x000F000F sits in a register: an instruction of this
+        // encoding takes at most one constant)
+        uint32_t bits;
+        asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(bits) : "v"(mask), "v"(w >> (4 * i)), "s"(0x64006400u));
         const half2v q = __builtin_bit_cast(half2v, bits) - c1031;
-        const half2v h = q * s2;
-        const half2v r = __builtin_elementwise_fma(q, s2, -h);
-        hi[2 * p] = h[0];
-        hi[2 * p + 1] = h[1];
-        lo[2 * p] = r[0];
-        lo[2 * p + 1] = r[1];
+        out[2 * i] = q[0];
+        out[2 * i + 1] = q[1];
     }
+    return out;
 }
 
-__device__ __forceinline__ uint32_t word(const uint4 &v, int t)
+// Cross-row exchanges of a wave (rows = lanes 16r .. 16r + 15): permlane16
+// swaps row 1 of a with row 0 of b and row 3 of a with row 2 of b; permlane32
+// swaps rows 2, 3 of a with rows 0, 1 of b.
+__device__ __forceinline__ void swap16(uint32_t &a, uint32_t &b)
 {
-    return t == 0 ? v.x : (t == 1 ? v.y : (t == 2 ? v.z : v.w));
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
 }
+
+__device__ __forceinline__ void swap32(uint32_t &a, uint32_t &b)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
+}
+
+// 4 x 4 transpose over (lane row, register): afterwards r[t] in row q holds
+// what r[q] held in row t.
+__device__ __forceinline__ void transpose_rows(uint32_t (&r)[4])
+{
+    swap32(r[0], r[2]);
+    swap32(r[1], r[3]);
+    swap16(r[0], r[1]);
+    swap16(r[2], r[3]);
+}
+
+// Row broadcast: afterwards out[t] in every row holds what v held in row t.
+__device__ __forceinline__ void broadcast_rows(uint32_t v, uint32_t (&out)[4])
+{
+    uint32_t p = v, q = v;
+    swap16(p, q);  // p: rows 0, 0, 2, 2; q: rows 1, 1, 3, 3
+    uint32_t p2 = p, q2 = q;
+    swap32(p, p2);  // p: row 0 everywhere; p2: row 2
+    swap32(q, q2);  // q: row 1; q2: row 3
+    out[0] = p;
+    out[1] = q;
+    out[2] = p2;
+    out[3] = q2;
+}
+
+// A 16-byte chunk of 8 activations x0..x7 in the pair order of codes_minus7.
+__device__ __forceinline__ u32x4 pair_order(u32x4 v)
+{
+    return u32x4{__builtin_amdgcn_perm(v.z, v.x, 0x05040100u),
+                 __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
+                 __builtin_amdgcn_perm(v.w, v.y, 0x05040100u),
+                 __builtin_amdgcn_perm(v.w, v.y, 0x07060302u)};
+}
+
+// The loads of one 16-row weight tile of a split: lane (n, kb) holds group
+// 4p + kb of row n (16 bytes) and its scale for step p = 0..kDepth-1.
+struct TileRegs {
+    uint4 w[kDepth];
+    uint32_t s[kDepth];
+};
 
 // The work of one workgroup for one split ks of K (groups [ks * gc, min(G,
 // (ks + 1) * gc)), gc = kGroupsPerSplit) and M <= 16 activation rows:
-// row_ptr(m) gives activation row m; its chunk is staged once, then wave w
-// takes the 16-row weight tiles tile0(w), + tstride, ... one after another,
-// and emit(m, n, value) receives every finished f32 result.
+// row_ptr(m) gives activation row m; wave w takes the 16-row weight tiles
+// tile0(w), + tstride, ... (at most kMaxTilesPerWave), and emit(m, n, value)
+// receives every finished f32 result. The loads of a wave's next tile are in
+// flight while it computes the current one, and the first tile's loads while
+// the workgroup stages its activation.
 template <typename RowPtr, typename Emit>
 __device__ __forceinline__ void mfma_rows(const uint4 *__restrict__ W,
                                           const uint16_t *__restrict__ S, int N, int G, int M,
@@ -92,94 +140,110 @@ __device__ __forceinline__ void mfma_rows(const uint4 *__restrict__ W,
                                           Emit emit)
 {
     extern __shared__ uint4 smem[];
-    const int t = threadIdx.x, l = t & 63, wave = t >> 6;
+    const int t = threadIdx.x, l = t & 63;
     const int g0 = ks * gc, gn = min(gc, G - g0);  // groups of this split, >= 1
     const int xstride = gc * 32 + 8;  // staged row: the chunk plus 16 bytes against bank conflicts
-    // LDS: finished tiles [kWaves][kMaxTilesPerWave][64 lanes] float4, then the activation
-    floatx4 *obuf = reinterpret_cast<floatx4 *>(smem);
-    _Float16 *xs = reinterpret_cast<_Float16 *>(smem + kWaves * kMaxTilesPerWave * 64);
+    // LDS: the activation chunk, M rows
+    _Float16 *xs = reinterpret_cast<_Float16 *>(smem);
     const int cpr = gn * 4;           // 16-byte chunks per staged row
 
-    // 1. the activation chunk (all loads issued together, then stored)
-    u32x4 xr[kXq];
-#pragma unroll
-    for (int q = 0; q < kXq; ++q) {
-        const int c = min(t + 256 * q, M * cpr - 1);  // branch-free: the tail re-reads
-        const int m = c / cpr, j = c - m * cpr;
-        xr[q] = *reinterpret_cast<const u32x4 *>(row_ptr(m) + (int64_t)g0 * 32 + 8 * j);
-    }
-#pragma unroll
-    for (int q = 0; q < kXq; ++q) {
-        const int c = min(t + 256 * q, M * cpr - 1);  // the tail rewrites the last chunk
-        const int m = c / cpr, j = c - m * cpr;
-        *reinterpret_cast<u32x4 *>(xs + m * xstride + 8 * j) = xr[q];
-    }
-    __syncthreads();
-
-    // 2. this wave's tiles, one after another, each in kBatches batches whose
-    //    loads (20 per lane) are issued together and consumed in the same
-    //    iteration; the resident waves of the CU (16) overlap one another's
-    //    loads. (Loads kept in flight across iterations make the compiler copy,
-    //    and so wait for, them at the loop edge.)
+    // the tiles of this wave (a wave-uniform count: the guards below are
+    // scalar branches)
+    tile0 = __builtin_amdgcn_readfirstlane(tile0);
     const int ntiles = (N + 15) >> 4;
     const int my_tiles = tile0 < ntiles ? (ntiles - 1 - tile0) / tstride + 1 : 0;
     const int n = l & 15, kb = l >> 4;
     const int m = l & 15;
-    const bool mok = m < M;
-    for (int j = 0; j < my_tiles; ++j) {
+    // this lane's A operand row: rows past M repeat row M - 1 (they only feed
+    // MFMA output rows that are never emitted)
+    const _Float16 *xrow = xs + min(m, M - 1) * xstride + 8 * kb;
+    const uint32_t mask = 0x000F000Fu;
+
+    // step p of a tile covers groups 4p .. 4p + 3 of the split; lane (n, kb)
+    // loads group 4p + kb of row n and its scale (branch-free: past the split
+    // it re-reads the last group, which gets scale 0 below)
+    auto load_tile = [&](TileRegs &r, int j) __attribute__((always_inline)) {
         const size_t rb = (size_t)min((tile0 + j * tstride) * 16 + n, N - 1) * G + g0;
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1  // one batch's loads at a time (unrolled, the batches' loads overlap)
-        for (int bt = 0; bt < kBatches; ++bt) {
-            // step p of batch bt covers groups g = 4 kDepth bt + 4p .. + 3 of the
-            // split; lane (n, kb) loads group g + kb of row n (16 bytes) and its
-            // scale; MFMA t of the step takes word t of that group, so lane
-            // (., kb) of both operands covers k = 32 (g + kb) + 8 t + 0..7
-            const int gb = 4 * kDepth * bt;
-            uint4 wq[kDepth];
-            uint32_t sq[kDepth];
 #pragma unroll
-            for (int p = 0; p < kDepth; ++p) {
-                const int gi = min(gb + 4 * p + kb, gn - 1);
-                wq[p] = load_weights(W + rb + gi);
-                sq[p] = load_scale(S + rb + gi);
-            }
+        for (int p = 0; p < kDepth; ++p) {
+            const int gi = min(4 * p + kb, gn - 1);
+            r.w[p] = load_weights(W + rb + gi);
+            r.s[p] = load_scale(S + rb + gi);
+        }
+    };
+    // Step p covers groups 4p .. 4p + 3 of the split, loaded by lane rows
+    // 0..3. After a transpose, lane (n, kb) holds word kb of group 4p + t in
+    // register t, so MFMA t takes exactly group 4p + t of the 16 rows: its B
+    // operand is the exact integers q - 7 and its f32 result, the group's sum
+    // of (q - 7) x, is scaled by that group's scale (broadcast from lane row t;
+    // 0 past the split).
+    auto compute_tile = [&](const TileRegs &r) __attribute__((always_inline)) {
+        const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+        floatx4 acc = zero;
 #pragma unroll
-            for (int p = 0; p < kDepth; ++p) {
-                const int gi = gb + 4 * p + kb;
-                const _Float16 *xa = xs + m * xstride + min(gi, gn - 1) * 32;
-                half8 a[4];
+        for (int p = 0; p < kDepth; ++p) {
+            half8 a[4];
 #pragma unroll
-                for (int tt = 0; tt < 4; ++tt)  // the four activation reads first
-                    a[tt] = mok ? *reinterpret_cast<const half8 *>(xa + 8 * tt) : half8{};
-                // groups past the split get scale 0
-                const uint16_t s16 = gi < gn ? (uint16_t)sq[p] : (uint16_t)0;
-                const _Float16 sh = __builtin_bit_cast(_Float16, s16);
-                const half2v s2 = {sh, sh};
+            for (int tt = 0; tt < 4; ++tt)  // the four activation reads first
+                a[tt] = *reinterpret_cast<const half8 *>(xrow + min(4 * p + tt, gn - 1) * 32);
+            uint32_t sc[4];
+            broadcast_rows(4 * p + kb < gn ? r.s[p] : 0u, sc);
+            uint32_t w[4] = {r.w[p].x, r.w[p].y, r.w[p].z, r.w[p].w};
+            transpose_rows(w);
 #pragma unroll
-                for (int tt = 0; tt < 4; ++tt) {
-                    half8 bh, bl;
-                    dequant_split(word(wq[p], tt), s2, bh, bl);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[tt], bh, acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[tt], bl, acc, 0, 0, 0);
-                }
+            for (int tt = 0; tt < 4; ++tt) {
+                const floatx4 d =
+                    __builtin_amdgcn_mfma_f32_16x16x32_f16(a[tt], codes_minus7(w[tt], mask), zero, 0, 0, 0);
+                const float sf = h2f((uint16_t)sc[tt]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[e] = fmaf(sf, d[e], acc[e]);
             }
         }
-        // park the finished tile in LDS: a global store here would count
-        // against the next tile's weight loads
-        obuf[(wave * kMaxTilesPerWave + j) * 64 + l] = acc;
-    }
+        return acc;
+    };
 
-    // 3. emit this wave's tiles: lane holds D[4 * (l / 16) + r][l % 16]
-    for (int j = 0; j < my_tiles; ++j) {
-        const floatx4 d = obuf[(wave * kMaxTilesPerWave + j) * 64 + l];
+    // 1. the activation chunk (all loads issued together, then stored in the
+    //    pair order)
+    u32x4 xr[kXq];
+#pragma unroll
+    for (int q = 0; q < kXq; ++q) {
+        const int c = min(t + 256 * q, M * cpr - 1);  // branch-free: the tail re-reads
+        const int mm = c / cpr, jj = c - mm * cpr;
+        xr[q] = *reinterpret_cast<const u32x4 *>(row_ptr(mm) + (int64_t)g0 * 32 + 8 * jj);
+    }
+#pragma unroll
+    for (int q = 0; q < kXq; ++q) {
+        const int c = min(t + 256 * q, M * cpr - 1);  // the tail rewrites the last chunk
+        const int mm = c / cpr, jj = c - mm * cpr;
+        *reinterpret_cast<u32x4 *>(xs + mm * xstride + 8 * jj) = pair_order(xr[q]);
+    }
+    __syncthreads();
+
+    // 2. the wave's tiles, one after another: a tile's loads are issued
+    //    together and consumed in the same step (loads kept in flight across
+    //    steps make the compiler copy, and so wait for, them); the resident
+    //    waves of the CU overlap one another. Finished tiles stay in registers
+    //    (a global store here would count against the loads in flight).
+    floatx4 res[kMaxTilesPerWave];
+#pragma unroll
+    for (int j = 0; j < kMaxTilesPerWave; ++j)
+        if (j < my_tiles) {
+            TileRegs r;
+            load_tile(r, j);
+            res[j] = compute_tile(r);
+        }
+
+    // 3. emit: lane holds D[4 * (l / 16) + r][l % 16] of each tile
+#pragma unroll
+    for (int j = 0; j < kMaxTilesPerWave; ++j) {
         const int col = (tile0 + j * tstride) * 16 + n;
-        if (col < N)
+        if (j < my_tiles && col < N)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int mr = 4 * kb + r;
                 if (mr < M)
-                    emit(mr, col, d[r]);
+                    emit(mr, col, res[j][r]);
             }
     }
 }
@@ -187,7 +251,8 @@ __device__ __forceinline__ void mfma_rows(const uint4 *__restrict__ W,
 // Batched matvec: grid (P, KS), 256 threads; wave w of workgroup b takes the
 // tiles b * 4 + w, + 4 P, ... KS == 1: the f32 result written to yf when set,
 // else rounded to y; KS > 1: f32 partials part[ks][m][n] for k_combine.
-__global__ __launch_bounds__(256) void k_gemv_mfma(const uint4 *__restrict__ W,
+// (at most 128 registers: four waves per SIMD)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_gemv_mfma(const uint4 *__restrict__ W,
                                                    const uint16_t *__restrict__ S,
                                                    const uint16_t *__restrict__ x, int64_t ldx,
                                                    uint16_t *__restrict__ y,
@@ -213,7 +278,7 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(const uint4 *__restrict__ W,
 // distinct expert of the routing (meta from k_moe_route), whose pairs (token,
 // slot) form the activation rows, 16 at a time. Per-pair f32 results go to
 // part[ks][pair][n].
-__global__ __launch_bounds__(256) void k_moe_mfma(const uint4 *__restrict__ Wall,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_moe_mfma(const uint4 *__restrict__ Wall,
                                                   const uint16_t *__restrict__ Sall,
                                                   const int32_t *__restrict__ meta, int P,
                                                   const uint16_t *__restrict__ x, int64_t ldx,
@@ -334,36 +399,54 @@ int cus()
 
 }  // namespace
 
-q4_status launch_gemv_mfma(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
-                           uint16_t *y, float *yf, int64_t ldy, int N, int K, int M,
-                           hipStream_t stream)
+int mfma_splits(int K)
+{
+    return (K / 32 + kGroupsPerSplit - 1) / kGroupsPerSplit;
+}
+
+size_t mfma_part_bytes(int N, int K)
+{
+    const int KS = mfma_splits(K);
+    return KS > 1 ? (size_t)KS * kMTile * N * sizeof(float) : 0;
+}
+
+q4_status launch_mfma_rows(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
+                           uint16_t *y, float *yf, int64_t ldy, int N, int K, int mt,
+                           float *part, hipStream_t stream)
 {
     const int G = K / 32;
     // K splits of kGroupsPerSplit groups (the last may be shorter)
     const int gc = kGroupsPerSplit;
-    const int KS = (G + gc - 1) / gc;
+    const int KS = mfma_splits(K);
     const int ntiles = (N + 15) / 16;
     // about three resident workgroups per CU, each looping over its tiles (at
     // most kMaxTilesPerWave per wave)
     const int P = std::max({1, (ntiles + kWaves * kMaxTilesPerWave - 1) / (kWaves * kMaxTilesPerWave),
                             std::min((ntiles + kWaves - 1) / kWaves, (3 * cus() + KS - 1) / KS)});
+    const size_t lds = (size_t)mt * (gc * 32 + 8) * 2;  // staged rows
+    Q4_LAUNCH_MATVEC(k_gemv_mfma, dim3(P, KS), dim3(256), lds, stream,
+                     reinterpret_cast<const uint4 *>(W), S, x, ldx, yf ? nullptr : y, yf, ldy,
+                     part, N, G, mt, gc);
+    return check_launch("k_gemv_mfma");
+}
+
+q4_status launch_gemv_mfma(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
+                           uint16_t *y, float *yf, int64_t ldy, int N, int K, int M,
+                           hipStream_t stream)
+{
+    const int KS = mfma_splits(K);
     float *part = nullptr;
+    if (KS > 1) {
+        char *ws = static_cast<char *>(workspace(stream, kWsHeader + mfma_part_bytes(N, K)));
+        if (!ws)
+            return Q4_EHIP;
+        part = reinterpret_cast<float *>(ws + kWsHeader);
+    }
     for (int m0 = 0; m0 < M; m0 += kMTile) {
         const int mt = std::min(kMTile, M - m0);
-        const size_t lds = (size_t)kWaves * kMaxTilesPerWave * 64 * 16 +  // finished tiles
-                           (size_t)mt * (gc * 32 + 8) * 2;  // staged rows of this launch
-        if (KS > 1 && !part) {
-            char *ws = static_cast<char *>(
-                workspace(stream, kWsHeader + (size_t)KS * kMTile * N * sizeof(float)));
-            if (!ws)
-                return Q4_EHIP;
-            part = reinterpret_cast<float *>(ws + kWsHeader);
-        }
-        Q4_LAUNCH_MATVEC(k_gemv_mfma, dim3(P, KS), dim3(256), lds, stream,
-                         reinterpret_cast<const uint4 *>(W), S, x + m0 * ldx, ldx,
-                         yf ? nullptr : y + m0 * ldy, yf ? yf + m0 * ldy : nullptr, ldy, part, N,
-                         G, mt, gc);
-        q4_status st = check_launch("k_gemv_mfma");
+        q4_status st = launch_mfma_rows(W, S, x + m0 * ldx, ldx, yf ? nullptr : y + m0 * ldy,
+                                        yf ? yf + m0 * ldy : nullptr, ldy, N, K, mt, part,
+                                        stream);
         if (st != Q4_OK)
             return st;
         if (KS > 1) {
@@ -387,7 +470,7 @@ q4_status launch_moe_mfma(const uint32_t *W, const uint16_t *S, const int32_t *i
     const int gc = kGroupsPerSplit, KS = (G + gc - 1) / gc;
     const int ntiles = (N + 15) / 16;
     const dim3 grid((ntiles + kWaves - 1) / kWaves, KS, std::min(P, E));
-    const size_t lds = (size_t)kWaves * kMaxTilesPerWave * 64 * 16 + (size_t)kMTile * (gc * 32 + 8) * 2;
+    const size_t lds = (size_t)kMTile * (gc * 32 + 8) * 2;  // staged rows
     Q4_LAUNCH_MATVEC(k_moe_mfma, grid, dim3(256), lds, stream, reinterpret_cast<const uint4 *>(W),
                      S, meta, P, x, ldx, x_slot_stride, TOPK, part, N, G, gc);
     q4_status st = check_launch("k_moe_mfma");
