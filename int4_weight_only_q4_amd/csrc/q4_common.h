@@ -106,13 +106,16 @@ q4_status launch_gemv_op(const GemvOp &op, hipStream_t stream);
 // Workgroups of one launch_gemv_op for N rows of K (the candidates LOGITS writes).
 int matvec_blocks(int N, int K);
 // MoE expert matvecs on the matrix cores (q4_mfma.hip): meta from the routing
-// kernel, part = f32 scratch of moe_part_bytes(N, K, T * TOPK); mode 0 per-slot
-// outputs, 1 SiLU-multiply of the gate and up halves, 2 routing-weighted combine.
+// kernel, or nullptr when moe_routes_in_kernel(P, E); part = f32 scratch of
+// moe_part_bytes(N, K, T * TOPK); mode 0 per-slot outputs, 1 SiLU-multiply of
+// the gate and up halves, 2 routing-weighted combine.
 q4_status launch_moe_mfma(const uint32_t *W, const uint16_t *S, const int32_t *ids,
                           const int32_t *meta, const uint16_t *route_w, const uint16_t *x,
                           int64_t ldx, int64_t x_slot_stride, uint16_t *y, float *part, int E,
                           int N, int K, int T, int TOPK, int mode, hipStream_t stream);
 size_t moe_part_bytes(int N, int K, int P);
+// Whether the expert kernel routes by itself (meta == nullptr) for P pairs and E experts.
+bool moe_routes_in_kernel(int P, int E);
 // M >= 2 rows on the matrix cores (q4_mfma.hip): f16 outputs y, or f32
 // outputs yf when yf is set (y is then ignored)
 q4_status launch_gemv_mfma(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,

@@ -274,23 +274,118 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
         });
 }
 
-// MoE expert stage: grid (ceil(ntiles / 4), KS, slots); blockIdx.z is a
-// distinct expert of the routing (meta from k_moe_route), whose pairs (token,
-// slot) form the activation rows, 16 at a time. Per-pair f32 results go to
-// part[ks][pair][n].
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_moe_mfma(const uint4 *__restrict__ Wall,
-                                                  const uint16_t *__restrict__ Sall,
-                                                  const int32_t *__restrict__ meta, int P,
-                                                  const uint16_t *__restrict__ x, int64_t ldx,
-                                                  int64_t slot_stride, int TOPK,
-                                                  float *__restrict__ part, int N, int G, int gc)
+// Block-wide exclusive prefix sum over 256 threads (wave scans, then the wave
+// totals); `red` is 4 ints of LDS. Returns the prefix, *total the sum.
+__device__ __forceinline__ int block_exclusive_scan(int v, int *red, int *total)
 {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off, 64);
+        if (lane >= off)
+            incl += o;
+    }
+    if (lane == 63)
+        red[wave] = incl;
+    __syncthreads();
+    int before = 0, sum = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        before += w < wave ? red[w] : 0;
+        sum += red[w];
+    }
+    __syncthreads();
+    *total = sum;
+    return before + incl - v;
+}
+
+// Routing of one workgroup when the pairs and experts are few (P <= kFusePairs,
+// E <= kFuseExperts): the d-th distinct expert (in increasing id order) of the
+// valid ids and its pairs in pair order, as k_moe_route would list them.
+// Returns the expert, or -1 when there are d or fewer distinct experts.
+constexpr int kFusePairs = 256;
+constexpr int kFuseExperts = 1024;
+__device__ int route_in_workgroup(const int32_t *__restrict__ ids, int P, int E, int d,
+                                  int *cnt, int *pairs, int *npairs)
+{
+    __shared__ int red[4];
+    __shared__ int s_e;
+    const int t = threadIdx.x;
+    for (int i = t; i < E; i += 256)
+        cnt[i] = 0;
+    if (t == 0)
+        s_e = -1;
+    __syncthreads();
+    const int my = t < P ? ids[t] : -1;
+    const bool valid = my >= 0 && my < E;
+    if (valid)
+        atomicAdd(&cnt[my], 1);
+    __syncthreads();
+    // thread t owns experts [4t, 4t + 4): the d-th present one is the expert
+    constexpr int kPer = kFuseExperts / 256;
+    int present = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+        present += (kPer * t + i < E && cnt[kPer * t + i] > 0) ? 1 : 0;
+    int total;
+    int rank = block_exclusive_scan(present, red, &total);
+    if (d >= rank && d < rank + present) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+            if (kPer * t + i < E && cnt[kPer * t + i] > 0) {
+                if (rank == d)
+                    s_e = kPer * t + i;
+                ++rank;
+            }
+    }
+    __syncthreads();
+    const int e = s_e;
+    if (e < 0)
+        return -1;
+    // the expert's pairs in pair order
+    int n_e;
+    const int pos = block_exclusive_scan(valid && my == e ? 1 : 0, red, &n_e);
+    if (valid && my == e)
+        pairs[pos] = t;
+    if (t == 0)
+        *npairs = n_e;
+    __syncthreads();
+    return e;
+}
+
+// MoE expert stage: grid (ceil(ntiles / 4), KS, slots); blockIdx.z is a
+// distinct expert of the routing, whose pairs (token, slot) form the activation
+// rows, 16 at a time. The routing comes from k_moe_route (meta), or, for few
+// pairs and experts (meta == nullptr), from the workgroup itself. Per-pair f32
+// results go to part[ks][pair][n].
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_moe_mfma(
+    const uint4 *__restrict__ Wall, const uint16_t *__restrict__ Sall,
+    const int32_t *__restrict__ ids, int E, const int32_t *__restrict__ meta, int P,
+    const uint16_t *__restrict__ x, int64_t ldx, int64_t slot_stride, int TOPK,
+    float *__restrict__ part, int N, int G, int gc)
+{
+    __shared__ int s_cnt[kFuseExperts];
+    __shared__ int s_pairs[kFusePairs];
+    __shared__ int s_np;
     const int d = blockIdx.z;
-    if (d >= meta[0])  // fewer distinct experts than slots: the whole workgroup leaves
-        return;
-    const int e = meta[1 + d];
-    const int q0 = meta[1 + P + d], q1 = meta[1 + P + d + 1];
-    const int32_t *order = meta + 2 + 2 * P;
+    int e, q0, q1;
+    const int32_t *order;
+    if (meta) {
+        if (d >= meta[0])  // fewer distinct experts than slots: the whole workgroup leaves
+            return;
+        e = meta[1 + d];
+        q0 = meta[1 + P + d];
+        q1 = meta[1 + P + d + 1];
+        order = meta + 2 + 2 * P;
+    } else {
+        e = route_in_workgroup(ids, P, E, d, s_cnt, s_pairs, &s_np);
+        if (e < 0)
+            return;
+        q0 = 0;
+        q1 = s_np;
+        order = s_pairs;
+    }
     const int ks = blockIdx.y;
     const uint4 *W = Wall + (size_t)e * N * G;
     const uint16_t *S = Sall + (size_t)e * N * G;
@@ -314,8 +409,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
 //  MOE_PER_SLOT: y[p][n] = f16(r);  MOE_SILU: y[p][i] = f16(silu(f16(r_gate)) *
 //  f16(r_up)) over the N / 2 gate and up rows;  MOE_COMBINE: y[t][n] =
 //  f16(sum over slots s, in order, of route_w[t][s] * r[t * TOPK + s][n]).
-// Pairs whose id is outside [0, E) were zeroed by k_moe_route (per-pair modes)
-// or contribute nothing (combine).
+// Pairs whose id is outside [0, E) get zeros (per-pair modes) or contribute
+// nothing (combine).
 __device__ __forceinline__ float moe_sum(const float *part, int KS, int P, int N, int p, int n)
 {
     float v = 0.f;
@@ -351,8 +446,10 @@ __global__ __launch_bounds__(256) void k_moe_finish(int mode, const float *__res
         return;
     const int p = (int)(i / w), c = (int)(i % w);
     const int e = ids[p];
-    if (e < 0 || e >= E)
+    if (e < 0 || e >= E) {  // an invalid id contributes zeros
+        y[(int64_t)p * w + c] = 0;
         return;
+    }
     if (mode == kMoeSilu) {
         const float g = h2f(f2h(moe_sum(part, KS, P, N, p, c)));
         const float u = h2f(f2h(moe_sum(part, KS, P, N, p, w + c)));
@@ -472,7 +569,7 @@ q4_status launch_moe_mfma(const uint32_t *W, const uint16_t *S, const int32_t *i
     const dim3 grid((ntiles + kWaves - 1) / kWaves, KS, std::min(P, E));
     const size_t lds = (size_t)kMTile * (gc * 32 + 8) * 2;  // staged rows
     Q4_LAUNCH_MATVEC(k_moe_mfma, grid, dim3(256), lds, stream, reinterpret_cast<const uint4 *>(W),
-                     S, meta, P, x, ldx, x_slot_stride, TOPK, part, N, G, gc);
+                     S, ids, E, meta, P, x, ldx, x_slot_stride, TOPK, part, N, G, gc);
     q4_status st = check_launch("k_moe_mfma");
     if (st != Q4_OK)
         return st;
@@ -482,6 +579,8 @@ q4_status launch_moe_mfma(const uint32_t *W, const uint16_t *S, const int32_t *i
                        mode, part, KS, P, N, ids, route_w, y, E, TOPK);
     return check_launch("k_moe_finish");
 }
+
+bool moe_routes_in_kernel(int P, int E) { return P <= kFusePairs && E <= kFuseExperts; }
 
 size_t moe_part_bytes(int N, int K, int P)
 {

@@ -6,8 +6,10 @@
 // ("MoE Phase B") as a loss on Apple, where caches absorb the repeated weight
 // reads. On MI355X each distinct expert's weights are streamed from HBM once
 // per call instead:
-//   1. k_moe_route (one workgroup) sorts the pairs by expert id, stable in pair
-//      order, and lists the distinct experts in increasing id order;
+//   1. the pairs are sorted by expert id, stable in pair order, and the
+//      distinct experts listed in increasing id order: for a decode-sized
+//      routing (at most 256 pairs and 1024 experts) by every expert workgroup
+//      itself, otherwise by k_moe_route (one workgroup) into a workspace;
 //   2. k_moe_mfma (q4_mfma.hip) runs one grid slice per distinct expert: the
 //      expert's pairs are the activation rows of a small matrix-core matvec
 //      that reads each weight once;
@@ -26,9 +28,7 @@ enum { MOE_PER_SLOT = 0, MOE_SILU = 1, MOE_COMBINE = 2 };
 // in `order`, [2P+2 .. 3P+1] order = pair indices sorted by (expert, pair).
 // O(P^2) comparisons in one workgroup; P <= Q4_MAX_PAIRS.
 __global__ __launch_bounds__(256) void k_moe_route(const int32_t *__restrict__ ids, int P, int E,
-                                                   int32_t *__restrict__ meta,
-                                                   uint16_t *__restrict__ y, int out_w,
-                                                   int zero_invalid)
+                                                   int32_t *__restrict__ meta)
 {
     extern __shared__ int32_t sid[];  // [P] expert or -1, then [P] first-occurrence flags
     int32_t *firstocc = sid + P;
@@ -56,12 +56,8 @@ __global__ __launch_bounds__(256) void k_moe_route(const int32_t *__restrict__ i
     int local_nd = 0, local_valid = 0;
     for (int p = threadIdx.x; p < P; p += 256) {
         const int e = sid[p];
-        if (e < 0) {
-            if (zero_invalid)
-                for (int i = 0; i < out_w; ++i)
-                    y[(int64_t)p * out_w + i] = 0;
+        if (e < 0)
             continue;
-        }
         int rank = 0, below = 0, slot = 0;
         for (int q = 0; q < P; ++q) {
             const int f = sid[q];
@@ -100,20 +96,21 @@ q4_status launch_moe(const uint32_t *W, const uint16_t *S, const int32_t *ids,
 {
     const int P = T * TOPK;
     const int mode = epi_silu ? MOE_SILU : (route_w ? MOE_COMBINE : MOE_PER_SLOT);
-    const size_t meta_bytes = ((size_t)(3 * P + 2) * 4 + 255) / 256 * 256;
+    const bool in_kernel = moe_routes_in_kernel(P, E);
+    const size_t meta_bytes = in_kernel ? 0 : ((size_t)(3 * P + 2) * 4 + 255) / 256 * 256;
     char *ws = static_cast<char *>(
         workspace(stream, kWsHeader + meta_bytes + moe_part_bytes(N, K, P)));
     if (!ws)
         return Q4_EHIP;
-    int32_t *meta = reinterpret_cast<int32_t *>(ws + kWsHeader);
+    int32_t *meta = in_kernel ? nullptr : reinterpret_cast<int32_t *>(ws + kWsHeader);
     float *part = reinterpret_cast<float *>(ws + kWsHeader + meta_bytes);
-
-    const int out_w = mode == MOE_SILU ? N / 2 : N;
-    hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(256), (size_t)P * 8, stream, ids, P, E, meta, y,
-                       out_w, mode != MOE_COMBINE ? 1 : 0);
-    q4_status st = check_launch("k_moe_route");
-    if (st != Q4_OK)
-        return st;
+    if (!in_kernel) {
+        hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(256), (size_t)P * 8, stream, ids, P, E,
+                           meta);
+        q4_status st = check_launch("k_moe_route");
+        if (st != Q4_OK)
+            return st;
+    }
     return launch_moe_mfma(W, S, ids, meta, route_w, x, ldx, x_slot_stride, y, part, E, N, K, T,
                            TOPK, mode, stream);
 }

@@ -198,3 +198,24 @@ def test_batched_one_hot_rows_are_exact(o, q4, n, k, m):
         g = ks[i] // 32  # the oracle dequantises the group holding column k_m
         grp = o.dequant(W[:, 4 * g:4 * g + 4], S[:, g:g + 1])
         assert np.array_equal(Y[i], o.d2h(grp[:, ks[i] % 32]).view(np.uint16)), i
+
+
+@pytest.mark.parametrize("t,topk,e", [(40, 8, 32), (2, 4, 1100), (32, 8, 64)])
+def test_moe_routing_paths(o, q4, t, topk, e):
+    """Routings beyond the in-kernel limit (more than 256 pairs, more than 1024
+    experts) take the sorting kernel; 256 pairs exactly stay in the kernel.
+    Per-slot and combine modes against the oracle, repeated ids included."""
+    n, k = 48, 128
+    W, S = experts(o, 1400 + e, e, n, k)
+    ids = np.random.default_rng(e + t).integers(0, e, size=(t, topk)).astype(np.int32)
+    ids[0, :2] = ids[0, 2]  # the same expert twice within a token
+    rw = (np.random.default_rng(t).random((t, topk)) / topk).astype(np.float16)
+    x = datagen.activations(1401 + e, t * topk, k)
+    Wd, Sd, idsd, xd = dev_tensor(W), dev_tensor(S), dev_tensor(ids), dev_tensor(x)
+    yp = q4.moe_gemv(Wd, Sd, idsd, xd, ldx=topk * k, x_slot_stride=k)
+    yc = q4.moe_gemv(Wd, Sd, idsd, xd, ldx=topk * k, x_slot_stride=k, route_w=dev_tensor(rw))
+    sync()
+    assert_within(host(yp), o.moe_stage(W, S, ids, None, x, topk * k, k, n, k, epi_silu=False),
+                  "per-slot")
+    assert_within(host(yc), o.moe_stage(W, S, ids, rw, x, topk * k, k, n, k, epi_silu=False),
+                  "combine")
