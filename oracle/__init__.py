@@ -56,6 +56,9 @@ _SIGS = {
     "q4o_stack": (None, [_I] * 6 + [_P] * 8 + [_P, _P, _P, C.c_double] + [_P] * 5),
     "q4o_argmax": (C.c_int64, [_P, _I]),
     "q4o_lm_head": (None, [_P, _P, _P, _I, _I, _I, _I, _P, _P]),
+    "q4o_rope": (None, [_P, _P, _I, _I, _I, C.c_double]),
+    "q4o_qkv_rope": (None, [_P, _P, _P, _I, _I, _I, _I, _I, C.c_double, _P, _P, _P]),
+    "q4o_attention": (None, [_P, _P, _P, _I, _I, _I, _I, _P]),
 }
 
 
@@ -171,6 +174,35 @@ class Oracle:
         self.lib.q4o_lm_head(self._ptr(W), self._ptr(S), self._ptr(X), k, n, k, m,
                              self._ptr(logits), self._ptr(tokens))
         return logits, tokens
+
+    # -- RoPE, KV cache, decode attention --------------------------------------
+    def rope(self, v, head_dim, pos, base=10000.0):
+        """v f64/f16 [n_heads * head_dim] -> rotated f64 (pairs i, i + head_dim/2)."""
+        v = np.ascontiguousarray(np.asarray(v, dtype=np.float64).ravel())
+        out = np.empty_like(v)
+        self.lib.q4o_rope(self._ptr(v), self._ptr(out), v.size // head_dim, head_dim, pos, base)
+        return out
+
+    def qkv_rope(self, W, S, x, n_heads, n_kv, head_dim, pos, base=10000.0):
+        """-> (q_rot f64 [n_heads*hd], k_rot f64 [n_kv*hd], v f64 [n_kv*hd])."""
+        W = np.ascontiguousarray(W, dtype=np.uint32)
+        S, x = self._u16(S), self._u16(x)
+        k = W.shape[1] * 8
+        q = np.empty(n_heads * head_dim, np.float64)
+        kr = np.empty(n_kv * head_dim, np.float64)
+        v = np.empty(n_kv * head_dim, np.float64)
+        self.lib.q4o_qkv_rope(self._ptr(W), self._ptr(S), self._ptr(x), k, n_heads, n_kv,
+                              head_dim, pos, base, self._ptr(q), self._ptr(kr), self._ptr(v))
+        return q, kr, v
+
+    def attention(self, q, kc, vc, n_heads, n_kv, head_dim):
+        """q f16 [n_heads*hd]; kc, vc f16 [L][n_kv][hd] -> f64 [n_heads*hd]."""
+        q, kc, vc = self._u16(q), self._u16(kc), self._u16(vc)
+        L = kc.size // (n_kv * head_dim)
+        out = np.empty(n_heads * head_dim, np.float64)
+        self.lib.q4o_attention(self._ptr(q), self._ptr(kc), self._ptr(vc), L, n_heads, n_kv,
+                               head_dim, self._ptr(out))
+        return out
 
     def add_rmsnorm(self, a, r, gamma, eps=1e-5):
         r = self._u16(np.atleast_2d(r))

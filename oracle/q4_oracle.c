@@ -412,3 +412,96 @@ void q4o_lm_head(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_
         token[b] = q4o_argmax(logits + b * n, n);
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* RoPE, paged KV cache and decode attention (Zero TVM Documentation,       */
+/* "KV cache"; shader 3 "QKV + RoPE + KV-append"; shader 4 "Paged            */
+/* Attention"; shaders 8 and 9, "KV Append" and "RoPE"; "Phi-3 model         */
+/* constants"; BENCH.md, split-K attention).                                 */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Rotary position embedding of n_heads head vectors of head_dim values at
+ * position pos: within each head the pairs are (i, i + head_dim/2), as the
+ * fused QKV shader pairs dim and dim + 48 of a 96-dim head, and pair i turns
+ * by theta_i = pos * base^(-2i/head_dim). The pages give no base; 10000 is the
+ * caller's reading.
+ */
+void q4o_rope(const double *in, double *out, int64_t n_heads, int64_t head_dim, int64_t pos,
+              double base)
+{
+    const int64_t half = head_dim / 2;
+    for (int64_t h = 0; h < n_heads; ++h) {
+        const double *a = in + h * head_dim;
+        double *b = out + h * head_dim;
+        for (int64_t i = 0; i < half; ++i) {
+            const double theta = (double)pos * pow(base, -2.0 * (double)i / (double)head_dim);
+            const double c = cos(theta), s = sin(theta);
+            b[i] = a[i] * c - a[i + half] * s;
+            b[i + half] = a[i + half] * c + a[i] * s;
+        }
+    }
+}
+
+/*
+ * The decode step around the QKV matvec for one token at position pos: qkv =
+ * f16(W . x) (rows: n_heads query heads, then n_kv key heads, then n_kv value
+ * heads, head_dim each), as the separate matvec stores it; q and k rotated in
+ * binary64 and returned unrounded (q_rot [n_heads][head_dim], k_rot
+ * [n_kv][head_dim]); v is the stored f16 slice, returned as its values.
+ */
+void q4o_qkv_rope(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t k,
+                  int64_t n_heads, int64_t n_kv, int64_t head_dim, int64_t pos, double base,
+                  double *q_rot, double *k_rot, double *v)
+{
+    const int64_t nq = n_heads * head_dim, nk = n_kv * head_dim;
+    const int64_t n = nq + 2 * nk;
+    double *y = (double *)malloc(sizeof(double) * (size_t)n);
+    for (int64_t r = 0; r < n; ++r)
+        y[r] = q4o_h2d(q4o_d2h(q4o_row_dot(W, S, x, k, r)));
+    q4o_rope(y, q_rot, n_heads, head_dim, pos, base);
+    q4o_rope(y + nq, k_rot, n_kv, head_dim, pos, base);
+    for (int64_t r = 0; r < nk; ++r)
+        v[r] = y[nq + nk + r];
+    free(y);
+}
+
+/*
+ * Decode attention for one query token over L cached positions: K and V are
+ * f16 [L][n_kv][head_dim] in position order (as read back from the pages);
+ * query head h uses key/value head h / (n_heads / n_kv). For each head
+ *   out[h] = sum_t softmax_t(q_h . k_t * scale) v_t,  scale = 1/sqrt(head_dim)
+ * in binary64, the softmax taken with its maximum subtracted.
+ */
+void q4o_attention(const uint16_t *q, const uint16_t *kc, const uint16_t *vc, int64_t L,
+                   int64_t n_heads, int64_t n_kv, int64_t head_dim, double *out)
+{
+    const int64_t group = n_heads / n_kv;
+    const double scale = 1.0 / sqrt((double)head_dim);
+    double *s = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+    for (int64_t h = 0; h < n_heads; ++h) {
+        const int64_t kvh = h / group;
+        double m = -INFINITY;
+        for (int64_t t = 0; t < L; ++t) {
+            double dot = 0.0;
+            for (int64_t j = 0; j < head_dim; ++j)
+                dot += q4o_h2d(q[h * head_dim + j]) *
+                       q4o_h2d(kc[(t * n_kv + kvh) * head_dim + j]);
+            s[t] = dot * scale;
+            if (s[t] > m)
+                m = s[t];
+        }
+        double l = 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            s[t] = exp(s[t] - m);
+            l += s[t];
+        }
+        for (int64_t j = 0; j < head_dim; ++j) {
+            double acc = 0.0;
+            for (int64_t t = 0; t < L; ++t)
+                acc += s[t] * q4o_h2d(vc[(t * n_kv + kvh) * head_dim + j]);
+            out[h * head_dim + j] = acc / l;
+        }
+    }
+    free(s);
+}

@@ -585,6 +585,114 @@ def pin_lm_head_rows_are_matvec_then_argmax(o):
         assert tok[b] == int(np.argmax(y))
 
 
+# -- RoPE, KV cache, decode attention ------------------------------------------
+# RoPE pairs (i, i + head_dim/2) of a head and turns pair i by pos * base^(-2i/d)
+# (Zero TVM Documentation, shader 3: a RoPE pair is dim and dim + 48 of a 96-dim
+# head); attention is softmax(q . K^T / sqrt(d)) V per head (shader 4).
+
+def pin_rope_closed_form(o):
+    """Unit vectors turn by the closed-form angle: theta_0 = pos, theta_1 = pos *
+    10000^(-2/96); the partner of dim i is dim i + 48."""
+    d = 96
+    cases = [(0, 1), (48, 1), (1, 3), (49, 3), (47, 2)]
+    for dim, pos in cases:
+        v = np.zeros(2 * d)
+        v[d + dim] = 1.0  # second head
+        r = o.rope(v, d, pos)
+        i = dim % 48
+        theta = pos * 10000.0 ** (-2.0 * i / d)
+        c, s_ = math.cos(theta), math.sin(theta)
+        want = np.zeros(2 * d)
+        if dim < 48:
+            want[d + i], want[d + i + 48] = c, s_
+        else:
+            want[d + i], want[d + i + 48] = -s_, c
+        assert np.allclose(r, want, rtol=0, atol=1e-15), (dim, pos)
+
+
+def pin_rope_position_zero_is_identity(o):
+    v = datagen.activations(601, 1, 3 * 96)[0].astype(np.float64)
+    assert np.array_equal(o.rope(v, 96, 0), v)
+
+
+def pin_rope_preserves_pair_norms_and_relative_positions(o):
+    """Each pair keeps its length, and the rotated dot product of a query at m
+    and a key at n depends only on m - n."""
+    d = 96
+    q = datagen.activations(602, 1, 4 * d)[0].astype(np.float64)
+    k = datagen.activations(603, 1, 4 * d)[0].astype(np.float64)
+    for pos in (1, 17, 4095):
+        r = o.rope(q, d, pos).reshape(4, 2, 48)
+        a = q.reshape(4, 2, 48)
+        assert np.allclose((r ** 2).sum(1), (a ** 2).sum(1), rtol=1e-12, atol=1e-12)
+    for m, n, c in ((5, 2, 7), (100, 40, 900), (3, 3, 50)):
+        qa, ka = o.rope(q, d, m).reshape(4, d), o.rope(k, d, n).reshape(4, d)
+        qb, kb = o.rope(q, d, m + c).reshape(4, d), o.rope(k, d, n + c).reshape(4, d)
+        assert np.allclose((qa * ka).sum(1), (qb * kb).sum(1), rtol=1e-9, atol=1e-9)
+
+
+def _attn_numpy(q, kc, vc, n_heads, n_kv, d):
+    """Independent formulation: numpy matmuls and scipy's softmax."""
+    from scipy.special import softmax
+    q = q.astype(np.float64).reshape(n_heads, d)
+    L = kc.size // (n_kv * d)
+    K = kc.astype(np.float64).reshape(L, n_kv, d)
+    V = vc.astype(np.float64).reshape(L, n_kv, d)
+    out = np.empty((n_heads, d))
+    for h in range(n_heads):
+        kv = h // (n_heads // n_kv)
+        p = softmax(K[:, kv, :] @ q[h] / math.sqrt(d))
+        out[h] = p @ V[:, kv, :]
+    return out.ravel()
+
+
+def pin_attention_matches_library_softmax(o):
+    for (nh, nkv, d, L, seed) in ((4, 4, 96, 37, 610), (8, 2, 64, 100, 611), (2, 1, 32, 1, 612)):
+        q = datagen.activations(seed, 1, nh * d)[0]
+        kc = datagen.activations(seed + 1, L, nkv * d)
+        vc = datagen.activations(seed + 2, L, nkv * d)
+        got = o.attention(q, kc, vc, nh, nkv, d)
+        assert np.allclose(got, _attn_numpy(q, kc, vc, nh, nkv, d), rtol=1e-12, atol=1e-12)
+
+
+def pin_attention_special_cases(o):
+    """One position returns its value exactly; equal keys average the values;
+    a dominant key returns its value; GQA equals MHA with repeated kv heads."""
+    d, nh = 96, 4
+    q = datagen.activations(620, 1, nh * d)[0]
+    kc = datagen.activations(621, 1, nh * d)
+    vc = datagen.activations(622, 1, nh * d)
+    assert np.array_equal(o.attention(q, kc, vc, nh, nh, d), o.h2d(vc[0]))
+    L = 10
+    k1 = np.tile(datagen.activations(623, 1, nh * d), (L, 1))
+    vL = datagen.activations(624, L, nh * d)
+    mean = o.h2d(vL).reshape(L, nh * d).mean(0)
+    assert np.allclose(o.attention(q, k1, vL, nh, nh, d), mean, rtol=1e-13, atol=1e-13)
+    kd = np.zeros((L, nh * d), np.float16)
+    kd[4] = (q.astype(np.float64) * 8).astype(np.float16)  # score ~ 8 |q|^2 / sqrt(d)
+    got = o.attention(q, kd, vL, nh, nh, d)
+    assert np.allclose(got, o.h2d(vL[4]), rtol=0, atol=1e-6)
+    nkv = 2
+    kg = datagen.activations(625, L, nkv * d)
+    vg = datagen.activations(626, L, nkv * d)
+    rep = lambda a: np.repeat(a.reshape(L, nkv, d), nh // nkv, axis=1).reshape(L, nh * d)
+    assert np.allclose(o.attention(q, kg, vg, nh, nkv, d),
+                       o.attention(q, rep(kg), rep(vg), nh, nh, d), rtol=0, atol=1e-15)
+
+
+def pin_qkv_rope_is_stored_matvec_then_rope(o):
+    """q and k are the RoPE of the f16-stored matvec rows; v is the stored V rows."""
+    nh, nkv, d, k = 4, 2, 32, 256
+    n = (nh + 2 * nkv) * d
+    _, W, S = _mat(o, 630, n, k)
+    x = datagen.activations(631, 1, k)[0]
+    q, kr, v = o.qkv_rope(W, S, x, nh, nkv, d, 21)
+    y = o.h2d(o.d2h(o.gemv(W, S, x)))
+    assert np.array_equal(q, o.rope(y[:nh * d], d, 21))
+    assert np.array_equal(kr, o.rope(y[nh * d:(nh + nkv) * d], d, 21))
+    assert np.array_equal(v, y[(nh + nkv) * d:])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -617,6 +725,15 @@ MUTANTS = [
     ("argmax_skips_first", "int64_t best = 0;\n    for (int64_t i = 1;", "int64_t best = n > 1 ? 1 : 0;\n    for (int64_t i = 2;"),
     ("lm_head_row_stride_ignored", "q4o_row_dot(W, S, x + b * ldx, k, r);\n        token", "q4o_row_dot(W, S, x, k, r);\n        token"),
     ("lm_head_token_of_first_row", "token[b] = q4o_argmax(logits + b * n, n);", "token[b] = q4o_argmax(logits, n);"),
+    ("rope_sign", "b[i] = a[i] * c - a[i + half] * s;", "b[i] = a[i] * c + a[i + half] * s;"),
+    ("rope_frequency_exponent", "-2.0 * (double)i / (double)head_dim", "-1.0 * (double)i / (double)head_dim"),
+    ("rope_position_ignored", "(double)pos * pow(", "1.0 * pow("),
+    ("rope_adjacent_pairs", "const int64_t half = head_dim / 2;\n    for (int64_t h = 0; h < n_heads; ++h) {\n        const double *a", "const int64_t half = 1;\n    for (int64_t h = 0; h < n_heads; ++h) {\n        const double *a"),
+    ("attention_unscaled", "s[t] = dot * scale;", "s[t] = dot;"),
+    ("attention_kv_head_mapping", "const int64_t kvh = h / group;", "const int64_t kvh = h % n_kv;"),
+    ("attention_values_from_keys", "acc += s[t] * q4o_h2d(vc[", "acc += s[t] * q4o_h2d(kc["),
+    ("qkv_rope_unrounded", "y[r] = q4o_h2d(q4o_d2h(q4o_row_dot(W, S, x, k, r)));", "y[r] = q4o_row_dot(W, S, x, k, r);"),
+    ("qkv_rope_v_slice", "v[r] = y[nq + nk + r];", "v[r] = y[nq + r];"),
 ]
 
 
