@@ -223,6 +223,66 @@ q4_status q4_lm_head_argmax(const uint32_t *W, const uint16_t *S, const uint16_t
                             int64_t K, int64_t M, q4_stream stream);
 
 /* ---------------------------------------------------------------------------
+ * RoPE, paged KV cache and decode attention (Zero TVM Documentation, "KV
+ * cache"; shader 3 "QKV + RoPE + KV-append (fused, decode)"; shader 4 "Paged
+ * Attention"; shaders 8 and 9 "KV Append" and "RoPE"; BENCH.md, split-K
+ * attention with a combine step).
+ *
+ * Geometry: the QKV matvec rows are n_heads query heads, then n_kv key heads,
+ * then n_kv value heads, head_dim rows each. RoPE turns the pairs (i, i +
+ * head_dim/2) of every query and key head by theta_i = pos * rope_base^(-2i /
+ * head_dim) (the pages pair dim and dim + 48 of a 96-dim head; they give no
+ * base: Phi-3 uses 10000). Cache: kv_pages f16
+ * [n_pages][2 (K, V)][n_kv][page_size][head_dim]; position t lives in physical
+ * page page_table[t / page_size], slot t % page_size (the pages use 16-slot
+ * pages and an identity table for one sequence). The position is read from
+ * device memory (pos: one int32), as the pages bind a position map.
+ * Positions, table entries or pages outside the table (max_pages entries) or
+ * the cache (n_pages pages) are neither written nor read.
+ * Rounding: the Q, K, V rows are rounded to f16 as a separate matvec stores
+ * them, rotated in f32 (angles from binary64) and stored as f16.
+ */
+typedef struct q4_attn_desc {
+    int64_t n_heads;    /* query heads */
+    int64_t n_kv;       /* key/value heads; divides n_heads */
+    int64_t head_dim;   /* multiple of 8, <= 256 */
+    int64_t page_size;  /* slots per page */
+    int64_t max_pages;  /* entries of page_table */
+    int64_t n_pages;    /* physical pages in kv_pages */
+    float rope_base;    /* e.g. 10000 */
+} q4_attn_desc;
+
+/* Bytes of one cache page: 2 * n_kv * page_size * head_dim * 2. Host-only. */
+int64_t q4_kv_page_bytes(const q4_attn_desc *desc);
+
+/* q4_qkv_rope_append -- the fused decode step: qkv = W . x (W u32[N][K/8],
+ * S f16[N][K/32], N = (n_heads + 2 n_kv) * head_dim, x f16[K]); q_out f16
+ * [n_heads * head_dim] gets the rotated query; the rotated key and the value
+ * are written to the cache slot of *pos. */
+q4_status q4_qkv_rope_append(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t K,
+                             const q4_attn_desc *desc, const int32_t *pos,
+                             const int32_t *page_table, uint16_t *kv_pages, uint16_t *q_out,
+                             q4_stream stream);
+
+/* q4_rope_append -- the same step from an already stored f16 qkv vector
+ * [(n_heads + 2 n_kv) * head_dim] (the unfused path; bit-identical results). */
+q4_status q4_rope_append(const uint16_t *qkv, const q4_attn_desc *desc, const int32_t *pos,
+                         const int32_t *page_table, uint16_t *kv_pages, uint16_t *q_out,
+                         q4_stream stream);
+
+/* q4_attention_decode -- out f16[n_heads * head_dim]: for query head h and
+ * key/value head h / (n_heads / n_kv),
+ *   out[h] = sum_{t <= *pos} softmax_t(q_h . k_t / sqrt(head_dim)) v_t
+ * over the cached positions 0 .. *pos. The positions are split over up to 16
+ * workgroups per head (max_len, the caller's bound on *pos + 1, sizes the
+ * split) whose partial softmax states (max, sum, weighted values) a second
+ * kernel combines in split order. q f16, 16-byte aligned; out must not overlap
+ * q or the cache. */
+q4_status q4_attention_decode(const uint16_t *q, const uint16_t *kv_pages,
+                              const int32_t *page_table, const int32_t *pos, int64_t max_len,
+                              const q4_attn_desc *desc, uint16_t *out, q4_stream stream);
+
+/* ---------------------------------------------------------------------------
  * q4_stack_decode -- one decode token through a stack of decoder layers whose
  * attention is replaced by the single-position identity on the V slice
  * (Zero TVM Documentation, "Decode loop": per layer QKV matmul -> attention ->

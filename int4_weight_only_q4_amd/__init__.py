@@ -34,7 +34,8 @@ ABI_SYMBOLS = (
     "q4_version", "q4_last_error", "q4_bytes_per_weight", "q4_pack", "q4_unpack", "q4_gemv",
     "q4_gemv_batched", "q4_moe_gemv", "q4_add_rmsnorm", "q4_silu_mul", "q4_gemv_ex",
     "q4_stack_decode", "q4_stack_status", "q4_timer_arm", "q4_timer_read", "q4_gemv_f32",
-    "q4_argmax", "q4_lm_head_argmax",
+    "q4_argmax", "q4_lm_head_argmax", "q4_kv_page_bytes", "q4_qkv_rope_append",
+    "q4_rope_append", "q4_attention_decode",
 )
 
 
@@ -60,6 +61,12 @@ class StackDesc(C.Structure):
                 ("gamma_final", C.c_void_p), ("mode", C.c_int)]
 
 
+class AttnDesc(C.Structure):
+    _fields_ = [("n_heads", C.c_int64), ("n_kv", C.c_int64), ("head_dim", C.c_int64),
+                ("page_size", C.c_int64), ("max_pages", C.c_int64), ("n_pages", C.c_int64),
+                ("rope_base", C.c_float)]
+
+
 _P, _I = C.c_void_p, C.c_int64
 _SIGS = {
     "q4_version": (C.c_char_p, []),
@@ -80,6 +87,10 @@ _SIGS = {
     "q4_gemv_f32": (C.c_int, [_P, _P, _P, _I, _P, _I, _I, _I, _I, _P]),
     "q4_argmax": (C.c_int, [_P, _I, _I, _I, _P, _P]),
     "q4_lm_head_argmax": (C.c_int, [_P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _P]),
+    "q4_kv_page_bytes": (C.c_int64, [C.POINTER(AttnDesc)]),
+    "q4_qkv_rope_append": (C.c_int, [_P, _P, _P, _I, C.POINTER(AttnDesc), _P, _P, _P, _P, _P]),
+    "q4_rope_append": (C.c_int, [_P, C.POINTER(AttnDesc), _P, _P, _P, _P, _P]),
+    "q4_attention_decode": (C.c_int, [_P, _P, _P, _P, _I, C.POINTER(AttnDesc), _P, _P]),
 }
 
 _lib = None
@@ -239,6 +250,55 @@ def lm_head_argmax(W, S, x, logits=None, tokens=None, stream=None):
     _check(lib().q4_lm_head_argmax(_ptr(W), _ptr(S), _ptr(x2), ldx, _ptr(l2), l2.stride(0),
                                    _ptr(tokens), n, k, m, _stream(stream)))
     return logits, tokens
+
+
+def attn_desc(n_heads, n_kv, head_dim, page_size=16, max_pages=257, n_pages=None,
+              rope_base=10000.0):
+    """Geometry of the RoPE / paged-KV / attention calls (see include/q4.h)."""
+    return AttnDesc(n_heads, n_kv, head_dim, page_size, max_pages,
+                    max_pages if n_pages is None else n_pages, rope_base)
+
+
+def kv_page_bytes(desc):
+    return int(lib().q4_kv_page_bytes(C.byref(desc)))
+
+
+def kv_cache(desc, device="cuda"):
+    """A zeroed cache f16 [n_pages][2][n_kv][page_size][head_dim]."""
+    import torch
+    return torch.zeros((desc.n_pages, 2, desc.n_kv, desc.page_size, desc.head_dim),
+                       dtype=torch.float16, device=device)
+
+
+def qkv_rope_append(W, S, x, desc, pos, page_table, kv, q_out=None, stream=None):
+    """Fused decode step: q_out f16 [n_heads * head_dim]; K, V into kv at *pos."""
+    import torch
+    k = W.shape[1] * 8
+    if q_out is None:
+        q_out = torch.empty(desc.n_heads * desc.head_dim, dtype=torch.float16, device=W.device)
+    _check(lib().q4_qkv_rope_append(_ptr(W), _ptr(S), _ptr(x), k, C.byref(desc), _ptr(pos),
+                                    _ptr(page_table), _ptr(kv), _ptr(q_out), _stream(stream)))
+    return q_out
+
+
+def rope_append(qkv, desc, pos, page_table, kv, q_out=None, stream=None):
+    """The same step from a stored f16 qkv vector."""
+    import torch
+    if q_out is None:
+        q_out = torch.empty(desc.n_heads * desc.head_dim, dtype=torch.float16, device=qkv.device)
+    _check(lib().q4_rope_append(_ptr(qkv), C.byref(desc), _ptr(pos), _ptr(page_table), _ptr(kv),
+                                _ptr(q_out), _stream(stream)))
+    return q_out
+
+
+def attention_decode(q, kv, page_table, pos, max_len, desc, out=None, stream=None):
+    """out f16 [n_heads * head_dim] = attention of q over cached positions 0..*pos."""
+    import torch
+    if out is None:
+        out = torch.empty(desc.n_heads * desc.head_dim, dtype=torch.float16, device=q.device)
+    _check(lib().q4_attention_decode(_ptr(q), _ptr(kv), _ptr(page_table), _ptr(pos), int(max_len),
+                                     C.byref(desc), _ptr(out), _stream(stream)))
+    return out
 
 
 def moe_gemv(W, S, ids, x, ldx, x_slot_stride, route_w=None, epi_silu=False, y=None,

@@ -442,6 +442,53 @@ q4_status check_argmax(const float *v, int64_t ld, int64_t N, int64_t M, const i
         return fail(Q4_EALIAS, "the index output overlaps the logits");
     return Q4_OK;
 }
+
+q4_status check_attn_desc(const q4_attn_desc *d, RopeArgs *r)
+{
+    if (!d)
+        return fail(Q4_EINVAL, "NULL attention descriptor");
+    if (d->n_heads < 1 || d->n_kv < 1 || d->n_heads % d->n_kv)
+        return fail(Q4_EINVAL, "n_kv must divide n_heads (n_heads=%lld, n_kv=%lld)",
+                    (long long)d->n_heads, (long long)d->n_kv);
+    if (d->head_dim < 8 || d->head_dim % 8 || d->head_dim > 256)
+        return fail(Q4_ESHAPE, "head_dim=%lld must be a multiple of 8 in [8, 256]",
+                    (long long)d->head_dim);
+    if (d->page_size < 1 || d->max_pages < 1 || d->n_pages < 1)
+        return fail(Q4_EINVAL, "page_size, max_pages and n_pages must be positive");
+    if (d->max_pages * d->page_size > (1ll << 30) || d->n_pages > (1ll << 30) ||
+        (d->n_heads + 2 * d->n_kv) * d->head_dim > (1ll << 30))
+        return fail(Q4_ERANGE, "attention geometry too large");
+    if (!(d->rope_base > 0.f))
+        return fail(Q4_EINVAL, "rope_base must be positive");
+    r->n_heads = (int)d->n_heads;
+    r->n_kv = (int)d->n_kv;
+    r->head_dim = (int)d->head_dim;
+    r->page_size = (int)d->page_size;
+    r->max_pages = (int)d->max_pages;
+    r->n_pages = (int)d->n_pages;
+    r->base = d->rope_base;
+    return Q4_OK;
+}
+
+inline size_t kv_bytes(const RopeArgs &r)
+{
+    return (size_t)r.n_pages * 2 * r.n_kv * r.page_size * r.head_dim * 2;
+}
+
+q4_status check_rope_io(const RopeArgs &r, const int32_t *pos, const int32_t *page_table,
+                        uint16_t *kv, uint16_t *q_out)
+{
+    if (!pos || !page_table || !kv || !q_out)
+        return fail(Q4_EINVAL, "NULL position, page table, cache or q_out pointer");
+    if (!aligned(pos, 4) || !aligned(page_table, 4) || !aligned(kv, 16) || !aligned(q_out, 2))
+        return fail(Q4_EALIGN, "misaligned position, page table (4), cache (16) or q_out (2)");
+    const size_t qb = (size_t)r.n_heads * r.head_dim * 2;
+    if (overlaps(q_out, qb, kv, kv_bytes(r)) || overlaps(q_out, qb, page_table, (size_t)r.max_pages * 4) ||
+        overlaps(kv, kv_bytes(r), page_table, (size_t)r.max_pages * 4) ||
+        overlaps(q_out, qb, pos, 4) || overlaps(kv, kv_bytes(r), pos, 4))
+        return fail(Q4_EALIAS, "q_out, the cache, the page table and the position overlap");
+    return Q4_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -633,6 +680,105 @@ q4_status q4_lm_head_argmax(const uint32_t *W, const uint16_t *S, const uint16_t
         return fail(Q4_EALIAS, "tokens overlap another argument");
     return launch_lm_head_argmax(W, S, x, ldx, logits, ldl, tokens, (int)N, (int)K, (int)M,
                                  as_stream(stream));
+}
+
+int64_t q4_kv_page_bytes(const q4_attn_desc *desc)
+{
+    if (!desc)
+        return 0;
+    return 2 * desc->n_kv * desc->page_size * desc->head_dim * 2;
+}
+
+q4_status q4_qkv_rope_append(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t K,
+                             const q4_attn_desc *desc, const int32_t *pos,
+                             const int32_t *page_table, uint16_t *kv_pages, uint16_t *q_out,
+                             q4_stream stream)
+{
+    RopeArgs r;
+    q4_status st = check_attn_desc(desc, &r);
+    if (st != Q4_OK)
+        return st;
+    const int64_t N = (int64_t)(r.n_heads + 2 * r.n_kv) * r.head_dim;
+    if ((st = check_matrix(W, S, N, K)) != Q4_OK)
+        return st;
+    if (!x)
+        return fail(Q4_EINVAL, "NULL activation");
+    if (!aligned(x, 16))
+        return fail(Q4_EALIGN, "the activation vector must be 16-byte aligned");
+    if ((st = check_rope_io(r, pos, page_table, kv_pages, q_out)) != Q4_OK)
+        return st;
+    const size_t qb = (size_t)r.n_heads * r.head_dim * 2, xb = (size_t)K * 2;
+    if (overlaps(q_out, qb, x, xb) || overlaps(q_out, qb, W, wbytes(N, K)) ||
+        overlaps(q_out, qb, S, sbytes(N, K)) || overlaps(kv_pages, kv_bytes(r), x, xb) ||
+        overlaps(kv_pages, kv_bytes(r), W, wbytes(N, K)) ||
+        overlaps(kv_pages, kv_bytes(r), S, sbytes(N, K)))
+        return fail(Q4_EALIAS, "q_out or the cache overlaps an input");
+    r.pos = pos;
+    r.page_table = page_table;
+    r.kv = kv_pages;
+    r.q_out = q_out;
+    GemvOp op;
+    op.W = W;
+    op.S = S;
+    op.N = (int)N;
+    op.K = (int)K;
+    op.x = x;
+    op.epi = GemvOp::ROPE;
+    op.rope = r;
+    return launch_gemv_op(op, as_stream(stream));
+}
+
+q4_status q4_rope_append(const uint16_t *qkv, const q4_attn_desc *desc, const int32_t *pos,
+                         const int32_t *page_table, uint16_t *kv_pages, uint16_t *q_out,
+                         q4_stream stream)
+{
+    RopeArgs r;
+    q4_status st = check_attn_desc(desc, &r);
+    if (st != Q4_OK)
+        return st;
+    if (!qkv)
+        return fail(Q4_EINVAL, "NULL qkv");
+    if (!aligned(qkv, 2))
+        return fail(Q4_EALIGN, "qkv must be 2-byte aligned");
+    if ((st = check_rope_io(r, pos, page_table, kv_pages, q_out)) != Q4_OK)
+        return st;
+    const size_t nb = (size_t)(r.n_heads + 2 * r.n_kv) * r.head_dim * 2;
+    if (overlaps(q_out, (size_t)r.n_heads * r.head_dim * 2, qkv, nb) ||
+        overlaps(kv_pages, kv_bytes(r), qkv, nb))
+        return fail(Q4_EALIAS, "q_out or the cache overlaps qkv");
+    r.pos = pos;
+    r.page_table = page_table;
+    r.kv = kv_pages;
+    r.q_out = q_out;
+    return launch_rope_append(qkv, r, as_stream(stream));
+}
+
+q4_status q4_attention_decode(const uint16_t *q, const uint16_t *kv_pages,
+                              const int32_t *page_table, const int32_t *pos, int64_t max_len,
+                              const q4_attn_desc *desc, uint16_t *out, q4_stream stream)
+{
+    RopeArgs r;
+    q4_status st = check_attn_desc(desc, &r);
+    if (st != Q4_OK)
+        return st;
+    if (!q || !kv_pages || !page_table || !pos || !out)
+        return fail(Q4_EINVAL, "NULL query, cache, page table, position or output pointer");
+    if (max_len < 1)
+        return fail(Q4_EINVAL, "max_len must be positive");
+    const int nc = r.head_dim / 8;
+    if (nc != 1 && nc != 2 && nc != 4 && nc != 6 && nc != 8 && nc != 12 && nc != 16 && nc != 20 &&
+        nc != 24 && nc != 32)
+        return fail(Q4_ESHAPE, "no attention kernel for head_dim %d", r.head_dim);
+    if (!aligned(q, 2) || !aligned(kv_pages, 16) || !aligned(page_table, 4) || !aligned(pos, 4) ||
+        !aligned(out, 2))
+        return fail(Q4_EALIGN, "misaligned query, cache (16), page table, position or output");
+    const size_t ob = (size_t)r.n_heads * r.head_dim * 2;
+    if (overlaps(out, ob, q, ob) || overlaps(out, ob, kv_pages, kv_bytes(r)) ||
+        overlaps(out, ob, page_table, (size_t)r.max_pages * 4) || overlaps(out, ob, pos, 4))
+        return fail(Q4_EALIAS, "the output overlaps an input");
+    r.pos = pos;
+    r.page_table = page_table;
+    return launch_attention(q, kv_pages, r, max_len, out, as_stream(stream));
 }
 
 q4_status q4_moe_gemv(const uint32_t *W, const uint16_t *S, const int32_t *ids,

@@ -1,0 +1,284 @@
+// RoPE + paged-KV append and decode attention for gfx950.
+//
+// What is computed follows the Zero TVM Documentation: "KV cache" (16-slot
+// pages behind a page table), shader 3 (the QKV matmul with RoPE of Q and K
+// and the K/V write fused, decode), shader 4 (paged attention with an online
+// softmax, one workgroup per head), shaders 8 and 9 (the unfused KV append and
+// RoPE), and BENCH.md's split-K attention (the positions split over several
+// workgroups, then a combine step).
+//
+// The fused QKV step is an epilogue of the matvec (q4_gemv.hip, EPI_ROPE);
+// this file holds the unfused RoPE + append (same device function, so the
+// same bits) and the attention:
+//  * k_attn: workgroup (head h, split s) walks its positions in blocks of 256,
+//    one position per thread for the scores (the key row, head_dim f16, all
+//    its 16-byte loads in flight), an online softmax across blocks (running
+//    maximum and sum, earlier partial sums rescaled), and the
+//    probability-weighted values accumulated by (8-dim chunk, position group)
+//    threads, four positions' loads at a time; the partial state
+//    (maximum, sum, head_dim weighted sums) goes to a workspace, or, with one
+//    split, the normalised output straight to out;
+//  * k_attn_combine merges the splits of a head in split order.
+// No atomics: results are identical run to run.
+#include <algorithm>
+#include <cmath>
+
+#include "q4_common.h"
+
+namespace q4 {
+namespace {
+
+constexpr int kAttnThreads = 256;
+constexpr int kMaxHeadDim = 256;
+constexpr int kMaxSplits = 16;
+
+// One thread per RoPE pair of a stored f16 qkv vector.
+__global__ __launch_bounds__(256) void k_rope_append(const uint16_t *__restrict__ qkv, RopeArgs r,
+                                                     int pairs)
+{
+    const int p = blockIdx.x * 256 + threadIdx.x;
+    if (p >= pairs)
+        return;
+    const int half = r.head_dim >> 1;
+    const int head = p / half, i = p - head * half;
+    const size_t row = (size_t)head * r.head_dim + i;
+    rope_pair_store(r, p, h2f(qkv[row]), h2f(qkv[row + half]));
+}
+
+// Offset (in f16 elements) of the cache row of position t of key/value head
+// kvh for K (add the K-to-V distance for V), or -1 when the position's page
+// is outside the table or the cache.
+__device__ __forceinline__ int64_t cache_row(const RopeArgs &r, int t, int kvh)
+{
+    const int lp = t / r.page_size, slot = t - lp * r.page_size;
+    if (lp >= r.max_pages)
+        return -1;
+    const int pp = r.page_table[lp];
+    if (pp < 0 || pp >= r.n_pages)
+        return -1;
+    return (((int64_t)pp * 2) * r.n_kv + kvh) * r.page_size * r.head_dim +
+           (int64_t)slot * r.head_dim;
+}
+
+__device__ __forceinline__ float block_reduce(float v, float *red, bool is_max)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const float o = __shfl_xor(v, off, 64);
+        v = is_max ? fmaxf(v, o) : v + o;
+    }
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0)
+        red[wave] = v;
+    __syncthreads();
+    float t = red[0];
+#pragma unroll
+    for (int w = 1; w < kAttnThreads / 64; ++w)
+        t = is_max ? fmaxf(t, red[w]) : t + red[w];
+    __syncthreads();
+    return t;
+}
+
+__device__ __forceinline__ void fma8(float (&o)[8], float p, uint4 w)
+{
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        o[2 * e] = fmaf(p, h2f((uint16_t)(u[e] & 0xFFFF)), o[2 * e]);
+        o[2 * e + 1] = fmaf(p, h2f((uint16_t)(u[e] >> 16)), o[2 * e + 1]);
+    }
+}
+
+// Workgroup (head, split): partial softmax state of the split's positions.
+// part layout: [n_heads][splits][2 + head_dim] = (max, sum, weighted values).
+// NC = head_dim / 8 (16-byte chunks of a cache row).
+template <int NC>
+__global__ __launch_bounds__(kAttnThreads) void k_attn(const uint16_t *__restrict__ q,
+                                                       const uint16_t *__restrict__ kv,
+                                                       RopeArgs r, float scale,
+                                                       float *__restrict__ part,
+                                                       uint16_t *__restrict__ out)
+{
+    constexpr int D = 8 * NC;
+    constexpr int groups = kAttnThreads / NC;  // position groups of the value phase
+    __shared__ float qs[D];
+    __shared__ float ps[kAttnThreads];
+    __shared__ int64_t vofs[kAttnThreads];
+    __shared__ float red[kAttnThreads / 64];
+    __shared__ float osum[groups * D];
+
+    const int h = blockIdx.x, s = blockIdx.y, NS = gridDim.y;
+    const int tid = threadIdx.x;
+    const int kvh = h / (r.n_heads / r.n_kv);
+    const int64_t kv_dist = (int64_t)r.n_kv * r.page_size * D;  // K row -> V row
+    const int cap = r.max_pages * r.page_size;
+    const int L = min(max(*r.pos + 1, 0), cap);
+    const int chunk = (L + NS - 1) / NS;
+    const int t0 = s * chunk, t1 = min(L, t0 + chunk);
+
+    for (int d = tid; d < D; d += kAttnThreads)
+        qs[d] = h2f(q[(size_t)h * D + d]);
+    __syncthreads();
+
+    const int dc = tid % NC, tg = tid / NC;
+    const bool pv_thread = tg < groups;
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    for (int tb = t0; tb < t1; tb += kAttnThreads) {
+        // scores: one position per thread, its key row's loads all in flight
+        const int t = tb + tid;
+        float sc = -INFINITY;
+        int64_t off = -1;
+        if (t < t1)
+            off = cache_row(r, t, kvh);
+        if (off >= 0) {
+            const uint4 *krow = reinterpret_cast<const uint4 *>(kv + off);
+            uint4 w[NC];
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                w[c] = krow[c];
+            float dot = 0.f;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const uint32_t u[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    dot = fmaf(qs[8 * c + 2 * e], h2f((uint16_t)(u[e] & 0xFFFF)), dot);
+                    dot = fmaf(qs[8 * c + 2 * e + 1], h2f((uint16_t)(u[e] >> 16)), dot);
+                }
+            }
+            sc = dot * scale;
+        }
+        vofs[tid] = off < 0 ? -1 : off + kv_dist;
+        const float m_blk = block_reduce(sc, red, true);
+        const float m_new = fmaxf(m_run, m_blk);
+        // with no valid position yet there is nothing to rescale or add
+        const float alpha = m_new == -INFINITY ? 1.f : expf(m_run - m_new);
+        const float p = sc == -INFINITY ? 0.f : expf(sc - m_new);
+        ps[tid] = p;
+        const float l_blk = block_reduce(p, red, false);  // its barrier publishes ps, vofs
+        l_run = l_run * alpha + l_blk;
+        m_run = m_new;
+        if (pv_thread) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                o[e] *= alpha;
+            const int nb = min(kAttnThreads, t1 - tb);
+            // four positions at a time, loads first (positions without a row,
+            // or past the block, add nothing)
+            for (int j = tg; j < nb; j += 4 * groups) {
+                uint4 w[4];
+                float pj[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int jj = j + u * groups;
+                    const int64_t vo = jj < nb ? vofs[jj] : -1;
+                    pj[u] = vo >= 0 ? ps[jj] : 0.f;
+                    w[u] = vo >= 0 ? reinterpret_cast<const uint4 *>(kv + vo)[dc]
+                                   : make_uint4(0u, 0u, 0u, 0u);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    fma8(o, pj[u], w[u]);
+            }
+        }
+        __syncthreads();  // ps and vofs are rewritten by the next block
+    }
+
+    // the position groups' sums of each dimension, added in group order
+    if (pv_thread)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            osum[tg * D + 8 * dc + e] = o[e];
+    __syncthreads();
+    for (int d = tid; d < D; d += kAttnThreads) {
+        float v = 0.f;
+        for (int g = 0; g < groups; ++g)
+            v += osum[g * D + d];
+        if (NS == 1) {
+            out[(size_t)h * D + d] = f2h(l_run > 0.f ? v / l_run : 0.f);
+        } else {
+            float *pp = part + ((size_t)h * NS + s) * (2 + D);
+            pp[2 + d] = v;
+            if (d == 0) {
+                pp[0] = m_run;
+                pp[1] = l_run;
+            }
+        }
+    }
+}
+
+// out[h][d] = sum_s o_s[d] e^(m_s - M) / sum_s l_s e^(m_s - M), splits in order
+// (splits without a position have l_s = 0 and are skipped).
+__global__ __launch_bounds__(kMaxHeadDim) void k_attn_combine(const float *__restrict__ part,
+                                                              int NS, int D,
+                                                              uint16_t *__restrict__ out)
+{
+    const int h = blockIdx.x, d = threadIdx.x;
+    if (d >= D)
+        return;
+    const float *ph = part + (size_t)h * NS * (2 + D);
+    float M = -INFINITY;
+    for (int s = 0; s < NS; ++s)
+        if (ph[s * (2 + D) + 1] > 0.f)
+            M = fmaxf(M, ph[s * (2 + D)]);
+    float l = 0.f, v = 0.f;
+    for (int s = 0; s < NS; ++s) {
+        const float *p = ph + s * (2 + D);
+        if (p[1] > 0.f) {
+            const float w = expf(p[0] - M);
+            l = fmaf(p[1], w, l);
+            v = fmaf(p[2 + d], w, v);
+        }
+    }
+    out[(size_t)h * D + d] = f2h(l > 0.f ? v / l : 0.f);
+}
+
+}  // namespace
+
+q4_status launch_rope_append(const uint16_t *qkv, const RopeArgs &r, hipStream_t stream)
+{
+    const int pairs = (r.n_heads + 2 * r.n_kv) * r.head_dim / 2;
+    hipLaunchKernelGGL(k_rope_append, dim3((pairs + 255) / 256), dim3(256), 0, stream, qkv, r,
+                       pairs);
+    return check_launch("k_rope_append");
+}
+
+q4_status launch_attention(const uint16_t *q, const uint16_t *kv, const RopeArgs &r,
+                           int64_t max_len, uint16_t *out, hipStream_t stream)
+{
+    const int64_t cap = (int64_t)r.max_pages * r.page_size;
+    const int64_t len = std::max<int64_t>(1, std::min(max_len, cap));
+    const int NS = (int)std::min<int64_t>(kMaxSplits, (len + kAttnThreads - 1) / kAttnThreads);
+    const float scale = (float)(1.0 / std::sqrt((double)r.head_dim));
+    float *part = nullptr;
+    if (NS > 1) {
+        char *ws = static_cast<char *>(workspace(
+            stream, kWsHeader + (size_t)r.n_heads * NS * (2 + r.head_dim) * sizeof(float)));
+        if (!ws)
+            return Q4_EHIP;
+        part = reinterpret_cast<float *>(ws + kWsHeader);
+    }
+    const dim3 grid(r.n_heads, NS);
+    switch (r.head_dim / 8) {
+#define Q4_ATTN_CASE(nc)                                                                          \
+    case nc:                                                                                      \
+        hipLaunchKernelGGL(k_attn<nc>, grid, dim3(kAttnThreads), 0, stream, q, kv, r, scale, part, \
+                           out);                                                                  \
+        break;
+        Q4_ATTN_CASE(1) Q4_ATTN_CASE(2) Q4_ATTN_CASE(4) Q4_ATTN_CASE(6) Q4_ATTN_CASE(8)
+        Q4_ATTN_CASE(12) Q4_ATTN_CASE(16) Q4_ATTN_CASE(20) Q4_ATTN_CASE(24) Q4_ATTN_CASE(32)
+#undef Q4_ATTN_CASE
+    default:
+        return fail(Q4_ESHAPE, "no attention kernel for head_dim %d", r.head_dim);
+    }
+    q4_status st = check_launch("k_attn");
+    if (st != Q4_OK || NS == 1)
+        return st;
+    hipLaunchKernelGGL(k_attn_combine, dim3(r.n_heads), dim3(kMaxHeadDim), 0, stream, part, NS,
+                       r.head_dim, out);
+    return check_launch("k_attn_combine");
+}
+
+}  // namespace q4

@@ -86,8 +86,18 @@ q4_status launch_gemv(const uint32_t *W, const uint16_t *S, const uint16_t *x, u
 //             RESID res_out[n] = f16(f16(acc) + res_in[n])
 //             LOGITS yf[n] = acc (f32); when cand is set, cand[workgroup] =
 //                    the largest argmax_key of the workgroup's rows
+//             ROPE   the rows are Q, K, V heads (rope geometry): Q and K
+//                    pairs rotated, Q to q_out, K and V into the cache slot
+struct RopeArgs {
+    int n_heads = 0, n_kv = 0, head_dim = 0, page_size = 0, max_pages = 0, n_pages = 0;
+    float base = 10000.f;
+    const int32_t *pos = nullptr;
+    const int32_t *page_table = nullptr;
+    uint16_t *kv = nullptr;
+    uint16_t *q_out = nullptr;
+};
 struct GemvOp {
-    enum { NONE = 0, SILU = 1, RESID = 2, LOGITS = 3 };
+    enum { NONE = 0, SILU = 1, RESID = 2, LOGITS = 3, ROPE = 4 };
     const uint32_t *W = nullptr;
     const uint16_t *S = nullptr;
     int N = 0, K = 0;
@@ -101,6 +111,7 @@ struct GemvOp {
     uint16_t *res_out = nullptr;
     float *yf = nullptr;
     unsigned long long *cand = nullptr;
+    RopeArgs rope;
 };
 q4_status launch_gemv_op(const GemvOp &op, hipStream_t stream);
 // Workgroups of one launch_gemv_op for N rows of K (the candidates LOGITS writes).
@@ -130,6 +141,10 @@ size_t mfma_part_bytes(int N, int K);
 q4_status launch_mfma_rows(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
                            uint16_t *y, float *yf, int64_t ldy, int N, int K, int mt,
                            float *part, hipStream_t stream);
+// RoPE + KV append from a stored qkv vector, and decode attention (q4_attn.hip)
+q4_status launch_rope_append(const uint16_t *qkv, const RopeArgs &r, hipStream_t stream);
+q4_status launch_attention(const uint16_t *q, const uint16_t *kv, const RopeArgs &r,
+                           int64_t max_len, uint16_t *out, hipStream_t stream);
 // LM head and greedy argmax (q4_lmhead.hip)
 q4_status launch_gemv_f32(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
                           float *y, int64_t ldy, int N, int K, int M, hipStream_t stream);
@@ -230,6 +245,50 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long k)
         k = o > k ? o : k;
     }
     return k;
+}
+
+// One RoPE pair of a decode step (the fused QKV epilogue and the unfused
+// kernel share it, so their results are identical): pair p of the
+// (n_heads + 2 n_kv) * head_dim / 2 pairs, x1 and x2 the stored f16 values of
+// rows head * head_dim + i and + head_dim / 2. Query pairs are rotated into
+// q_out, key pairs rotated into the cache, value pairs copied into it. The
+// angle pos * base^(-2i / head_dim) and its cosine and sine are taken in
+// binary64, the rotation in f32.
+__device__ __forceinline__ void rope_pair_store(const RopeArgs &r, int p, float x1, float x2)
+{
+    const int half = r.head_dim >> 1;
+    const int head = p / half, i = p - head * half;
+    const int pos = *r.pos;
+    float c = 1.f, s = 0.f;
+    if (head < r.n_heads + r.n_kv) {
+        const double theta = (double)pos * pow((double)r.base, -2.0 * (double)i / (double)r.head_dim);
+        double sd, cd;
+        sincos(theta, &sd, &cd);
+        c = (float)cd;
+        s = (float)sd;
+    }
+    const float y1 = x1 * c - x2 * s;
+    const float y2 = x2 * c + x1 * s;
+    if (head < r.n_heads) {
+        r.q_out[head * r.head_dim + i] = f2h(y1);
+        r.q_out[head * r.head_dim + i + half] = f2h(y2);
+        return;
+    }
+    const bool is_v = head >= r.n_heads + r.n_kv;
+    const int kvh = head - r.n_heads - (is_v ? r.n_kv : 0);
+    if (pos < 0)
+        return;
+    const int lp = pos / r.page_size, slot = pos - lp * r.page_size;
+    if (lp >= r.max_pages)
+        return;
+    const int pp = r.page_table[lp];
+    if (pp < 0 || pp >= r.n_pages)
+        return;
+    uint16_t *dst = r.kv + (((size_t)pp * 2 + (is_v ? 1 : 0)) * r.n_kv + kvh) *
+                               (size_t)r.page_size * r.head_dim +
+                    (size_t)slot * r.head_dim;
+    dst[i] = f2h(is_v ? x1 : y1);
+    dst[i + half] = f2h(is_v ? x2 : y2);
 }
 
 }  // namespace q4

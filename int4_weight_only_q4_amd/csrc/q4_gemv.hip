@@ -29,7 +29,7 @@ namespace {
 constexpr int kWaves = 4;  // 256 threads per workgroup
 
 enum { PRO_X = 0, PRO_NORM = 1 };
-enum { EPI_NONE_ = 0, EPI_SILU = 1, EPI_RESID = 2, EPI_LOGITS = 3 };
+enum { EPI_NONE_ = 0, EPI_SILU = 1, EPI_RESID = 2, EPI_LOGITS = 3, EPI_ROPE = 4 };
 
 struct GemvParams {
     const uint4 *W;     // [N][G] groups of 16 bytes
@@ -45,6 +45,7 @@ struct GemvParams {
     uint16_t *res_out;
     float *yf;                 // LOGITS: yf[n] = acc
     unsigned long long *cand;  // LOGITS: this workgroup's largest argmax_key, or null
+    RopeArgs rope;             // ROPE: geometry, position, cache and q_out
 };
 
 template <int LPR, int NG, int RPS, int EPI, int PRO>
@@ -55,7 +56,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams a)
     constexpr int XCH = (LPR * NG + 63) / 64; // activation chunks (8 values) per thread
     extern __shared__ uint4 smem[];
     __shared__ float red[4];
-    __shared__ float vals[EPI == EPI_SILU ? RB : 1];
+    __shared__ float vals[(EPI == EPI_SILU || EPI == EPI_ROPE) ? RB : 1];
     __shared__ unsigned long long wkey;  // LOGITS: the workgroup's best key so far
     __shared__ uint32_t wdone;           // LOGITS: waves that have added theirs
 
@@ -93,6 +94,14 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams a)
             const int gi = blockIdx.x * (RB / 2) + (li[r] % (RB / 2));
             ok[r] = gi < half;
             rr = li[r] < RB / 2 ? gi : half + gi;
+        } else if (EPI == EPI_ROPE) {
+            // local rows [0, RB/2) are the first rows of RoPE pairs, the rest
+            // their partners (head_dim / 2 further on)
+            const int hh = a.rope.head_dim >> 1;
+            const int pi = blockIdx.x * (RB / 2) + (li[r] % (RB / 2));
+            ok[r] = pi < half;
+            const int head = pi / hh;
+            rr = head * a.rope.head_dim + (pi - head * hh) + (li[r] < RB / 2 ? 0 : hh);
         } else {
             rr = blockIdx.x * RB + li[r];
             ok[r] = rr < a.N;
@@ -196,6 +205,17 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams a)
             if (gi < half)
                 a.y[gi] = f2h(silu_mul_f(vals[tid], vals[tid + RB / 2]));
         }
+    } else if (EPI == EPI_ROPE) {  // RoPE of the pairs, Q out, K and V into the cache
+        if (j == 0)
+#pragma unroll
+            for (int r = 0; r < RPS; ++r)
+                vals[li[r]] = h2f(f2h(acc[r]));  // as stored by an unfused matvec
+        __syncthreads();
+        if (tid < RB / 2) {
+            const int pi = blockIdx.x * (RB / 2) + tid;
+            if (pi < half)
+                rope_pair_store(a.rope, pi, vals[tid], vals[tid + RB / 2]);
+        }
     } else if (EPI == EPI_LOGITS) {  // f32 logits and this workgroup's argmax candidate
         unsigned long long key = 0;
         if (j == 0)
@@ -266,8 +286,9 @@ q4_status run_gemv(const GemvParams &p, hipStream_t st)
 {
     constexpr int RPS = rows_per_segment(NG);
     constexpr int RB = kWaves * (64 / LPR) * RPS;
-    const int rows = EPI == EPI_SILU ? p.N / 2 : p.N;
-    const int rb = EPI == EPI_SILU ? RB / 2 : RB;
+    const bool paired = EPI == EPI_SILU || EPI == EPI_ROPE;
+    const int rows = paired ? p.N / 2 : p.N;
+    const int rb = paired ? RB / 2 : RB;
     const int blocks = (rows + rb - 1) / rb;
     const size_t lds = (size_t)p.G * 32 * 2 + (size_t)p.G * 4;
     Q4_LAUNCH_MATVEC((k_gemv<LPR, NG, RPS, EPI, PRO>), dim3(blocks), dim3(256), lds, st, p);
@@ -345,6 +366,7 @@ q4_status launch_gemv_op(const GemvOp &op, hipStream_t stream)
     p.res_out = op.res_out;
     p.yf = op.yf;
     p.cand = op.cand;
+    p.rope = op.rope;
     const Cfg c = choose_cfg(p.G);
     const bool norm = op.norm_src != nullptr;
     switch (op.epi) {
@@ -362,6 +384,9 @@ q4_status launch_gemv_op(const GemvOp &op, hipStream_t stream)
         if (norm)
             return fail(Q4_EINVAL, "internal: normalising prologue with the logits epilogue");
         return dispatch_lpr<EPI_LOGITS, PRO_X>(c, p, stream);
+    case GemvOp::ROPE:
+        return norm ? dispatch_lpr<EPI_ROPE, PRO_NORM>(c, p, stream)
+                    : dispatch_lpr<EPI_ROPE, PRO_X>(c, p, stream);
     default:
         return fail(Q4_EINVAL, "internal: unknown matvec epilogue %d", op.epi);
     }

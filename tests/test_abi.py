@@ -203,3 +203,42 @@ def test_lm_head_validation():
     assert status("q4_lm_head_argmax", A, B, X, 64, Y, 16, Y + 32, 16, 64, 1, None) == q4.Q4_EALIAS
     assert status("q4_lm_head_argmax", A, B, X, 64, Y, 16, X, 16, 64, 1, None) == q4.Q4_EALIAS
     assert status("q4_lm_head_argmax", A, B, X, 64, Y, 16, R, 16, 48, 1, None) == q4.Q4_ESHAPE
+
+
+def test_kv_cache_geometry_matches_page_table():
+    """Zero TVM Documentation, 'KV cache': 16-slot pages of 196,608 bytes (32
+    heads x 16 slots x 96 dims x K+V x 2 bytes), 257 pages ~ 4096 tokens,
+    ~50 MB per layer and ~1.6 GB for 32 layers."""
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "kv_cache_phi3.json")))
+    assert g["heads"] * g["head_dim"] == g["hidden"]
+    d = q4.attn_desc(g["heads"], g["heads"], g["head_dim"], g["page_size"], g["max_pages"])
+    assert q4.kv_page_bytes(d) == g["bytes_per_page"]
+    per_layer = g["max_pages"] * g["bytes_per_page"]
+    assert abs(per_layer / 1e6 - g["per_layer_MB_approx"]) < 1.0
+    assert abs(g["layers"] * per_layer / 1e9 - g["total_GB_approx"]) < 0.05
+    assert abs(g["max_pages"] * g["page_size"] - g["context_tokens_approx"]) <= g["page_size"]
+
+
+def test_attention_validation():
+    L = q4.lib()
+    d = q4.attn_desc(32, 32, 96)
+    args = lambda **kw: [kw.get(k, v) for k, v in
+                         (("W", A), ("S", B), ("x", X), ("K", 3072), ("d", C.byref(d)),
+                          ("pos", R), ("pt", R + 64), ("kv", R + 65536), ("q", Y), ("s", None))]
+    assert L.q4_qkv_rope_append(*args(d=None)) == q4.Q4_EINVAL
+    bad = q4.attn_desc(32, 5, 96)  # n_kv does not divide n_heads
+    assert L.q4_qkv_rope_append(*args(d=C.byref(bad))) == q4.Q4_EINVAL
+    bad = q4.attn_desc(32, 32, 100)  # head_dim not a multiple of 8
+    assert L.q4_qkv_rope_append(*args(d=C.byref(bad))) == q4.Q4_ESHAPE
+    assert L.q4_qkv_rope_append(*args(K=48)) == q4.Q4_ESHAPE
+    assert L.q4_qkv_rope_append(*args(pos=None)) == q4.Q4_EINVAL
+    assert L.q4_qkv_rope_append(*args(kv=R + 65536 + 8)) == q4.Q4_EALIGN
+    assert L.q4_qkv_rope_append(*args(q=R + 65536 + 64)) == q4.Q4_EALIAS  # q_out inside the cache
+    assert L.q4_rope_append(None, C.byref(d), R, R + 64, R + 65536, Y, None) == q4.Q4_EINVAL
+    assert L.q4_rope_append(X, C.byref(d), R, R + 64, X + 64, Y, None) == q4.Q4_EALIAS
+    att = L.q4_attention_decode
+    assert att(X, R + 65536, R + 64, R, 0, C.byref(d), Y, None) == q4.Q4_EINVAL
+    assert att(X, R + 65536 + 2, R + 64, R, 16, C.byref(d), Y, None) == q4.Q4_EALIGN
+    assert att(X, R + 65536, R + 64, R, 16, C.byref(d), X + 2, None) == q4.Q4_EALIAS
+    odd = q4.attn_desc(4, 4, 80)  # a multiple of 8 without a kernel
+    assert att(X, R + 65536, R + 64, R, 16, C.byref(odd), Y, None) == q4.Q4_ESHAPE

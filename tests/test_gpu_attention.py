@@ -1,0 +1,187 @@
+"""GPU parity of RoPE + paged-KV append and decode attention against the oracle.
+
+Bar (per element, |y - y_ref| <= 1e-2 + 5e-3 |y_ref| against binary64):
+* q4_qkv_rope_append: the rotated query and the rotated key written into the
+  cache slot of the position against the oracle's RoPE of the f16-stored
+  matvec rows; the value slot against those rows; nothing else in the cache
+  changes; the fused call equals q4_gemv followed by q4_rope_append bit for
+  bit.
+* q4_attention_decode: against the oracle's attention over the cache contents
+  read back in position order, through shuffled page tables, with one and with
+  several splits, grouped key/value heads, and pages missing from the table;
+  a single cached position returns its value exactly.
+* A decode loop (append, then attend, position by position) against the
+  oracle fed the GPU's own cache (teacher forcing).
+Shapes: Phi-3-mini (32 heads of 96, QKV 9216 x 3072, 16-slot pages, 257 pages)
+and a grouped geometry like Qwen3-4B's (32 query heads, 8 key/value heads of
+128, QKV 6144 x 2560).
+"""
+import numpy as np
+import pytest
+
+import datagen
+import oracle
+from gpu_common import assert_within, bits, dev_tensor, host
+
+pytestmark = pytest.mark.gpu
+
+PHI3 = dict(n_heads=32, n_kv=32, head_dim=96, k=3072)
+GQA = dict(n_heads=32, n_kv=8, head_dim=128, k=2560)
+
+
+@pytest.fixture(scope="module")
+def o():
+    return oracle.load()
+
+
+@pytest.fixture(scope="module")
+def q4():
+    import torch
+    import int4_weight_only_q4_amd as m
+    m.lib()
+    assert torch.cuda.is_available()
+    return m
+
+
+def sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def i32(v):
+    import torch
+    return torch.tensor(np.asarray(v, np.int32).ravel(), dtype=torch.int32, device="cuda")
+
+
+def desc_for(q4, g, max_pages=257, n_pages=None, page_size=16):
+    return q4.attn_desc(g["n_heads"], g["n_kv"], g["head_dim"], page_size, max_pages,
+                        n_pages if n_pages is not None else max_pages)
+
+
+def cache_rows(cache, table, L, page_size, kind):
+    """Host cache f16 [n_pages][2][n_kv][page][hd] -> [L][n_kv][hd] in position order."""
+    t = np.arange(L)
+    return cache[table[t // page_size], kind, :, t % page_size, :]
+
+
+def qkv_matrix(o, g, seed):
+    n = (g["n_heads"] + 2 * g["n_kv"]) * g["head_dim"]
+    W = datagen.words(seed, n, g["k"])
+    S = datagen.scales(seed + 1, n, g["k"])
+    return W, S
+
+
+@pytest.mark.parametrize("geom,pos", [("phi3", 0), ("phi3", 5), ("phi3", 4095), ("gqa", 77)])
+def test_qkv_rope_append_vs_oracle(o, q4, geom, pos):
+    import torch
+    g = PHI3 if geom == "phi3" else GQA
+    nh, nkv, hd = g["n_heads"], g["n_kv"], g["head_dim"]
+    W, S = qkv_matrix(o, g, datagen.seed_for(7, 10 + pos))
+    x = datagen.activations(datagen.seed_for(7, 20 + pos), 1, g["k"])[0]
+    d = desc_for(q4, g)
+    table = np.random.default_rng(pos).permutation(257).astype(np.int32)
+    kv = q4.kv_cache(d)
+    kv.fill_(7.0)  # sentinel: only the position's slot may change
+    q = q4.qkv_rope_append(dev_tensor(W), dev_tensor(S), dev_tensor(x), d, i32([pos]), i32(table),
+                           kv)
+    sync()
+    q_ref, k_ref, v_ref = o.qkv_rope(W, S, x, nh, nkv, hd, pos)
+    assert_within(host(q), q_ref, "rotated query")
+    c = host(kv)
+    page, slot = table[pos // 16], pos % 16
+    assert_within(c[page, 0, :, slot, :].ravel(), k_ref, "rotated key in the cache")
+    assert_within(c[page, 1, :, slot, :].ravel(), v_ref, "value in the cache")
+    c[page, :, :, slot, :] = 7.0
+    assert np.all(c == np.float16(7.0)), "the cache changed outside the position's slot"
+
+
+@pytest.mark.parametrize("geom", ["phi3", "gqa"])
+def test_fused_equals_matvec_then_rope_append(o, q4, geom):
+    g = PHI3 if geom == "phi3" else GQA
+    W, S = qkv_matrix(o, g, datagen.seed_for(7, 40))
+    x = datagen.activations(datagen.seed_for(7, 41), 1, g["k"])[0]
+    d = desc_for(q4, g, max_pages=8)
+    Wd, Sd, xd, pos, table = dev_tensor(W), dev_tensor(S), dev_tensor(x), i32([37]), i32(range(8))
+    kv1, kv2 = q4.kv_cache(d), q4.kv_cache(d)
+    q1 = q4.qkv_rope_append(Wd, Sd, xd, d, pos, table, kv1)
+    qkv = q4.gemv(Wd, Sd, xd)
+    q2 = q4.rope_append(qkv, d, pos, table, kv2)
+    sync()
+    assert np.array_equal(bits(q1), bits(q2))
+    assert np.array_equal(bits(kv1), bits(kv2))
+
+
+def fill_cache(q4, d, seed, L, table):
+    """Random f16 K and V for positions 0..L-1 (written through the table)."""
+    import torch
+    n_kv, hd, ps = d.n_kv, d.head_dim, d.page_size
+    kc = datagen.activations(seed, L, n_kv * hd).reshape(L, n_kv, hd)
+    vc = datagen.activations(seed + 1, L, n_kv * hd).reshape(L, n_kv, hd)
+    cache = np.zeros((d.n_pages, 2, n_kv, ps, hd), np.float16)
+    t = np.arange(L)
+    cache[table[t // ps], 0, :, t % ps, :] = kc
+    cache[table[t // ps], 1, :, t % ps, :] = vc
+    return torch.from_numpy(cache).cuda(), kc, vc
+
+
+@pytest.mark.parametrize("geom,L,max_len", [
+    ("phi3", 1, 1), ("phi3", 2, 2), ("phi3", 17, 17), ("phi3", 256, 256), ("phi3", 257, 257),
+    ("phi3", 1000, 1000), ("phi3", 4112, 4112), ("phi3", 10, 4112), ("gqa", 300, 300),
+    ("gqa", 2048, 2048)])
+def test_attention_vs_oracle(o, q4, geom, L, max_len):
+    g = PHI3 if geom == "phi3" else GQA
+    nh, nkv, hd = g["n_heads"], g["n_kv"], g["head_dim"]
+    d = desc_for(q4, g)
+    table = np.random.default_rng(L).permutation(257).astype(np.int32)
+    kv, kc, vc = fill_cache(q4, d, datagen.seed_for(7, 100 + L), L, table)
+    q = datagen.activations(datagen.seed_for(7, 200 + L), 1, nh * hd)[0]
+    out = q4.attention_decode(dev_tensor(q), kv, i32(table), i32([L - 1]), max_len, d)
+    sync()
+    ref = o.attention(q, kc, vc, nh, nkv, hd)
+    assert_within(host(out), ref, "attention L=%d" % L)
+    if L == 1:
+        assert np.array_equal(bits(out), vc[0].repeat(nh // nkv, axis=0).view(np.uint16).ravel())
+
+
+def test_attention_skips_pages_outside_the_table(o, q4):
+    """A table entry outside the cache drops its 16 positions; a position past
+    the table is clamped to the table's capacity."""
+    g = PHI3
+    nh, hd = g["n_heads"], g["head_dim"]
+    d = desc_for(q4, g, max_pages=10, n_pages=10)
+    table = np.arange(10, dtype=np.int32)
+    kv, kc, vc = fill_cache(q4, d, 900, 160, table)
+    q = datagen.activations(901, 1, nh * hd)[0]
+    bad = table.copy()
+    bad[3] = 99  # page 3 missing
+    out = q4.attention_decode(dev_tensor(q), kv, i32(bad), i32([159]), 160, d)
+    keep = np.r_[0:48, 64:160]
+    over = q4.attention_decode(dev_tensor(q), kv, i32(table), i32([5000]), 160, d)
+    sync()
+    assert_within(host(out), o.attention(q, kc[keep], vc[keep], nh, nh, hd), "missing page")
+    assert_within(host(over), o.attention(q, kc, vc, nh, nh, hd), "clamped position")
+
+
+def test_decode_loop_append_then_attend(o, q4):
+    """Twenty decode steps on a small grouped geometry: each step appends its
+    rotated K and V, then attends over everything cached so far. The oracle is
+    fed the GPU's stored cache and query (teacher forcing)."""
+    g = dict(n_heads=8, n_kv=2, head_dim=64, k=512)
+    nh, nkv, hd = g["n_heads"], g["n_kv"], g["head_dim"]
+    W, S = qkv_matrix(o, g, 1500)
+    Wd, Sd = dev_tensor(W), dev_tensor(S)
+    d = desc_for(q4, g, max_pages=4, n_pages=4)
+    table = np.array([2, 0, 3, 1], np.int32)
+    kv = q4.kv_cache(d)
+    X = datagen.activations(1501, 20, g["k"])
+    for pos in range(20):
+        q = q4.qkv_rope_append(Wd, Sd, dev_tensor(X[pos]), d, i32([pos]), i32(table), kv)
+        out = q4.attention_decode(q, kv, i32(table), i32([pos]), 64, d)
+        sync()
+        qr, kr, vr = o.qkv_rope(W, S, X[pos], nh, nkv, hd, pos)
+        assert_within(host(q), qr, "query at %d" % pos)
+        c = host(kv)
+        kc = cache_rows(c, table, pos + 1, 16, 0)
+        vc = cache_rows(c, table, pos + 1, 16, 1)
+        assert_within(kc[pos].ravel(), kr, "key at %d" % pos)
+        assert_within(host(out), o.attention(host(q), kc, vc, nh, nkv, hd), "output at %d" % pos)
