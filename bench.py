@@ -280,6 +280,34 @@ def _time(q4, torch, launch, count, timed_kernels=True):
     return per_call, per_kernel
 
 
+def _time_graph(q4, torch, launch, count, reps=5):
+    """us per call from a captured HIP graph of `count` calls, replayed `reps`
+    times (no host launch overhead; the calls enqueue kernels only: no
+    allocation, copy or memset, the workspace of the capture stream being
+    sized by eager warm-up calls on that stream)."""
+    # warm-up and capture on one stream: the library's workspace is per stream
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        for i in range(4):
+            launch(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        for i in range(count):
+            launch(i)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * count)
+
+
 def gemv_table(q4, torch):
     """Per-GEMV throughput at the single-GEMV, Phi-3-mini, Qwen3-4B (M = 1 and
     8) and MoE workloads, weights rotated past the Infinity Cache."""
@@ -344,6 +372,58 @@ def gemv_table(q4, torch):
         del rot
         torch.cuda.empty_cache()
 
+    # RoPE + paged KV append fused into the Phi-3 QKV matvec, and decode
+    # attention over the paged cache (Phi-3: 32 heads of 96, 16-slot pages);
+    # every cache is one layer's, rotated past 512 MB as the layers' caches
+    # would be in a decode step. Attention bytes = L * heads * 96 * 2 (K, V) * 2.
+    d = q4.attn_desc(32, 32, 96, 16, 257)
+    table = torch.arange(257, dtype=torch.int32, device="cuda")
+    rot = _rotation(torch, 9216, 3072, base + 2800)
+    x = torch.from_numpy(datagen.activations(base + 2802, 1, 3072)).cuda()
+    kv = q4.kv_cache(d)
+    qo = torch.empty(3072, dtype=torch.float16, device="cuda")
+    pos1 = torch.tensor([1234], dtype=torch.int32, device="cuda")
+
+    def launch(i, rot=rot, x=x, kv=kv, qo=qo):
+        W, S = rot[i % len(rot)]
+        q4.qkv_rope_append(W, S, x[0], d, pos1, table, kv, q_out=qo)
+    add("Phi-3-mini QKV + RoPE + KV append", "9216x3072", 1, 9216 * 3072 * BPW, launch,
+        count=200, note="fused epilogue: Q rotated out, K and V into the cache slot")
+    del rot, kv
+    torch.cuda.empty_cache()
+    for L in (256, 1024, 4112):
+        npages = -(-L // 16)
+        dl = q4.attn_desc(32, 32, 96, 16, npages)
+        cache_bytes = npages * q4.kv_page_bytes(dl)
+        first = torch.from_numpy(datagen.normal_f16(base + 2900, (npages, 2, 32, 16, 96))).cuda()
+        caches = [first] + [first.clone() for _ in range(max(2, -(-(512 << 20) // cache_bytes)) - 1)]
+        tab = torch.arange(npages, dtype=torch.int32, device="cuda")
+        q = torch.from_numpy(datagen.activations(base + 2950, 1, 3072)).cuda()
+        out = torch.empty(3072, dtype=torch.float16, device="cuda")
+        posL = torch.tensor([L - 1], dtype=torch.int32, device="cuda")
+
+        def launch(i, caches=caches, tab=tab, q=q, out=out, posL=posL, dl=dl, L=L):
+            q4.attention_decode(q[0], caches[i % len(caches)], tab, posL, L, dl, out=out)
+        launch(0)
+        torch.cuda.synchronize()
+        eager = out.clone()
+        call_us = _time_graph(q4, torch, launch, 2 * len(caches))
+        launch(0)
+        torch.cuda.synchronize()
+        if not torch.equal(out, eager):
+            raise RuntimeError("graph replay of the attention differs from the eager call")
+        wb = L * 32 * 96 * 2 * 2
+        gbs = wb / (call_us * 1e-6) / 1e9
+        rows.append(dict(workload="attention decode (32 heads x 96, paged)", shape="L=%d" % L, m=1,
+                         weight_bytes=int(wb), us_kernel=None, us_per_call=round(call_us, 3),
+                         gbs=round(gbs, 1), pct_peak=round(100 * gbs / HBM_PEAK_GBS, 1),
+                         note="K and V bytes read; %d caches rotated; split attention + "
+                              "combine; timed from a HIP graph of the calls" % len(caches)))
+        print("  attention L=%-5d %8.3f us/call %8.1f GB/s" % (L, call_us, gbs), file=sys.stderr,
+              flush=True)
+        del caches, first
+        torch.cuda.empty_cache()
+
     # MoE layer: 128 experts, top-8; gate_up stage (SiLU-multiply) + down stage
     # with the routing-weighted combine. Two copies of the expert stack are
     # alternated and the routing is drawn from a pool of 256, so the touched
@@ -389,7 +469,7 @@ def gemv_table(q4, torch):
 
 def write_gemv_table(rows):
     text = ["# Per-GEMV throughput: single GEMV, Phi-3-mini, Qwen3-4B (M = 1, 8), LM heads with "
-            "argmax, and MoE shapes",
+            "argmax, QKV + RoPE + KV append, decode attention, and MoE shapes",
             "",
             "Command (from the repository root, on one MI355X): `python3 bench.py --gemv-table`",
             "",
@@ -400,8 +480,9 @@ def write_gemv_table(rows):
             "is the time per call of 20-200 calls back to back (one event pair, includes "
             "the gaps between launches). GB/s = weight bytes (0.5625 B per weight) / "
             "us/kernel, except for the rows that run several kernels per call (the LM head + "
-            "argmax: 2 kernels at M = 1, 4 at M = 8; the MoE layer: 5), where it is weight "
-            "bytes / us/call. For those rows us/kernel is the first matvec kernel alone.",
+            "argmax: 2 kernels at M = 1, 4 at M = 8; attention: 1 or 2; the MoE layer: 3 to "
+            "5), where it is bytes / us/call (attention: the K and V bytes read). For those "
+            "rows us/kernel is the first matvec kernel alone.",
             "",
             "| workload | shape | M | weight bytes | us/kernel | us/call | GB/s | % of 8 TB/s | note |",
             "|---|---|---|---|---|---|---|---|---|"]

@@ -12,10 +12,10 @@
 // same bits) and the attention:
 //  * k_attn: workgroup (head h, split s) walks its positions in blocks of 256,
 //    one position per thread for the scores (the key row, head_dim f16, all
-//    its 16-byte loads in flight), an online softmax across blocks (running
-//    maximum and sum, earlier partial sums rescaled), and the
-//    probability-weighted values accumulated by (8-dim chunk, position group)
-//    threads, four positions' loads at a time; the partial state
+//    its loads in flight) and (8-dim chunk, position group) threads for the
+//    probability-weighted values (all of a thread's loads in flight, their
+//    rows located in the score phase); an online softmax across blocks
+//    (running maximum and sum, earlier partial sums rescaled); the partial state
 //    (maximum, sum, head_dim weighted sums) goes to a workspace, or, with one
 //    split, the normalised output straight to out;
 //  * k_attn_combine merges the splits of a head in split order.
@@ -30,7 +30,7 @@ namespace {
 
 constexpr int kAttnThreads = 256;
 constexpr int kMaxHeadDim = 256;
-constexpr int kMaxSplits = 16;
+constexpr int kMaxSplits = 32;
 
 // One thread per RoPE pair of a stored f16 qkv vector.
 __global__ __launch_bounds__(256) void k_rope_append(const uint16_t *__restrict__ qkv, RopeArgs r,
@@ -89,7 +89,8 @@ __device__ __forceinline__ void fma8(float (&o)[8], float p, uint4 w)
     }
 }
 
-// Workgroup (head, split): partial softmax state of the split's positions.
+// Workgroup (head, split): partial softmax state of the split's positions,
+// whole blocks of 256 positions per split.
 // part layout: [n_heads][splits][2 + head_dim] = (max, sum, weighted values).
 // NC = head_dim / 8 (16-byte chunks of a cache row).
 template <int NC>
@@ -100,7 +101,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(const uint16_t *__restric
                                                        uint16_t *__restrict__ out)
 {
     constexpr int D = 8 * NC;
-    constexpr int groups = kAttnThreads / NC;  // position groups of the value phase
+    constexpr int groups = kAttnThreads / NC;             // position groups of the value phase
+    constexpr int U = (kAttnThreads + groups - 1) / groups;  // positions per value thread
     __shared__ float qs[D];
     __shared__ float ps[kAttnThreads];
     __shared__ int64_t vofs[kAttnThreads];
@@ -113,7 +115,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(const uint16_t *__restric
     const int64_t kv_dist = (int64_t)r.n_kv * r.page_size * D;  // K row -> V row
     const int cap = r.max_pages * r.page_size;
     const int L = min(max(*r.pos + 1, 0), cap);
-    const int chunk = (L + NS - 1) / NS;
+    const int nblk = (L + kAttnThreads - 1) / kAttnThreads;
+    const int chunk = kAttnThreads * ((nblk + NS - 1) / NS);
     const int t0 = s * chunk, t1 = min(L, t0 + chunk);
 
     for (int d = tid; d < D; d += kAttnThreads)
@@ -126,14 +129,13 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(const uint16_t *__restric
     float m_run = -INFINITY, l_run = 0.f;
 
     for (int tb = t0; tb < t1; tb += kAttnThreads) {
-        // scores: one position per thread, its key row's loads all in flight
-        const int t = tb + tid;
+        const int nb = min(kAttnThreads, t1 - tb);
+        // scores: one position per thread, its key row's loads all in flight;
+        // the row's value offset goes to LDS for the value phase
+        const int64_t koff = tid < nb ? cache_row(r, tb + tid, kvh) : -1;
         float sc = -INFINITY;
-        int64_t off = -1;
-        if (t < t1)
-            off = cache_row(r, t, kvh);
-        if (off >= 0) {
-            const uint4 *krow = reinterpret_cast<const uint4 *>(kv + off);
+        if (koff >= 0) {
+            const uint4 *krow = reinterpret_cast<const uint4 *>(kv + koff);
             uint4 w[NC];
 #pragma unroll
             for (int c = 0; c < NC; ++c)
@@ -141,16 +143,16 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(const uint16_t *__restric
             float dot = 0.f;
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                const uint32_t u[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
+                const uint32_t uu[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    dot = fmaf(qs[8 * c + 2 * e], h2f((uint16_t)(u[e] & 0xFFFF)), dot);
-                    dot = fmaf(qs[8 * c + 2 * e + 1], h2f((uint16_t)(u[e] >> 16)), dot);
+                    dot = fmaf(qs[8 * c + 2 * e], h2f((uint16_t)(uu[e] & 0xFFFF)), dot);
+                    dot = fmaf(qs[8 * c + 2 * e + 1], h2f((uint16_t)(uu[e] >> 16)), dot);
                 }
             }
             sc = dot * scale;
         }
-        vofs[tid] = off < 0 ? -1 : off + kv_dist;
+        vofs[tid] = koff < 0 ? -1 : koff + kv_dist;
         const float m_blk = block_reduce(sc, red, true);
         const float m_new = fmaxf(m_run, m_blk);
         // with no valid position yet there is nothing to rescale or add
@@ -164,24 +166,20 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(const uint16_t *__restric
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 o[e] *= alpha;
-            const int nb = min(kAttnThreads, t1 - tb);
-            // four positions at a time, loads first (positions without a row,
-            // or past the block, add nothing)
-            for (int j = tg; j < nb; j += 4 * groups) {
-                uint4 w[4];
-                float pj[4];
+            // every value load of this thread in flight, then the sums
+            // (positions without a row, or past the block, add nothing)
+            uint4 vw[U];
+            float pj[U];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int jj = j + u * groups;
-                    const int64_t vo = jj < nb ? vofs[jj] : -1;
-                    pj[u] = vo >= 0 ? ps[jj] : 0.f;
-                    w[u] = vo >= 0 ? reinterpret_cast<const uint4 *>(kv + vo)[dc]
-                                   : make_uint4(0u, 0u, 0u, 0u);
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    fma8(o, pj[u], w[u]);
+            for (int u = 0; u < U; ++u) {
+                const int j = min(tg + u * groups, kAttnThreads - 1);
+                const int64_t vo = vofs[j];
+                pj[u] = (tg + u * groups < kAttnThreads && vo >= 0) ? ps[j] : 0.f;
+                vw[u] = reinterpret_cast<const uint4 *>(kv + (vo >= 0 ? vo : 0))[dc];
             }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                fma8(o, pj[u], vw[u]);
         }
         __syncthreads();  // ps and vofs are rewritten by the next block
     }
@@ -209,30 +207,45 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(const uint16_t *__restric
     }
 }
 
-// out[h][d] = sum_s o_s[d] e^(m_s - M) / sum_s l_s e^(m_s - M), splits in order
-// (splits without a position have l_s = 0 and are skipped).
+// out[h][d] = sum_s o_s[d] e^(m_s - M) / sum_s l_s e^(m_s - M) (splits without
+// a position have l_s = 0 and weight 0). One wave reads every split's
+// (max, sum) at once and forms the weights; then each dimension's loads are
+// independent of one another.
 __global__ __launch_bounds__(kMaxHeadDim) void k_attn_combine(const float *__restrict__ part,
                                                               int NS, int D,
                                                               uint16_t *__restrict__ out)
 {
-    const int h = blockIdx.x, d = threadIdx.x;
-    if (d >= D)
-        return;
+    __shared__ float wgt[kMaxSplits];
+    __shared__ float inv_l;
+    const int h = blockIdx.x, tid = threadIdx.x;
     const float *ph = part + (size_t)h * NS * (2 + D);
-    float M = -INFINITY;
-    for (int s = 0; s < NS; ++s)
-        if (ph[s * (2 + D) + 1] > 0.f)
-            M = fmaxf(M, ph[s * (2 + D)]);
-    float l = 0.f, v = 0.f;
-    for (int s = 0; s < NS; ++s) {
-        const float *p = ph + s * (2 + D);
-        if (p[1] > 0.f) {
-            const float w = expf(p[0] - M);
-            l = fmaf(p[1], w, l);
-            v = fmaf(p[2 + d], w, v);
-        }
+    if (tid < 64) {
+        const bool has = tid < NS;
+        const float m = has ? ph[tid * (2 + D)] : -INFINITY;
+        const float l = has ? ph[tid * (2 + D) + 1] : 0.f;
+        const bool valid = l > 0.f;
+        float M = valid ? m : -INFINITY;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1)
+            M = fmaxf(M, __shfl_xor(M, off, 64));
+        const float w = valid ? expf(m - M) : 0.f;
+        float sum = l * w;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1)
+            sum += __shfl_xor(sum, off, 64);
+        if (has)
+            wgt[tid] = w;
+        if (tid == 0)
+            inv_l = sum > 0.f ? 1.f / sum : 0.f;
     }
-    out[(size_t)h * D + d] = f2h(l > 0.f ? v / l : 0.f);
+    __syncthreads();
+    if (tid >= D)
+        return;
+    float v = 0.f;
+#pragma unroll 8
+    for (int s = 0; s < NS; ++s)
+        v = fmaf(ph[s * (2 + D) + 2 + tid], wgt[s], v);
+    out[(size_t)h * D + tid] = f2h(v * inv_l);
 }
 
 }  // namespace
@@ -250,6 +263,7 @@ q4_status launch_attention(const uint16_t *q, const uint16_t *kv, const RopeArgs
 {
     const int64_t cap = (int64_t)r.max_pages * r.page_size;
     const int64_t len = std::max<int64_t>(1, std::min(max_len, cap));
+    // one split per block of 256 positions, up to kMaxSplits
     const int NS = (int)std::min<int64_t>(kMaxSplits, (len + kAttnThreads - 1) / kAttnThreads);
     const float scale = (float)(1.0 / std::sqrt((double)r.head_dim));
     float *part = nullptr;
