@@ -59,6 +59,8 @@ _SIGS = {
     "q4o_rope": (None, [_P, _P, _I, _I, _I, C.c_double]),
     "q4o_qkv_rope": (None, [_P, _P, _P, _I, _I, _I, _I, _I, C.c_double, _P, _P, _P]),
     "q4o_attention": (None, [_P, _P, _P, _I, _I, _I, _I, _P]),
+    "q4o_layer_attn": (None, [_I] * 6 + [C.c_double] + [_P] * 8 + [_P, _P, C.c_double] +
+                       [_P] * 9),
 }
 
 
@@ -260,6 +262,30 @@ class Oracle:
                            self._ptr(gn), eps, self._ptr(r), self._ptr(h), self._ptr(r_out),
                            self._ptr(h_out), self._ptr(h64))
         return r_out.view(np.float16), h_out.view(np.float16), h64
+
+    def layer_attn(self, geom, pos, mats, gamma_post, gamma_next, r, h, kc_prev, vc_prev,
+                   eps=1e-5, base=10000.0):
+        """One layer with RoPE, the KV append at pos and attention over 0..pos.
+        geom = (d, f, n_heads, n_kv, head_dim); kc_prev, vc_prev f16
+        [pos][n_kv][head_dim]. Returns (r_out, h_out, h64, k_new, v_new)."""
+        d, f, nh, nkv, hd = geom
+        mats = [np.ascontiguousarray(m) if m.dtype == np.uint32 else self._u16(m)
+                for m in mats]
+        r, h = self._u16(r), self._u16(h)
+        gp, gn = self._u16(gamma_post), self._u16(gamma_next)
+        kp = self._u16(np.ascontiguousarray(kc_prev).reshape(-1)) if pos > 0 else np.zeros(1, np.uint16)
+        vp = self._u16(np.ascontiguousarray(vc_prev).reshape(-1)) if pos > 0 else np.zeros(1, np.uint16)
+        r_out = np.empty(d, np.uint16)
+        h_out = np.empty(d, np.uint16)
+        h64 = np.empty(d, np.float64)
+        k_new = np.empty(nkv * hd, np.uint16)
+        v_new = np.empty(nkv * hd, np.uint16)
+        self.lib.q4o_layer_attn(d, f, nh, nkv, hd, pos, base, *[self._ptr(m) for m in mats],
+                                self._ptr(gp), self._ptr(gn), eps, self._ptr(r), self._ptr(h),
+                                self._ptr(kp), self._ptr(vp), self._ptr(r_out), self._ptr(h_out),
+                                self._ptr(h64), self._ptr(k_new), self._ptr(v_new))
+        return (r_out.view(np.float16), h_out.view(np.float16), h64, k_new.view(np.float16),
+                v_new.view(np.float16))
 
     def stack(self, dims, layers, gamma_in, gamma_post, gamma_final, r, h, eps=1e-5,
               trace=False):

@@ -505,3 +505,72 @@ void q4o_attention(const uint16_t *q, const uint16_t *kc, const uint16_t *vc, in
     }
     free(s);
 }
+
+/*
+ * One decoder layer with the real attention step in place of the
+ * single-position identity (Zero TVM Documentation, "Decode loop": QKV with
+ * RoPE and the KV append -> paged attention -> O -> add+norm -> FFN ->
+ * add+norm). The token sits at position pos; kc_prev, vc_prev hold the cached
+ * f16 rows of positions 0 .. pos-1 ([pos][n_kv][hd]). Rounded to f16 where a
+ * call stores f16: the rotated query, the appended key and value (returned in
+ * k_new, v_new), the attention output, then as q4o_layer.
+ */
+void q4o_layer_attn(int64_t d, int64_t f, int64_t n_heads, int64_t n_kv, int64_t hd,
+                    int64_t pos, double base,
+                    const uint32_t *Wqkv, const uint16_t *Sqkv,
+                    const uint32_t *Wo, const uint16_t *So,
+                    const uint32_t *Wgu, const uint16_t *Sgu,
+                    const uint32_t *Wdn, const uint16_t *Sdn,
+                    const uint16_t *gamma_post, const uint16_t *gamma_next, double eps,
+                    const uint16_t *r_in, const uint16_t *h_in,
+                    const uint16_t *kc_prev, const uint16_t *vc_prev,
+                    uint16_t *r_out, uint16_t *h_out, double *h_out_f64,
+                    uint16_t *k_new, uint16_t *v_new)
+{
+    const int64_t nq = n_heads * hd, nk = n_kv * hd, L = pos + 1;
+    double *qd = (double *)malloc(sizeof(double) * (size_t)nq);
+    double *kd = (double *)malloc(sizeof(double) * (size_t)nk);
+    double *vd = (double *)malloc(sizeof(double) * (size_t)nk);
+    uint16_t *q = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)nq);
+    uint16_t *kc = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(L * nk));
+    uint16_t *vc = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(L * nk));
+    int64_t big = 2 * f > nq ? 2 * f : nq;
+    double *tmp = (double *)malloc(sizeof(double) * (size_t)big);
+    uint16_t *att = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)nq);
+    uint16_t *o = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)d);
+    uint16_t *ra = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)d);
+    uint16_t *h1 = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)d);
+    uint16_t *gu = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(2 * f));
+    uint16_t *u = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)f);
+    uint16_t *dn = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)d);
+
+    q4o_qkv_rope(Wqkv, Sqkv, h_in, d, n_heads, n_kv, hd, pos, base, qd, kd, vd);
+    q4o_d2h_array(qd, q, nq);
+    q4o_d2h_array(kd, k_new, nk);
+    q4o_d2h_array(vd, v_new, nk);
+    if (pos > 0) {
+        memcpy(kc, kc_prev, sizeof(uint16_t) * (size_t)(pos * nk));
+        memcpy(vc, vc_prev, sizeof(uint16_t) * (size_t)(pos * nk));
+    }
+    memcpy(kc + pos * nk, k_new, sizeof(uint16_t) * (size_t)nk);
+    memcpy(vc + pos * nk, v_new, sizeof(uint16_t) * (size_t)nk);
+    q4o_attention(q, kc, vc, L, n_heads, n_kv, hd, tmp);
+    q4o_d2h_array(tmp, att, nq);
+    q4o_gemv(Wo, So, att, d, nq, tmp);
+    q4o_d2h_array(tmp, o, d);
+    q4o_add_rmsnorm(o, r_in, gamma_post, d, 1, eps, ra, tmp);
+    q4o_d2h_array(tmp, h1, d);
+    q4o_gemv(Wgu, Sgu, h1, 2 * f, d, tmp);
+    q4o_d2h_array(tmp, gu, 2 * f);
+    q4o_silu_mul(gu, f, 1, tmp);
+    q4o_d2h_array(tmp, u, f);
+    q4o_gemv(Wdn, Sdn, u, d, f, tmp);
+    q4o_d2h_array(tmp, dn, d);
+    q4o_add_rmsnorm(dn, ra, gamma_next, d, 1, eps, r_out, tmp);
+    q4o_d2h_array(tmp, h_out, d);
+    if (h_out_f64)
+        memcpy(h_out_f64, tmp, sizeof(double) * (size_t)d);
+
+    free(qd); free(kd); free(vd); free(q); free(kc); free(vc); free(tmp); free(att);
+    free(o); free(ra); free(h1); free(gu); free(u); free(dn);
+}

@@ -693,6 +693,56 @@ def pin_qkv_rope_is_stored_matvec_then_rope(o):
     assert np.array_equal(v, y[(nh + nkv) * d:])
 
 
+def _attn_layer_mats(o, seed, d, f, nq_rows):
+    return [m for pair in (_mat(o, seed, nq_rows, d)[1:], _mat(o, seed + 2, d, nq_rows // 3)[1:],
+                           _mat(o, seed + 4, 2 * f, d)[1:], _mat(o, seed + 6, d, f)[1:])
+            for m in pair]
+
+
+def pin_layer_attn_at_position_zero_is_the_v_slice_layer(o):
+    """With one cached position attention returns that position's value, so
+    the layer at pos 0 is the single-position layer that feeds O the V slice of
+    the QKV rows (and its key and value rows are the RoPE'd, stored rows)."""
+    d, f, nh, hd = 128, 256, 4, 32
+    mats = _attn_layer_mats(o, 700, d, f, 3 * nh * hd)
+    gp, gn = datagen.gammas(710, 1, d)[0], datagen.gammas(711, 1, d)[0]
+    r = datagen.activations(712, 1, d)[0]
+    h = datagen.activations(713, 1, d)[0]
+    ra, ha, h64a, k_new, v_new = o.layer_attn((d, f, nh, nh, hd), 0, mats, gp, gn, r, h, None, None)
+    dims = (d, f, 3 * nh * hd, 2 * nh * hd, nh * hd)  # d, f, n_qkv, v_off, dv
+    rb, hb, h64b = o.layer(dims, mats, gp, gn, r, h)
+    assert np.array_equal(ra.view(np.uint16), rb.view(np.uint16))
+    assert np.array_equal(h64a, h64b)
+    q, kr, v = o.qkv_rope(mats[0], mats[1], h, nh, nh, hd, 0)
+    assert np.array_equal(k_new.view(np.uint16), o.d2h(kr).view(np.uint16))
+    assert np.array_equal(v_new.view(np.uint16), o.d2h(v).view(np.uint16))
+
+
+def pin_layer_attn_is_rope_attention_then_layer(o):
+    """At pos > 0 the O input is the stored attention output over the cached
+    rows and the new ones."""
+    d, f, nh, nkv, hd, pos = 128, 256, 4, 2, 32, 9
+    nrows = (nh + 2 * nkv) * hd
+    mats = [m for pair in (_mat(o, 720, nrows, d)[1:], _mat(o, 722, d, nh * hd)[1:],
+                           _mat(o, 724, 2 * f, d)[1:], _mat(o, 726, d, f)[1:]) for m in pair]
+    gp, gn = datagen.gammas(730, 1, d)[0], datagen.gammas(731, 1, d)[0]
+    r = datagen.activations(732, 1, d)[0]
+    h = datagen.activations(733, 1, d)[0]
+    kc = datagen.activations(734, pos, nkv * hd)
+    vc = datagen.activations(735, pos, nkv * hd)
+    ra, ha, h64a, k_new, v_new = o.layer_attn((d, f, nh, nkv, hd), pos, mats, gp, gn, r, h, kc, vc)
+    q, kr, v = o.qkv_rope(mats[0], mats[1], h, nh, nkv, hd, pos)
+    att = o.attention(o.d2h(q), np.vstack([kc, o.d2h(kr)]), np.vstack([vc, o.d2h(v)]), nh, nkv, hd)
+    # the rest of the layer from the stored attention output: O, add+norm, FFN, add+norm
+    ao = o.d2h(o.gemv(mats[2], mats[3], o.d2h(att)))
+    r1, h1 = o.add_rmsnorm(ao, r, gp)
+    u = o.d2h(o.silu_mul(o.d2h(o.gemv(mats[4], mats[5], o.d2h(h1)))))
+    dn = o.d2h(o.gemv(mats[6], mats[7], u))
+    r2, h2 = o.add_rmsnorm(dn, r1, gn)
+    assert np.array_equal(ra.view(np.uint16), np.asarray(r2).view(np.uint16).ravel())
+    assert np.array_equal(h64a, np.asarray(h2).ravel())
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -734,6 +784,9 @@ MUTANTS = [
     ("attention_values_from_keys", "acc += s[t] * q4o_h2d(vc[", "acc += s[t] * q4o_h2d(kc["),
     ("qkv_rope_unrounded", "y[r] = q4o_h2d(q4o_d2h(q4o_row_dot(W, S, x, k, r)));", "y[r] = q4o_row_dot(W, S, x, k, r);"),
     ("qkv_rope_v_slice", "v[r] = y[nq + nk + r];", "v[r] = y[nq + r];"),
+    ("layer_attn_second_norm_uses_first_residual", "q4o_add_rmsnorm(dn, ra, gamma_next", "q4o_add_rmsnorm(dn, r_in, gamma_next"),
+    ("layer_attn_o_reads_values", "q4o_gemv(Wo, So, att, d, nq, tmp);", "q4o_gemv(Wo, So, v_new, d, nq, tmp);"),
+    ("layer_attn_new_key_not_cached", "memcpy(kc + pos * nk, k_new, sizeof(uint16_t) * (size_t)nk);", "memcpy(kc + pos * nk, kc, sizeof(uint16_t) * (size_t)nk);"),
 ]
 
 
