@@ -330,6 +330,31 @@ q4_status q4_stack_decode(const q4_stack_desc *desc, const uint16_t *r_in,
                           const uint16_t *h_in, uint16_t *r_out, uint16_t *h_out,
                           uint16_t *trace, q4_stream stream);
 
+/* q4_stack_decode_attn -- the same stack with the real attention step in place
+ * of the single-position identity ("Decode loop"): per layer
+ *   q = RoPE(f16(Wqkv[L] . h)) queries; the rotated key and the value of the
+ *       token written to kv_pages[L] at *pos (as q4_qkv_rope_append)
+ *   a = attention of q over positions 0 .. *pos of kv_pages[L]
+ *       (as q4_attention_decode)
+ *   o = f16(Wo[L] . a), then add+RMSNorm, gate_up + SiLU*mul, down, add+RMSNorm
+ *       as in q4_stack_decode.
+ * The descriptor's n_qkv must be (n_heads + 2 n_kv) * head_dim and dv must be
+ * n_heads * head_dim (v_off is unused); mode Q4_STACK_PERSISTENT is
+ * Q4_EINVAL (the attention runs on the multi-kernel path). attn->kv_pages is a
+ * HOST array of n_layers device caches of attn->geom's geometry; the page
+ * table and the position (device) are shared by the layers. */
+typedef struct q4_stack_attn {
+    const q4_attn_desc *geom;
+    uint16_t *const *kv_pages;
+    const int32_t *page_table;
+    const int32_t *pos;
+    int64_t max_len;
+} q4_stack_attn;
+
+q4_status q4_stack_decode_attn(const q4_stack_desc *desc, const q4_stack_attn *attn,
+                               const uint16_t *r_in, const uint16_t *h_in, uint16_t *r_out,
+                               uint16_t *h_out, uint16_t *trace, q4_stream stream);
+
 /* q4_stack_status -- synchronises `stream` and reports whether a persistent
  * q4_stack_decode on it gave up waiting for data (every wait inside the kernel
  * is bounded; a timeout makes the kernel finish with undefined outputs and is

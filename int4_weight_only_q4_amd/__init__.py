@@ -35,7 +35,7 @@ ABI_SYMBOLS = (
     "q4_gemv_batched", "q4_moe_gemv", "q4_add_rmsnorm", "q4_silu_mul", "q4_gemv_ex",
     "q4_stack_decode", "q4_stack_status", "q4_timer_arm", "q4_timer_read", "q4_gemv_f32",
     "q4_argmax", "q4_lm_head_argmax", "q4_kv_page_bytes", "q4_qkv_rope_append",
-    "q4_rope_append", "q4_attention_decode",
+    "q4_rope_append", "q4_attention_decode", "q4_stack_decode_attn",
 )
 
 
@@ -67,6 +67,11 @@ class AttnDesc(C.Structure):
                 ("rope_base", C.c_float)]
 
 
+class StackAttn(C.Structure):
+    _fields_ = [("geom", C.POINTER(AttnDesc)), ("kv_pages", C.c_void_p), ("page_table", C.c_void_p),
+                ("pos", C.c_void_p), ("max_len", C.c_int64)]
+
+
 _P, _I = C.c_void_p, C.c_int64
 _SIGS = {
     "q4_version": (C.c_char_p, []),
@@ -91,6 +96,8 @@ _SIGS = {
     "q4_qkv_rope_append": (C.c_int, [_P, _P, _P, _I, C.POINTER(AttnDesc), _P, _P, _P, _P, _P]),
     "q4_rope_append": (C.c_int, [_P, C.POINTER(AttnDesc), _P, _P, _P, _P, _P]),
     "q4_attention_decode": (C.c_int, [_P, _P, _P, _P, _I, C.POINTER(AttnDesc), _P, _P]),
+    "q4_stack_decode_attn": (C.c_int, [C.POINTER(StackDesc), C.POINTER(StackAttn), _P, _P, _P, _P,
+                                       _P, _P]),
 }
 
 _lib = None
@@ -373,6 +380,18 @@ class Stack:
 
     def set_mode(self, mode):
         self.desc.mode = mode
+
+    def decode_attn(self, geom, caches, page_table, pos, max_len, r_in, h_in, r_out, h_out,
+                    trace=None, stream=None):
+        """One token with the real attention step: caches is a list of one
+        device cache per layer (see kv_cache), pos an int32 device tensor."""
+        arr = (C.c_void_p * len(caches))(*[c.data_ptr() for c in caches])
+        self._attn_keep = (arr, geom)
+        a = StackAttn(C.pointer(geom), C.cast(arr, C.c_void_p), page_table.data_ptr(),
+                      pos.data_ptr(), int(max_len))
+        _check(lib().q4_stack_decode_attn(C.byref(self.desc), C.byref(a), _ptr(r_in), _ptr(h_in),
+                                          _ptr(r_out), _ptr(h_out), _ptr(trace),
+                                          _stream(stream)))
 
 
 def stack_status(stream=None):

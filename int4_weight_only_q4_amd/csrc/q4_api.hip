@@ -145,8 +145,17 @@ q4_status check_gemv_args(const uint32_t *W, const uint16_t *S, const uint16_t *
 // ---------------------------------------------------------------------------
 // Decode stack: multi-kernel path (four matvec launches per layer)
 // ---------------------------------------------------------------------------
-q4_status stack_multi(const q4_stack_desc *d, const uint16_t *r_in, const uint16_t *h_in,
-                      uint16_t *r_out, uint16_t *h_out, uint16_t *trace, hipStream_t st)
+// The attention step of a stack layer (q4_stack_decode_attn): geometry, the
+// layers' caches, and the bound on the position.
+struct StackAttn {
+    RopeArgs geom;  // pos and page_table set; kv and q_out per layer
+    uint16_t *const *kv_pages = nullptr;
+    int64_t max_len = 0;
+};
+
+q4_status stack_multi(const q4_stack_desc *d, const StackAttn *attn, const uint16_t *r_in,
+                      const uint16_t *h_in, uint16_t *r_out, uint16_t *h_out, uint16_t *trace,
+                      hipStream_t st)
 {
     const int64_t D = d->d, F = d->f;
     const size_t vb = (size_t)D * 2;
@@ -154,14 +163,19 @@ q4_status stack_multi(const q4_stack_desc *d, const uint16_t *r_in, const uint16
     // residual add happens row by row in the O / down epilogues, and the
     // RMSNorm that follows it is recomputed by every workgroup of the next
     // matvec while it stages its activation (bit-identical to q4_add_rmsnorm).
-    // workspace: header | qkv | r1 | u | rA | rB   (256-byte aligned pieces)
+    // workspace: header | qkv | r1 | u | rA | rB [| attention output | partials]
+    // (256-byte aligned pieces)
     auto al = [](size_t b) { return (b + 255) / 256 * 256; };
     const size_t q_b = al((size_t)d->n_qkv * 2), v_b = al(vb), u_b = al((size_t)F * 2);
-    const size_t total = kWsHeader + q_b + 3 * v_b + u_b;
+    const size_t a_b = attn ? al((size_t)d->dv * 2) : 0;
+    const size_t part_b = attn ? al(attention_part_bytes(attn->geom)) : 0;
+    const size_t total = kWsHeader + q_b + 3 * v_b + u_b + a_b + part_b;
     char *ws = static_cast<char *>(workspace(st, total));
     if (!ws)
         return Q4_EHIP;
     uint16_t *qkv = reinterpret_cast<uint16_t *>(ws + kWsHeader);
+    uint16_t *att = reinterpret_cast<uint16_t *>(ws + kWsHeader + q_b + 3 * v_b + u_b);
+    float *part = reinterpret_cast<float *>(ws + kWsHeader + q_b + 3 * v_b + u_b + a_b);
     char *p = ws + kWsHeader + q_b;
     uint16_t *r1 = reinterpret_cast<uint16_t *>(p);
     uint16_t *u = reinterpret_cast<uint16_t *>(p + v_b);
@@ -186,16 +200,31 @@ q4_status stack_multi(const q4_stack_desc *d, const uint16_t *r_in, const uint16
             qk.norm_gamma = d->gamma_in + L * D;
             qk.norm_eps = d->eps;
         }
-        qk.epi = GemvOp::NONE;
-        qk.y = qkv;
-        if ((s = launch_gemv_op(qk, st)) != Q4_OK)
-            return s;
+        const uint16_t *o_in = qkv + d->v_off;  // single position: attention returns V
+        if (attn) {
+            // RoPE and the cache write in the QKV epilogue, then attention
+            qk.epi = GemvOp::ROPE;
+            qk.rope = attn->geom;
+            qk.rope.kv = attn->kv_pages[L];
+            qk.rope.q_out = qkv;
+            if ((s = launch_gemv_op(qk, st)) != Q4_OK)
+                return s;
+            if ((s = launch_attention(qkv, attn->kv_pages[L], attn->geom, attn->max_len, att, st,
+                                      part)) != Q4_OK)
+                return s;
+            o_in = att;
+        } else {
+            qk.epi = GemvOp::NONE;
+            qk.y = qkv;
+            if ((s = launch_gemv_op(qk, st)) != Q4_OK)
+                return s;
+        }
         GemvOp o;
         o.W = d->Wo[L];
         o.S = d->So[L];
         o.N = (int)D;
         o.K = (int)d->dv;
-        o.x = qkv + d->v_off;
+        o.x = o_in;
         o.epi = GemvOp::RESID;
         o.res_in = rc;
         o.res_out = r1;
@@ -487,6 +516,58 @@ q4_status check_rope_io(const RopeArgs &r, const int32_t *pos, const int32_t *pa
         overlaps(kv, kv_bytes(r), page_table, (size_t)r.max_pages * 4) ||
         overlaps(q_out, qb, pos, 4) || overlaps(kv, kv_bytes(r), pos, 4))
         return fail(Q4_EALIAS, "q_out, the cache, the page table and the position overlap");
+    return Q4_OK;
+}
+// Validation shared by the two stack entry points; vslice: the V rows of the
+// QKV output feed O directly.
+q4_status check_stack(const q4_stack_desc *d, const uint16_t *r_in, const uint16_t *h_in,
+                      uint16_t *r_out, uint16_t *h_out, uint16_t *trace, bool vslice)
+{
+    if (!d)
+        return fail(Q4_EINVAL, "NULL descriptor");
+    if (d->n_layers <= 0 || d->d <= 0 || d->f <= 0 || d->n_qkv <= 0 || d->dv <= 0 || d->v_off < 0)
+        return fail(Q4_EINVAL, "non-positive stack dimension");
+    if (vslice && d->v_off + d->dv > d->n_qkv)
+        return fail(Q4_ESHAPE, "V slice [%lld, %lld) outside the QKV rows", (long long)d->v_off,
+                    (long long)(d->v_off + d->dv));
+    if (vslice && d->v_off % 8)
+        return fail(Q4_EALIGN, "v_off must be a multiple of 8 (16-byte aligned slice)");
+    if (!d->Wqkv || !d->Sqkv || !d->Wo || !d->So || !d->Wgu || !d->Sgu || !d->Wdn || !d->Sdn ||
+        !d->gamma_in || !d->gamma_post || !d->gamma_final)
+        return fail(Q4_EINVAL, "NULL pointer in the stack descriptor");
+    if (!r_in || !h_in || !r_out || !h_out)
+        return fail(Q4_EINVAL, "NULL state pointer");
+    if (!(d->eps >= 0.f))
+        return fail(Q4_EINVAL, "eps must be non-negative");
+    const int64_t D = d->d, F = d->f;
+    if (!aligned(h_in, 16) || !aligned(r_in, 2) || !aligned(r_out, 2) || !aligned(h_out, 2) ||
+        (trace && !aligned(trace, 2)))
+        return fail(Q4_EALIGN, "h_in must be 16-byte aligned, other state vectors 2-byte");
+    if (!aligned(d->gamma_in, 16) || !aligned(d->gamma_post, 16) || !aligned(d->gamma_final, 2))
+        return fail(Q4_EALIGN, "gamma_in / gamma_post must be 16-byte aligned");
+    const size_t vb = (size_t)D * 2;
+    const void *ins[2] = {r_in, h_in};
+    const void *outs[2] = {r_out, h_out};
+    for (const void *o : outs) {
+        for (const void *i : ins)
+            if (overlaps(o, vb, i, vb))
+                return fail(Q4_EALIAS, "stack outputs overlap its inputs");
+        if (trace && overlaps(o, vb, trace, (size_t)d->n_layers * 2 * vb))
+            return fail(Q4_EALIAS, "stack outputs overlap the trace");
+    }
+    if (overlaps(r_out, vb, h_out, vb))
+        return fail(Q4_EALIAS, "r_out overlaps h_out");
+    for (int64_t L = 0; L < d->n_layers; ++L) {
+        q4_status st;
+        if ((st = check_matrix(d->Wqkv[L], d->Sqkv[L], d->n_qkv, D)) != Q4_OK ||
+            (st = check_matrix(d->Wo[L], d->So[L], D, d->dv)) != Q4_OK ||
+            (st = check_matrix(d->Wgu[L], d->Sgu[L], 2 * F, D)) != Q4_OK ||
+            (st = check_matrix(d->Wdn[L], d->Sdn[L], D, F)) != Q4_OK)
+            return st;
+    }
+    const int mode = d->mode;
+    if (mode != Q4_STACK_AUTO && mode != Q4_STACK_MULTI && mode != Q4_STACK_PERSISTENT)
+        return fail(Q4_EINVAL, "unknown stack mode %d", mode);
     return Q4_OK;
 }
 }  // namespace
@@ -860,66 +941,69 @@ q4_status q4_silu_mul(const uint16_t *gu, uint16_t *out, int64_t F, int64_t M, q
     return launch_silu_mul(gu, out, (int)F, (int)M, as_stream(stream));
 }
 
+
 q4_status q4_stack_decode(const q4_stack_desc *d, const uint16_t *r_in, const uint16_t *h_in,
                           uint16_t *r_out, uint16_t *h_out, uint16_t *trace, q4_stream stream)
 {
-    if (!d)
-        return fail(Q4_EINVAL, "NULL descriptor");
-    if (d->n_layers <= 0 || d->d <= 0 || d->f <= 0 || d->n_qkv <= 0 || d->dv <= 0 || d->v_off < 0)
-        return fail(Q4_EINVAL, "non-positive stack dimension");
-    if (d->v_off + d->dv > d->n_qkv)
-        return fail(Q4_ESHAPE, "V slice [%lld, %lld) outside the QKV rows", (long long)d->v_off,
-                    (long long)(d->v_off + d->dv));
-    if (d->v_off % 8)
-        return fail(Q4_EALIGN, "v_off must be a multiple of 8 (16-byte aligned slice)");
-    if (!d->Wqkv || !d->Sqkv || !d->Wo || !d->So || !d->Wgu || !d->Sgu || !d->Wdn || !d->Sdn ||
-        !d->gamma_in || !d->gamma_post || !d->gamma_final)
-        return fail(Q4_EINVAL, "NULL pointer in the stack descriptor");
-    if (!r_in || !h_in || !r_out || !h_out)
-        return fail(Q4_EINVAL, "NULL state pointer");
-    if (!(d->eps >= 0.f))
-        return fail(Q4_EINVAL, "eps must be non-negative");
-    const int64_t D = d->d, F = d->f;
-    if (!aligned(h_in, 16) || !aligned(r_in, 2) || !aligned(r_out, 2) || !aligned(h_out, 2) ||
-        (trace && !aligned(trace, 2)))
-        return fail(Q4_EALIGN, "h_in must be 16-byte aligned, other state vectors 2-byte");
-    if (!aligned(d->gamma_in, 16) || !aligned(d->gamma_post, 16) || !aligned(d->gamma_final, 2))
-        return fail(Q4_EALIGN, "gamma_in / gamma_post must be 16-byte aligned");
-    const size_t vb = (size_t)D * 2;
-    const void *ins[2] = {r_in, h_in};
-    const void *outs[2] = {r_out, h_out};
-    for (const void *o : outs) {
-        for (const void *i : ins)
-            if (overlaps(o, vb, i, vb))
-                return fail(Q4_EALIAS, "stack outputs overlap its inputs");
-        if (trace && overlaps(o, vb, trace, (size_t)d->n_layers * 2 * vb))
-            return fail(Q4_EALIAS, "stack outputs overlap the trace");
-    }
-    if (overlaps(r_out, vb, h_out, vb))
-        return fail(Q4_EALIAS, "r_out overlaps h_out");
-    for (int64_t L = 0; L < d->n_layers; ++L) {
-        q4_status st;
-        if ((st = check_matrix(d->Wqkv[L], d->Sqkv[L], d->n_qkv, D)) != Q4_OK ||
-            (st = check_matrix(d->Wo[L], d->So[L], D, d->dv)) != Q4_OK ||
-            (st = check_matrix(d->Wgu[L], d->Sgu[L], 2 * F, D)) != Q4_OK ||
-            (st = check_matrix(d->Wdn[L], d->Sdn[L], D, F)) != Q4_OK)
-            return st;
-    }
-
-    const int mode = d->mode;
-    if (mode != Q4_STACK_AUTO && mode != Q4_STACK_MULTI && mode != Q4_STACK_PERSISTENT)
-        return fail(Q4_EINVAL, "unknown stack mode %d", mode);
+    q4_status s = check_stack(d, r_in, h_in, r_out, h_out, trace, true);
+    if (s != Q4_OK)
+        return s;
     hipStream_t st = as_stream(stream);
-    if (mode == Q4_STACK_PERSISTENT) {
+    if (d->mode == Q4_STACK_PERSISTENT) {
         bool ran = false;
-        q4_status s = stack_persistent(d, r_in, h_in, r_out, h_out, trace, st, &ran);
+        s = stack_persistent(d, r_in, h_in, r_out, h_out, trace, st, &ran);
         if (s != Q4_OK || ran)
             return s;
         char why[sizeof(g_err)];
         memcpy(why, g_err, sizeof(why));
         return fail(Q4_ERANGE, "the persistent stack kernel cannot run here: %s", why);
     }
-    return stack_multi(d, r_in, h_in, r_out, h_out, trace, st);
+    return stack_multi(d, nullptr, r_in, h_in, r_out, h_out, trace, st);
+}
+
+q4_status q4_stack_decode_attn(const q4_stack_desc *d, const q4_stack_attn *attn,
+                               const uint16_t *r_in, const uint16_t *h_in, uint16_t *r_out,
+                               uint16_t *h_out, uint16_t *trace, q4_stream stream)
+{
+    q4_status s = check_stack(d, r_in, h_in, r_out, h_out, trace, false);
+    if (s != Q4_OK)
+        return s;
+    if (d->mode == Q4_STACK_PERSISTENT)
+        return fail(Q4_EINVAL, "the attention stack runs on the multi-kernel path");
+    if (!attn || !attn->kv_pages)
+        return fail(Q4_EINVAL, "NULL attention description or cache array");
+    StackAttn a;
+    if ((s = check_attn_desc(attn->geom, &a.geom)) != Q4_OK)
+        return s;
+    const RopeArgs &g = a.geom;
+    if (d->n_qkv != (int64_t)(g.n_heads + 2 * g.n_kv) * g.head_dim ||
+        d->dv != (int64_t)g.n_heads * g.head_dim)
+        return fail(Q4_ESHAPE, "n_qkv must be (n_heads + 2 n_kv) * head_dim and dv n_heads * head_dim");
+    const int nc = g.head_dim / 8;
+    if (nc != 1 && nc != 2 && nc != 4 && nc != 6 && nc != 8 && nc != 12 && nc != 16 && nc != 20 &&
+        nc != 24 && nc != 32)
+        return fail(Q4_ESHAPE, "no attention kernel for head_dim %d", g.head_dim);
+    if (attn->max_len < 1)
+        return fail(Q4_EINVAL, "max_len must be positive");
+    if (!attn->pos || !attn->page_table || !aligned(attn->pos, 4) || !aligned(attn->page_table, 4))
+        return fail(Q4_EINVAL, "NULL or misaligned position or page table");
+    const size_t cb = kv_bytes(g), vb = (size_t)d->d * 2;
+    for (int64_t L = 0; L < d->n_layers; ++L) {
+        uint16_t *kv = attn->kv_pages[L];
+        if (!kv || !aligned(kv, 16))
+            return fail(Q4_EALIGN, "NULL or misaligned cache of layer %lld", (long long)L);
+        if (overlaps(kv, cb, r_out, vb) || overlaps(kv, cb, h_out, vb) ||
+            overlaps(kv, cb, r_in, vb) || overlaps(kv, cb, h_in, vb) ||
+            overlaps(kv, cb, attn->page_table, (size_t)g.max_pages * 4) ||
+            overlaps(kv, cb, attn->pos, 4) ||
+            (trace && overlaps(kv, cb, trace, (size_t)d->n_layers * 2 * vb)))
+            return fail(Q4_EALIAS, "the cache of layer %lld overlaps another argument", (long long)L);
+    }
+    a.geom.pos = attn->pos;
+    a.geom.page_table = attn->page_table;
+    a.kv_pages = attn->kv_pages;
+    a.max_len = attn->max_len;
+    return stack_multi(d, &a, r_in, h_in, r_out, h_out, trace, as_stream(stream));
 }
 
 q4_status q4_stack_status(q4_stream stream)

@@ -258,18 +258,21 @@ q4_status launch_rope_append(const uint16_t *qkv, const RopeArgs &r, hipStream_t
     return check_launch("k_rope_append");
 }
 
+size_t attention_part_bytes(const RopeArgs &r)
+{
+    return (size_t)r.n_heads * kMaxSplits * (2 + r.head_dim) * sizeof(float);
+}
+
 q4_status launch_attention(const uint16_t *q, const uint16_t *kv, const RopeArgs &r,
-                           int64_t max_len, uint16_t *out, hipStream_t stream)
+                           int64_t max_len, uint16_t *out, hipStream_t stream, float *part)
 {
     const int64_t cap = (int64_t)r.max_pages * r.page_size;
     const int64_t len = std::max<int64_t>(1, std::min(max_len, cap));
     // one split per block of 256 positions, up to kMaxSplits
     const int NS = (int)std::min<int64_t>(kMaxSplits, (len + kAttnThreads - 1) / kAttnThreads);
     const float scale = (float)(1.0 / std::sqrt((double)r.head_dim));
-    float *part = nullptr;
-    if (NS > 1) {
-        char *ws = static_cast<char *>(workspace(
-            stream, kWsHeader + (size_t)r.n_heads * NS * (2 + r.head_dim) * sizeof(float)));
+    if (NS > 1 && !part) {
+        char *ws = static_cast<char *>(workspace(stream, kWsHeader + attention_part_bytes(r)));
         if (!ws)
             return Q4_EHIP;
         part = reinterpret_cast<float *>(ws + kWsHeader);

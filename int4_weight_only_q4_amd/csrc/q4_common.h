@@ -143,8 +143,12 @@ q4_status launch_mfma_rows(const uint32_t *W, const uint16_t *S, const uint16_t 
                            float *part, hipStream_t stream);
 // RoPE + KV append from a stored qkv vector, and decode attention (q4_attn.hip)
 q4_status launch_rope_append(const uint16_t *qkv, const RopeArgs &r, hipStream_t stream);
+// part: f32 scratch of attention_part_bytes(r), or nullptr for the library
+// workspace of the stream
+size_t attention_part_bytes(const RopeArgs &r);
 q4_status launch_attention(const uint16_t *q, const uint16_t *kv, const RopeArgs &r,
-                           int64_t max_len, uint16_t *out, hipStream_t stream);
+                           int64_t max_len, uint16_t *out, hipStream_t stream,
+                           float *part = nullptr);
 // LM head and greedy argmax (q4_lmhead.hip)
 q4_status launch_gemv_f32(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
                           float *y, int64_t ldy, int N, int K, int M, hipStream_t stream);

@@ -242,3 +242,28 @@ def test_attention_validation():
     assert att(X, R + 65536, R + 64, R, 16, C.byref(d), X + 2, None) == q4.Q4_EALIAS
     odd = q4.attn_desc(4, 4, 80)  # a multiple of 8 without a kernel
     assert att(X, R + 65536, R + 64, R, 16, C.byref(odd), Y, None) == q4.Q4_ESHAPE
+
+
+def test_stack_attention_validation():
+    arr = (C.c_void_p * 1)(A)
+    sarr = (C.c_void_p * 1)(B)
+    ptr, sptr = C.cast(arr, C.c_void_p), C.cast(sarr, C.c_void_p)
+    g = q4.attn_desc(4, 2, 64, 16, 8, 8)
+    kv = (C.c_void_p * 1)(R + 0x100000)
+    a = q4.StackAttn(C.pointer(g), C.cast(kv, C.c_void_p), R, R + 64, 128)
+    # n_qkv = (4 + 4) * 64 = 512, dv = 256
+    d = q4.StackDesc(1, 256, 512, 512, 0, 256, 1e-5, ptr, sptr, ptr, sptr, ptr, sptr, ptr, sptr,
+                     R + 4096, R + 8192, R + 12288)
+    st = q4.lib().q4_stack_decode_attn
+    assert st(C.byref(d), None, X, X + 4096, Y, Y + 4096, None, None) == q4.Q4_EINVAL
+    d.dv = 192
+    assert st(C.byref(d), C.byref(a), X, X + 4096, Y, Y + 4096, None, None) == q4.Q4_ESHAPE
+    d.dv = 256
+    d.mode = q4.STACK_PERSISTENT
+    assert st(C.byref(d), C.byref(a), X, X + 4096, Y, Y + 4096, None, None) == q4.Q4_EINVAL
+    d.mode = q4.STACK_AUTO
+    a.max_len = 0
+    assert st(C.byref(d), C.byref(a), X, X + 4096, Y, Y + 4096, None, None) == q4.Q4_EINVAL
+    a.max_len = 128
+    kv[0] = Y  # the cache over the outputs
+    assert st(C.byref(d), C.byref(a), X, X + 4096, Y, Y + 4096, None, None) == q4.Q4_EALIAS

@@ -188,3 +188,104 @@ def test_persistent_equals_multi_kernel(o, q4, phi3, which):
     c = _run_mode(q4, stack, st, p["d"], p["layers"], q4.STACK_PERSISTENT)
     q4.stack_status()
     assert np.array_equal(np.asarray(c[1]).view(np.uint16), np.asarray(a[1]).view(np.uint16))
+
+
+# ---------------------------------------------------------------------------
+# the stack with the real attention step (q4_stack_decode_attn)
+# ---------------------------------------------------------------------------
+
+def _attn_stack(o, q4, geom, n_layers, seed):
+    """Host and device weights of a stack whose QKV rows are n_heads query,
+    n_kv key and n_kv value heads, and whose O matrix reads n_heads heads."""
+    d, f, nh, nkv, hd = geom
+    nrows = (nh + 2 * nkv) * hd
+    host_layers, dev_layers = [], []
+    for L in range(n_layers):
+        mats = []
+        for j, (n, k) in enumerate(((nrows, d), (d, nh * hd), (2 * f, d), (d, f))):
+            s = seed + 100 * L + 10 * j
+            mats += [o.pack(datagen.codes(s, n, k)), datagen.scales(s + 1, n, k)]
+        host_layers.append(mats)
+        dev_layers.append([dev_tensor(m) for m in mats])
+    gi = datagen.gammas(seed + 7, n_layers, d)
+    gp = datagen.gammas(seed + 8, n_layers, d)
+    gf = datagen.gammas(seed + 9, 1, d)[0]
+    return host_layers, dev_layers, gi, gp, gf
+
+
+@pytest.mark.parametrize("geom,n_layers,pos", [((256, 512, 4, 2, 64), 3, 37),
+                                               ((256, 512, 4, 4, 64), 2, 0)])
+def test_stack_with_attention_teacher_forced(o, q4, geom, n_layers, pos):
+    import torch
+    d, f, nh, nkv, hd = geom
+    eps = 1e-5
+    hl, dl, gi, gp, gf = _attn_stack(o, q4, geom, n_layers, 2100 + pos)
+    desc = q4.attn_desc(nh, nkv, hd, 16, 8, 8)
+    table = np.array([5, 2, 7, 0, 1, 3, 6, 4], np.int32)
+    tab = torch.from_numpy(table).cuda()
+    posd = torch.tensor([pos], dtype=torch.int32, device="cuda")
+    # caches with random rows for positions < pos (position pos is written by the step)
+    caches0 = []
+    for L in range(n_layers):
+        c = np.zeros((8, 2, nkv, 16, hd), np.float16)
+        if pos:
+            t = np.arange(pos)
+            c[table[t // 16], 0, :, t % 16, :] = datagen.activations(2200 + L, pos, nkv * hd).reshape(pos, nkv, hd)
+            c[table[t // 16], 1, :, t % 16, :] = datagen.activations(2300 + L, pos, nkv * hd).reshape(pos, nkv, hd)
+        caches0.append(c)
+    caches = [torch.from_numpy(c.copy()).cuda() for c in caches0]
+    st = q4.Stack(dl, dev_tensor(gi), dev_tensor(gp), dev_tensor(gf), d, f, (nh + 2 * nkv) * hd, 0,
+                  nh * hd, eps=eps)
+    r0 = datagen.activations(2400, 1, d)[0]
+    h0 = datagen.activations(2401, 1, d)[0]
+    r_out = torch.empty(d, dtype=torch.float16, device="cuda")
+    h_out = torch.empty(d, dtype=torch.float16, device="cuda")
+    trace = torch.empty((n_layers, 2, d), dtype=torch.float16, device="cuda")
+    st.decode_attn(desc, caches, tab, posd, 128, dev_tensor(r0), dev_tensor(h0), r_out, h_out,
+                   trace=trace)
+    torch.cuda.synchronize()
+    tr = host(trace)
+    f64 = lambda a: np.abs(np.asarray(a, dtype=np.float64))
+    r_in, h_in = r0, h0
+    for L in range(n_layers):
+        Wq, Sq, Wo, So, Wg, Sg, Wd, Sd = hl[L]
+        dev = dl[L]
+        g_next = gi[L + 1] if L + 1 < n_layers else gf
+        what = "layer %d" % L
+        # the chain of single calls from the same inputs and the cache before the step
+        kv = torch.from_numpy(caches0[L].copy()).cuda()
+        rd, hd_ = dev_tensor(r_in), dev_tensor(h_in)
+        q = q4.qkv_rope_append(dev[0], dev[1], hd_, desc, posd, tab, kv)
+        a = q4.attention_decode(q, kv, tab, posd, 128, desc)
+        r1 = torch.empty_like(rd)
+        h1 = q4.gemv_ex(dev[2], dev[3], a, kind=q4.EPI_ADD_RMSNORM, res_in=rd, gamma=dev_tensor(gp[L]),
+                        res_out=r1, eps=eps)
+        u = q4.gemv_ex(dev[4], dev[5], h1, kind=q4.EPI_SILU_MUL)
+        r2 = torch.empty_like(rd)
+        h2 = q4.gemv_ex(dev[6], dev[7], u, kind=q4.EPI_ADD_RMSNORM, res_in=r1,
+                        gamma=dev_tensor(g_next), res_out=r2, eps=eps)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(r2), tr[L, 0].view(np.uint16)), what + ": stack r != op chain"
+        assert np.array_equal(bits(h2), tr[L, 1].view(np.uint16)), what + ": stack h != op chain"
+        assert np.array_equal(bits(kv), bits(caches[L])), what + ": stack cache != op chain"
+        # every op against the oracle, from the GPU's own inputs
+        qr, kr, vr = o.qkv_rope(Wq, Sq, h_in, nh, nkv, hd, pos)
+        assert_within(host(q), qr, what + " q")
+        c = host(kv)
+        t = np.arange(pos + 1)
+        kc = c[table[t // 16], 0, :, t % 16, :]
+        vc = c[table[t // 16], 1, :, t % 16, :]
+        assert_within(kc[pos].ravel(), kr, what + " k")
+        assert_within(vc[pos].ravel(), vr, what + " v")
+        assert_within(host(a), o.attention(host(q), kc, vc, nh, nkv, hd), what + " attention")
+        o_ref = o.gemv(Wo, So, host(a))
+        r1_ref, _ = o.add_rmsnorm(o.d2h(o_ref), r_in, gp[L], eps=eps)
+        assert_within_scaled(host(r1), r1_ref[0], f64(o_ref) + f64(r_in), what + " r1")
+        _, h1_ref = o.add_rmsnorm(None, host(r1), gp[L], eps=eps)
+        assert_within(host(h1), h1_ref[0], what + " h1")
+        assert_within(host(u), o.silu_mul(o.d2h(o.gemv(Wg, Sg, host(h1))))[0], what + " u")
+        dn_ref = o.gemv(Wd, Sd, host(u))
+        r2_ref, _ = o.add_rmsnorm(o.d2h(dn_ref), host(r1), g_next, eps=eps)
+        assert_within_scaled(host(r2), r2_ref[0], f64(dn_ref) + f64(host(r1)), what + " r2")
+        r_in, h_in = tr[L, 0], tr[L, 1]
+    assert np.array_equal(bits(r_out), tr[-1, 0].view(np.uint16))
