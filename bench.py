@@ -464,6 +464,36 @@ def gemv_table(q4, torch):
                               "(5 kernels) back to back" % uniq))
         print("  MoE T=%-2d %8.3f us/layer %8.1f GB/s (unique experts %.2f)" % (
             t, call_us, gbs, uniq), file=sys.stderr, flush=True)
+    # Phi-3-mini decode token, 32 layers, with the real attention step over L
+    # cached positions (each layer its own cache; the step appends at L - 1)
+    stack, stt = build_stack(q4, torch, PHI3)
+    r_out = torch.empty(PHI3["d"], dtype=torch.float16, device="cuda")
+    h_out = torch.empty(PHI3["d"], dtype=torch.float16, device="cuda")
+    for L in (1024, 4096):
+        npages = -(-L // 16)
+        g = q4.attn_desc(32, 32, 96, 16, npages)
+        first = torch.from_numpy(datagen.normal_f16(base + 3500, (npages, 2, 32, 16, 96))).cuda()
+        caches = [first] + [first.clone() for _ in range(PHI3["layers"] - 1)]
+        tab = torch.arange(npages, dtype=torch.int32, device="cuda")
+        posL = torch.tensor([L - 1], dtype=torch.int32, device="cuda")
+
+        def launch(i, g=g, caches=caches, tab=tab, posL=posL, L=L):
+            stack.decode_attn(g, caches, tab, posL, L, stt["r0"], stt["h0"], r_out, h_out)
+        call_us, _ = _time(q4, torch, launch, 20, timed_kernels=False)
+        wb = stack_weight_bytes(PHI3) + PHI3["layers"] * L * 32 * 96 * 2 * 2
+        gbs = wb / (call_us * 1e-6) / 1e9
+        rows.append(dict(workload="Phi-3-mini decode token with attention (32 layers)",
+                         shape="L=%d" % L, m=1, weight_bytes=int(wb), us_kernel=None,
+                         us_per_call=round(call_us, 3), gbs=round(gbs, 1),
+                         pct_peak=round(100 * gbs / HBM_PEAK_GBS, 1),
+                         note="q4_stack_decode_attn: 6 or 7 kernels per layer; bytes = weights "
+                              "+ K and V of every layer"))
+        print("  decode token + attention L=%-5d %9.1f us/token %8.1f GB/s" % (L, call_us, gbs),
+              file=sys.stderr, flush=True)
+        del caches, first
+        torch.cuda.empty_cache()
+    del stack
+    torch.cuda.empty_cache()
     return rows
 
 

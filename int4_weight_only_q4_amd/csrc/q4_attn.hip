@@ -31,6 +31,7 @@ namespace {
 constexpr int kAttnThreads = 256;
 constexpr int kMaxHeadDim = 256;
 constexpr int kMaxSplits = 32;
+constexpr int kSplitGrain = 64;  // positions: a split covers whole pieces of this size
 
 // One thread per RoPE pair of a stored f16 qkv vector.
 __global__ __launch_bounds__(256) void k_rope_append(const uint16_t *__restrict__ qkv, RopeArgs r,
@@ -115,8 +116,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(const uint16_t *__restric
     const int64_t kv_dist = (int64_t)r.n_kv * r.page_size * D;  // K row -> V row
     const int cap = r.max_pages * r.page_size;
     const int L = min(max(*r.pos + 1, 0), cap);
-    const int nblk = (L + kAttnThreads - 1) / kAttnThreads;
-    const int chunk = kAttnThreads * ((nblk + NS - 1) / NS);
+    // splits of whole kSplitGrain-position pieces
+    const int npc = (L + kSplitGrain - 1) / kSplitGrain;
+    const int chunk = kSplitGrain * ((npc + NS - 1) / NS);
     const int t0 = s * chunk, t1 = min(L, t0 + chunk);
 
     for (int d = tid; d < D; d += kAttnThreads)
@@ -268,8 +270,21 @@ q4_status launch_attention(const uint16_t *q, const uint16_t *kv, const RopeArgs
 {
     const int64_t cap = (int64_t)r.max_pages * r.page_size;
     const int64_t len = std::max<int64_t>(1, std::min(max_len, cap));
-    // one split per block of 256 positions, up to kMaxSplits
-    const int NS = (int)std::min<int64_t>(kMaxSplits, (len + kAttnThreads - 1) / kAttnThreads);
+    // one workgroup per head up to one block of positions (no combine step);
+    // beyond, about two workgroups per CU over the heads, in splits of whole
+    // kSplitGrain pieces, and no fewer splits than blocks of 256 positions
+    int cu = 256;
+    {
+        int dev = 0;
+        if (hipGetDevice(&dev) == hipSuccess)
+            hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev);
+    }
+    const int64_t fill = (2 * (int64_t)cu + r.n_heads - 1) / r.n_heads;
+    const int64_t by_grain = std::min<int64_t>((len + kSplitGrain - 1) / kSplitGrain, fill);
+    const int64_t by_block = (len + kAttnThreads - 1) / kAttnThreads;
+    const int NS = len <= kAttnThreads
+                       ? 1
+                       : (int)std::min<int64_t>(kMaxSplits, std::max(by_grain, by_block));
     const float scale = (float)(1.0 / std::sqrt((double)r.head_dim));
     if (NS > 1 && !part) {
         char *ws = static_cast<char *>(workspace(stream, kWsHeader + attention_part_bytes(r)));
