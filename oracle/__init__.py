@@ -59,6 +59,7 @@ _SIGS = {
     "q4o_rope": (None, [_P, _P, _I, _I, _I, C.c_double]),
     "q4o_qkv_rope": (None, [_P, _P, _P, _I, _I, _I, _I, _I, C.c_double, _P, _P, _P]),
     "q4o_attention": (None, [_P, _P, _P, _I, _I, _I, _I, _P]),
+    "q4o_gemv_affine": (None, [_P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "q4o_layer_attn": (None, [_I] * 6 + [C.c_double] + [_P] * 8 + [_P, _P, C.c_double] +
                        [_P] * 9),
 }
@@ -157,6 +158,21 @@ class Oracle:
         return y
 
     # -- epilogues -----------------------------------------------------------
+    # -- MLX affine format ------------------------------------------------------
+    def gemv_affine(self, W, S, B, X):
+        """X f16 [M, K] (or [K]) -> y f64 [M, N] (or [N]); w = S*q + B, group 64."""
+        W = np.ascontiguousarray(W, dtype=np.uint32)
+        S, B = self._u16(S), self._u16(B)
+        one = np.asarray(X).ndim == 1
+        X = self._u16(np.atleast_2d(X))
+        n, k = W.shape[0], W.shape[1] * 8
+        m = X.shape[0]
+        assert X.shape[1] == k and S.shape == (n, k // 64) and B.shape == (n, k // 64)
+        y = np.empty((m, n), np.float64)
+        self.lib.q4o_gemv_affine(self._ptr(W), self._ptr(S), self._ptr(B), self._ptr(X), k, n, k,
+                                 m, self._ptr(y))
+        return y[0] if one else y
+
     # -- LM head and greedy sampling ------------------------------------------
     def argmax(self, v):
         """Index of the largest value (ties: smallest index; NaN ranks highest)."""

@@ -574,3 +574,36 @@ void q4o_layer_attn(int64_t d, int64_t f, int64_t n_heads, int64_t n_kv, int64_t
     free(qd); free(kd); free(vd); free(q); free(kc); free(vc); free(tmp); free(att);
     free(o); free(ra); free(h1); free(gu); free(u); free(dn);
 }
+
+/* ------------------------------------------------------------------------ */
+/* MLX affine 4-bit format (Zero TVM Documentation, "Qwen3.6-35B-A3B MoE":    */
+/* affine w = s*q + b with group 64; BENCH.md, "Affine wide loads": a group  */
+/* of 64 codes is eight uint32 words, a vec2<u32> one quarter of it).       */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Weight r, k of an affine matrix: codes packed as in the Q4F16 format
+ * (element i of a word in bits 4i..4i+3; the pages give no other order), q
+ * unsigned in 0..15, and w = S[r][k/64] * q + B[r][k/64] with binary16 scales
+ * and biases, exact in binary64.
+ */
+static double q4o_weight_affine(const uint32_t *W, const uint16_t *S, const uint16_t *B,
+                                int64_t k_total, int64_t r, int64_t k)
+{
+    const int q = q4o_code(W, k_total, r, k);
+    const int64_t gi = r * (k_total / 64) + k / 64;
+    return q4o_h2d(S[gi]) * (double)q + q4o_h2d(B[gi]);
+}
+
+/* y[b][r] = sum_k w[r][k] * x[b*ldx + k] for m activation rows, binary64. */
+void q4o_gemv_affine(const uint32_t *W, const uint16_t *S, const uint16_t *B,
+                     const uint16_t *x, int64_t ldx, int64_t n, int64_t k, int64_t m, double *y)
+{
+    for (int64_t b = 0; b < m; ++b)
+        for (int64_t r = 0; r < n; ++r) {
+            double acc = 0.0;
+            for (int64_t c = 0; c < k; ++c)
+                acc += q4o_weight_affine(W, S, B, k, r, c) * q4o_h2d(x[b * ldx + c]);
+            y[b * n + r] = acc;
+        }
+}

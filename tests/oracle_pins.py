@@ -743,6 +743,66 @@ def pin_layer_attn_is_rope_attention_then_layer(o):
     assert np.array_equal(h64a, np.asarray(h2).ravel())
 
 
+# -- MLX affine format ------------------------------------------------------------
+# w = s * q + b with q unsigned, s and b per 64-code group (Zero TVM
+# Documentation, the Qwen3.6 MoE model entry; BENCH.md, "Affine wide loads").
+
+def _affine(o, seed, n, k):
+    codes = datagen.codes(seed, n, k)
+    S = datagen.scales(seed + 1, n, k // 2)  # one per 64 codes
+    B = datagen.normal_f16(seed + 2, (n, k // 64), 0.0, 0.05)
+    return codes, o.pack(codes), S, B
+
+
+def pin_affine_one_hot_is_weight(o):
+    n, k = 40, 256
+    codes, W, S, B = _affine(o, 800, n, k)
+    for c in (0, 1, 7, 31, 32, 63, 64, 130, 255):
+        x = np.zeros(k, np.float16)
+        x[c] = 1.0
+        want = o.h2d(S[:, c // 64]) * codes[:, c] + o.h2d(B[:, c // 64])
+        assert np.array_equal(o.gemv_affine(W, S, B, x), want), c
+
+
+def pin_affine_zero_codes_sum_biases(o):
+    """All codes 0: y = sum_g b_g * (sum of x over group g)."""
+    n, k = 24, 512
+    _, _, S, B = _affine(o, 801, n, k)
+    W = o.pack(np.zeros((n, k), np.uint8))
+    x = datagen.activations(802, 1, k)[0]
+    xs = o.h2d(x).reshape(k // 64, 64).sum(1)
+    want = (o.h2d(B) * xs).sum(1)
+    assert np.allclose(o.gemv_affine(W, S, B, x), want, rtol=1e-13, atol=1e-13)
+
+
+def pin_affine_matches_symmetric_format(o):
+    """With b = -7 s (exact here: s has at most 8 significant bits) and both
+    32-halves of a group sharing s, the affine weight equals the q4f16_1 one."""
+    n, k = 32, 256
+    codes = datagen.codes(803, n, k)
+    rng = np.random.default_rng(803)
+    S = (rng.integers(20, 200, size=(n, k // 64)) * 2.0 ** -12).astype(np.float16)
+    B = (-7.0 * S.astype(np.float64)).astype(np.float16)
+    assert np.array_equal(B.astype(np.float64), -7.0 * S.astype(np.float64))
+    W = o.pack(codes)
+    S32 = np.repeat(S, 2, axis=1)
+    x = datagen.activations(804, 2, k)
+    assert np.array_equal(o.gemv_affine(W, S, B, x), np.stack([o.gemv(W, S32, x[i]) for i in range(2)]))
+
+
+def pin_affine_brute_force(o):
+    n, k = 3, 128
+    codes, W, S, B = _affine(o, 805, n, k)
+    x = datagen.activations(806, 1, k)[0]
+    xd = [float(v) for v in x.astype(np.float64)]
+    for r in range(n):
+        acc = Fraction(0)
+        for c in range(k):
+            w = Fraction(float(S[r, c // 64])) * int(codes[r, c]) + Fraction(float(B[r, c // 64]))
+            acc += w * Fraction(xd[c])
+        assert abs(o.gemv_affine(W, S, B, x)[r] - float(acc)) <= 1e-12 * (1 + abs(float(acc)))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -785,6 +845,9 @@ MUTANTS = [
     ("qkv_rope_unrounded", "y[r] = q4o_h2d(q4o_d2h(q4o_row_dot(W, S, x, k, r)));", "y[r] = q4o_row_dot(W, S, x, k, r);"),
     ("qkv_rope_v_slice", "v[r] = y[nq + nk + r];", "v[r] = y[nq + r];"),
     ("layer_attn_second_norm_uses_first_residual", "q4o_add_rmsnorm(dn, ra, gamma_next", "q4o_add_rmsnorm(dn, r_in, gamma_next"),
+    ("affine_bias_dropped", "return q4o_h2d(S[gi]) * (double)q + q4o_h2d(B[gi]);", "return q4o_h2d(S[gi]) * (double)q;"),
+    ("affine_group_of_32", "const int64_t gi = r * (k_total / 64) + k / 64;", "const int64_t gi = r * (k_total / 64) + (k / 32) % (k_total / 64);"),
+    ("affine_zero_point_7", "return q4o_h2d(S[gi]) * (double)q + q4o_h2d(B[gi]);", "return q4o_h2d(S[gi]) * (double)(q - 7) + q4o_h2d(B[gi]);"),
     ("layer_attn_o_reads_values", "q4o_gemv(Wo, So, att, d, nq, tmp);", "q4o_gemv(Wo, So, v_new, d, nq, tmp);"),
     ("layer_attn_new_key_not_cached", "memcpy(kc + pos * nk, k_new, sizeof(uint16_t) * (size_t)nk);", "memcpy(kc + pos * nk, kc, sizeof(uint16_t) * (size_t)nk);"),
 ]
