@@ -351,6 +351,28 @@ def gemv_table(q4, torch):
               base + 1000)
     gemv_rows("Qwen3-4B", list(QWEN3.items()), [1, 8], base + 2000)
 
+    # the MLX affine format (w = s * q + b, group 64) at the Qwen3-4B shapes
+    for j, (name, (n, k)) in enumerate([("qkv", (6144, 2560)), ("gate_up", (19456, 2560)),
+                                        ("down", (2560, 9728))]):
+        Wh = torch.from_numpy(datagen.words(base + 2600 + 10 * j, n, k).view(np.int32)).cuda()
+        Sh = torch.from_numpy(datagen.scales(base + 2601 + 10 * j, n, k // 2)).cuda()
+        Bh = torch.from_numpy(datagen.normal_f16(base + 2602 + 10 * j, (n, k // 64), 0.0, 0.05)).cuda()
+        copies = max(2, -(-(512 << 20) // int(n * k * BPW)))
+        rot = [(Wh, Sh, Bh)] + [(Wh.clone(), Sh.clone(), Bh.clone()) for _ in range(copies - 1)]
+        wb = n * k * BPW
+        for m in (1, 8):
+            x = torch.from_numpy(datagen.activations(base + 2603 + 10 * j, m, k)).cuda()
+            y = torch.empty((m, n), dtype=torch.float16, device="cuda")
+
+            def launch(i, rot=rot, x=x, y=y, m=m):
+                W, S, B = rot[i % len(rot)]
+                q4.gemv_affine(W, S, B, x[0] if m == 1 else x, y=y[0] if m == 1 else y)
+            add("Qwen3-4B MLX affine", "%s %dx%d" % (name, n, k), m, wb, launch,
+                count=max(20, min(200, int(4e9 / wb))),
+                note="w = s*q + b, group 64 (scales and biases f16: 4.5 bits per weight)")
+        del rot
+        torch.cuda.empty_cache()
+
     # LM head with f32 logits and the greedy token (the whole call: matvec and
     # argmax kernels); the Qwen3-4B head is tied to the embedding matrix
     for j, (workload, n, k, ms) in enumerate([("Phi-3-mini LM head", 32064, 3072, [1]),

@@ -186,6 +186,20 @@ q4_status q4_gemv_ex(const uint32_t *W, const uint16_t *S, const uint16_t *x, ui
                      int64_t N, int64_t K, const q4_epilogue *epi, q4_stream stream);
 
 /* ---------------------------------------------------------------------------
+ * q4_gemv_affine -- the MLX affine 4-bit format (Zero TVM Documentation, the
+ * Qwen3.6-35B-A3B entry: affine w = s * q + b, group 64; BENCH.md, "Affine
+ * wide loads"): M activation rows, unsigned codes q (0..15) packed as for
+ * q4_gemv (the pages give no other order), scales and biases per 64 codes:
+ *   y[m*ldy + n] = f16( sum_k (S[n][k/64] * q[n][k] + B[n][k/64]) * x[m*ldx + k] )
+ * W u32[N][K/8], S and B f16[N][K/64] (2-byte aligned), K % 64 == 0; x and y
+ * as for q4_gemv_batched. f32 accumulation; M = 1 runs the single-row kernel,
+ * M >= 2 the matrix cores (exact integer operands, scale and bias in f32).
+ */
+q4_status q4_gemv_affine(const uint32_t *W, const uint16_t *S, const uint16_t *B,
+                         const uint16_t *x, int64_t ldx, uint16_t *y, int64_t ldy, int64_t N,
+                         int64_t K, int64_t M, q4_stream stream);
+
+/* ---------------------------------------------------------------------------
  * LM head and greedy sampling (Zero TVM Documentation, "Decode loop": the LM
  * head's matmul writes the logits and an argmax picks the next token; shader
  * 10, "Argmax Sampler"; RESEARCH.md, "Why Fewer Dispatches Matter", the

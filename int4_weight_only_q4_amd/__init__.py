@@ -35,7 +35,7 @@ ABI_SYMBOLS = (
     "q4_gemv_batched", "q4_moe_gemv", "q4_add_rmsnorm", "q4_silu_mul", "q4_gemv_ex",
     "q4_stack_decode", "q4_stack_status", "q4_timer_arm", "q4_timer_read", "q4_gemv_f32",
     "q4_argmax", "q4_lm_head_argmax", "q4_kv_page_bytes", "q4_qkv_rope_append",
-    "q4_rope_append", "q4_attention_decode", "q4_stack_decode_attn",
+    "q4_rope_append", "q4_attention_decode", "q4_stack_decode_attn", "q4_gemv_affine",
 )
 
 
@@ -93,6 +93,7 @@ _SIGS = {
     "q4_argmax": (C.c_int, [_P, _I, _I, _I, _P, _P]),
     "q4_lm_head_argmax": (C.c_int, [_P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _P]),
     "q4_kv_page_bytes": (C.c_int64, [C.POINTER(AttnDesc)]),
+    "q4_gemv_affine": (C.c_int, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _P]),
     "q4_qkv_rope_append": (C.c_int, [_P, _P, _P, _I, C.POINTER(AttnDesc), _P, _P, _P, _P, _P]),
     "q4_rope_append": (C.c_int, [_P, C.POINTER(AttnDesc), _P, _P, _P, _P, _P]),
     "q4_attention_decode": (C.c_int, [_P, _P, _P, _P, _I, C.POINTER(AttnDesc), _P, _P]),
@@ -208,6 +209,21 @@ def gemv_batched(W, S, x, y=None, stream=None):
         y = torch.empty((m, n), dtype=torch.float16, device=W.device)
     _check(lib().q4_gemv_batched(_ptr(W), _ptr(S), _ptr(x), x.stride(0), _ptr(y), y.stride(0),
                                  n, k, m, _stream(stream)))
+    return y
+
+
+def gemv_affine(W, S, B, x, y=None, stream=None):
+    """MLX affine 4-bit matvec: x f16 [K] or [M, K] -> y f16 [N] or [M, N];
+    S, B f16 [N, K/64] (w = S*q + B)."""
+    import torch
+    n, k = W.shape[0], W.shape[1] * 8
+    x2 = x.unsqueeze(0) if x.dim() == 1 else x
+    m = x2.shape[0]
+    if y is None:
+        y = torch.empty((m, n) if x.dim() > 1 else (n,), dtype=torch.float16, device=W.device)
+    y2 = y.unsqueeze(0) if y.dim() == 1 else y
+    _check(lib().q4_gemv_affine(_ptr(W), _ptr(S), _ptr(B), _ptr(x2), x2.stride(0), _ptr(y2),
+                                y2.stride(0), n, k, m, _stream(stream)))
     return y
 
 

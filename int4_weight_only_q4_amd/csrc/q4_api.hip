@@ -862,6 +862,46 @@ q4_status q4_attention_decode(const uint16_t *q, const uint16_t *kv_pages,
     return launch_attention(q, kv_pages, r, max_len, out, as_stream(stream));
 }
 
+q4_status q4_gemv_affine(const uint32_t *W, const uint16_t *S, const uint16_t *B,
+                         const uint16_t *x, int64_t ldx, uint16_t *y, int64_t ldy, int64_t N,
+                         int64_t K, int64_t M, q4_stream stream)
+{
+    q4_status st = check_matrix(W, S, N, K);
+    if (st != Q4_OK)
+        return st;
+    if (K % 64)
+        return fail(Q4_ESHAPE, "K=%lld is not a multiple of 64 (affine groups)", (long long)K);
+    if (!B || !x || !y)
+        return fail(Q4_EINVAL, "NULL bias, activation or output pointer");
+    if (M < 1 || M > Q4_MAX_M)
+        return fail(Q4_ERANGE, "M=%lld outside [1, %d]", (long long)M, Q4_MAX_M);
+    if (ldx < K || ldy < N)
+        return fail(Q4_EINVAL, "leading dimensions too small (ldx=%lld, ldy=%lld)",
+                    (long long)ldx, (long long)ldy);
+    if (!aligned(x, 16) || ldx % 8)
+        return fail(Q4_EALIGN, "activation rows must be 16-byte aligned (ldx %% 8 == 0)");
+    if (!aligned(y, 2) || !aligned(B, 2))
+        return fail(Q4_EALIGN, "the output and the biases must be 2-byte aligned");
+    const size_t yb = ((size_t)(M - 1) * ldy + N) * 2, xb = ((size_t)(M - 1) * ldx + K) * 2;
+    const size_t sb = (size_t)N * (K / 64) * 2;
+    if (overlaps(y, yb, W, wbytes(N, K)) || overlaps(y, yb, S, sb) || overlaps(y, yb, B, sb) ||
+        overlaps(y, yb, x, xb))
+        return fail(Q4_EALIAS, "the output overlaps an input");
+    hipStream_t s = as_stream(stream);
+    if (M == 1) {
+        GemvOp op;
+        op.W = W;
+        op.S = S;
+        op.bias = B;
+        op.N = (int)N;
+        op.K = (int)K;
+        op.x = x;
+        op.y = y;
+        return launch_gemv_op(op, s);
+    }
+    return launch_gemv_mfma(W, S, x, ldx, y, nullptr, ldy, (int)N, (int)K, (int)M, s, B);
+}
+
 q4_status q4_moe_gemv(const uint32_t *W, const uint16_t *S, const int32_t *ids,
                       const uint16_t *route_w, const uint16_t *x, int64_t ldx,
                       int64_t x_slot_stride, uint16_t *y, int64_t E, int64_t N, int64_t K,

@@ -112,6 +112,9 @@ struct GemvOp {
     float *yf = nullptr;
     unsigned long long *cand = nullptr;
     RopeArgs rope;
+    // the MLX affine format (biases [N][K/64], scales [N][K/64]): plain NONE
+    // epilogue with x only
+    const uint16_t *bias = nullptr;
 };
 q4_status launch_gemv_op(const GemvOp &op, hipStream_t stream);
 // Workgroups of one launch_gemv_op for N rows of K (the candidates LOGITS writes).
@@ -128,10 +131,11 @@ size_t moe_part_bytes(int N, int K, int P);
 // Whether the expert kernel routes by itself (meta == nullptr) for P pairs and E experts.
 bool moe_routes_in_kernel(int P, int E);
 // M >= 2 rows on the matrix cores (q4_mfma.hip): f16 outputs y, or f32
-// outputs yf when yf is set (y is then ignored)
+// outputs yf when yf is set (y is then ignored); bias set: the MLX affine
+// format (scales and biases [N][K/64])
 q4_status launch_gemv_mfma(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
                            uint16_t *y, float *yf, int64_t ldy, int N, int K, int M,
-                           hipStream_t stream);
+                           hipStream_t stream, const uint16_t *bias = nullptr);
 // One matrix-core launch for mt <= 16 activation rows. With mfma_splits(K) > 1
 // it leaves f32 partials part[ks][m][n] (mfma_part_bytes(N, K) bytes) and
 // writes neither y nor yf; otherwise the results go to yf (f32) when set, else
@@ -140,7 +144,7 @@ int mfma_splits(int K);
 size_t mfma_part_bytes(int N, int K);
 q4_status launch_mfma_rows(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
                            uint16_t *y, float *yf, int64_t ldy, int N, int K, int mt,
-                           float *part, hipStream_t stream);
+                           float *part, hipStream_t stream, const uint16_t *bias = nullptr);
 // RoPE + KV append from a stored qkv vector, and decode attention (q4_attn.hip)
 q4_status launch_rope_append(const uint16_t *qkv, const RopeArgs &r, hipStream_t stream);
 // part: f32 scratch of attention_part_bytes(r), or nullptr for the library

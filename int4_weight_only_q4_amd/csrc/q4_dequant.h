@@ -7,8 +7,8 @@
 // Unpack without conversions (see group_dot): codes are masked straight into
 // subnormal binary16 pairs that v_dot2_f32_f16 multiplies exactly. The
 // activation is staged with each 8-element chunk stored as the pairs (x0,x4)
-// (x1,x5) (x2,x6) (x3,x7), which line up with the masks, and with 7 * (group
-// sum) beside it.
+// (x1,x5) (x2,x6) (x3,x7), which line up with the masks, and with each 32-value
+// group's sum beside it.
 #pragma once
 
 #include "q4_common.h"
@@ -47,8 +47,8 @@ __device__ __forceinline__ uint32_t load_scale(const uint16_t *p)
 // activation chunk is staged as the matching pairs (x0,x4) (x1,x5) (x2,x6)
 // (x3,x7). v_dot2_f32_f16 multiplies exactly (f16 denormals are kept) and
 // accumulates in f32; lo gathers the 2^-24-scaled pairs, hi the 2^-20-scaled
-// ones, and sum (c - 7) x = 2^24 lo + 2^20 hi - 7 sum(x), with c7 = 7 sum(x)
-// staged beside the activation. A one-hot x therefore gives (c - 7) exactly.
+// ones, and sum (c - 7) x = 2^24 lo + 2^20 hi - 7 sum(x), with sum(x) staged
+// beside the activation. A one-hot x therefore gives (c - 7) exactly.
 // Position in the staged activation of quarter q (chunk 4 g + q) of group g.
 // The four 16-byte quarters of a group are rotated by g / 2: lanes that read
 // the same quarter of consecutive groups (64 bytes apart) would otherwise hit
@@ -56,10 +56,12 @@ __device__ __forceinline__ uint32_t load_scale(const uint16_t *p)
 // groups.
 __device__ __forceinline__ int staged_index(int g, int q) { return 4 * g + ((q + (g >> 1)) & 3); }
 
-__device__ __forceinline__ float group_dot(uint4 wv, const uint4 *xs, int g, float c7)
+// lo (the 2^-24-scaled pairs) and hi (the 2^-20-scaled ones) of the 32 codes
+// of wv against staged group g, accumulated onto the values passed in.
+__device__ __forceinline__ void group_dot_parts(uint4 wv, const uint4 *xs, int g, float &lo,
+                                                float &hi)
 {
     const uint32_t m0 = 0x000F000Fu, m1 = 0x00F000F0u;
-    float lo = 0.f, hi = 0.f;
     const uint32_t w[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -70,11 +72,26 @@ __device__ __forceinline__ float group_dot(uint4 wv, const uint4 *xs, int g, flo
         lo = __builtin_amdgcn_fdot2(as_h2(t & m0), as_h2(xq.z), lo, false);
         hi = __builtin_amdgcn_fdot2(as_h2(t & m1), as_h2(xq.w), hi, false);
     }
-    return fmaf(0x1p24f, lo, fmaf(0x1p20f, hi, -c7));
+}
+
+// sum over the group of (c - 7) x; sx = the staged sum of x over the group.
+__device__ __forceinline__ float group_dot(uint4 wv, const uint4 *xs, int g, float sx)
+{
+    float lo = 0.f, hi = 0.f;
+    group_dot_parts(wv, xs, g, lo, hi);
+    return fmaf(0x1p24f, lo, fmaf(0x1p20f, hi, -7.f * sx));
+}
+
+// sum over the group of c x (the unsigned codes of the affine format).
+__device__ __forceinline__ float group_dot_unsigned(uint4 wv, const uint4 *xs, int g)
+{
+    float lo = 0.f, hi = 0.f;
+    group_dot_parts(wv, xs, g, lo, hi);
+    return fmaf(0x1p24f, lo, 0x1p20f * hi);
 }
 
 // Stage x[K] (K % 32 == 0) into LDS: xs[K/8] pair-interleaved chunks and
-// cs[K/32] = 7 * group sums. Must be called by all 256 threads.
+// cs[K/32] = group sums. Must be called by all 256 threads.
 __device__ __forceinline__ void stage_activation(const uint16_t *__restrict__ x, int K, uint4 *xs, float *cs)
 {
     const int chunks = K >> 3;
@@ -95,7 +112,7 @@ __device__ __forceinline__ void stage_activation(const uint16_t *__restrict__ x,
         sum += __shfl_xor(sum, 1, 64);
         sum += __shfl_xor(sum, 2, 64);
         if (c < chunks && (c & 3) == 0)
-            cs[c >> 2] = 7.f * sum;
+            cs[c >> 2] = sum;
     }
 }
 
@@ -109,7 +126,7 @@ __device__ __forceinline__ void chunk_to_float(uint4 v, float f[8])
 }
 
 // Write one staged chunk (thread-held, chunk index c of a K-vector) into LDS in
-// the pair-interleaved order, and 7 * (group sum) for every 4th chunk. All
+// the pair-interleaved order, and the group sum for every 4th chunk. All
 // 256 threads must call it together (for every j), since it shuffles.
 __device__ __forceinline__ void put_chunk(uint4 v, int c, bool valid, uint4 *xs, float *cs)
 {
@@ -127,7 +144,7 @@ __device__ __forceinline__ void put_chunk(uint4 v, int c, bool valid, uint4 *xs,
     sum += __shfl_xor(sum, 1, 64);
     sum += __shfl_xor(sum, 2, 64);
     if (valid && (c & 3) == 0)
-        cs[c >> 2] = 7.f * sum;
+        cs[c >> 2] = sum;
 }
 
 }  // namespace q4

@@ -33,7 +33,8 @@ enum { EPI_NONE_ = 0, EPI_SILU = 1, EPI_RESID = 2, EPI_LOGITS = 3, EPI_ROPE = 4 
 
 struct GemvParams {
     const uint4 *W;     // [N][G] groups of 16 bytes
-    const uint16_t *S;  // [N][G]
+    const uint16_t *S;  // [N][G]; affine: [N][G/2] (one scale per 64 codes)
+    const uint16_t *Bias;  // affine: biases [N][G/2]
     int N, G;
     // prologue: PRO_X reads x; PRO_NORM stages f16(RMSNorm(src) * gamma)
     const uint16_t *x;  // [K], 16-byte aligned (PRO_X) or the residual (PRO_NORM)
@@ -48,7 +49,9 @@ struct GemvParams {
     RopeArgs rope;             // ROPE: geometry, position, cache and q_out
 };
 
-template <int LPR, int NG, int RPS, int EPI, int PRO>
+// AFF: the MLX affine format (unsigned codes, w = s * q + b per 64 codes): a
+// 16-byte load is half a group, its scale and bias are those of group g / 2.
+template <int LPR, int NG, int RPS, int EPI, int PRO, bool AFF = false>
 __global__ __launch_bounds__(256) void k_gemv(GemvParams a)
 {
     constexpr int SPW = 64 / LPR;             // segments (rows) per wave
@@ -112,6 +115,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams a)
     // 1. weight and scale loads, in the order they are consumed (group-major)
     uint4 wv[NG][RPS];
     uint32_t sv[NG][RPS];
+    uint32_t bv[AFF ? NG : 1][AFF ? RPS : 1];
     // (branch-free: a lane past the last group re-reads group G - 1, which the
     // accumulation skips; a conditional load would let the compiler convert the
     // scale inside the branch and wait for it there)
@@ -122,7 +126,13 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams a)
             const int g = min(j + LPR * i, G - 1);
             const size_t off = (size_t)row[r] * G + g;
             wv[i][r] = load_weights(a.W + off);
-            sv[i][r] = load_scale(a.S + off);
+            if (AFF) {
+                const size_t soff = (size_t)row[r] * (G >> 1) + (g >> 1);
+                sv[i][r] = load_scale(a.S + soff);
+                bv[i][r] = load_scale(a.Bias + soff);
+            } else {
+                sv[i][r] = load_scale(a.S + off);
+            }
         }
 
     // 2. activation into LDS (after an RMSNorm of the residual for PRO_NORM)
@@ -173,10 +183,16 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams a)
     for (int i = 0; i < NG; ++i) {
         const int g = j + LPR * i;
         if (g < G) {
-            const float c7 = cs[g];
+            const float sx = cs[g];
 #pragma unroll
-            for (int r = 0; r < RPS; ++r)
-                acc[r] = fmaf(h2f(sv[i][r]), group_dot(wv[i][r], xs, g, c7), acc[r]);
+            for (int r = 0; r < RPS; ++r) {
+                if (AFF) {
+                    acc[r] = fmaf(h2f(sv[i][r]), group_dot_unsigned(wv[i][r], xs, g), acc[r]);
+                    acc[r] = fmaf(h2f(bv[i][r]), sx, acc[r]);
+                } else {
+                    acc[r] = fmaf(h2f(sv[i][r]), group_dot(wv[i][r], xs, g, sx), acc[r]);
+                }
+            }
         }
     }
 
@@ -281,7 +297,7 @@ Cfg choose_cfg(int G)
     return best;
 }
 
-template <int LPR, int NG, int EPI, int PRO>
+template <int LPR, int NG, int EPI, int PRO, bool AFF>
 q4_status run_gemv(const GemvParams &p, hipStream_t st)
 {
     constexpr int RPS = rows_per_segment(NG);
@@ -291,44 +307,44 @@ q4_status run_gemv(const GemvParams &p, hipStream_t st)
     const int rb = paired ? RB / 2 : RB;
     const int blocks = (rows + rb - 1) / rb;
     const size_t lds = (size_t)p.G * 32 * 2 + (size_t)p.G * 4;
-    Q4_LAUNCH_MATVEC((k_gemv<LPR, NG, RPS, EPI, PRO>), dim3(blocks), dim3(256), lds, st, p);
+    Q4_LAUNCH_MATVEC((k_gemv<LPR, NG, RPS, EPI, PRO, AFF>), dim3(blocks), dim3(256), lds, st, p);
     return check_launch("k_gemv");
 }
 
-template <int LPR, int EPI, int PRO>
+template <int LPR, int EPI, int PRO, bool AFF = false>
 q4_status dispatch_ng(int ng, const GemvParams &p, hipStream_t st)
 {
     switch (ng) {
-    case 1: return run_gemv<LPR, 1, EPI, PRO>(p, st);
-    case 2: return run_gemv<LPR, 2, EPI, PRO>(p, st);
-    case 3: return run_gemv<LPR, 3, EPI, PRO>(p, st);
-    case 4: return run_gemv<LPR, 4, EPI, PRO>(p, st);
-    case 5: return run_gemv<LPR, 5, EPI, PRO>(p, st);
-    case 6: return run_gemv<LPR, 6, EPI, PRO>(p, st);
-    case 7: return run_gemv<LPR, 7, EPI, PRO>(p, st);
-    case 8: return run_gemv<LPR, 8, EPI, PRO>(p, st);
+    case 1: return run_gemv<LPR, 1, EPI, PRO, AFF>(p, st);
+    case 2: return run_gemv<LPR, 2, EPI, PRO, AFF>(p, st);
+    case 3: return run_gemv<LPR, 3, EPI, PRO, AFF>(p, st);
+    case 4: return run_gemv<LPR, 4, EPI, PRO, AFF>(p, st);
+    case 5: return run_gemv<LPR, 5, EPI, PRO, AFF>(p, st);
+    case 6: return run_gemv<LPR, 6, EPI, PRO, AFF>(p, st);
+    case 7: return run_gemv<LPR, 7, EPI, PRO, AFF>(p, st);
+    case 8: return run_gemv<LPR, 8, EPI, PRO, AFF>(p, st);
     default: break;
     }
     if constexpr (LPR == 64) {
         switch (ng) {
-        case 9: return run_gemv<64, 9, EPI, PRO>(p, st);
-        case 10: return run_gemv<64, 10, EPI, PRO>(p, st);
-        case 11: return run_gemv<64, 11, EPI, PRO>(p, st);
-        case 12: return run_gemv<64, 12, EPI, PRO>(p, st);
+        case 9: return run_gemv<64, 9, EPI, PRO, AFF>(p, st);
+        case 10: return run_gemv<64, 10, EPI, PRO, AFF>(p, st);
+        case 11: return run_gemv<64, 11, EPI, PRO, AFF>(p, st);
+        case 12: return run_gemv<64, 12, EPI, PRO, AFF>(p, st);
         default: break;
         }
     }
     return fail(Q4_ERANGE, "no matvec configuration for %d groups per lane", ng);
 }
 
-template <int EPI, int PRO>
+template <int EPI, int PRO, bool AFF = false>
 q4_status dispatch_lpr(const Cfg &c, const GemvParams &p, hipStream_t st)
 {
     switch (c.lpr) {
-    case 64: return dispatch_ng<64, EPI, PRO>(c.ng, p, st);
-    case 32: return dispatch_ng<32, EPI, PRO>(c.ng, p, st);
-    case 16: return dispatch_ng<16, EPI, PRO>(c.ng, p, st);
-    case 8: return dispatch_ng<8, EPI, PRO>(c.ng, p, st);
+    case 64: return dispatch_ng<64, EPI, PRO, AFF>(c.ng, p, st);
+    case 32: return dispatch_ng<32, EPI, PRO, AFF>(c.ng, p, st);
+    case 16: return dispatch_ng<16, EPI, PRO, AFF>(c.ng, p, st);
+    case 8: return dispatch_ng<8, EPI, PRO, AFF>(c.ng, p, st);
     default: return fail(Q4_ERANGE, "no matvec configuration for K = %d", p.G * 32);
     }
 }
@@ -367,8 +383,14 @@ q4_status launch_gemv_op(const GemvOp &op, hipStream_t stream)
     p.yf = op.yf;
     p.cand = op.cand;
     p.rope = op.rope;
+    p.Bias = op.bias;
     const Cfg c = choose_cfg(p.G);
     const bool norm = op.norm_src != nullptr;
+    if (op.bias) {  // the affine format: plain output only
+        if (norm || op.epi != GemvOp::NONE)
+            return fail(Q4_EINVAL, "internal: the affine format has no prologue or epilogue");
+        return dispatch_lpr<EPI_NONE_, PRO_X, true>(c, p, stream);
+    }
     switch (op.epi) {
     case GemvOp::NONE:
         return norm ? dispatch_lpr<EPI_NONE_, PRO_NORM>(c, p, stream)

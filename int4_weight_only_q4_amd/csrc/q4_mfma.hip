@@ -51,9 +51,12 @@ constexpr int kMoePerSlot = 0, kMoeSilu = 1, kMoeCombine = 2;
 // order (e0, e4) (e1, e5) (e2, e6) (e3, e7): (w >> 4i) & 0x000F000F puts codes i
 // and i + 4 in the two halves, the exponent pattern 0x6400 makes them 1024 + q
 // and subtracting 1031 is exact. The activation is staged in the same order.
+// (UNSIGNED: the codes q themselves, the 1024 of the exponent pattern removed.)
+template <bool UNSIGNED = false>
 __device__ __forceinline__ half8 codes_minus7(uint32_t w, uint32_t mask)
 {
-    const half2v c1031 = {(_Float16)1031.0f, (_Float16)1031.0f};
+    const _Float16 off = UNSIGNED ? (_Float16)1024.0f : (_Float16)1031.0f;
+    const half2v c1031 = {off, off};
     half8 out;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -124,18 +127,21 @@ __device__ __forceinline__ u32x4 pair_order(u32x4 v)
 struct TileRegs {
     uint4 w[kDepth];
     uint32_t s[kDepth];
+    uint32_t b[kDepth];  // affine format: biases
 };
 
 // The work of one workgroup for one split ks of K (groups [ks * gc, min(G,
 // (ks + 1) * gc)), gc = kGroupsPerSplit) and M <= 16 activation rows:
 // row_ptr(m) gives activation row m; wave w takes the 16-row weight tiles
 // tile0(w), + tstride, ... (at most kMaxTilesPerWave), and emit(m, n, value)
-// receives every finished f32 result. The loads of a wave's next tile are in
-// flight while it computes the current one, and the first tile's loads while
-// the workgroup stages its activation.
-template <typename RowPtr, typename Emit>
+// receives every finished f32 result.
+// AFF: the MLX affine format (unsigned codes, w = s * q + b per 64 codes, scales
+// and biases [N][G/2]): each group's MFMA sum is scaled, and the bias times the
+// group's sum of x (staged per row) added.
+template <bool AFF, typename RowPtr, typename Emit>
 __device__ __forceinline__ void mfma_rows(const uint4 *__restrict__ W,
-                                          const uint16_t *__restrict__ S, int N, int G, int M,
+                                          const uint16_t *__restrict__ S,
+                                          const uint16_t *__restrict__ Bias, int N, int G, int M,
                                           int gc, int ks, int tile0, int tstride, RowPtr row_ptr,
                                           Emit emit)
 {
@@ -143,8 +149,10 @@ __device__ __forceinline__ void mfma_rows(const uint4 *__restrict__ W,
     const int t = threadIdx.x, l = t & 63;
     const int g0 = ks * gc, gn = min(gc, G - g0);  // groups of this split, >= 1
     const int xstride = gc * 32 + 8;  // staged row: the chunk plus 16 bytes against bank conflicts
-    // LDS: the activation chunk, M rows
+    // LDS: the activation chunk, M rows; affine: then the groups' sums of x,
+    // [group of the split][16 rows]
     _Float16 *xs = reinterpret_cast<_Float16 *>(smem);
+    float *xsum = reinterpret_cast<float *>(xs + M * xstride);
     const int cpr = gn * 4;           // 16-byte chunks per staged row
 
     // the tiles of this wave (a wave-uniform count: the guards below are
@@ -168,7 +176,14 @@ __device__ __forceinline__ void mfma_rows(const uint4 *__restrict__ W,
         for (int p = 0; p < kDepth; ++p) {
             const int gi = min(4 * p + kb, gn - 1);
             r.w[p] = load_weights(W + rb + gi);
-            r.s[p] = load_scale(S + rb + gi);
+            if (AFF) {
+                const size_t sb = (size_t)min((tile0 + j * tstride) * 16 + n, N - 1) * (G >> 1) +
+                                  ((g0 + gi) >> 1);
+                r.s[p] = load_scale(S + sb);
+                r.b[p] = load_scale(Bias + sb);
+            } else {
+                r.s[p] = load_scale(S + rb + gi);
+            }
         }
     };
     // Step p covers groups 4p .. 4p + 3 of the split, loaded by lane rows
@@ -186,25 +201,40 @@ __device__ __forceinline__ void mfma_rows(const uint4 *__restrict__ W,
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt)  // the four activation reads first
                 a[tt] = *reinterpret_cast<const half8 *>(xrow + min(4 * p + tt, gn - 1) * 32);
-            uint32_t sc[4];
+            uint32_t sc[4], bc[4];
             broadcast_rows(4 * p + kb < gn ? r.s[p] : 0u, sc);
+            if (AFF)
+                broadcast_rows(4 * p + kb < gn ? r.b[p] : 0u, bc);
             uint32_t w[4] = {r.w[p].x, r.w[p].y, r.w[p].z, r.w[p].w};
             transpose_rows(w);
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
-                const floatx4 d =
-                    __builtin_amdgcn_mfma_f32_16x16x32_f16(a[tt], codes_minus7(w[tt], mask), zero, 0, 0, 0);
+                const floatx4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    a[tt], codes_minus7<AFF>(w[tt], mask), zero, 0, 0, 0);
                 const float sf = h2f((uint16_t)sc[tt]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     acc[e] = fmaf(sf, d[e], acc[e]);
+                if (AFF) {  // + bias * (sum of x over the group) of rows 4 kb .. 4 kb + 3
+                    const floatx4 sx = *reinterpret_cast<const floatx4 *>(
+                        xsum + min(4 * p + tt, gn - 1) * 16 + 4 * kb);
+                    const float bf = h2f((uint16_t)bc[tt]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[e] = fmaf(bf, sx[e], acc[e]);
+                }
             }
         }
         return acc;
     };
 
     // 1. the activation chunk (all loads issued together, then stored in the
-    //    pair order)
+    //    pair order); affine: rows M .. 15 of the group sums are zero
+    if (AFF) {
+        for (int i = t; i < gc * 16; i += 256)
+            xsum[i] = 0.f;
+        __syncthreads();
+    }
     u32x4 xr[kXq];
 #pragma unroll
     for (int q = 0; q < kXq; ++q) {
@@ -217,6 +247,21 @@ __device__ __forceinline__ void mfma_rows(const uint4 *__restrict__ W,
         const int c = min(t + 256 * q, M * cpr - 1);  // the tail rewrites the last chunk
         const int mm = c / cpr, jj = c - mm * cpr;
         *reinterpret_cast<u32x4 *>(xs + mm * xstride + 8 * jj) = pair_order(xr[q]);
+        if (AFF) {
+            // the group's sum: 8 values in order, then the four 16-byte pieces
+            // of the group, held by four consecutive lanes (chunk rows are
+            // whole groups, so a quad of lanes never mixes groups or rows;
+            // the tail's clamped lanes form quads of their own and do not write)
+            const uint32_t u[4] = {xr[q].x, xr[q].y, xr[q].z, xr[q].w};
+            float sm = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sm = (sm + h2f((uint16_t)(u[e] & 0xFFFF))) + h2f((uint16_t)(u[e] >> 16));
+            sm += __shfl_xor(sm, 1, 64);
+            sm += __shfl_xor(sm, 2, 64);
+            if ((jj & 3) == 0 && t + 256 * q < M * cpr)
+                xsum[(jj >> 2) * 16 + mm] = sm;
+        }
     }
     __syncthreads();
 
@@ -252,8 +297,10 @@ __device__ __forceinline__ void mfma_rows(const uint4 *__restrict__ W,
 // tiles b * 4 + w, + 4 P, ... KS == 1: the f32 result written to yf when set,
 // else rounded to y; KS > 1: f32 partials part[ks][m][n] for k_combine.
 // (at most 128 registers: four waves per SIMD)
+template <bool AFF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_gemv_mfma(const uint4 *__restrict__ W,
                                                    const uint16_t *__restrict__ S,
+                                                   const uint16_t *__restrict__ Bias,
                                                    const uint16_t *__restrict__ x, int64_t ldx,
                                                    uint16_t *__restrict__ y,
                                                    float *__restrict__ yf, int64_t ldy,
@@ -261,8 +308,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
                                                    int gc)
 {
     const int ks = blockIdx.y, KS = gridDim.y;
-    mfma_rows(
-        W, S, N, G, M, gc, ks, blockIdx.x * kWaves + (threadIdx.x >> 6), gridDim.x * kWaves,
+    mfma_rows<AFF>(
+        W, S, Bias, N, G, M, gc, ks, blockIdx.x * kWaves + (threadIdx.x >> 6), gridDim.x * kWaves,
         [&](int m) { return x + m * ldx; },
         [&](int mr, int col, float v) {
             if (KS > 1)
@@ -392,8 +439,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     for (int qa = q0; qa < q1; qa += kMTile) {
         if (qa > q0)
             __syncthreads();  // the previous rows' staged activation is still read
-        mfma_rows(
-            W, S, N, G, min(kMTile, q1 - qa), gc, ks, blockIdx.x * kWaves + (threadIdx.x >> 6),
+        mfma_rows<false>(
+            W, S, nullptr, N, G, min(kMTile, q1 - qa), gc, ks, blockIdx.x * kWaves + (threadIdx.x >> 6),
             gridDim.x * kWaves,
             [&](int m) {
                 const int pr = order[qa + m];
@@ -509,7 +556,7 @@ size_t mfma_part_bytes(int N, int K)
 
 q4_status launch_mfma_rows(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
                            uint16_t *y, float *yf, int64_t ldy, int N, int K, int mt,
-                           float *part, hipStream_t stream)
+                           float *part, hipStream_t stream, const uint16_t *bias)
 {
     const int G = K / 32;
     // K splits of kGroupsPerSplit groups (the last may be shorter)
@@ -520,16 +567,22 @@ q4_status launch_mfma_rows(const uint32_t *W, const uint16_t *S, const uint16_t 
     // most kMaxTilesPerWave per wave)
     const int P = std::max({1, (ntiles + kWaves * kMaxTilesPerWave - 1) / (kWaves * kMaxTilesPerWave),
                             std::min((ntiles + kWaves - 1) / kWaves, (3 * cus() + KS - 1) / KS)});
-    const size_t lds = (size_t)mt * (gc * 32 + 8) * 2;  // staged rows
-    Q4_LAUNCH_MATVEC(k_gemv_mfma, dim3(P, KS), dim3(256), lds, stream,
-                     reinterpret_cast<const uint4 *>(W), S, x, ldx, yf ? nullptr : y, yf, ldy,
-                     part, N, G, mt, gc);
+    const size_t lds = (size_t)mt * (gc * 32 + 8) * 2 +          // staged rows
+                       (bias ? (size_t)gc * 16 * sizeof(float) : 0);  // affine: group sums
+    if (bias)
+        Q4_LAUNCH_MATVEC(k_gemv_mfma<true>, dim3(P, KS), dim3(256), lds, stream,
+                         reinterpret_cast<const uint4 *>(W), S, bias, x, ldx, yf ? nullptr : y, yf,
+                         ldy, part, N, G, mt, gc);
+    else
+        Q4_LAUNCH_MATVEC(k_gemv_mfma<false>, dim3(P, KS), dim3(256), lds, stream,
+                         reinterpret_cast<const uint4 *>(W), S, nullptr, x, ldx,
+                         yf ? nullptr : y, yf, ldy, part, N, G, mt, gc);
     return check_launch("k_gemv_mfma");
 }
 
 q4_status launch_gemv_mfma(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
                            uint16_t *y, float *yf, int64_t ldy, int N, int K, int M,
-                           hipStream_t stream)
+                           hipStream_t stream, const uint16_t *bias)
 {
     const int KS = mfma_splits(K);
     float *part = nullptr;
@@ -543,7 +596,7 @@ q4_status launch_gemv_mfma(const uint32_t *W, const uint16_t *S, const uint16_t 
         const int mt = std::min(kMTile, M - m0);
         q4_status st = launch_mfma_rows(W, S, x + m0 * ldx, ldx, yf ? nullptr : y + m0 * ldy,
                                         yf ? yf + m0 * ldy : nullptr, ldy, N, K, mt, part,
-                                        stream);
+                                        stream, bias);
         if (st != Q4_OK)
             return st;
         if (KS > 1) {

@@ -267,3 +267,13 @@ def test_stack_attention_validation():
     a.max_len = 128
     kv[0] = Y  # the cache over the outputs
     assert st(C.byref(d), C.byref(a), X, X + 4096, Y, Y + 4096, None, None) == q4.Q4_EALIAS
+
+
+def test_affine_validation():
+    f = q4.lib().q4_gemv_affine
+    assert f(A, B, None, X, 128, Y, 16, 16, 128, 1, None) == q4.Q4_EINVAL
+    assert f(A, B, R, X, 96, Y, 16, 16, 96, 1, None) == q4.Q4_ESHAPE      # K % 64
+    assert f(A, B, R, X, 128, Y, 16, 16, 128, 0, None) == q4.Q4_ERANGE
+    assert f(A, B, R, X, 128, Y, 8, 16, 128, 2, None) == q4.Q4_EINVAL     # ldy < N
+    assert f(A, B, R + 1, X, 128, Y, 16, 16, 128, 1, None) == q4.Q4_EALIGN
+    assert f(A, B, R, X, 128, R, 16, 16, 128, 1, None) == q4.Q4_EALIAS    # y over the biases
