@@ -60,6 +60,7 @@ _SIGS = {
     "q4o_qkv_rope": (None, [_P, _P, _P, _I, _I, _I, _I, _I, C.c_double, _P, _P, _P]),
     "q4o_attention": (None, [_P, _P, _P, _I, _I, _I, _I, _P]),
     "q4o_gemv_affine": (None, [_P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "q4o_gemv_w16": (None, [_P, _P, _P, _I, _I, _I, _I, _P]),
     "q4o_layer_attn": (None, [_I] * 6 + [C.c_double] + [_P] * 8 + [_P, _P, C.c_double] +
                        [_P] * 9),
 }
@@ -156,6 +157,19 @@ class Oracle:
         self.lib.q4o_gemv_batched(self._ptr(W), self._ptr(S), self._ptr(X), k, n, k, m,
                                   self._ptr(y))
         return y
+
+    def gemv_w16(self, W, S, X):
+        """Like gemv_batched, with every weight rounded to f16 before the sum."""
+        W = np.ascontiguousarray(W, dtype=np.uint32)
+        S = self._u16(S)
+        one = np.asarray(X).ndim == 1
+        X = self._u16(np.atleast_2d(X))
+        n, k = W.shape[0], W.shape[1] * 8
+        m = X.shape[0]
+        assert X.shape[1] == k
+        y = np.empty((m, n), np.float64)
+        self.lib.q4o_gemv_w16(self._ptr(W), self._ptr(S), self._ptr(X), k, n, k, m, self._ptr(y))
+        return y[0] if one else y
 
     # -- epilogues -----------------------------------------------------------
     # -- MLX affine format ------------------------------------------------------

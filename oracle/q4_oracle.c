@@ -607,3 +607,25 @@ void q4o_gemv_affine(const uint32_t *W, const uint16_t *S, const uint16_t *B,
             y[b * n + r] = acc;
         }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Weights rounded to binary16 first (Zero TVM Documentation, "Q4F16       */
+/* quantization format": the dequantization formula multiplies f16(q - 7)   */
+/* by the binary16 scale in binary16, so the weight it yields is the exact  */
+/* product rounded once to binary16).                                       */
+/* ------------------------------------------------------------------------ */
+
+/* y[b][r] = sum_k f16((q - 7) * s) * x[b*ldx + k] for m rows, binary64 sums. */
+void q4o_gemv_w16(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
+                  int64_t n, int64_t k, int64_t m, double *y)
+{
+    for (int64_t b = 0; b < m; ++b)
+        for (int64_t r = 0; r < n; ++r) {
+            double acc = 0.0;
+            for (int64_t c = 0; c < k; ++c) {
+                const double w16 = q4o_h2d(q4o_d2h(q4o_weight(W, S, k, r, c)));
+                acc += w16 * q4o_h2d(x[b * ldx + c]);
+            }
+            y[b * n + r] = acc;
+        }
+}

@@ -803,6 +803,46 @@ def pin_affine_brute_force(o):
         assert abs(o.gemv_affine(W, S, B, x)[r] - float(acc)) <= 1e-12 * (1 + abs(float(acc)))
 
 
+# -- weights rounded to f16 (the format's dequantization formula multiplies in
+# binary16: Zero TVM Documentation, "Q4F16 quantization format") -------------------
+
+def _dense_f16(codes, S):
+    """numpy's binary16 product f16(q - 7) * s (exact in float32, rounded once)."""
+    q = (codes.astype(np.int32) - 7).astype(np.float16)
+    return (q * np.repeat(S, 32, axis=1)).astype(np.float64)
+
+
+def pin_w16_one_hot_is_numpy_f16_product(o):
+    n, k = 24, 128
+    codes, W, S = _mat(o, 820, n, k)
+    exact = (codes.astype(np.float64) - 7.0) * np.repeat(S.astype(np.float64), 32, axis=1)
+    want = _dense_f16(codes, S)
+    assert np.any(want != exact), "the sample must hold weights that round"
+    for c in (0, 1, 5, 7, 31, 32, 77, 127):
+        x = np.zeros(k, np.float16)
+        x[c] = 1.0
+        assert np.array_equal(o.gemv_w16(W, S, x), want[:, c]), c
+
+
+def pin_w16_equals_exact_for_power_of_two_scales(o):
+    """Scales 2^-e make (q - 7) * s exact in binary16: no rounding happens."""
+    n, k, m = 16, 96, 3
+    codes = datagen.codes(821, n, k)
+    e = np.random.default_rng(821).integers(4, 12, size=(n, k // 32))
+    S = (2.0 ** -e).astype(np.float16)
+    W = o.pack(codes)
+    X = datagen.activations(822, m, k)
+    assert np.array_equal(o.gemv_w16(W, S, X), o.gemv_batched(W, S, X))
+
+
+def pin_w16_matches_library_matmul(o):
+    n, k, m = 29, 160, 4
+    codes, W, S = _mat(o, 823, n, k)
+    X = datagen.activations(824, m, k)
+    want = X.astype(np.float64) @ _dense_f16(codes, S).T
+    assert np.allclose(o.gemv_w16(W, S, X), want, rtol=1e-12, atol=1e-12)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -849,6 +889,8 @@ MUTANTS = [
     ("affine_group_of_32", "const int64_t gi = r * (k_total / 64) + k / 64;", "const int64_t gi = r * (k_total / 64) + (k / 32) % (k_total / 64);"),
     ("affine_zero_point_7", "return q4o_h2d(S[gi]) * (double)q + q4o_h2d(B[gi]);", "return q4o_h2d(S[gi]) * (double)(q - 7) + q4o_h2d(B[gi]);"),
     ("layer_attn_o_reads_values", "q4o_gemv(Wo, So, att, d, nq, tmp);", "q4o_gemv(Wo, So, v_new, d, nq, tmp);"),
+    ("w16_not_rounded", "const double w16 = q4o_h2d(q4o_d2h(q4o_weight(W, S, k, r, c)));", "const double w16 = q4o_weight(W, S, k, r, c);"),
+    ("w16_row_stride_ignored", "acc += w16 * q4o_h2d(x[b * ldx + c]);", "acc += w16 * q4o_h2d(x[c]);"),
     ("layer_attn_new_key_not_cached", "memcpy(kc + pos * nk, k_new, sizeof(uint16_t) * (size_t)nk);", "memcpy(kc + pos * nk, kc, sizeof(uint16_t) * (size_t)nk);"),
 ]
 
