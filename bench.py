@@ -34,6 +34,7 @@ if ROOT not in sys.path:
 import datagen  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense f16 matrix-core peak
 METRIC = "effective weight GB/s (% of HBM peak) and µs/token for int4 dequant-GEMV decode stack"
 
 PHI3 = dict(d=3072, f=8192, n_qkv=9216, v_off=6144, dv=3072, layers=32, eps=1e-5)
@@ -519,6 +520,87 @@ def gemv_table(q4, torch):
     return rows
 
 
+PREFILL = [("Phi-3-mini prefill", "QKV", 9216, 3072, 1024),
+           ("Phi-3-mini prefill", "O", 3072, 3072, 1024),
+           ("Phi-3-mini prefill", "gate_up", 16384, 3072, 1024),
+           ("Phi-3-mini prefill", "down", 3072, 8192, 1024),
+           ("Qwen3-4B prefill chunk", "gate_up", 19456, 2560, 256),
+           ("Qwen3-4B prefill chunk", "down", 2560, 9728, 256),
+           ("Qwen3-4B prefill chunk", "o", 2560, 4096, 256)]
+
+
+def prefill_table(q4, torch):
+    """Prefill matmul (q4_gemm) throughput at the Phi-3-mini (M = 1024) and
+    Qwen3-4B (M = 256, the pages' chunk shapes) matrices, both weight modes,
+    and the 16-row decode launches (q4_gemv_batched) at M = 64 beside q4_gemm
+    at M = 64 for the crossover. Weights rotated past the Infinity Cache."""
+    rows = []
+    base = datagen.SEED_BASE + 6_000_000
+
+    def add(workload, shape, m, n, k, launch, note):
+        call_us, kern_us = _time(q4, torch, launch, 40)
+        us = kern_us if kern_us is not None else call_us
+        tf = 2.0 * m * n * k / (us * 1e-6) / 1e12
+        rows.append(dict(workload=workload, shape=shape, m=m, us_kernel=round(us, 2),
+                         us_per_call=round(call_us, 2), tflops=round(tf, 1),
+                         pct_f16_peak=round(100 * tf / F16_MFMA_PEAK_TFLOPS, 1), note=note))
+        print("  %-24s %-18s M=%-5d %9.2f us %8.1f TFLOP/s  %s" % (workload, shape, m, us, tf,
+                                                                     note), file=sys.stderr,
+              flush=True)
+
+    for j, (workload, name, n, k, m) in enumerate(PREFILL):
+        rot = _rotation(torch, n, k, base + 10 * j)
+        x = torch.from_numpy(datagen.activations(base + 10 * j + 2, m, k)).cuda()
+        y = torch.empty((m, n), dtype=torch.float16, device="cuda")
+        for mode, label in ((q4.GEMM_EXACT, "exact weights"), (q4.GEMM_F16_WEIGHT, "f16 weights")):
+            def launch(i, rot=rot, x=x, y=y, mode=mode):
+                W, S = rot[i % len(rot)]
+                q4.gemm(W, S, x, y=y, weights=mode)
+            add(workload, "%s %dx%d" % (name, n, k), m, n, k, launch, "q4_gemm, " + label)
+        if j == 0:
+            for mm in (16, 64):
+                xs, ys = x[:mm], y[:mm]
+
+                def launch(i, rot=rot, xs=xs, ys=ys):
+                    W, S = rot[i % len(rot)]
+                    q4.gemv_batched(W, S, xs, y=ys)
+                add(workload, "%s %dx%d" % (name, n, k), mm, n, k, launch,
+                    "q4_gemv_batched (16-row decode launches)")
+
+                def launch(i, rot=rot, xs=xs, ys=ys):
+                    W, S = rot[i % len(rot)]
+                    q4.gemm(W, S, xs, y=ys)
+                add(workload, "%s %dx%d" % (name, n, k), mm, n, k, launch,
+                    "q4_gemm, exact weights")
+        del rot
+        torch.cuda.empty_cache()
+    return rows
+
+
+def write_prefill_table(rows):
+    text = ["# Prefill matmul (q4_gemm) on the matrix cores: Phi-3-mini M = 1024 and "
+            "Qwen3-4B M = 256",
+            "",
+            "Command (from the repository root, on one MI355X): `python3 bench.py --prefill-table`",
+            "",
+            "Weights are seeded synthetic int4 group-32 (codes U{0..15}, scales U[0.005, 0.05]), "
+            "cycled through device copies totalling more than 512 MB; activations N(0, 1) f16. "
+            "`us` is the kernel's own duration from HIP events recorded by its dispatch "
+            "(mean of up to 40 launches); TFLOP/s = 2 M N K / us; the peak is the dense f16 "
+            "matrix-core figure (2.5 PFLOP/s). Exact weights take two MFMAs per product "
+            "(binary16 hi and lo of (q - 7) s), f16 weights one.",
+            "",
+            "| workload | matrix | M | us | TFLOP/s | % of f16 peak | path |",
+            "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        text.append("| %s | %s | %d | %.2f | %.1f | %.1f | %s |" % (
+            r["workload"], r["shape"], r["m"], r["us_kernel"], r["tflops"], r["pct_f16_peak"],
+            r["note"]))
+    os.makedirs(os.path.join(ROOT, "gpurun_out"), exist_ok=True)
+    with open(os.path.join(ROOT, "gpurun_out", "prefill_table.md"), "w") as fh:
+        fh.write("\n".join(text) + "\n")
+
+
 def write_gemv_table(rows):
     text = ["# Per-GEMV throughput: single GEMV, Phi-3-mini, Qwen3-4B (M = 1, 8), LM heads with "
             "argmax, QKV + RoPE + KV append, decode attention, and MoE shapes",
@@ -603,6 +685,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--gemv-table", action="store_true",
                     help="measure the per-GEMV table (Phi-3, Qwen3 M=1/8, MoE) and exit")
+    ap.add_argument("--prefill-table", action="store_true",
+                    help="measure the prefill matmul table (q4_gemm) and exit")
     ap.add_argument("--counters", action="store_true",
                     help="run only the workload of the rocprofv3 counter passes")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -626,6 +710,11 @@ def main():
         rows = gemv_table(q4, torch)
         write_gemv_table(rows)
         print(json.dumps({"gemv_table": rows}), flush=True)
+        return
+    if args.prefill_table:
+        rows = prefill_table(q4, torch)
+        write_prefill_table(rows)
+        print(json.dumps({"prefill_table": rows}), flush=True)
         return
     p = PHI3
     print("building the %d-layer stack (%.3f GB of int4 weights)..." % (

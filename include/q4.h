@@ -200,6 +200,29 @@ q4_status q4_gemv_affine(const uint32_t *W, const uint16_t *S, const uint16_t *B
                          int64_t K, int64_t M, q4_stream stream);
 
 /* ---------------------------------------------------------------------------
+ * q4_gemm -- the prefill (many-token) int4 matmul (BENCH.md, "Tiled batched
+ * GEMM (2026-08-12)" and "Subgroup-matrix GEMM graduated": chunked prefill
+ * runs the matmul over M >= 64 activation rows at once, f16 matrix-unit
+ * fragments with f32 accumulation):
+ *   y[m*ldy + n] = f16( sum_k w[n][k] * x[m*ldx + k] ),  m = 0..M-1
+ * with, by `weights`:
+ *   Q4_GEMM_EXACT      w = (q - 7) * s exactly, as q4_gemv_batched;
+ *   Q4_GEMM_F16_WEIGHT w = f16((q - 7) * s): the dequantised weight rounded to
+ *                      binary16, as the format's dequantization formula
+ *                      computes it (Zero TVM Documentation, "Q4F16
+ *                      quantization format"); half the matrix-core work.
+ * W, S as for q4_gemv; x f16 rows, 16-byte aligned, ldx % 8 == 0, ldx >= K;
+ * y f16, 2-byte aligned, ldy >= N, caller-owned, not overlapping the inputs.
+ * 1 <= M <= Q4_MAX_GEMM_M. f32 accumulation over all of K in an unspecified
+ * order. No workspace; one kernel launch. Q4_EINVAL for an unknown `weights`.
+ */
+#define Q4_MAX_GEMM_M 65536
+typedef enum q4_gemm_weights { Q4_GEMM_EXACT = 0, Q4_GEMM_F16_WEIGHT = 1 } q4_gemm_weights;
+q4_status q4_gemm(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
+                  uint16_t *y, int64_t ldy, int64_t N, int64_t K, int64_t M, int weights,
+                  q4_stream stream);
+
+/* ---------------------------------------------------------------------------
  * LM head and greedy sampling (Zero TVM Documentation, "Decode loop": the LM
  * head's matmul writes the logits and an argmax picks the next token; shader
  * 10, "Argmax Sampler"; RESEARCH.md, "Why Fewer Dispatches Matter", the

@@ -25,6 +25,7 @@ EPI_NONE, EPI_SILU_MUL, EPI_ADD_RMSNORM = 0, 1, 2
 STACK_AUTO, STACK_MULTI, STACK_PERSISTENT = 0, 1, 2
 MAX_K = 24576
 MAX_M = 64
+MAX_GEMM_M = 65536
 MAX_PAIRS = 4096
 
 #: Bytes per int4 weight in this format: 4 bits + one f16 scale per 32 weights.
@@ -36,6 +37,7 @@ ABI_SYMBOLS = (
     "q4_stack_decode", "q4_stack_status", "q4_timer_arm", "q4_timer_read", "q4_gemv_f32",
     "q4_argmax", "q4_lm_head_argmax", "q4_kv_page_bytes", "q4_qkv_rope_append",
     "q4_rope_append", "q4_attention_decode", "q4_stack_decode_attn", "q4_gemv_affine",
+    "q4_gemm",
 )
 
 
@@ -81,6 +83,7 @@ _SIGS = {
     "q4_unpack": (C.c_int, [_P, _P, _I, _I, _P]),
     "q4_gemv": (C.c_int, [_P, _P, _P, _P, _I, _I, _P]),
     "q4_gemv_batched": (C.c_int, [_P, _P, _P, _I, _P, _I, _I, _I, _I, _P]),
+    "q4_gemm": (C.c_int, [_P, _P, _P, _I, _P, _I, _I, _I, _I, C.c_int, _P]),
     "q4_moe_gemv": (C.c_int, [_P, _P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _I, C.c_int, _P]),
     "q4_add_rmsnorm": (C.c_int, [_P, _P, _P, _P, _P, _I, _I, C.c_float, _P]),
     "q4_silu_mul": (C.c_int, [_P, _P, _I, _I, _P]),
@@ -224,6 +227,23 @@ def gemv_affine(W, S, B, x, y=None, stream=None):
     y2 = y.unsqueeze(0) if y.dim() == 1 else y
     _check(lib().q4_gemv_affine(_ptr(W), _ptr(S), _ptr(B), _ptr(x2), x2.stride(0), _ptr(y2),
                                 y2.stride(0), n, k, m, _stream(stream)))
+    return y
+
+
+GEMM_EXACT = 0
+GEMM_F16_WEIGHT = 1
+
+
+def gemm(W, S, x, y=None, weights=GEMM_EXACT, stream=None):
+    """Prefill matmul: x f16 [M, ldx >= K] -> y f16 [M, N] (any M >= 1);
+    weights GEMM_EXACT (w = (q - 7) * s) or GEMM_F16_WEIGHT (w rounded to f16)."""
+    import torch
+    n, k = W.shape[0], W.shape[1] * 8
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float16, device=W.device)
+    _check(lib().q4_gemm(_ptr(W), _ptr(S), _ptr(x), x.stride(0), _ptr(y), y.stride(0), n, k, m,
+                         int(weights), _stream(stream)))
     return y
 
 

@@ -724,6 +724,36 @@ q4_status q4_gemv_batched(const uint32_t *W, const uint16_t *S, const uint16_t *
     return launch_gemv_batched(W, S, x, ldx, y, ldy, (int)N, (int)K, (int)M, as_stream(stream));
 }
 
+q4_status q4_gemm(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
+                  uint16_t *y, int64_t ldy, int64_t N, int64_t K, int64_t M, int weights,
+                  q4_stream stream)
+{
+    q4_status st = check_matrix(W, S, N, K);
+    if (st != Q4_OK)
+        return st;
+    if (!x || !y)
+        return fail(Q4_EINVAL, "NULL activation or output pointer");
+    if (weights != Q4_GEMM_EXACT && weights != Q4_GEMM_F16_WEIGHT)
+        return fail(Q4_EINVAL, "unknown weights mode %d", weights);
+    if (M < 1 || M > Q4_MAX_GEMM_M)
+        return fail(Q4_ERANGE, "M=%lld outside [1, %d]", (long long)M, Q4_MAX_GEMM_M);
+    if ((M + 63) / 64 * ((N + 127) / 128) > 0x7FFFFFFFll)
+        return fail(Q4_ERANGE, "M=%lld x N=%lld needs too many tiles", (long long)M, (long long)N);
+    if (ldx < K || ldy < N)
+        return fail(Q4_EINVAL, "leading dimensions too small (ldx=%lld, ldy=%lld)",
+                    (long long)ldx, (long long)ldy);
+    if (!aligned(x, 16) || ldx % 8)
+        return fail(Q4_EALIGN, "activation rows must be 16-byte aligned (ldx %% 8 == 0)");
+    if (!aligned(y, 2))
+        return fail(Q4_EALIGN, "the output must be 2-byte aligned");
+    const size_t yb = ((size_t)(M - 1) * ldy + N) * 2, xb = ((size_t)(M - 1) * ldx + K) * 2;
+    if (overlaps(y, yb, W, wbytes(N, K)) || overlaps(y, yb, S, sbytes(N, K)) ||
+        overlaps(y, yb, x, xb))
+        return fail(Q4_EALIAS, "the output overlaps an input");
+    return launch_gemm(W, S, x, ldx, y, ldy, (int)N, (int)K, (int)M,
+                       weights == Q4_GEMM_EXACT, as_stream(stream));
+}
+
 
 q4_status q4_gemv_f32(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
                       float *y, int64_t ldy, int64_t N, int64_t K, int64_t M, q4_stream stream)

@@ -161,6 +161,11 @@ q4_status launch_argmax(const float *v, int64_t ld, int N, int M, int32_t *index
 q4_status launch_lm_head_argmax(const uint32_t *W, const uint16_t *S, const uint16_t *x,
                                 int64_t ldx, float *logits, int64_t ldl, int32_t *tokens, int N,
                                 int K, int M, hipStream_t stream);
+// Prefill matmul on the matrix cores (q4_gemm.hip): exact weights, or
+// weights rounded to f16 when exact is false.
+q4_status launch_gemm(const uint32_t *W, const uint16_t *S, const uint16_t *X, int64_t ldx,
+                      uint16_t *Y, int64_t ldy, int N, int K, int M, bool exact,
+                      hipStream_t stream);
 q4_status launch_gemv_batched(const uint32_t *W, const uint16_t *S, const uint16_t *x,
                               int64_t ldx, uint16_t *y, int64_t ldy, int N, int K, int M,
                               hipStream_t stream);

@@ -277,3 +277,19 @@ def test_affine_validation():
     assert f(A, B, R, X, 128, Y, 8, 16, 128, 2, None) == q4.Q4_EINVAL     # ldy < N
     assert f(A, B, R + 1, X, 128, Y, 16, 16, 128, 1, None) == q4.Q4_EALIGN
     assert f(A, B, R, X, 128, R, 16, 16, 128, 1, None) == q4.Q4_EALIAS    # y over the biases
+
+
+def test_gemm_validation():
+    f = q4.lib().q4_gemm
+    assert f(A, B, None, 128, Y, 16, 16, 128, 1, 0, None) == q4.Q4_EINVAL
+    assert f(A, B, X, 128, Y, 16, 16, 128, 4, 2, None) == q4.Q4_EINVAL     # unknown weights mode
+    assert f(A, B, X, 96, Y, 16, 16, 100, 4, 0, None) == q4.Q4_ESHAPE      # K % 32
+    assert f(A, B, X, 128, Y, 16, 16, 128, 0, 0, None) == q4.Q4_ERANGE     # M < 1
+    assert f(A, B, X, 128, Y, 16, 16, 128, q4.MAX_GEMM_M + 1, 1, None) == q4.Q4_ERANGE
+    assert f(A, B, X, 120, Y, 16, 16, 128, 4, 0, None) == q4.Q4_EINVAL     # ldx < K
+    assert f(A, B, X, 128, Y, 8, 16, 128, 4, 0, None) == q4.Q4_EINVAL      # ldy < N
+    assert f(A, B, X + 8, 128, Y, 16, 16, 128, 4, 0, None) == q4.Q4_EALIGN
+    assert f(A, B, X, 132, Y, 16, 16, 128, 4, 0, None) == q4.Q4_EALIGN     # ldx % 8
+    assert f(A, B, X, 128, Y + 1, 16, 16, 128, 4, 0, None) == q4.Q4_EALIGN
+    assert f(A, B, X, 128, X + 64, 16, 16, 128, 4, 0, None) == q4.Q4_EALIAS  # y over x
+    assert f(A, B, X, 128, B, 16, 16, 128, 4, 1, None) == q4.Q4_EALIAS     # y over the scales
