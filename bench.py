@@ -538,8 +538,9 @@ def prefill_table(q4, torch):
     base = datagen.SEED_BASE + 6_000_000
 
     def add(workload, shape, m, n, k, launch, note):
-        call_us, kern_us = _time(q4, torch, launch, 40)
-        us = kern_us if kern_us is not None else call_us
+        # whole calls back to back: a K-split call is two kernels (tiles, combine)
+        call_us, _ = _time(q4, torch, launch, 40, timed_kernels=False)
+        us = call_us
         tf = 2.0 * m * n * k / (us * 1e-6) / 1e12
         rows.append(dict(workload=workload, shape=shape, m=m, us_kernel=round(us, 2),
                          us_per_call=round(call_us, 2), tflops=round(tf, 1),
@@ -572,7 +573,22 @@ def prefill_table(q4, torch):
                     q4.gemm(W, S, xs, y=ys)
                 add(workload, "%s %dx%d" % (name, n, k), mm, n, k, launch,
                     "q4_gemm, exact weights")
-        del rot
+        # context: torch's dense f16 matmul (hipBLASLt) of the same shape, weights
+        # already f16 (four times the weight bytes, no dequantisation)
+        xd = x.clone()
+        wd = torch.randn(k, n, dtype=torch.float16, device="cuda")
+
+        def launch(i, xd=xd, wd=wd, y=y):
+            torch.mm(xd, wd, out=y)
+        call_us, _ = _time(q4, torch, launch, 40, timed_kernels=False)
+        tf = 2.0 * m * n * k / (call_us * 1e-6) / 1e12
+        rows.append(dict(workload=workload, shape="%s %dx%d" % (name, n, k), m=m,
+                         us_kernel=round(call_us, 2), us_per_call=round(call_us, 2),
+                         tflops=round(tf, 1), pct_f16_peak=round(100 * tf / F16_MFMA_PEAK_TFLOPS, 1),
+                         note="reference: torch.mm dense f16 (not int4)"))
+        print("  %-24s %-18s M=%-5d %9.2f us %8.1f TFLOP/s  reference: torch.mm dense f16" % (
+            workload, "%s %dx%d" % (name, n, k), m, call_us, tf), file=sys.stderr, flush=True)
+        del rot, wd, xd
         torch.cuda.empty_cache()
     return rows
 
@@ -585,10 +601,13 @@ def write_prefill_table(rows):
             "",
             "Weights are seeded synthetic int4 group-32 (codes U{0..15}, scales U[0.005, 0.05]), "
             "cycled through device copies totalling more than 512 MB; activations N(0, 1) f16. "
-            "`us` is the kernel's own duration from HIP events recorded by its dispatch "
-            "(mean of up to 40 launches); TFLOP/s = 2 M N K / us; the peak is the dense f16 "
+            "`us` is the mean time per call over 40 calls back to back (a call whose grid would "
+            "fill under half the GPU splits K: tile kernel + combine kernel); "
+            "TFLOP/s = 2 M N K / us; the peak is the dense f16 "
             "matrix-core figure (2.5 PFLOP/s). Exact weights take two MFMAs per product "
-            "(binary16 hi and lo of (q - 7) s), f16 weights one.",
+            "(binary16 hi and lo of (q - 7) s), f16 weights one. The reference rows time "
+            "torch.mm on dense f16 weights of the same shape (back-to-back calls, event "
+            "timing), for context only.",
             "",
             "| workload | matrix | M | us | TFLOP/s | % of f16 peak | path |",
             "|---|---|---|---|---|---|---|"]

@@ -58,6 +58,23 @@ q4_status check_launch(const char *what)
     return Q4_OK;
 }
 
+// Compute units of the current device (cached per device; 256 if unknown).
+int cu_count()
+{
+    static int n[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (!n[dev]) {
+        int c = 0;
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            c <= 0)
+            c = 256;
+        n[dev] = c;
+    }
+    return n[dev];
+}
+
 void *workspace(hipStream_t stream, size_t bytes)
 {
     int dev = 0;

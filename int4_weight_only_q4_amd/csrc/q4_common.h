@@ -51,6 +51,8 @@ bool take_armed_timer(hipEvent_t *start, hipEvent_t *stop);
 constexpr size_t kCounterBytes = 256;
 constexpr size_t kWsHeader = kCounterBytes;
 void *workspace(hipStream_t stream, size_t bytes);
+// Compute units of the current device (cached per device; 256 if unknown).
+int cu_count();
 
 inline bool overlaps(const void *a, size_t an, const void *b, size_t bn)
 {

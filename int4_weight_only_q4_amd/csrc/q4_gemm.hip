@@ -41,6 +41,7 @@ constexpr int kBN = 128;               // weight rows per workgroup (32 per wave
 constexpr int kStepK = 128;            // K values per step (four groups)
 constexpr int kAStride = kStepK + 8;   // staged row in halves (16 bytes of padding)
 constexpr int kXcds = 8;
+constexpr int kMaxSplits = 16;   // K splits of one launch
 
 __device__ __forceinline__ void swap16(uint32_t &a, uint32_t &b)
 {
@@ -119,48 +120,61 @@ __device__ __forceinline__ u32x4 pair_order(u32x4 v)
                  __builtin_amdgcn_perm(v.w, v.y, 0x07060302u)};
 }
 
-// One step's global loads of a thread: its lane's word group of the wave's
-// two weight rows and their scales, and MS 16-byte pieces of the activation tile.
+// The buffers of one launch (sizes in bytes; an offset past the size reads 0).
+struct Bufs {
+    __amdgpu_buffer_rsrc_t w, s, x;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+constexpr uint32_t kOut = 0x80000000u;  // an offset beyond every buffer: loads return 0
+
+// A thread's byte offsets at step 0, the same at every step but for the
+// step's own scalar offset: its lane's word group and scale of the wave's two
+// weight rows, and MS 16-byte pieces of the activation tile (piece q: row
+// (t + 256 q) / 16, eight values (t % 16) of the step). Rows past N or M read 0.
+template <int MS>
+struct Offsets {
+    uint32_t w[2], s[2], x[MS];
+};
+
+// One step's loaded data of a thread.
 template <int MS>
 struct StepLoads {
-    uint4 w[2];
+    u32x4 w[2];
     uint32_t s[2];
     u32x4 x[MS];
 };
 
 template <int MS>
-__device__ __forceinline__ void load_step(StepLoads<MS> &L, const uint4 *__restrict__ W,
-                                          const uint16_t *__restrict__ S,
-                                          const uint16_t *__restrict__ X, int64_t ldx,
-                                          const size_t (&wrow)[2], int m0, int M, int G, int gs,
-                                          int kb, int t)
+__device__ __forceinline__ void load_step(StepLoads<MS> &L, const Bufs &B, const Offsets<MS> &O,
+                                          int st)
 {
-    const int gi = min(gs + kb, G - 1);
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns) {
-        L.w[ns] = load_weights(W + wrow[ns] + gi);
-        L.s[ns] = load_scale(S + wrow[ns] + gi);
+        L.w[ns] = __builtin_amdgcn_raw_buffer_load_b128(B.w, O.w[ns], st * 64, 0);
+        L.s[ns] = __builtin_amdgcn_raw_buffer_load_b16(B.s, O.s[ns], st * 8, 0);
     }
 #pragma unroll
-    for (int q = 0; q < MS; ++q) {
-        const int c = t + 256 * q;  // piece c: row c / 16, eight values c % 16 of the step
-        const int mr = min(m0 + (c >> 4), M - 1);
-        const int kk = min(gs * 32 + 8 * (c & 15), G * 32 - 8);
-        L.x[q] = *reinterpret_cast<const u32x4 *>(X + (int64_t)mr * ldx + kk);
-    }
+    for (int q = 0; q < MS; ++q)
+        L.x[q] = __builtin_amdgcn_raw_buffer_load_b128(B.x, O.x[q], st * 256, 0);
 }
 
 // Weight words and scales of a step, rearranged for the matrix core:
 // wt[ns][tt] is this lane row's word of group tt, s2[ns][tt] that group's
-// scale (both halves).
+// scale (both halves). LAST: groups past K get scale 0.
 struct StepWeights {
     uint32_t wt[2][4];
     half2v s2[2][4];
 };
 
-template <int MS>
-__device__ __forceinline__ void prepare(StepWeights &P, const StepLoads<MS> &L, bool tail,
-                                        int gs, int kb, int G)
+template <int MS, bool LAST>
+__device__ __forceinline__ void prepare(StepWeights &P, const StepLoads<MS> &L, int gs, int kb,
+                                        int G)
 {
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns) {
@@ -170,8 +184,8 @@ __device__ __forceinline__ void prepare(StepWeights &P, const StepLoads<MS> &L, 
         P.wt[ns][3] = L.w[ns].w;
         transpose_rows(P.wt[ns]);
         uint32_t s = L.s[ns];
-        if (tail && gs + kb >= G)
-            s = 0;  // a group past K gets scale 0
+        if (LAST && gs + kb >= G)
+            s = 0;
         uint32_t sc[4];
         broadcast_rows(s, sc);
 #pragma unroll
@@ -180,31 +194,62 @@ __device__ __forceinline__ void prepare(StepWeights &P, const StepLoads<MS> &L, 
     }
 }
 
-// Stores a step's activation pieces into an LDS buffer (pair order; values
-// past K zero in the tail step).
-template <int MS>
-__device__ __forceinline__ void stage(_Float16 *buf, const StepLoads<MS> &L, bool tail, int gs,
-                                      int G, int t)
+// Stores a step's activation pieces into an LDS buffer in pair order. LAST:
+// values past K are zero.
+template <int MS, bool LAST>
+__device__ __forceinline__ void stage(_Float16 *buf, const StepLoads<MS> &L, int gs, int G, int t)
 {
 #pragma unroll
     for (int q = 0; q < MS; ++q) {
         const int c = t + 256 * q;
         u32x4 v = pair_order(L.x[q]);
-        if (tail && gs * 32 + 8 * (c & 15) >= G * 32)
+        if (LAST && gs * 32 + 8 * (c & 15) >= G * 32)
             v = u32x4{0u, 0u, 0u, 0u};
         *reinterpret_cast<u32x4 *>(buf + (c >> 4) * kAStride + 8 * (c & 15)) = v;
     }
 }
 
+template <int MS, bool EXACT>
+__device__ __forceinline__ void multiply(floatx4 (&acc)[MS][2], const _Float16 *cur,
+                                         const StepWeights &P, int n, int kb)
+{
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        half8 a[MS], bh[2], bl[2];
+        __builtin_amdgcn_iglp_opt(1);  // interleave the matrix-core and LDS work
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms)
+            a[ms] = *reinterpret_cast<const half8 *>(cur + (16 * ms + n) * kAStride + 8 * kb +
+                                                     32 * tt);
+#pragma unroll
+        for (int ns = 0; ns < 2; ++ns)
+            weights_of<EXACT>(P.wt[ns][tt], P.s2[ns][tt], bh[ns], bl[ns]);
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+            for (int ns = 0; ns < 2; ++ns)
+                acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[ms], bh[ns], acc[ms][ns],
+                                                                     0, 0, 0);
+        if (EXACT) {
+#pragma unroll
+            for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                for (int ns = 0; ns < 2; ++ns)
+                    acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[ms], bl[ns],
+                                                                         acc[ms][ns], 0, 0, 0);
+        }
+    }
+}
+
 // Grid: one workgroup per (16 MS-row activation tile, 128-row weight tile),
 // 256 threads; wave w owns weight rows [32 w, 32 w + 32) of the tile and all
-// MS 16-row activation tiles.
+// MS 16-row activation tiles. Buffer sizes below 2^31 bytes (the launcher
+// splits larger problems).
 template <int MS, bool EXACT>
-__global__ __launch_bounds__(256, 2) void k_gemm_q4(const uint4 *__restrict__ W,
-                                                    const uint16_t *__restrict__ S,
-                                                    const uint16_t *__restrict__ X, int64_t ldx,
-                                                    uint16_t *__restrict__ Y, int64_t ldy, int M,
-                                                    int N, int G)
+__global__ __launch_bounds__(256, MS == 8 ? 2 : 3) void k_gemm_q4(
+    const uint4 *__restrict__ W, const uint16_t *__restrict__ S, const uint16_t *__restrict__ X,
+    int64_t ldx, uint16_t *__restrict__ Y, int64_t ldy, float *__restrict__ part, int M, int N,
+    int G, int sps)
 {
     constexpr int BM = 16 * MS;
     __shared__ _Float16 xs[2][BM * kAStride];
@@ -219,10 +264,23 @@ __global__ __launch_bounds__(256, 2) void k_gemm_q4(const uint4 *__restrict__ W,
     const int r = x * per + min(x, rem) + b / kXcds;
     const int m0 = (r % mtiles) * BM, n0 = (r / mtiles) * kBN + 32 * wave;
 
-    size_t wrow[2];
+    Bufs B;
+    B.w = rsrc(W, (uint32_t)N * (uint32_t)G * 16u);
+    B.s = rsrc(S, (uint32_t)N * (uint32_t)G * 2u);
+    B.x = rsrc(X, (uint32_t)(((int64_t)(M - 1) * ldx + G * 32) * 2));
+    Offsets<MS> O;
 #pragma unroll
-    for (int ns = 0; ns < 2; ++ns)
-        wrow[ns] = (size_t)min(n0 + 16 * ns + n, N - 1) * G;
+    for (int ns = 0; ns < 2; ++ns) {
+        const int row = n0 + 16 * ns + n;
+        O.w[ns] = row < N ? (uint32_t)(row * G + kb) * 16u : kOut;
+        O.s[ns] = row < N ? (uint32_t)(row * G + kb) * 2u : kOut;
+    }
+#pragma unroll
+    for (int q = 0; q < MS; ++q) {
+        const int c = t + 256 * q, row = m0 + (c >> 4);
+        O.x[q] = row < M ? (uint32_t)((row * ldx + 8 * (c & 15)) * 2) : kOut;
+    }
+
     floatx4 acc[MS][2];
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms)
@@ -230,53 +288,31 @@ __global__ __launch_bounds__(256, 2) void k_gemm_q4(const uint4 *__restrict__ W,
         for (int ns = 0; ns < 2; ++ns)
             acc[ms][ns] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    const int steps = (G + 3) / 4;
+    // step st: groups [4 st, 4 st + 4); its loads are issued one step ahead.
+    // K split z (grid y) takes the steps [z sps, min((z + 1) sps, steps)).
+    const int steps = (G + 3) / 4, z = blockIdx.y;
+    const int st0 = z * sps, st1 = min(steps, st0 + sps);
     StepLoads<MS> L;
     StepWeights P;
-    load_step<MS>(L, W, S, X, ldx, wrow, m0, M, G, 0, kb, t);
-    stage<MS>(xs[0], L, G < 4, 0, G, t);
-    prepare<MS>(P, L, G < 4, 0, kb, G);
-    load_step<MS>(L, W, S, X, ldx, wrow, m0, M, G, min(4, 4 * (steps - 1)), kb, t);
-    __syncthreads();
-    for (int st = 0; st < steps; ++st) {
-        const _Float16 *cur = xs[st & 1];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            half8 a[MS], bh[2], bl[2];
-#pragma unroll
-            for (int ms = 0; ms < MS; ++ms)
-                a[ms] = *reinterpret_cast<const half8 *>(cur + (16 * ms + n) * kAStride + 8 * kb +
-                                                         32 * tt);
-#pragma unroll
-            for (int ns = 0; ns < 2; ++ns)
-                weights_of<EXACT>(P.wt[ns][tt], P.s2[ns][tt], bh[ns], bl[ns]);
-#pragma unroll
-            for (int ms = 0; ms < MS; ++ms)
-#pragma unroll
-                for (int ns = 0; ns < 2; ++ns)
-                    acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[ms], bh[ns],
-                                                                         acc[ms][ns], 0, 0, 0);
-            if (EXACT) {
-#pragma unroll
-                for (int ms = 0; ms < MS; ++ms)
-#pragma unroll
-                    for (int ns = 0; ns < 2; ++ns)
-                        acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            a[ms], bl[ns], acc[ms][ns], 0, 0, 0);
-            }
-        }
-        // the next step: its activation tile into the other buffer (last read
-        // before the previous barrier), its weights rearranged, and the loads
-        // of the step after it (the last steps re-read the final one, unused)
-        const int gn = 4 * min(st + 1, steps - 1);
-        const bool tail = gn + 4 > G;
-        stage<MS>(xs[(st + 1) & 1], L, tail, gn, G, t);
-        prepare<MS>(P, L, tail, gn, kb, G);
-        load_step<MS>(L, W, S, X, ldx, wrow, m0, M, G, 4 * min(st + 2, steps - 1), kb, t);
+    load_step<MS>(L, B, O, st0);
+    for (int st = st0; st < st1 - 1; ++st) {
+        stage<MS, false>(xs[st & 1], L, 4 * st, G, t);
+        prepare<MS, false>(P, L, 4 * st, kb, G);
+        load_step<MS>(L, B, O, st + 1);
+        __syncthreads();  // the tile is staged; the other buffer was last read before this
+        multiply<MS, EXACT>(acc, xs[st & 1], P, n, kb);
+    }
+    {
+        const int st = st1 - 1;  // groups past K only in the last step of the last split
+        stage<MS, true>(xs[st & 1], L, 4 * st, G, t);
+        prepare<MS, true>(P, L, 4 * st, kb, G);
         __syncthreads();
+        multiply<MS, EXACT>(acc, xs[st & 1], P, n, kb);
     }
 
-    // lane (n, kb) holds D[4 kb + i][n] of each (activation, weight) tile
+    // lane (n, kb) holds D[4 kb + i][n] of each (activation, weight) tile:
+    // rounded to Y, or with several K splits the f32 partial part[z][row][col]
+    const bool split = gridDim.y > 1;
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
@@ -285,10 +321,96 @@ __global__ __launch_bounds__(256, 2) void k_gemm_q4(const uint4 *__restrict__ W,
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = m0 + 16 * ms + 4 * kb + i;
-                if (row < M && col < N)
-                    Y[(int64_t)row * ldy + col] = f2h(acc[ms][ns][i]);
+                if (row < M && col < N) {
+                    if (split)
+                        part[((size_t)z * M + row) * N + col] = acc[ms][ns][i];
+                    else
+                        Y[(int64_t)row * ldy + col] = f2h(acc[ms][ns][i]);
+                }
             }
         }
+}
+
+// Y[m][n] = f16(sum over z, in order, of part[z][m][n]); thread i takes the
+// V consecutive outputs from V i (V = 4: N % 4 == 0 and Y rows 8-byte aligned).
+template <int V>
+__global__ __launch_bounds__(256) void k_gemm_combine(const float *__restrict__ part, int KS,
+                                                      int M, int N, uint16_t *__restrict__ Y,
+                                                      int64_t ldy)
+{
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * V;
+    const int64_t plane = (int64_t)M * N;
+    if (i >= plane)
+        return;
+    const int row = (int)(i / N), col = (int)(i % N);
+    if (V == 4) {
+        float4 v[kMaxSplits];
+#pragma unroll
+        for (int z = 0; z < kMaxSplits; ++z)
+            if (z < KS)
+                v[z] = *reinterpret_cast<const float4 *>(part + z * plane + i);
+        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int z = 0; z < kMaxSplits; ++z)
+            if (z < KS) {
+                s.x += v[z].x;
+                s.y += v[z].y;
+                s.z += v[z].z;
+                s.w += v[z].w;
+            }
+        const uint32_t lo = f2h(s.x) | (uint32_t)f2h(s.y) << 16;
+        const uint32_t hi = f2h(s.z) | (uint32_t)f2h(s.w) << 16;
+        *reinterpret_cast<uint2 *>(Y + (int64_t)row * ldy + col) = make_uint2(lo, hi);
+    } else {
+        float s = 0.f;
+        for (int z = 0; z < KS; ++z)
+            s += part[z * plane + i];
+        Y[(int64_t)row * ldy + col] = f2h(s);
+    }
+}
+
+// Launch shape of one chunk: activation rows per workgroup (16 MS) and the
+// number of K splits. 128-row tiles run two workgroups per CU, 64-row tiles
+// three at about 0.74 of the time per tile; the shape with fewer estimated
+// tile-rounds wins. A grid that fills fewer than half the workgroup slots
+// splits K (at least four steps per split, at most kMaxSplits) into f32
+// partials that k_gemm_combine sums in split order.
+struct GemmShape {
+    int ms, splits, sps;
+};
+
+GemmShape gemm_shape(int M, int N, int G, size_t max_part_bytes)
+{
+    const int cus = cu_count(), nt = (N + kBN - 1) / kBN, steps = (G + 3) / 4;
+    const int64_t t8 = (int64_t)((M + 127) / 128) * nt, t4 = (int64_t)((M + 63) / 64) * nt;
+    const double r8 = (double)((t8 + 2 * cus - 1) / (2 * cus));
+    const double r4 = 0.74 * (double)((t4 + 3 * cus - 1) / (3 * cus));
+    GemmShape g;
+    g.ms = r4 < r8 ? 4 : 8;
+    const int64_t tiles = g.ms == 4 ? t4 : t8, slots = (g.ms == 4 ? 3 : 2) * (int64_t)cus;
+    int ks = 1;
+    if (2 * tiles <= slots) {
+        ks = (int)std::min<int64_t>({(slots + tiles - 1) / tiles, std::max(1, steps / 4), kMaxSplits});
+        while (ks > 1 && (size_t)ks * M * N * sizeof(float) > max_part_bytes)
+            --ks;
+    }
+    g.sps = (steps + ks - 1) / ks;
+    g.splits = (steps + g.sps - 1) / g.sps;  // every split has at least one step
+    return g;
+}
+
+template <int MS>
+q4_status launch_tiles(bool exact, dim3 grid, hipStream_t stream, const uint4 *w, const uint16_t *s,
+                       const uint16_t *x, int64_t ldx, uint16_t *y, int64_t ldy, float *part,
+                       int M, int N, int G, int sps)
+{
+    if (exact)
+        Q4_LAUNCH_MATVEC((k_gemm_q4<MS, true>), grid, dim3(256), 0, stream, w, s, x, ldx, y, ldy,
+                         part, M, N, G, sps);
+    else
+        Q4_LAUNCH_MATVEC((k_gemm_q4<MS, false>), grid, dim3(256), 0, stream, w, s, x, ldx, y,
+                         ldy, part, M, N, G, sps);
+    return check_launch("k_gemm_q4");
 }
 
 }  // namespace
@@ -297,15 +419,54 @@ q4_status launch_gemm(const uint32_t *W, const uint16_t *S, const uint16_t *X, i
                       uint16_t *Y, int64_t ldy, int N, int K, int M, bool exact,
                       hipStream_t stream)
 {
-    constexpr int MS = 8;
-    const int64_t tiles = (int64_t)((M + 16 * MS - 1) / (16 * MS)) * ((N + kBN - 1) / kBN);
-    if (exact)
-        Q4_LAUNCH_MATVEC((k_gemm_q4<MS, true>), dim3((unsigned)tiles), dim3(256), 0, stream,
-                         reinterpret_cast<const uint4 *>(W), S, X, ldx, Y, ldy, M, N, K / 32);
-    else
-        Q4_LAUNCH_MATVEC((k_gemm_q4<MS, false>), dim3((unsigned)tiles), dim3(256), 0, stream,
-                         reinterpret_cast<const uint4 *>(W), S, X, ldx, Y, ldy, M, N, K / 32);
-    return check_launch("k_gemm_q4");
+    constexpr size_t kMaxPart = size_t(256) << 20;  // f32 partials of a split launch
+    const int G = K / 32;
+    // every buffer of a launch under 2^31 bytes: chunks of weight rows (whole
+    // 128-row tiles) and of activation rows (whole 128-row tiles)
+    const int64_t wrow_bytes = (int64_t)G * 16;
+    const int nchunk = (int)std::max<int64_t>(kBN, ((int64_t(1) << 31) / wrow_bytes) / kBN * kBN);
+    const int mchunk = (int)std::max<int64_t>(
+        128, ((int64_t(1) << 31) / (2 * std::max<int64_t>(ldx, 1)) - 1) / 128 * 128);
+    for (int n0 = 0; n0 < N; n0 += nchunk)
+        for (int m0 = 0; m0 < M; m0 += mchunk) {
+            const int nn = std::min(nchunk, N - n0), mm = std::min(mchunk, M - m0);
+            const GemmShape g = gemm_shape(mm, nn, G, kMaxPart);
+            const int BM = 16 * g.ms;
+            const int64_t tiles = (int64_t)((mm + BM - 1) / BM) * ((nn + kBN - 1) / kBN);
+            const dim3 grid((unsigned)tiles, (unsigned)g.splits);
+            float *part = nullptr;
+            if (g.splits > 1) {
+                char *ws = static_cast<char *>(
+                    workspace(stream, kWsHeader + (size_t)g.splits * mm * nn * sizeof(float)));
+                if (!ws)
+                    return Q4_EHIP;
+                part = reinterpret_cast<float *>(ws + kWsHeader);
+            }
+            const uint4 *w = reinterpret_cast<const uint4 *>(W) + (size_t)n0 * G;
+            const uint16_t *s = S + (size_t)n0 * G, *x = X + (size_t)m0 * ldx;
+            uint16_t *y = Y + (size_t)m0 * ldy + n0;
+            q4_status st = g.ms == 4
+                               ? launch_tiles<4>(exact, grid, stream, w, s, x, ldx, y, ldy, part,
+                                                 mm, nn, G, g.sps)
+                               : launch_tiles<8>(exact, grid, stream, w, s, x, ldx, y, ldy, part,
+                                                 mm, nn, G, g.sps);
+            if (st != Q4_OK)
+                return st;
+            if (g.splits > 1) {
+                const int64_t total = (int64_t)mm * nn;
+                const bool vec = nn % 4 == 0 && ldy % 4 == 0 &&
+                                 reinterpret_cast<uintptr_t>(y) % 8 == 0;
+                if (vec)
+                    hipLaunchKernelGGL(k_gemm_combine<4>, dim3((unsigned)((total / 4 + 255) / 256)),
+                                       dim3(256), 0, stream, part, g.splits, mm, nn, y, ldy);
+                else
+                    hipLaunchKernelGGL(k_gemm_combine<1>, dim3((unsigned)((total + 255) / 256)),
+                                       dim3(256), 0, stream, part, g.splits, mm, nn, y, ldy);
+                if ((st = check_launch("k_gemm_combine")) != Q4_OK)
+                    return st;
+            }
+        }
+    return Q4_OK;
 }
 
 }  // namespace q4

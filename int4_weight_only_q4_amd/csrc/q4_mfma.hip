@@ -525,21 +525,6 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ part,
         y[mr * ldy + col] = f2h(s);
 }
 
-int cus()
-{
-    static int n[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        return 256;
-    if (!n[dev]) {
-        int c = 0;
-        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            c <= 0)
-            c = 256;
-        n[dev] = c;
-    }
-    return n[dev];
-}
 
 }  // namespace
 
@@ -566,7 +551,7 @@ q4_status launch_mfma_rows(const uint32_t *W, const uint16_t *S, const uint16_t 
     // about three resident workgroups per CU, each looping over its tiles (at
     // most kMaxTilesPerWave per wave)
     const int P = std::max({1, (ntiles + kWaves * kMaxTilesPerWave - 1) / (kWaves * kMaxTilesPerWave),
-                            std::min((ntiles + kWaves - 1) / kWaves, (3 * cus() + KS - 1) / KS)});
+                            std::min((ntiles + kWaves - 1) / kWaves, (3 * cu_count() + KS - 1) / KS)});
     const size_t lds = (size_t)mt * (gc * 32 + 8) * 2 +          // staged rows
                        (bias ? (size_t)gc * 16 * sizeof(float) : 0);  // affine: group sums
     if (bias)

@@ -8,10 +8,12 @@ bar of the exact result. Bit-exact cases:
   (f16 mode) for every weight row, with scales small enough that the low half
   of the exact split is a binary16 subnormal;
 * every output row is independent of M and of the row's position in the batch
-  (the same bits computed alone and inside a batch of 300).
-Shapes: ragged small cases that the oracle computes whole (tiles of 64 x 128,
-steps of 128 values of K, a last step of one group), and the prefill shapes of
-Phi-3-mini (M = 1024) and Qwen3-4B (M = 256) checked on sampled outputs.
+  (the same bits computed alone and inside a batch of 300) while the launch
+  splits K the same way (here: two splits at every M).
+Shapes: ragged small cases that the oracle computes whole (tiles of 64 or 128
+x 128, steps of 128 values of K, a last step of one group, K split in 2 and 7
+parts with a partial last step), and the prefill shapes of Phi-3-mini
+(M = 1024) and Qwen3-4B (M = 256, K split) checked on sampled outputs.
 """
 import zlib
 
@@ -68,7 +70,8 @@ def run(q4, W, S, X, mode, ldx=None, ldy=None):
 
 SMALL = [("tiny", 1, 1, 32), ("one_step_short", 17, 200, 96), ("one_tile", 64, 128, 256),
          ("ragged", 65, 129, 160), ("ragged_tail_group", 130, 300, 544),
-         ("square", 256, 256, 1024), ("tall", 1000, 40, 128)]
+         ("square", 256, 256, 1024), ("tall", 1000, 40, 128),
+         ("split_tail", 100, 200, 1184), ("many_splits", 64, 128, 4160)]
 
 
 @pytest.mark.parametrize("mode", [EXACT, F16W], ids=["exact", "f16w"])
