@@ -175,7 +175,7 @@ def summarize_counters(fetch_dir, write_dir):
         # the calibration copy is the largest copy dispatch of the run (weight
         # uploads before it are smaller)
         copy = sorted(v for k, _, v in rows if "copy" in k.lower())[-3:]
-        dom = [v for k, _, v in rows if "k_gemv<32, 3, 2, 1, 1>" in k]
+        dom = [v for k, _, v in rows if "k_gemv<32, 3, 2, 1, 1," in k]
         if not copy or not dom:
             raise SystemExit("%s: missing copy (%d) or dominant-kernel (%d) dispatches" % (
                 cname, len(copy), len(dom)))
@@ -186,7 +186,7 @@ def summarize_counters(fetch_dir, write_dir):
     traffic = 1024.0 * (res["FETCH_SIZE"]["dominant_kib"] * res["FETCH_SIZE"]["factor"] +
                         res["WRITE_SIZE"]["dominant_kib"] * res["WRITE_SIZE"]["factor"])
     algo = 2 * PHI3["f"] * PHI3["d"] * BPW
-    rec = dict(kernel="gate_up 16384x3072 matvec (k_gemv<32, 3, 2, 1, 1>)",
+    rec = dict(kernel="gate_up 16384x3072 matvec (k_gemv<32, 3, 2, 1, 1, false>)",
                source_hash=kernel_source_hash(), traffic_bytes_per_launch=int(traffic),
                algorithmic_bytes_per_launch=int(algo), ratio=round(traffic / algo, 4), **res)
     cmd = ("export REPO=$PWD && cd /tmp && export TMPDIR=/tmp && timeout -s KILL 150 "
