@@ -206,7 +206,8 @@ __device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast
 // kernel, so fused and unfused paths give identical bits.
 __device__ __forceinline__ float silu_mul_f(float g, float u)
 {
-    float s = g / (1.0f + __expf(-g));
+    // g * sigma(g) with the hardware reciprocal (v_rcp_f32, within 1 ulp)
+    float s = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
     return s * u;
 }
 
@@ -216,13 +217,90 @@ __device__ __forceinline__ float silu_mul_f(float g, float u)
 // that normalises (standalone or as a matvec prologue) follows it, so their
 // results are bit-identical.
 
-// Block-wide sum over 256 threads in a fixed order: xor-butterfly inside each
+// Cross-lane sums without the LDS crossbar (ds_bpermute, which a shuffle
+// becomes): DPP moves inside each 16-lane row, permlane swaps across rows.
+// dpp<CTRL>(v): v of another lane of the row (CTRL: 0xB1 lane i ^ 1, 0x4E
+// lane i ^ 2, 0x141 lane 7 - i within each 8, 0x128 lane i ^ 8).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Cross-row exchanges of a wave (rows = lanes 16r .. 16r + 15): swap16
+// exchanges row 1 of a with row 0 of b and row 3 of a with row 2 of b; swap32
+// exchanges rows 2, 3 of a with rows 0, 1 of b. Written as inline assembly:
+// this compiler has generated code that reads one output of the permlane-swap
+// builtins twice and the other not at all. The s_nop give the wait states
+// between a VALU write and the swap's read, and between the swap and a read of
+// its results, which the compiler cannot insert around inline assembly.
+__device__ __forceinline__ void swap16(uint32_t &a, uint32_t &b)
+{
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 0" : "+v"(a), "+v"(b));
+}
+
+__device__ __forceinline__ void swap32(uint32_t &a, uint32_t &b)
+{
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 0" : "+v"(a), "+v"(b));
+}
+
+// v(lane) + v(lane ^ 16), the same bits in both lanes of a pair
+__device__ __forceinline__ float add_xor16(float v)
+{
+    uint32_t a = __builtin_bit_cast(uint32_t, v), b = a;
+    swap16(a, b);
+    return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+
+// v(lane) + v(lane ^ 32), the same bits in both lanes of a pair
+__device__ __forceinline__ float add_xor32(float v)
+{
+    uint32_t a = __builtin_bit_cast(uint32_t, v), b = a;
+    swap32(a, b);
+    return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+
+// Sum over each aligned segment of w lanes (w = 8, 16, 32 or 64), in one fixed
+// order; every lane of a segment ends with the same bits. The runtime-w form
+// performs the same steps.
+__device__ __forceinline__ float segment_sum(float v, int w)
+{
+    if (w >= 64)
+        v = add_xor32(v);
+    if (w >= 32)
+        v = add_xor16(v);
+    if (w >= 16)
+        v += dpp<0x128>(v);
+    v += dpp<0x141>(v);
+    v += dpp<0x4E>(v);
+    v += dpp<0xB1>(v);
+    return v;
+}
+
+// Sum over the four lanes of each aligned quad (partners i ^ 1, then i ^ 2).
+__device__ __forceinline__ float quad_sum(float v)
+{
+    v += dpp<0xB1>(v);
+    v += dpp<0x4E>(v);
+    return v;
+}
+
+// 1 / sqrt(mean + eps) of an RMSNorm from its sum of squares over D values:
+// the hardware reciprocal and reciprocal square root (v_rcp_f32, v_rsq_f32,
+// each within 1 ulp) as rsq(ss * rcp(D) + eps), no IEEE division. One
+// definition for every kernel that normalises, so their results agree bit
+// for bit.
+__device__ __forceinline__ float rms_inv(float ss, int D, float eps)
+{
+    return __builtin_amdgcn_rsqf(fmaf(ss, __builtin_amdgcn_rcpf((float)D), eps));
+}
+
+// Block-wide sum over 256 threads in a fixed order: segment_sum over each
 // wave, then the four wave totals added in wave order. `red` is 4 floats of LDS.
 __device__ __forceinline__ float block_sum_256(float v, float *red)
 {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
-        v += __shfl_xor(v, off, 64);
+    v = segment_sum(v, 64);
     const int wave = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0)
         red[wave] = v;

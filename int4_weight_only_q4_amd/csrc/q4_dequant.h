@@ -109,8 +109,7 @@ __device__ __forceinline__ void stage_activation(const uint16_t *__restrict__ x,
             sum = ((h2f(v.x & 0xFFFF) + h2f(v.x >> 16)) + (h2f(v.y & 0xFFFF) + h2f(v.y >> 16))) +
                   ((h2f(v.z & 0xFFFF) + h2f(v.z >> 16)) + (h2f(v.w & 0xFFFF) + h2f(v.w >> 16)));
         }
-        sum += __shfl_xor(sum, 1, 64);
-        sum += __shfl_xor(sum, 2, 64);
+        sum = quad_sum(sum);
         if (c < chunks && (c & 3) == 0)
             cs[c >> 2] = sum;
     }
@@ -141,8 +140,7 @@ __device__ __forceinline__ void put_chunk(uint4 v, int c, bool valid, uint4 *xs,
         sum = ((h2f(v.x & 0xFFFF) + h2f(v.x >> 16)) + (h2f(v.y & 0xFFFF) + h2f(v.y >> 16))) +
               ((h2f(v.z & 0xFFFF) + h2f(v.z >> 16)) + (h2f(v.w & 0xFFFF) + h2f(v.w >> 16)));
     }
-    sum += __shfl_xor(sum, 1, 64);
-    sum += __shfl_xor(sum, 2, 64);
+    sum = quad_sum(sum);
     if (valid && (c & 3) == 0)
         cs[c >> 2] = sum;
 }

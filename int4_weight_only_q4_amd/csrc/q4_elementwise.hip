@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm(const uint16_t *__restrict_
             }
         }
     ss = block_sum_256(ss, red);
-    const float inv = 1.0f / sqrtf(ss / (float)D + eps);
+    const float inv = rms_inv(ss, D, eps);
     for (int c = threadIdx.x; c * 8 < D; c += 256)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {

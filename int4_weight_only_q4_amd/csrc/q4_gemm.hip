@@ -43,20 +43,6 @@ constexpr int kAStride = kStepK + 8;   // staged row in halves (16 bytes of padd
 constexpr int kXcds = 8;
 constexpr int kMaxSplits = 16;   // K splits of one launch
 
-__device__ __forceinline__ void swap16(uint32_t &a, uint32_t &b)
-{
-    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
-    a = r[0];
-    b = r[1];
-}
-
-__device__ __forceinline__ void swap32(uint32_t &a, uint32_t &b)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
-    a = r[0];
-    b = r[1];
-}
-
 // 4 x 4 transpose over (lane row, register): afterwards r[t] in lane row q
 // holds what r[q] held in lane row t.
 __device__ __forceinline__ void transpose_rows(uint32_t (&r)[4])

@@ -18,8 +18,8 @@
 //    exact subnormal binary16 pairs for v_dot2_f32_f16 (1 shift + 4 ANDs +
 //    4 dot2 per word), and the group's sum of (c - 7) x is applied with its
 //    scale in f32. A one-hot x therefore reproduces (c - 7) * s exactly.
-//  * The LPR partial sums of a row are combined with an xor butterfly in a
-//    fixed order, so results are identical run to run.
+//  * The LPR partial sums of a row are combined in a fixed order by DPP and
+//    permlane steps (no LDS round trips), so results are identical run to run.
 #include "q4_dequant.h"
 #include "q4_stack.h"
 
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams a)
                     ss = fmaf(f[e], f[e], ss);
             }
         ss = block_sum_256(ss, red);
-        const float inv = 1.0f / sqrtf(ss / (float)K + a.pro_eps);
+        const float inv = rms_inv(ss, K, a.pro_eps);
 #pragma unroll
         for (int q = 0; q < XCH; ++q)
             if (tid + 256 * q < chunks) {
@@ -199,9 +199,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams a)
     // 4. combine the LPR lanes of each row
 #pragma unroll
     for (int r = 0; r < RPS; ++r)
-#pragma unroll
-        for (int off = LPR / 2; off > 0; off >>= 1)
-            acc[r] += __shfl_xor(acc[r], off, 64);
+        acc[r] = segment_sum(acc[r], LPR);
 
     // 5. epilogue
     if (EPI == EPI_NONE_) {

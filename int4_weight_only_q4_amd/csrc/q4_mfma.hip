@@ -72,23 +72,6 @@ __device__ __forceinline__ half8 codes_minus7(uint32_t w, uint32_t mask)
     return out;
 }
 
-// Cross-row exchanges of a wave (rows = lanes 16r .. 16r + 15): permlane16
-// swaps row 1 of a with row 0 of b and row 3 of a with row 2 of b; permlane32
-// swaps rows 2, 3 of a with rows 0, 1 of b.
-__device__ __forceinline__ void swap16(uint32_t &a, uint32_t &b)
-{
-    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
-    a = r[0];
-    b = r[1];
-}
-
-__device__ __forceinline__ void swap32(uint32_t &a, uint32_t &b)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
-    a = r[0];
-    b = r[1];
-}
-
 // 4 x 4 transpose over (lane row, register): afterwards r[t] in row q holds
 // what r[q] held in row t.
 __device__ __forceinline__ void transpose_rows(uint32_t (&r)[4])
@@ -257,8 +240,7 @@ __device__ __forceinline__ void mfma_rows(const uint4 *__restrict__ W,
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 sm = (sm + h2f((uint16_t)(u[e] & 0xFFFF))) + h2f((uint16_t)(u[e] >> 16));
-            sm += __shfl_xor(sm, 1, 64);
-            sm += __shfl_xor(sm, 2, 64);
+            sm = quad_sum(sm);
             if ((jj & 3) == 0 && t + 256 * q < M * cpr)
                 xsum[(jj >> 2) * 16 + mm] = sm;
         }

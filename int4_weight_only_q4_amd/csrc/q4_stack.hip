@@ -186,9 +186,7 @@ __device__ __forceinline__ float reduce_row(const PhaseMap &m, int v, int j, con
                 acc = fmaf(e.x, e.y, acc);
             }
         }
-    for (int off = m.lpr >> 1; off > 0; off >>= 1)
-        acc += __shfl_xor(acc, off, 64);
-    return acc;
+    return segment_sum(acc, m.lpr);
 }
 
 __device__ __forceinline__ bool chunk_ready(const uint64_t (&q)[4], uint32_t tag)
@@ -314,9 +312,7 @@ __device__ __forceinline__ void norm_sum(const uint32_t *tagged, uint32_t tag,
         for (int e = 0; e < 8; ++e)
             ss = fmaf(f[e], f[e], ss);
     });
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
-        ss += __shfl_xor(ss, off, 64);
+    ss = segment_sum(ss, 64);
     if ((threadIdx.x & 63) == 0)
         l.red[s >> 6] = ss;
 }
@@ -327,7 +323,7 @@ __device__ __forceinline__ void norm_apply(const uint16_t *gamma, float eps, int
     const int chunks = K >> 3;
     const int s = threadIdx.x - kCompute;
     const float tot = ((l.red[0] + l.red[1]) + l.red[2]) + l.red[3];
-    const float inv = 1.0f / sqrtf(tot / (float)K + eps);
+    const float inv = rms_inv(tot, K, eps);
     for (int base = 0; base < chunks; base += kStagers) {
         const int c = base + s;
         uint4 hv = make_uint4(0, 0, 0, 0);
