@@ -590,12 +590,34 @@ def prefill_table(q4, torch):
             workload, "%s %dx%d" % (name, n, k), m, call_us, tf), file=sys.stderr, flush=True)
         del rot, wd, xd
         torch.cuda.empty_cache()
+
+    # the MLX affine format (w = s * q + b, group 64) at the chunk shapes of the
+    # pages' GEMM microbench (qwen3mlx, M = 256)
+    for j, (name, n, k) in enumerate([("gate_up", 19456, 2560), ("down", 2560, 9728),
+                                      ("o", 2560, 4096)]):
+        m = 256
+        Wh = torch.from_numpy(datagen.words(base + 700 + 10 * j, n, k).view(np.int32)).cuda()
+        Sh = torch.from_numpy(datagen.scales(base + 701 + 10 * j, n, k // 2)).cuda()
+        Bh = torch.from_numpy(datagen.normal_f16(base + 702 + 10 * j, (n, k // 64), 0.0,
+                                                 0.05)).cuda()
+        copies = max(2, -(-(512 << 20) // int(n * k * BPW)))
+        rot = [(Wh, Sh, Bh)] + [(Wh.clone(), Sh.clone(), Bh.clone()) for _ in range(copies - 1)]
+        x = torch.from_numpy(datagen.activations(base + 703 + 10 * j, m, k)).cuda()
+        y = torch.empty((m, n), dtype=torch.float16, device="cuda")
+
+        def launch(i, rot=rot, x=x, y=y):
+            W, S, B = rot[i % len(rot)]
+            q4.gemm_affine(W, S, B, x, y=y)
+        add("Qwen3-4B MLX affine prefill chunk", "%s %dx%d" % (name, n, k), m, n, k, launch,
+            "q4_gemm_affine, exact weights")
+        del rot
+        torch.cuda.empty_cache()
     return rows
 
 
 def write_prefill_table(rows):
-    text = ["# Prefill matmul (q4_gemm) on the matrix cores: Phi-3-mini M = 1024 and "
-            "Qwen3-4B M = 256",
+    text = ["# Prefill matmul (q4_gemm, q4_gemm_affine) on the matrix cores: Phi-3-mini "
+            "M = 1024, Qwen3-4B M = 256 (q4f16_1 and MLX affine)",
             "",
             "Command (from the repository root, on one MI355X): `python3 bench.py --prefill-table`",
             "",

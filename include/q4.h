@@ -223,6 +223,22 @@ q4_status q4_gemm(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64
                   q4_stream stream);
 
 /* ---------------------------------------------------------------------------
+ * q4_gemm_affine -- the prefill matmul in the MLX affine format (Zero TVM
+ * Documentation, the Qwen3.6-35B-A3B entry: w = s * q + b, group 64; BENCH.md,
+ * "Subgroup-matrix GEMM graduated" and "GEMM microbench": the _affine prefill
+ * GEMMs at the qwen3mlx chunk shapes):
+ *   y[m*ldy + n] = f16( sum_k (S[n][k/64] * q[n][k] + B[n][k/64]) * x[m*ldx + k] )
+ * W, S, B as for q4_gemv_affine (K % 64 == 0); x, y as for q4_gemm.
+ * 1 <= M <= Q4_MAX_GEMM_M. Exact weights: s * q enters the matrix cores as
+ * two binary16 terms and the bias as b * (sum of x over the group), the group
+ * sums split into binary16 hi and lo. Uses the library workspace of the
+ * stream (the group sums, and f32 partials when K is split).
+ */
+q4_status q4_gemm_affine(const uint32_t *W, const uint16_t *S, const uint16_t *B,
+                         const uint16_t *x, int64_t ldx, uint16_t *y, int64_t ldy, int64_t N,
+                         int64_t K, int64_t M, q4_stream stream);
+
+/* ---------------------------------------------------------------------------
  * LM head and greedy sampling (Zero TVM Documentation, "Decode loop": the LM
  * head's matmul writes the logits and an argmax picks the next token; shader
  * 10, "Argmax Sampler"; RESEARCH.md, "Why Fewer Dispatches Matter", the

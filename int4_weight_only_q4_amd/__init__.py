@@ -37,7 +37,7 @@ ABI_SYMBOLS = (
     "q4_stack_decode", "q4_stack_status", "q4_timer_arm", "q4_timer_read", "q4_gemv_f32",
     "q4_argmax", "q4_lm_head_argmax", "q4_kv_page_bytes", "q4_qkv_rope_append",
     "q4_rope_append", "q4_attention_decode", "q4_stack_decode_attn", "q4_gemv_affine",
-    "q4_gemm",
+    "q4_gemm", "q4_gemm_affine",
 )
 
 
@@ -84,6 +84,7 @@ _SIGS = {
     "q4_gemv": (C.c_int, [_P, _P, _P, _P, _I, _I, _P]),
     "q4_gemv_batched": (C.c_int, [_P, _P, _P, _I, _P, _I, _I, _I, _I, _P]),
     "q4_gemm": (C.c_int, [_P, _P, _P, _I, _P, _I, _I, _I, _I, C.c_int, _P]),
+    "q4_gemm_affine": (C.c_int, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _P]),
     "q4_moe_gemv": (C.c_int, [_P, _P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _I, C.c_int, _P]),
     "q4_add_rmsnorm": (C.c_int, [_P, _P, _P, _P, _P, _I, _I, C.c_float, _P]),
     "q4_silu_mul": (C.c_int, [_P, _P, _I, _I, _P]),
@@ -244,6 +245,19 @@ def gemm(W, S, x, y=None, weights=GEMM_EXACT, stream=None):
         y = torch.empty((m, n), dtype=torch.float16, device=W.device)
     _check(lib().q4_gemm(_ptr(W), _ptr(S), _ptr(x), x.stride(0), _ptr(y), y.stride(0), n, k, m,
                          int(weights), _stream(stream)))
+    return y
+
+
+def gemm_affine(W, S, B, x, y=None, stream=None):
+    """Prefill matmul in the MLX affine format: x f16 [M, ldx >= K] -> y f16 [M, N];
+    S, B f16 [N, K/64] (w = S*q + B), exact weights."""
+    import torch
+    n, k = W.shape[0], W.shape[1] * 8
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float16, device=W.device)
+    _check(lib().q4_gemm_affine(_ptr(W), _ptr(S), _ptr(B), _ptr(x), x.stride(0), _ptr(y),
+                                y.stride(0), n, k, m, _stream(stream)))
     return y
 
 

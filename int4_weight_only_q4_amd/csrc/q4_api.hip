@@ -741,17 +741,15 @@ q4_status q4_gemv_batched(const uint32_t *W, const uint16_t *S, const uint16_t *
     return launch_gemv_batched(W, S, x, ldx, y, ldy, (int)N, (int)K, (int)M, as_stream(stream));
 }
 
-q4_status q4_gemm(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
-                  uint16_t *y, int64_t ldy, int64_t N, int64_t K, int64_t M, int weights,
-                  q4_stream stream)
+namespace {
+// Shared checks of the prefill matmuls: x, y, M and the sizes of the scales
+// (sb bytes) and biases (bb bytes, 0 without).
+q4_status check_gemm_io(const uint32_t *W, const uint16_t *S, const uint16_t *B, size_t sb,
+                        size_t bb, const uint16_t *x, int64_t ldx, const uint16_t *y, int64_t ldy,
+                        int64_t N, int64_t K, int64_t M)
 {
-    q4_status st = check_matrix(W, S, N, K);
-    if (st != Q4_OK)
-        return st;
     if (!x || !y)
         return fail(Q4_EINVAL, "NULL activation or output pointer");
-    if (weights != Q4_GEMM_EXACT && weights != Q4_GEMM_F16_WEIGHT)
-        return fail(Q4_EINVAL, "unknown weights mode %d", weights);
     if (M < 1 || M > Q4_MAX_GEMM_M)
         return fail(Q4_ERANGE, "M=%lld outside [1, %d]", (long long)M, Q4_MAX_GEMM_M);
     if ((M + 63) / 64 * ((N + 127) / 128) > 0x7FFFFFFFll)
@@ -764,13 +762,46 @@ q4_status q4_gemm(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64
     if (!aligned(y, 2))
         return fail(Q4_EALIGN, "the output must be 2-byte aligned");
     const size_t yb = ((size_t)(M - 1) * ldy + N) * 2, xb = ((size_t)(M - 1) * ldx + K) * 2;
-    if (overlaps(y, yb, W, wbytes(N, K)) || overlaps(y, yb, S, sbytes(N, K)) ||
+    if (overlaps(y, yb, W, wbytes(N, K)) || overlaps(y, yb, S, sb) || overlaps(y, yb, B, bb) ||
         overlaps(y, yb, x, xb))
         return fail(Q4_EALIAS, "the output overlaps an input");
+    return Q4_OK;
+}
+}  // namespace
+
+q4_status q4_gemm_affine(const uint32_t *W, const uint16_t *S, const uint16_t *B,
+                         const uint16_t *x, int64_t ldx, uint16_t *y, int64_t ldy, int64_t N,
+                         int64_t K, int64_t M, q4_stream stream)
+{
+    q4_status st = check_matrix(W, S, N, K);
+    if (st != Q4_OK)
+        return st;
+    if (K % 64)
+        return fail(Q4_ESHAPE, "K=%lld is not a multiple of 64 (affine groups)", (long long)K);
+    if (!B)
+        return fail(Q4_EINVAL, "NULL bias pointer");
+    if (!aligned(B, 2))
+        return fail(Q4_EALIGN, "the biases must be 2-byte aligned");
+    const size_t sb = (size_t)N * (K / 64) * 2;
+    if ((st = check_gemm_io(W, S, B, sb, sb, x, ldx, y, ldy, N, K, M)) != Q4_OK)
+        return st;
+    return launch_gemm(W, S, x, ldx, y, ldy, (int)N, (int)K, (int)M, true, as_stream(stream), B);
+}
+
+q4_status q4_gemm(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
+                  uint16_t *y, int64_t ldy, int64_t N, int64_t K, int64_t M, int weights,
+                  q4_stream stream)
+{
+    q4_status st = check_matrix(W, S, N, K);
+    if (st != Q4_OK)
+        return st;
+    if (weights != Q4_GEMM_EXACT && weights != Q4_GEMM_F16_WEIGHT)
+        return fail(Q4_EINVAL, "unknown weights mode %d", weights);
+    if ((st = check_gemm_io(W, S, nullptr, sbytes(N, K), 0, x, ldx, y, ldy, N, K, M)) != Q4_OK)
+        return st;
     return launch_gemm(W, S, x, ldx, y, ldy, (int)N, (int)K, (int)M,
                        weights == Q4_GEMM_EXACT, as_stream(stream));
 }
-
 
 q4_status q4_gemv_f32(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
                       float *y, int64_t ldy, int64_t N, int64_t K, int64_t M, q4_stream stream)

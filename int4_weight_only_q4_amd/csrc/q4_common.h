@@ -164,10 +164,11 @@ q4_status launch_lm_head_argmax(const uint32_t *W, const uint16_t *S, const uint
                                 int64_t ldx, float *logits, int64_t ldl, int32_t *tokens, int N,
                                 int K, int M, hipStream_t stream);
 // Prefill matmul on the matrix cores (q4_gemm.hip): exact weights, or
-// weights rounded to f16 when exact is false.
+// weights rounded to f16 when exact is false; bias set: the MLX affine format
+// (scales and biases [N][K/64], exact weights only).
 q4_status launch_gemm(const uint32_t *W, const uint16_t *S, const uint16_t *X, int64_t ldx,
                       uint16_t *Y, int64_t ldy, int N, int K, int M, bool exact,
-                      hipStream_t stream);
+                      hipStream_t stream, const uint16_t *bias = nullptr);
 q4_status launch_gemv_batched(const uint32_t *W, const uint16_t *S, const uint16_t *x,
                               int64_t ldx, uint16_t *y, int64_t ldy, int N, int K, int M,
                               hipStream_t stream);

@@ -25,6 +25,13 @@
 //    fastest, so an XCD's L2 keeps the weight tile for all its row blocks;
 //  * rows past M or N are clamped on load and never stored; groups past K get
 //    scale 0 and zero activations.
+// The MLX affine format (w = s * q + b, q unsigned, s and b per 64 codes; Zero
+// TVM Documentation, the Qwen3.6-35B-A3B entry; BENCH.md "Subgroup-matrix GEMM
+// graduated", the _affine variants) runs through the same loop with unsigned
+// codes and the scale of group g / 2; its bias term sum_g b[n][g] * xs[m][g],
+// xs[m][g] = the sum of row m's activations over group g, is a few more K steps
+// of the same matrix product: A = xs split into binary16 hi and lo halves (a
+// small kernel forms them), B = the binary16 biases.
 #include <algorithm>
 
 #include "q4_dequant.h"
@@ -72,11 +79,12 @@ __device__ __forceinline__ void broadcast_rows(uint32_t v, uint32_t (&out)[4])
 // otherwise hi = f16(w) alone. A nibble in mantissa bits 0..3 under exponent
 // field 25 is the binary16 1024 + q; in bits 4..7 under exponent field 21 it
 // is 64 + q, so one shift of the word by 8 reaches all four pairs.
-template <bool EXACT>
+// AFF: unsigned codes (w = q * s; the affine bias is added separately).
+template <bool EXACT, bool AFF>
 __device__ __forceinline__ void weights_of(uint32_t w, half2v s2, half8 &hi, half8 &lo)
 {
-    const half2v c1031 = {(_Float16)-1031.0f, (_Float16)-1031.0f};
-    const half2v c71 = {(_Float16)-71.0f, (_Float16)-71.0f};
+    const half2v c1031 = {(_Float16)(AFF ? -1024.0f : -1031.0f), (_Float16)(AFF ? -1024.0f : -1031.0f)};
+    const half2v c71 = {(_Float16)(AFF ? -64.0f : -71.0f), (_Float16)(AFF ? -64.0f : -71.0f)};
     const uint32_t w8 = w >> 8;
     uint32_t b[4];
     asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(b[0]) : "v"(0x000F000Fu), "v"(w), "s"(0x64006400u));
@@ -85,7 +93,7 @@ __device__ __forceinline__ void weights_of(uint32_t w, half2v s2, half8 &hi, hal
     asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(b[3]) : "v"(0x00F000F0u), "v"(w8), "s"(0x54005400u));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const half2v q = __builtin_bit_cast(half2v, b[i]) + ((i & 1) ? c71 : c1031);  // exact q - 7
+        const half2v q = __builtin_bit_cast(half2v, b[i]) + ((i & 1) ? c71 : c1031);  // exact q (- 7)
         const half2v h = q * s2;
         hi[2 * i] = h[0];
         hi[2 * i + 1] = h[1];
@@ -136,14 +144,15 @@ struct StepLoads {
     u32x4 x[MS];
 };
 
-template <int MS>
+// (AFF: a step spans two 64-code groups, so its scales are 4 bytes on)
+template <int MS, bool AFF>
 __device__ __forceinline__ void load_step(StepLoads<MS> &L, const Bufs &B, const Offsets<MS> &O,
                                           int st)
 {
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns) {
         L.w[ns] = __builtin_amdgcn_raw_buffer_load_b128(B.w, O.w[ns], st * 64, 0);
-        L.s[ns] = __builtin_amdgcn_raw_buffer_load_b16(B.s, O.s[ns], st * 8, 0);
+        L.s[ns] = __builtin_amdgcn_raw_buffer_load_b16(B.s, O.s[ns], st * (AFF ? 4 : 8), 0);
     }
 #pragma unroll
     for (int q = 0; q < MS; ++q)
@@ -195,7 +204,7 @@ __device__ __forceinline__ void stage(_Float16 *buf, const StepLoads<MS> &L, int
     }
 }
 
-template <int MS, bool EXACT>
+template <int MS, bool EXACT, bool AFF>
 __device__ __forceinline__ void multiply(floatx4 (&acc)[MS][2], const _Float16 *cur,
                                          const StepWeights &P, int n, int kb)
 {
@@ -209,7 +218,7 @@ __device__ __forceinline__ void multiply(floatx4 (&acc)[MS][2], const _Float16 *
                                                      32 * tt);
 #pragma unroll
         for (int ns = 0; ns < 2; ++ns)
-            weights_of<EXACT>(P.wt[ns][tt], P.s2[ns][tt], bh[ns], bl[ns]);
+            weights_of<EXACT, AFF>(P.wt[ns][tt], P.s2[ns][tt], bh[ns], bl[ns]);
 #pragma unroll
         for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
@@ -227,15 +236,103 @@ __device__ __forceinline__ void multiply(floatx4 (&acc)[MS][2], const _Float16 *
     }
 }
 
+// The affine bias term as extra K steps: step bs covers entries [128 bs,
+// 128 bs + 128) of the group-sum rows xs[m][0 .. 2 GP) (hi halves of groups
+// 0..GP-1, then the lo halves; entries of groups past G64 are 0) against
+// B[j][n] = bias[n][j mod GP] (0 past G64), in natural order (no pair order
+// on either side). The caller has passed the last barrier of the main loop.
+// Bias steps [b0, b1); bvec: the bias rows allow 16-byte loads (G64 % 8 == 0,
+// Bias 16-byte aligned).
+template <int MS>
+__device__ __forceinline__ void bias_steps(floatx4 (&acc)[MS][2], _Float16 *buf,
+                                           const uint16_t *__restrict__ XS, int M, int m0,
+                                           const uint16_t *__restrict__ Bias, int N, int n0,
+                                           int G64, int GP, int b0, int b1, bool bvec, int t,
+                                           int n, int kb)
+{
+    const int ld = 2 * GP;
+    const __amdgpu_buffer_rsrc_t rx = rsrc(XS, (uint32_t)((int64_t)M * ld * 2));
+    const __amdgpu_buffer_rsrc_t rb = rsrc(Bias, (uint32_t)N * (uint32_t)G64 * 2u);
+    for (int bs = b0; bs < b1; ++bs) {
+        __syncthreads();  // the buffer's previous contents are no longer read
+#pragma unroll
+        for (int q = 0; q < MS; ++q) {
+            const int c = t + 256 * q, row = m0 + (c >> 4);
+            const uint32_t off = row < M ? (uint32_t)((row * ld + 128 * bs + 8 * (c & 15)) * 2) : kOut;
+            *reinterpret_cast<u32x4 *>(buf + (c >> 4) * kAStride + 8 * (c & 15)) =
+                __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const int j0 = 128 * bs + 32 * tt + 8 * kb;  // this lane row's 8 K entries
+            const int g0 = j0 < GP ? j0 : j0 - GP;
+            half8 bb[2];
+#pragma unroll
+            for (int ns = 0; ns < 2; ++ns) {
+                const int row = n0 + 16 * ns + n;
+                if (bvec) {  // eight biases of one group range in one load (0 past G64)
+                    const uint32_t off = row < N && g0 < G64 ? (uint32_t)(row * G64 + g0) * 2u : kOut;
+                    bb[ns] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const uint32_t off = row < N && g0 + e < G64 ? (uint32_t)(row * G64 + g0 + e) * 2u : kOut;
+                        bb[ns][e] = __builtin_bit_cast(_Float16, (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rb, off, 0, 0));
+                    }
+                }
+            }
+#pragma unroll
+            for (int ms = 0; ms < MS; ++ms) {
+                const half8 a = *reinterpret_cast<const half8 *>(buf + (16 * ms + n) * kAStride + 8 * kb + 32 * tt);
+#pragma unroll
+                for (int ns = 0; ns < 2; ++ns)
+                    acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bb[ns], acc[ms][ns], 0, 0, 0);
+            }
+        }
+    }
+}
+
+// Group sums of the activation rows for the affine bias: xs[m][g] = hi and
+// xs[m][GP + g] = lo with s = the f32 sum over x[m][64 g .. 64 g + 63] in
+// order, hi = f16(s), lo = f16(s - hi); 0 for g >= G64. One thread per (m, g).
+__global__ __launch_bounds__(256) void k_group_sums(const uint16_t *__restrict__ X, int64_t ldx,
+                                                    uint16_t *__restrict__ XS, int M, int G64,
+                                                    int GP)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)M * GP)
+        return;
+    const int m = (int)(i / GP), g = (int)(i % GP);
+    float s = 0.f;
+    if (g < G64) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(X + (int64_t)m * ldx + 64 * g);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            float f[8];
+            chunk_to_float(p[c], f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                s += f[e];
+        }
+    }
+    const uint16_t hi = f2h(s);
+    XS[(int64_t)m * 2 * GP + g] = hi;
+    XS[(int64_t)m * 2 * GP + GP + g] = f2h(s - h2f(hi));
+}
+
 // Grid: one workgroup per (16 MS-row activation tile, 128-row weight tile),
 // 256 threads; wave w owns weight rows [32 w, 32 w + 32) of the tile and all
 // MS 16-row activation tiles. Buffer sizes below 2^31 bytes (the launcher
 // splits larger problems).
-template <int MS, bool EXACT>
+// AFF: the affine format; S and Bias [N][G / 2]; XS the group sums of X
+// (k_group_sums, GP groups per half).
+template <int MS, bool EXACT, bool AFF>
 __global__ __launch_bounds__(256, MS == 8 ? 2 : 3) void k_gemm_q4(
     const uint4 *__restrict__ W, const uint16_t *__restrict__ S, const uint16_t *__restrict__ X,
     int64_t ldx, uint16_t *__restrict__ Y, int64_t ldy, float *__restrict__ part, int M, int N,
-    int G, int sps)
+    int G, int sps, const uint16_t *__restrict__ Bias, const uint16_t *__restrict__ XS, int GP,
+    int bvec)
 {
     constexpr int BM = 16 * MS;
     __shared__ _Float16 xs[2][BM * kAStride];
@@ -252,14 +349,14 @@ __global__ __launch_bounds__(256, MS == 8 ? 2 : 3) void k_gemm_q4(
 
     Bufs B;
     B.w = rsrc(W, (uint32_t)N * (uint32_t)G * 16u);
-    B.s = rsrc(S, (uint32_t)N * (uint32_t)G * 2u);
+    B.s = rsrc(S, (uint32_t)N * (uint32_t)(AFF ? G / 2 : G) * 2u);
     B.x = rsrc(X, (uint32_t)(((int64_t)(M - 1) * ldx + G * 32) * 2));
     Offsets<MS> O;
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns) {
         const int row = n0 + 16 * ns + n;
         O.w[ns] = row < N ? (uint32_t)(row * G + kb) * 16u : kOut;
-        O.s[ns] = row < N ? (uint32_t)(row * G + kb) * 2u : kOut;
+        O.s[ns] = row < N ? (uint32_t)(AFF ? row * (G / 2) + kb / 2 : row * G + kb) * 2u : kOut;
     }
 #pragma unroll
     for (int q = 0; q < MS; ++q) {
@@ -275,26 +372,34 @@ __global__ __launch_bounds__(256, MS == 8 ? 2 : 3) void k_gemm_q4(
             acc[ms][ns] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     // step st: groups [4 st, 4 st + 4); its loads are issued one step ahead.
-    // K split z (grid y) takes the steps [z sps, min((z + 1) sps, steps)).
+    // K split z (grid y) takes the steps [z sps, min((z + 1) sps, total)); in
+    // the affine format the bias steps follow the weight steps.
     const int steps = (G + 3) / 4, z = blockIdx.y;
+    const int total_steps = steps + (AFF ? GP / 64 : 0);
     const int st0 = z * sps, st1 = min(steps, st0 + sps);
+    const int bs1 = min(total_steps, st0 + sps);
     StepLoads<MS> L;
     StepWeights P;
-    load_step<MS>(L, B, O, st0);
+    if (st0 < st1) {
+    load_step<MS, AFF>(L, B, O, st0);
     for (int st = st0; st < st1 - 1; ++st) {
         stage<MS, false>(xs[st & 1], L, 4 * st, G, t);
         prepare<MS, false>(P, L, 4 * st, kb, G);
-        load_step<MS>(L, B, O, st + 1);
+        load_step<MS, AFF>(L, B, O, st + 1);
         __syncthreads();  // the tile is staged; the other buffer was last read before this
-        multiply<MS, EXACT>(acc, xs[st & 1], P, n, kb);
+        multiply<MS, EXACT, AFF>(acc, xs[st & 1], P, n, kb);
     }
     {
         const int st = st1 - 1;  // groups past K only in the last step of the last split
         stage<MS, true>(xs[st & 1], L, 4 * st, G, t);
         prepare<MS, true>(P, L, 4 * st, kb, G);
         __syncthreads();
-        multiply<MS, EXACT>(acc, xs[st & 1], P, n, kb);
+        multiply<MS, EXACT, AFF>(acc, xs[st & 1], P, n, kb);
     }
+    }
+    if (AFF && bs1 > steps)  // this split's share of the bias steps
+        bias_steps<MS>(acc, xs[0], XS, M, m0, Bias, N, n0, G / 2, GP, max(st0, steps) - steps,
+                       bs1 - steps, bvec != 0, t, n, kb);
 
     // lane (n, kb) holds D[4 kb + i][n] of each (activation, weight) tile:
     // rounded to Y, or with several K splits the f32 partial part[z][row][col]
@@ -365,9 +470,10 @@ struct GemmShape {
     int ms, splits, sps;
 };
 
-GemmShape gemm_shape(int M, int N, int G, size_t max_part_bytes)
+// (extra: steps after the weight steps, the affine bias steps)
+GemmShape gemm_shape(int M, int N, int G, size_t max_part_bytes, int extra = 0)
 {
-    const int cus = cu_count(), nt = (N + kBN - 1) / kBN, steps = (G + 3) / 4;
+    const int cus = cu_count(), nt = (N + kBN - 1) / kBN, steps = (G + 3) / 4 + extra;
     const int64_t t8 = (int64_t)((M + 127) / 128) * nt, t4 = (int64_t)((M + 63) / 64) * nt;
     const double r8 = (double)((t8 + 2 * cus - 1) / (2 * cus));
     const double r4 = 0.74 * (double)((t4 + 3 * cus - 1) / (3 * cus));
@@ -388,14 +494,19 @@ GemmShape gemm_shape(int M, int N, int G, size_t max_part_bytes)
 template <int MS>
 q4_status launch_tiles(bool exact, dim3 grid, hipStream_t stream, const uint4 *w, const uint16_t *s,
                        const uint16_t *x, int64_t ldx, uint16_t *y, int64_t ldy, float *part,
-                       int M, int N, int G, int sps)
+                       int M, int N, int G, int sps, const uint16_t *bias, const uint16_t *xsum,
+                       int gp)
 {
-    if (exact)
-        Q4_LAUNCH_MATVEC((k_gemm_q4<MS, true>), grid, dim3(256), 0, stream, w, s, x, ldx, y, ldy,
-                         part, M, N, G, sps);
+    const int bvec = bias && (G / 2) % 8 == 0 && reinterpret_cast<uintptr_t>(bias) % 16 == 0;
+    if (bias)
+        Q4_LAUNCH_MATVEC((k_gemm_q4<MS, true, true>), grid, dim3(256), 0, stream, w, s, x, ldx,
+                         y, ldy, part, M, N, G, sps, bias, xsum, gp, bvec);
+    else if (exact)
+        Q4_LAUNCH_MATVEC((k_gemm_q4<MS, true, false>), grid, dim3(256), 0, stream, w, s, x, ldx,
+                         y, ldy, part, M, N, G, sps, nullptr, nullptr, 0, 0);
     else
-        Q4_LAUNCH_MATVEC((k_gemm_q4<MS, false>), grid, dim3(256), 0, stream, w, s, x, ldx, y,
-                         ldy, part, M, N, G, sps);
+        Q4_LAUNCH_MATVEC((k_gemm_q4<MS, false, false>), grid, dim3(256), 0, stream, w, s, x, ldx,
+                         y, ldy, part, M, N, G, sps, nullptr, nullptr, 0, 0);
     return check_launch("k_gemm_q4");
 }
 
@@ -403,10 +514,13 @@ q4_status launch_tiles(bool exact, dim3 grid, hipStream_t stream, const uint4 *w
 
 q4_status launch_gemm(const uint32_t *W, const uint16_t *S, const uint16_t *X, int64_t ldx,
                       uint16_t *Y, int64_t ldy, int N, int K, int M, bool exact,
-                      hipStream_t stream)
+                      hipStream_t stream, const uint16_t *bias)
 {
     constexpr size_t kMaxPart = size_t(256) << 20;  // f32 partials of a split launch
     const int G = K / 32;
+    // affine: scales and biases per 64 codes; group sums padded to GP groups
+    const int G64 = G / 2, GP = (G64 + 63) / 64 * 64;
+    const int sg = bias ? G64 : G;  // scales per weight row
     // every buffer of a launch under 2^31 bytes: chunks of weight rows (whole
     // 128-row tiles) and of activation rows (whole 128-row tiles)
     const int64_t wrow_bytes = (int64_t)G * 16;
@@ -416,26 +530,38 @@ q4_status launch_gemm(const uint32_t *W, const uint16_t *S, const uint16_t *X, i
     for (int n0 = 0; n0 < N; n0 += nchunk)
         for (int m0 = 0; m0 < M; m0 += mchunk) {
             const int nn = std::min(nchunk, N - n0), mm = std::min(mchunk, M - m0);
-            const GemmShape g = gemm_shape(mm, nn, G, kMaxPart);
+            const GemmShape g = gemm_shape(mm, nn, G, kMaxPart, bias ? GP / 64 : 0);
             const int BM = 16 * g.ms;
             const int64_t tiles = (int64_t)((mm + BM - 1) / BM) * ((nn + kBN - 1) / kBN);
             const dim3 grid((unsigned)tiles, (unsigned)g.splits);
+            const uint4 *w = reinterpret_cast<const uint4 *>(W) + (size_t)n0 * G;
+            const uint16_t *s = S + (size_t)n0 * sg, *x = X + (size_t)m0 * ldx;
+            uint16_t *y = Y + (size_t)m0 * ldy + n0;
             float *part = nullptr;
-            if (g.splits > 1) {
-                char *ws = static_cast<char *>(
-                    workspace(stream, kWsHeader + (size_t)g.splits * mm * nn * sizeof(float)));
+            uint16_t *xsum = nullptr;
+            const size_t part_b = g.splits > 1 ? (size_t)g.splits * mm * nn * sizeof(float) : 0;
+            const size_t xsum_b = bias ? (size_t)mm * 2 * GP * sizeof(uint16_t) : 0;
+            if (part_b + xsum_b) {
+                char *ws = static_cast<char *>(workspace(stream, kWsHeader + part_b + xsum_b));
                 if (!ws)
                     return Q4_EHIP;
-                part = reinterpret_cast<float *>(ws + kWsHeader);
+                part = part_b ? reinterpret_cast<float *>(ws + kWsHeader) : nullptr;
+                xsum = xsum_b ? reinterpret_cast<uint16_t *>(ws + kWsHeader + part_b) : nullptr;
             }
-            const uint4 *w = reinterpret_cast<const uint4 *>(W) + (size_t)n0 * G;
-            const uint16_t *s = S + (size_t)n0 * G, *x = X + (size_t)m0 * ldx;
-            uint16_t *y = Y + (size_t)m0 * ldy + n0;
+            if (bias) {
+                const int64_t cnt = (int64_t)mm * GP;
+                hipLaunchKernelGGL(k_group_sums, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0,
+                                   stream, x, ldx, xsum, mm, G64, GP);
+                q4_status st = check_launch("k_group_sums");
+                if (st != Q4_OK)
+                    return st;
+            }
+            const uint16_t *bz = bias ? bias + (size_t)n0 * G64 : nullptr;
             q4_status st = g.ms == 4
                                ? launch_tiles<4>(exact, grid, stream, w, s, x, ldx, y, ldy, part,
-                                                 mm, nn, G, g.sps)
+                                                 mm, nn, G, g.sps, bz, xsum, GP)
                                : launch_tiles<8>(exact, grid, stream, w, s, x, ldx, y, ldy, part,
-                                                 mm, nn, G, g.sps);
+                                                 mm, nn, G, g.sps, bz, xsum, GP);
             if (st != Q4_OK)
                 return st;
             if (g.splits > 1) {

@@ -293,3 +293,14 @@ def test_gemm_validation():
     assert f(A, B, X, 128, Y + 1, 16, 16, 128, 4, 0, None) == q4.Q4_EALIGN
     assert f(A, B, X, 128, X + 64, 16, 16, 128, 4, 0, None) == q4.Q4_EALIAS  # y over x
     assert f(A, B, X, 128, B, 16, 16, 128, 4, 1, None) == q4.Q4_EALIAS     # y over the scales
+
+
+def test_gemm_affine_validation():
+    f = q4.lib().q4_gemm_affine
+    assert f(A, B, None, X, 128, Y, 16, 16, 128, 4, None) == q4.Q4_EINVAL     # no biases
+    assert f(A, B, R, X, 96, Y, 16, 16, 96, 4, None) == q4.Q4_ESHAPE        # K % 64
+    assert f(A, B, R, X, 128, Y, 16, 16, 128, 0, None) == q4.Q4_ERANGE      # M < 1
+    assert f(A, B, R, X, 128, Y, 8, 16, 128, 4, None) == q4.Q4_EINVAL       # ldy < N
+    assert f(A, B, R + 1, X, 128, Y, 16, 16, 128, 4, None) == q4.Q4_EALIGN
+    assert f(A, B, R, X + 8, 128, Y, 16, 16, 128, 4, None) == q4.Q4_EALIGN
+    assert f(A, B, R, X, 128, R, 16, 16, 128, 4, None) == q4.Q4_EALIAS      # y over the biases

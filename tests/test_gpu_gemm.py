@@ -141,3 +141,91 @@ def test_gemm_prefill_sampled(o, q4, name, n, k, m, mode):
     ref = ref_fn(W[cols], S[cols], X[rows])
     assert_within(y[np.ix_(rows, cols)], ref, "%s sampled" % name)
     assert np.all(np.isfinite(y)), "non-finite outputs"
+
+
+# -- MLX affine format (w = s * q + b, group 64) ----------------------------------
+
+def make_affine(name, n, k, m):
+    seed = datagen.seed_for(9, 500 + zlib.crc32(name.encode()) % 400)
+    W = datagen.words(seed, n, k)
+    S = datagen.scales(seed + 1, n, k // 2)
+    B = datagen.normal_f16(seed + 2, (n, k // 64), 0.0, 0.05)
+    X = datagen.activations(seed + 3, m, k)
+    return W, S, B, X
+
+
+def run_affine(q4, W, S, B, X, ldx=None, ldy=None):
+    import torch
+    m, k = X.shape
+    n = W.shape[0]
+    ldx = ldx or k
+    ldy = ldy or n
+    xb = np.zeros((m, ldx), np.float16)
+    xb[:, :k] = X
+    xd = dev_tensor(xb)
+    yd = torch.full((m, ldy), 3.0, dtype=torch.float16, device="cuda")
+    q4.gemm_affine(dev_tensor(W), dev_tensor(S), dev_tensor(B), xd[:, :k], yd[:, :n])
+    torch.cuda.synchronize()
+    y = host(yd)
+    assert np.all(y[:, n:] == np.float16(3.0)), "wrote past N in the padded rows"
+    return y[:, :n]
+
+
+AFFINE_SMALL = [("a_tiny", 1, 5, 64), ("a_short", 17, 200, 192), ("a_tile", 64, 128, 256),
+                ("a_ragged", 65, 129, 640), ("a_tail", 130, 300, 1088),
+                ("a_two_bias_steps_split", 256, 256, 4160)]
+
+
+@pytest.mark.parametrize("name,m,n,k", AFFINE_SMALL, ids=[s[0] for s in AFFINE_SMALL])
+def test_gemm_affine_vs_oracle(o, q4, name, m, n, k):
+    W, S, B, X = make_affine(name, n, k, m)
+    y = run_affine(q4, W, S, B, X)
+    assert_within(y, o.gemv_affine(W, S, B, X), name)
+
+
+def test_gemm_affine_strided_rows(o, q4):
+    W, S, B, X = make_affine("a_strided", 200, 384, 70)
+    y = run_affine(q4, W, S, B, X, ldx=392, ldy=216)
+    assert_within(y, o.gemv_affine(W, S, B, X), "affine strided")
+
+
+def test_gemm_affine_one_hot_is_the_weight(o, q4):
+    """Row i of X is e_{k_i}: y[i][n] = f16(s q + b) of weight (n, k_i), bit for bit."""
+    n, k, m = 160, 1024, 96
+    codes = datagen.codes(911, n, k)
+    W = o.pack(codes)
+    S = datagen.scales(912, n, k // 2)
+    B = datagen.normal_f16(913, (n, k // 64), 0.0, 0.05)
+    rng = np.random.default_rng(914)
+    ks = np.concatenate([np.arange(8), rng.integers(0, k, m - 8)])
+    X = np.zeros((m, k), np.float16)
+    X[np.arange(m), ks] = 1.0
+    y = run_affine(q4, W, S, B, X)
+    for i in range(m):
+        c = ks[i]
+        want = o.d2h(o.h2d(S[:, c // 64]) * codes[:, c] + o.h2d(B[:, c // 64]))
+        assert np.array_equal(y[i].view(np.uint16), want.view(np.uint16)), (i, c)
+
+
+def test_gemm_affine_rows_independent_of_m(q4):
+    W, S, B, X = make_affine("a_m_invariance", 384, 1024, 300)
+    full = run_affine(q4, W, S, B, X)
+    for lo, hi in ((0, 1), (77, 78), (250, 300), (64, 129)):
+        part = run_affine(q4, W, S, B, X[lo:hi])
+        assert np.array_equal(part.view(np.uint16), full[lo:hi].view(np.uint16)), (lo, hi)
+
+
+AFFINE_PREFILL = [("qwen3_gate_up", 19456, 2560, 256), ("qwen3_down", 2560, 9728, 256),
+                  ("qwen3_o", 2560, 4096, 256), ("qwen3_qkv_1024", 6144, 2560, 1024)]
+
+
+@pytest.mark.parametrize("name,n,k,m", AFFINE_PREFILL, ids=[s[0] for s in AFFINE_PREFILL])
+def test_gemm_affine_prefill_sampled(o, q4, name, n, k, m):
+    W, S, B, X = make_affine(name, n, k, m)
+    y = run_affine(q4, W, S, B, X)
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    rows = np.unique(np.r_[0, m - 1, rng.integers(0, m, 10)])
+    cols = np.unique(np.r_[0, 127, 128, n - 1, rng.integers(0, n, 92)])
+    ref = o.gemv_affine(W[cols], S[cols], B[cols], X[rows])
+    assert_within(y[np.ix_(rows, cols)], ref, "%s sampled" % name)
+    assert np.all(np.isfinite(y)), "non-finite outputs"
