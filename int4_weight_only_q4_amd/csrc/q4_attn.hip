@@ -63,11 +63,7 @@ __device__ __forceinline__ int64_t cache_row(const RopeArgs &r, int t, int kvh)
 
 __device__ __forceinline__ float block_reduce(float v, float *red, bool is_max)
 {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        const float o = __shfl_xor(v, off, 64);
-        v = is_max ? fmaxf(v, o) : v + o;
-    }
+    v = is_max ? segment_max(v, 64) : segment_sum(v, 64);
     const int wave = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0)
         red[wave] = v;
@@ -227,14 +223,9 @@ __global__ __launch_bounds__(kMaxHeadDim) void k_attn_combine(const float *__res
         const float l = has ? ph[tid * (2 + D) + 1] : 0.f;
         const bool valid = l > 0.f;
         float M = valid ? m : -INFINITY;
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1)
-            M = fmaxf(M, __shfl_xor(M, off, 64));
+        M = segment_max(M, 64);
         const float w = valid ? expf(m - M) : 0.f;
-        float sum = l * w;
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1)
-            sum += __shfl_xor(sum, off, 64);
+        const float sum = segment_sum(l * w, 64);
         if (has)
             wgt[tid] = w;
         if (tid == 0)

@@ -279,6 +279,28 @@ __device__ __forceinline__ float segment_sum(float v, int w)
     return v;
 }
 
+// Maximum (fmaxf) over each aligned segment of w lanes, as segment_sum;
+// every lane of a segment ends with the same value.
+__device__ __forceinline__ float segment_max(float v, int w)
+{
+    if (w >= 64) {
+        uint32_t a = __builtin_bit_cast(uint32_t, v), b = a;
+        swap32(a, b);
+        v = fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+    }
+    if (w >= 32) {
+        uint32_t a = __builtin_bit_cast(uint32_t, v), b = a;
+        swap16(a, b);
+        v = fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+    }
+    if (w >= 16)
+        v = fmaxf(v, dpp<0x128>(v));
+    v = fmaxf(v, dpp<0x141>(v));
+    v = fmaxf(v, dpp<0x4E>(v));
+    v = fmaxf(v, dpp<0xB1>(v));
+    return v;
+}
+
 // Sum over the four lanes of each aligned quad (partners i ^ 1, then i ^ 2).
 __device__ __forceinline__ float quad_sum(float v)
 {
