@@ -264,12 +264,7 @@ q4_status launch_attention(const uint16_t *q, const uint16_t *kv, const RopeArgs
     // one workgroup per head up to one block of positions (no combine step);
     // beyond, about two workgroups per CU over the heads, in splits of whole
     // kSplitGrain pieces, and no fewer splits than blocks of 256 positions
-    int cu = 256;
-    {
-        int dev = 0;
-        if (hipGetDevice(&dev) == hipSuccess)
-            hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev);
-    }
+    const int cu = cu_count();
     const int64_t fill = (2 * (int64_t)cu + r.n_heads - 1) / r.n_heads;
     const int64_t by_grain = std::min<int64_t>((len + kSplitGrain - 1) / kSplitGrain, fill);
     const int64_t by_block = (len + kAttnThreads - 1) / kAttnThreads;
