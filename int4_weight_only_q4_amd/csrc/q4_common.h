@@ -197,7 +197,7 @@ __device__ __forceinline__ float h2f(uint16_t h) { return (float)__builtin_bit_c
 // some kernels and not in others: every path rounds the same f32 value.
 __device__ __forceinline__ uint16_t f2h(float f)
 {
-    asm volatile("" : "+v"(f));
+    asm("" : "+v"(f));  // opaque (no fusion across the rounding), freely scheduled
     return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
