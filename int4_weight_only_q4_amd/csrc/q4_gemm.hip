@@ -294,31 +294,34 @@ __device__ __forceinline__ void bias_steps(floatx4 (&acc)[MS][2], _Float16 *buf,
 }
 
 // Group sums of the activation rows for the affine bias: xs[m][g] = hi and
-// xs[m][GP + g] = lo with s = the f32 sum over x[m][64 g .. 64 g + 63] in
-// order, hi = f16(s), lo = f16(s - hi); 0 for g >= G64. One thread per (m, g).
+// xs[m][GP + g] = lo with s = the f32 sum over x[m][64 g .. 64 g + 63], hi =
+// f16(s), lo = f16(s - hi); 0 for g >= G64. One thread per 8-value chunk sums
+// its chunk in order; the 8 chunks of a group (8 consecutive lanes) are added
+// by segment_sum, in one fixed order.
 __global__ __launch_bounds__(256) void k_group_sums(const uint16_t *__restrict__ X, int64_t ldx,
                                                     uint16_t *__restrict__ XS, int M, int G64,
                                                     int GP)
 {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (int64_t)M * GP)
-        return;
-    const int m = (int)(i / GP), g = (int)(i % GP);
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // chunk index
+    const int64_t gi = i >> 3;                                     // (m, g)
+    const bool live = gi < (int64_t)M * GP;
+    const int m = live ? (int)(gi / GP) : 0, g = live ? (int)(gi % GP) : 0;
     float s = 0.f;
-    if (g < G64) {
-        const uint4 *p = reinterpret_cast<const uint4 *>(X + (int64_t)m * ldx + 64 * g);
+    if (live && g < G64) {
+        float f[8];
+        chunk_to_float(*reinterpret_cast<const uint4 *>(X + (int64_t)m * ldx + 64 * g +
+                                                        8 * (int)(i & 7)),
+                       f);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            float f[8];
-            chunk_to_float(p[c], f);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                s += f[e];
-        }
+        for (int e = 0; e < 8; ++e)
+            s += f[e];
     }
-    const uint16_t hi = f2h(s);
-    XS[(int64_t)m * 2 * GP + g] = hi;
-    XS[(int64_t)m * 2 * GP + GP + g] = f2h(s - h2f(hi));
+    s = segment_sum(s, 8);  // all lanes take part
+    if (live && (i & 7) == 0) {
+        const uint16_t hi = f2h(s);
+        XS[(int64_t)m * 2 * GP + g] = hi;
+        XS[(int64_t)m * 2 * GP + GP + g] = f2h(s - h2f(hi));
+    }
 }
 
 // Grid: one workgroup per (16 MS-row activation tile, 128-row weight tile),
@@ -549,7 +552,7 @@ q4_status launch_gemm(const uint32_t *W, const uint16_t *S, const uint16_t *X, i
                 xsum = xsum_b ? reinterpret_cast<uint16_t *>(ws + kWsHeader + part_b) : nullptr;
             }
             if (bias) {
-                const int64_t cnt = (int64_t)mm * GP;
+                const int64_t cnt = (int64_t)mm * GP * 8;  // one thread per 8-value chunk
                 hipLaunchKernelGGL(k_group_sums, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0,
                                    stream, x, ldx, xsum, mm, G64, GP);
                 q4_status st = check_launch("k_group_sums");
