@@ -350,7 +350,7 @@ def gemv_table(q4, torch):
     gemv_rows("Phi-3-mini layer", [("QKV", (9216, 3072)), ("O", (3072, 3072)),
                                    ("gate_up", (16384, 3072)), ("down", (3072, 8192))], [1],
               base + 1000)
-    gemv_rows("Qwen3-4B", list(QWEN3.items()), [1, 8], base + 2000)
+    gemv_rows("Qwen3-4B", list(QWEN3.items()), [1, 2, 4, 8], base + 2000)
 
     # the MLX affine format (w = s * q + b, group 64) at the Qwen3-4B shapes
     for j, (name, (n, k)) in enumerate([("qkv", (6144, 2560)), ("gate_up", (19456, 2560)),
@@ -361,7 +361,7 @@ def gemv_table(q4, torch):
         copies = max(2, -(-(512 << 20) // int(n * k * BPW)))
         rot = [(Wh, Sh, Bh)] + [(Wh.clone(), Sh.clone(), Bh.clone()) for _ in range(copies - 1)]
         wb = n * k * BPW
-        for m in (1, 8):
+        for m in (1, 2, 4, 8):
             x = torch.from_numpy(datagen.activations(base + 2603 + 10 * j, m, k)).cuda()
             y = torch.empty((m, n), dtype=torch.float16, device="cuda")
 
@@ -643,7 +643,7 @@ def write_prefill_table(rows):
 
 
 def write_gemv_table(rows):
-    text = ["# Per-GEMV throughput: single GEMV, Phi-3-mini, Qwen3-4B (M = 1, 8), LM heads with "
+    text = ["# Per-GEMV throughput: single GEMV, Phi-3-mini, Qwen3-4B (M = 1, 2, 4, 8), LM heads with "
             "argmax, QKV + RoPE + KV append, decode attention, and MoE shapes",
             "",
             "Command (from the repository root, on one MI355X): `python3 bench.py --gemv-table`",
@@ -725,7 +725,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--gemv-table", action="store_true",
-                    help="measure the per-GEMV table (Phi-3, Qwen3 M=1/8, MoE) and exit")
+                    help="measure the per-GEMV table (Phi-3, Qwen3 M=1/2/4/8, MoE) and exit")
     ap.add_argument("--prefill-table", action="store_true",
                     help="measure the prefill matmul table (q4_gemm) and exit")
     ap.add_argument("--counters", action="store_true",

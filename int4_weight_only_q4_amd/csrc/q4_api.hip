@@ -977,6 +977,8 @@ q4_status q4_gemv_affine(const uint32_t *W, const uint16_t *S, const uint16_t *B
         op.y = y;
         return launch_gemv_op(op, s);
     }
+    if (gemv_rows_fits((int)M, (int)K))  // a few rows: the single-row arithmetic per row
+        return launch_gemv_rows(W, S, x, ldx, y, ldy, (int)N, (int)K, (int)M, s, B);
     return launch_gemv_mfma(W, S, x, ldx, y, nullptr, ldy, (int)N, (int)K, (int)M, s, B);
 }
 

@@ -27,6 +27,7 @@ namespace q4 {
 namespace {
 
 constexpr int kWaves = 4;  // 256 threads per workgroup
+constexpr int kMaxRowsDot = 4;  // batched rows handled by the dot2 kernel
 
 enum { PRO_X = 0, PRO_NORM = 1 };
 enum { EPI_NONE_ = 0, EPI_SILU = 1, EPI_RESID = 2, EPI_LOGITS = 3, EPI_ROPE = 4 };
@@ -269,6 +270,113 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams a)
     }
 }
 
+// MR activation rows (2..4) against the same weights, plain f16 outputs
+// y[m * ldy + n]: the single-row kernel's loads, unpack and arithmetic per
+// activation row (each nibble pair's dot2 issued once per row), so every row's
+// result equals the single-row matvec of that row bit for bit. The MR rows are
+// staged one after another in LDS (pair order, group sums). AFF: the MLX
+// affine format, as in k_gemv.
+template <int LPR, int NG, int RPS, int MR, bool AFF>
+__global__ __launch_bounds__(256) void k_gemv_rows(GemvParams a, int64_t ldx, int64_t ldy)
+{
+    constexpr int SPW = 64 / LPR;
+    constexpr int RB = kWaves * SPW * RPS;
+    constexpr int XCH = (LPR * NG + 63) / 64;
+    extern __shared__ uint4 smem[];
+    const int G = a.G, K = G * 32, chunks = K >> 3;
+    // row m: xs at smem + m * stride, its group sums after the chunks
+    const int stride = chunks + G / 4 + 1;  // uint4 units (G floats rounded up)
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int seg = lane / LPR, j = lane % LPR;
+
+    uint4 xr[MR][XCH];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int q = 0; q < XCH; ++q) {
+            const int c = tid + 256 * q;
+            if (c < chunks)
+                xr[m][q] = reinterpret_cast<const uint4 *>(a.x + m * ldx)[c];
+        }
+    int row[RPS];
+    bool ok[RPS];
+#pragma unroll
+    for (int r = 0; r < RPS; ++r) {
+        const int rr = blockIdx.x * RB + (wave * SPW + seg) * RPS + r;
+        ok[r] = rr < a.N;
+        row[r] = ok[r] ? rr : 0;
+    }
+    uint4 wv[NG][RPS];
+    uint32_t sv[NG][RPS];
+    uint32_t bv[AFF ? NG : 1][AFF ? RPS : 1];
+#pragma unroll
+    for (int i = 0; i < NG; ++i)
+#pragma unroll
+        for (int r = 0; r < RPS; ++r) {
+            const int g = min(j + LPR * i, G - 1);
+            const size_t off = (size_t)row[r] * G + g;
+            wv[i][r] = load_weights(a.W + off);
+            if (AFF) {
+                const size_t soff = (size_t)row[r] * (G >> 1) + (g >> 1);
+                sv[i][r] = load_scale(a.S + soff);
+                bv[i][r] = load_scale(a.Bias + soff);
+            } else {
+                sv[i][r] = load_scale(a.S + off);
+            }
+        }
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        uint4 *xs = smem + m * stride;
+        float *cs = reinterpret_cast<float *>(xs + chunks);
+#pragma unroll
+        for (int q = 0; q < XCH; ++q) {
+            const int c = tid + 256 * q;
+            put_chunk(xr[m][q], c, c < chunks, xs, cs);
+        }
+    }
+    __syncthreads();
+
+    float acc[RPS][MR];
+#pragma unroll
+    for (int r = 0; r < RPS; ++r)
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+            acc[r][m] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+        const int g = j + LPR * i;
+        if (g < G) {
+#pragma unroll
+            for (int r = 0; r < RPS; ++r) {
+                const float s = h2f(sv[i][r]);
+#pragma unroll
+                for (int m = 0; m < MR; ++m) {
+                    const uint4 *xs = smem + m * stride;
+                    const float sx = reinterpret_cast<const float *>(xs + chunks)[g];
+                    if (AFF) {
+                        acc[r][m] = fmaf(s, group_dot_unsigned(wv[i][r], xs, g), acc[r][m]);
+                        acc[r][m] = fmaf(h2f(bv[i][r]), sx, acc[r][m]);
+                    } else {
+                        acc[r][m] = fmaf(s, group_dot(wv[i][r], xs, g, sx), acc[r][m]);
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < RPS; ++r)
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+            acc[r][m] = segment_sum(acc[r][m], LPR);
+    if (j == 0)
+#pragma unroll
+        for (int r = 0; r < RPS; ++r)
+            if (ok[r])
+#pragma unroll
+                for (int m = 0; m < MR; ++m)
+                    a.y[m * ldy + row[r]] = f2h(acc[r][m]);
+}
+
 struct Cfg {
     int lpr, ng;
 };
@@ -343,6 +451,61 @@ q4_status dispatch_lpr(const Cfg &c, const GemvParams &p, hipStream_t st)
     case 32: return dispatch_ng<32, EPI, PRO, AFF>(c.ng, p, st);
     case 16: return dispatch_ng<16, EPI, PRO, AFF>(c.ng, p, st);
     case 8: return dispatch_ng<8, EPI, PRO, AFF>(c.ng, p, st);
+    default: return fail(Q4_ERANGE, "no matvec configuration for K = %d", p.G * 32);
+    }
+}
+
+template <int LPR, int NG, int MR>
+q4_status run_gemv_rows(const GemvParams &p, int64_t ldx, int64_t ldy, hipStream_t st)
+{
+    constexpr int RPS = rows_per_segment(NG);
+    constexpr int RB = kWaves * (64 / LPR) * RPS;
+    const int blocks = (p.N + RB - 1) / RB;
+    const int chunks = p.G * 4;
+    const size_t lds = (size_t)MR * (chunks + p.G / 4 + 1) * 16;
+    if (p.Bias)
+        Q4_LAUNCH_MATVEC((k_gemv_rows<LPR, NG, RPS, MR, true>), dim3(blocks), dim3(256), lds, st,
+                         p, ldx, ldy);
+    else
+        Q4_LAUNCH_MATVEC((k_gemv_rows<LPR, NG, RPS, MR, false>), dim3(blocks), dim3(256), lds, st,
+                         p, ldx, ldy);
+    return check_launch("k_gemv_rows");
+}
+
+template <int LPR, int MR>
+q4_status rows_ng(int ng, const GemvParams &p, int64_t ldx, int64_t ldy, hipStream_t st)
+{
+    switch (ng) {
+    case 1: return run_gemv_rows<LPR, 1, MR>(p, ldx, ldy, st);
+    case 2: return run_gemv_rows<LPR, 2, MR>(p, ldx, ldy, st);
+    case 3: return run_gemv_rows<LPR, 3, MR>(p, ldx, ldy, st);
+    case 4: return run_gemv_rows<LPR, 4, MR>(p, ldx, ldy, st);
+    case 5: return run_gemv_rows<LPR, 5, MR>(p, ldx, ldy, st);
+    case 6: return run_gemv_rows<LPR, 6, MR>(p, ldx, ldy, st);
+    case 7: return run_gemv_rows<LPR, 7, MR>(p, ldx, ldy, st);
+    case 8: return run_gemv_rows<LPR, 8, MR>(p, ldx, ldy, st);
+    default: break;
+    }
+    if constexpr (LPR == 64) {
+        switch (ng) {
+        case 9: return run_gemv_rows<64, 9, MR>(p, ldx, ldy, st);
+        case 10: return run_gemv_rows<64, 10, MR>(p, ldx, ldy, st);
+        case 11: return run_gemv_rows<64, 11, MR>(p, ldx, ldy, st);
+        case 12: return run_gemv_rows<64, 12, MR>(p, ldx, ldy, st);
+        default: break;
+        }
+    }
+    return fail(Q4_ERANGE, "no matvec configuration for %d groups per lane", ng);
+}
+
+template <int MR>
+q4_status rows_lpr(const Cfg &c, const GemvParams &p, int64_t ldx, int64_t ldy, hipStream_t st)
+{
+    switch (c.lpr) {
+    case 64: return rows_ng<64, MR>(c.ng, p, ldx, ldy, st);
+    case 32: return rows_ng<32, MR>(c.ng, p, ldx, ldy, st);
+    case 16: return rows_ng<16, MR>(c.ng, p, ldx, ldy, st);
+    case 8: return rows_ng<8, MR>(c.ng, p, ldx, ldy, st);
     default: return fail(Q4_ERANGE, "no matvec configuration for K = %d", p.G * 32);
     }
 }
@@ -455,12 +618,37 @@ q4_status launch_gemv(const uint32_t *W, const uint16_t *S, const uint16_t *x, u
 
 // Batched matvec: M = 1 is the matvec above; M >= 2 rows share each weight
 // read on the matrix cores (q4_mfma.hip).
+bool gemv_rows_fits(int M, int K) { return M >= 2 && M <= kMaxRowsDot && M * K <= 16384; }
+
+q4_status launch_gemv_rows(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
+                           uint16_t *y, int64_t ldy, int N, int K, int M, hipStream_t stream,
+                           const uint16_t *bias)
+{
+    GemvParams p{};
+    p.W = reinterpret_cast<const uint4 *>(W);
+    p.S = S;
+    p.Bias = bias;
+    p.N = N;
+    p.G = K / 32;
+    p.x = x;
+    p.y = y;
+    const Cfg c = choose_cfg(p.G);
+    switch (M) {
+    case 2: return rows_lpr<2>(c, p, ldx, ldy, stream);
+    case 3: return rows_lpr<3>(c, p, ldx, ldy, stream);
+    case 4: return rows_lpr<4>(c, p, ldx, ldy, stream);
+    default: return fail(Q4_EINVAL, "internal: %d rows for the dot2 batched matvec", M);
+    }
+}
+
 q4_status launch_gemv_batched(const uint32_t *W, const uint16_t *S, const uint16_t *x,
                               int64_t ldx, uint16_t *y, int64_t ldy, int N, int K, int M,
                               hipStream_t stream)
 {
     if (M == 1)  // a single row is the bandwidth-bound matvec
         return launch_gemv(W, S, x, y, N, K, EpiArgs{}, stream);
+    if (gemv_rows_fits(M, K))  // a few rows: the single-row kernel's arithmetic per row
+        return launch_gemv_rows(W, S, x, ldx, y, ldy, N, K, M, stream);
     return launch_gemv_mfma(W, S, x, ldx, y, nullptr, ldy, N, K, M, stream);
 }
 

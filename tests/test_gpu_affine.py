@@ -4,7 +4,8 @@ Bar: per element |y - y_ref| <= 1e-2 + 5e-3 |y_ref| against the binary64
 oracle (w = s * q + b, group 64); a one-hot activation gives f16(s * q + b)
 bit for bit at M = 1 and on the matrix cores (M >= 2); a reference with the
 bias dropped must fail the gate. Shapes: Qwen3-4B's layer matrices (the pages
-run Qwen3 as an MLX-affine build), ragged N, and M = 1, 2, 8, 17.
+run Qwen3 as an MLX-affine build), ragged N, and M = 1, 2, 3, 4, 8, 17; at
+M = 2..4 every row equals the single-row matvec of that row bit for bit.
 """
 import zlib
 
@@ -53,7 +54,8 @@ def run(q4, W, S, B, X):
 SHAPES = [("qwen3_qkv", 6144, 2560, 1), ("qwen3_gate_up", 19456, 2560, 1),
           ("qwen3_down", 2560, 9728, 1), ("ragged", 333, 640, 1), ("one_group", 5, 64, 1),
           ("qwen3_qkv", 6144, 2560, 8), ("qwen3_down", 2560, 9728, 2), ("ragged", 333, 640, 2),
-          ("ragged", 333, 640, 17), ("one_group", 5, 64, 8)]
+          ("ragged", 333, 640, 17), ("one_group", 5, 64, 8), ("qwen3_qkv", 6144, 2560, 4),
+          ("qwen3_gate_up", 19456, 2560, 3)]
 
 
 @pytest.mark.parametrize("name,n,k,m", SHAPES, ids=["%s-M%d" % (s[0], s[3]) for s in SHAPES])
@@ -86,3 +88,17 @@ def test_affine_gate_rejects_a_dropped_bias(o, q4):
     assert within(y, o.gemv_affine(W, S, B, X))
     bad = oracle_pins.mutant("affine_bias_dropped")
     assert not within(y, bad.gemv_affine(W, S, B, X))
+
+
+@pytest.mark.parametrize("n,k,m", [(6144, 2560, 2), (19456, 2560, 4), (2560, 4096, 3), (333, 640, 4)])
+def test_affine_few_rows_equal_single_row_matvecs(q4, n, k, m):
+    """M = 2..4 (M K <= 16384) runs the single-row affine arithmetic per row."""
+    W, S, B, X = make("rows_%d_%d_%d" % (n, k, m), n, k, m)
+    Wd, Sd, Bd = dev_tensor(W), dev_tensor(S), dev_tensor(B)
+    Y = q4.gemv_affine(Wd, Sd, Bd, dev_tensor(X))
+    singles = [q4.gemv_affine(Wd, Sd, Bd, dev_tensor(X[i])) for i in range(m)]
+    import torch
+    torch.cuda.synchronize()
+    b = bits(Y)
+    for i in range(m):
+        assert np.array_equal(b[i], bits(singles[i])), i

@@ -1,7 +1,9 @@
 """GPU parity of q4_gemv_batched and q4_moe_gemv against the oracle.
 
 Batched: the Qwen3-4B matrices at batch 8 (8 independent activation rows),
-ragged and larger M, identical rows giving identical outputs.
+ragged and larger M, identical rows giving identical outputs; at M = 2..4
+(the dot2 kernel) every row equals the single-row matvec of that row bit for
+bit.
 MoE: 128 experts with gate_up 1536 x 2048 and down 2048 x 768, top-8 routing at
 token batches 1, 4 and 16 (both stages, combined by routing weight), plus
 small cases with repeated experts and an out-of-range id.
@@ -42,6 +44,11 @@ BATCHED = [
     ("ragged_m13", 37, 96, 13),
     ("m64", 300, 512, 64),
     ("m3_kmax", 33, 24576, 3),
+    ("phi3_qkv_m2", 9216, 3072, 2),
+    ("phi3_gate_up_m4", 16384, 3072, 4),
+    ("phi3_down_m2", 3072, 8192, 2),
+    ("qwen3_qkv_m3", 6144, 2560, 3),
+    ("ragged_m4", 37, 96, 4),
 ]
 
 
@@ -78,6 +85,24 @@ def test_batched_identical_rows(o, q4):
     sync()
     b = bits(Y)
     assert all(np.array_equal(b[0], b[i]) for i in range(8))
+
+
+@pytest.mark.parametrize("n,k,m", [(9216, 3072, 2), (16384, 3072, 3), (3072, 3072, 4),
+                                   (3072, 8192, 2), (6144, 2560, 4), (37, 96, 3)])
+def test_batched_few_rows_equal_single_row_matvecs(q4, n, k, m):
+    """M = 2..4 (M K <= 16384) runs the single-row kernel's arithmetic per row:
+    every row equals q4_gemv of that row bit for bit."""
+    seed = 950 + n + k + m
+    W = datagen.words(seed, n, k)
+    S = datagen.scales(seed + 1, n, k)
+    X = datagen.activations(seed + 2, m, k)
+    Wd, Sd = dev_tensor(W), dev_tensor(S)
+    Y = q4.gemv_batched(Wd, Sd, dev_tensor(X))
+    singles = [q4.gemv(Wd, Sd, dev_tensor(X[i])) for i in range(m)]
+    sync()
+    b = bits(Y)
+    for i in range(m):
+        assert np.array_equal(b[i], bits(singles[i])), i
 
 
 def test_batched_strided_rows(o, q4):
