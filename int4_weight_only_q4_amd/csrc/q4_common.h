@@ -170,7 +170,7 @@ q4_status launch_gemm(const uint32_t *W, const uint16_t *S, const uint16_t *X, i
                       uint16_t *Y, int64_t ldy, int N, int K, int M, bool exact,
                       hipStream_t stream, const uint16_t *bias = nullptr);
 // M = 2..4 activation rows with the single-row kernel's arithmetic per row
-// (bit-identical to M single-row matvecs) when M * K <= 16384 (staging in LDS).
+// (bit-identical to M single-row matvecs) when M * K <= 24576 (staging in LDS).
 bool gemv_rows_fits(int M, int K);
 q4_status launch_gemv_rows(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
                            uint16_t *y, int64_t ldy, int N, int K, int M, hipStream_t stream,

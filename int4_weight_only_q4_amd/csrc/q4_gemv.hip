@@ -618,7 +618,7 @@ q4_status launch_gemv(const uint32_t *W, const uint16_t *S, const uint16_t *x, u
 
 // Batched matvec: M = 1 is the matvec above; M >= 2 rows share each weight
 // read on the matrix cores (q4_mfma.hip).
-bool gemv_rows_fits(int M, int K) { return M >= 2 && M <= kMaxRowsDot && M * K <= 16384; }
+bool gemv_rows_fits(int M, int K) { return M >= 2 && M <= kMaxRowsDot && M * K <= 24576; }
 
 q4_status launch_gemv_rows(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
                            uint16_t *y, int64_t ldy, int N, int K, int M, hipStream_t stream,

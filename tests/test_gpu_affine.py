@@ -90,9 +90,10 @@ def test_affine_gate_rejects_a_dropped_bias(o, q4):
     assert not within(y, bad.gemv_affine(W, S, B, X))
 
 
-@pytest.mark.parametrize("n,k,m", [(6144, 2560, 2), (19456, 2560, 4), (2560, 4096, 3), (333, 640, 4)])
+@pytest.mark.parametrize("n,k,m", [(6144, 2560, 2), (19456, 2560, 4), (2560, 4096, 3), (333, 640, 4),
+                                   (2560, 9728, 2)])
 def test_affine_few_rows_equal_single_row_matvecs(q4, n, k, m):
-    """M = 2..4 (M K <= 16384) runs the single-row affine arithmetic per row."""
+    """M = 2..4 (M K <= 24576) runs the single-row affine arithmetic per row."""
     W, S, B, X = make("rows_%d_%d_%d" % (n, k, m), n, k, m)
     Wd, Sd, Bd = dev_tensor(W), dev_tensor(S), dev_tensor(B)
     Y = q4.gemv_affine(Wd, Sd, Bd, dev_tensor(X))

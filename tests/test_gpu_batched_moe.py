@@ -88,9 +88,10 @@ def test_batched_identical_rows(o, q4):
 
 
 @pytest.mark.parametrize("n,k,m", [(9216, 3072, 2), (16384, 3072, 3), (3072, 3072, 4),
-                                   (3072, 8192, 2), (6144, 2560, 4), (37, 96, 3)])
+                                   (3072, 8192, 2), (3072, 8192, 3), (2560, 9728, 2),
+                                   (6144, 2560, 4), (37, 96, 3)])
 def test_batched_few_rows_equal_single_row_matvecs(q4, n, k, m):
-    """M = 2..4 (M K <= 16384) runs the single-row kernel's arithmetic per row:
+    """M = 2..4 (M K <= 24576) runs the single-row kernel's arithmetic per row:
     every row equals q4_gemv of that row bit for bit."""
     seed = 950 + n + k + m
     W = datagen.words(seed, n, k)
