@@ -377,7 +377,7 @@ def gemv_table(q4, torch):
     # LM head with f32 logits and the greedy token (the whole call: matvec and
     # argmax kernels); the Qwen3-4B head is tied to the embedding matrix
     for j, (workload, n, k, ms) in enumerate([("Phi-3-mini LM head", 32064, 3072, [1]),
-                                             ("Qwen3-4B LM head", 151936, 2560, [1, 8])]):
+                                             ("Qwen3-4B LM head", 151936, 2560, [1, 2, 4, 8])]):
         rot = _rotation(torch, n, k, base + 2500 + 10 * j)
         wb = n * k * BPW
         for m in ms:

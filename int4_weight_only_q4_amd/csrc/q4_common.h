@@ -172,9 +172,10 @@ q4_status launch_gemm(const uint32_t *W, const uint16_t *S, const uint16_t *X, i
 // M = 2..4 activation rows with the single-row kernel's arithmetic per row
 // (bit-identical to M single-row matvecs) when M * K <= 24576 (staging in LDS).
 bool gemv_rows_fits(int M, int K);
+// (yf set: f32 outputs there, y ignored)
 q4_status launch_gemv_rows(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
                            uint16_t *y, int64_t ldy, int N, int K, int M, hipStream_t stream,
-                           const uint16_t *bias = nullptr);
+                           const uint16_t *bias = nullptr, float *yf = nullptr);
 q4_status launch_gemv_batched(const uint32_t *W, const uint16_t *S, const uint16_t *x,
                               int64_t ldx, uint16_t *y, int64_t ldy, int N, int K, int M,
                               hipStream_t stream);

@@ -270,8 +270,8 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams a)
     }
 }
 
-// MR activation rows (2..4) against the same weights, plain f16 outputs
-// y[m * ldy + n]: the single-row kernel's loads, unpack and arithmetic per
+// MR activation rows (2..4) against the same weights, f16 outputs
+// y[m * ldy + n] (or f32 ones in yf when set): the single-row kernel's loads, unpack and arithmetic per
 // activation row (each nibble pair's dot2 issued once per row), so every row's
 // result equals the single-row matvec of that row bit for bit. The MR rows are
 // staged one after another in LDS (pair order, group sums). AFF: the MLX
@@ -373,8 +373,12 @@ __global__ __launch_bounds__(256) void k_gemv_rows(GemvParams a, int64_t ldx, in
         for (int r = 0; r < RPS; ++r)
             if (ok[r])
 #pragma unroll
-                for (int m = 0; m < MR; ++m)
-                    a.y[m * ldy + row[r]] = f2h(acc[r][m]);
+                for (int m = 0; m < MR; ++m) {
+                    if (a.yf)  // f32 outputs (the LM head's logits)
+                        a.yf[m * ldy + row[r]] = acc[r][m];
+                    else
+                        a.y[m * ldy + row[r]] = f2h(acc[r][m]);
+                }
 }
 
 struct Cfg {
@@ -622,12 +626,13 @@ bool gemv_rows_fits(int M, int K) { return M >= 2 && M <= kMaxRowsDot && M * K <
 
 q4_status launch_gemv_rows(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
                            uint16_t *y, int64_t ldy, int N, int K, int M, hipStream_t stream,
-                           const uint16_t *bias)
+                           const uint16_t *bias, float *yf)
 {
     GemvParams p{};
     p.W = reinterpret_cast<const uint4 *>(W);
     p.S = S;
     p.Bias = bias;
+    p.yf = yf;
     p.N = N;
     p.G = K / 32;
     p.x = x;

@@ -173,6 +173,8 @@ q4_status launch_gemv_f32(const uint32_t *W, const uint16_t *S, const uint16_t *
         op.yf = y;
         return launch_gemv_op(op, stream);
     }
+    if (gemv_rows_fits(M, K))  // a few rows: the single-row arithmetic per row
+        return launch_gemv_rows(W, S, x, ldx, nullptr, ldy, N, K, M, stream, nullptr, y);
     return launch_gemv_mfma(W, S, x, ldx, nullptr, y, ldy, N, K, M, stream);
 }
 
@@ -207,6 +209,14 @@ q4_status launch_lm_head_argmax(const uint32_t *W, const uint16_t *S, const uint
                                 int64_t ldx, float *logits, int64_t ldl, int32_t *tokens, int N,
                                 int K, int M, hipStream_t stream)
 {
+    if (M > 1 && gemv_rows_fits(M, K)) {
+        // a few rows: their f32 logits as M single-row matvecs, then the argmax
+        q4_status st = launch_gemv_rows(W, S, x, ldx, nullptr, ldl, N, K, M, stream, nullptr,
+                                        logits);
+        if (st != Q4_OK)
+            return st;
+        return launch_argmax(logits, ldl, N, M, tokens, stream);
+    }
     if (M > 1) {
         // per launch of up to 16 rows: the matrix-core partials, then their sum
         // in split order fused with the first argmax pass (or, without a K

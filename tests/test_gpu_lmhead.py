@@ -208,6 +208,21 @@ def test_lm_head_argmax_qwen3_tied_m8_sampled(o, q4):
         check_token(int(tk[b]), lg[b], ref, "row %d" % b)
 
 
+@pytest.mark.parametrize("n,k,m", [(32064, 3072, 3), (151936, 2560, 2), (1001, 96, 4)])
+def test_lm_head_few_rows_equal_single_rows(o, q4, n, k, m):
+    """M = 2..4 runs the single-row arithmetic per row: each row's f32 logits and
+    token equal those of the M = 1 LM head on that row, bit for bit."""
+    W, S, X = make(o, "few_rows_%d" % n, n, k, m)
+    Wd, Sd = dev_tensor(W), dev_tensor(S)
+    logits, tok = q4.lm_head_argmax(Wd, Sd, dev_tensor(X))
+    singles = [q4.lm_head_argmax(Wd, Sd, dev_tensor(X[i])) for i in range(m)]
+    sync()
+    lg, tk = host(logits), host(tok)
+    for i in range(m):
+        assert np.array_equal(lg[i].view(np.uint32), host(singles[i][0]).view(np.uint32)), i
+        assert int(tk[i]) == int(host(singles[i][1])[0]), i
+
+
 def test_lm_head_planted_maximum(o, q4):
     """All weights zero except two identical rows of codes 15 and x > 0: the
     token is the first of them, wherever it falls among the workgroups."""
