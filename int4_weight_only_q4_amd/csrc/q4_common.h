@@ -130,6 +130,18 @@ q4_status launch_moe_mfma(const uint32_t *W, const uint16_t *S, const int32_t *i
                           int64_t ldx, int64_t x_slot_stride, uint16_t *y, float *part, int E,
                           int N, int K, int T, int TOPK, int mode, hipStream_t stream);
 size_t moe_part_bytes(int N, int K, int P);
+// The outputs of an expert stage from per-pair f32 partials part[ks][pair][n]
+// (KS splits), per mode (q4_mfma.hip).
+q4_status launch_moe_finish(int mode, const float *part, int KS, int P, int N,
+                            const int32_t *ids, const uint16_t *route_w, uint16_t *y, int E,
+                            int T, int TOPK, hipStream_t stream);
+// Expert matvecs with the single-row arithmetic per (token, slot) pair (q4_gemv.hip):
+// per-pair f32 results part[pair][n]; routing from meta, or in each workgroup
+// when meta == nullptr (moe_routes_in_kernel).
+q4_status launch_moe_rows(const uint32_t *W, const uint16_t *S, const int32_t *ids,
+                          const int32_t *meta, const uint16_t *x, int64_t ldx,
+                          int64_t x_slot_stride, float *part, int E, int N, int K, int T,
+                          int TOPK, hipStream_t stream);
 // Whether the expert kernel routes by itself (meta == nullptr) for P pairs and E experts.
 bool moe_routes_in_kernel(int P, int E);
 // M >= 2 rows on the matrix cores (q4_mfma.hip): f16 outputs y, or f32

@@ -20,7 +20,10 @@
 //    scale in f32. A one-hot x therefore reproduces (c - 7) * s exactly.
 //  * The LPR partial sums of a row are combined in a fixed order by DPP and
 //    permlane steps (no LDS round trips), so results are identical run to run.
+#include <algorithm>
+
 #include "q4_dequant.h"
+#include "q4_moe_route.h"
 #include "q4_stack.h"
 
 namespace q4 {
@@ -381,6 +384,152 @@ __global__ __launch_bounds__(256) void k_gemv_rows(GemvParams a, int64_t ldx, in
                 }
 }
 
+// MoE expert stage with the single-row arithmetic per (token, slot) pair:
+// grid (row blocks, 1, P), P <= 256. The distinct experts of the routing
+// (k_moe_route's meta, or each workgroup's own when meta == nullptr) own
+// ceil(pairs / MR) units of at most MR of their pairs; blockIdx.z is a unit
+// (P bounds their number). The workgroup runs its unit's pairs through its rows of the expert,
+// each pair with k_gemv_rows' arithmetic (activations staged in LDS), and
+// writes the per-pair f32 results part[pair][n] (k_moe_finish forms the
+// stage's outputs).
+template <int LPR, int NG, int RPS>
+__global__ __launch_bounds__(256) void k_moe_rows(const uint4 *__restrict__ Wall,
+                                                  const uint16_t *__restrict__ Sall,
+                                                  const int32_t *__restrict__ ids, int E,
+                                                  const int32_t *__restrict__ meta, int P,
+                                                  const uint16_t *__restrict__ x, int64_t ldx,
+                                                  int64_t slot_stride, int TOPK,
+                                                  float *__restrict__ part, int N, int G)
+{
+    constexpr int MR = kMaxRowsDot;
+    constexpr int SPW = 64 / LPR;
+    constexpr int RB = kWaves * SPW * RPS;
+    constexpr int XCH = (LPR * NG + 63) / 64;
+    extern __shared__ uint4 smem[];
+    __shared__ int s_cnt[kFuseExperts];
+    __shared__ int s_pairs[kFusePairs];
+    __shared__ int s_np;
+    const int u = blockIdx.z;
+    int e, q0, q1;
+    const int32_t *order;
+    if (meta) {
+        // the unit's expert: thread k holds listed expert k's unit count (at
+        // most P <= 256 experts are listed), a block scan places unit u
+        __shared__ int s_red[4], s_k, s_first;
+        const int nd = meta[0], t = threadIdx.x;
+        const int uk = t < nd ? (meta[1 + P + t + 1] - meta[1 + P + t] + MR - 1) / MR : 0;
+        if (t == 0)
+            s_k = -1;
+        int total;
+        const int before = block_exclusive_scan(uk, s_red, &total);
+        if (u >= before && u < before + uk) {
+            s_k = t;
+            s_first = (u - before) * MR;
+        }
+        __syncthreads();
+        const int k = s_k;
+        if (k < 0)  // fewer units than slots: the whole workgroup leaves
+            return;
+        e = meta[1 + k];
+        q0 = meta[1 + P + k] + s_first;
+        q1 = min(q0 + MR, meta[1 + P + k + 1]);
+        order = meta + 2 + 2 * P;
+    } else {
+        e = route_in_workgroup(ids, P, E, u, MR, s_cnt, s_pairs, &s_np, &q0);
+        if (e < 0)
+            return;
+        q1 = min(q0 + MR, s_np);
+        order = s_pairs;
+    }
+    const int nr = q1 - q0;  // 1..MR pairs
+    const int K = G * 32, chunks = K >> 3;
+    const int stride = chunks + G / 4 + 1;  // uint4 units per staged row
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int seg = lane / LPR, j = lane % LPR;
+    const uint4 *W = Wall + (size_t)e * N * G;
+    const uint16_t *S = Sall + (size_t)e * N * G;
+
+    // activation rows first (the pairs' rows; missing ones repeat the last)
+    uint4 xr[MR][XCH];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        const int pr = order[q0 + min(m, nr - 1)];
+        const uint16_t *xp = x + (int64_t)(pr / TOPK) * ldx + (int64_t)(pr % TOPK) * slot_stride;
+#pragma unroll
+        for (int q = 0; q < XCH; ++q) {
+            const int c = tid + 256 * q;
+            if (c < chunks)
+                xr[m][q] = reinterpret_cast<const uint4 *>(xp)[c];
+        }
+    }
+    int row[RPS];
+    bool ok[RPS];
+#pragma unroll
+    for (int r = 0; r < RPS; ++r) {
+        const int rr = blockIdx.x * RB + (wave * SPW + seg) * RPS + r;
+        ok[r] = rr < N;
+        row[r] = ok[r] ? rr : 0;
+    }
+    uint4 wv[NG][RPS];
+    uint32_t sv[NG][RPS];
+#pragma unroll
+    for (int i = 0; i < NG; ++i)
+#pragma unroll
+        for (int r = 0; r < RPS; ++r) {
+            const int g = min(j + LPR * i, G - 1);
+            const size_t off = (size_t)row[r] * G + g;
+            wv[i][r] = load_weights(W + off);
+            sv[i][r] = load_scale(S + off);
+        }
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        uint4 *xs = smem + m * stride;
+        float *cs = reinterpret_cast<float *>(xs + chunks);
+#pragma unroll
+        for (int q = 0; q < XCH; ++q) {
+            const int c = tid + 256 * q;
+            put_chunk(xr[m][q], c, c < chunks, xs, cs);
+        }
+    }
+    __syncthreads();
+
+    float acc[RPS][MR];
+#pragma unroll
+    for (int r = 0; r < RPS; ++r)
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+            acc[r][m] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+        const int g = j + LPR * i;
+        if (g < G) {
+#pragma unroll
+            for (int r = 0; r < RPS; ++r) {
+                const float s = h2f(sv[i][r]);
+#pragma unroll
+                for (int m = 0; m < MR; ++m) {
+                    const uint4 *xs = smem + m * stride;
+                    const float sx = reinterpret_cast<const float *>(xs + chunks)[g];
+                    acc[r][m] = fmaf(s, group_dot(wv[i][r], xs, g, sx), acc[r][m]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < RPS; ++r)
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+            acc[r][m] = segment_sum(acc[r][m], LPR);
+    if (j == 0)
+#pragma unroll
+        for (int r = 0; r < RPS; ++r)
+            if (ok[r])
+#pragma unroll
+                for (int m = 0; m < MR; ++m)
+                    if (m < nr)
+                        part[(size_t)order[q0 + m] * N + row[r]] = acc[r][m];
+}
+
 struct Cfg {
     int lpr, ng;
 };
@@ -514,7 +663,88 @@ q4_status rows_lpr(const Cfg &c, const GemvParams &p, int64_t ldx, int64_t ldy, 
     }
 }
 
+struct MoeRowsArgs {
+    const uint4 *W;
+    const uint16_t *S;
+    const int32_t *ids, *meta;
+    const uint16_t *x;
+    int64_t ldx, slot_stride;
+    float *part;
+    int E, N, G, P, TOPK, slots;
+};
+
+template <int LPR, int NG>
+q4_status run_moe_rows(const MoeRowsArgs &a, hipStream_t st)
+{
+    constexpr int RPS = rows_per_segment(NG);
+    constexpr int RB = kWaves * (64 / LPR) * RPS;
+    const size_t lds = (size_t)kMaxRowsDot * (a.G * 4 + a.G / 4 + 1) * 16;
+    Q4_LAUNCH_MATVEC((k_moe_rows<LPR, NG, RPS>), dim3((a.N + RB - 1) / RB, 1, a.slots), dim3(256),
+                     lds, st, a.W, a.S, a.ids, a.E, a.meta, a.P, a.x, a.ldx, a.slot_stride, a.TOPK,
+                     a.part, a.N, a.G);
+    return check_launch("k_moe_rows");
+}
+
+template <int LPR>
+q4_status moe_rows_ng(int ng, const MoeRowsArgs &a, hipStream_t st)
+{
+    switch (ng) {
+    case 1: return run_moe_rows<LPR, 1>(a, st);
+    case 2: return run_moe_rows<LPR, 2>(a, st);
+    case 3: return run_moe_rows<LPR, 3>(a, st);
+    case 4: return run_moe_rows<LPR, 4>(a, st);
+    case 5: return run_moe_rows<LPR, 5>(a, st);
+    case 6: return run_moe_rows<LPR, 6>(a, st);
+    case 7: return run_moe_rows<LPR, 7>(a, st);
+    case 8: return run_moe_rows<LPR, 8>(a, st);
+    default: break;
+    }
+    if constexpr (LPR == 64) {
+        switch (ng) {
+        case 9: return run_moe_rows<64, 9>(a, st);
+        case 10: return run_moe_rows<64, 10>(a, st);
+        case 11: return run_moe_rows<64, 11>(a, st);
+        case 12: return run_moe_rows<64, 12>(a, st);
+        default: break;
+        }
+    }
+    return fail(Q4_ERANGE, "no matvec configuration for %d groups per lane", ng);
+}
+
 }  // namespace
+
+q4_status launch_moe_rows(const uint32_t *W, const uint16_t *S, const int32_t *ids,
+                          const int32_t *meta, const uint16_t *x, int64_t ldx,
+                          int64_t x_slot_stride, float *part, int E, int N, int K, int T,
+                          int TOPK, hipStream_t stream)
+{
+    MoeRowsArgs a;
+    a.W = reinterpret_cast<const uint4 *>(W);
+    a.S = S;
+    a.ids = ids;
+    a.meta = meta;
+    a.x = x;
+    a.ldx = ldx;
+    a.slot_stride = x_slot_stride;
+    a.part = part;
+    a.E = E;
+    a.N = N;
+    a.G = K / 32;
+    a.P = T * TOPK;
+    a.TOPK = TOPK;
+    if (a.P > kFusePairs)
+        return fail(Q4_ERANGE, "the dot2 expert kernel takes at most %d pairs (got %d)",
+                    kFusePairs, a.P);
+    a.slots = a.P;  // units of at most kMaxRowsDot pairs: never more than the pairs
+    const Cfg c = choose_cfg(a.G);
+    switch (c.lpr) {
+    case 64: return moe_rows_ng<64>(c.ng, a, stream);
+    case 32: return moe_rows_ng<32>(c.ng, a, stream);
+    case 16: return moe_rows_ng<16>(c.ng, a, stream);
+    case 8: return moe_rows_ng<8>(c.ng, a, stream);
+    default: return fail(Q4_ERANGE, "no matvec configuration for K = %d", K);
+    }
+}
 
 int matvec_blocks(int N, int K)
 {

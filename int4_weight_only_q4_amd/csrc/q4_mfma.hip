@@ -27,6 +27,7 @@
 #include <algorithm>
 
 #include "q4_dequant.h"
+#include "q4_moe_route.h"
 
 namespace q4 {
 namespace {
@@ -303,86 +304,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
         });
 }
 
-// Block-wide exclusive prefix sum over 256 threads (wave scans, then the wave
-// totals); `red` is 4 ints of LDS. Returns the prefix, *total the sum.
-__device__ __forceinline__ int block_exclusive_scan(int v, int *red, int *total)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off, 64);
-        if (lane >= off)
-            incl += o;
-    }
-    if (lane == 63)
-        red[wave] = incl;
-    __syncthreads();
-    int before = 0, sum = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        before += w < wave ? red[w] : 0;
-        sum += red[w];
-    }
-    __syncthreads();
-    *total = sum;
-    return before + incl - v;
-}
-
-// Routing of one workgroup when the pairs and experts are few (P <= kFusePairs,
-// E <= kFuseExperts): the d-th distinct expert (in increasing id order) of the
-// valid ids and its pairs in pair order, as k_moe_route would list them.
-// Returns the expert, or -1 when there are d or fewer distinct experts.
-constexpr int kFusePairs = 256;
-constexpr int kFuseExperts = 1024;
-__device__ int route_in_workgroup(const int32_t *__restrict__ ids, int P, int E, int d,
-                                  int *cnt, int *pairs, int *npairs)
-{
-    __shared__ int red[4];
-    __shared__ int s_e;
-    const int t = threadIdx.x;
-    for (int i = t; i < E; i += 256)
-        cnt[i] = 0;
-    if (t == 0)
-        s_e = -1;
-    __syncthreads();
-    const int my = t < P ? ids[t] : -1;
-    const bool valid = my >= 0 && my < E;
-    if (valid)
-        atomicAdd(&cnt[my], 1);
-    __syncthreads();
-    // thread t owns experts [4t, 4t + 4): the d-th present one is the expert
-    constexpr int kPer = kFuseExperts / 256;
-    int present = 0;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i)
-        present += (kPer * t + i < E && cnt[kPer * t + i] > 0) ? 1 : 0;
-    int total;
-    int rank = block_exclusive_scan(present, red, &total);
-    if (d >= rank && d < rank + present) {
-#pragma unroll
-        for (int i = 0; i < kPer; ++i)
-            if (kPer * t + i < E && cnt[kPer * t + i] > 0) {
-                if (rank == d)
-                    s_e = kPer * t + i;
-                ++rank;
-            }
-    }
-    __syncthreads();
-    const int e = s_e;
-    if (e < 0)
-        return -1;
-    // the expert's pairs in pair order
-    int n_e;
-    const int pos = block_exclusive_scan(valid && my == e ? 1 : 0, red, &n_e);
-    if (valid && my == e)
-        pairs[pos] = t;
-    if (t == 0)
-        *npairs = n_e;
-    __syncthreads();
-    return e;
-}
-
 // MoE expert stage: grid (ceil(ntiles / 4), KS, slots); blockIdx.z is a
 // distinct expert of the routing, whose pairs (token, slot) form the activation
 // rows, 16 at a time. The routing comes from k_moe_route (meta), or, for few
@@ -408,10 +329,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
         q1 = meta[1 + P + d + 1];
         order = meta + 2 + 2 * P;
     } else {
-        e = route_in_workgroup(ids, P, E, d, s_cnt, s_pairs, &s_np);
+        e = route_in_workgroup(ids, P, E, d, kFusePairs, s_cnt, s_pairs, &s_np, &q0);
         if (e < 0)
             return;
-        q0 = 0;
         q1 = s_np;
         order = s_pairs;
     }
@@ -593,6 +513,13 @@ q4_status launch_moe_mfma(const uint32_t *W, const uint16_t *S, const int32_t *i
     q4_status st = check_launch("k_moe_mfma");
     if (st != Q4_OK)
         return st;
+    return launch_moe_finish(mode, part, KS, P, N, ids, route_w, y, E, T, TOPK, stream);
+}
+
+q4_status launch_moe_finish(int mode, const float *part, int KS, int P, int N,
+                            const int32_t *ids, const uint16_t *route_w, uint16_t *y, int E,
+                            int T, int TOPK, hipStream_t stream)
+{
     const int64_t total = mode == kMoeCombine ? (int64_t)T * N
                                               : (int64_t)P * (mode == kMoeSilu ? N / 2 : N);
     hipLaunchKernelGGL(k_moe_finish, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,

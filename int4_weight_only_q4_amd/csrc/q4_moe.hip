@@ -23,6 +23,12 @@ namespace {
 
 enum { MOE_PER_SLOT = 0, MOE_SILU = 1, MOE_COMBINE = 2 };
 
+// The expert matvecs run the dot2 kernel (the single-row arithmetic per pair)
+// while the experts get about two pairs each or fewer (P <= 2 E), at most 256
+// pairs, and four activation rows fit the staging in LDS; the matrix cores
+// take larger batches. (128 experts, top 8: the dot2 kernel up to 32 tokens.)
+bool moe_rows_fits(int P, int E, int K) { return P <= 256 && P <= 2 * E && 4 * K <= 24576; }
+
 // Workspace layout (int32): [0] number of distinct experts, [1 .. P] expert of
 // each distinct slot (increasing id), [P+1 .. 2P+1] start of each slot's pairs
 // in `order`, [2P+2 .. 3P+1] order = pair indices sorted by (expert, pair).
@@ -110,6 +116,14 @@ q4_status launch_moe(const uint32_t *W, const uint16_t *S, const int32_t *ids,
         q4_status st = check_launch("k_moe_route");
         if (st != Q4_OK)
             return st;
+    }
+    if (moe_rows_fits(P, E, K)) {
+        // few pairs per expert: the single-row arithmetic per pair, then the outputs
+        q4_status st = launch_moe_rows(W, S, ids, meta, x, ldx, x_slot_stride, part, E, N, K, T,
+                                       TOPK, stream);
+        if (st != Q4_OK)
+            return st;
+        return launch_moe_finish(mode, part, 1, P, N, ids, route_w, y, E, T, TOPK, stream);
     }
     return launch_moe_mfma(W, S, ids, meta, route_w, x, ldx, x_slot_stride, y, part, E, N, K, T,
                            TOPK, mode, stream);

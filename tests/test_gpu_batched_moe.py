@@ -226,11 +226,14 @@ def test_batched_one_hot_rows_are_exact(o, q4, n, k, m):
         assert np.array_equal(Y[i], o.d2h(grp[:, ks[i] % 32]).view(np.uint16)), i
 
 
-@pytest.mark.parametrize("t,topk,e", [(40, 8, 32), (2, 4, 1100), (32, 8, 64)])
+@pytest.mark.parametrize("t,topk,e", [(40, 8, 32), (2, 4, 1100), (32, 8, 64), (32, 8, 1100)])
 def test_moe_routing_paths(o, q4, t, topk, e):
     """Routings beyond the in-kernel limit (more than 256 pairs, more than 1024
     experts) take the sorting kernel; 256 pairs exactly stay in the kernel.
-    Per-slot and combine modes against the oracle, repeated ids included."""
+    Few pairs per expert (at most two on average) take the dot2 expert kernel:
+    with the sorting kernel's list at 8 and 256 pairs (about 230 experts
+    listed), the matrix cores otherwise. Per-slot and combine modes against the
+    oracle, repeated ids included."""
     n, k = 48, 128
     W, S = experts(o, 1400 + e, e, n, k)
     ids = np.random.default_rng(e + t).integers(0, e, size=(t, topk)).astype(np.int32)
@@ -245,3 +248,37 @@ def test_moe_routing_paths(o, q4, t, topk, e):
                   "per-slot")
     assert_within(host(yc), o.moe_stage(W, S, ids, rw, x, topk * k, k, n, k, epi_silu=False),
                   "combine")
+
+
+@pytest.mark.parametrize("e", [12, 1100], ids=["in_kernel_routing", "sorted_routing"])
+def test_moe_few_tokens_expert_with_many_pairs(o, q4, e):
+    """Few tokens (the dot2 expert path) with one expert repeated into 12 pairs:
+    its pairs run in several units of at most 4. Per-slot and combine modes
+    against the oracle, an out-of-range id included; every valid per-slot
+    output equals the single-row matvec of its expert and activation, bit for
+    bit (the same arithmetic per pair). 1100 experts take the sorting kernel."""
+    n, k, topk = 80, 256, 6
+    W, S = experts(o, 1500 + e, e, n, k)
+    ids = np.array([[2, 2, 2, 2, 2, 2], [2, 2, 2, 1, 0, 4], [2, 3, 2, -1, 2, 1]], np.int32)
+    t = ids.shape[0]
+    rw = (np.random.default_rng(e).random((t, topk)) / topk).astype(np.float16)
+    x = datagen.activations(1501 + e, t * topk, k)
+    Wd, Sd, idsd, xd = dev_tensor(W), dev_tensor(S), dev_tensor(ids), dev_tensor(x)
+    yp = q4.moe_gemv(Wd, Sd, idsd, xd, ldx=topk * k, x_slot_stride=k)
+    yc = q4.moe_gemv(Wd, Sd, idsd, xd, ldx=topk * k, x_slot_stride=k, route_w=dev_tensor(rw))
+    singles = {}
+    for p, ex in enumerate(ids.reshape(-1)):
+        if 0 <= ex < e:
+            singles[p] = q4.gemv(Wd[ex], Sd[ex], xd[p])
+    sync()
+    ok = np.where((ids >= 0) & (ids < e), ids, 0).astype(np.int32)
+    w_eff = np.where((ids >= 0) & (ids < e), rw, np.float16(0))
+    ref_p = o.moe_stage(W, S, ok, None, x, topk * k, k, n, k, epi_silu=False)
+    ref_c = o.moe_stage(W, S, ok, w_eff, x, topk * k, k, n, k, epi_silu=False)
+    yph = host(yp).reshape(t * topk, n)
+    valid = ((ids >= 0) & (ids < e)).reshape(-1)
+    assert_within(yph[valid], ref_p.reshape(t * topk, n)[valid], "per-slot")
+    assert np.all(yph[~valid] == 0)
+    assert_within(host(yc), ref_c, "combine")
+    for p, y1 in singles.items():
+        assert np.array_equal(yph[p].view(np.uint16), bits(y1)), p
