@@ -696,6 +696,27 @@ def verify_one_token(q4, torch, stack, st, p, o, layers_checked=(0, 1)):
     return worst
 
 
+def measured_copy_gbs(torch, nbytes=1 << 30, reps=20):
+    """HBM bytes moved per second (read + write) by a plain device-to-device
+    copy of `nbytes`: the box's measured ceiling, reported beside the nominal
+    peak for information (it is not the roofline's peak)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    secs = e0.elapsed_time(e1) * 1e-3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / secs / 1e9
+
+
 def cpu_baseline(p, o, seconds=10.0):
     """The oracle (single-threaded C, binary64) on whole decode layers of the same
     stack, chained, until about `seconds` of CPU time has been spent."""
@@ -803,6 +824,7 @@ def main():
     gbs = wb / (ms * 1e-3) / 1e9
     dom_us, dom_bytes = time_dominant_kernel(q4, torch, stack, st, p)
     dom_gbs = dom_bytes / (dom_us * 1e-6) / 1e9
+    copy_gbs = measured_copy_gbs(torch)
 
     rec = {
         "metric": METRIC,
@@ -836,6 +858,9 @@ def main():
             "us_per_launch": round(dom_us, 3),
             "bytes_per_launch": int(dom_bytes),
             "traffic": committed_traffic(),
+            "measured_copy_gbs": round(copy_gbs, 1),
+            "measured_copy_note": "1 GiB device-to-device copy, read + write bytes per "
+                                  "second; informational, the peak is the nominal 8 TB/s",
         },
     }
     if not args.no_cpu_baseline:
