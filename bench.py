@@ -696,6 +696,46 @@ def verify_one_token(q4, torch, stack, st, p, o, layers_checked=(0, 1)):
     return worst
 
 
+def token_graphs(torch, stack, hs, r_out, warm=3):
+    """Two captured HIP graphs of one decode token each (the 129 kernel
+    launches of q4_stack_decode): graph a reads (residual, normalised) =
+    (hs[a], hs[a]) and writes hs[1 - a] (r_out takes the residual). They are
+    captured on a side stream after eager calls on that stream, so the
+    library's per-stream workspace exists before capture and the graphs hold
+    kernels only. Returns (stream, [graph0, graph1])."""
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        for _ in range(warm):  # same input each time: hs[0] is left as it was
+            stack.decode(hs[0], hs[0], r_out, hs[1])
+    torch.cuda.synchronize()
+    graphs = []
+    for a in (0, 1):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=st):
+            stack.decode(hs[a], hs[a], r_out, hs[1 - a])
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return st, graphs
+
+
+def check_graph_tokens(torch, stack, graphs, hs, r_out, n=3):
+    """n tokens replayed from the graphs equal n eager tokens from the same
+    state bit for bit; leaves the state in hs[n & 1]."""
+    d = hs[0].numel()
+    start = hs[0].clone()
+    e = [start.clone(), torch.empty_like(start)]
+    r_tmp = torch.empty(d, dtype=torch.float16, device="cuda")
+    for i in range(n):
+        stack.decode(e[i & 1], e[i & 1], r_tmp, e[(i + 1) & 1])
+    torch.cuda.synchronize()
+    for i in range(n):
+        graphs[i & 1].replay()
+    torch.cuda.synchronize()
+    if not torch.equal(hs[n & 1].view(torch.int16), e[n & 1].view(torch.int16)):
+        raise SystemExit("graph-replayed tokens differ from eager tokens")
+
+
 def measured_copy_gbs(torch, nbytes=1 << 30, reps=20):
     """HBM bytes moved per second (read + write) by a plain device-to-device
     copy of `nbytes`: the box's measured ceiling, reported beside the nominal
@@ -744,6 +784,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch each token's kernels from the host instead of replaying "
+                         "a captured graph of them")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--gemv-table", action="store_true",
                     help="measure the per-GEMV table (Phi-3, Qwen3 M=1/2/4/8, MoE) and exit")
@@ -798,25 +841,42 @@ def main():
     hs = [st["h0"].clone(), torch.empty(d, dtype=torch.float16, device="cuda")]
     stack.decode(st["r0"], st["h0"], r_out, hs[0])      # first token from the seeded state
 
-    def run(i0, count):
-        # token i+1 starts from (residual, normalised) = (h_i, h_i)
-        for i in range(i0, i0 + count):
-            a, b = i & 1, (i + 1) & 1
-            stack.decode(hs[a], hs[a], r_out, hs[b])
+    # token i+1 starts from (residual, normalised) = (h_i, h_i); the state
+    # alternates between hs[0] and hs[1]
+    tok = 0
+    if args.eager:
+        run_stream = torch.cuda.current_stream()
 
-    run(0, args.warmup)
+        def run(count):
+            nonlocal tok
+            for _ in range(count):
+                a = tok & 1
+                stack.decode(hs[a], hs[a], r_out, hs[1 - a])
+                tok += 1
+    else:
+        run_stream, graphs = token_graphs(torch, stack, hs, r_out)
+        check_graph_tokens(torch, stack, graphs, hs, r_out)
+        tok = 3
+
+        def run(count):
+            nonlocal tok
+            for _ in range(count):
+                graphs[tok & 1].replay()
+                tok += 1
+
+    run(args.warmup)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    e0.record()
-    run(args.warmup, args.steps)
-    e1.record()
+    e0.record(run_stream)
+    run(args.steps)
+    e1.record(run_stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall_ms = (t1 - t0) * 1e3 / args.steps
     gpu_ms = e0.elapsed_time(e1) / args.steps
     ms = max(wall_ms, gpu_ms)
-    h_last = hs[(args.warmup + args.steps) & 1].float()
+    h_last = hs[tok & 1].float()
     if not torch.isfinite(h_last).all() or float(h_last.abs().max()) == 0.0:
         raise SystemExit("timed output is not finite / all zero")
 
@@ -845,6 +905,8 @@ def main():
             "weight_bytes_per_token": wb,
             "us_per_token": round(ms * 1e3, 2),
             "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "launch": ("eager: 129 kernel launches per token" if args.eager else
+                       "one HIP graph per token (its 129 kernels), replayed"),
             "gpu_event_ms_per_token": round(gpu_ms, 6),
             "wall_ms_per_token": round(wall_ms, 6),
         },

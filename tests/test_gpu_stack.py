@@ -190,6 +190,35 @@ def test_persistent_equals_multi_kernel(o, q4, phi3, which):
     assert np.array_equal(np.asarray(c[1]).view(np.uint16), np.asarray(a[1]).view(np.uint16))
 
 
+@pytest.mark.parametrize("which", ["small", "phi3"])
+def test_stack_graph_replays_equal_eager(q4, phi3, which):
+    """The captured token graphs that bench.py replays: every replay (four,
+    alternating the two graphs, with eager calls and synchronisations between
+    them) gives the bits of the same token computed by eager calls."""
+    import torch
+    if which == "small":
+        p = SMALL
+        stack, st = bench.build_stack(q4, torch, p)
+    else:
+        p = bench.PHI3
+        stack, st = phi3
+    d = p["d"]
+    hs = [st["h0"].clone(), torch.empty_like(st["h0"])]
+    r_out = torch.empty(d, dtype=torch.float16, device="cuda")
+    _, graphs = bench.token_graphs(torch, stack, hs, r_out)
+    for rep in range(4):
+        a = rep & 1
+        h_ref = torch.empty_like(hs[0])
+        r_ref = torch.empty_like(hs[0])
+        stack.decode(hs[a], hs[a], r_ref, h_ref)
+        torch.cuda.synchronize()
+        graphs[a].replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(hs[1 - a]), bits(h_ref)), ("h", rep)
+        assert np.array_equal(bits(r_out), bits(r_ref)), ("r", rep)
+    assert np.all(np.isfinite(host(hs[0]).astype(np.float64)))
+
+
 # ---------------------------------------------------------------------------
 # the stack with the real attention step (q4_stack_decode_attn)
 # ---------------------------------------------------------------------------
