@@ -484,7 +484,8 @@ def gemv_table(q4, torch):
                          weight_bytes=int(wb), us_kernel=None, us_per_call=round(call_us, 3),
                          gbs=round(gbs, 1), pct_peak=round(100 * gbs / HBM_PEAK_GBS, 1),
                          note="%.2f unique experts per layer on average; time of both stages "
-                              "(5 kernels) back to back" % uniq))
+                              "back to back (an expert kernel and a finishing kernel each)"
+                              % uniq))
         print("  MoE T=%-2d %8.3f us/layer %8.1f GB/s (unique experts %.2f)" % (
             t, call_us, gbs, uniq), file=sys.stderr, flush=True)
     # Phi-3-mini decode token, 32 layers, with the real attention step over L
@@ -854,9 +855,10 @@ def main():
                 stack.decode(hs[a], hs[a], r_out, hs[1 - a])
                 tok += 1
     else:
-        run_stream, graphs = token_graphs(torch, stack, hs, r_out)
+        _, graphs = token_graphs(torch, stack, hs, r_out)
         check_graph_tokens(torch, stack, graphs, hs, r_out)
         tok = 3
+        run_stream = torch.cuda.current_stream()  # replay() launches on the current stream
 
         def run(count):
             nonlocal tok
