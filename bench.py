@@ -627,10 +627,10 @@ def write_prefill_table(rows):
             "`us` is the mean time per call over 40 calls back to back (a call whose grid would "
             "fill under half the GPU splits K: tile kernel + combine kernel); "
             "TFLOP/s = 2 M N K / us; the peak is the dense f16 "
-            "matrix-core figure (2.5 PFLOP/s). Exact weights take two MFMAs per product "
-            "(binary16 hi and lo of (q - 7) s), f16 weights one. The reference rows time "
-            "torch.mm on dense f16 weights of the same shape (back-to-back calls, event "
-            "timing), for context only.",
+            "matrix-core figure (2.5 PFLOP/s). Exact weights feed the codes q - 7 to the "
+            "matrix cores and scale each 32-value group sum by s in f32; f16 weights feed "
+            "f16((q - 7) s). The reference rows time torch.mm on dense f16 weights of the "
+            "same shape (back-to-back calls, event timing), for context only.",
             "",
             "| workload | matrix | M | us | TFLOP/s | % of f16 peak | path |",
             "|---|---|---|---|---|---|---|"]

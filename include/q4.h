@@ -206,11 +206,13 @@ q4_status q4_gemv_affine(const uint32_t *W, const uint16_t *S, const uint16_t *B
  * fragments with f32 accumulation):
  *   y[m*ldy + n] = f16( sum_k w[n][k] * x[m*ldx + k] ),  m = 0..M-1
  * with, by `weights`:
- *   Q4_GEMM_EXACT      w = (q - 7) * s exactly, as q4_gemv_batched;
+ *   Q4_GEMM_EXACT      w = (q - 7) * s exactly, as q4_gemv_batched (the
+ *                      codes enter the matrix cores, each 32-value group's
+ *                      f32 sum is scaled by s);
  *   Q4_GEMM_F16_WEIGHT w = f16((q - 7) * s): the dequantised weight rounded to
  *                      binary16, as the format's dequantization formula
  *                      computes it (Zero TVM Documentation, "Q4F16
- *                      quantization format"); half the matrix-core work.
+ *                      quantization format"); no per-group scaling of sums.
  * W, S as for q4_gemv; x f16 rows, 16-byte aligned, ldx % 8 == 0, ldx >= K;
  * y f16, 2-byte aligned, ldy >= N, caller-owned, not overlapping the inputs.
  * 1 <= M <= Q4_MAX_GEMM_M. f32 accumulation over all of K in an unspecified
@@ -229,9 +231,9 @@ q4_status q4_gemm(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64
  * GEMMs at the qwen3mlx chunk shapes):
  *   y[m*ldy + n] = f16( sum_k (S[n][k/64] * q[n][k] + B[n][k/64]) * x[m*ldx + k] )
  * W, S, B as for q4_gemv_affine (K % 64 == 0); x, y as for q4_gemm.
- * 1 <= M <= Q4_MAX_GEMM_M. Exact weights: s * q enters the matrix cores as
- * two binary16 terms and the bias as b * (sum of x over the group), the group
- * sums split into binary16 hi and lo. Uses the library workspace of the
+ * 1 <= M <= Q4_MAX_GEMM_M. Exact weights: the codes q enter the matrix cores
+ * and each 32-value sum is scaled by s; the bias enters as b * (sum of x over
+ * the group), the group sums split into binary16 hi and lo. Uses the library workspace of the
  * stream (the group sums, and f32 partials when K is split).
  */
 q4_status q4_gemm_affine(const uint32_t *W, const uint16_t *S, const uint16_t *B,

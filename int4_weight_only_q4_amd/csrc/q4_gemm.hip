@@ -9,12 +9,12 @@
 //  * workgroup tile: 64 activation rows x 128 weight rows; wave w owns weight
 //    rows [32 w, 32 w + 32) of the tile (two 16-row matrix-core tiles) and all
 //    four 16-row activation tiles, so each dequantised weight feeds four MFMAs;
-//  * the weights enter the matrix core exactly: w = (q - 7) * s is split into
-//    binary16 hi = f16(w) and lo = w - hi (exact: the product of a 4-bit
-//    integer and a binary16 scale has at most 15 significant bits), and both
-//    are multiplied with f32 accumulation, so the accumulator runs over all of
-//    K with no per-group arithmetic on the results (the page's matrix-unit
-//    kernel rounds the staged weights to f16 instead);
+//  * exact weights: the codes q - 7 (exact in binary16) enter the matrix
+//    core, one MFMA per 32-value group gives the group's f32 sum over the
+//    tile, and each lane (its output column is its weight row) adds s times
+//    it into its accumulator with one f32 FMA per element, so no dequantised
+//    weight is rounded (the page's matrix-unit kernel rounds the staged
+//    weights to f16: the f16-weight mode, which multiplies f16((q - 7) s));
 //  * a step covers four quantisation groups (128 values of K): lane (n, kb)
 //    loads group 4 p + kb of its weight row (16 bytes), a 4 x 4 transpose over
 //    the lane rows (permlane swaps) gives each lane row its word of every
@@ -27,8 +27,9 @@
 //    scale 0 and zero activations.
 // The MLX affine format (w = s * q + b, q unsigned, s and b per 64 codes; Zero
 // TVM Documentation, the Qwen3.6-35B-A3B entry; BENCH.md "Subgroup-matrix GEMM
-// graduated", the _affine variants) runs through the same loop with unsigned
-// codes and the scale of group g / 2; its bias term sum_g b[n][g] * xs[m][g],
+// graduated", the _affine variants) runs through the same exact loop with
+// unsigned codes and the scale of group g / 2 (applied per 32 values); its
+// bias term sum_g b[n][g] * xs[m][g],
 // xs[m][g] = the sum of row m's activations over group g, is a few more K steps
 // of the same matrix product: A = xs split into binary16 hi and lo halves (a
 // small kernel forms them), B = the binary16 biases.
@@ -74,14 +75,12 @@ __device__ __forceinline__ void broadcast_rows(uint32_t v, uint32_t (&out)[4])
     out[3] = q2;
 }
 
-// The 8 weights of word w, w = (q - 7) * s, in the pair order (e0, e4) (e1,
-// e5) (e2, e6) (e3, e7): EXACT gives binary16 hi = f16(w) and lo = w - hi,
-// otherwise hi = f16(w) alone. A nibble in mantissa bits 0..3 under exponent
-// field 25 is the binary16 1024 + q; in bits 4..7 under exponent field 21 it
-// is 64 + q, so one shift of the word by 8 reaches all four pairs.
-// AFF: unsigned codes (w = q * s; the affine bias is added separately).
-template <bool EXACT, bool AFF>
-__device__ __forceinline__ void weights_of(uint32_t w, half2v s2, half8 &hi, half8 &lo)
+// The 8 codes of word w as binary16 q - 7 (AFF: q), exact, in the pair order
+// (e0, e4) (e1, e5) (e2, e6) (e3, e7). A nibble in mantissa bits 0..3 under
+// exponent field 25 is the binary16 1024 + q; in bits 4..7 under exponent
+// field 21 it is 64 + q, so one shift of the word by 8 reaches all four pairs.
+template <bool AFF>
+__device__ __forceinline__ half8 codes_of(uint32_t w)
 {
     const half2v c1031 = {(_Float16)(AFF ? -1024.0f : -1031.0f), (_Float16)(AFF ? -1024.0f : -1031.0f)};
     const half2v c71 = {(_Float16)(AFF ? -64.0f : -71.0f), (_Float16)(AFF ? -64.0f : -71.0f)};
@@ -91,21 +90,31 @@ __device__ __forceinline__ void weights_of(uint32_t w, half2v s2, half8 &hi, hal
     asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(b[1]) : "v"(0x00F000F0u), "v"(w), "s"(0x54005400u));
     asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(b[2]) : "v"(0x000F000Fu), "v"(w8), "s"(0x64006400u));
     asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(b[3]) : "v"(0x00F000F0u), "v"(w8), "s"(0x54005400u));
+    half8 q;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const half2v q = __builtin_bit_cast(half2v, b[i]) + ((i & 1) ? c71 : c1031);  // exact q (- 7)
-        const half2v h = q * s2;
-        hi[2 * i] = h[0];
-        hi[2 * i + 1] = h[1];
-        if (EXACT) {
-            const half2v r = __builtin_elementwise_fma(q, s2, -h);
-            lo[2 * i] = r[0];
-            lo[2 * i + 1] = r[1];
-        }
+        const half2v v = __builtin_bit_cast(half2v, b[i]) + ((i & 1) ? c71 : c1031);
+        q[2 * i] = v[0];
+        q[2 * i + 1] = v[1];
     }
+    return q;
 }
 
-// A 16-byte chunk of 8 activations in the pair order of weights_of.
+// The 8 binary16 weights f16((q - 7) s) of word w, in the pair order of codes_of.
+__device__ __forceinline__ half8 f16_weights_of(uint32_t w, half2v s2)
+{
+    const half8 q = codes_of<false>(w);
+    half8 h;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const half2v p = half2v{q[2 * i], q[2 * i + 1]} * s2;
+        h[2 * i] = p[0];
+        h[2 * i + 1] = p[1];
+    }
+    return h;
+}
+
+// A 16-byte chunk of 8 activations in the pair order of codes_of.
 __device__ __forceinline__ u32x4 pair_order(u32x4 v)
 {
     return u32x4{__builtin_amdgcn_perm(v.z, v.x, 0x05040100u),
@@ -204,13 +213,48 @@ __device__ __forceinline__ void stage(_Float16 *buf, const StepLoads<MS> &L, int
     }
 }
 
-template <int MS, bool EXACT, bool AFF>
+// Weight modes: binary16 weights f16((q - 7) s) (kWF16), or exact products
+// (kWGroup): the codes q - 7 enter the matrix core as they are, one MFMA per
+// 32-value group gives that group's sum over the tile in f32, and the lane
+// (whose output column is its weight row) adds s times it into the
+// accumulator with one f32 FMA per element.
+enum : int { kWF16 = 0, kWGroup = 1 };
+
+template <int MS, int MODE, bool AFF>
 __device__ __forceinline__ void multiply(floatx4 (&acc)[MS][2], const _Float16 *cur,
                                          const StepWeights &P, int n, int kb)
 {
+    if constexpr (MODE == kWGroup) {
+        const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            half8 a[MS], bq[2];
+            __builtin_amdgcn_iglp_opt(1);  // interleave the matrix-core and LDS work
+#pragma unroll
+            for (int ms = 0; ms < MS; ++ms)
+                a[ms] = *reinterpret_cast<const half8 *>(cur + (16 * ms + n) * kAStride + 8 * kb +
+                                                         32 * tt);
+#pragma unroll
+            for (int ns = 0; ns < 2; ++ns)
+                bq[ns] = codes_of<AFF>(P.wt[ns][tt]);
+#pragma unroll
+            for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                for (int ns = 0; ns < 2; ++ns) {
+                    const floatx4 gsum =
+                        __builtin_amdgcn_mfma_f32_16x16x32_f16(a[ms], bq[ns], zero, 0, 0, 0);
+                    const float s = (float)P.s2[ns][tt][0];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[ms][ns][i] = fmaf(s, gsum[i], acc[ms][ns][i]);
+                }
+        }
+        return;
+    }
+    // kWF16 (symmetric codes only)
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-        half8 a[MS], bh[2], bl[2];
+        half8 a[MS], bh[2];
         __builtin_amdgcn_iglp_opt(1);  // interleave the matrix-core and LDS work
 #pragma unroll
         for (int ms = 0; ms < MS; ++ms)
@@ -218,21 +262,13 @@ __device__ __forceinline__ void multiply(floatx4 (&acc)[MS][2], const _Float16 *
                                                      32 * tt);
 #pragma unroll
         for (int ns = 0; ns < 2; ++ns)
-            weights_of<EXACT, AFF>(P.wt[ns][tt], P.s2[ns][tt], bh[ns], bl[ns]);
+            bh[ns] = f16_weights_of(P.wt[ns][tt], P.s2[ns][tt]);
 #pragma unroll
         for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
             for (int ns = 0; ns < 2; ++ns)
                 acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[ms], bh[ns], acc[ms][ns],
                                                                      0, 0, 0);
-        if (EXACT) {
-#pragma unroll
-            for (int ms = 0; ms < MS; ++ms)
-#pragma unroll
-                for (int ns = 0; ns < 2; ++ns)
-                    acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[ms], bl[ns],
-                                                                         acc[ms][ns], 0, 0, 0);
-        }
     }
 }
 
@@ -330,7 +366,7 @@ __global__ __launch_bounds__(256) void k_group_sums(const uint16_t *__restrict__
 // splits larger problems).
 // AFF: the affine format; S and Bias [N][G / 2]; XS the group sums of X
 // (k_group_sums, GP groups per half).
-template <int MS, bool EXACT, bool AFF>
+template <int MS, int MODE, bool AFF>
 __global__ __launch_bounds__(256, MS == 8 ? 2 : 3) void k_gemm_q4(
     const uint4 *__restrict__ W, const uint16_t *__restrict__ S, const uint16_t *__restrict__ X,
     int64_t ldx, uint16_t *__restrict__ Y, int64_t ldy, float *__restrict__ part, int M, int N,
@@ -390,14 +426,14 @@ __global__ __launch_bounds__(256, MS == 8 ? 2 : 3) void k_gemm_q4(
         prepare<MS, false>(P, L, 4 * st, kb, G);
         load_step<MS, AFF>(L, B, O, st + 1);
         __syncthreads();  // the tile is staged; the other buffer was last read before this
-        multiply<MS, EXACT, AFF>(acc, xs[st & 1], P, n, kb);
+        multiply<MS, MODE, AFF>(acc, xs[st & 1], P, n, kb);
     }
     {
         const int st = st1 - 1;  // groups past K only in the last step of the last split
         stage<MS, true>(xs[st & 1], L, 4 * st, G, t);
         prepare<MS, true>(P, L, 4 * st, kb, G);
         __syncthreads();
-        multiply<MS, EXACT, AFF>(acc, xs[st & 1], P, n, kb);
+        multiply<MS, MODE, AFF>(acc, xs[st & 1], P, n, kb);
     }
     }
     if (AFF && bs1 > steps)  // this split's share of the bias steps
@@ -502,13 +538,13 @@ q4_status launch_tiles(bool exact, dim3 grid, hipStream_t stream, const uint4 *w
 {
     const int bvec = bias && (G / 2) % 8 == 0 && reinterpret_cast<uintptr_t>(bias) % 16 == 0;
     if (bias)
-        Q4_LAUNCH_MATVEC((k_gemm_q4<MS, true, true>), grid, dim3(256), 0, stream, w, s, x, ldx,
+        Q4_LAUNCH_MATVEC((k_gemm_q4<MS, kWGroup, true>), grid, dim3(256), 0, stream, w, s, x, ldx,
                          y, ldy, part, M, N, G, sps, bias, xsum, gp, bvec);
     else if (exact)
-        Q4_LAUNCH_MATVEC((k_gemm_q4<MS, true, false>), grid, dim3(256), 0, stream, w, s, x, ldx,
+        Q4_LAUNCH_MATVEC((k_gemm_q4<MS, kWGroup, false>), grid, dim3(256), 0, stream, w, s, x, ldx,
                          y, ldy, part, M, N, G, sps, nullptr, nullptr, 0, 0);
     else
-        Q4_LAUNCH_MATVEC((k_gemm_q4<MS, false, false>), grid, dim3(256), 0, stream, w, s, x, ldx,
+        Q4_LAUNCH_MATVEC((k_gemm_q4<MS, kWF16, false>), grid, dim3(256), 0, stream, w, s, x, ldx,
                          y, ldy, part, M, N, G, sps, nullptr, nullptr, 0, 0);
     return check_launch("k_gemm_q4");
 }

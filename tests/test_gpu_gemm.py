@@ -5,8 +5,8 @@ oracle: gemv_batched (w = (q - 7) s exact) for Q4_GEMM_EXACT, gemv_w16 (w
 rounded to f16 first) for Q4_GEMM_F16_WEIGHT, which must also stay within the
 bar of the exact result. Bit-exact cases:
 * a one-hot activation row gives f16(w) (exact mode) or the f16 weight itself
-  (f16 mode) for every weight row, with scales small enough that the low half
-  of the exact split is a binary16 subnormal;
+  (f16 mode) for every weight row, with scales small enough that many of them
+  are binary16 subnormals;
 * every output row is independent of M and of the row's position in the batch
   (the same bits computed alone and inside a batch of 300) while the launch
   splits K the same way (here: two splits at every M).
@@ -94,7 +94,7 @@ def test_gemm_strided_rows(o, q4):
 @pytest.mark.parametrize("mode", [EXACT, F16W], ids=["exact", "f16w"])
 def test_gemm_one_hot_is_the_weight(o, q4, mode):
     """Row i of X is e_{k_i}: y[i][n] is f16 of the weight at (n, k_i). Scales in
-    [2^-12, 2^-8] put the low half of the split below the binary16 normal range."""
+    [2^-12, 2^-8] put many weights below the binary16 normal range."""
     n, k, m = 160, 512, 96
     codes = datagen.codes(901, n, k)
     W = o.pack(codes)
