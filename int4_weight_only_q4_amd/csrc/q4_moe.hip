@@ -17,6 +17,7 @@
 //      them over the slots in slot order with the routing weights; no
 //      floating-point atomics, so results are deterministic).
 #include "q4_dequant.h"
+#include "q4_moe_route.h"
 
 namespace q4 {
 namespace {
@@ -32,64 +33,71 @@ bool moe_rows_fits(int P, int E, int K) { return P <= 256 && P <= 2 * E && 4 * K
 // Workspace layout (int32): [0] number of distinct experts, [1 .. P] expert of
 // each distinct slot (increasing id), [P+1 .. 2P+1] start of each slot's pairs
 // in `order`, [2P+2 .. 3P+1] order = pair indices sorted by (expert, pair).
-// O(P^2) comparisons in one workgroup; P <= Q4_MAX_PAIRS.
+// One workgroup: a bitonic sort of the n (a power of two >= P) keys
+// (expert << 32 | pair) in LDS, invalid ids and padding keyed past every
+// valid pair, then a block scan over the run starts of the sorted experts.
+// P <= Q4_MAX_PAIRS.
 __global__ __launch_bounds__(256) void k_moe_route(const int32_t *__restrict__ ids, int P, int E,
-                                                   int32_t *__restrict__ meta)
+                                                   int n, int32_t *__restrict__ meta)
 {
-    extern __shared__ int32_t sid[];  // [P] expert or -1, then [P] first-occurrence flags
-    int32_t *firstocc = sid + P;
+    extern __shared__ unsigned long long key[];  // [n]
+    __shared__ int red[4];
     int32_t *distinct = meta + 1;
     int32_t *seg = meta + 1 + P;
     int32_t *order = meta + 2 + 2 * P;
-    __shared__ int s_nd, s_valid;
-    for (int p = threadIdx.x; p < P; p += 256) {
-        const int e = ids[p];
-        sid[p] = (e >= 0 && e < E) ? e : -1;
-    }
-    if (threadIdx.x == 0) {
-        s_nd = 0;
-        s_valid = 0;
-    }
-    __syncthreads();
-    for (int p = threadIdx.x; p < P; p += 256) {
-        const int e = sid[p];
-        bool first = e >= 0;
-        for (int q = 0; q < p && first; ++q)
-            first = sid[q] != e;
-        firstocc[p] = first;
+    const int t = threadIdx.x;
+    constexpr unsigned long long kNone = ~0ull;
+    for (int i = t; i < n; i += 256) {
+        unsigned long long k = kNone;
+        if (i < P) {
+            const int e = ids[i];
+            if (e >= 0 && e < E)
+                k = (unsigned long long)e << 32 | (unsigned)i;
+        }
+        key[i] = k;
     }
     __syncthreads();
-    int local_nd = 0, local_valid = 0;
-    for (int p = threadIdx.x; p < P; p += 256) {
-        const int e = sid[p];
-        if (e < 0)
-            continue;
-        int rank = 0, below = 0, slot = 0;
-        for (int q = 0; q < P; ++q) {
-            const int f = sid[q];
-            if (f < 0)
-                continue;
-            if (f < e) {
-                ++below;
-                slot += firstocc[q];
-            } else if (f == e && q < p) {
-                ++rank;
+    // ascending bitonic sort: stage (size, stride) compares element lo with
+    // lo + stride, ascending where lo & size == 0
+    for (int size = 2; size <= n; size <<= 1)
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = t; i < (n >> 1); i += 256) {
+                const int lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
+                const unsigned long long x = key[lo], y = key[hi];
+                if ((x > y) == ((lo & size) == 0)) {
+                    key[lo] = y;
+                    key[hi] = x;
+                }
             }
+            __syncthreads();
         }
-        order[below + rank] = p;
-        if (firstocc[p]) {
-            distinct[slot] = e;
-            seg[slot] = below;
-            ++local_nd;
-        }
-        ++local_valid;
+    // thread t owns sorted positions [c t, c t + c): its run starts and valid pairs
+    const int c = (n + 255) / 256, i0 = min(n, c * t), i1 = min(n, i0 + c);
+    int starts = 0, valid = 0;
+    for (int i = i0; i < i1; ++i) {
+        const unsigned long long k = key[i];
+        if (k == kNone)
+            break;
+        ++valid;
+        starts += (i == 0 || (key[i - 1] >> 32) != (k >> 32)) ? 1 : 0;
     }
-    atomicAdd(&s_nd, local_nd);
-    atomicAdd(&s_valid, local_valid);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        meta[0] = s_nd;
-        seg[s_nd] = s_valid;
+    int nd, nvalid;
+    int slot = block_exclusive_scan(starts, red, &nd);
+    block_exclusive_scan(valid, red, &nvalid);
+    for (int i = i0; i < i1; ++i) {
+        const unsigned long long k = key[i];
+        if (k == kNone)
+            break;
+        order[i] = (int32_t)(k & 0xFFFFFFFFu);
+        if (i == 0 || (key[i - 1] >> 32) != (k >> 32)) {
+            distinct[slot] = (int32_t)(k >> 32);
+            seg[slot] = i;
+            ++slot;
+        }
+    }
+    if (t == 0) {
+        meta[0] = nd;
+        seg[nd] = nvalid;
     }
 }
 
@@ -111,7 +119,10 @@ q4_status launch_moe(const uint32_t *W, const uint16_t *S, const int32_t *ids,
     int32_t *meta = in_kernel ? nullptr : reinterpret_cast<int32_t *>(ws + kWsHeader);
     float *part = reinterpret_cast<float *>(ws + kWsHeader + meta_bytes);
     if (!in_kernel) {
-        hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(256), (size_t)P * 8, stream, ids, P, E,
+        int n = 2;
+        while (n < P)
+            n <<= 1;
+        hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(256), (size_t)n * 8, stream, ids, P, E, n,
                            meta);
         q4_status st = check_launch("k_moe_route");
         if (st != Q4_OK)

@@ -282,3 +282,35 @@ def test_moe_few_tokens_expert_with_many_pairs(o, q4, e):
     assert_within(host(yc), ref_c, "combine")
     for p, y1 in singles.items():
         assert np.array_equal(yph[p].view(np.uint16), bits(y1)), p
+
+
+@pytest.mark.parametrize("t,topk,e", [(40, 8, 32), (64, 8, 128), (3, 6, 1100)])
+def test_moe_sorted_routing_with_invalid_ids(o, q4, t, topk, e):
+    """The sorting kernel's list (more than 256 pairs or more than 1024
+    experts) with out-of-range ids and one expert repeated within a token:
+    invalid pairs give zero per-slot outputs and no combine term, every other
+    output within the bar of the oracle."""
+    n, k = 64, 128
+    W, S = experts(o, 1600 + e + t, e, n, k)
+    rng = np.random.default_rng(1601 + t)
+    ids = rng.integers(0, e, size=(t, topk)).astype(np.int32)
+    ids[0, :3] = ids[0, 3]
+    ids[1, 1] = -1
+    ids[t - 1, topk - 1] = e
+    ids[t // 2, 0] = e + 5
+    rw = (rng.random((t, topk)) / topk).astype(np.float16)
+    x = datagen.activations(1602 + t, t * topk, k)
+    Wd, Sd, idsd, xd = dev_tensor(W), dev_tensor(S), dev_tensor(ids), dev_tensor(x)
+    yp = q4.moe_gemv(Wd, Sd, idsd, xd, ldx=topk * k, x_slot_stride=k)
+    yc = q4.moe_gemv(Wd, Sd, idsd, xd, ldx=topk * k, x_slot_stride=k, route_w=dev_tensor(rw))
+    sync()
+    valid = (ids >= 0) & (ids < e)
+    ok = np.where(valid, ids, 0).astype(np.int32)
+    w_eff = np.where(valid, rw, np.float16(0))
+    ref_p = o.moe_stage(W, S, ok, None, x, topk * k, k, n, k, epi_silu=False)
+    ref_c = o.moe_stage(W, S, ok, w_eff, x, topk * k, k, n, k, epi_silu=False)
+    yph = host(yp).reshape(t * topk, n)
+    v = valid.reshape(-1)
+    assert_within(yph[v], ref_p.reshape(t * topk, n)[v], "per-slot")
+    assert np.all(yph[~v] == 0)
+    assert_within(host(yc), ref_c, "combine")
