@@ -384,64 +384,21 @@ __global__ __launch_bounds__(256) void k_gemv_rows(GemvParams a, int64_t ldx, in
                 }
 }
 
-// MoE expert stage with the single-row arithmetic per (token, slot) pair:
-// grid (row blocks, 1, P), P <= 256. The distinct experts of the routing
-// (k_moe_route's meta, or each workgroup's own when meta == nullptr) own
-// ceil(pairs / MR) units of at most MR of their pairs; blockIdx.z is a unit
-// (P bounds their number). The workgroup runs its unit's pairs through its rows of the expert,
-// each pair with k_gemv_rows' arithmetic (activations staged in LDS), and
-// writes the per-pair f32 results part[pair][n] (k_moe_finish forms the
-// stage's outputs).
-template <int LPR, int NG, int RPS>
-__global__ __launch_bounds__(256) void k_moe_rows(const uint4 *__restrict__ Wall,
-                                                  const uint16_t *__restrict__ Sall,
-                                                  const int32_t *__restrict__ ids, int E,
-                                                  const int32_t *__restrict__ meta, int P,
-                                                  const uint16_t *__restrict__ x, int64_t ldx,
-                                                  int64_t slot_stride, int TOPK,
-                                                  float *__restrict__ part, int N, int G)
+// One unit of k_moe_rows: the nr <= MR pairs pairs[0 .. nr) of expert e
+// through this workgroup's rows (MR activation rows staged in LDS, missing
+// ones repeating the last pair; results stored for the nr pairs).
+template <int LPR, int NG, int RPS, int MR>
+__device__ __forceinline__ void moe_rows_unit(const uint4 *__restrict__ Wall,
+                                              const uint16_t *__restrict__ Sall, int e,
+                                              const int32_t *pairs, int nr,
+                                              const uint16_t *__restrict__ x, int64_t ldx,
+                                              int64_t slot_stride, int TOPK,
+                                              float *__restrict__ part, int N, int G)
 {
-    constexpr int MR = kMaxRowsDot;
     constexpr int SPW = 64 / LPR;
     constexpr int RB = kWaves * SPW * RPS;
     constexpr int XCH = (LPR * NG + 63) / 64;
     extern __shared__ uint4 smem[];
-    __shared__ int s_cnt[kFuseExperts];
-    __shared__ int s_pairs[kFusePairs];
-    __shared__ int s_np;
-    const int u = blockIdx.z;
-    int e, q0, q1;
-    const int32_t *order;
-    if (meta) {
-        // the unit's expert: thread k holds listed expert k's unit count (at
-        // most P <= 256 experts are listed), a block scan places unit u
-        __shared__ int s_red[4], s_k, s_first;
-        const int nd = meta[0], t = threadIdx.x;
-        const int uk = t < nd ? (meta[1 + P + t + 1] - meta[1 + P + t] + MR - 1) / MR : 0;
-        if (t == 0)
-            s_k = -1;
-        int total;
-        const int before = block_exclusive_scan(uk, s_red, &total);
-        if (u >= before && u < before + uk) {
-            s_k = t;
-            s_first = (u - before) * MR;
-        }
-        __syncthreads();
-        const int k = s_k;
-        if (k < 0)  // fewer units than slots: the whole workgroup leaves
-            return;
-        e = meta[1 + k];
-        q0 = meta[1 + P + k] + s_first;
-        q1 = min(q0 + MR, meta[1 + P + k + 1]);
-        order = meta + 2 + 2 * P;
-    } else {
-        e = route_in_workgroup(ids, P, E, u, MR, s_cnt, s_pairs, &s_np, &q0);
-        if (e < 0)
-            return;
-        q1 = min(q0 + MR, s_np);
-        order = s_pairs;
-    }
-    const int nr = q1 - q0;  // 1..MR pairs
     const int K = G * 32, chunks = K >> 3;
     const int stride = chunks + G / 4 + 1;  // uint4 units per staged row
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -453,7 +410,7 @@ __global__ __launch_bounds__(256) void k_moe_rows(const uint4 *__restrict__ Wall
     uint4 xr[MR][XCH];
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
-        const int pr = order[q0 + min(m, nr - 1)];
+        const int pr = pairs[min(m, nr - 1)];
         const uint16_t *xp = x + (int64_t)(pr / TOPK) * ldx + (int64_t)(pr % TOPK) * slot_stride;
 #pragma unroll
         for (int q = 0; q < XCH; ++q) {
@@ -527,7 +484,73 @@ __global__ __launch_bounds__(256) void k_moe_rows(const uint4 *__restrict__ Wall
 #pragma unroll
                 for (int m = 0; m < MR; ++m)
                     if (m < nr)
-                        part[(size_t)order[q0 + m] * N + row[r]] = acc[r][m];
+                        part[(size_t)pairs[m] * N + row[r]] = acc[r][m];
+}
+
+// MoE expert stage with the single-row arithmetic per (token, slot) pair:
+// grid (row blocks, 1, P), P <= 256. The distinct experts of the routing
+// (k_moe_route's meta, or each workgroup's own when meta == nullptr) own
+// ceil(pairs / MR) units of at most MR of their pairs; blockIdx.z is a unit
+// (P bounds their number). The workgroup runs its unit's pairs through its rows of the expert,
+// each pair with k_gemv_rows' arithmetic (activations staged in LDS), and
+// writes the per-pair f32 results part[pair][n] (k_moe_finish forms the
+// stage's outputs).
+template <int LPR, int NG, int RPS>
+__global__ __launch_bounds__(256) void k_moe_rows(const uint4 *__restrict__ Wall,
+                                                  const uint16_t *__restrict__ Sall,
+                                                  const int32_t *__restrict__ ids, int E,
+                                                  const int32_t *__restrict__ meta, int P,
+                                                  const uint16_t *__restrict__ x, int64_t ldx,
+                                                  int64_t slot_stride, int TOPK,
+                                                  float *__restrict__ part, int N, int G)
+{
+    constexpr int MR = kMaxRowsDot;
+    __shared__ int s_cnt[kFuseExperts];
+    __shared__ int s_pairs[kFusePairs];
+    __shared__ int s_np;
+    const int u = blockIdx.z;
+    int e, q0, q1;
+    const int32_t *order;
+    if (meta) {
+        // the unit's expert: thread k holds listed expert k's unit count (at
+        // most P <= 256 experts are listed), a block scan places unit u
+        __shared__ int s_red[4], s_k, s_first;
+        const int nd = meta[0], t = threadIdx.x;
+        const int uk = t < nd ? (meta[1 + P + t + 1] - meta[1 + P + t] + MR - 1) / MR : 0;
+        if (t == 0)
+            s_k = -1;
+        int total;
+        const int before = block_exclusive_scan(uk, s_red, &total);
+        if (u >= before && u < before + uk) {
+            s_k = t;
+            s_first = (u - before) * MR;
+        }
+        __syncthreads();
+        const int k = s_k;
+        if (k < 0)  // fewer units than slots: the whole workgroup leaves
+            return;
+        e = meta[1 + k];
+        q0 = meta[1 + P + k] + s_first;
+        q1 = min(q0 + MR, meta[1 + P + k + 1]);
+        order = meta + 2 + 2 * P;
+    } else {
+        e = route_in_workgroup(ids, P, E, u, MR, s_cnt, s_pairs, &s_np, &q0);
+        if (e < 0)
+            return;
+        q1 = min(q0 + MR, s_np);
+        order = s_pairs;
+    }
+    const int nr = q1 - q0;  // 1..MR pairs
+    // as many activation rows as the unit has pairs (1, 2 or 4)
+    if (nr == 1)
+        moe_rows_unit<LPR, NG, RPS, 1>(Wall, Sall, e, order + q0, nr, x, ldx, slot_stride, TOPK,
+                                       part, N, G);
+    else if (nr == 2)
+        moe_rows_unit<LPR, NG, RPS, 2>(Wall, Sall, e, order + q0, nr, x, ldx, slot_stride, TOPK,
+                                       part, N, G);
+    else
+        moe_rows_unit<LPR, NG, RPS, MR>(Wall, Sall, e, order + q0, nr, x, ldx, slot_stride, TOPK,
+                                        part, N, G);
 }
 
 struct Cfg {
