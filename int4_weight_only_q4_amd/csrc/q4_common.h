@@ -135,13 +135,16 @@ size_t moe_part_bytes(int N, int K, int P);
 q4_status launch_moe_finish(int mode, const float *part, int KS, int P, int N,
                             const int32_t *ids, const uint16_t *route_w, uint16_t *y, int E,
                             int T, int TOPK, hipStream_t stream);
-// Expert matvecs with the single-row arithmetic per (token, slot) pair (q4_gemv.hip):
-// per-pair f32 results part[pair][n]; routing from meta, or in each workgroup
-// when meta == nullptr (moe_routes_in_kernel).
+// Expert matvecs with the single-row arithmetic per (token, slot) pair
+// (q4_gemv.hip), P = T * TOPK <= 256 pairs; routing from meta, or in each
+// workgroup when meta == nullptr (moe_routes_in_kernel). out: 0 per-pair f32
+// results part[pair][n] (for launch_moe_finish), 1 f16 outputs y[pair][n],
+// 2 y[pair][i] = f16(silu(f16(gate_i)) * f16(up_i)) over N / 2 (N even); in
+// forms 1 and 2 pairs with an id outside [0, E) get zeros.
 q4_status launch_moe_rows(const uint32_t *W, const uint16_t *S, const int32_t *ids,
                           const int32_t *meta, const uint16_t *x, int64_t ldx,
-                          int64_t x_slot_stride, float *part, int E, int N, int K, int T,
-                          int TOPK, hipStream_t stream);
+                          int64_t x_slot_stride, int out, float *part, uint16_t *y, int E, int N,
+                          int K, int T, int TOPK, hipStream_t stream);
 // Whether the expert kernel routes by itself (meta == nullptr) for P pairs and E experts.
 bool moe_routes_in_kernel(int P, int E);
 // M >= 2 rows on the matrix cores (q4_mfma.hip): f16 outputs y, or f32

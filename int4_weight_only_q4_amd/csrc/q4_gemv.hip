@@ -384,16 +384,24 @@ __global__ __launch_bounds__(256) void k_gemv_rows(GemvParams a, int64_t ldx, in
                 }
 }
 
+// Outputs of k_moe_rows: f32 per-pair results for k_moe_finish (the down
+// stage's routing-weighted sum), f16 per-pair outputs, or the SiLU-multiply
+// of each pair's gate and up halves.
+enum : int { kMoeOutPart = 0, kMoeOutSlot = 1, kMoeOutSilu = 2 };
+
 // One unit of k_moe_rows: the nr <= MR pairs pairs[0 .. nr) of expert e
 // through this workgroup's rows (MR activation rows staged in LDS, missing
-// ones repeating the last pair; results stored for the nr pairs).
-template <int LPR, int NG, int RPS, int MR>
+// ones repeating the last pair; results stored for the nr pairs). SILU: local
+// rows [0, RB/2) are gate rows, [RB/2, RB) the matching up rows (as k_gemv's
+// SiLU epilogue), and vals is MR * RB floats of LDS.
+template <int LPR, int NG, int RPS, int MR, bool SILU>
 __device__ __forceinline__ void moe_rows_unit(const uint4 *__restrict__ Wall,
                                               const uint16_t *__restrict__ Sall, int e,
                                               const int32_t *pairs, int nr,
                                               const uint16_t *__restrict__ x, int64_t ldx,
-                                              int64_t slot_stride, int TOPK,
-                                              float *__restrict__ part, int N, int G)
+                                              int64_t slot_stride, int TOPK, int out,
+                                              float *__restrict__ part, uint16_t *__restrict__ y,
+                                              float *vals, int N, int G)
 {
     constexpr int SPW = 64 / LPR;
     constexpr int RB = kWaves * SPW * RPS;
@@ -403,6 +411,7 @@ __device__ __forceinline__ void moe_rows_unit(const uint4 *__restrict__ Wall,
     const int stride = chunks + G / 4 + 1;  // uint4 units per staged row
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int seg = lane / LPR, j = lane % LPR;
+    const int half = N >> 1;
     const uint4 *W = Wall + (size_t)e * N * G;
     const uint16_t *S = Sall + (size_t)e * N * G;
 
@@ -419,12 +428,20 @@ __device__ __forceinline__ void moe_rows_unit(const uint4 *__restrict__ Wall,
                 xr[m][q] = reinterpret_cast<const uint4 *>(xp)[c];
         }
     }
-    int row[RPS];
+    int row[RPS], li[RPS];
     bool ok[RPS];
 #pragma unroll
     for (int r = 0; r < RPS; ++r) {
-        const int rr = blockIdx.x * RB + (wave * SPW + seg) * RPS + r;
-        ok[r] = rr < N;
+        li[r] = (wave * SPW + seg) * RPS + r;
+        int rr;
+        if (SILU) {
+            const int gi = blockIdx.x * (RB / 2) + (li[r] % (RB / 2));
+            ok[r] = gi < half;
+            rr = li[r] < RB / 2 ? gi : half + gi;
+        } else {
+            rr = blockIdx.x * RB + li[r];
+            ok[r] = rr < N;
+        }
         row[r] = ok[r] ? rr : 0;
     }
     uint4 wv[NG][RPS];
@@ -477,34 +494,73 @@ __device__ __forceinline__ void moe_rows_unit(const uint4 *__restrict__ Wall,
 #pragma unroll
         for (int m = 0; m < MR; ++m)
             acc[r][m] = segment_sum(acc[r][m], LPR);
-    if (j == 0)
+    if (SILU) {
+        if (j == 0)
+#pragma unroll
+            for (int r = 0; r < RPS; ++r)
+#pragma unroll
+                for (int m = 0; m < MR; ++m)
+                    vals[m * RB + li[r]] = h2f(f2h(acc[r][m]));  // as a stored gate_up output
+        __syncthreads();
+        if (tid < RB / 2) {
+            const int gi = blockIdx.x * (RB / 2) + tid;
+            if (gi < half)
+#pragma unroll
+                for (int m = 0; m < MR; ++m)
+                    if (m < nr)
+                        y[(int64_t)pairs[m] * half + gi] =
+                            f2h(silu_mul_f(vals[m * RB + tid], vals[m * RB + tid + RB / 2]));
+        }
+    } else if (j == 0) {
 #pragma unroll
         for (int r = 0; r < RPS; ++r)
             if (ok[r])
 #pragma unroll
                 for (int m = 0; m < MR; ++m)
-                    if (m < nr)
-                        part[(size_t)pairs[m] * N + row[r]] = acc[r][m];
+                    if (m < nr) {
+                        if (out == kMoeOutSlot)
+                            y[(int64_t)pairs[m] * N + row[r]] = f2h(acc[r][m]);
+                        else
+                            part[(size_t)pairs[m] * N + row[r]] = acc[r][m];
+                    }
+    }
 }
 
 // MoE expert stage with the single-row arithmetic per (token, slot) pair:
 // grid (row blocks, 1, P), P <= 256. The distinct experts of the routing
 // (k_moe_route's meta, or each workgroup's own when meta == nullptr) own
 // ceil(pairs / MR) units of at most MR of their pairs; blockIdx.z is a unit
-// (P bounds their number). The workgroup runs its unit's pairs through its rows of the expert,
-// each pair with k_gemv_rows' arithmetic (activations staged in LDS), and
-// writes the per-pair f32 results part[pair][n] (k_moe_finish forms the
-// stage's outputs).
-template <int LPR, int NG, int RPS>
+// (P bounds their number). The workgroup runs its unit's pairs through its
+// rows of the expert, each pair with k_gemv_rows' arithmetic (activations
+// staged in LDS), and writes by `out`: the per-pair f32 results part[pair][n]
+// for k_moe_finish, the f16 outputs y[pair][n], or (SILU) y[pair][i] =
+// f16(silu(f16(gate_i)) * f16(up_i)) over the N / 2 gate and up rows, as
+// k_moe_finish would form them. In the last two forms the slice z = 0 also
+// writes zeros for the pairs whose id is outside [0, E) (they have no unit).
+template <int LPR, int NG, int RPS, bool SILU>
 __global__ __launch_bounds__(256) void k_moe_rows(const uint4 *__restrict__ Wall,
                                                   const uint16_t *__restrict__ Sall,
                                                   const int32_t *__restrict__ ids, int E,
                                                   const int32_t *__restrict__ meta, int P,
                                                   const uint16_t *__restrict__ x, int64_t ldx,
-                                                  int64_t slot_stride, int TOPK,
-                                                  float *__restrict__ part, int N, int G)
+                                                  int64_t slot_stride, int TOPK, int out,
+                                                  float *__restrict__ part,
+                                                  uint16_t *__restrict__ y, int N, int G)
 {
     constexpr int MR = kMaxRowsDot;
+    constexpr int RB = kWaves * (64 / LPR) * RPS;
+    __shared__ float s_vals[SILU ? MR * RB : 1];
+    if (out != kMoeOutPart && blockIdx.z == 0) {
+        // zeros for the pairs routed nowhere, over this workgroup's outputs
+        const int width = SILU ? RB / 2 : RB, ncol = SILU ? N / 2 : N;
+        const int c0 = blockIdx.x * width;
+        for (int i = threadIdx.x; i < P * width; i += 256) {
+            const int p = i / width, c = c0 + i % width;
+            const int id = ids[p];
+            if ((id < 0 || id >= E) && c < ncol)
+                y[(int64_t)p * ncol + c] = 0;
+        }
+    }
     __shared__ int s_cnt[kFuseExperts];
     __shared__ int s_pairs[kFusePairs];
     __shared__ int s_np;
@@ -543,14 +599,14 @@ __global__ __launch_bounds__(256) void k_moe_rows(const uint4 *__restrict__ Wall
     const int nr = q1 - q0;  // 1..MR pairs
     // as many activation rows as the unit has pairs (1, 2 or 4)
     if (nr == 1)
-        moe_rows_unit<LPR, NG, RPS, 1>(Wall, Sall, e, order + q0, nr, x, ldx, slot_stride, TOPK,
-                                       part, N, G);
+        moe_rows_unit<LPR, NG, RPS, 1, SILU>(Wall, Sall, e, order + q0, nr, x, ldx, slot_stride,
+                                             TOPK, out, part, y, s_vals, N, G);
     else if (nr == 2)
-        moe_rows_unit<LPR, NG, RPS, 2>(Wall, Sall, e, order + q0, nr, x, ldx, slot_stride, TOPK,
-                                       part, N, G);
+        moe_rows_unit<LPR, NG, RPS, 2, SILU>(Wall, Sall, e, order + q0, nr, x, ldx, slot_stride,
+                                             TOPK, out, part, y, s_vals, N, G);
     else
-        moe_rows_unit<LPR, NG, RPS, MR>(Wall, Sall, e, order + q0, nr, x, ldx, slot_stride, TOPK,
-                                        part, N, G);
+        moe_rows_unit<LPR, NG, RPS, MR, SILU>(Wall, Sall, e, order + q0, nr, x, ldx, slot_stride,
+                                              TOPK, out, part, y, s_vals, N, G);
 }
 
 struct Cfg {
@@ -693,7 +749,8 @@ struct MoeRowsArgs {
     const uint16_t *x;
     int64_t ldx, slot_stride;
     float *part;
-    int E, N, G, P, TOPK, slots;
+    uint16_t *y;
+    int out, E, N, G, P, TOPK, slots;
 };
 
 template <int LPR, int NG>
@@ -702,9 +759,15 @@ q4_status run_moe_rows(const MoeRowsArgs &a, hipStream_t st)
     constexpr int RPS = rows_per_segment(NG);
     constexpr int RB = kWaves * (64 / LPR) * RPS;
     const size_t lds = (size_t)kMaxRowsDot * (a.G * 4 + a.G / 4 + 1) * 16;
-    Q4_LAUNCH_MATVEC((k_moe_rows<LPR, NG, RPS>), dim3((a.N + RB - 1) / RB, 1, a.slots), dim3(256),
-                     lds, st, a.W, a.S, a.ids, a.E, a.meta, a.P, a.x, a.ldx, a.slot_stride, a.TOPK,
-                     a.part, a.N, a.G);
+    if (a.out == kMoeOutSilu)
+        Q4_LAUNCH_MATVEC((k_moe_rows<LPR, NG, RPS, true>),
+                         dim3((a.N / 2 + RB / 2 - 1) / (RB / 2), 1, a.slots), dim3(256), lds, st,
+                         a.W, a.S, a.ids, a.E, a.meta, a.P, a.x, a.ldx, a.slot_stride, a.TOPK,
+                         a.out, a.part, a.y, a.N, a.G);
+    else
+        Q4_LAUNCH_MATVEC((k_moe_rows<LPR, NG, RPS, false>), dim3((a.N + RB - 1) / RB, 1, a.slots),
+                         dim3(256), lds, st, a.W, a.S, a.ids, a.E, a.meta, a.P, a.x, a.ldx,
+                         a.slot_stride, a.TOPK, a.out, a.part, a.y, a.N, a.G);
     return check_launch("k_moe_rows");
 }
 
@@ -738,10 +801,12 @@ q4_status moe_rows_ng(int ng, const MoeRowsArgs &a, hipStream_t st)
 
 q4_status launch_moe_rows(const uint32_t *W, const uint16_t *S, const int32_t *ids,
                           const int32_t *meta, const uint16_t *x, int64_t ldx,
-                          int64_t x_slot_stride, float *part, int E, int N, int K, int T,
-                          int TOPK, hipStream_t stream)
+                          int64_t x_slot_stride, int out, float *part, uint16_t *y, int E, int N,
+                          int K, int T, int TOPK, hipStream_t stream)
 {
     MoeRowsArgs a;
+    a.out = out;
+    a.y = y;
     a.W = reinterpret_cast<const uint4 *>(W);
     a.S = S;
     a.ids = ids;

@@ -129,10 +129,13 @@ q4_status launch_moe(const uint32_t *W, const uint16_t *S, const int32_t *ids,
             return st;
     }
     if (moe_rows_fits(P, E, K)) {
-        // few pairs per expert: the single-row arithmetic per pair, then the outputs
-        q4_status st = launch_moe_rows(W, S, ids, meta, x, ldx, x_slot_stride, part, E, N, K, T,
-                                       TOPK, stream);
-        if (st != Q4_OK)
+        // few pairs per expert: the single-row arithmetic per pair; per-pair
+        // outputs straight from the expert kernel, the routing-weighted sum
+        // over a token's slots by the finishing kernel
+        const int out = mode == MOE_SILU ? 2 : (mode == MOE_PER_SLOT ? 1 : 0);
+        q4_status st = launch_moe_rows(W, S, ids, meta, x, ldx, x_slot_stride, out, part, y, E,
+                                       N, K, T, TOPK, stream);
+        if (st != Q4_OK || mode != MOE_COMBINE)
             return st;
         return launch_moe_finish(mode, part, 1, P, N, ids, route_w, y, E, T, TOPK, stream);
     }

@@ -184,13 +184,21 @@ def test_moe_out_of_range_id_contributes_zero(o, q4):
                     ldx=topk * k, x_slot_stride=k, route_w=dev_tensor(rw))
     yp = q4.moe_gemv(dev_tensor(W), dev_tensor(S), dev_tensor(ids), dev_tensor(x),
                      ldx=topk * k, x_slot_stride=k)
+    ys = q4.moe_gemv(dev_tensor(W), dev_tensor(S), dev_tensor(ids), dev_tensor(x),
+                     ldx=topk * k, x_slot_stride=k, epi_silu=True)
     sync()
-    ok = np.where((ids >= 0) & (ids < e), ids, 0)
-    w_eff = np.where((ids >= 0) & (ids < e), rw, np.float16(0))
+    valid = (ids >= 0) & (ids < e)
+    ok = np.where(valid, ids, 0)
+    w_eff = np.where(valid, rw, np.float16(0))
     ref = o.moe_stage(W, S, ok.astype(np.int32), w_eff, x, topk * k, k, n, k, epi_silu=False)
     assert_within(host(y), ref, "combine with invalid ids")
     yp = host(yp)
     assert np.all(yp[0, 1] == 0) and np.all(yp[1, 0] == 0)
+    # the SiLU-multiply form: zeros for the invalid pairs, the oracle elsewhere
+    ref_s = o.moe_stage(W, S, ok.astype(np.int32), None, x, topk * k, k, n, k, epi_silu=True)
+    ys = host(ys)
+    assert np.all(ys[~valid] == 0)
+    assert_within(ys[valid], ref_s[valid], "SiLU form with invalid ids")
 
 
 def test_moe_deterministic(o, q4, moe128):
