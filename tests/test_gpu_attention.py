@@ -185,3 +185,40 @@ def test_decode_loop_append_then_attend(o, q4):
         vc = cache_rows(c, table, pos + 1, 16, 1)
         assert_within(kc[pos].ravel(), kr, "key at %d" % pos)
         assert_within(host(out), o.attention(host(q), kc, vc, nh, nkv, hd), "output at %d" % pos)
+
+
+def test_attention_back_to_back_calls_keep_their_bits(q4):
+    """Calls that share the stream's workspace (the split partials), issued
+    back to back with no synchronisation at split counts that change from call
+    to call (4112, 1000, 300 and 257 positions, then 4112 again), give the bits
+    of the same calls made one at a time."""
+    g = PHI3
+    nh, hd = g["n_heads"], g["head_dim"]
+    d = desc_for(q4, g)
+    table = np.random.default_rng(5).permutation(257).astype(np.int32)
+    kv, _, _ = fill_cache(q4, d, 950, 4112, table)
+    q = dev_tensor(datagen.activations(951, 1, nh * hd)[0])
+    lens = [4112, 1000, 300, 257, 4112, 4112]
+    alone = []
+    for L in lens:
+        alone.append(bits(q4.attention_decode(q, kv, i32(table), i32([L - 1]), L, d)))
+        sync()
+    outs = [q4.attention_decode(q, kv, i32(table), i32([L - 1]), L, d) for L in lens]
+    sync()
+    for L, a, b in zip(lens, alone, outs):
+        assert np.array_equal(a, bits(b)), L
+
+
+def test_attention_many_heads_vs_oracle(o, q4):
+    """80 query heads over 8 key/value heads (ten query heads per key/value
+    head), 1000 positions in 63 pages of a permuted table."""
+    g = dict(n_heads=80, n_kv=8, head_dim=64, k=5120)
+    nh, nkv, hd = g["n_heads"], g["n_kv"], g["head_dim"]
+    d = desc_for(q4, g, max_pages=64, n_pages=64)
+    table = np.random.default_rng(80).permutation(64).astype(np.int32)
+    L = 1000
+    kv, kc, vc = fill_cache(q4, d, 960, L, table)
+    q = datagen.activations(961, 1, nh * hd)[0]
+    out = q4.attention_decode(dev_tensor(q), kv, i32(table), i32([L - 1]), L, d)
+    sync()
+    assert_within(host(out), o.attention(q, kc, vc, nh, nkv, hd), "80 heads")
