@@ -123,9 +123,13 @@ q4_status q4_gemv_batched(const uint32_t *W, const uint16_t *S, const uint16_t *
  *   epi_silu == 0, route_w == NULL : y f16[T][TOPK][N] = f16(v)
  *   epi_silu == 0, route_w f16[T][TOPK] : y f16[T][N] =
  *        f16( sum_s route_w[t][s] * v(t, s) )       (down stage + combine)
- * epi_silu together with route_w is Q4_EINVAL. Each distinct expert's weights
- * are streamed once per call for all (t, s) that chose it. Ids are validated on
- * the device; an out-of-range id contributes zeros. T*TOPK <= Q4_MAX_PAIRS.
+ * epi_silu together with route_w is Q4_EINVAL. The (t, s) pairs are grouped by
+ * expert, so each distinct expert's weights are read once per group of its
+ * pairs: groups of up to 4 pairs while experts get about two pairs each or
+ * fewer (at most 256 pairs), otherwise groups of up to 16 on the matrix cores;
+ * an expert with more pairs than one group re-reads its rows, mostly from
+ * cache. Ids are validated on the device; an out-of-range id contributes
+ * zeros. T*TOPK <= Q4_MAX_PAIRS.
  */
 #define Q4_MAX_PAIRS 4096
 q4_status q4_moe_gemv(const uint32_t *W, const uint16_t *S, const int32_t *ids,
@@ -215,8 +219,11 @@ q4_status q4_gemv_affine(const uint32_t *W, const uint16_t *S, const uint16_t *B
  *                      quantization format"); no per-group scaling of sums.
  * W, S as for q4_gemv; x f16 rows, 16-byte aligned, ldx % 8 == 0, ldx >= K;
  * y f16, 2-byte aligned, ldy >= N, caller-owned, not overlapping the inputs.
- * 1 <= M <= Q4_MAX_GEMM_M. f32 accumulation over all of K in an unspecified
- * order. No workspace; one kernel launch. Q4_EINVAL for an unknown `weights`.
+ * 1 <= M <= Q4_MAX_GEMM_M. f32 accumulation over K in an order fixed by
+ * (M, N, K). A call whose tile grid would fill under half the GPU splits K:
+ * f32 partials in the library workspace of the stream, summed in split order
+ * by a second kernel; otherwise one kernel launch. Q4_EINVAL for an unknown
+ * `weights`.
  */
 #define Q4_MAX_GEMM_M 65536
 typedef enum q4_gemm_weights { Q4_GEMM_EXACT = 0, Q4_GEMM_F16_WEIGHT = 1 } q4_gemm_weights;
