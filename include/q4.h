@@ -31,11 +31,13 @@
  *   - Accumulation is f32; results are rounded to binary16 (nearest even).
  *     Results are bit-identical from run to run for the same arguments on the
  *     same device (fixed reduction order, no floating-point atomics).
- *   - Entry points that need scratch memory (fused add+RMSNorm, MoE, stack)
- *     use a library-owned workspace allocated once per (device, stream) on first
- *     use and kept until the process ends; concurrent calls on distinct streams
- *     do not share it. The first such call on a stream allocates, so warm up
- *     before capturing a HIP graph.
+ *   - Entry points that need scratch memory (split partials of the batched,
+ *     prefill and attention kernels, MoE routing and partials, LM-head argmax
+ *     candidates, the stack's intermediate vectors) use a library-owned
+ *     workspace allocated per (device, stream) on first use, grown when a
+ *     larger call needs more, and kept until the process ends; concurrent calls
+ *     on distinct streams do not share it. A call that allocates synchronises
+ *     the device, so warm up on a stream before capturing a HIP graph on it.
  */
 #ifndef Q4_H
 #define Q4_H
@@ -197,7 +199,9 @@ q4_status q4_gemv_ex(const uint32_t *W, const uint16_t *S, const uint16_t *x, ui
  *   y[m*ldy + n] = f16( sum_k (S[n][k/64] * q[n][k] + B[n][k/64]) * x[m*ldx + k] )
  * W u32[N][K/8], S and B f16[N][K/64] (2-byte aligned), K % 64 == 0; x and y
  * as for q4_gemv_batched. f32 accumulation; M = 1 runs the single-row kernel,
- * M >= 2 the matrix cores (exact integer operands, scale and bias in f32).
+ * M = 2..4 with M*K <= 24576 the same arithmetic per row (each row equals its
+ * M = 1 result bit for bit), larger M the matrix cores (exact integer
+ * operands, scale and bias in f32).
  */
 q4_status q4_gemv_affine(const uint32_t *W, const uint16_t *S, const uint16_t *B,
                          const uint16_t *x, int64_t ldx, uint16_t *y, int64_t ldy, int64_t N,
