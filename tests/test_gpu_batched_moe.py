@@ -322,3 +322,23 @@ def test_moe_sorted_routing_with_invalid_ids(o, q4, t, topk, e):
     assert_within(yph[v], ref_p.reshape(t * topk, n)[v], "per-slot")
     assert np.all(yph[~v] == 0)
     assert_within(host(yc), ref_c, "combine")
+
+
+def test_moe_max_pairs(o, q4):
+    """T * TOPK = Q4_MAX_PAIRS (512 tokens x 8 slots over 64 experts): the
+    sorting kernel at its largest list and the matrix-core expert kernel,
+    per-slot and combine modes against the oracle."""
+    e, n, k, t, topk = 64, 32, 64, 512, 8
+    W, S = experts(o, 1700, e, n, k)
+    rng = np.random.default_rng(1701)
+    ids = np.stack([rng.permutation(e)[:topk] for _ in range(t)]).astype(np.int32)
+    rw = (rng.random((t, topk)) / topk).astype(np.float16)
+    x = datagen.activations(1702, t * topk, k)
+    Wd, Sd, idsd, xd = dev_tensor(W), dev_tensor(S), dev_tensor(ids), dev_tensor(x)
+    yp = q4.moe_gemv(Wd, Sd, idsd, xd, ldx=topk * k, x_slot_stride=k)
+    yc = q4.moe_gemv(Wd, Sd, idsd, xd, ldx=topk * k, x_slot_stride=k, route_w=dev_tensor(rw))
+    sync()
+    assert_within(host(yp), o.moe_stage(W, S, ids, None, x, topk * k, k, n, k, epi_silu=False),
+                  "per-slot")
+    assert_within(host(yc), o.moe_stage(W, S, ids, rw, x, topk * k, k, n, k, epi_silu=False),
+                  "combine")

@@ -229,3 +229,24 @@ def test_gemm_affine_prefill_sampled(o, q4, name, n, k, m):
     ref = o.gemv_affine(W[cols], S[cols], B[cols], X[rows])
     assert_within(y[np.ix_(rows, cols)], ref, "%s sampled" % name)
     assert np.all(np.isfinite(y)), "non-finite outputs"
+
+
+@pytest.mark.parametrize("mode", [EXACT, F16W], ids=["exact", "f16w"])
+def test_gemm_k_max(o, q4, mode):
+    """K = Q4_MAX_K (24576, 768 groups): one tile of rows, K split."""
+    W, S, X = make("k_max", 40, 24576, 70)
+    y = run(q4, W, S, X, mode)
+    ref = o.gemv_batched(W, S, X) if mode == EXACT else o.gemv_w16(W, S, X)
+    assert_within(y, ref, "K max")
+
+
+def test_gemm_m_max(o, q4):
+    """M = Q4_MAX_GEMM_M (65536 activation rows) on a small matrix: sampled rows
+    (the first and last tiles and random ones) against the oracle."""
+    m = q4.MAX_GEMM_M
+    W, S, X = make("m_max", 24, 64, m)
+    y = run(q4, W, S, X, EXACT)
+    rng = np.random.default_rng(65536)
+    rows = np.unique(np.r_[0, 1, 127, 128, m - 129, m - 1, rng.integers(0, m, 200)])
+    assert_within(y[rows], o.gemv_batched(W, S, X[rows]), "M max sampled")
+    assert np.all(np.isfinite(y.astype(np.float64)))
