@@ -552,13 +552,18 @@ __global__ __launch_bounds__(256) void k_moe_rows(const uint4 *__restrict__ Wall
     __shared__ float s_vals[SILU ? MR * RB : 1];
     if (out != kMoeOutPart && blockIdx.z == 0) {
         // zeros for the pairs routed nowhere, over this workgroup's outputs
-        const int width = SILU ? RB / 2 : RB, ncol = SILU ? N / 2 : N;
-        const int c0 = blockIdx.x * width;
-        for (int i = threadIdx.x; i < P * width; i += 256) {
-            const int p = i / width, c = c0 + i % width;
-            const int id = ids[p];
-            if ((id < 0 || id >= E) && c < ncol)
-                y[(int64_t)p * ncol + c] = 0;
+        // (thread t checks pair t, P <= 256; nothing to do when all are valid)
+        const int id_t = (int)threadIdx.x < P ? ids[threadIdx.x] : 0;
+        const bool bad = (int)threadIdx.x < P && (id_t < 0 || id_t >= E);
+        if (__syncthreads_or(bad)) {
+            const int width = SILU ? RB / 2 : RB, ncol = SILU ? N / 2 : N;
+            const int c0 = blockIdx.x * width;
+            for (int i = threadIdx.x; i < P * width; i += 256) {
+                const int p = i / width, c = c0 + i % width;
+                const int id = ids[p];
+                if ((id < 0 || id >= E) && c < ncol)
+                    y[(int64_t)p * ncol + c] = 0;
+            }
         }
     }
     __shared__ int s_cnt[kFuseExperts];
