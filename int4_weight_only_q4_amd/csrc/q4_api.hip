@@ -101,7 +101,7 @@ void *workspace(hipStream_t stream, size_t bytes)
         return nullptr;
     }
     if (hipMemset(p, 0, kCounterBytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
-        hipFree(p);
+        (void)hipFree(p);  // the error reported is the one above
         fail(Q4_EHIP, "clearing the workspace counters failed");
         return nullptr;
     }

@@ -40,13 +40,13 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;            // 16 weight rows per wave
-constexpr int kRowsPerWg = 16 * kWaves;
 constexpr int kDepth = 4;            // steps (4 groups each) of one tile's weight loads
 constexpr int kGroupsPerSplit = 4 * kDepth;  // K chunk per workgroup: 512 values
 constexpr int kMTile = 16;           // activation rows per launch
 constexpr int kXq = (kMTile * kGroupsPerSplit * 4 + 255) / 256;  // x chunks per thread
 constexpr int kMaxTilesPerWave = 4;  // finished tiles wait in LDS until the last is done
-constexpr int kMoePerSlot = 0, kMoeSilu = 1, kMoeCombine = 2;
+// k_moe_finish modes (the per-slot mode is the remaining one, 0)
+constexpr int kMoeSilu = 1, kMoeCombine = 2;
 
 // The 8 codes of word w as the exact binary16 integers q - 7, in the pair
 // order (e0, e4) (e1, e5) (e2, e6) (e3, e7): (w >> 4i) & 0x000F000F puts codes i
