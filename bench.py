@@ -503,15 +503,15 @@ def gemv_table(q4, torch):
 
         def launch(i, g=g, caches=caches, tab=tab, posL=posL, L=L):
             stack.decode_attn(g, caches, tab, posL, L, stt["r0"], stt["h0"], r_out, h_out)
-        call_us, _ = _time(q4, torch, launch, 20, timed_kernels=False)
+        call_us = _time_graph(q4, torch, launch, 10)
         wb = stack_weight_bytes(PHI3) + PHI3["layers"] * L * 32 * 96 * 2 * 2
         gbs = wb / (call_us * 1e-6) / 1e9
         rows.append(dict(workload="Phi-3-mini decode token with attention (32 layers)",
                          shape="L=%d" % L, m=1, weight_bytes=int(wb), us_kernel=None,
                          us_per_call=round(call_us, 3), gbs=round(gbs, 1),
                          pct_peak=round(100 * gbs / HBM_PEAK_GBS, 1),
-                         note="q4_stack_decode_attn: 6 or 7 kernels per layer; bytes = weights "
-                              "+ K and V of every layer"))
+                         note="q4_stack_decode_attn: 6 or 7 kernels per layer, timed from a "
+                              "HIP graph of the calls; bytes = weights + K and V of every layer"))
         print("  decode token + attention L=%-5d %9.1f us/token %8.1f GB/s" % (L, call_us, gbs),
               file=sys.stderr, flush=True)
         del caches, first

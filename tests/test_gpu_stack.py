@@ -318,3 +318,52 @@ def test_stack_with_attention_teacher_forced(o, q4, geom, n_layers, pos):
         assert_within_scaled(host(r2), r2_ref[0], f64(dn_ref) + f64(host(r1)), what + " r2")
         r_in, h_in = tr[L, 0], tr[L, 1]
     assert np.array_equal(bits(r_out), tr[-1, 0].view(np.uint16))
+
+
+def test_stack_with_attention_graph_replays_equal_eager(o, q4):
+    """A captured HIP graph of one decode token with the attention step
+    (q4_stack_decode_attn: cache append, split attention and merge kernels,
+    matvecs), replayed four times between eager calls: every replay gives the
+    eager token's bits and cache. The position grows the cache past one split."""
+    import torch
+    d, f, nh, nkv, hd = 256, 512, 4, 2, 64
+    n_layers, L = 2, 600
+    _, dl, gi, gp, gf = _attn_stack(o, q4, (d, f, nh, nkv, hd), n_layers, 2600)
+    npages = (L + 15) // 16
+    desc = q4.attn_desc(nh, nkv, hd, 16, npages, npages)
+    tab = torch.from_numpy(np.random.default_rng(3).permutation(npages).astype(np.int32)).cuda()
+    posd = torch.tensor([L - 1], dtype=torch.int32, device="cuda")
+    c0 = [torch.from_numpy(datagen.normal_f16(2700 + i, (npages, 2, nkv, 16, hd))).cuda()
+          for i in range(n_layers)]
+    st = q4.Stack(dl, dev_tensor(gi), dev_tensor(gp), dev_tensor(gf), d, f, (nh + 2 * nkv) * hd, 0,
+                  nh * hd, eps=1e-5)
+    r0 = dev_tensor(datagen.activations(2800, 1, d)[0])
+    h0 = dev_tensor(datagen.activations(2801, 1, d)[0])
+    caches = [c.clone() for c in c0]
+    r_g = torch.empty(d, dtype=torch.float16, device="cuda")
+    h_g = torch.empty(d, dtype=torch.float16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            st.decode_attn(desc, caches, tab, posd, L, r0, h0, r_g, h_g)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        st.decode_attn(desc, caches, tab, posd, L, r0, h0, r_g, h_g)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        ce = [c.clone() for c in c0]
+        r_e = torch.empty_like(r_g)
+        h_e = torch.empty_like(h_g)
+        st.decode_attn(desc, ce, tab, posd, L, r0, h0, r_e, h_e)
+        torch.cuda.synchronize()
+        for c, c_0 in zip(caches, c0):
+            c.copy_(c_0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(h_g), bits(h_e)), ("h", rep)
+        assert np.array_equal(bits(r_g), bits(r_e)), ("r", rep)
+        for c, e_ in zip(caches, ce):
+            assert torch.equal(c.view(torch.int16), e_.view(torch.int16)), ("cache", rep)
