@@ -803,7 +803,7 @@ def main():
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: the int4 decode path is built and timed on a single "
-              "MI355X (multi-GPU sharding is a design note, not part of this build); "
+              "MI355X (how the path would shard over several GPUs is described, not built); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
