@@ -191,17 +191,18 @@ def summarize_counters(fetch_dir, write_dir):
                algorithmic_bytes_per_launch=int(algo), ratio=round(traffic / algo, 4), **res)
     cmd = ("export REPO=$PWD && cd /tmp && export TMPDIR=/tmp && timeout -s KILL 150 "
            "rocprofv3 --pmc {C} "
-           "--output-format csv -d $REPO/gpurun_out/pmc_{c} -o pmc -- "
+           "--output-format csv -d $OUT/pmc_{c} -o pmc -- "
            "python3 $REPO/bench.py --counters")
     text = [
         "# HBM traffic of the dominant kernel: gate_up 16384x3072 matvec, Phi-3-mini stack",
         "",
-        "Two counter runs (one counter group each), from the repository root on one MI355X:",
+        "Two counter runs (one counter group each), from the repository root on one MI355X "
+        "(OUT: an output directory):",
         "",
         "```",
         cmd.format(C="FETCH_SIZE", c="fetch"),
         cmd.format(C="WRITE_SIZE", c="write"),
-        "python3 bench.py --summarize-counters gpurun_out/pmc_fetch gpurun_out/pmc_write",
+        "python3 bench.py --summarize-counters $OUT/pmc_fetch $OUT/pmc_write",
         "```",
         "",
         "`bench.py --counters` runs a plain %d MiB device copy three times, then the "
@@ -616,7 +617,8 @@ def prefill_table(q4, torch):
     return rows
 
 
-def write_prefill_table(rows):
+def write_prefill_table(rows, out_dir):
+    """The prefill table as markdown, to out_dir/prefill_table.md."""
     text = ["# Prefill matmul (q4_gemm, q4_gemm_affine) on the matrix cores: Phi-3-mini "
             "M = 1024, Qwen3-4B M = 256 (q4f16_1 and MLX affine)",
             "",
@@ -638,8 +640,8 @@ def write_prefill_table(rows):
         text.append("| %s | %s | %d | %.2f | %.1f | %.1f | %s |" % (
             r["workload"], r["shape"], r["m"], r["us_kernel"], r["tflops"], r["pct_f16_peak"],
             r["note"]))
-    os.makedirs(os.path.join(ROOT, "gpurun_out"), exist_ok=True)
-    with open(os.path.join(ROOT, "gpurun_out", "prefill_table.md"), "w") as fh:
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, "prefill_table.md"), "w") as fh:
         fh.write("\n".join(text) + "\n")
 
 
@@ -789,6 +791,8 @@ def main():
                     help="launch each token's kernels from the host instead of replaying "
                          "a captured graph of them")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--out-dir", default=os.path.join(ROOT, "bench_out"),
+                    help="directory for the markdown of --prefill-table")
     ap.add_argument("--gemv-table", action="store_true",
                     help="measure the per-GEMV table (Phi-3, Qwen3 M=1/2/4/8, MoE) and exit")
     ap.add_argument("--prefill-table", action="store_true",
@@ -819,7 +823,7 @@ def main():
         return
     if args.prefill_table:
         rows = prefill_table(q4, torch)
-        write_prefill_table(rows)
+        write_prefill_table(rows, args.out_dir)
         print(json.dumps({"prefill_table": rows}), flush=True)
         return
     p = PHI3
