@@ -643,10 +643,11 @@ Cfg choose_cfg(int G)
 template <int LPR, int NG, int EPI, int PRO, bool AFF>
 q4_status run_gemv(const GemvParams &p, hipStream_t st)
 {
-    // residual-epilogue launches at three groups per lane (the O projection,
-    // 3072 x 3072) take one row per segment: twice the workgroups of a matrix
-    // too small to fill the GPU at two (measured: 0.5 % off a decode token)
-    constexpr int RPS = (EPI == EPI_RESID && NG == 3) ? 1 : rows_per_segment(NG);
+    // residual-epilogue launches at three or four groups per lane (the O and
+    // down projections, 3072 x 3072 and 3072 x 8192) take one row per segment:
+    // twice the workgroups of matrices with few rows (measured: 0.5 % and
+    // 1.2 % off a decode token; the norm-prologue QKV launch loses with it)
+    constexpr int RPS = (EPI == EPI_RESID && (NG == 3 || NG == 4)) ? 1 : rows_per_segment(NG);
     constexpr int RB = kWaves * (64 / LPR) * RPS;
     const bool paired = EPI == EPI_SILU || EPI == EPI_ROPE;
     const int rows = paired ? p.N / 2 : p.N;
