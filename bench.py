@@ -20,6 +20,7 @@ events on the stream it runs on) and the CPU oracle timed on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import concurrent.futures as cf
 import json
 import os
 import sys
@@ -36,6 +37,21 @@ import datagen  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense f16 matrix-core peak
 METRIC = "effective weight GB/s (% of HBM peak) and µs/token for int4 dequant-GEMV decode stack"
+
+# Threads of the all-cores oracle leg: every host core, at most the 16 the GPU
+# box grants one GPU's jobs.
+HOST_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+# The pages' own decode rates for Phi-3-mini q4f16_1 (BENCH.md, "Why a third
+# baseline"; Zero TVM Documentation, "vs WebLLM"): a browser on an Apple GPU,
+# a whole decode step with attention and the LM head. Context, not a target.
+BROWSER_CONTEXT = {
+    "what": "Phi-3-mini q4f16_1 decode tokens/s in a browser (context only, other hardware, "
+            "a whole decode step with attention and LM head)",
+    "hardware": "Apple M2 Max, Chrome 150, WebGPU",
+    "zero_tvm_tok_s": 83.20,
+    "webllm_0_2_80_tok_s": 60.07,
+}
 
 PHI3 = dict(d=3072, f=8192, n_qkv=9216, v_off=6144, dv=3072, layers=32, eps=1e-5)
 BPW = 0.5625  # bytes per int4 weight: 4 bits + one f16 scale per 32 weights
@@ -310,29 +326,41 @@ def _time_graph(q4, torch, launch, count, reps=5):
     return e0.elapsed_time(e1) * 1e3 / (reps * count)
 
 
-def gemv_table(q4, torch):
+def gemv_table(q4, torch, o=None, threads=HOST_THREADS):
     """Per-GEMV throughput at the single-GEMV, Phi-3-mini, Qwen3-4B (M = 1 and
-    8) and MoE workloads, weights rotated past the Infinity Cache."""
+    8) and MoE workloads, weights rotated past the Infinity Cache; with the
+    oracle `o`, the oracle's time for the same matmul (or MoE layer) on one
+    host thread and on `threads` threads beside each GPU row."""
     rows = []
     base = datagen.SEED_BASE + 5_000_000
 
-    def add(workload, shape, m, weight_bytes, launch, count=200, note="", per_call=False):
+    def add(workload, shape, m, weight_bytes, launch, count=200, note="", per_call=False,
+            oracle_us=None):
         call_us, kern_us = _time(q4, torch, launch, count)
         us = call_us if per_call or kern_us is None else kern_us
         gbs = weight_bytes / (us * 1e-6) / 1e9
-        rows.append(dict(workload=workload, shape=shape, m=m, weight_bytes=int(weight_bytes),
-                         us_kernel=round(kern_us, 3) if kern_us is not None else None,
-                         us_per_call=round(call_us, 3), gbs=round(gbs, 1),
-                         pct_peak=round(100 * gbs / HBM_PEAK_GBS, 1), note=note))
-        print("  %-22s %-12s M=%-2d %8.3f us/kernel %8.3f us/call %8.1f GB/s" % (
-            workload, shape, m, us, call_us, gbs), file=sys.stderr, flush=True)
+        row = dict(workload=workload, shape=shape, m=m, weight_bytes=int(weight_bytes),
+                   us_kernel=round(kern_us, 3) if kern_us is not None else None,
+                   us_per_call=round(call_us, 3), gbs=round(gbs, 1),
+                   pct_peak=round(100 * gbs / HBM_PEAK_GBS, 1), note=note)
+        if o is not None and oracle_us is not None:
+            row["oracle_us_1t"] = round(oracle_us(1)[0], 1)
+            row["oracle_us_all"] = round(oracle_us(threads)[0], 1)
+        rows.append(row)
+        print("  %-22s %-12s M=%-2d %8.3f us/kernel %8.3f us/call %8.1f GB/s%s" % (
+            workload, shape, m, us, call_us, gbs,
+            "  oracle %.0f / %.0f us" % (row["oracle_us_1t"], row["oracle_us_all"])
+            if "oracle_us_1t" in row else ""), file=sys.stderr, flush=True)
 
     def gemv_rows(workload, shapes, ms, seed0):
         for j, (name, (n, k)) in enumerate(shapes):
             rot = _rotation(torch, n, k, seed0 + 10 * j)
             wb = n * k * BPW
+            Wh = datagen.words(seed0 + 10 * j, n, k) if o is not None else None
+            Sh = datagen.scales(seed0 + 10 * j + 1, n, k) if o is not None else None
             for m in ms:
-                x = torch.from_numpy(datagen.activations(seed0 + 10 * j + 2, m, k)).cuda()
+                xh = datagen.activations(seed0 + 10 * j + 2, m, k)
+                x = torch.from_numpy(xh).cuda()
                 y = torch.empty((m, n), dtype=torch.float16, device="cuda")
                 if m == 1:
                     def launch(i, rot=rot, x=x, y=y):
@@ -343,8 +371,9 @@ def gemv_table(q4, torch):
                         W, S = rot[i % len(rot)]
                         q4.gemv_batched(W, S, x, y=y)
                 add(workload, "%s %dx%d" % (name, n, k), m, wb, launch,
-                    count=max(20, min(200, int(4e9 / wb))))
-            del rot
+                    count=max(20, min(200, int(4e9 / wb))),
+                    oracle_us=lambda t, Wh=Wh, Sh=Sh, xh=xh: oracle_rows_us(o, Wh, Sh, xh, t))
+            del rot, Wh, Sh
             torch.cuda.empty_cache()
 
     gemv_rows("single GEMV", [("W", (512, 256))], [1], base)
@@ -465,6 +494,12 @@ def gemv_table(q4, torch):
                               .reshape(E, hidden, f // 32)).cuda()
         stacks.append((Wg, Sg, Wd, Sd))
     expert_bytes = (2 * f * hidden + hidden * f) * BPW
+    moe_host = None
+    if o is not None:  # the first copy of the expert stack on the host
+        moe_host = (datagen.words(base + 3000, E * 2 * f, hidden).reshape(E, 2 * f, hidden // 8),
+                    datagen.scales(base + 3100, E * 2 * f, hidden).reshape(E, 2 * f, hidden // 32),
+                    datagen.words(base + 3200, E * hidden, f).reshape(E, hidden, f // 8),
+                    datagen.scales(base + 3300, E * hidden, f).reshape(E, hidden, f // 32))
     for t in (1, 4, 16):
         ids_h, w_h = datagen.routing_pool(base + 4000 + t, 256, t, E, topk)
         ids = torch.from_numpy(ids_h).cuda()
@@ -481,14 +516,21 @@ def gemv_table(q4, torch):
         call_us, _ = _time(q4, torch, launch, 200, timed_kernels=False)
         wb = uniq * expert_bytes
         gbs = wb / (call_us * 1e-6) / 1e9
-        rows.append(dict(workload="MoE layer (128 experts, top-8)", shape="T=%d" % t, m=t,
-                         weight_bytes=int(wb), us_kernel=None, us_per_call=round(call_us, 3),
-                         gbs=round(gbs, 1), pct_peak=round(100 * gbs / HBM_PEAK_GBS, 1),
-                         note="%.2f unique experts per layer on average; time of both stages "
-                              "back to back (an expert kernel and a finishing kernel each)"
-                              % uniq))
-        print("  MoE T=%-2d %8.3f us/layer %8.1f GB/s (unique experts %.2f)" % (
-            t, call_us, gbs, uniq), file=sys.stderr, flush=True)
+        row = dict(workload="MoE layer (128 experts, top-8)", shape="T=%d" % t, m=t,
+                   weight_bytes=int(wb), us_kernel=None, us_per_call=round(call_us, 3),
+                   gbs=round(gbs, 1), pct_peak=round(100 * gbs / HBM_PEAK_GBS, 1),
+                   note="%.2f unique experts per layer on average; time of both stages "
+                        "back to back (an expert kernel and a finishing kernel each)" % uniq)
+        if o is not None:
+            row["oracle_us_1t"], row["oracle_us_all"] = (
+                round(oracle_moe_us(o, moe_host, ids_h[0], w_h[0],
+                                    datagen.activations(base + 4100 + t, t, hidden), f, thr), 1)
+                for thr in (1, threads))
+        rows.append(row)
+        print("  MoE T=%-2d %8.3f us/layer %8.1f GB/s (unique experts %.2f)%s" % (
+            t, call_us, gbs, uniq, "  oracle %.0f / %.0f us" % (
+                row["oracle_us_1t"], row["oracle_us_all"]) if o is not None else ""),
+            file=sys.stderr, flush=True)
     # Phi-3-mini decode token, 32 layers, with the real attention step over L
     # cached positions (each layer its own cache; the step appends at L - 1)
     stack, stt = build_stack(q4, torch, PHI3)
@@ -699,18 +741,17 @@ def verify_one_token(q4, torch, stack, st, p, o, layers_checked=(0, 1)):
     return worst
 
 
-def token_graphs(torch, stack, hs, r_out, warm=3):
+def token_graphs(torch, stack, hs, r_out):
     """Two captured HIP graphs of one decode token each (the 129 kernel
     launches of q4_stack_decode): graph a reads (residual, normalised) =
     (hs[a], hs[a]) and writes hs[1 - a] (r_out takes the residual). They are
-    captured on a side stream after eager calls on that stream, so the
-    library's per-stream workspace exists before capture and the graphs hold
-    kernels only. Returns (stream, [graph0, graph1])."""
+    captured on a side stream whose library workspace was reserved first
+    (q4_workspace_reserve), so the graphs hold kernels only. Returns (stream,
+    [graph0, graph1])."""
+    import int4_weight_only_q4_amd as q4
     st = torch.cuda.Stream()
     st.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(st):
-        for _ in range(warm):  # same input each time: hs[0] is left as it was
-            stack.decode(hs[0], hs[0], r_out, hs[1])
+    q4.workspace_reserve(q4.stack_workspace_bytes(stack), stream=st)
     torch.cuda.synchronize()
     graphs = []
     for a in (0, 1):
@@ -760,9 +801,98 @@ def measured_copy_gbs(torch, nbytes=1 << 30, reps=20):
     return 2 * nbytes / secs / 1e9
 
 
-def cpu_baseline(p, o, seconds=10.0):
-    """The oracle (single-threaded C, binary64) on whole decode layers of the same
-    stack, chained, until about `seconds` of CPU time has been spent."""
+def host_info(threads):
+    """The host the oracle legs ran on: CPU model (/proc/cpuinfo), os.cpu_count()
+    (what std::thread::hardware_concurrency reports), the CPUs this process may
+    run on (what nproc prints) and the threads the all-cores leg used."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = None
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "nproc": nproc,
+            "threads": threads}
+
+
+def _split(n, parts):
+    """n items as `parts` contiguous (start, end) ranges (empty ones dropped)."""
+    b = [n * i // parts for i in range(parts + 1)]
+    return [(b[i], b[i + 1]) for i in range(parts) if b[i + 1] > b[i]]
+
+
+def _in_threads(fn, items, threads):
+    """fn over items in `threads` host threads (the oracle is one single-threaded
+    C call per item; ctypes releases the GIL during it)."""
+    if threads == 1:
+        return [fn(it) for it in items]
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        return list(ex.map(fn, items))
+
+
+def oracle_rows_us(o, W, S, X, threads, target_s=0.25):
+    """Oracle microseconds for one matmul of all N rows of W against the M
+    activation rows X, extrapolated from a contiguous block of rows sized for
+    about target_s of work per thread; the block is split into `threads`
+    contiguous parts, each run by the single-threaded oracle (gemv for M = 1,
+    gemv_batched otherwise) in a thread of its own. Returns (us, rows timed)."""
+    n = W.shape[0]
+
+    def run(rng):
+        r0, r1 = rng
+        if X.shape[0] == 1:
+            o.gemv(W[r0:r1], S[r0:r1], X[0])
+        else:
+            o.gemv_batched(W[r0:r1], S[r0:r1], X)
+
+    r = min(n, 4)
+    t0 = time.perf_counter()
+    run((0, r))
+    per_row = max((time.perf_counter() - t0) / r, 1e-9)
+    rows = int(min(n, max(r, target_s * threads / per_row)))
+    t0 = time.perf_counter()
+    _in_threads(run, _split(rows, threads), threads)
+    return (time.perf_counter() - t0) / rows * n * 1e6, rows
+
+
+def oracle_moe_us(o, mats, ids, route_w, x, f, threads):
+    """Oracle microseconds for one MoE layer (the gate_up stage with the
+    SiLU-multiply, its output rounded to binary16 as stored between the stages,
+    then the down stage with the routing-weighted sum) over the tokens of ids
+    [T][top-k]; the tokens are split over `threads` threads, each running the
+    single-threaded oracle's stages on its tokens."""
+    Wg, Sg, Wd, Sd = mats
+    t, topk = ids.shape
+    hidden = x.shape[1]
+
+    def run(rng):
+        a, b = rng
+        u = o.moe_stage(Wg, Sg, ids[a:b], None, x[a:b], hidden, 0, 2 * f, hidden, True)
+        u16 = np.ascontiguousarray(u.astype(np.float16))
+        o.moe_stage(Wd, Sd, ids[a:b], route_w[a:b], u16, topk * f, f, hidden, f, False)
+
+    t0 = time.perf_counter()
+    _in_threads(run, _split(t, min(threads, t)), min(threads, t))
+    return (time.perf_counter() - t0) * 1e6
+
+
+def cpu_baseline(p, o, seconds=10.0, threads=HOST_THREADS):
+    """The oracle (plain C, binary64, single-threaded per call) on the decode
+    stack's layers:
+      single thread: whole layers of one token, chained, until about `seconds`
+        of CPU time has been spent;
+      all cores: the 32 layers of one token's weights spread over `threads`
+        threads, each layer run by the single-threaded oracle from the same
+        input state (the chain cannot be split across cores, the layers' weight
+        streams can).
+    The main value is the all-cores rate; both are weight GB/s."""
     gi, gp, gf, r0, h0 = host_state(p, p["layers"])
     dims = (p["d"], p["f"], p["n_qkv"], p["v_off"], p["dv"])
     r, h = r0, h0
@@ -774,11 +904,30 @@ def cpu_baseline(p, o, seconds=10.0):
                           r, h, eps=p["eps"])
         spent += time.perf_counter() - t0
         done += 1
-    gbs = stack_weight_bytes(p, done) / spent / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "%d of 32 decode layers of one token (%.1f MB of int4 weights), "
-                      "single-threaded C oracle in binary64, %.1f s" % (
-                          done, stack_weight_bytes(p, done) / 1e6, spent)}
+    one_gbs = stack_weight_bytes(p, done) / spent / 1e9
+    nl = p["layers"]
+    mats_all = [host_layer(p, L) for L in range(nl)]
+
+    def run_layers(rng):
+        for L in range(*rng):
+            o.layer(dims, mats_all[L], gp[L], gi[L + 1] if L + 1 < nl else gf, r0, h0,
+                    eps=p["eps"])
+
+    t0 = time.perf_counter()
+    _in_threads(run_layers, _split(nl, threads), threads)
+    wall = time.perf_counter() - t0
+    all_gbs = stack_weight_bytes(p) / wall / 1e9
+    return {"value": round(all_gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "the 32 decode layers of one token (%.1f MB of int4 weights) over %d "
+                      "threads, each layer one single-threaded call of the C oracle in "
+                      "binary64: %.2f s wall (%.1f us per token's weights)" % (
+                          stack_weight_bytes(p) / 1e6, threads, wall, wall * 1e6),
+            "single_thread": {"value": round(one_gbs, 4), "unit": "GB/s", "cores": 1,
+                              "sample": "%d of 32 layers of one token chained (%.1f MB), "
+                                        "%.1f s" % (done, stack_weight_bytes(p, done) / 1e6,
+                                                    spent),
+                              "us_per_token": round(stack_weight_bytes(p) / (one_gbs * 1e3), 1)},
+            "host": host_info(threads)}
 
 
 def main():
@@ -817,7 +966,8 @@ def main():
     q4.lib()
     assert torch.cuda.is_available(), "no GPU"
     if args.gemv_table:
-        rows = gemv_table(q4, torch)
+        import oracle
+        rows = gemv_table(q4, torch, None if args.no_cpu_baseline else oracle.load())
         write_gemv_table(rows)
         print(json.dumps({"gemv_table": rows}), flush=True)
         return
@@ -931,6 +1081,10 @@ def main():
                                   "second; informational, the peak is the nominal 8 TB/s",
         },
     }
+    rec["context"] = dict(BROWSER_CONTEXT)
+    rec["context"]["this_stack_tok_s"] = round(1e3 / ms, 1)
+    rec["context"]["this_stack_note"] = ("tokens/s of the stack measured here: 32 layers' "
+                                         "matmuls and norms, identity attention, no LM head")
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(p, o, args.cpu_seconds)
     print(json.dumps(rec), flush=True)

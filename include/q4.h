@@ -34,10 +34,17 @@
  *   - Entry points that need scratch memory (split partials of the batched,
  *     prefill and attention kernels, MoE routing and partials, LM-head argmax
  *     candidates, the stack's intermediate vectors) use a library-owned
- *     workspace allocated per (device, stream) on first use, grown when a
- *     larger call needs more, and kept until the process ends; concurrent calls
- *     on distinct streams do not share it. A call that allocates synchronises
- *     the device, so warm up on a stream before capturing a HIP graph on it.
+ *     workspace per (device, stream); concurrent calls on distinct streams do
+ *     not share it. q4_workspace_bytes / q4_attention_workspace_bytes /
+ *     q4_stack_workspace_bytes give what a call needs and q4_workspace_reserve
+ *     allocates it ahead of time. A call whose need exceeds the stream's
+ *     workspace allocates a larger one (hipMalloc; the header is cleared in
+ *     stream order, no device synchronisation) and keeps the replaced buffer
+ *     until q4_workspace_release, since work already enqueued or a HIP graph
+ *     captured earlier may still use it. During HIP graph capture on the
+ *     stream nothing is allocated: such a call returns Q4_ERANGE and enqueues
+ *     nothing, so reserve before capturing. Calls on one stream are ordered by
+ *     the stream and may share the workspace.
  */
 #ifndef Q4_H
 #define Q4_H
@@ -366,12 +373,11 @@ q4_status q4_attention_decode(const uint16_t *q, const uint16_t *kv_pages,
  * gamma_final f16[d]. r_in/h_in are read, r_out/h_out written (f16[d]); inputs
  * and outputs must not overlap. trace (may be NULL) receives the state after
  * every layer: f16[n_layers][2][d] as (r, h) pairs.
- * mode: Q4_STACK_AUTO and Q4_STACK_MULTI run four matvec launches per layer
- * (the faster path on gfx950 at the shapes measured); Q4_STACK_PERSISTENT runs
- * every layer in one cooperative launch and requires that the shapes and
- * buffers allow it (V slice last in the QKV rows; r_out, h_out, trace 16-byte
- * aligned; a phase's slice per CU within the kernel's register budget),
- * Q4_ERANGE otherwise. Both paths give bit-identical results.
+ * mode: Q4_STACK_AUTO and Q4_STACK_MULTI (the same path) run four matvec
+ * launches per layer; the dependent steps are ordered by kernel boundaries,
+ * which on gfx950 cost less than any grid-wide synchronisation inside a
+ * kernel while the weights stream. Any other mode is Q4_EINVAL.
+ * Workspace: q4_stack_workspace_bytes(desc, NULL) bytes of the stream's.
  */
 typedef struct q4_stack_desc {
     int64_t n_layers, d, f, n_qkv, v_off, dv;
@@ -390,7 +396,7 @@ typedef struct q4_stack_desc {
     int mode; /* q4_stack_mode */
 } q4_stack_desc;
 
-typedef enum q4_stack_mode { Q4_STACK_AUTO = 0, Q4_STACK_MULTI = 1, Q4_STACK_PERSISTENT = 2 } q4_stack_mode;
+typedef enum q4_stack_mode { Q4_STACK_AUTO = 0, Q4_STACK_MULTI = 1 } q4_stack_mode;
 
 q4_status q4_stack_decode(const q4_stack_desc *desc, const uint16_t *r_in,
                           const uint16_t *h_in, uint16_t *r_out, uint16_t *h_out,
@@ -405,10 +411,10 @@ q4_status q4_stack_decode(const q4_stack_desc *desc, const uint16_t *r_in,
  *   o = f16(Wo[L] . a), then add+RMSNorm, gate_up + SiLU*mul, down, add+RMSNorm
  *       as in q4_stack_decode.
  * The descriptor's n_qkv must be (n_heads + 2 n_kv) * head_dim and dv must be
- * n_heads * head_dim (v_off is unused); mode Q4_STACK_PERSISTENT is
- * Q4_EINVAL (the attention runs on the multi-kernel path). attn->kv_pages is a
- * HOST array of n_layers device caches of attn->geom's geometry; the page
- * table and the position (device) are shared by the layers. */
+ * n_heads * head_dim (v_off is unused). attn->kv_pages is a HOST array of
+ * n_layers device caches of attn->geom's geometry; the page table and the
+ * position (device) are shared by the layers. Workspace:
+ * q4_stack_workspace_bytes(desc, attn) bytes of the stream's. */
 typedef struct q4_stack_attn {
     const q4_attn_desc *geom;
     uint16_t *const *kv_pages;
@@ -421,11 +427,41 @@ q4_status q4_stack_decode_attn(const q4_stack_desc *desc, const q4_stack_attn *a
                                const uint16_t *r_in, const uint16_t *h_in, uint16_t *r_out,
                                uint16_t *h_out, uint16_t *trace, q4_stream stream);
 
-/* q4_stack_status -- synchronises `stream` and reports whether a persistent
- * q4_stack_decode on it gave up waiting for data (every wait inside the kernel
- * is bounded; a timeout makes the kernel finish with undefined outputs and is
- * reported here as Q4_EHIP, once). Q4_OK otherwise. */
-q4_status q4_stack_status(q4_stream stream);
+/* ---------------------------------------------------------------------------
+ * Workspace (the library-owned scratch of a stream; see the conventions at the
+ * top). Sizes are in bytes and include a 256-byte header; 0 means the call
+ * needs none (or the arguments are invalid). Host-only; no device work.
+ *
+ * q4_workspace_bytes -- the most any one matmul-family call on an N x K
+ * matrix with M activation rows needs: q4_gemv_batched, q4_gemv_f32,
+ * q4_gemv_affine (M <= Q4_MAX_M), q4_lm_head_argmax (M <= Q4_MAX_M),
+ * q4_argmax over M rows of N (M <= 65535), q4_gemm and q4_gemm_affine (M <=
+ * Q4_MAX_GEMM_M, any ldx), q4_moe_gemv with M = T * TOPK pairs (any E).
+ * q4_gemv, q4_gemv_ex, q4_qkv_rope_append, q4_rope_append, q4_add_rmsnorm,
+ * q4_silu_mul, q4_pack and q4_unpack use no workspace.
+ */
+size_t q4_workspace_bytes(int64_t N, int64_t K, int64_t M);
+
+/* q4_attention_workspace_bytes -- what q4_attention_decode needs for the
+ * geometry and max_len (its split partials; 0 when one split suffices). */
+size_t q4_attention_workspace_bytes(const q4_attn_desc *desc, int64_t max_len);
+
+/* q4_stack_workspace_bytes -- what q4_stack_decode (attn NULL) or
+ * q4_stack_decode_attn needs: the intermediate vectors of a layer and, with
+ * attention, its output and split partials. */
+size_t q4_stack_workspace_bytes(const q4_stack_desc *desc, const q4_stack_attn *attn);
+
+/* q4_workspace_reserve -- makes the workspace of `stream` on the current
+ * device at least `bytes` large (allocating as a growing call does; Q4_ERANGE
+ * during graph capture on the stream if it would have to grow). After it, no
+ * call on the stream whose need is at most `bytes` allocates or synchronises,
+ * so such calls may be captured into a HIP graph. */
+q4_status q4_workspace_reserve(q4_stream stream, size_t bytes);
+
+/* q4_workspace_release -- synchronises `stream` and frees its workspace and
+ * every buffer it replaced. The caller guarantees that no HIP graph still to
+ * be launched uses them. Q4_OK if the stream has none. */
+q4_status q4_workspace_release(q4_stream stream);
 
 /* Measurement hook (not part of the method): q4_timer_arm(slot) makes the next
  * matvec kernel that this thread launches through libq4 record its dispatch

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(PKG, "libq4.so")
 
 Q4_OK, Q4_EINVAL, Q4_ESHAPE, Q4_EALIGN, Q4_EALIAS, Q4_ERANGE, Q4_EHIP = range(7)
 EPI_NONE, EPI_SILU_MUL, EPI_ADD_RMSNORM = 0, 1, 2
-STACK_AUTO, STACK_MULTI, STACK_PERSISTENT = 0, 1, 2
+STACK_AUTO, STACK_MULTI = 0, 1
 MAX_K = 24576
 MAX_M = 64
 MAX_GEMM_M = 65536
@@ -34,10 +34,11 @@ BYTES_PER_WEIGHT = 0.5 + 2.0 / 32.0
 ABI_SYMBOLS = (
     "q4_version", "q4_last_error", "q4_bytes_per_weight", "q4_pack", "q4_unpack", "q4_gemv",
     "q4_gemv_batched", "q4_moe_gemv", "q4_add_rmsnorm", "q4_silu_mul", "q4_gemv_ex",
-    "q4_stack_decode", "q4_stack_status", "q4_timer_arm", "q4_timer_read", "q4_gemv_f32",
+    "q4_stack_decode", "q4_timer_arm", "q4_timer_read", "q4_gemv_f32",
     "q4_argmax", "q4_lm_head_argmax", "q4_kv_page_bytes", "q4_qkv_rope_append",
     "q4_rope_append", "q4_attention_decode", "q4_stack_decode_attn", "q4_gemv_affine",
-    "q4_gemm", "q4_gemm_affine",
+    "q4_gemm", "q4_gemm_affine", "q4_workspace_bytes", "q4_attention_workspace_bytes",
+    "q4_stack_workspace_bytes", "q4_workspace_reserve", "q4_workspace_release",
 )
 
 
@@ -90,7 +91,6 @@ _SIGS = {
     "q4_silu_mul": (C.c_int, [_P, _P, _I, _I, _P]),
     "q4_gemv_ex": (C.c_int, [_P, _P, _P, _P, _I, _I, C.POINTER(Epilogue), _P]),
     "q4_stack_decode": (C.c_int, [C.POINTER(StackDesc), _P, _P, _P, _P, _P, _P]),
-    "q4_stack_status": (C.c_int, [_P]),
     "q4_timer_arm": (C.c_int, [C.c_int]),
     "q4_timer_read": (C.c_int, [C.c_int, C.POINTER(C.c_float)]),
     "q4_gemv_f32": (C.c_int, [_P, _P, _P, _I, _P, _I, _I, _I, _I, _P]),
@@ -103,6 +103,11 @@ _SIGS = {
     "q4_attention_decode": (C.c_int, [_P, _P, _P, _P, _I, C.POINTER(AttnDesc), _P, _P]),
     "q4_stack_decode_attn": (C.c_int, [C.POINTER(StackDesc), C.POINTER(StackAttn), _P, _P, _P, _P,
                                        _P, _P]),
+    "q4_workspace_bytes": (C.c_size_t, [_I, _I, _I]),
+    "q4_attention_workspace_bytes": (C.c_size_t, [C.POINTER(AttnDesc), _I]),
+    "q4_stack_workspace_bytes": (C.c_size_t, [C.POINTER(StackDesc), C.POINTER(StackAttn)]),
+    "q4_workspace_reserve": (C.c_int, [_P, C.c_size_t]),
+    "q4_workspace_release": (C.c_int, [_P]),
 }
 
 _lib = None
@@ -444,9 +449,32 @@ class Stack:
                                           _stream(stream)))
 
 
-def stack_status(stream=None):
-    """Synchronise and raise if a persistent stack kernel timed out waiting."""
-    _check(lib().q4_stack_status(_stream(stream)))
+def workspace_bytes(n, k, m):
+    """Workspace bytes the largest matmul-family call on an n x k matrix with m
+    activation rows (or MoE pairs) needs (q4_workspace_bytes)."""
+    return int(lib().q4_workspace_bytes(int(n), int(k), int(m)))
+
+
+def attention_workspace_bytes(desc, max_len):
+    return int(lib().q4_attention_workspace_bytes(C.byref(desc), int(max_len)))
+
+
+def stack_workspace_bytes(stack, geom=None):
+    """Workspace bytes of stack.decode (geom None) or stack.decode_attn."""
+    if geom is None:
+        return int(lib().q4_stack_workspace_bytes(C.byref(stack.desc), None))
+    a = StackAttn(C.pointer(geom), None, None, None, 1)
+    return int(lib().q4_stack_workspace_bytes(C.byref(stack.desc), C.byref(a)))
+
+
+def workspace_reserve(nbytes, stream=None):
+    """Allocate the stream's workspace ahead of time (q4_workspace_reserve)."""
+    _check(lib().q4_workspace_reserve(_stream(stream), int(nbytes)))
+
+
+def workspace_release(stream=None):
+    """Synchronise the stream and free its workspace (q4_workspace_release)."""
+    _check(lib().q4_workspace_release(_stream(stream)))
 
 
 def timer_arm(slot):

@@ -8,7 +8,7 @@
 #include <utility>
 
 #include "q4_common.h"
-#include "q4_stack.h"
+#include <algorithm>
 #include <cstring>
 #include <vector>
 
@@ -16,6 +16,7 @@ namespace q4 {
 
 namespace {
 thread_local char g_err[512] = "";
+thread_local q4_status g_ws_status = Q4_OK;  // last workspace() failure
 
 // q4_timer_arm / q4_timer_read state, per thread
 constexpr int kTimerSlots = 64;
@@ -25,8 +26,16 @@ struct TimerSlot {
 };
 thread_local TimerSlot g_timers[kTimerSlots];
 thread_local int g_armed = -1;
+// Library workspace per (device, stream): the current buffer and the buffers it
+// replaced (kept until q4_workspace_release or the end of the process; no HIP
+// call is made at static teardown).
+struct Workspace {
+    void *buf = nullptr;
+    size_t bytes = 0;
+    std::vector<void *> retired;
+};
 std::mutex g_ws_mu;
-std::map<std::pair<int, hipStream_t>, std::pair<void *, size_t>> g_ws;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 }  // namespace
 
 q4_status fail(q4_status st, const char *fmt, ...)
@@ -75,39 +84,59 @@ int cu_count()
     return n[dev];
 }
 
+namespace {
+// Grows the (device, stream) workspace to at least `bytes` (caller holds
+// g_ws_mu). The replaced buffer is not freed: work already enqueued, or a HIP
+// graph captured earlier, may still use it; q4_workspace_release frees it.
+void *grow_locked(int dev, hipStream_t stream, size_t bytes)
+{
+    Workspace &e = g_ws[{dev, stream}];
+    if (e.buf && e.bytes >= bytes)
+        return e.buf;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess) {
+        g_ws_status = fail(Q4_EHIP, "hipStreamIsCapturing failed");
+        return nullptr;
+    }
+    if (cap != hipStreamCaptureStatusNone) {
+        g_ws_status = fail(Q4_ERANGE,
+             "the stream's workspace (%zu bytes) is smaller than the %zu bytes this call needs "
+             "and cannot grow during graph capture; call q4_workspace_reserve before capturing",
+             e.bytes, bytes);
+        return nullptr;
+    }
+    const size_t nb = bytes < (size_t)(1 << 20) ? (size_t)(1 << 20) : bytes;
+    void *p = nullptr;
+    if (hipMalloc(&p, nb) != hipSuccess) {
+        g_ws_status = fail(Q4_EHIP, "hipMalloc of a %zu-byte workspace failed", nb);
+        return nullptr;
+    }
+    // the header is cleared in stream order, ahead of every use on this stream
+    if (hipMemsetAsync(p, 0, kCounterBytes, stream) != hipSuccess) {
+        (void)hipFree(p);  // nothing was enqueued on it; the error reported is the one below
+        g_ws_status = fail(Q4_EHIP, "clearing the workspace header failed");
+        return nullptr;
+    }
+    if (e.buf)
+        e.retired.push_back(e.buf);
+    e.buf = p;
+    e.bytes = nb;
+    return p;
+}
+}  // namespace
+
 void *workspace(hipStream_t stream, size_t bytes)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) {
-        fail(Q4_EHIP, "hipGetDevice failed");
+        g_ws_status = fail(Q4_EHIP, "hipGetDevice failed");
         return nullptr;
     }
     std::lock_guard<std::mutex> lock(g_ws_mu);
-    auto &e = g_ws[{dev, stream}];
-    if (e.first && e.second >= bytes)
-        return e.first;
-    if (e.first) {
-        // growing: the old buffer may still be in use by work on this stream
-        if (hipStreamSynchronize(stream) != hipSuccess || hipFree(e.first) != hipSuccess) {
-            fail(Q4_EHIP, "releasing the workspace failed");
-            return nullptr;
-        }
-        e = {nullptr, 0};
-    }
-    size_t nb = bytes < (size_t)(1 << 20) ? (size_t)(1 << 20) : bytes;
-    void *p = nullptr;
-    if (hipMalloc(&p, nb) != hipSuccess) {
-        fail(Q4_EHIP, "hipMalloc of a %zu-byte workspace failed", nb);
-        return nullptr;
-    }
-    if (hipMemset(p, 0, kCounterBytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
-        (void)hipFree(p);  // the error reported is the one above
-        fail(Q4_EHIP, "clearing the workspace counters failed");
-        return nullptr;
-    }
-    e = {p, nb};
-    return p;
+    return grow_locked(dev, stream, bytes);
 }
+
+q4_status workspace_status() { return g_ws_status == Q4_OK ? Q4_EHIP : g_ws_status; }
 
 }  // namespace q4
 
@@ -170,6 +199,23 @@ struct StackAttn {
     int64_t max_len = 0;
 };
 
+// Workspace of a stack call: header | qkv | r1 | u | rA | rB [| attention
+// output | attention partials] (256-byte aligned pieces); geom: the attention
+// geometry, or nullptr for the single-position stack.
+struct StackWs {
+    size_t q_b, v_b, u_b, a_b, part_b, total;
+    StackWs(const q4_stack_desc *d, const RopeArgs *geom)
+    {
+        auto al = [](size_t b) { return (b + 255) / 256 * 256; };
+        q_b = al((size_t)d->n_qkv * 2);
+        v_b = al((size_t)d->d * 2);
+        u_b = al((size_t)d->f * 2);
+        a_b = geom ? al((size_t)d->dv * 2) : 0;
+        part_b = geom ? al(attention_part_bytes(*geom)) : 0;
+        total = kWsHeader + q_b + 3 * v_b + u_b + a_b + part_b;
+    }
+};
+
 q4_status stack_multi(const q4_stack_desc *d, const StackAttn *attn, const uint16_t *r_in,
                       const uint16_t *h_in, uint16_t *r_out, uint16_t *h_out, uint16_t *trace,
                       hipStream_t st)
@@ -180,16 +226,11 @@ q4_status stack_multi(const q4_stack_desc *d, const StackAttn *attn, const uint1
     // residual add happens row by row in the O / down epilogues, and the
     // RMSNorm that follows it is recomputed by every workgroup of the next
     // matvec while it stages its activation (bit-identical to q4_add_rmsnorm).
-    // workspace: header | qkv | r1 | u | rA | rB [| attention output | partials]
-    // (256-byte aligned pieces)
-    auto al = [](size_t b) { return (b + 255) / 256 * 256; };
-    const size_t q_b = al((size_t)d->n_qkv * 2), v_b = al(vb), u_b = al((size_t)F * 2);
-    const size_t a_b = attn ? al((size_t)d->dv * 2) : 0;
-    const size_t part_b = attn ? al(attention_part_bytes(attn->geom)) : 0;
-    const size_t total = kWsHeader + q_b + 3 * v_b + u_b + a_b + part_b;
-    char *ws = static_cast<char *>(workspace(st, total));
+    const StackWs w(d, attn ? &attn->geom : nullptr);
+    const size_t q_b = w.q_b, v_b = w.v_b, u_b = w.u_b, a_b = w.a_b;
+    char *ws = static_cast<char *>(workspace(st, w.total));
     if (!ws)
-        return Q4_EHIP;
+        return workspace_status();
     uint16_t *qkv = reinterpret_cast<uint16_t *>(ws + kWsHeader);
     uint16_t *att = reinterpret_cast<uint16_t *>(ws + kWsHeader + q_b + 3 * v_b + u_b);
     float *part = reinterpret_cast<float *>(ws + kWsHeader + q_b + 3 * v_b + u_b + a_b);
@@ -283,170 +324,6 @@ q4_status stack_multi(const q4_stack_desc *d, const StackAttn *attn, const uint1
                               st);
 }
 
-
-// ---------------------------------------------------------------------------
-// Decode stack: persistent path (one cooperative launch per token)
-// ---------------------------------------------------------------------------
-struct StackState {
-    char *mem = nullptr;
-    size_t bytes = 0;
-    uint32_t epoch = 0;                 // tag of the next call's first phase
-    std::vector<const void *> table;    // host copy of the uploaded pointer tables
-    size_t off_tab = 0, off_v = 0, off_r1 = 0, off_u = 0, off_r2 = 0, off_qkv = 0;
-};
-std::mutex g_stack_mu;
-std::map<std::pair<int, hipStream_t>, StackState> g_stack;
-
-q4_status stack_persistent(const q4_stack_desc *d, const uint16_t *r_in, const uint16_t *h_in,
-                           uint16_t *r_out, uint16_t *h_out, uint16_t *trace, hipStream_t st,
-                           bool *ran)
-{
-    *ran = false;
-    const int L = (int)d->n_layers, D = (int)d->d, F = (int)d->f, NQ = (int)d->n_qkv;
-    const int DV = (int)d->dv, VOFF = (int)d->v_off;
-    if (VOFF + DV != NQ)
-        return fail(Q4_OK, "the V slice is not the last rows of the QKV matrix");
-    if (!aligned(r_out, 16) || !aligned(h_out, 16) || (trace && !aligned(trace, 16)))
-        return fail(Q4_OK, "r_out, h_out and trace must be 16-byte aligned");
-    int dev = 0;
-    Q4_HIP(hipGetDevice(&dev));
-    int coop = 0, nb = 0;
-    Q4_HIP(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev));
-    Q4_HIP(hipDeviceGetAttribute(&nb, hipDeviceAttributeMultiprocessorCount, dev));
-    if (!coop)
-        return fail(Q4_OK, "cooperative launch is not supported");
-    auto per = [&](int n) { return (n + nb - 1) / nb; };
-    const int kmax = std::max(D, std::max(DV, F));
-    int stmax = std::max(std::max(per(DV) * (D / 32), per(VOFF) * (D / 32)),
-                         std::max(per(D) * (DV / 32),
-                                  std::max(2 * per(F) * (D / 32), per(D) * (F / 32))));
-    // the compute lanes hold the weights of a phase, kStackNch groups per lane
-    if (stmax > kStackNch * kStackCompute)
-        return fail(Q4_OK, "a phase slice of %d groups exceeds the kernel's %d", stmax,
-                    kStackNch * kStackCompute);
-    // LDS carve-up: staged activation (+ 7 * group sums) for K = kmax and for
-    // the O phase, per-chunk partials, the residual of a norm, SiLU row values
-    // and this workgroup's residual rows
-    auto a16 = [](size_t b) { return (b + 15) / 16 * 16; };
-    size_t lds = 0;
-    auto carve = [&](size_t bytes) {
-        const size_t o = lds;
-        lds += a16(bytes);
-        return (int)o;
-    };
-    const int lds_xs = carve((size_t)kmax * 2), lds_cs = carve((size_t)kmax / 8);
-    const int lds_xo = carve((size_t)DV * 2), lds_co = carve((size_t)DV / 8);
-    const int lds_st = carve((size_t)stmax * 8), lds_raw = carve((size_t)D * 2);
-    const int lds_rowv = carve((size_t)2 * per(F) * 4), lds_lres = carve((size_t)per(D) * 4);
-    int max_lds = 0;
-    Q4_HIP(hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev));
-    if (lds + 64 > (size_t)max_lds)
-        return fail(Q4_OK, "the persistent kernel would need %zu bytes of LDS", lds);
-    Q4_HIP(hipFuncSetAttribute(stack_kernel(), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)lds));
-    int occ = 0;
-    Q4_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, stack_kernel(), kStackThreads, lds));
-    if (occ < 1)
-        return fail(Q4_OK, "one workgroup per CU does not fit");
-
-    auto al = [](size_t b) { return (b + 255) / 256 * 256; };
-    StackState *S;
-    {
-        std::lock_guard<std::mutex> lock(g_stack_mu);
-        S = &g_stack[{dev, st}];
-    }
-    const size_t off_tab = 256, tab_b = al((size_t)L * 8 * sizeof(void *));
-    const size_t R = kStackCopies;  // copies of each published vector and flag array
-    const size_t off_v = off_tab + tab_b, off_r1 = off_v + al(R * DV * 4);
-    const size_t off_u = off_r1 + al(R * D * 4), off_r2 = off_u + al(R * F * 4);
-    const size_t off_fl = off_r2 + al(R * D * 4), off_qkv = off_fl + al(4 * R * nb * 4);
-    const size_t total = off_qkv + al((size_t)NQ * 2);
-    if (!S->mem || S->bytes < total || S->off_v != off_v || S->off_r1 != off_r1 ||
-        S->off_u != off_u || S->off_r2 != off_r2) {
-        if (S->mem) {
-            Q4_HIP(hipStreamSynchronize(st));
-            Q4_HIP(hipFree(S->mem));
-            S->mem = nullptr;
-        }
-        void *m = nullptr;
-        Q4_HIP(hipMalloc(&m, total));
-        // tags 0xFFFF never match a phase: every buffer starts out stale
-        Q4_HIP(hipMemset(m, 0, 256));
-        Q4_HIP(hipMemset(static_cast<char *>(m) + off_v, 0xFF, off_qkv - off_v));
-        Q4_HIP(hipDeviceSynchronize());
-        S->mem = static_cast<char *>(m);
-        S->bytes = total;
-        S->table.clear();
-        S->off_tab = off_tab;
-        S->off_v = off_v;
-        S->off_r1 = off_r1;
-        S->off_u = off_u;
-        S->off_r2 = off_r2;
-        S->off_qkv = off_qkv;
-    }
-    // device pointer tables [L][4] of weights, then scales (uploaded when they change)
-    std::vector<const void *> tab((size_t)L * 8);
-    for (int l = 0; l < L; ++l) {
-        tab[l * 4 + 0] = d->Wqkv[l];
-        tab[l * 4 + 1] = d->Wo[l];
-        tab[l * 4 + 2] = d->Wgu[l];
-        tab[l * 4 + 3] = d->Wdn[l];
-        tab[(size_t)L * 4 + l * 4 + 0] = d->Sqkv[l];
-        tab[(size_t)L * 4 + l * 4 + 1] = d->So[l];
-        tab[(size_t)L * 4 + l * 4 + 2] = d->Sgu[l];
-        tab[(size_t)L * 4 + l * 4 + 3] = d->Sdn[l];
-    }
-    if (tab != S->table) {
-        Q4_HIP(hipStreamSynchronize(st));
-        Q4_HIP(hipMemcpy(S->mem + off_tab, tab.data(), tab.size() * sizeof(void *),
-                         hipMemcpyHostToDevice));
-        S->table = tab;
-    }
-
-    StackParams p{};
-    p.n_layers = L;
-    p.d = D;
-    p.f = F;
-    p.n_qkv = NQ;
-    p.v_off = VOFF;
-    p.dv = DV;
-    p.eps = d->eps;
-    p.W = reinterpret_cast<const uint32_t *const *>(S->mem + off_tab);
-    p.S = reinterpret_cast<const uint16_t *const *>(S->mem + off_tab + (size_t)L * 4 * sizeof(void *));
-    p.gamma_in = d->gamma_in;
-    p.gamma_post = d->gamma_post;
-    p.gamma_final = d->gamma_final;
-    p.r_in = r_in;
-    p.h_in = h_in;
-    p.r_out = r_out;
-    p.h_out = h_out;
-    p.trace = trace;
-    p.qkv = reinterpret_cast<uint16_t *>(S->mem + off_qkv);
-    p.vbuf = reinterpret_cast<uint32_t *>(S->mem + off_v);
-    p.r1buf = reinterpret_cast<uint32_t *>(S->mem + off_r1);
-    p.ubuf = reinterpret_cast<uint32_t *>(S->mem + off_u);
-    p.r2buf = reinterpret_cast<uint32_t *>(S->mem + off_r2);
-    p.flags = reinterpret_cast<uint32_t *>(S->mem + off_fl);
-    p.epoch0 = S->epoch;
-    S->epoch = (uint32_t)((S->epoch + 4ull * L) % 0xFFFFu);
-    p.err = reinterpret_cast<unsigned *>(S->mem);
-    p.lds_xs = lds_xs;
-    p.lds_cs = lds_cs;
-    p.lds_xo = lds_xo;
-    p.lds_co = lds_co;
-    p.lds_st = lds_st;
-    p.lds_raw = lds_raw;
-    p.lds_rowv = lds_rowv;
-    p.lds_lres = lds_lres;
-    matvec_layout(D / 32, &p.lpr_d, &p.ng_d);
-    matvec_layout(DV / 32, &p.lpr_v, &p.ng_v);
-    matvec_layout(F / 32, &p.lpr_f, &p.ng_f);
-    void *args[] = {&p};
-    Q4_HIP(hipLaunchCooperativeKernel(stack_kernel(), dim3(nb), dim3(kStackThreads), args, (unsigned)lds,
-                                      st));
-    *ran = true;
-    return Q4_OK;
-}
 
 q4_status check_f32_matvec(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
                            const float *y, int64_t ldy, int64_t N, int64_t K, int64_t M)
@@ -583,8 +460,8 @@ q4_status check_stack(const q4_stack_desc *d, const uint16_t *r_in, const uint16
             return st;
     }
     const int mode = d->mode;
-    if (mode != Q4_STACK_AUTO && mode != Q4_STACK_MULTI && mode != Q4_STACK_PERSISTENT)
-        return fail(Q4_EINVAL, "unknown stack mode %d", mode);
+    if (mode != Q4_STACK_AUTO && mode != Q4_STACK_MULTI)
+        return fail(Q4_EINVAL, "unknown stack mode %d (Q4_STACK_AUTO or Q4_STACK_MULTI)", mode);
     return Q4_OK;
 }
 }  // namespace
@@ -1062,6 +939,74 @@ q4_status q4_silu_mul(const uint16_t *gu, uint16_t *out, int64_t F, int64_t M, q
 }
 
 
+size_t q4_workspace_bytes(int64_t N, int64_t K, int64_t M)
+{
+    if (N < 1 || N > (1ll << 30) || K < 32 || K % 32 || K > Q4_MAX_K || M < 1)
+        return 0;
+    const int n = (int)N, k = (int)K;
+    size_t need = 0;
+    if (M <= Q4_MAX_M) {  // batched, f32 and affine matvecs; LM head + argmax
+        need = std::max(need, ws_rows(n, k, (int)M));
+        need = std::max(need, ws_lm_head(n, k, (int)M));
+    }
+    if (M <= 65535)  // argmax over M rows of N logits
+        need = std::max(need, ws_argmax(n, (int)M));
+    if (M <= Q4_MAX_GEMM_M) {  // prefill, both formats (ldx = K needs the most)
+        need = std::max(need, ws_gemm(n, k, (int)M, false, K));
+        if (K % 64 == 0)
+            need = std::max(need, ws_gemm(n, k, (int)M, true, K));
+    }
+    if (M <= Q4_MAX_PAIRS)  // one MoE expert stage over M (token, slot) pairs, any E
+        need = std::max(need, ws_moe(1 << 30, n, k, (int)M));
+    return need;
+}
+
+size_t q4_attention_workspace_bytes(const q4_attn_desc *desc, int64_t max_len)
+{
+    RopeArgs r;
+    if (max_len < 1 || check_attn_desc(desc, &r) != Q4_OK)
+        return 0;
+    return ws_attention(r, max_len);
+}
+
+size_t q4_stack_workspace_bytes(const q4_stack_desc *desc, const q4_stack_attn *attn)
+{
+    if (!desc || desc->d <= 0 || desc->f <= 0 || desc->n_qkv <= 0 || desc->dv <= 0)
+        return 0;
+    RopeArgs r;
+    if (attn && check_attn_desc(attn->geom, &r) != Q4_OK)
+        return 0;
+    return StackWs(desc, attn ? &r : nullptr).total;
+}
+
+q4_status q4_workspace_reserve(q4_stream stream, size_t bytes)
+{
+    if (bytes == 0)
+        return Q4_OK;
+    return workspace(as_stream(stream), bytes) ? Q4_OK : workspace_status();
+}
+
+q4_status q4_workspace_release(q4_stream stream)
+{
+    hipStream_t st = as_stream(stream);
+    int dev = 0;
+    Q4_HIP(hipGetDevice(&dev));
+    Q4_HIP(hipStreamSynchronize(st));
+    Workspace w;
+    {
+        std::lock_guard<std::mutex> lock(g_ws_mu);
+        auto it = g_ws.find({dev, st});
+        if (it == g_ws.end())
+            return Q4_OK;
+        w = std::move(it->second);
+        g_ws.erase(it);
+    }
+    w.retired.push_back(w.buf);
+    for (void *p : w.retired)
+        Q4_HIP(hipFree(p));
+    return Q4_OK;
+}
+
 q4_status q4_stack_decode(const q4_stack_desc *d, const uint16_t *r_in, const uint16_t *h_in,
                           uint16_t *r_out, uint16_t *h_out, uint16_t *trace, q4_stream stream)
 {
@@ -1069,15 +1014,6 @@ q4_status q4_stack_decode(const q4_stack_desc *d, const uint16_t *r_in, const ui
     if (s != Q4_OK)
         return s;
     hipStream_t st = as_stream(stream);
-    if (d->mode == Q4_STACK_PERSISTENT) {
-        bool ran = false;
-        s = stack_persistent(d, r_in, h_in, r_out, h_out, trace, st, &ran);
-        if (s != Q4_OK || ran)
-            return s;
-        char why[sizeof(g_err)];
-        memcpy(why, g_err, sizeof(why));
-        return fail(Q4_ERANGE, "the persistent stack kernel cannot run here: %s", why);
-    }
     return stack_multi(d, nullptr, r_in, h_in, r_out, h_out, trace, st);
 }
 
@@ -1088,8 +1024,6 @@ q4_status q4_stack_decode_attn(const q4_stack_desc *d, const q4_stack_attn *attn
     q4_status s = check_stack(d, r_in, h_in, r_out, h_out, trace, false);
     if (s != Q4_OK)
         return s;
-    if (d->mode == Q4_STACK_PERSISTENT)
-        return fail(Q4_EINVAL, "the attention stack runs on the multi-kernel path");
     if (!attn || !attn->kv_pages)
         return fail(Q4_EINVAL, "NULL attention description or cache array");
     StackAttn a;
@@ -1124,29 +1058,6 @@ q4_status q4_stack_decode_attn(const q4_stack_desc *d, const q4_stack_attn *attn
     a.kv_pages = attn->kv_pages;
     a.max_len = attn->max_len;
     return stack_multi(d, &a, r_in, h_in, r_out, h_out, trace, as_stream(stream));
-}
-
-q4_status q4_stack_status(q4_stream stream)
-{
-    hipStream_t st = as_stream(stream);
-    Q4_HIP(hipStreamSynchronize(st));
-    int dev = 0;
-    Q4_HIP(hipGetDevice(&dev));
-    unsigned *err = nullptr;
-    {
-        std::lock_guard<std::mutex> lock(g_stack_mu);
-        auto it = g_stack.find({dev, st});
-        if (it == g_stack.end())
-            return Q4_OK;
-        err = reinterpret_cast<unsigned *>(it->second.mem);
-    }
-    unsigned h = 0;
-    Q4_HIP(hipMemcpy(&h, err, sizeof(h), hipMemcpyDeviceToHost));
-    if (!h)
-        return Q4_OK;
-    const unsigned zero = 0;
-    Q4_HIP(hipMemcpy(err, &zero, sizeof(zero), hipMemcpyHostToDevice));
-    return fail(Q4_EHIP, "a persistent decode-stack kernel timed out waiting for data");
 }
 
 }  // extern "C"

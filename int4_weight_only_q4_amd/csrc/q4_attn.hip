@@ -256,8 +256,9 @@ size_t attention_part_bytes(const RopeArgs &r)
     return (size_t)r.n_heads * kMaxSplits * (2 + r.head_dim) * sizeof(float);
 }
 
-q4_status launch_attention(const uint16_t *q, const uint16_t *kv, const RopeArgs &r,
-                           int64_t max_len, uint16_t *out, hipStream_t stream, float *part)
+namespace {
+// Splits of the positions per head for a call bounded by max_len positions.
+int attention_splits(const RopeArgs &r, int64_t max_len)
 {
     const int64_t cap = (int64_t)r.max_pages * r.page_size;
     const int64_t len = std::max<int64_t>(1, std::min(max_len, cap));
@@ -268,14 +269,25 @@ q4_status launch_attention(const uint16_t *q, const uint16_t *kv, const RopeArgs
     const int64_t fill = (2 * (int64_t)cu + r.n_heads - 1) / r.n_heads;
     const int64_t by_grain = std::min<int64_t>((len + kSplitGrain - 1) / kSplitGrain, fill);
     const int64_t by_block = (len + kAttnThreads - 1) / kAttnThreads;
-    const int NS = len <= kAttnThreads
-                       ? 1
-                       : (int)std::min<int64_t>(kMaxSplits, std::max(by_grain, by_block));
+    return len <= kAttnThreads ? 1
+                               : (int)std::min<int64_t>(kMaxSplits, std::max(by_grain, by_block));
+}
+}  // namespace
+
+size_t ws_attention(const RopeArgs &r, int64_t max_len)
+{
+    return attention_splits(r, max_len) > 1 ? kWsHeader + attention_part_bytes(r) : 0;
+}
+
+q4_status launch_attention(const uint16_t *q, const uint16_t *kv, const RopeArgs &r,
+                           int64_t max_len, uint16_t *out, hipStream_t stream, float *part)
+{
+    const int NS = attention_splits(r, max_len);
     const float scale = (float)(1.0 / std::sqrt((double)r.head_dim));
     if (NS > 1 && !part) {
-        char *ws = static_cast<char *>(workspace(stream, kWsHeader + attention_part_bytes(r)));
+        char *ws = static_cast<char *>(workspace(stream, ws_attention(r, max_len)));
         if (!ws)
-            return Q4_EHIP;
+            return workspace_status();
         part = reinterpret_cast<float *>(ws + kWsHeader);
     }
     const dim3 grid(r.n_heads, NS);

@@ -46,11 +46,27 @@ bool take_armed_timer(hipEvent_t *start, hipEvent_t *stop);
     } while (0)
 
 // Library-owned scratch for one (device, stream): at least `bytes` bytes. Its
-// first kWsHeader bytes are reserved (zero-initialised counters); callers place
-// their own data after them. Returns nullptr (and sets the error) on failure.
+// first kWsHeader bytes are reserved (zero-initialised); callers place their
+// own data after them. A call that needs more than the stream holds allocates
+// a larger buffer, except during graph capture (then it fails with Q4_ERANGE);
+// the replaced buffer stays allocated. Returns nullptr (and sets the error) on
+// failure.
 constexpr size_t kCounterBytes = 256;
 constexpr size_t kWsHeader = kCounterBytes;
 void *workspace(hipStream_t stream, size_t bytes);
+// The status of this thread's last workspace() failure (Q4_ERANGE during graph
+// capture, Q4_EHIP for a HIP error).
+q4_status workspace_status();
+
+// Workspace bytes (header included, 0 = none) that each launcher asks
+// workspace() for; the launchers and q4_workspace_bytes share them.
+size_t ws_rows(int N, int K, int M);   // launch_gemv_batched, launch_gemv_f32, affine rows
+size_t ws_argmax(int N, int M);
+size_t ws_lm_head(int N, int K, int M);
+size_t ws_gemm(int N, int K, int M, bool affine, int64_t ldx);
+size_t ws_moe(int E, int N, int K, int P);
+struct RopeArgs;
+size_t ws_attention(const RopeArgs &r, int64_t max_len);
 // Compute units of the current device (cached per device; 256 if unknown).
 int cu_count();
 

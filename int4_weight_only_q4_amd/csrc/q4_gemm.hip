@@ -551,21 +551,58 @@ q4_status launch_tiles(bool exact, dim3 grid, hipStream_t stream, const uint4 *w
 
 }  // namespace
 
+namespace {
+constexpr size_t kMaxPart = size_t(256) << 20;  // f32 partials of a split launch
+
+// The launches of one prefill call: weight rows in chunks of nchunk, activation
+// rows in chunks of mchunk, so that every buffer of a launch stays under 2^31
+// bytes (whole 128-row tiles).
+struct GemmChunks {
+    int nchunk, mchunk;
+    GemmChunks(int K, int64_t ldx)
+    {
+        const int64_t wrow_bytes = (int64_t)(K / 32) * 16;
+        nchunk = (int)std::max<int64_t>(kBN, ((int64_t(1) << 31) / wrow_bytes) / kBN * kBN);
+        mchunk = (int)std::max<int64_t>(
+            128, ((int64_t(1) << 31) / (2 * std::max<int64_t>(ldx, 1)) - 1) / 128 * 128);
+    }
+};
+
+// f32 partials and (affine) group sums of the launch over mm x nn
+void gemm_scratch(int mm, int nn, int G, bool affine, size_t *part_b, size_t *xsum_b)
+{
+    const int GP = (G / 2 + 63) / 64 * 64;
+    const GemmShape g = gemm_shape(mm, nn, G, kMaxPart, affine ? GP / 64 : 0);
+    *part_b = g.splits > 1 ? (size_t)g.splits * mm * nn * sizeof(float) : 0;
+    *xsum_b = affine ? (size_t)mm * 2 * GP * sizeof(uint16_t) : 0;
+}
+}  // namespace
+
+size_t ws_gemm(int N, int K, int M, bool affine, int64_t ldx)
+{
+    const GemmChunks c(K, ldx);
+    size_t need = 0;
+    for (int n0 = 0; n0 < N; n0 += c.nchunk)
+        for (int m0 = 0; m0 < M; m0 += c.mchunk) {
+            size_t part_b, xsum_b;
+            gemm_scratch(std::min(c.mchunk, M - m0), std::min(c.nchunk, N - n0), K / 32, affine,
+                         &part_b, &xsum_b);
+            if (part_b + xsum_b)
+                need = std::max(need, kWsHeader + part_b + xsum_b);
+        }
+    return need;
+}
+
 q4_status launch_gemm(const uint32_t *W, const uint16_t *S, const uint16_t *X, int64_t ldx,
                       uint16_t *Y, int64_t ldy, int N, int K, int M, bool exact,
                       hipStream_t stream, const uint16_t *bias)
 {
-    constexpr size_t kMaxPart = size_t(256) << 20;  // f32 partials of a split launch
     const int G = K / 32;
     // affine: scales and biases per 64 codes; group sums padded to GP groups
     const int G64 = G / 2, GP = (G64 + 63) / 64 * 64;
     const int sg = bias ? G64 : G;  // scales per weight row
-    // every buffer of a launch under 2^31 bytes: chunks of weight rows (whole
-    // 128-row tiles) and of activation rows (whole 128-row tiles)
-    const int64_t wrow_bytes = (int64_t)G * 16;
-    const int nchunk = (int)std::max<int64_t>(kBN, ((int64_t(1) << 31) / wrow_bytes) / kBN * kBN);
-    const int mchunk = (int)std::max<int64_t>(
-        128, ((int64_t(1) << 31) / (2 * std::max<int64_t>(ldx, 1)) - 1) / 128 * 128);
+    const GemmChunks c(K, ldx);
+    const int nchunk = c.nchunk, mchunk = c.mchunk;
     for (int n0 = 0; n0 < N; n0 += nchunk)
         for (int m0 = 0; m0 < M; m0 += mchunk) {
             const int nn = std::min(nchunk, N - n0), mm = std::min(mchunk, M - m0);
@@ -578,12 +615,14 @@ q4_status launch_gemm(const uint32_t *W, const uint16_t *S, const uint16_t *X, i
             uint16_t *y = Y + (size_t)m0 * ldy + n0;
             float *part = nullptr;
             uint16_t *xsum = nullptr;
-            const size_t part_b = g.splits > 1 ? (size_t)g.splits * mm * nn * sizeof(float) : 0;
-            const size_t xsum_b = bias ? (size_t)mm * 2 * GP * sizeof(uint16_t) : 0;
+            size_t part_b, xsum_b;
+            gemm_scratch(mm, nn, G, bias != nullptr, &part_b, &xsum_b);
             if (part_b + xsum_b) {
-                char *ws = static_cast<char *>(workspace(stream, kWsHeader + part_b + xsum_b));
+                // the largest launch of the call: the workspace is sized once
+                char *ws = static_cast<char *>(
+                    workspace(stream, ws_gemm(N, K, M, bias != nullptr, ldx)));
                 if (!ws)
-                    return Q4_EHIP;
+                    return workspace_status();
                 part = part_b ? reinterpret_cast<float *>(ws + kWsHeader) : nullptr;
                 xsum = xsum_b ? reinterpret_cast<uint16_t *>(ws + kWsHeader + part_b) : nullptr;
             }

@@ -24,7 +24,6 @@
 
 #include "q4_dequant.h"
 #include "q4_moe_route.h"
-#include "q4_stack.h"
 
 namespace q4 {
 namespace {
@@ -850,13 +849,6 @@ int matvec_blocks(int N, int K)
         return 0;
     const int rb = kWaves * (64 / c.lpr) * rows_per_segment(c.ng);
     return (N + rb - 1) / rb;
-}
-
-void matvec_layout(int G, int *lpr, int *ng)
-{
-    const Cfg c = choose_cfg(G);
-    *lpr = c.lpr;
-    *ng = c.ng;
 }
 
 q4_status launch_gemv_op(const GemvOp &op, hipStream_t stream)

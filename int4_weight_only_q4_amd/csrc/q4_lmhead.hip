@@ -187,15 +187,47 @@ void partial_grid(int N, int *blocks, int *chunk)
 }
 }  // namespace
 
+size_t ws_argmax(int N, int M)
+{
+    int blocks, chunk;
+    partial_grid(N, &blocks, &chunk);
+    return kWsHeader + (size_t)M * blocks * sizeof(unsigned long long);
+}
+
+namespace {
+// M >= 2 rows on the matrix cores: argmax candidates per (row, block) and the
+// K-split partials
+int lm_head_mfma_blocks(int N, int K)
+{
+    int blocks, chunk;
+    partial_grid(N, &blocks, &chunk);
+    if (mfma_splits(K) > 1)
+        blocks = (N + kCombineChunk - 1) / kCombineChunk;
+    return blocks;
+}
+size_t lm_head_cand_bytes(int N, int K, int M)
+{
+    return ((size_t)M * lm_head_mfma_blocks(N, K) * sizeof(unsigned long long) + 255) / 256 * 256;
+}
+}  // namespace
+
+size_t ws_lm_head(int N, int K, int M)
+{
+    if (M > 1 && gemv_rows_fits(M, K))
+        return ws_argmax(N, M);
+    if (M > 1)
+        return kWsHeader + lm_head_cand_bytes(N, K, M) + mfma_part_bytes(N, K);
+    return kWsHeader + (size_t)matvec_blocks(N, K) * sizeof(unsigned long long);
+}
+
 q4_status launch_argmax(const float *v, int64_t ld, int N, int M, int32_t *index,
                         hipStream_t stream)
 {
     int blocks, chunk;
     partial_grid(N, &blocks, &chunk);
-    char *ws = static_cast<char *>(
-        workspace(stream, kWsHeader + (size_t)M * blocks * sizeof(unsigned long long)));
+    char *ws = static_cast<char *>(workspace(stream, ws_argmax(N, M)));
     if (!ws)
-        return Q4_EHIP;
+        return workspace_status();
     auto *cand = reinterpret_cast<unsigned long long *>(ws + kWsHeader);
     hipLaunchKernelGGL(k_argmax_partial, dim3(blocks, M), dim3(kThreads), 0, stream, v, ld, N,
                        chunk, cand);
@@ -224,13 +256,11 @@ q4_status launch_lm_head_argmax(const uint32_t *W, const uint16_t *S, const uint
         const int KS = mfma_splits(K);
         int blocks, chunk;
         partial_grid(N, &blocks, &chunk);
-        if (KS > 1)
-            blocks = (N + kCombineChunk - 1) / kCombineChunk;
-        const size_t cand_b = ((size_t)M * blocks * sizeof(unsigned long long) + 255) / 256 * 256;
-        char *ws = static_cast<char *>(
-            workspace(stream, kWsHeader + cand_b + mfma_part_bytes(N, K)));
+        blocks = lm_head_mfma_blocks(N, K);
+        const size_t cand_b = lm_head_cand_bytes(N, K, M);
+        char *ws = static_cast<char *>(workspace(stream, ws_lm_head(N, K, M)));
         if (!ws)
-            return Q4_EHIP;
+            return workspace_status();
         auto *cand = reinterpret_cast<unsigned long long *>(ws + kWsHeader);
         float *part = reinterpret_cast<float *>(ws + kWsHeader + cand_b);
         for (int m0 = 0; m0 < M; m0 += 16) {
@@ -257,10 +287,9 @@ q4_status launch_lm_head_argmax(const uint32_t *W, const uint16_t *S, const uint
     const int blocks = matvec_blocks(N, K);
     if (blocks <= 0)
         return fail(Q4_ERANGE, "no matvec configuration for K = %d", K);
-    char *ws = static_cast<char *>(
-        workspace(stream, kWsHeader + (size_t)blocks * sizeof(unsigned long long)));
+    char *ws = static_cast<char *>(workspace(stream, ws_lm_head(N, K, 1)));
     if (!ws)
-        return Q4_EHIP;
+        return workspace_status();
     GemvOp op;
     op.W = W;
     op.S = S;

@@ -467,6 +467,13 @@ q4_status launch_mfma_rows(const uint32_t *W, const uint16_t *S, const uint16_t 
     return check_launch("k_gemv_mfma");
 }
 
+size_t ws_rows(int N, int K, int M)
+{
+    if (M <= 1 || gemv_rows_fits(M, K) || mfma_splits(K) <= 1)
+        return 0;  // single-row and few-row kernels, or no K split
+    return kWsHeader + mfma_part_bytes(N, K);
+}
+
 q4_status launch_gemv_mfma(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
                            uint16_t *y, float *yf, int64_t ldy, int N, int K, int M,
                            hipStream_t stream, const uint16_t *bias)
@@ -474,9 +481,9 @@ q4_status launch_gemv_mfma(const uint32_t *W, const uint16_t *S, const uint16_t 
     const int KS = mfma_splits(K);
     float *part = nullptr;
     if (KS > 1) {
-        char *ws = static_cast<char *>(workspace(stream, kWsHeader + mfma_part_bytes(N, K)));
+        char *ws = static_cast<char *>(workspace(stream, ws_rows(N, K, M)));
         if (!ws)
-            return Q4_EHIP;
+            return workspace_status();
         part = reinterpret_cast<float *>(ws + kWsHeader);
     }
     for (int m0 = 0; m0 < M; m0 += kMTile) {

@@ -103,6 +103,18 @@ __global__ __launch_bounds__(256) void k_moe_route(const int32_t *__restrict__ i
 
 }  // namespace
 
+namespace {
+size_t moe_meta_bytes(int E, int P)
+{
+    return moe_routes_in_kernel(P, E) ? 0 : ((size_t)(3 * P + 2) * 4 + 255) / 256 * 256;
+}
+}  // namespace
+
+size_t ws_moe(int E, int N, int K, int P)
+{
+    return kWsHeader + moe_meta_bytes(E, P) + moe_part_bytes(N, K, P);
+}
+
 q4_status launch_moe(const uint32_t *W, const uint16_t *S, const int32_t *ids,
                      const uint16_t *route_w, const uint16_t *x, int64_t ldx,
                      int64_t x_slot_stride, uint16_t *y, int E, int N, int K, int T, int TOPK,
@@ -111,11 +123,10 @@ q4_status launch_moe(const uint32_t *W, const uint16_t *S, const int32_t *ids,
     const int P = T * TOPK;
     const int mode = epi_silu ? MOE_SILU : (route_w ? MOE_COMBINE : MOE_PER_SLOT);
     const bool in_kernel = moe_routes_in_kernel(P, E);
-    const size_t meta_bytes = in_kernel ? 0 : ((size_t)(3 * P + 2) * 4 + 255) / 256 * 256;
-    char *ws = static_cast<char *>(
-        workspace(stream, kWsHeader + meta_bytes + moe_part_bytes(N, K, P)));
+    const size_t meta_bytes = moe_meta_bytes(E, P);
+    char *ws = static_cast<char *>(workspace(stream, ws_moe(E, N, K, P)));
     if (!ws)
-        return Q4_EHIP;
+        return workspace_status();
     int32_t *meta = in_kernel ? nullptr : reinterpret_cast<int32_t *>(ws + kWsHeader);
     float *part = reinterpret_cast<float *>(ws + kWsHeader + meta_bytes);
     if (!in_kernel) {

@@ -259,7 +259,7 @@ def test_stack_attention_validation():
     d.dv = 192
     assert st(C.byref(d), C.byref(a), X, X + 4096, Y, Y + 4096, None, None) == q4.Q4_ESHAPE
     d.dv = 256
-    d.mode = q4.STACK_PERSISTENT
+    d.mode = 2  # no such mode (only the multi-kernel path exists)
     assert st(C.byref(d), C.byref(a), X, X + 4096, Y, Y + 4096, None, None) == q4.Q4_EINVAL
     d.mode = q4.STACK_AUTO
     a.max_len = 0
@@ -304,3 +304,71 @@ def test_gemm_affine_validation():
     assert f(A, B, R + 1, X, 128, Y, 16, 16, 128, 4, None) == q4.Q4_EALIGN
     assert f(A, B, R, X + 8, 128, Y, 16, 16, 128, 4, None) == q4.Q4_EALIGN
     assert f(A, B, R, X, 128, R, 16, 16, 128, 4, None) == q4.Q4_EALIAS      # y over the biases
+
+
+# ---------------------------------------------------------------------------
+# workspace sizes (host-only queries; no device work)
+# ---------------------------------------------------------------------------
+
+def _al(b):
+    return (b + 255) // 256 * 256
+
+
+def test_workspace_bytes_invalid_shapes_are_zero():
+    f = q4.lib().q4_workspace_bytes
+    assert f(0, 256, 1) == 0
+    assert f(16, 100, 1) == 0                 # K % 32
+    assert f(16, q4.MAX_K + 32, 1) == 0       # K > Q4_MAX_K
+    assert f(16, 256, 0) == 0
+
+
+def test_workspace_bytes_at_each_entry_points_maximum_shapes():
+    """Every matmul-family entry point at its largest shape gets a finite size
+    that covers the 256-byte header, and the size never shrinks as M grows
+    (prefill partials, MoE pairs, argmax rows)."""
+    f = q4.lib().q4_workspace_bytes
+    cases = [
+        (151936, 2560, q4.MAX_M),          # LM head / batched matvec, largest M
+        (151936, 2560, 1),                 # LM head + argmax at one row
+        (65536, q4.MAX_K, q4.MAX_M),       # batched matvec at the largest K
+        (16384, q4.MAX_K, q4.MAX_GEMM_M),  # prefill, largest M and K
+        (1536, 2048, q4.MAX_PAIRS),        # one MoE stage, largest pair count
+        (2048, 768, q4.MAX_PAIRS),
+    ]
+    for n, k, m in cases:
+        b = f(n, k, m)
+        assert 256 < b < (1 << 36), (n, k, m, b)
+    for n, k in ((3072, 8192), (19456, 2560), (512, 256)):
+        prev = 0
+        for m in (1, 2, 5, 16, 64, 256, 1024, 4096):
+            b = f(n, k, m)
+            assert b >= prev, (n, k, m)
+            prev = b
+
+
+def test_attention_workspace_bytes():
+    """One split (at most 256 positions) needs nothing; more positions need the
+    split partials: (max, sum, weighted values) per head and split, 32 splits."""
+    g = q4.attn_desc(32, 32, 96)
+    f = q4.lib().q4_attention_workspace_bytes
+    assert f(C.byref(g), 1) == 0
+    assert f(C.byref(g), 256) == 0
+    assert f(C.byref(g), 4096) == 256 + 32 * 32 * (2 + 96) * 4
+    assert f(C.byref(g), 0) == 0
+    assert f(None, 4096) == 0
+
+
+def test_stack_workspace_bytes():
+    """header | qkv | r1 | u | two residual buffers [| attention output |
+    attention partials], each 256-byte aligned (Phi-3-mini shapes)."""
+    arr = (C.c_void_p * 1)(A)
+    ptr = C.cast(arr, C.c_void_p)
+    d = q4.StackDesc(32, 3072, 8192, 9216, 6144, 3072, 1e-5, ptr, ptr, ptr, ptr, ptr, ptr, ptr,
+                     ptr, R, R + 4096, R + 8192)
+    f = q4.lib().q4_stack_workspace_bytes
+    base = 256 + _al(9216 * 2) + 3 * _al(3072 * 2) + _al(8192 * 2)
+    assert f(C.byref(d), None) == base
+    g = q4.attn_desc(32, 32, 96)
+    a = q4.StackAttn(C.pointer(g), None, None, None, 1024)
+    assert f(C.byref(d), C.byref(a)) == base + _al(3072 * 2) + _al(32 * 32 * (2 + 96) * 4)
+    assert f(None, None) == 0

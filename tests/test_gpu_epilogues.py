@@ -46,6 +46,45 @@ def test_add_rmsnorm_vs_oracle(o, q4, d, m, with_a):
     assert_within(host(out), ref_out, "add_rmsnorm")
 
 
+def _offset_copy(t, off):
+    """t's values in a fresh buffer starting `off` elements in (off = 1 gives a
+    2-byte-aligned, not 16-byte-aligned, view)."""
+    import torch
+    buf = torch.zeros(t.numel() + 16, dtype=t.dtype, device=t.device)
+    v = buf[off:off + t.numel()].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("d,m,with_a", [(2048, 1, True), (4096, 2, False), (5120, 1, True),
+                                        (5120, 3, False), (6144, 1, True), (6144, 2, True),
+                                        (8192, 1, False)])
+def test_add_rmsnorm_row_in_registers_equals_scalar_path(o, q4, d, m, with_a):
+    """The add+RMSNorm with the row held in registers (16-byte aligned vectors,
+    D % 8 == 0, up to 8192 values: 1 to 4 chunks of 8 values per thread) and the
+    general kernel, which the same call takes when a pointer is only 2-byte
+    aligned, give the same bits, and both match the oracle."""
+    import torch
+    a = datagen.activations(210 + d + m, m, d) if with_a else None
+    r = datagen.activations(211 + d + m, m, d)
+    g = datagen.gammas(212 + d, 1, d)[0]
+    ad = None if a is None else dev_tensor(a)
+    rd, gd = dev_tensor(r), dev_tensor(g)
+    out_v, res_v = q4.add_rmsnorm(ad, rd, gd, eps=1e-5)
+    # the same values one element into fresh buffers: every vector misaligned
+    ad1 = None if ad is None else _offset_copy(ad, 1)
+    rd1, gd1 = _offset_copy(rd, 1), _offset_copy(gd, 1)
+    out_s = _offset_copy(torch.empty_like(rd), 1)
+    res_s = _offset_copy(torch.empty_like(rd), 1)
+    q4.add_rmsnorm(ad1, rd1, gd1, out=out_s, res_out=res_s, eps=1e-5)
+    sync()
+    assert np.array_equal(bits(out_v), bits(out_s)), "normalised output: vector != scalar path"
+    assert np.array_equal(bits(res_v), bits(res_s)), "residual: vector != scalar path"
+    ref_res, ref_out = o.add_rmsnorm(a, r, g, eps=1e-5)
+    assert np.array_equal(bits(res_v), ref_res.view(np.uint16))
+    assert_within(host(out_v), ref_out, "add_rmsnorm d=%d" % d)
+
+
 @pytest.mark.parametrize("f,m", [(8192, 1), (9728, 2), (768, 16), (37, 3)])
 def test_silu_mul_vs_oracle(o, q4, f, m):
     gu = datagen.normal_f16(300 + f, (m, 2 * f), 0.0, 3.0)

@@ -160,36 +160,6 @@ def test_phi3_stack_repeatable(q4, phi3):
     assert np.all(np.isfinite(a[1].astype(np.float64))) and np.abs(a[1]).max() > 0
 
 
-def _run_mode(q4, stack, st, d, n, mode):
-    stack.set_mode(mode)
-    try:
-        return _run(q4, stack, st, d, n)
-    finally:
-        stack.set_mode(q4.STACK_AUTO)
-
-
-@pytest.mark.parametrize("which", ["small", "phi3"])
-def test_persistent_equals_multi_kernel(o, q4, phi3, which):
-    """The persistent kernel and the four-launches-per-layer path give the same
-    bits for every traced layer, and no wait inside the persistent kernel timed out."""
-    import torch
-    if which == "small":
-        p = SMALL
-        stack, st = bench.build_stack(q4, torch, p)
-    else:
-        p = bench.PHI3
-        stack, st = phi3
-    a = _run_mode(q4, stack, st, p["d"], p["layers"], q4.STACK_PERSISTENT)
-    q4.stack_status()
-    b = _run_mode(q4, stack, st, p["d"], p["layers"], q4.STACK_MULTI)
-    for x, y, name in zip(a, b, ("r_out", "h_out", "trace")):
-        assert np.array_equal(np.asarray(x).view(np.uint16), np.asarray(y).view(np.uint16)), name
-    # repeated persistent calls (the phase tags advance) stay identical
-    c = _run_mode(q4, stack, st, p["d"], p["layers"], q4.STACK_PERSISTENT)
-    q4.stack_status()
-    assert np.array_equal(np.asarray(c[1]).view(np.uint16), np.asarray(a[1]).view(np.uint16))
-
-
 @pytest.mark.parametrize("which", ["small", "phi3"])
 def test_stack_graph_replays_equal_eager(q4, phi3, which):
     """The captured token graphs that bench.py replays: every replay (four,
