@@ -402,6 +402,22 @@ q4_status q4_stack_decode(const q4_stack_desc *desc, const uint16_t *r_in,
                           const uint16_t *h_in, uint16_t *r_out, uint16_t *h_out,
                           uint16_t *trace, q4_stream stream);
 
+/* q4_stack_decode_noalloc -- q4_stack_decode (same arguments, same kernels, the
+ * same bits) for callers that cannot allocate: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. It allocates nothing
+ * and uses no stream workspace: its intermediate vectors live in a fixed
+ * scratch array of Q4_NOALLOC_SCRATCH_BYTES in the library's device image,
+ * one per GPU, held until the process ends. A stack whose
+ * q4_stack_workspace_bytes(desc, NULL) exceeds that is Q4_ERANGE (nothing
+ * enqueued). Every call on a GPU shares that GPU's scratch: calls that overlap
+ * on one GPU (e.g. on two streams at once) race; calls ordered on one stream do
+ * not. The scratch keeps the last call's contents; nothing in it needs to
+ * start at zero. */
+#define Q4_NOALLOC_SCRATCH_BYTES (1 << 20)
+q4_status q4_stack_decode_noalloc(const q4_stack_desc *desc, const uint16_t *r_in,
+                                  const uint16_t *h_in, uint16_t *r_out, uint16_t *h_out,
+                                  uint16_t *trace, q4_stream stream);
+
 /* q4_stack_decode_attn -- the same stack with the real attention step in place
  * of the single-position identity ("Decode loop"): per layer
  *   q = RoPE(f16(Wqkv[L] . h)) queries; the rotated key and the value of the

@@ -27,6 +27,7 @@ MAX_K = 24576
 MAX_M = 64
 MAX_GEMM_M = 65536
 MAX_PAIRS = 4096
+NOALLOC_SCRATCH_BYTES = 1 << 20
 
 #: Bytes per int4 weight in this format: 4 bits + one f16 scale per 32 weights.
 BYTES_PER_WEIGHT = 0.5 + 2.0 / 32.0
@@ -39,6 +40,7 @@ ABI_SYMBOLS = (
     "q4_rope_append", "q4_attention_decode", "q4_stack_decode_attn", "q4_gemv_affine",
     "q4_gemm", "q4_gemm_affine", "q4_workspace_bytes", "q4_attention_workspace_bytes",
     "q4_stack_workspace_bytes", "q4_workspace_reserve", "q4_workspace_release",
+    "q4_stack_decode_noalloc",
 )
 
 
@@ -108,6 +110,7 @@ _SIGS = {
     "q4_stack_workspace_bytes": (C.c_size_t, [C.POINTER(StackDesc), C.POINTER(StackAttn)]),
     "q4_workspace_reserve": (C.c_int, [_P, C.c_size_t]),
     "q4_workspace_release": (C.c_int, [_P]),
+    "q4_stack_decode_noalloc": (C.c_int, [C.POINTER(StackDesc), _P, _P, _P, _P, _P, _P]),
 }
 
 _lib = None
@@ -432,6 +435,13 @@ class Stack:
     def decode(self, r_in, h_in, r_out, h_out, trace=None, stream=None):
         _check(lib().q4_stack_decode(C.byref(self.desc), _ptr(r_in), _ptr(h_in), _ptr(r_out),
                                      _ptr(h_out), _ptr(trace), _stream(stream)))
+
+    def decode_noalloc(self, r_in, h_in, r_out, h_out, trace=None, stream=None):
+        """decode() through q4_stack_decode_noalloc (no allocation: the
+        library's fixed per-GPU scratch)."""
+        _check(lib().q4_stack_decode_noalloc(C.byref(self.desc), _ptr(r_in), _ptr(h_in),
+                                             _ptr(r_out), _ptr(h_out), _ptr(trace),
+                                             _stream(stream)))
 
     def set_mode(self, mode):
         self.desc.mode = mode

@@ -146,6 +146,39 @@ namespace {
 
 inline hipStream_t as_stream(q4_stream s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Scratch of q4_stack_decode_noalloc: a fixed array in the library's device
+// image (each GPU holds its own copy until the process ends), so the call
+// allocates nothing. Host code must not pass `scratch` itself to a kernel (in
+// host code it names a host-side stand-in): the device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kNoAllocScratchBytes = Q4_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char *g_scratch_dev[kMaxDevices] = {};  // device address of `scratch`, per device
+
+// The device address of `scratch` on the current device.
+q4_status scratch_address(char **out)
+{
+    int dev = 0;
+    Q4_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(Q4_ERANGE, "device %d beyond the %d the fixed scratch serves", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(Q4_EHIP, "hipGetSymbolAddress of the fixed scratch failed: %s",
+                        hipGetErrorString(e));
+        g_scratch_dev[dev] = static_cast<char *>(p);
+    }
+    *out = g_scratch_dev[dev];
+    return Q4_OK;
+}
+
 q4_status check_matrix(const uint32_t *W, const uint16_t *S, int64_t N, int64_t K)
 {
     if (!W || !S)
@@ -216,9 +249,11 @@ struct StackWs {
     }
 };
 
+// buffers: device memory for the call's intermediate vectors (StackWs(d,
+// ...).total bytes), or nullptr for the stream's library workspace.
 q4_status stack_multi(const q4_stack_desc *d, const StackAttn *attn, const uint16_t *r_in,
                       const uint16_t *h_in, uint16_t *r_out, uint16_t *h_out, uint16_t *trace,
-                      hipStream_t st)
+                      hipStream_t st, char *buffers = nullptr)
 {
     const int64_t D = d->d, F = d->f;
     const size_t vb = (size_t)D * 2;
@@ -228,7 +263,7 @@ q4_status stack_multi(const q4_stack_desc *d, const StackAttn *attn, const uint1
     // matvec while it stages its activation (bit-identical to q4_add_rmsnorm).
     const StackWs w(d, attn ? &attn->geom : nullptr);
     const size_t q_b = w.q_b, v_b = w.v_b, u_b = w.u_b, a_b = w.a_b;
-    char *ws = static_cast<char *>(workspace(st, w.total));
+    char *ws = buffers ? buffers : static_cast<char *>(workspace(st, w.total));
     if (!ws)
         return workspace_status();
     uint16_t *qkv = reinterpret_cast<uint16_t *>(ws + kWsHeader);
@@ -1015,6 +1050,25 @@ q4_status q4_stack_decode(const q4_stack_desc *d, const uint16_t *r_in, const ui
         return s;
     hipStream_t st = as_stream(stream);
     return stack_multi(d, nullptr, r_in, h_in, r_out, h_out, trace, st);
+}
+
+q4_status q4_stack_decode_noalloc(const q4_stack_desc *d, const uint16_t *r_in,
+                                  const uint16_t *h_in, uint16_t *r_out, uint16_t *h_out,
+                                  uint16_t *trace, q4_stream stream)
+{
+    q4_status s = check_stack(d, r_in, h_in, r_out, h_out, trace, true);
+    if (s != Q4_OK)
+        return s;
+    const size_t need = StackWs(d, nullptr).total;
+    if (need > kNoAllocScratchBytes)
+        return fail(Q4_ERANGE,
+                    "this stack needs %zu bytes of scratch; the fixed scratch of "
+                    "q4_stack_decode_noalloc holds %zu (use q4_stack_decode)",
+                    need, kNoAllocScratchBytes);
+    char *base = nullptr;
+    if ((s = scratch_address(&base)) != Q4_OK)
+        return s;
+    return stack_multi(d, nullptr, r_in, h_in, r_out, h_out, trace, as_stream(stream), base);
 }
 
 q4_status q4_stack_decode_attn(const q4_stack_desc *d, const q4_stack_attn *attn,

@@ -372,3 +372,19 @@ def test_stack_workspace_bytes():
     a = q4.StackAttn(C.pointer(g), None, None, None, 1024)
     assert f(C.byref(d), C.byref(a)) == base + _al(3072 * 2) + _al(32 * 32 * (2 + 96) * 4)
     assert f(None, None) == 0
+
+
+def test_noalloc_stack_refuses_vectors_beyond_the_fixed_scratch():
+    """q4_stack_decode_noalloc checks on the host that the stack's intermediate
+    vectors fit its fixed scratch; a larger stack is Q4_ERANGE with nothing
+    enqueued (fake device addresses are never touched)."""
+    arr = (C.c_void_p * 1)(A)
+    ptr = C.cast(arr, C.c_void_p)
+    f = q4.lib().q4_stack_decode_noalloc
+    # 600000 QKV rows: 1.2 MB of qkv alone
+    d = q4.StackDesc(1, 256, 512, 600000, 512, 256, 1e-5, ptr, ptr, ptr, ptr, ptr, ptr, ptr,
+                     ptr, R, R + 4096, R + 8192)
+    assert q4.lib().q4_stack_workspace_bytes(C.byref(d), None) > q4.NOALLOC_SCRATCH_BYTES
+    assert f(C.byref(d), X, X + 4096, Y, Y + 4096, None, None) == q4.Q4_ERANGE
+    assert "fixed scratch" in q4.lib().q4_last_error().decode()
+    assert f(None, X, X + 4096, Y, Y + 4096, None, None) == q4.Q4_EINVAL
