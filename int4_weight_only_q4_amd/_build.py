@@ -29,6 +29,12 @@ FLAGS = [
     "-ffp-contract=off",
     "-Wno-unused-result",
 ]
+# Per-source additions. The matvec matrix-core kernels take their MFMA results
+# in ordinary VGPRs, which the scaling FMAs read directly (the accumulation-
+# register form costs a v_accvgpr_read per value).
+EXTRA_FLAGS = {
+    "q4_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def _headers_mtime() -> float:
@@ -41,7 +47,7 @@ def _compile(src: str, force: bool) -> str:
     if (not force and os.path.exists(obj)
             and os.path.getmtime(obj) > max(os.path.getmtime(src), _headers_mtime())):
         return obj
-    cmd = [HIPCC] + FLAGS + ["-c", src, "-o", obj + ".tmp"]
+    cmd = [HIPCC] + FLAGS + EXTRA_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj + ".tmp"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s" % (src, r.stderr))

@@ -213,7 +213,7 @@ size_t lm_head_cand_bytes(int N, int K, int M)
 
 size_t ws_lm_head(int N, int K, int M)
 {
-    if (M > 1 && gemv_rows_fits(M, K))
+    if (M > 1 && (gemv_rows_fits(M, K) || mma_fits(N, K, M)))
         return ws_argmax(N, M);
     if (M > 1)
         return kWsHeader + lm_head_cand_bytes(N, K, M) + mfma_part_bytes(N, K);
@@ -241,10 +241,11 @@ q4_status launch_lm_head_argmax(const uint32_t *W, const uint16_t *S, const uint
                                 int64_t ldx, float *logits, int64_t ldl, int32_t *tokens, int N,
                                 int K, int M, hipStream_t stream)
 {
-    if (M > 1 && gemv_rows_fits(M, K)) {
-        // a few rows: their f32 logits as M single-row matvecs, then the argmax
-        q4_status st = launch_gemv_rows(W, S, x, ldx, nullptr, ldl, N, K, M, stream, nullptr,
-                                        logits);
+    if (M > 1 && (gemv_rows_fits(M, K) || mma_fits(N, K, M))) {
+        // the f32 logits without a workspace (a few rows: M single-row
+        // matvecs; more: the workgroup-reduced matrix-core kernel), then the
+        // argmax
+        q4_status st = launch_gemv_f32(W, S, x, ldx, logits, ldl, N, K, M, stream);
         if (st != Q4_OK)
             return st;
         return launch_argmax(logits, ldl, N, M, tokens, stream);

@@ -428,6 +428,275 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ part,
 }
 
 
+// ---------------------------------------------------------------------------
+// Batched matvec for a few activation rows on the matrix cores with the
+// single-row kernel's nibble unpack (k_gemv_mma).
+//
+// With y[m][n] = sum_g s[n][g] * (sum_{k in g} c[n][k] x[m][k] - 7 X_g[m]),
+// X_g[m] the sum of activation row m over group g:
+//  * the code sums take one MFMA per group and 16-row tile
+//    (v_mfma_f32_16x16x32_f16, A = activation rows, B = weights). B holds the
+//    codes as the exact binary16 subnormals the single-row kernel forms (one
+//    shift and four ANDs per word): c * 2^-24 in the pairs (e0, e4) and
+//    (e2, e6), c * 2^-20 in (e1, e5) and (e3, e7). A holds the activation in
+//    the same pair order, the values that meet the 2^-20 pairs divided by 16
+//    (exact for |x| >= 2^-10), so that each product is c * x * 2^-24. The lane
+//    adds the group's f32 sum times the row's scale to its accumulator;
+//  * the zero-point term sum_g s[n][g] X_g[m] is itself a contraction over the
+//    groups: one v_mfma_f32_16x16x4_f32 per four groups and tile, A = the
+//    activation's group sums (f32), B = the scales;
+//  * y = 2^24 * (code part) - 7 * (zero-point part).
+// For a one-hot activation both parts are exact (c s and 7 s, at most 15
+// significant bits) and so is their difference: the result is (q - 7) * s
+// exactly, as with the other matvecs. A-operand rows m >= M repeat row M - 1
+// and are never stored.
+//
+// Work split. One workgroup of kMmaWaves waves per CU stages the activation
+// once in LDS (pair order, odd positions / 16, group sums) and keeps it for
+// the whole launch. A unit of work is one 16-row tile times one of KP equal
+// parts of K (SK = 2 SK2 steps of four groups); the KP waves of a tile run in
+// step, one unit per round each, and the tiles of a round are blockIdx.x +
+// gridDim.x * (slot + (kMmaWaves / KP) * round). A wave issues all loads of a
+// unit at once, in whole memory lines: the unit's scales as a row-major block
+// (64 consecutive scales per load), then its weights as 8 rows x 128 bytes
+// per load (a pair of steps per two loads). The scales go to a per-wave LDS
+// block, each pair of steps' weights to a per-wave LDS tile from which every
+// lane reads the words of its MFMA lane (word kb of each group of row n):
+// no exchanges across lanes in registers. After each round the waves' f32
+// parts meet in LDS (two slots, one barrier) and the tile's kp = 0 wave adds
+// them in K order and stores. Every wave runs the same number of rounds
+// (units past the last tile re-read valid data and are not stored), so the
+// barriers match.
+constexpr int kMmaWaves = 12;   // three waves per SIMD
+constexpr int kMmaMaxPairs = 6;  // steps per unit <= 12 (7 pairs spill registers)
+constexpr int kMmaXq = 8;       // activation chunks per thread held in registers
+constexpr int kMmaTileStride = 9;  // 16-byte slots per row of the weight tile (8 + 1 against conflicts)
+
+// The subnormal codes of word w as a B operand, pairs (e0,e4) (e1,e5) (e2,e6)
+// (e3,e7).
+__device__ __forceinline__ half8 codes_subnormal(uint32_t w)
+{
+    const uint32_t m0 = 0x000F000Fu, m1 = 0x00F000F0u, t = w >> 8;
+    const u32x4 v = {w & m0, w & m1, t & m0, t & m1};
+    return __builtin_bit_cast(half8, v);
+}
+
+struct MmaArgs {
+    const uint4 *W;
+    const uint16_t *S;
+    const uint16_t *x;
+    int64_t ldx;
+    uint16_t *y;  // f16 results, or
+    float *yf;    // f32 results
+    int64_t ldy;
+    int N, G, M;
+    int KP, rounds;  // K parts, rounds
+};
+
+// LDS bytes of one wave's scale block and weight tile
+constexpr int mma_wave_lds(int SK2) { return 16 * 8 * SK2 * 2 + 16 * kMmaTileStride * 16; }
+
+template <int SK2>
+__global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
+{
+    constexpr int SK = 2 * SK2;  // steps per unit
+    constexpr int GU = 4 * SK;   // groups per unit
+    extern __shared__ uint4 smem[];
+    const int G = a.G, K = G * 32, M = a.M, N = a.N;
+    const int xstride = K + 8;  // staged row: 16 bytes of padding against bank conflicts
+    const int t = threadIdx.x, l = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int n = l & 15, kb = l >> 4;
+    // LDS: per wave a scale block [16][GU] and a weight tile [16][9] x 16 B;
+    // the waves' parts [2][kMmaWaves][64 lanes][4] f32; the staged rows
+    // [M][xstride] binary16; the group sums [G][16] f32
+    char *wbase = reinterpret_cast<char *>(smem) + (size_t)wave * mma_wave_lds(SK2);
+    uint16_t *sblk = reinterpret_cast<uint16_t *>(wbase);
+    uint4 *wtile = reinterpret_cast<uint4 *>(wbase + 16 * GU * 2);
+    float *red = reinterpret_cast<float *>(reinterpret_cast<char *>(smem) +
+                                           (size_t)kMmaWaves * mma_wave_lds(SK2));
+    _Float16 *xs = reinterpret_cast<_Float16 *>(red + 2 * kMmaWaves * 256);
+    float *xsum = reinterpret_cast<float *>(xs + M * xstride);
+
+    const int KP = a.KP, rounds = a.rounds;
+    const int kp = wave % KP, tslot = wave / KP, tpr = kMmaWaves / KP;
+    const int ntiles = (N + 15) >> 4;
+    const int gp0 = kp * GU;  // first group of this wave's part of K
+    auto tile_of = [&](int r) { return (int)blockIdx.x + (int)gridDim.x * (tslot + tpr * r); };
+
+    // 1. the activation's chunks (up to kMmaXq per thread) into registers, then
+    //    into LDS: the pair order, the odd positions x1 x3 x5 x7 (the high
+    //    halves of the words, which meet the 2^-20 pairs) divided by 16, and
+    //    each group's sum of the unscaled values (a quad of lanes holds the
+    //    four chunks of a group: cpr and the thread count are multiples of 4,
+    //    so quads never mix rows)
+    {
+        const int cpr = K >> 3;
+        const int total = M * cpr;  // a multiple of 4
+        constexpr int kThreads = 64 * kMmaWaves;
+        const half2v odd16 = {(_Float16)1.0f, (_Float16)0.0625f};
+        const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
+        auto chunk = [&](int c) __attribute__((always_inline)) {
+            // a quad past the end re-reads the last group and stores nothing
+            const int cc = c < total ? c : total - 4 + (c & 3);
+            const int m = cc / cpr, j = cc - m * cpr;
+            return *reinterpret_cast<const u32x4 *>(a.x + m * a.ldx + 8 * j);
+        };
+        auto stage = [&](int c, u32x4 v) __attribute__((always_inline)) {
+            const bool live = c < total;
+            const int cc = live ? c : total - 4 + (c & 3);
+            const int m = cc / cpr, j = cc - m * cpr;
+            float sum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                // through a scalar: this compiler's bit_cast of a vector
+                // element reads element 0
+                const uint32_t h = v[e];
+                sum = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, h), ones, sum, false);
+                v[e] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, h) * odd16);
+            }
+            sum = quad_sum(sum);
+            if (live) {
+                *reinterpret_cast<u32x4 *>(xs + m * xstride + 8 * j) = pair_order(v);
+                if ((j & 3) == 0)
+                    xsum[(j >> 2) * 16 + m] = sum;
+            }
+        };
+        const int xq = min((total + kThreads - 1) / kThreads, kMmaXq);  // uniform
+        u32x4 xr[kMmaXq];
+#pragma unroll
+        for (int i = 0; i < kMmaXq; ++i)
+            if (i < xq)
+                xr[i] = chunk(i * kThreads + t);
+#pragma unroll
+        for (int i = 0; i < kMmaXq; ++i)
+            if (i < xq)
+                stage(i * kThreads + t, xr[i]);
+        // more chunks than the registers hold: the rest one by one
+        for (int c0 = kMmaXq * kThreads; c0 < total; c0 += kThreads)
+            stage(c0 + t, chunk(c0 + t));
+    }
+    __syncthreads();
+
+    // 2. the rounds
+    const int mrow = min(n, M - 1);  // A row m = n
+    const _Float16 *xrow = xs + mrow * xstride + 8 * kb;
+    const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < rounds; ++r) {
+        const int tile = tile_of(r);
+        const int row0 = min(tile, ntiles - 1) * 16;  // units past the end re-read the last tile
+        // the unit's scales, element e = 64 j + l of the row-major block
+        // [16][GU] (branch-free: groups past G re-read group G - 1 and are
+        // zeroed at use; rows past N re-read row N - 1)
+        uint32_t sl[SK];
+#pragma unroll
+        for (int j = 0; j < SK; ++j) {
+            const int e = 64 * j + l;
+            const int rr = e / GU, cc = e - rr * GU;
+            sl[j] = load_scale(a.S + (size_t)min(row0 + rr, N - 1) * G + min(gp0 + cc, G - 1));
+        }
+        // the unit's weights: pair q, half i: lane l reads group gp0 + 8 q +
+        // (l & 7) of row 8 i + (l >> 3), 8 rows x 128 bytes per load
+        uint4 wl[SK2][2];
+#pragma unroll
+        for (int q = 0; q < SK2; ++q)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int rr = min(row0 + 8 * i + (l >> 3), N - 1);
+                wl[q][i] = load_weights(a.W + (size_t)rr * G + min(gp0 + 8 * q + (l & 7), G - 1));
+            }
+        // the scales into the wave's block (waiting for the scale loads only:
+        // they were issued first)
+#pragma unroll
+        for (int j = 0; j < SK; ++j)
+            sblk[64 * j + l] = (uint16_t)sl[j];
+
+        floatx4 acc = zero, acc0 = zero;
+#pragma unroll
+        for (int q = 0; q < SK2; ++q) {
+            // the pair's weights into the wave's tile: row 8 i + (l >> 3), slot
+            // l & 7 (a wave's LDS accesses complete in order: the reads of the
+            // previous pair are done before these writes)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                wtile[(8 * i + (l >> 3)) * kMmaTileStride + (l & 7)] = wl[q][i];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int p = 2 * q + h;
+                const int gb = gp0 + 4 * p;  // the step's first group (uniform)
+                half8 av[4];
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+                    av[tt] = *reinterpret_cast<const half8 *>(xrow + min(gb + tt, G - 1) * 32);
+                const float a0 = xsum[min(gb + kb, G - 1) * 16 + mrow];
+                // word kb of group 4 h + tt of row n
+                uint32_t w[4];
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+                    w[tt] = reinterpret_cast<const uint32_t *>(
+                        &wtile[n * kMmaTileStride + 4 * h + tt])[kb];
+                // the step's four scales of row n (zero past G)
+                const uint2 s4 = *reinterpret_cast<const uint2 *>(&sblk[n * GU + 4 * p]);
+                uint32_t sc[4] = {s4.x & 0xFFFFu, s4.x >> 16, s4.y & 0xFFFFu, s4.y >> 16};
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+                    if (gb + tt >= G)
+                        sc[tt] = 0u;
+                const uint32_t hs = (kb & 2) ? s4.y : s4.x;
+                const uint32_t sk = gb + kb < G ? ((kb & 1) ? hs >> 16 : hs & 0xFFFFu) : 0u;
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, h2f((uint16_t)sk), acc0, 0, 0, 0);
+                floatx4 d[4];
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+                    d[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[tt], codes_subnormal(w[tt]),
+                                                                   zero, 0, 0, 0);
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    // the f16 scale converted inside the FMA (v_fma_mix_f32)
+                    const float sf = h2f((uint16_t)sc[tt]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[e] = fmaf(sf, d[tt][e], acc[e]);
+                }
+                // the step's products are accumulated here, not deferred to
+                // the end of the unrolled steps (which would keep every
+                // step's MFMA results live at once)
+                asm volatile("" : "+v"(acc));
+            }
+        }
+        // this wave's part: 2^24 * code part - 7 * zero-point part
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            acc[e] = fmaf(-7.0f, acc0[e], acc[e] * 0x1p24f);
+        float *slot = red + (size_t)(r & 1) * kMmaWaves * 256;
+        *reinterpret_cast<floatx4 *>(slot + (wave * 64 + l) * 4) = acc;
+        __syncthreads();
+        // the tile's kp = 0 wave adds the KP parts in K order and stores: lane
+        // (n, kb) holds rows m = 4 kb .. 4 kb + 3 of column n
+        if (kp == 0 && tile < ntiles) {
+            floatx4 v = acc;
+            for (int qq = 1; qq < KP; ++qq) {
+                const floatx4 o = *reinterpret_cast<const floatx4 *>(slot + ((wave + qq) * 64 + l) * 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[e] += o[e];
+            }
+            const int col = tile * 16 + n;
+            if (col < N)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int m = 4 * kb + e;
+                    if (m < M) {
+                        if (a.yf)
+                            a.yf[m * a.ldy + col] = v[e];
+                        else
+                            a.y[m * a.ldy + col] = f2h(v[e]);
+                    }
+                }
+        }
+    }
+}
+
 }  // namespace
 
 int mfma_splits(int K)
@@ -467,10 +736,95 @@ q4_status launch_mfma_rows(const uint32_t *W, const uint16_t *S, const uint16_t 
     return check_launch("k_gemv_mfma");
 }
 
+namespace {
+// The launch of k_gemv_mma for an N x K matrix and mt <= 16 activation rows:
+// K parts per tile (enough units of work for most waves of the chip, at most
+// 12 steps and no part empty), the rounds, workgroups and LDS bytes.
+struct MmaPlan {
+    int KP, SK2, rounds, blocks;
+    size_t lds;
+};
+
+MmaPlan mma_plan(int N, int K, int mt)
+{
+    MmaPlan pl;
+    const int G = K / 32, ntiles = (N + 15) / 16;
+    const int steps = (G + 3) / 4;  // steps of four groups over the whole of K
+    const int target = kMmaWaves * cu_count() * 3 / 4;
+    static const int kParts[] = {1, 2, 3, 4, 6, 12};  // divisors of kMmaWaves
+    pl.KP = 0;
+    for (int c : kParts) {
+        if (c > steps && pl.KP)
+            break;
+        if ((steps + c - 1) / c > 2 * kMmaMaxPairs)
+            continue;  // a unit of more than 16 steps
+        pl.KP = c;
+        if ((int64_t)ntiles * c >= target)
+            break;
+    }
+    if (pl.KP == 0) {  // K too long for 12 parts of 16 steps
+        pl.lds = SIZE_MAX;
+        return pl;
+    }
+    pl.SK2 = ((steps + pl.KP - 1) / pl.KP + 1) / 2;
+    const int tpr = kMmaWaves / pl.KP;
+    pl.blocks = std::min(cu_count(), ntiles);
+    pl.rounds = (ntiles + pl.blocks * tpr - 1) / (pl.blocks * tpr);
+    pl.lds = (size_t)kMmaWaves * mma_wave_lds(pl.SK2) + (size_t)2 * kMmaWaves * 256 * sizeof(float) +
+             (size_t)mt * (K + 8) * 2 + (size_t)G * 16 * sizeof(float);
+    return pl;
+}
+
+template <int SK2>
+q4_status run_mma(const MmaArgs &args, const MmaPlan &pl, hipStream_t stream)
+{
+    Q4_LAUNCH_MATVEC((k_gemv_mma<SK2>), dim3(pl.blocks), dim3(64 * kMmaWaves), pl.lds, stream, args);
+    return check_launch("k_gemv_mma");
+}
+}  // namespace
+
+bool mma_fits(int N, int K, int M) { return mma_plan(N, K, std::min(M, kMTile)).lds <= 160 * 1024; }
+
+q4_status launch_gemv_mma(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
+                          uint16_t *y, float *yf, int64_t ldy, int N, int K, int M,
+                          hipStream_t stream)
+{
+    for (int m0 = 0; m0 < M; m0 += kMTile) {
+        const int mt = std::min(kMTile, M - m0);
+        const MmaPlan pl = mma_plan(N, K, mt);
+        if (pl.lds > 160 * 1024)
+            return fail(Q4_ERANGE, "internal: the batched matrix-core kernel does not fit K = %d", K);
+        MmaArgs args;
+        args.W = reinterpret_cast<const uint4 *>(W);
+        args.S = S;
+        args.x = x + m0 * ldx;
+        args.ldx = ldx;
+        args.y = yf ? nullptr : y + m0 * ldy;
+        args.yf = yf ? yf + m0 * ldy : nullptr;
+        args.ldy = ldy;
+        args.N = N;
+        args.G = K / 32;
+        args.M = mt;
+        args.KP = pl.KP;
+        args.rounds = pl.rounds;
+        q4_status st;
+        switch (pl.SK2) {
+#define Q4_MMA_CASE(d)                                                                            \
+    case d: st = run_mma<d>(args, pl, stream); break;
+            Q4_MMA_CASE(1) Q4_MMA_CASE(2) Q4_MMA_CASE(3) Q4_MMA_CASE(4) Q4_MMA_CASE(5) Q4_MMA_CASE(6)
+#undef Q4_MMA_CASE
+        default: return fail(Q4_ERANGE, "internal: %d step pairs for the batched matrix-core kernel", pl.SK2);
+        }
+        if (st != Q4_OK)
+            return st;
+    }
+    return Q4_OK;
+}
+
 size_t ws_rows(int N, int K, int M)
 {
-    if (M <= 1 || gemv_rows_fits(M, K) || mfma_splits(K) <= 1)
-        return 0;  // single-row and few-row kernels, or no K split
+    if (M <= 1 || gemv_rows_fits(M, K) || mma_fits(N, K, M) || mfma_splits(K) <= 1)
+        return 0;  // single-row, few-row and workgroup-reduced kernels, or no K split
     return kWsHeader + mfma_part_bytes(N, K);
 }
 
@@ -478,6 +832,8 @@ q4_status launch_gemv_mfma(const uint32_t *W, const uint16_t *S, const uint16_t 
                            uint16_t *y, float *yf, int64_t ldy, int N, int K, int M,
                            hipStream_t stream, const uint16_t *bias)
 {
+    if (!bias && mma_fits(N, K, M))
+        return launch_gemv_mma(W, S, x, ldx, y, yf, ldy, N, K, M, stream);
     const int KS = mfma_splits(K);
     float *part = nullptr;
     if (KS > 1) {

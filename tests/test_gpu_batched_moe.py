@@ -49,6 +49,13 @@ BATCHED = [
     ("phi3_down_m2", 3072, 8192, 2),
     ("qwen3_qkv_m3", 6144, 2560, 3),
     ("ragged_m4", 37, 96, 4),
+    # the workgroup-reduced matrix-core kernel: a group count that leaves the
+    # last wave's quarter part empty, four 16-row tiles per workgroup with a
+    # half-empty last workgroup, 16 rows, and 17 rows (two launches)
+    ("mma_ragged_groups_m8", 1000, 2528, 8),
+    ("mma_four_tiles_tail_m6", 32800, 256, 6),
+    ("mma_m16", 3000, 2048, 16),
+    ("mma_m17", 500, 1024, 17),
 ]
 
 
@@ -215,7 +222,8 @@ def test_moe_deterministic(o, q4, moe128):
     assert np.array_equal(outs[0], outs[1])
 
 
-@pytest.mark.parametrize("n,k,m", [(3072, 3072, 8), (2560, 9728, 5), (96, 256, 16)])
+@pytest.mark.parametrize("n,k,m", [(3072, 3072, 8), (2560, 9728, 5), (96, 256, 16),
+                                   (19456, 2560, 8), (1000, 2528, 13)])
 def test_batched_one_hot_rows_are_exact(o, q4, n, k, m):
     """Row m of X is one-hot at column k_m: y[m][n] = f16((q[n][k_m] - 7) *
     s[n][k_m / 32]) exactly, so the batched path must not round a dequantised

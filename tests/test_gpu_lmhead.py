@@ -235,7 +235,7 @@ def test_lm_head_planted_maximum(o, q4):
         S = datagen.scales(601, n, k)
         S[r1] = S[r0]
         x = np.abs(datagen.activations(602, 1, k)[0]).astype(np.float16)
-        for m in (1, 2):
+        for m in (1, 2, 8):
             X = np.stack([x] * m)
             logits, tok = q4.lm_head_argmax(dev_tensor(W), dev_tensor(S),
                                             dev_tensor(X if m > 1 else x))
