@@ -454,19 +454,20 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ part,
 // Work split. One workgroup of kMmaWaves waves per CU stages the activation
 // once in LDS (pair order, odd positions / 16, group sums) and keeps it for
 // the whole launch. A unit of work is one 16-row tile times one of KP equal
-// parts of K (SK = 2 SK2 steps of four groups); the KP waves of a tile run in
-// step, one unit per round each, and the tiles of a round are blockIdx.x +
-// gridDim.x * (slot + (kMmaWaves / KP) * round). A wave issues all loads of a
-// unit at once, in whole memory lines: the unit's scales as a row-major block
-// (64 consecutive scales per load), then its weights as 8 rows x 128 bytes
-// per load (a pair of steps per two loads). The scales go to a per-wave LDS
-// block, each pair of steps' weights to a per-wave LDS tile from which every
-// lane reads the words of its MFMA lane (word kb of each group of row n):
-// no exchanges across lanes in registers. After each round the waves' f32
-// parts meet in LDS (two slots, one barrier) and the tile's kp = 0 wave adds
-// them in K order and stores. Every wave runs the same number of rounds
-// (units past the last tile re-read valid data and are not stored), so the
-// barriers match.
+// parts of K (SK = 2 SK2 steps of four groups); wave w takes part w % KP of
+// the tiles blockIdx.x + gridDim.x * (w / KP + (kMmaWaves / KP) * round), one
+// unit per round. A wave issues all loads of a unit at once, in whole memory
+// lines: the unit's scales as a row-major block (64 consecutive scales, or
+// pairs of them, per load), then its weights as 8 rows x 128 bytes per load
+// (a pair of steps per two loads). The scales go to a per-wave LDS block, each
+// pair of steps' weights to a per-wave LDS tile from which every lane reads
+// the words of its MFMA lane (word kb of each group of row n): no exchanges
+// across lanes in registers. The KP parts of a tile meet in an LDS slot
+// without a barrier, so the waves of a CU drift apart and one wave's loads
+// overlap another's arithmetic: the last of the KP waves to arrive (an LDS
+// counter) adds the parts in K order, stores, and frees the slot for its use
+// two rounds later. Every wave of a tile runs the same number of rounds
+// (units past the last tile re-read valid data and are not stored).
 constexpr int kMmaWaves = 12;   // three waves per SIMD
 constexpr int kMmaMaxPairs = 6;  // steps per unit <= 12 (7 pairs spill registers)
 constexpr int kMmaXq = 8;       // activation chunks per thread held in registers
@@ -496,11 +497,15 @@ struct MmaArgs {
 // LDS bytes of one wave's scale block and weight tile
 constexpr int mma_wave_lds(int SK2) { return 16 * 8 * SK2 * 2 + 16 * kMmaTileStride * 16; }
 
-template <int SK2>
+template <int SK2, bool SP>
 __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
 {
     constexpr int SK = 2 * SK2;  // steps per unit
     constexpr int GU = 4 * SK;   // groups per unit
+    // short units: the first unit's loads go out before the activation is
+    // staged (behind its loads); with long units, the whole matrix at once
+    // would hold the activation's loads back in the memory queues
+    constexpr bool kEarly = SK2 <= 3;
     extern __shared__ uint4 smem[];
     const int G = a.G, K = G * 32, M = a.M, N = a.N;
     const int xstride = K + 8;  // staged row: 16 bytes of padding against bank conflicts
@@ -508,14 +513,17 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int n = l & 15, kb = l >> 4;
     // LDS: per wave a scale block [16][GU] and a weight tile [16][9] x 16 B;
-    // the waves' parts [2][kMmaWaves][64 lanes][4] f32; the staged rows
-    // [M][xstride] binary16; the group sums [G][16] f32
+    // the waves' parts [2][kMmaWaves][64 lanes][4] f32; arrival counters and
+    // use counts [2][kMmaWaves] u32 each; the staged rows [M][xstride]
+    // binary16; the group sums [G][16] f32
     char *wbase = reinterpret_cast<char *>(smem) + (size_t)wave * mma_wave_lds(SK2);
     uint16_t *sblk = reinterpret_cast<uint16_t *>(wbase);
     uint4 *wtile = reinterpret_cast<uint4 *>(wbase + 16 * GU * 2);
     float *red = reinterpret_cast<float *>(reinterpret_cast<char *>(smem) +
                                            (size_t)kMmaWaves * mma_wave_lds(SK2));
-    _Float16 *xs = reinterpret_cast<_Float16 *>(red + 2 * kMmaWaves * 256);
+    uint32_t *arrived = reinterpret_cast<uint32_t *>(red + 2 * kMmaWaves * 256);
+    uint32_t *uses = arrived + 2 * kMmaWaves;
+    _Float16 *xs = reinterpret_cast<_Float16 *>(uses + 2 * kMmaWaves);
     float *xsum = reinterpret_cast<float *>(xs + M * xstride);
 
     const int KP = a.KP, rounds = a.rounds;
@@ -524,12 +532,47 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
     const int gp0 = kp * GU;  // first group of this wave's part of K
     auto tile_of = [&](int r) { return (int)blockIdx.x + (int)gridDim.x * (tslot + tpr * r); };
 
-    // 1. the activation's chunks (up to kMmaXq per thread) into registers, then
-    //    into LDS: the pair order, the odd positions x1 x3 x5 x7 (the high
-    //    halves of the words, which meet the 2^-20 pairs) divided by 16, and
-    //    each group's sum of the unscaled values (a quad of lanes holds the
-    //    four chunks of a group: cpr and the thread count are multiples of 4,
-    //    so quads never mix rows)
+    // the loads of unit r (branch-free: groups past G re-read group G - 1 and
+    // are zeroed at use; rows past N re-read row N - 1; units past the last
+    // tile re-read the last tile and are not stored): its scales as elements
+    // e = 64 j + l of the row-major block [16][GU], then its weights, pair q
+    // and half i as lane l reading group gp0 + 8 q + (l & 7) of row 8 i +
+    // (l >> 3): 8 rows x 128 bytes per load
+    // (SP, G even: the scales in pairs, elements 2 (64 j + l) and the next, one
+    // 4-byte load each: a pair never straddles a row and is 4-byte aligned)
+    constexpr int NSL = SP ? SK2 : SK;  // scale loads per unit
+    struct Unit {
+        uint32_t sl[NSL];
+        uint4 wl[SK2][2];
+    };
+    auto load_unit = [&](int r, Unit &u) __attribute__((always_inline)) {
+        const int row0 = min(tile_of(r), ntiles - 1) * 16;
+#pragma unroll
+        for (int j = 0; j < NSL; ++j) {
+            const int e = SP ? 2 * (64 * j + l) : 64 * j + l;
+            const int rr = e / GU, cc = e - rr * GU;
+            const size_t off = (size_t)min(row0 + rr, N - 1) * G + min(gp0 + cc, G - (SP ? 2 : 1));
+            if (SP)
+                u.sl[j] = __builtin_nontemporal_load(
+                    (__attribute__((address_space(1))) const uint32_t *)(a.S + off));
+            else
+                u.sl[j] = load_scale(a.S + off);
+        }
+#pragma unroll
+        for (int q = 0; q < SK2; ++q)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int rr = min(row0 + 8 * i + (l >> 3), N - 1);
+                u.wl[q][i] = load_weights(a.W + (size_t)rr * G + min(gp0 + 8 * q + (l & 7), G - 1));
+            }
+    };
+
+    // 1. the activation's chunks (up to kMmaXq per thread) into registers,
+    //    then into LDS: the pair order, the odd positions x1 x3 x5 x7 (the high halves of the words,
+    //    which meet the 2^-20 pairs) divided by 16, and each group's sum of the
+    //    unscaled values (a quad of lanes holds the four chunks of a group: cpr
+    //    and the thread count are multiples of 4, so quads never mix rows)
+    Unit ua;
     {
         const int cpr = K >> 3;
         const int total = M * cpr;  // a multiple of 4
@@ -568,6 +611,8 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
         for (int i = 0; i < kMmaXq; ++i)
             if (i < xq)
                 xr[i] = chunk(i * kThreads + t);
+        if (kEarly)
+            load_unit(0, ua);
 #pragma unroll
         for (int i = 0; i < kMmaXq; ++i)
             if (i < xq)
@@ -576,50 +621,32 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
         for (int c0 = kMmaXq * kThreads; c0 < total; c0 += kThreads)
             stage(c0 + t, chunk(c0 + t));
     }
+    if (t < 4 * kMmaWaves)
+        arrived[t] = 0u;  // and uses[]
     __syncthreads();
 
-    // 2. the rounds
+    // 2. the rounds: each unit issues all of its loads, then computes
     const int mrow = min(n, M - 1);  // A row m = n
     const _Float16 *xrow = xs + mrow * xstride + 8 * kb;
     const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
-    for (int r = 0; r < rounds; ++r) {
-        const int tile = tile_of(r);
-        const int row0 = min(tile, ntiles - 1) * 16;  // units past the end re-read the last tile
-        // the unit's scales, element e = 64 j + l of the row-major block
-        // [16][GU] (branch-free: groups past G re-read group G - 1 and are
-        // zeroed at use; rows past N re-read row N - 1)
-        uint32_t sl[SK];
+    auto compute_unit = [&](int r, const Unit &u) __attribute__((always_inline)) {
+        // the scales into the wave's block (a wave's LDS accesses complete in
+        // order: the previous unit's reads are done)
 #pragma unroll
-        for (int j = 0; j < SK; ++j) {
-            const int e = 64 * j + l;
-            const int rr = e / GU, cc = e - rr * GU;
-            sl[j] = load_scale(a.S + (size_t)min(row0 + rr, N - 1) * G + min(gp0 + cc, G - 1));
+        for (int j = 0; j < NSL; ++j) {
+            if (SP)
+                reinterpret_cast<uint32_t *>(sblk)[64 * j + l] = u.sl[j];
+            else
+                sblk[64 * j + l] = (uint16_t)u.sl[j];
         }
-        // the unit's weights: pair q, half i: lane l reads group gp0 + 8 q +
-        // (l & 7) of row 8 i + (l >> 3), 8 rows x 128 bytes per load
-        uint4 wl[SK2][2];
-#pragma unroll
-        for (int q = 0; q < SK2; ++q)
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int rr = min(row0 + 8 * i + (l >> 3), N - 1);
-                wl[q][i] = load_weights(a.W + (size_t)rr * G + min(gp0 + 8 * q + (l & 7), G - 1));
-            }
-        // the scales into the wave's block (waiting for the scale loads only:
-        // they were issued first)
-#pragma unroll
-        for (int j = 0; j < SK; ++j)
-            sblk[64 * j + l] = (uint16_t)sl[j];
-
         floatx4 acc = zero, acc0 = zero;
 #pragma unroll
         for (int q = 0; q < SK2; ++q) {
             // the pair's weights into the wave's tile: row 8 i + (l >> 3), slot
-            // l & 7 (a wave's LDS accesses complete in order: the reads of the
-            // previous pair are done before these writes)
+            // l & 7 (the previous pair's reads are done)
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-                wtile[(8 * i + (l >> 3)) * kMmaTileStride + (l & 7)] = wl[q][i];
+                wtile[(8 * i + (l >> 3)) * kMmaTileStride + (l & 7)] = u.wl[q][i];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int p = 2 * q + h;
@@ -668,19 +695,48 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             acc[e] = fmaf(-7.0f, acc0[e], acc[e] * 0x1p24f);
-        float *slot = red + (size_t)(r & 1) * kMmaWaves * 256;
-        *reinterpret_cast<floatx4 *>(slot + (wave * 64 + l) * 4) = acc;
-        __syncthreads();
-        // the tile's kp = 0 wave adds the KP parts in K order and stores: lane
-        // (n, kb) holds rows m = 4 kb .. 4 kb + 3 of column n
-        if (kp == 0 && tile < ntiles) {
-            floatx4 v = acc;
-            for (int qq = 1; qq < KP; ++qq) {
-                const floatx4 o = *reinterpret_cast<const floatx4 *>(slot + ((wave + qq) * 64 + l) * 4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    v[e] += o[e];
+        // the KP parts of the tile meet in LDS slot r & 1 without a barrier:
+        // each wave waits until the slot's previous use (round r - 2) has
+        // been read, writes its part, and counts itself in; the last to
+        // arrive adds the parts in K order, stores, and releases the slot.
+        // Lane (n, kb) holds rows m = 4 kb .. 4 kb + 3 of column n.
+        const int tile = tile_of(r);
+        bool last = true;
+        floatx4 v = acc;
+        if (KP > 1) {
+            const int sl = (r & 1) * kMmaWaves + tslot;
+            float *slot = red + (size_t)(r & 1) * kMmaWaves * 256;
+            const uint32_t want = (uint32_t)(r >> 1);
+            // (bounded: the reader of round r - 2 depends on no other wave)
+            for (int spin = 0; spin < (1 << 22); ++spin) {
+                const uint32_t u =
+                    __hip_atomic_load(&uses[sl], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+                if (__builtin_amdgcn_readfirstlane(u) == want)
+                    break;
+                __builtin_amdgcn_s_sleep(2);
             }
+            *reinterpret_cast<floatx4 *>(slot + (wave * 64 + l) * 4) = acc;
+            uint32_t before = 0;
+            if (l == 0)
+                before = __hip_atomic_fetch_add(&arrived[sl], 1u, __ATOMIC_ACQ_REL,
+                                                __HIP_MEMORY_SCOPE_WORKGROUP);
+            last = __builtin_amdgcn_readfirstlane(before) == (uint32_t)(KP - 1);
+            if (last) {
+                const int w0 = tslot * KP;  // the tile's kp = 0 wave
+                v = *reinterpret_cast<const floatx4 *>(slot + (w0 * 64 + l) * 4);
+                for (int qq = 1; qq < KP; ++qq) {
+                    const floatx4 o = *reinterpret_cast<const floatx4 *>(slot + ((w0 + qq) * 64 + l) * 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        v[e] += o[e];
+                }
+                if (l == 0) {
+                    __hip_atomic_store(&arrived[sl], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    __hip_atomic_store(&uses[sl], want + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+                }
+            }
+        }
+        if (last && tile < ntiles) {
             const int col = tile * 16 + n;
             if (col < N)
 #pragma unroll
@@ -694,6 +750,11 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
                     }
                 }
         }
+    };
+    for (int r = 0; r < rounds; ++r) {
+        if (!kEarly || r > 0)
+            load_unit(r, ua);
+        compute_unit(r, ua);
     }
 }
 
@@ -752,12 +813,14 @@ MmaPlan mma_plan(int N, int K, int mt)
     const int steps = (G + 3) / 4;  // steps of four groups over the whole of K
     const int target = kMmaWaves * cu_count() * 3 / 4;
     static const int kParts[] = {1, 2, 3, 4, 6, 12};  // divisors of kMmaWaves
+    // (6 pairs with single scales, G odd, spill registers)
+    const int max_pairs = G % 2 == 0 ? kMmaMaxPairs : kMmaMaxPairs - 1;
     pl.KP = 0;
     for (int c : kParts) {
         if (c > steps && pl.KP)
             break;
-        if ((steps + c - 1) / c > 2 * kMmaMaxPairs)
-            continue;  // a unit of more than 16 steps
+        if ((steps + c - 1) / c > 2 * max_pairs)
+            continue;  // a unit of too many steps
         pl.KP = c;
         if ((int64_t)ntiles * c >= target)
             break;
@@ -771,14 +834,20 @@ MmaPlan mma_plan(int N, int K, int mt)
     pl.blocks = std::min(cu_count(), ntiles);
     pl.rounds = (ntiles + pl.blocks * tpr - 1) / (pl.blocks * tpr);
     pl.lds = (size_t)kMmaWaves * mma_wave_lds(pl.SK2) + (size_t)2 * kMmaWaves * 256 * sizeof(float) +
-             (size_t)mt * (K + 8) * 2 + (size_t)G * 16 * sizeof(float);
+             (size_t)4 * kMmaWaves * sizeof(uint32_t) + (size_t)mt * (K + 8) * 2 +
+             (size_t)G * 16 * sizeof(float);
     return pl;
 }
 
 template <int SK2>
 q4_status run_mma(const MmaArgs &args, const MmaPlan &pl, hipStream_t stream)
 {
-    Q4_LAUNCH_MATVEC((k_gemv_mma<SK2>), dim3(pl.blocks), dim3(64 * kMmaWaves), pl.lds, stream, args);
+    if (args.G % 2 == 0 && (reinterpret_cast<uintptr_t>(args.S) & 3) == 0)
+        Q4_LAUNCH_MATVEC((k_gemv_mma<SK2, true>), dim3(pl.blocks), dim3(64 * kMmaWaves), pl.lds,
+                         stream, args);
+    else
+        Q4_LAUNCH_MATVEC((k_gemv_mma<SK2, false>), dim3(pl.blocks), dim3(64 * kMmaWaves), pl.lds,
+                         stream, args);
     return check_launch("k_gemv_mma");
 }
 }  // namespace
