@@ -260,6 +260,7 @@ def committed_traffic():
 
 
 GEMV_TABLE_PROFILE = os.path.join(ROOT, "profiles", "gemv_table_phi3_qwen3_moe.md")
+MOE_KERNELS = "the gate_up stage one expert kernel, the down stage an expert kernel and a finishing kernel"
 QWEN3 = dict(qkv=(6144, 2560), o=(2560, 4096), gate_up=(19456, 2560), down=(2560, 9728),
              lm_head=(151936, 2560))
 
@@ -507,20 +508,24 @@ def gemv_table(q4, torch, o=None, threads=HOST_THREADS):
         x = torch.from_numpy(datagen.activations(base + 4100 + t, t, hidden)).cuda()
         uniq = float(np.mean([len(np.unique(ids_h[i])) for i in range(len(ids_h))]))
 
-        def launch(i, ids=ids, rw=rw, x=x):
-            Wg, Sg, Wd, Sd = stacks[i & 1]
-            u = q4.moe_gemv(Wg, Sg, ids[i % 256], x, ldx=hidden, x_slot_stride=0, epi_silu=True)
-            q4.moe_gemv(Wd, Sd, ids[i % 256], u, ldx=topk * f, x_slot_stride=f,
-                        route_w=rw[i % 256])
+        u = torch.empty((t, topk, f), dtype=torch.float16, device="cuda")
+        y = torch.empty((t, hidden), dtype=torch.float16, device="cuda")
 
-        call_us, _ = _time(q4, torch, launch, 200, timed_kernels=False)
+        def launch(i, ids=ids, rw=rw, x=x, u=u, y=y):
+            Wg, Sg, Wd, Sd = stacks[i & 1]
+            q4.moe_gemv(Wg, Sg, ids[i % 256], x, ldx=hidden, x_slot_stride=0, epi_silu=True,
+                        y=u)
+            q4.moe_gemv(Wd, Sd, ids[i % 256], u, ldx=topk * f, x_slot_stride=f,
+                        route_w=rw[i % 256], y=y)
+
+        call_us = _time_graph(q4, torch, launch, 32)
         wb = uniq * expert_bytes
         gbs = wb / (call_us * 1e-6) / 1e9
         row = dict(workload="MoE layer (128 experts, top-8)", shape="T=%d" % t, m=t,
                    weight_bytes=int(wb), us_kernel=None, us_per_call=round(call_us, 3),
                    gbs=round(gbs, 1), pct_peak=round(100 * gbs / HBM_PEAK_GBS, 1),
-                   note="%.2f unique experts per layer on average; time of both stages "
-                        "back to back (an expert kernel and a finishing kernel each)" % uniq)
+                   note="%.2f unique experts per layer on average; both stages, timed from a "
+                        "HIP graph of 32 layers (%s)" % (uniq, MOE_KERNELS))
         if o is not None:
             row["oracle_us_1t"], row["oracle_us_all"] = (
                 round(oracle_moe_us(o, moe_host, ids_h[0], w_h[0],

@@ -30,6 +30,11 @@ namespace {
 
 constexpr int kWaves = 4;  // 256 threads per workgroup
 constexpr int kMaxRowsDot = 4;  // batched rows handled by the dot2 kernel
+// pairs from which the dot2 expert kernel takes twice the single-row kernel's
+// rows per workgroup: each workgroup routes and stages its pairs' activations
+// once, for more weight rows (measured on 128 experts, top 8: 32 pairs and
+// up gain, 8 pairs need the workgroups)
+constexpr int kMoeWideRowsPairs = 32;
 
 enum { PRO_X = 0, PRO_NORM = 1 };
 enum { EPI_NONE_ = 0, EPI_SILU = 1, EPI_RESID = 2, EPI_LOGITS = 3, EPI_ROPE = 4 };
@@ -761,10 +766,12 @@ struct MoeRowsArgs {
     int out, E, N, G, P, TOPK, slots;
 };
 
-template <int LPR, int NG>
+template <int LPR, int NG, int SC = 1>
 q4_status run_moe_rows(const MoeRowsArgs &a, hipStream_t st)
 {
-    constexpr int RPS = rows_per_segment(NG);
+    if (a.P >= kMoeWideRowsPairs && SC == 1)
+        return run_moe_rows<LPR, NG, 2>(a, st);
+    constexpr int RPS = SC * rows_per_segment(NG);
     constexpr int RB = kWaves * (64 / LPR) * RPS;
     const size_t lds = (size_t)kMaxRowsDot * (a.G * 4 + a.G / 4 + 1) * 16;
     if (a.out == kMoeOutSilu)
