@@ -157,6 +157,14 @@ q4_status launch_moe_finish(int mode, const float *part, int KS, int P, int N,
 // results part[pair][n] (for launch_moe_finish), 1 f16 outputs y[pair][n],
 // 2 y[pair][i] = f16(silu(f16(gate_i)) * f16(up_i)) over N / 2 (N even); in
 // forms 1 and 2 pairs with an id outside [0, E) get zeros.
+// The down stage with the routing-weighted combine, token by token (few
+// pairs, moe_tokens_fits): one kernel, no routing step, no per-pair results.
+// shared_x: every slot reads the token's one activation row (x_slot_stride 0).
+bool moe_tokens_fits(int T, int TOPK, int K, bool shared_x);
+q4_status launch_moe_tokens(const uint32_t *W, const uint16_t *S, const int32_t *ids,
+                            const uint16_t *route_w, const uint16_t *x, int64_t ldx,
+                            int64_t x_slot_stride, uint16_t *y, int E, int N, int K, int T,
+                            int TOPK, hipStream_t stream);
 q4_status launch_moe_rows(const uint32_t *W, const uint16_t *S, const int32_t *ids,
                           const int32_t *meta, const uint16_t *x, int64_t ldx,
                           int64_t x_slot_stride, int out, float *part, uint16_t *y, int E, int N,

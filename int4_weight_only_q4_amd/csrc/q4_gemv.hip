@@ -35,6 +35,12 @@ constexpr int kMaxRowsDot = 4;  // batched rows handled by the dot2 kernel
 // once, for more weight rows (measured on 128 experts, top 8: 32 pairs and
 // up gain, 8 pairs need the workgroups)
 constexpr int kMoeWideRowsPairs = 32;
+// the token-by-token down kernel: activation chunks per thread held in
+// registers, 64-lane weight units per wave, output rows per workgroup
+constexpr int kMoeTokXq = 4;
+constexpr int kMoeTokCpt = 8;
+constexpr int kMoeTokRows = 8;
+constexpr int kMoeTokMaxPairs = 32;  // pairs from which experts chosen twice cost too much
 
 enum { PRO_X = 0, PRO_NORM = 1 };
 enum { EPI_NONE_ = 0, EPI_SILU = 1, EPI_RESID = 2, EPI_LOGITS = 3, EPI_ROPE = 4 };
@@ -618,6 +624,127 @@ __global__ __launch_bounds__(256) void k_moe_rows(const uint4 *__restrict__ Wall
                                               TOPK, out, part, y, s_vals, N, G);
 }
 
+// MoE down stage with the routing-weighted combine, token by token, for few
+// pairs: grid (row blocks, T). Workgroup (b, t) runs block b of rows of each
+// of token t's TOPK experts against the slot's activation row, with the
+// single-row group arithmetic, and stores y[t][n] = f16(sum_s route_w[t][s]
+// v_s[n]) over the slots with a valid id, in slot order, as k_moe_finish
+// forms it: the combine without per-pair results, a routing step or a second
+// kernel. An expert chosen by several tokens is read once per token (the
+// expert-grouped kernels read it once), so the host takes this path for few
+// pairs.
+// Work split: each slot's rows * G weight chunks (one contiguous block of its
+// expert's matrix: row-major, rows of G chunks) are cut into segs units of 64
+// lanes; wave w takes units w, w + 4, ..., so every unit's slot, and with it
+// the expert id, is the same for the whole wave (a scalar load). Each chunk's
+// scaled group sum goes to LDS; 8 lanes per (slot, row) add the G sums.
+template <int CPT>
+__global__ __launch_bounds__(256) void k_moe_tokens(const uint4 *__restrict__ Wall,
+                                                    const uint16_t *__restrict__ Sall,
+                                                    const int32_t *__restrict__ ids,
+                                                    const uint16_t *__restrict__ route_w,
+                                                    const uint16_t *__restrict__ x, int64_t ldx,
+                                                    int64_t slot_stride, uint16_t *__restrict__ y,
+                                                    int E, int N, int G, int TOPK, int rows,
+                                                    int segs)
+{
+    extern __shared__ uint4 smem[];
+    const int K = G * 32, chunks = K >> 3;
+    const int stride = chunks + G / 4 + 1;  // uint4 units per staged activation row
+    const int nx = slot_stride ? TOPK : 1;  // staged activation rows (one when all slots share it)
+    const int t = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int per_slot = rows * G, units = TOPK * segs, nrow = TOPK * rows;
+    float *part = reinterpret_cast<float *>(smem + nx * stride);  // [TOPK][rows][G]
+    float *vrow = part + TOPK * per_slot;                         // [TOPK][rows]
+    float *s_w = vrow + nrow;                                     // [TOPK] routing weights
+    int *s_ok = reinterpret_cast<int *>(s_w + TOPK);              // [TOPK] id in [0, E)
+    // matrix row of local row r, or -1 past the matrix
+    auto row_of = [&](int r) {
+        const int n = blockIdx.x * rows + r;
+        return n < N ? n : -1;
+    };
+
+    // 1. the slots' validity and weights, and the activation rows
+    //    (kMoeTokXq chunks per thread at most) into registers
+    if (tid < TOPK) {
+        const int e = ids[t * TOPK + tid];
+        s_ok[tid] = e >= 0 && e < E;
+        s_w[tid] = h2f(route_w[t * TOPK + tid]);
+    }
+    const int xtot = nx * chunks;
+    uint4 xr[kMoeTokXq];
+#pragma unroll
+    for (int i = 0; i < kMoeTokXq; ++i) {
+        const int c = tid + 256 * i;
+        xr[i] = make_uint4(0u, 0u, 0u, 0u);
+        if (c < xtot) {
+            const int sl = c / chunks, j = c - sl * chunks;
+            xr[i] = reinterpret_cast<const uint4 *>(x + (int64_t)t * ldx + (int64_t)sl * slot_stride)[j];
+        }
+    }
+    // 2. the weight chunks, unit wave + 4 i (branch-free: units and chunks
+    //    past the end re-read the last one, an invalid id reads expert 0, a
+    //    row past the matrix reads row 0; none of these is used)
+    uint4 wv[CPT];
+    uint32_t sv[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int u = min(wave + 4 * i, units - 1);  // uniform
+        const int sl = u / segs;
+        const int cs = min((u - sl * segs) * 64 + lane, per_slot - 1);
+        const int r = cs / G, g = cs - r * G;
+        const int e = ids[t * TOPK + sl];  // uniform
+        const size_t off = ((size_t)(e >= 0 && e < E ? e : 0) * N + max(row_of(r), 0)) * G + g;
+        wv[i] = load_weights(Wall + off);
+        sv[i] = load_scale(Sall + off);
+    }
+    // 3. the activation rows into LDS (pair order and group sums)
+#pragma unroll
+    for (int i = 0; i < kMoeTokXq; ++i) {
+        const int c = tid + 256 * i;
+        const bool live = c < xtot;
+        const int sl = live ? c / chunks : 0, j = live ? c - sl * chunks : 0;
+        uint4 *xs = smem + sl * stride;
+        put_chunk(xr[i], j, live, xs, reinterpret_cast<float *>(xs + chunks));
+    }
+    __syncthreads();
+    // 4. every chunk's scaled group sum
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int u = wave + 4 * i;
+        const int sl = u / segs, cs = (u - sl * segs) * 64 + lane;
+        if (u < units && cs < per_slot) {
+            const int g = cs % G;
+            const uint4 *xs = smem + (slot_stride ? sl : 0) * stride;
+            const float sx = reinterpret_cast<const float *>(xs + chunks)[g];
+            part[sl * per_slot + cs] = h2f(sv[i]) * group_dot(wv[i], xs, g, sx);
+        }
+    }
+    __syncthreads();
+    // 5. each (slot, row): its G group sums, 8 lanes in a fixed order
+    for (int q0 = 0; q0 < nrow; q0 += 32) {
+        const int q = q0 + (tid >> 3), k = tid & 7;
+        float v = 0.f;
+        if (q < nrow)
+            for (int g = k; g < G; g += 8)
+                v += part[q * G + g];
+        v = segment_sum(v, 8);
+        if (k == 0 && q < nrow)
+            vrow[q] = v;
+    }
+    __syncthreads();
+    // 6. each row: the valid slots in order, by routing weight
+    const int n = tid < rows ? row_of(tid) : -1;
+    if (n >= 0) {
+        float acc = 0.f;
+        for (int sl = 0; sl < TOPK; ++sl)
+            if (s_ok[sl])
+                acc = fmaf(s_w[sl], vrow[sl * rows + tid], acc);
+        y[(int64_t)t * N + n] = f2h(acc);
+    }
+}
+
 struct Cfg {
     int lpr, ng;
 };
@@ -847,6 +974,55 @@ q4_status launch_moe_rows(const uint32_t *W, const uint16_t *S, const int32_t *i
     case 8: return moe_rows_ng<8>(c.ng, a, stream);
     default: return fail(Q4_ERANGE, "no matvec configuration for K = %d", K);
     }
+}
+
+namespace {
+// Rows per workgroup of the token-wise down kernel: at most kMoeTokRows and
+// within kMoeTokCpt units per wave; 0 if none fits. (The row count barely
+// matters at one token on 128 experts, top 8: 1 to 8 rows measured within
+// 0.5 us; the kernel waits on two memory round trips, ids then weights.)
+int moe_tokens_rows(int TOPK, int K)
+{
+    const int G = K / 32;
+    for (int rows = kMoeTokRows; rows >= 1; --rows)
+        if (TOPK * ((rows * G + 63) / 64) <= 4 * kMoeTokCpt)
+            return rows;
+    return 0;
+}
+}  // namespace
+
+bool moe_tokens_fits(int T, int TOPK, int K, bool shared_x)
+{
+    return T * TOPK <= kMoeTokMaxPairs && (shared_x ? 1 : TOPK) * (K / 8) <= 256 * kMoeTokXq &&
+           moe_tokens_rows(TOPK, K) > 0;
+}
+
+q4_status launch_moe_tokens(const uint32_t *W, const uint16_t *S, const int32_t *ids,
+                            const uint16_t *route_w, const uint16_t *x, int64_t ldx,
+                            int64_t x_slot_stride, uint16_t *y, int E, int N, int K, int T,
+                            int TOPK, hipStream_t stream)
+{
+    const int G = K / 32, chunks = K / 8, stride = chunks + G / 4 + 1;
+    const int rows = moe_tokens_rows(TOPK, K);
+    if (rows == 0)
+        return fail(Q4_ERANGE, "internal: no row block for the token-wise expert kernel");
+    const int segs = (rows * G + 63) / 64, cpt = (TOPK * segs + 3) / 4;
+    const int nx = x_slot_stride ? TOPK : 1;
+    const size_t lds = (size_t)nx * stride * 16 + (size_t)TOPK * (segs * 64 + rows + 2) * 4;
+    const dim3 grid((N + rows - 1) / rows, T);
+    const uint4 *Wv = reinterpret_cast<const uint4 *>(W);
+#define Q4_TOK_CASE(c)                                                                            \
+    case c:                                                                                       \
+        Q4_LAUNCH_MATVEC((k_moe_tokens<c>), grid, dim3(256), lds, stream, Wv, S, ids, route_w, x,  \
+                         ldx, x_slot_stride, y, E, N, G, TOPK, rows, segs);                       \
+        break;
+    switch (cpt) {
+        Q4_TOK_CASE(1) Q4_TOK_CASE(2) Q4_TOK_CASE(3) Q4_TOK_CASE(4) Q4_TOK_CASE(5) Q4_TOK_CASE(6)
+        Q4_TOK_CASE(7) Q4_TOK_CASE(8)
+    default: return fail(Q4_ERANGE, "internal: %d units per wave for the token-wise down kernel", cpt);
+    }
+#undef Q4_TOK_CASE
+    return check_launch("k_moe_tokens");
 }
 
 int matvec_blocks(int N, int K)

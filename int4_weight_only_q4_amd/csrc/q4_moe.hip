@@ -122,6 +122,11 @@ q4_status launch_moe(const uint32_t *W, const uint16_t *S, const int32_t *ids,
 {
     const int P = T * TOPK;
     const int mode = epi_silu ? MOE_SILU : (route_w ? MOE_COMBINE : MOE_PER_SLOT);
+    if (mode == MOE_COMBINE && moe_tokens_fits(T, TOPK, K, x_slot_stride == 0))
+        // few pairs: token by token, the combine in the same kernel (no
+        // routing step, no finishing kernel)
+        return launch_moe_tokens(W, S, ids, route_w, x, ldx, x_slot_stride, y, E, N, K, T, TOPK,
+                                 stream);
     const bool in_kernel = moe_routes_in_kernel(P, E);
     const size_t meta_bytes = moe_meta_bytes(E, P);
     char *ws = static_cast<char *>(workspace(stream, ws_moe(E, N, K, P)));

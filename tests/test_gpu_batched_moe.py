@@ -350,3 +350,53 @@ def test_moe_max_pairs(o, q4):
                   "per-slot")
     assert_within(host(yc), o.moe_stage(W, S, ids, rw, x, topk * k, k, n, k, epi_silu=False),
                   "combine")
+
+
+@pytest.mark.parametrize("t,topk,n,k", [(2, 4, 83, 1024), (1, 8, 2051, 768), (4, 8, 40, 96),
+                                        (3, 5, 17, 32)])
+def test_moe_token_wise_combine(o, q4, t, topk, n, k):
+    """At most 32 pairs the combine stage runs token by token (the routing-
+    weighted sum in the expert kernel): output rows not a multiple of the
+    kernel's 8-row blocks, an expert repeated within a token, an out-of-range
+    id, against the oracle with the invalid slot's weight set to zero."""
+    e = 9
+    W, S = experts(o, 1800 + n + k, e, n, k)
+    rng = np.random.default_rng(1801 + t * topk)
+    ids = rng.integers(0, e, size=(t, topk)).astype(np.int32)
+    ids[0, 0] = ids[0, topk - 1]
+    ids[t - 1, topk // 2] = -3 if t > 1 else e
+    rw = (rng.random((t, topk)) / topk).astype(np.float16)
+    x = datagen.activations(1802 + n, t * topk, k)
+    yc = q4.moe_gemv(dev_tensor(W), dev_tensor(S), dev_tensor(ids), dev_tensor(x),
+                     ldx=topk * k, x_slot_stride=k, route_w=dev_tensor(rw))
+    sync()
+    valid = (ids >= 0) & (ids < e)
+    ok = np.where(valid, ids, 0).astype(np.int32)
+    w_eff = np.where(valid, rw, np.float16(0))
+    ref = o.moe_stage(W, S, ok, w_eff, x, topk * k, k, n, k, epi_silu=False)
+    assert_within(host(yc), ref, "token-wise combine")
+
+
+@pytest.mark.parametrize("t,topk,n,k", [(2, 4, 84, 1024), (1, 8, 1536, 2048), (4, 8, 40, 96),
+                                        (3, 5, 18, 32)])
+def test_moe_silu_few_pairs_shared_activation(o, q4, t, topk, n, k):
+    """The SiLU-multiply stage at few pairs with every slot reading its token's
+    one activation row (slot stride 0): gate rows not a multiple of the row
+    block, an expert repeated within a token, an out-of-range id (zeros)
+    against the oracle."""
+    e = 7
+    W, S = experts(o, 1900 + n + k, e, n, k)
+    rng = np.random.default_rng(1901 + t * topk)
+    ids = rng.integers(0, e, size=(t, topk)).astype(np.int32)
+    ids[0, 1] = ids[0, topk - 1]
+    ids[t - 1, 0] = e + 1
+    x = datagen.activations(1902 + n, t, k)
+    ys = q4.moe_gemv(dev_tensor(W), dev_tensor(S), dev_tensor(ids), dev_tensor(x), ldx=k,
+                     x_slot_stride=0, epi_silu=True)
+    sync()
+    valid = (ids >= 0) & (ids < e)
+    ok = np.where(valid, ids, 0).astype(np.int32)
+    ref = o.moe_stage(W, S, ok, None, x, k, 0, n, k, epi_silu=True)
+    ys = host(ys)
+    assert np.all(ys[~valid] == 0)
+    assert_within(ys[valid], ref[valid], "SiLU-multiply, shared activation")
