@@ -5,10 +5,12 @@
 // and "Subgroup-matrix GEMM graduated"): Y[m][n] = f16( sum_k (q[n][k] - 7) *
 // s[n][k/32] * X[m][k] ), f32 accumulation, for any number M of activation
 // rows. The decode kernels stream the weights once for at most 16 rows; here
-// each weight tile is dequantised once per 64 rows:
-//  * workgroup tile: 64 activation rows x 128 weight rows; wave w owns weight
-//    rows [32 w, 32 w + 32) of the tile (two 16-row matrix-core tiles) and all
-//    four 16-row activation tiles, so each dequantised weight feeds four MFMAs;
+// each weight tile is dequantised once per 64 or 128 rows:
+//  * workgroup tile: 64 activation rows x 128 weight rows (four waves, three
+//    workgroups per CU) or 128 x 256 (eight waves, one per CU, two steps of
+//    loads in flight); wave w owns weight rows [32 w, 32 w + 32) of the tile
+//    (two 16-row matrix-core tiles) and all 16-row activation tiles, so each
+//    dequantised weight feeds four or eight MFMAs;
 //  * exact weights: the codes q - 7 (exact in binary16) enter the matrix
 //    core, one MFMA per 32-value group gives the group's f32 sum over the
 //    tile, and each lane (its output column is its weight row) adds s times
@@ -34,6 +36,7 @@
 // of the same matrix product: A = xs split into binary16 hi and lo halves (a
 // small kernel forms them), B = the binary16 biases.
 #include <algorithm>
+#include <type_traits>
 
 #include "q4_dequant.h"
 
@@ -45,7 +48,7 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBN = 128;               // weight rows per workgroup (32 per wave)
+constexpr int kBNMax = 256;            // weight rows per workgroup: 32 per wave, up to 8 waves
 constexpr int kStepK = 128;            // K values per step (four groups)
 constexpr int kAStride = kStepK + 8;   // staged row in halves (16 bytes of padding)
 constexpr int kXcds = 8;
@@ -138,24 +141,25 @@ constexpr uint32_t kOut = 0x80000000u;  // an offset beyond every buffer: loads 
 
 // A thread's byte offsets at step 0, the same at every step but for the
 // step's own scalar offset: its lane's word group and scale of the wave's two
-// weight rows, and MS 16-byte pieces of the activation tile (piece q: row
-// (t + 256 q) / 16, eight values (t % 16) of the step). Rows past N or M read 0.
-template <int MS>
+// weight rows, and XP 16-byte pieces of the activation tile (piece q: row
+// (t + NT q) / 16, eight values (t % 16) of the step, NT threads per
+// workgroup). Rows past N or M read 0.
+template <int XP>
 struct Offsets {
-    uint32_t w[2], s[2], x[MS];
+    uint32_t w[2], s[2], x[XP];
 };
 
 // One step's loaded data of a thread.
-template <int MS>
+template <int XP>
 struct StepLoads {
     u32x4 w[2];
     uint32_t s[2];
-    u32x4 x[MS];
+    u32x4 x[XP];
 };
 
 // (AFF: a step spans two 64-code groups, so its scales are 4 bytes on)
-template <int MS, bool AFF>
-__device__ __forceinline__ void load_step(StepLoads<MS> &L, const Bufs &B, const Offsets<MS> &O,
+template <int XP, bool AFF>
+__device__ __forceinline__ void load_step(StepLoads<XP> &L, const Bufs &B, const Offsets<XP> &O,
                                           int st)
 {
 #pragma unroll
@@ -164,7 +168,7 @@ __device__ __forceinline__ void load_step(StepLoads<MS> &L, const Bufs &B, const
         L.s[ns] = __builtin_amdgcn_raw_buffer_load_b16(B.s, O.s[ns], st * (AFF ? 4 : 8), 0);
     }
 #pragma unroll
-    for (int q = 0; q < MS; ++q)
+    for (int q = 0; q < XP; ++q)
         L.x[q] = __builtin_amdgcn_raw_buffer_load_b128(B.x, O.x[q], st * 256, 0);
 }
 
@@ -176,8 +180,8 @@ struct StepWeights {
     half2v s2[2][4];
 };
 
-template <int MS, bool LAST>
-__device__ __forceinline__ void prepare(StepWeights &P, const StepLoads<MS> &L, int gs, int kb,
+template <int XP, bool LAST>
+__device__ __forceinline__ void prepare(StepWeights &P, const StepLoads<XP> &L, int gs, int kb,
                                         int G)
 {
 #pragma unroll
@@ -200,12 +204,12 @@ __device__ __forceinline__ void prepare(StepWeights &P, const StepLoads<MS> &L, 
 
 // Stores a step's activation pieces into an LDS buffer in pair order. LAST:
 // values past K are zero.
-template <int MS, bool LAST>
-__device__ __forceinline__ void stage(_Float16 *buf, const StepLoads<MS> &L, int gs, int G, int t)
+template <int XP, bool LAST, int NT>
+__device__ __forceinline__ void stage(_Float16 *buf, const StepLoads<XP> &L, int gs, int G, int t)
 {
 #pragma unroll
-    for (int q = 0; q < MS; ++q) {
-        const int c = t + 256 * q;
+    for (int q = 0; q < XP; ++q) {
+        const int c = t + NT * q;
         u32x4 v = pair_order(L.x[q]);
         if (LAST && gs * 32 + 8 * (c & 15) >= G * 32)
             v = u32x4{0u, 0u, 0u, 0u};
@@ -279,7 +283,7 @@ __device__ __forceinline__ void multiply(floatx4 (&acc)[MS][2], const _Float16 *
 // on either side). The caller has passed the last barrier of the main loop.
 // Bias steps [b0, b1); bvec: the bias rows allow 16-byte loads (G64 % 8 == 0,
 // Bias 16-byte aligned).
-template <int MS>
+template <int MS, int XP, int NT>
 __device__ __forceinline__ void bias_steps(floatx4 (&acc)[MS][2], _Float16 *buf,
                                            const uint16_t *__restrict__ XS, int M, int m0,
                                            const uint16_t *__restrict__ Bias, int N, int n0,
@@ -292,8 +296,8 @@ __device__ __forceinline__ void bias_steps(floatx4 (&acc)[MS][2], _Float16 *buf,
     for (int bs = b0; bs < b1; ++bs) {
         __syncthreads();  // the buffer's previous contents are no longer read
 #pragma unroll
-        for (int q = 0; q < MS; ++q) {
-            const int c = t + 256 * q, row = m0 + (c >> 4);
+        for (int q = 0; q < XP; ++q) {
+            const int c = t + NT * q, row = m0 + (c >> 4);
             const uint32_t off = row < M ? (uint32_t)((row * ld + 128 * bs + 8 * (c & 15)) * 2) : kOut;
             *reinterpret_cast<u32x4 *>(buf + (c >> 4) * kAStride + 8 * (c & 15)) =
                 __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
@@ -360,37 +364,41 @@ __global__ __launch_bounds__(256) void k_group_sums(const uint16_t *__restrict__
     }
 }
 
-// Grid: one workgroup per (16 MS-row activation tile, 128-row weight tile),
-// 256 threads; wave w owns weight rows [32 w, 32 w + 32) of the tile and all
-// MS 16-row activation tiles. Buffer sizes below 2^31 bytes (the launcher
-// splits larger problems).
+// Grid: one workgroup per (16 MS-row activation tile, 32 NW-row weight tile),
+// NW waves; wave w owns weight rows [32 w, 32 w + 32) of the tile and all MS
+// 16-row activation tiles. A thread stages XP pieces of the step's activation
+// tile. Eight waves share each staged tile between twice the weight rows and
+// keep two steps of loads in flight (register buffers used in turn); four
+// waves keep one. Buffer sizes below 2^31 bytes (the launcher splits larger
+// problems).
 // AFF: the affine format; S and Bias [N][G / 2]; XS the group sums of X
 // (k_group_sums, GP groups per half).
-template <int MS, int MODE, bool AFF>
-__global__ __launch_bounds__(256, MS == 8 ? 2 : 3) void k_gemm_q4(
+template <int MS, int MODE, bool AFF, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (MS == 8 ? 2 : 3)) void k_gemm_q4(
     const uint4 *__restrict__ W, const uint16_t *__restrict__ S, const uint16_t *__restrict__ X,
     int64_t ldx, uint16_t *__restrict__ Y, int64_t ldy, float *__restrict__ part, int M, int N,
     int G, int sps, const uint16_t *__restrict__ Bias, const uint16_t *__restrict__ XS, int GP,
     int bvec)
 {
-    constexpr int BM = 16 * MS;
+    constexpr int BM = 16 * MS, BN = 32 * NW, NT = 64 * NW, XP = 4 * MS / NW;
+    constexpr int D = NW == 8 ? 2 : 1;  // steps of loads in flight
     __shared__ _Float16 xs[2][BM * kAStride];
     const int t = threadIdx.x, l = t & 63, wave = t >> 6;
     const int n = l & 15, kb = l >> 4;
 
     // XCD-aware tile order: workgroup b runs on XCD b % 8; XCD x takes the
     // contiguous tile range [start(x), start(x) + count(x)), activation tile fastest
-    const int mtiles = (M + BM - 1) / BM, ntiles = (N + kBN - 1) / kBN;
+    const int mtiles = (M + BM - 1) / BM, ntiles = (N + BN - 1) / BN;
     const int total = mtiles * ntiles, per = total / kXcds, rem = total % kXcds;
     const int b = blockIdx.x, x = b % kXcds;
     const int r = x * per + min(x, rem) + b / kXcds;
-    const int m0 = (r % mtiles) * BM, n0 = (r / mtiles) * kBN + 32 * wave;
+    const int m0 = (r % mtiles) * BM, n0 = (r / mtiles) * BN + 32 * wave;
 
     Bufs B;
     B.w = rsrc(W, (uint32_t)N * (uint32_t)G * 16u);
     B.s = rsrc(S, (uint32_t)N * (uint32_t)(AFF ? G / 2 : G) * 2u);
     B.x = rsrc(X, (uint32_t)(((int64_t)(M - 1) * ldx + G * 32) * 2));
-    Offsets<MS> O;
+    Offsets<XP> O;
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns) {
         const int row = n0 + 16 * ns + n;
@@ -398,8 +406,8 @@ __global__ __launch_bounds__(256, MS == 8 ? 2 : 3) void k_gemm_q4(
         O.s[ns] = row < N ? (uint32_t)(AFF ? row * (G / 2) + kb / 2 : row * G + kb) * 2u : kOut;
     }
 #pragma unroll
-    for (int q = 0; q < MS; ++q) {
-        const int c = t + 256 * q, row = m0 + (c >> 4);
+    for (int q = 0; q < XP; ++q) {
+        const int c = t + NT * q, row = m0 + (c >> 4);
         O.x[q] = row < M ? (uint32_t)((row * ldx + 8 * (c & 15)) * 2) : kOut;
     }
 
@@ -417,28 +425,51 @@ __global__ __launch_bounds__(256, MS == 8 ? 2 : 3) void k_gemm_q4(
     const int total_steps = steps + (AFF ? GP / 64 : 0);
     const int st0 = z * sps, st1 = min(steps, st0 + sps);
     const int bs1 = min(total_steps, st0 + sps);
-    StepLoads<MS> L;
+    StepLoads<XP> L[D];
     StepWeights P;
-    if (st0 < st1) {
-    load_step<MS, AFF>(L, B, O, st0);
-    for (int st = st0; st < st1 - 1; ++st) {
-        stage<MS, false>(xs[st & 1], L, 4 * st, G, t);
-        prepare<MS, false>(P, L, 4 * st, kb, G);
-        load_step<MS, AFF>(L, B, O, st + 1);
-        __syncthreads();  // the tile is staged; the other buffer was last read before this
-        multiply<MS, MODE, AFF>(acc, xs[st & 1], P, n, kb);
-    }
-    {
-        const int st = st1 - 1;  // groups past K only in the last step of the last split
-        stage<MS, true>(xs[st & 1], L, 4 * st, G, t);
-        prepare<MS, true>(P, L, 4 * st, kb, G);
+    // one step from register buffer Lr: stage its activation tile into LDS
+    // buffer st & 1 and its weights into P, refill Lr with step `next` (LOAD;
+    // the loads stay in flight D steps), then multiply once the tile is
+    // staged. The LDS buffer was last read two steps before, ahead of the
+    // previous step's barrier. LAST: groups past K (only the last step of the
+    // last split). A refill past the split's last step re-reads that step
+    // (unconditional loads keep the two buffers' registers apart).
+    auto body = [&](StepLoads<XP> &Lr, int st, int next, auto last, auto load)
+                    __attribute__((always_inline)) {
+        stage<XP, decltype(last)::value, NT>(xs[st & 1], Lr, 4 * st, G, t);
+        prepare<XP, decltype(last)::value>(P, Lr, 4 * st, kb, G);
+        if constexpr (decltype(load)::value)
+            load_step<XP, AFF>(Lr, B, O, next);
         __syncthreads();
         multiply<MS, MODE, AFF>(acc, xs[st & 1], P, n, kb);
-    }
+    };
+    const std::false_type no;
+    const std::true_type yes;
+    if (st0 < st1) {
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            load_step<XP, AFF>(L[d], B, O, min(st0 + d, st1 - 1));
+        if constexpr (D == 1) {
+            for (int st = st0; st < st1 - 1; ++st)
+                body(L[0], st, st + 1, no, yes);
+            body(L[0], st1 - 1, 0, yes, no);
+        } else {
+            int st = st0;
+            for (; st + 2 < st1; st += 2) {
+                body(L[0], st, st + 2, no, yes);
+                body(L[1], st + 1, min(st + 3, st1 - 1), no, yes);
+            }
+            if (st + 1 < st1) {
+                body(L[0], st, 0, no, no);
+                body(L[1], st + 1, 0, yes, no);
+            } else {
+                body(L[0], st, 0, yes, no);
+            }
+        }
     }
     if (AFF && bs1 > steps)  // this split's share of the bias steps
-        bias_steps<MS>(acc, xs[0], XS, M, m0, Bias, N, n0, G / 2, GP, max(st0, steps) - steps,
-                       bs1 - steps, bvec != 0, t, n, kb);
+        bias_steps<MS, XP, NT>(acc, xs[0], XS, M, m0, Bias, N, n0, G / 2, GP,
+                               max(st0, steps) - steps, bs1 - steps, bvec != 0, t, n, kb);
 
     // lane (n, kb) holds D[4 kb + i][n] of each (activation, weight) tile:
     // rounded to Y, or with several K splits the f32 partial part[z][row][col]
@@ -499,26 +530,30 @@ __global__ __launch_bounds__(256) void k_gemm_combine(const float *__restrict__ 
     }
 }
 
-// Launch shape of one chunk: activation rows per workgroup (16 MS) and the
-// number of K splits. 128-row tiles run two workgroups per CU, 64-row tiles
-// three at about 0.74 of the time per tile; the shape with fewer estimated
-// tile-rounds wins. A grid that fills fewer than half the workgroup slots
+// Launch shape of one chunk: activation rows per workgroup (16 MS), waves per
+// workgroup (NW, 32 weight rows each) and the number of K splits. 128 x 256
+// tiles (eight waves) run one workgroup per CU, 64 x 128 tiles (four waves)
+// three at about kRound4 of the time per 128 x 256 tile; the shape with fewer
+// estimated rounds wins. A grid that fills fewer than half the workgroup slots
 // splits K (at least four steps per split, at most kMaxSplits) into f32
 // partials that k_gemm_combine sums in split order.
 struct GemmShape {
-    int ms, splits, sps;
+    int ms, nw, splits, sps;
 };
+constexpr double kRound4 = 0.72;  // measured: Phi-3 gate_up at M = 1024, exact weights
 
 // (extra: steps after the weight steps, the affine bias steps)
 GemmShape gemm_shape(int M, int N, int G, size_t max_part_bytes, int extra = 0)
 {
-    const int cus = cu_count(), nt = (N + kBN - 1) / kBN, steps = (G + 3) / 4 + extra;
-    const int64_t t8 = (int64_t)((M + 127) / 128) * nt, t4 = (int64_t)((M + 63) / 64) * nt;
-    const double r8 = (double)((t8 + 2 * cus - 1) / (2 * cus));
-    const double r4 = 0.74 * (double)((t4 + 3 * cus - 1) / (3 * cus));
+    const int cus = cu_count(), steps = (G + 3) / 4 + extra;
+    const int64_t t8 = (int64_t)((M + 127) / 128) * ((N + 255) / 256);
+    const int64_t t4 = (int64_t)((M + 63) / 64) * ((N + 127) / 128);
+    const double r8 = (double)((t8 + cus - 1) / cus);
+    const double r4 = kRound4 * (double)((t4 + 3 * cus - 1) / (3 * cus));
     GemmShape g;
     g.ms = r4 < r8 ? 4 : 8;
-    const int64_t tiles = g.ms == 4 ? t4 : t8, slots = (g.ms == 4 ? 3 : 2) * (int64_t)cus;
+    g.nw = g.ms == 4 ? 4 : 8;
+    const int64_t tiles = g.ms == 4 ? t4 : t8, slots = (g.ms == 4 ? 3 : 1) * (int64_t)cus;
     int ks = 1;
     if (2 * tiles <= slots) {
         ks = (int)std::min<int64_t>({(slots + tiles - 1) / tiles, std::max(1, steps / 4), kMaxSplits});
@@ -530,7 +565,7 @@ GemmShape gemm_shape(int M, int N, int G, size_t max_part_bytes, int extra = 0)
     return g;
 }
 
-template <int MS>
+template <int MS, int NW>
 q4_status launch_tiles(bool exact, dim3 grid, hipStream_t stream, const uint4 *w, const uint16_t *s,
                        const uint16_t *x, int64_t ldx, uint16_t *y, int64_t ldy, float *part,
                        int M, int N, int G, int sps, const uint16_t *bias, const uint16_t *xsum,
@@ -538,13 +573,13 @@ q4_status launch_tiles(bool exact, dim3 grid, hipStream_t stream, const uint4 *w
 {
     const int bvec = bias && (G / 2) % 8 == 0 && reinterpret_cast<uintptr_t>(bias) % 16 == 0;
     if (bias)
-        Q4_LAUNCH_MATVEC((k_gemm_q4<MS, kWGroup, true>), grid, dim3(256), 0, stream, w, s, x, ldx,
+        Q4_LAUNCH_MATVEC((k_gemm_q4<MS, kWGroup, true, NW>), grid, dim3(64 * NW), 0, stream, w, s, x, ldx,
                          y, ldy, part, M, N, G, sps, bias, xsum, gp, bvec);
     else if (exact)
-        Q4_LAUNCH_MATVEC((k_gemm_q4<MS, kWGroup, false>), grid, dim3(256), 0, stream, w, s, x, ldx,
+        Q4_LAUNCH_MATVEC((k_gemm_q4<MS, kWGroup, false, NW>), grid, dim3(64 * NW), 0, stream, w, s, x, ldx,
                          y, ldy, part, M, N, G, sps, nullptr, nullptr, 0, 0);
     else
-        Q4_LAUNCH_MATVEC((k_gemm_q4<MS, kWF16, false>), grid, dim3(256), 0, stream, w, s, x, ldx,
+        Q4_LAUNCH_MATVEC((k_gemm_q4<MS, kWF16, false, NW>), grid, dim3(64 * NW), 0, stream, w, s, x, ldx,
                          y, ldy, part, M, N, G, sps, nullptr, nullptr, 0, 0);
     return check_launch("k_gemm_q4");
 }
@@ -562,7 +597,7 @@ struct GemmChunks {
     GemmChunks(int K, int64_t ldx)
     {
         const int64_t wrow_bytes = (int64_t)(K / 32) * 16;
-        nchunk = (int)std::max<int64_t>(kBN, ((int64_t(1) << 31) / wrow_bytes) / kBN * kBN);
+        nchunk = (int)std::max<int64_t>(kBNMax, ((int64_t(1) << 31) / wrow_bytes) / kBNMax * kBNMax);
         mchunk = (int)std::max<int64_t>(
             128, ((int64_t(1) << 31) / (2 * std::max<int64_t>(ldx, 1)) - 1) / 128 * 128);
     }
@@ -607,8 +642,8 @@ q4_status launch_gemm(const uint32_t *W, const uint16_t *S, const uint16_t *X, i
         for (int m0 = 0; m0 < M; m0 += mchunk) {
             const int nn = std::min(nchunk, N - n0), mm = std::min(mchunk, M - m0);
             const GemmShape g = gemm_shape(mm, nn, G, kMaxPart, bias ? GP / 64 : 0);
-            const int BM = 16 * g.ms;
-            const int64_t tiles = (int64_t)((mm + BM - 1) / BM) * ((nn + kBN - 1) / kBN);
+            const int BM = 16 * g.ms, BN = 32 * g.nw;
+            const int64_t tiles = (int64_t)((mm + BM - 1) / BM) * ((nn + BN - 1) / BN);
             const dim3 grid((unsigned)tiles, (unsigned)g.splits);
             const uint4 *w = reinterpret_cast<const uint4 *>(W) + (size_t)n0 * G;
             const uint16_t *s = S + (size_t)n0 * sg, *x = X + (size_t)m0 * ldx;
@@ -636,10 +671,10 @@ q4_status launch_gemm(const uint32_t *W, const uint16_t *S, const uint16_t *X, i
             }
             const uint16_t *bz = bias ? bias + (size_t)n0 * G64 : nullptr;
             q4_status st = g.ms == 4
-                               ? launch_tiles<4>(exact, grid, stream, w, s, x, ldx, y, ldy, part,
-                                                 mm, nn, G, g.sps, bz, xsum, GP)
-                               : launch_tiles<8>(exact, grid, stream, w, s, x, ldx, y, ldy, part,
-                                                 mm, nn, G, g.sps, bz, xsum, GP);
+                               ? launch_tiles<4, 4>(exact, grid, stream, w, s, x, ldx, y, ldy, part,
+                                                    mm, nn, G, g.sps, bz, xsum, GP)
+                               : launch_tiles<8, 8>(exact, grid, stream, w, s, x, ldx, y, ldy, part,
+                                                    mm, nn, G, g.sps, bz, xsum, GP);
             if (st != Q4_OK)
                 return st;
             if (g.splits > 1) {
