@@ -229,11 +229,16 @@ __device__ __forceinline__ void multiply(floatx4 (&acc)[MS][2], const _Float16 *
                                          const StepWeights &P, int n, int kb)
 {
     if constexpr (MODE == kWGroup) {
+        // each group sum is scaled into its accumulator after the next MFMA
+        // has been issued (read right after its own MFMA, it would wait out
+        // the MFMA's latency)
         const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+        floatx4 prev = zero;
+        float sprev = 0.f;
+        int pm = 0, pn = 0;
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
             half8 a[MS], bq[2];
-            __builtin_amdgcn_iglp_opt(1);  // interleave the matrix-core and LDS work
 #pragma unroll
             for (int ms = 0; ms < MS; ++ms)
                 a[ms] = *reinterpret_cast<const half8 *>(cur + (16 * ms + n) * kAStride + 8 * kb +
@@ -247,12 +252,19 @@ __device__ __forceinline__ void multiply(floatx4 (&acc)[MS][2], const _Float16 *
                 for (int ns = 0; ns < 2; ++ns) {
                     const floatx4 gsum =
                         __builtin_amdgcn_mfma_f32_16x16x32_f16(a[ms], bq[ns], zero, 0, 0, 0);
-                    const float s = (float)P.s2[ns][tt][0];
+                    if (tt > 0 || ms > 0 || ns > 0)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        acc[ms][ns][i] = fmaf(s, gsum[i], acc[ms][ns][i]);
+                        for (int i = 0; i < 4; ++i)
+                            acc[pm][pn][i] = fmaf(sprev, prev[i], acc[pm][pn][i]);
+                    prev = gsum;
+                    sprev = (float)P.s2[ns][tt][0];
+                    pm = ms;
+                    pn = ns;
                 }
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc[pm][pn][i] = fmaf(sprev, prev[i], acc[pm][pn][i]);
         return;
     }
     // kWF16 (symmetric codes only)
