@@ -216,8 +216,11 @@ q4_status launch_gemm(const uint32_t *W, const uint16_t *S, const uint16_t *X, i
                       uint16_t *Y, int64_t ldy, int N, int K, int M, bool exact,
                       hipStream_t stream, const uint16_t *bias = nullptr);
 // M = 2..4 activation rows with the single-row kernel's arithmetic per row
-// (bit-identical to M single-row matvecs) when M * K <= 24576 (staging in LDS).
-bool gemv_rows_fits(int M, int K);
+// (bit-identical to M single-row matvecs) when M * K <= 24576 (staging in LDS);
+// given the symmetric format's N, not for M >= 3 on LM-head-sized matrices
+// (N K >= 2^26) that the matrix-core kernel takes (its time does not grow with
+// M: the Qwen3-4B LM head at M = 4 measured 53 against 72 us).
+bool gemv_rows_fits(int M, int K, int64_t N = 0);
 // (yf set: f32 outputs there, y ignored)
 q4_status launch_gemv_rows(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
                            uint16_t *y, int64_t ldy, int N, int K, int M, hipStream_t stream,

@@ -1124,7 +1124,12 @@ q4_status launch_gemv(const uint32_t *W, const uint16_t *S, const uint16_t *x, u
 
 // Batched matvec: M = 1 is the matvec above; M >= 2 rows share each weight
 // read on the matrix cores (q4_mfma.hip).
-bool gemv_rows_fits(int M, int K) { return M >= 2 && M <= kMaxRowsDot && M * K <= 24576; }
+bool gemv_rows_fits(int M, int K, int64_t N)
+{
+    if (M < 2 || M > kMaxRowsDot || M * K > 24576)
+        return false;
+    return !(M >= 3 && N * K >= (int64_t(1) << 26) && mma_fits((int)N, K, M));
+}
 
 q4_status launch_gemv_rows(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
                            uint16_t *y, int64_t ldy, int N, int K, int M, hipStream_t stream,
@@ -1154,7 +1159,7 @@ q4_status launch_gemv_batched(const uint32_t *W, const uint16_t *S, const uint16
 {
     if (M == 1)  // a single row is the bandwidth-bound matvec
         return launch_gemv(W, S, x, y, N, K, EpiArgs{}, stream);
-    if (gemv_rows_fits(M, K))  // a few rows: the single-row kernel's arithmetic per row
+    if (gemv_rows_fits(M, K, N))  // a few rows: the single-row kernel's arithmetic per row
         return launch_gemv_rows(W, S, x, ldx, y, ldy, N, K, M, stream);
     return launch_gemv_mfma(W, S, x, ldx, y, nullptr, ldy, N, K, M, stream);
 }

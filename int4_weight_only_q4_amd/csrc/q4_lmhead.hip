@@ -173,7 +173,7 @@ q4_status launch_gemv_f32(const uint32_t *W, const uint16_t *S, const uint16_t *
         op.yf = y;
         return launch_gemv_op(op, stream);
     }
-    if (gemv_rows_fits(M, K))  // a few rows: the single-row arithmetic per row
+    if (gemv_rows_fits(M, K, N))  // a few rows: the single-row arithmetic per row
         return launch_gemv_rows(W, S, x, ldx, nullptr, ldy, N, K, M, stream, nullptr, y);
     return launch_gemv_mfma(W, S, x, ldx, nullptr, y, ldy, N, K, M, stream);
 }
@@ -213,7 +213,7 @@ size_t lm_head_cand_bytes(int N, int K, int M)
 
 size_t ws_lm_head(int N, int K, int M)
 {
-    if (M > 1 && (gemv_rows_fits(M, K) || mma_fits(N, K, M)))
+    if (M > 1 && (gemv_rows_fits(M, K, N) || mma_fits(N, K, M)))
         return ws_argmax(N, M);
     if (M > 1)
         return kWsHeader + lm_head_cand_bytes(N, K, M) + mfma_part_bytes(N, K);
@@ -241,7 +241,7 @@ q4_status launch_lm_head_argmax(const uint32_t *W, const uint16_t *S, const uint
                                 int64_t ldx, float *logits, int64_t ldl, int32_t *tokens, int N,
                                 int K, int M, hipStream_t stream)
 {
-    if (M > 1 && (gemv_rows_fits(M, K) || mma_fits(N, K, M))) {
+    if (M > 1 && (gemv_rows_fits(M, K, N) || mma_fits(N, K, M))) {
         // the f32 logits without a workspace (a few rows: M single-row
         // matvecs; more: the workgroup-reduced matrix-core kernel), then the
         // argmax

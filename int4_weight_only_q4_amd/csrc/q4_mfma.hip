@@ -892,7 +892,7 @@ q4_status launch_gemv_mma(const uint32_t *W, const uint16_t *S, const uint16_t *
 
 size_t ws_rows(int N, int K, int M)
 {
-    if (M <= 1 || gemv_rows_fits(M, K) || mma_fits(N, K, M) || mfma_splits(K) <= 1)
+    if (M <= 1 || gemv_rows_fits(M, K, N) || mma_fits(N, K, M) || mfma_splits(K) <= 1)
         return 0;  // single-row, few-row and workgroup-reduced kernels, or no K split
     return kWsHeader + mfma_part_bytes(N, K);
 }

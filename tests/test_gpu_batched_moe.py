@@ -56,6 +56,10 @@ BATCHED = [
     ("mma_four_tiles_tail_m6", 32800, 256, 6),
     ("mma_m16", 3000, 2048, 16),
     ("mma_m17", 500, 1024, 17),
+    # LM-head-sized matrices (N K >= 2^26) at M = 3 and 4 take the matrix
+    # cores instead of the few-row kernel
+    ("lm_sized_m3", 32768, 2048, 3),
+    ("lm_sized_m4", 33000, 2080, 4),
 ]
 
 

@@ -208,10 +208,11 @@ def test_lm_head_argmax_qwen3_tied_m8_sampled(o, q4):
         check_token(int(tk[b]), lg[b], ref, "row %d" % b)
 
 
-@pytest.mark.parametrize("n,k,m", [(32064, 3072, 3), (151936, 2560, 2), (1001, 96, 4)])
+@pytest.mark.parametrize("n,k,m", [(20000, 3072, 3), (151936, 2560, 2), (1001, 96, 4)])
 def test_lm_head_few_rows_equal_single_rows(o, q4, n, k, m):
-    """M = 2..4 runs the single-row arithmetic per row: each row's f32 logits and
-    token equal those of the M = 1 LM head on that row, bit for bit."""
+    """M = 2..4 runs the single-row arithmetic per row (up to N K < 2^26 at M = 3
+    and 4): each row's f32 logits and token equal those of the M = 1 LM head on
+    that row, bit for bit."""
     W, S, X = make(o, "few_rows_%d" % n, n, k, m)
     Wd, Sd = dev_tensor(W), dev_tensor(S)
     logits, tok = q4.lm_head_argmax(Wd, Sd, dev_tensor(X))
@@ -221,6 +222,21 @@ def test_lm_head_few_rows_equal_single_rows(o, q4, n, k, m):
     for i in range(m):
         assert np.array_equal(lg[i].view(np.uint32), host(singles[i][0]).view(np.uint32)), i
         assert int(tk[i]) == int(host(singles[i][1])[0]), i
+
+
+@pytest.mark.parametrize("m", [3, 4])
+def test_lm_head_phi3_few_rows_matrix_cores(o, q4, m):
+    """The Phi-3 LM head (N K >= 2^26) at M = 3 and 4 runs on the matrix cores:
+    every logit of each row against the oracle, and each token."""
+    n, k = 32064, 3072
+    W, S, X = make(o, "phi3_lm_head_m%d" % m, n, k, m)
+    logits, tok = q4.lm_head_argmax(dev_tensor(W), dev_tensor(S), dev_tensor(X))
+    sync()
+    lg, tk = host(logits), host(tok).astype(np.int64)
+    ref, _ = o.lm_head(W, S, X)
+    for b in range(m):
+        assert_within(lg[b], ref[b], "row %d" % b)
+        check_token(int(tk[b]), lg[b], ref[b], "row %d" % b)
 
 
 def test_lm_head_planted_maximum(o, q4):
@@ -235,7 +251,7 @@ def test_lm_head_planted_maximum(o, q4):
         S = datagen.scales(601, n, k)
         S[r1] = S[r0]
         x = np.abs(datagen.activations(602, 1, k)[0]).astype(np.float16)
-        for m in (1, 2, 8):
+        for m in (1, 2, 4, 8):
             X = np.stack([x] * m)
             logits, tok = q4.lm_head_argmax(dev_tensor(W), dev_tensor(S),
                                             dev_tensor(X if m > 1 else x))
