@@ -707,15 +707,26 @@ def write_gemv_table(rows):
             "us/kernel, except for the rows that run several kernels per call (the LM head + "
             "argmax: 2 kernels at M = 1, 4 at M = 8; attention: 1 or 2; the MoE layer: 3 to "
             "5), where it is bytes / us/call (attention: the K and V bytes read). For those "
-            "rows us/kernel is the first matvec kernel alone.",
+            "rows us/kernel is the first matvec kernel alone. `oracle us` is the plain C "
+            "oracle (binary64) on the same matmul or MoE layer on the host of the same run: "
+            "one thread, then all host threads (the oracle single-threaded per part); "
+            "empty where it was not run.",
             "",
-            "| workload | shape | M | weight bytes | us/kernel | us/call | GB/s | % of 8 TB/s | note |",
-            "|---|---|---|---|---|---|---|---|---|"]
+            "Context only (other hardware, a whole decode step with attention and the LM "
+            "head): %s, %s: Zero TVM %.2f tok/s, WebLLM 0.2.80 %.2f tok/s." % (
+                BROWSER_CONTEXT["what"].split(" (")[0], BROWSER_CONTEXT["hardware"],
+                BROWSER_CONTEXT["zero_tvm_tok_s"], BROWSER_CONTEXT["webllm_0_2_80_tok_s"]),
+            "",
+            "| workload | shape | M | weight bytes | us/kernel | us/call | GB/s | % of 8 TB/s "
+            "| oracle us, 1 thread | oracle us, all threads | note |",
+            "|---|---|---|---|---|---|---|---|---|---|---|"]
+    fmt = lambda v: "%.1f" % v if v is not None else ""
     for r in rows:
-        text.append("| %s | %s | %d | %d | %s | %.3f | %.1f | %.1f | %s |" % (
+        text.append("| %s | %s | %d | %d | %s | %.3f | %.1f | %.1f | %s | %s | %s |" % (
             r["workload"], r["shape"], r["m"], r["weight_bytes"],
             "%.3f" % r["us_kernel"] if r["us_kernel"] is not None else "",
-            r["us_per_call"], r["gbs"], r["pct_peak"], r["note"]))
+            r["us_per_call"], r["gbs"], r["pct_peak"], fmt(r.get("oracle_us_1t")),
+            fmt(r.get("oracle_us_all")), r["note"]))
     text.append("")
     with open(GEMV_TABLE_PROFILE, "w") as fh:
         fh.write("\n".join(text))
