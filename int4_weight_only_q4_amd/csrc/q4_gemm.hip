@@ -150,22 +150,31 @@ struct Offsets {
 };
 
 // One step's loaded data of a thread.
-template <int XP>
+template <int XP, bool S4>
 struct StepLoads {
     u32x4 w[2];
-    uint32_t s[2];
+    uint32_t s[2][S4 ? 2 : 1];
     u32x4 x[XP];
 };
 
-// (AFF: a step spans two 64-code groups, so its scales are 4 bytes on)
-template <int XP, bool AFF>
-__device__ __forceinline__ void load_step(StepLoads<XP> &L, const Bufs &B, const Offsets<XP> &O,
-                                          int st)
+// (AFF: a step spans two 64-code groups, so its scales are 4 bytes on.) S4
+// (symmetric format, G % 4 == 0): each lane loads the four scales of the
+// step's groups of its row in one 8-byte load (the same bytes the lane row
+// loads two at a time otherwise), so no exchange across lane rows is needed.
+template <int XP, bool AFF, bool S4>
+__device__ __forceinline__ void load_step(StepLoads<XP, S4> &L, const Bufs &B,
+                                          const Offsets<XP> &O, int st)
 {
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns) {
         L.w[ns] = __builtin_amdgcn_raw_buffer_load_b128(B.w, O.w[ns], st * 64, 0);
-        L.s[ns] = __builtin_amdgcn_raw_buffer_load_b16(B.s, O.s[ns], st * (AFF ? 4 : 8), 0);
+        if (S4) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(B.s, O.s[ns], st * 8, 0);
+            L.s[ns][0] = v[0];
+            L.s[ns][S4 ? 1 : 0] = v[1];
+        } else {
+            L.s[ns][0] = __builtin_amdgcn_raw_buffer_load_b16(B.s, O.s[ns], st * (AFF ? 4 : 8), 0);
+        }
     }
 #pragma unroll
     for (int q = 0; q < XP; ++q)
@@ -180,9 +189,9 @@ struct StepWeights {
     half2v s2[2][4];
 };
 
-template <int XP, bool LAST>
-__device__ __forceinline__ void prepare(StepWeights &P, const StepLoads<XP> &L, int gs, int kb,
-                                        int G)
+template <int XP, bool LAST, bool S4>
+__device__ __forceinline__ void prepare(StepWeights &P, const StepLoads<XP, S4> &L, int gs,
+                                        int kb, int G)
 {
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns) {
@@ -191,11 +200,19 @@ __device__ __forceinline__ void prepare(StepWeights &P, const StepLoads<XP> &L, 
         P.wt[ns][2] = L.w[ns].z;
         P.wt[ns][3] = L.w[ns].w;
         transpose_rows(P.wt[ns]);
-        uint32_t s = L.s[ns];
-        if (LAST && gs + kb >= G)
-            s = 0;
         uint32_t sc[4];
-        broadcast_rows(s, sc);
+        if (S4) {
+            // (G % 4 == 0: a step never reaches past K)
+            sc[0] = L.s[ns][0] & 0xFFFFu;
+            sc[1] = L.s[ns][0] >> 16;
+            sc[2] = L.s[ns][S4 ? 1 : 0] & 0xFFFFu;
+            sc[3] = L.s[ns][S4 ? 1 : 0] >> 16;
+        } else {
+            uint32_t s = L.s[ns][0];
+            if (LAST && gs + kb >= G)
+                s = 0;
+            broadcast_rows(s, sc);
+        }
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
             P.s2[ns][tt] = __builtin_bit_cast(half2v, sc[tt] * 0x10001u);
@@ -204,8 +221,9 @@ __device__ __forceinline__ void prepare(StepWeights &P, const StepLoads<XP> &L, 
 
 // Stores a step's activation pieces into an LDS buffer in pair order. LAST:
 // values past K are zero.
-template <int XP, bool LAST, int NT>
-__device__ __forceinline__ void stage(_Float16 *buf, const StepLoads<XP> &L, int gs, int G, int t)
+template <int XP, bool LAST, int NT, bool S4>
+__device__ __forceinline__ void stage(_Float16 *buf, const StepLoads<XP, S4> &L, int gs, int G,
+                                      int t)
 {
 #pragma unroll
     for (int q = 0; q < XP; ++q) {
@@ -385,7 +403,7 @@ __global__ __launch_bounds__(256) void k_group_sums(const uint16_t *__restrict__
 // problems).
 // AFF: the affine format; S and Bias [N][G / 2]; XS the group sums of X
 // (k_group_sums, GP groups per half).
-template <int MS, int MODE, bool AFF, int NW>
+template <int MS, int MODE, bool AFF, int NW, bool S4>
 __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (MS == 8 ? 2 : 3)) void k_gemm_q4(
     const uint4 *__restrict__ W, const uint16_t *__restrict__ S, const uint16_t *__restrict__ X,
     int64_t ldx, uint16_t *__restrict__ Y, int64_t ldy, float *__restrict__ part, int M, int N,
@@ -415,7 +433,8 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (MS == 8 ? 2 : 3)) void k_ge
     for (int ns = 0; ns < 2; ++ns) {
         const int row = n0 + 16 * ns + n;
         O.w[ns] = row < N ? (uint32_t)(row * G + kb) * 16u : kOut;
-        O.s[ns] = row < N ? (uint32_t)(AFF ? row * (G / 2) + kb / 2 : row * G + kb) * 2u : kOut;
+        O.s[ns] = row < N ? (uint32_t)(AFF ? row * (G / 2) + kb / 2 : row * G + (S4 ? 0 : kb)) * 2u
+                          : kOut;
     }
 #pragma unroll
     for (int q = 0; q < XP; ++q) {
@@ -437,7 +456,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (MS == 8 ? 2 : 3)) void k_ge
     const int total_steps = steps + (AFF ? GP / 64 : 0);
     const int st0 = z * sps, st1 = min(steps, st0 + sps);
     const int bs1 = min(total_steps, st0 + sps);
-    StepLoads<XP> L[D];
+    StepLoads<XP, S4> L[D];
     StepWeights P;
     // one step from register buffer Lr: stage its activation tile into LDS
     // buffer st & 1 and its weights into P, refill Lr with step `next` (LOAD;
@@ -446,12 +465,12 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (MS == 8 ? 2 : 3)) void k_ge
     // previous step's barrier. LAST: groups past K (only the last step of the
     // last split). A refill past the split's last step re-reads that step
     // (unconditional loads keep the two buffers' registers apart).
-    auto body = [&](StepLoads<XP> &Lr, int st, int next, auto last, auto load)
+    auto body = [&](StepLoads<XP, S4> &Lr, int st, int next, auto last, auto load)
                     __attribute__((always_inline)) {
-        stage<XP, decltype(last)::value, NT>(xs[st & 1], Lr, 4 * st, G, t);
-        prepare<XP, decltype(last)::value>(P, Lr, 4 * st, kb, G);
+        stage<XP, decltype(last)::value, NT, S4>(xs[st & 1], Lr, 4 * st, G, t);
+        prepare<XP, decltype(last)::value, S4>(P, Lr, 4 * st, kb, G);
         if constexpr (decltype(load)::value)
-            load_step<XP, AFF>(Lr, B, O, next);
+            load_step<XP, AFF, S4>(Lr, B, O, next);
         __syncthreads();
         multiply<MS, MODE, AFF>(acc, xs[st & 1], P, n, kb);
     };
@@ -460,7 +479,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (MS == 8 ? 2 : 3)) void k_ge
     if (st0 < st1) {
 #pragma unroll
         for (int d = 0; d < D; ++d)
-            load_step<XP, AFF>(L[d], B, O, min(st0 + d, st1 - 1));
+            load_step<XP, AFF, S4>(L[d], B, O, min(st0 + d, st1 - 1));
         if constexpr (D == 1) {
             for (int st = st0; st < st1 - 1; ++st)
                 body(L[0], st, st + 1, no, yes);
@@ -584,14 +603,21 @@ q4_status launch_tiles(bool exact, dim3 grid, hipStream_t stream, const uint4 *w
                        int gp)
 {
     const int bvec = bias && (G / 2) % 8 == 0 && reinterpret_cast<uintptr_t>(bias) % 16 == 0;
-    if (bias)
-        Q4_LAUNCH_MATVEC((k_gemm_q4<MS, kWGroup, true, NW>), grid, dim3(64 * NW), 0, stream, w, s, x, ldx,
+    if (!bias && G % 4 == 0) {  // four scales per lane in one load
+        if (exact)
+            Q4_LAUNCH_MATVEC((k_gemm_q4<MS, kWGroup, false, NW, true>), grid, dim3(64 * NW), 0, stream, w, s, x, ldx,
+                             y, ldy, part, M, N, G, sps, nullptr, nullptr, 0, 0);
+        else
+            Q4_LAUNCH_MATVEC((k_gemm_q4<MS, kWF16, false, NW, true>), grid, dim3(64 * NW), 0, stream, w, s, x, ldx,
+                             y, ldy, part, M, N, G, sps, nullptr, nullptr, 0, 0);
+    } else if (bias)
+        Q4_LAUNCH_MATVEC((k_gemm_q4<MS, kWGroup, true, NW, false>), grid, dim3(64 * NW), 0, stream, w, s, x, ldx,
                          y, ldy, part, M, N, G, sps, bias, xsum, gp, bvec);
     else if (exact)
-        Q4_LAUNCH_MATVEC((k_gemm_q4<MS, kWGroup, false, NW>), grid, dim3(64 * NW), 0, stream, w, s, x, ldx,
+        Q4_LAUNCH_MATVEC((k_gemm_q4<MS, kWGroup, false, NW, false>), grid, dim3(64 * NW), 0, stream, w, s, x, ldx,
                          y, ldy, part, M, N, G, sps, nullptr, nullptr, 0, 0);
     else
-        Q4_LAUNCH_MATVEC((k_gemm_q4<MS, kWF16, false, NW>), grid, dim3(64 * NW), 0, stream, w, s, x, ldx,
+        Q4_LAUNCH_MATVEC((k_gemm_q4<MS, kWF16, false, NW, false>), grid, dim3(64 * NW), 0, stream, w, s, x, ldx,
                          y, ldy, part, M, N, G, sps, nullptr, nullptr, 0, 0);
     return check_launch("k_gemm_q4");
 }
