@@ -158,9 +158,10 @@ struct StepLoads {
 };
 
 // (AFF: a step spans two 64-code groups, so its scales are 4 bytes on.) S4
-// (symmetric format, G % 4 == 0): each lane loads the four scales of the
-// step's groups of its row in one 8-byte load (the same bytes the lane row
-// loads two at a time otherwise), so no exchange across lane rows is needed.
+// (G % 4 == 0): each lane loads the scales of the step's groups of its row in
+// one load (8 bytes, four scales; affine: 4 bytes, two scales of 64 codes),
+// the same bytes its lane row loads two at a time otherwise, so no exchange
+// across lane rows is needed.
 template <int XP, bool AFF, bool S4>
 __device__ __forceinline__ void load_step(StepLoads<XP, S4> &L, const Bufs &B,
                                           const Offsets<XP> &O, int st)
@@ -168,7 +169,9 @@ __device__ __forceinline__ void load_step(StepLoads<XP, S4> &L, const Bufs &B,
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns) {
         L.w[ns] = __builtin_amdgcn_raw_buffer_load_b128(B.w, O.w[ns], st * 64, 0);
-        if (S4) {
+        if (S4 && AFF) {
+            L.s[ns][0] = __builtin_amdgcn_raw_buffer_load_b32(B.s, O.s[ns], st * 4, 0);
+        } else if (S4) {
             const auto v = __builtin_amdgcn_raw_buffer_load_b64(B.s, O.s[ns], st * 8, 0);
             L.s[ns][0] = v[0];
             L.s[ns][S4 ? 1 : 0] = v[1];
@@ -189,7 +192,7 @@ struct StepWeights {
     half2v s2[2][4];
 };
 
-template <int XP, bool LAST, bool S4>
+template <int XP, bool LAST, bool S4, bool AFF>
 __device__ __forceinline__ void prepare(StepWeights &P, const StepLoads<XP, S4> &L, int gs,
                                         int kb, int G)
 {
@@ -201,7 +204,11 @@ __device__ __forceinline__ void prepare(StepWeights &P, const StepLoads<XP, S4> 
         P.wt[ns][3] = L.w[ns].w;
         transpose_rows(P.wt[ns]);
         uint32_t sc[4];
-        if (S4) {
+        if (S4 && AFF) {
+            // groups 0, 1 of the step share the first 64-code scale, 2, 3 the second
+            sc[0] = sc[1] = L.s[ns][0] & 0xFFFFu;
+            sc[2] = sc[3] = L.s[ns][0] >> 16;
+        } else if (S4) {
             // (G % 4 == 0: a step never reaches past K)
             sc[0] = L.s[ns][0] & 0xFFFFu;
             sc[1] = L.s[ns][0] >> 16;
@@ -433,7 +440,8 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (MS == 8 ? 2 : 3)) void k_ge
     for (int ns = 0; ns < 2; ++ns) {
         const int row = n0 + 16 * ns + n;
         O.w[ns] = row < N ? (uint32_t)(row * G + kb) * 16u : kOut;
-        O.s[ns] = row < N ? (uint32_t)(AFF ? row * (G / 2) + kb / 2 : row * G + (S4 ? 0 : kb)) * 2u
+        O.s[ns] = row < N ? (uint32_t)(AFF ? row * (G / 2) + (S4 ? 0 : kb / 2)
+                                           : row * G + (S4 ? 0 : kb)) * 2u
                           : kOut;
     }
 #pragma unroll
@@ -468,7 +476,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (MS == 8 ? 2 : 3)) void k_ge
     auto body = [&](StepLoads<XP, S4> &Lr, int st, int next, auto last, auto load)
                     __attribute__((always_inline)) {
         stage<XP, decltype(last)::value, NT, S4>(xs[st & 1], Lr, 4 * st, G, t);
-        prepare<XP, decltype(last)::value, S4>(P, Lr, 4 * st, kb, G);
+        prepare<XP, decltype(last)::value, S4, AFF>(P, Lr, 4 * st, kb, G);
         if constexpr (decltype(load)::value)
             load_step<XP, AFF, S4>(Lr, B, O, next);
         __syncthreads();
@@ -610,7 +618,10 @@ q4_status launch_tiles(bool exact, dim3 grid, hipStream_t stream, const uint4 *w
         else
             Q4_LAUNCH_MATVEC((k_gemm_q4<MS, kWF16, false, NW, true>), grid, dim3(64 * NW), 0, stream, w, s, x, ldx,
                              y, ldy, part, M, N, G, sps, nullptr, nullptr, 0, 0);
-    } else if (bias)
+    } else if (bias && G % 4 == 0)
+        Q4_LAUNCH_MATVEC((k_gemm_q4<MS, kWGroup, true, NW, true>), grid, dim3(64 * NW), 0, stream, w, s, x, ldx,
+                         y, ldy, part, M, N, G, sps, bias, xsum, gp, bvec);
+    else if (bias)
         Q4_LAUNCH_MATVEC((k_gemm_q4<MS, kWGroup, true, NW, false>), grid, dim3(64 * NW), 0, stream, w, s, x, ldx,
                          y, ldy, part, M, N, G, sps, bias, xsum, gp, bvec);
     else if (exact)
