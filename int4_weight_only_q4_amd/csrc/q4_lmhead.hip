@@ -11,7 +11,13 @@
 //    and one candidate per workgroup, the largest (value, index) key of its
 //    rows; k_argmax_finish reduces the candidates in one workgroup. No logit
 //    is read back and no atomics are used, so the token is deterministic.
-//  * M >= 2: the matrix-core matvec's split-K partials are summed by
+//  * M = 2..4 on the few-row kernel: the f32 logits, then k_argmax_partial
+//    and k_argmax_finish;
+//  * M >= 2 on the workgroup-reduced matrix-core kernel (k_gemv_mma): as it
+//    stores a tile it keeps each lane's largest key per row; at its end the
+//    workgroup's per-row best (an LDS maximum, order-independent) goes to a
+//    candidate array that k_argmax_finish reduces;
+//  * otherwise the matrix-core matvec's split-K partials are summed by
 //    k_combine_argmax, which writes the f32 logits and the first argmax pass's
 //    candidates (k_argmax_partial when K is not split), then k_argmax_finish.
 // Ties go to the smallest index, -0 equals +0 and a NaN ranks above every
@@ -213,8 +219,10 @@ size_t lm_head_cand_bytes(int N, int K, int M)
 
 size_t ws_lm_head(int N, int K, int M)
 {
-    if (M > 1 && (gemv_rows_fits(M, K, N) || mma_fits(N, K, M)))
+    if (M > 1 && gemv_rows_fits(M, K, N))
         return ws_argmax(N, M);
+    if (M > 1 && mma_fits(N, K, M))
+        return kWsHeader + (size_t)M * mma_blocks(N) * sizeof(unsigned long long);
     if (M > 1)
         return kWsHeader + lm_head_cand_bytes(N, K, M) + mfma_part_bytes(N, K);
     return kWsHeader + (size_t)matvec_blocks(N, K) * sizeof(unsigned long long);
@@ -241,14 +249,24 @@ q4_status launch_lm_head_argmax(const uint32_t *W, const uint16_t *S, const uint
                                 int64_t ldx, float *logits, int64_t ldl, int32_t *tokens, int N,
                                 int K, int M, hipStream_t stream)
 {
-    if (M > 1 && (gemv_rows_fits(M, K, N) || mma_fits(N, K, M))) {
-        // the f32 logits without a workspace (a few rows: M single-row
-        // matvecs; more: the workgroup-reduced matrix-core kernel), then the
-        // argmax
+    if (M > 1 && gemv_rows_fits(M, K, N)) {
+        // a few rows: the f32 logits by M single-row matvecs, then the argmax
         q4_status st = launch_gemv_f32(W, S, x, ldx, logits, ldl, N, K, M, stream);
         if (st != Q4_OK)
             return st;
         return launch_argmax(logits, ldl, N, M, tokens, stream);
+    }
+    if (M > 1 && mma_fits(N, K, M)) {
+        // the workgroup-reduced matrix-core kernel writes the f32 logits and
+        // each workgroup's best key per row; one finish reduces them
+        char *ws = static_cast<char *>(workspace(stream, ws_lm_head(N, K, M)));
+        if (!ws)
+            return workspace_status();
+        auto *cand = reinterpret_cast<unsigned long long *>(ws + kWsHeader);
+        q4_status st = launch_gemv_mma(W, S, x, ldx, nullptr, logits, ldl, N, K, M, stream, cand);
+        if (st != Q4_OK)
+            return st;
+        return finish(cand, mma_blocks(N), M, tokens, stream);
     }
     if (M > 1) {
         // per launch of up to 16 rows: the matrix-core partials, then their sum

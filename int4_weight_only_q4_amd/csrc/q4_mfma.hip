@@ -490,6 +490,9 @@ struct MmaArgs {
     uint16_t *y;  // f16 results, or
     float *yf;    // f32 results
     int64_t ldy;
+    // when set: the workgroup's largest argmax_key of each of its rows' results,
+    // cand[m * gridDim.x + blockIdx.x]
+    unsigned long long *cand;
     int N, G, M;
     int KP, rounds;  // K parts, rounds
 };
@@ -507,6 +510,7 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
     // would hold the activation's loads back in the memory queues
     constexpr bool kEarly = SK2 <= 3;
     extern __shared__ uint4 smem[];
+    __shared__ unsigned long long s_cand[16];  // (cand) each row's largest key so far
     const int G = a.G, K = G * 32, M = a.M, N = a.N;
     const int xstride = K + 8;  // staged row: 16 bytes of padding against bank conflicts
     const int t = threadIdx.x, l = t & 63;
@@ -623,9 +627,12 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
     }
     if (t < 4 * kMmaWaves)
         arrived[t] = 0u;  // and uses[]
+    if (t < 16)
+        s_cand[t] = 0ull;
     __syncthreads();
 
     // 2. the rounds: each unit issues all of its loads, then computes
+    unsigned long long best[4] = {0ull, 0ull, 0ull, 0ull};  // (cand) rows 4 kb + e
     const int mrow = min(n, M - 1);  // A row m = n
     const _Float16 *xrow = xs + mrow * xstride + 8 * kb;
     const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -747,6 +754,10 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
                             a.yf[m * a.ldy + col] = v[e];
                         else
                             a.y[m * a.ldy + col] = f2h(v[e]);
+                        if (a.cand) {
+                            const unsigned long long key = argmax_key(v[e], (uint32_t)col);
+                            best[e] = key > best[e] ? key : best[e];
+                        }
                     }
                 }
         }
@@ -755,6 +766,25 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
         if (!kEarly || r > 0)
             load_unit(r, ua);
         compute_unit(r, ua);
+    }
+    if (a.cand) {
+        // the lane row's largest keys over its 16 lanes (rows 4 kb + e), into
+        // the workgroup's, and once every wave is done, out
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1)
+            {
+                const unsigned long long o = __shfl_xor(best[e], off);
+                best[e] = o > best[e] ? o : best[e];
+            }
+            if (n == 0 && 4 * kb + e < M)
+                __hip_atomic_fetch_max(&s_cand[4 * kb + e], best[e], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        __syncthreads();
+        if (t < M)
+            a.cand[(size_t)t * gridDim.x + blockIdx.x] = s_cand[t];
     }
 }
 
@@ -854,9 +884,11 @@ q4_status run_mma(const MmaArgs &args, const MmaPlan &pl, hipStream_t stream)
 
 bool mma_fits(int N, int K, int M) { return mma_plan(N, K, std::min(M, kMTile)).lds <= 160 * 1024; }
 
+int mma_blocks(int N) { return std::min(cu_count(), (N + 15) / 16); }
+
 q4_status launch_gemv_mma(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
                           uint16_t *y, float *yf, int64_t ldy, int N, int K, int M,
-                          hipStream_t stream)
+                          hipStream_t stream, unsigned long long *cand)
 {
     for (int m0 = 0; m0 < M; m0 += kMTile) {
         const int mt = std::min(kMTile, M - m0);
@@ -871,6 +903,7 @@ q4_status launch_gemv_mma(const uint32_t *W, const uint16_t *S, const uint16_t *
         args.y = yf ? nullptr : y + m0 * ldy;
         args.yf = yf ? yf + m0 * ldy : nullptr;
         args.ldy = ldy;
+        args.cand = cand ? cand + (size_t)m0 * pl.blocks : nullptr;
         args.N = N;
         args.G = K / 32;
         args.M = mt;
