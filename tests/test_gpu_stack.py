@@ -212,21 +212,28 @@ def _attn_stack(o, q4, geom, n_layers, seed):
     return host_layers, dev_layers, gi, gp, gf
 
 
-@pytest.mark.parametrize("geom,n_layers,pos", [((256, 512, 4, 2, 64), 3, 37),
-                                               ((256, 512, 4, 4, 64), 2, 0)])
-def test_stack_with_attention_teacher_forced(o, q4, geom, n_layers, pos):
+@pytest.mark.parametrize("geom,n_layers,pos,max_len,pages", [
+    ((256, 512, 4, 2, 64), 3, 37, 128, 8),
+    ((256, 512, 4, 4, 64), 2, 0, 128, 8),
+    # several splits of the positions (their combine may be the O matvec's
+    # prologue): 521 cached positions over 3 splits, and a bound of 1000
+    # positions whose later splits are empty
+    ((256, 512, 4, 2, 64), 2, 520, 600, 40),
+    ((256, 512, 4, 4, 64), 2, 300, 1000, 64)])
+def test_stack_with_attention_teacher_forced(o, q4, geom, n_layers, pos, max_len, pages):
     import torch
     d, f, nh, nkv, hd = geom
     eps = 1e-5
     hl, dl, gi, gp, gf = _attn_stack(o, q4, geom, n_layers, 2100 + pos)
-    desc = q4.attn_desc(nh, nkv, hd, 16, 8, 8)
-    table = np.array([5, 2, 7, 0, 1, 3, 6, 4], np.int32)
+    desc = q4.attn_desc(nh, nkv, hd, 16, pages, pages)
+    table = (np.array([5, 2, 7, 0, 1, 3, 6, 4], np.int32) if pages == 8
+             else np.random.default_rng(pages).permutation(pages).astype(np.int32))
     tab = torch.from_numpy(table).cuda()
     posd = torch.tensor([pos], dtype=torch.int32, device="cuda")
     # caches with random rows for positions < pos (position pos is written by the step)
     caches0 = []
     for L in range(n_layers):
-        c = np.zeros((8, 2, nkv, 16, hd), np.float16)
+        c = np.zeros((pages, 2, nkv, 16, hd), np.float16)
         if pos:
             t = np.arange(pos)
             c[table[t // 16], 0, :, t % 16, :] = datagen.activations(2200 + L, pos, nkv * hd).reshape(pos, nkv, hd)
@@ -240,7 +247,7 @@ def test_stack_with_attention_teacher_forced(o, q4, geom, n_layers, pos):
     r_out = torch.empty(d, dtype=torch.float16, device="cuda")
     h_out = torch.empty(d, dtype=torch.float16, device="cuda")
     trace = torch.empty((n_layers, 2, d), dtype=torch.float16, device="cuda")
-    st.decode_attn(desc, caches, tab, posd, 128, dev_tensor(r0), dev_tensor(h0), r_out, h_out,
+    st.decode_attn(desc, caches, tab, posd, max_len, dev_tensor(r0), dev_tensor(h0), r_out, h_out,
                    trace=trace)
     torch.cuda.synchronize()
     tr = host(trace)
@@ -255,7 +262,7 @@ def test_stack_with_attention_teacher_forced(o, q4, geom, n_layers, pos):
         kv = torch.from_numpy(caches0[L].copy()).cuda()
         rd, hd_ = dev_tensor(r_in), dev_tensor(h_in)
         q = q4.qkv_rope_append(dev[0], dev[1], hd_, desc, posd, tab, kv)
-        a = q4.attention_decode(q, kv, tab, posd, 128, desc)
+        a = q4.attention_decode(q, kv, tab, posd, max_len, desc)
         r1 = torch.empty_like(rd)
         h1 = q4.gemv_ex(dev[2], dev[3], a, kind=q4.EPI_ADD_RMSNORM, res_in=rd, gamma=dev_tensor(gp[L]),
                         res_out=r1, eps=eps)
