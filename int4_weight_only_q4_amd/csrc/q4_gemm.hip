@@ -158,10 +158,10 @@ struct StepLoads {
 };
 
 // (AFF: a step spans two 64-code groups, so its scales are 4 bytes on.) S4
-// (G % 4 == 0): each lane loads the scales of the step's groups of its row in
-// one load (8 bytes, four scales; affine: 4 bytes, two scales of 64 codes),
-// the same bytes its lane row loads two at a time otherwise, so no exchange
-// across lane rows is needed.
+// (G % 4 == 0): each lane loads all the scales of the step's groups of its row
+// in one load (8 bytes, four scales; affine: 4 bytes, two scales of 64 codes);
+// otherwise each of the row's four lanes loads one 2-byte scale and permlane
+// swaps hand every lane the other three.
 template <int XP, bool AFF, bool S4>
 __device__ __forceinline__ void load_step(StepLoads<XP, S4> &L, const Bufs &B,
                                           const Offsets<XP> &O, int st)
