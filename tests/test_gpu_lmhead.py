@@ -239,6 +239,22 @@ def test_lm_head_phi3_few_rows_matrix_cores(o, q4, m):
         check_token(int(tk[b]), lg[b], ref[b], "row %d" % b)
 
 
+def test_lm_head_more_than_16_rows(o, q4):
+    """20 rows on the matrix cores run as two launches of 16 and 4 rows, each
+    leaving its workgroups' row candidates for one finish: every logit against
+    the oracle, each token, and tokens equal to those of the first maximum of
+    the returned logits."""
+    n, k, m = 5003, 256, 20
+    W, S, X = make(o, "rows20", n, k, m)
+    logits, tok = q4.lm_head_argmax(dev_tensor(W), dev_tensor(S), dev_tensor(X))
+    sync()
+    lg, tk = host(logits), host(tok).astype(np.int64)
+    ref, _ = o.lm_head(W, S, X)
+    for b in range(m):
+        assert_within(lg[b], ref[b], "row %d" % b)
+        check_token(int(tk[b]), lg[b], ref[b], "row %d" % b)
+
+
 def test_lm_head_planted_maximum(o, q4):
     """All weights zero except two identical rows of codes 15 and x > 0: the
     token is the first of them, wherever it falls among the workgroups."""
@@ -251,7 +267,7 @@ def test_lm_head_planted_maximum(o, q4):
         S = datagen.scales(601, n, k)
         S[r1] = S[r0]
         x = np.abs(datagen.activations(602, 1, k)[0]).astype(np.float16)
-        for m in (1, 2, 4, 8):
+        for m in (1, 2, 4, 8, 18):
             X = np.stack([x] * m)
             logits, tok = q4.lm_head_argmax(dev_tensor(W), dev_tensor(S),
                                             dev_tensor(X if m > 1 else x))
