@@ -137,7 +137,9 @@ q4_status q4_gemv_batched(const uint32_t *W, const uint16_t *S, const uint16_t *
  * pairs: groups of up to 4 pairs while experts get about two pairs each or
  * fewer (at most 256 pairs), otherwise groups of up to 16 on the matrix cores;
  * an expert with more pairs than one group re-reads its rows, mostly from
- * cache. Ids are validated on the device; an out-of-range id contributes
+ * cache. Exception: the down stage with the combine at T*TOPK <= 32 runs token
+ * by token (each token's experts read for that token, the combine in the same
+ * kernel). Ids are validated on the device; an out-of-range id contributes
  * zeros. T*TOPK <= Q4_MAX_PAIRS.
  */
 #define Q4_MAX_PAIRS 4096
@@ -286,7 +288,8 @@ q4_status q4_argmax(const float *v, int64_t ld, int64_t N, int64_t M, int32_t *i
                     q4_stream stream);
 
 /* q4_lm_head_argmax -- q4_gemv_f32 into logits (f32, rows of ldl >= N) and
- * q4_argmax of each row into tokens int32[M], in one call (for M = 1 the
+ * q4_argmax of each row into tokens int32[M], in one call (for M = 1, and on
+ * the matrix cores for M >= 2 where the activation rows fit in LDS, the
  * matmul's workgroups hand their rows' best (value, index) to a one-workgroup
  * reduction; the logits are not read back). Arguments and errors as for the
  * two calls; logits and tokens must not overlap each other or the inputs.
