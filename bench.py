@@ -260,7 +260,9 @@ def committed_traffic():
 
 
 GEMV_TABLE_PROFILE = os.path.join(ROOT, "profiles", "gemv_table_phi3_qwen3_moe.md")
-MOE_KERNELS = "the gate_up stage one expert kernel, the down stage an expert kernel and a finishing kernel"
+MOE_KERNELS = ("the gate_up stage one expert kernel; the down stage one kernel with the "
+               "routing-weighted combine up to 32 (token, slot) pairs, else an expert kernel "
+               "and a finishing kernel")
 QWEN3 = dict(qkv=(6144, 2560), o=(2560, 4096), gate_up=(19456, 2560), down=(2560, 9728),
              lm_head=(151936, 2560))
 

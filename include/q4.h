@@ -349,10 +349,11 @@ q4_status q4_rope_append(const uint16_t *qkv, const q4_attn_desc *desc, const in
 /* q4_attention_decode -- out f16[n_heads * head_dim]: for query head h and
  * key/value head h / (n_heads / n_kv),
  *   out[h] = sum_{t <= *pos} softmax_t(q_h . k_t / sqrt(head_dim)) v_t
- * over the cached positions 0 .. *pos. The positions are split over up to 16
+ * over the cached positions 0 .. *pos. The positions are split over up to 32
  * workgroups per head (max_len, the caller's bound on *pos + 1, sizes the
- * split) whose partial softmax states (max, sum, weighted values) a second
- * kernel combines in split order. q f16, 16-byte aligned; out must not overlap
+ * split; a larger *pos is still attended in full, only more slowly) whose
+ * partial softmax states (max, sum, weighted values) a second kernel combines
+ * in split order. q f16, 16-byte aligned; out must not overlap
  * q or the cache. */
 q4_status q4_attention_decode(const uint16_t *q, const uint16_t *kv_pages,
                               const int32_t *page_table, const int32_t *pos, int64_t max_len,

@@ -87,10 +87,12 @@ __device__ __forceinline__ void fma8(float (&o)[8], float p, uint4 w)
 }
 
 // Workgroup (head, split): partial softmax state of the split's positions,
-// whole blocks of 256 positions per split.
+// in blocks of PB positions (256, or 64 where every split is at most 64
+// positions long: the value phase then loads and adds only a quarter of the
+// chunks; the positions dropped are those past the block, whose weight is 0).
 // part layout: [n_heads][splits][2 + head_dim] = (max, sum, weighted values).
 // NC = head_dim / 8 (16-byte chunks of a cache row).
-template <int NC>
+template <int NC, int PB>
 __global__ __launch_bounds__(kAttnThreads) void k_attn(const uint16_t *__restrict__ q,
                                                        const uint16_t *__restrict__ kv,
                                                        RopeArgs r, float scale,
@@ -98,11 +100,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(const uint16_t *__restric
                                                        uint16_t *__restrict__ out)
 {
     constexpr int D = 8 * NC;
-    constexpr int groups = kAttnThreads / NC;             // position groups of the value phase
-    constexpr int U = (kAttnThreads + groups - 1) / groups;  // positions per value thread
+    static_assert(PB == 64 || PB == kAttnThreads, "positions per block");
+    constexpr int groups = kAttnThreads / NC;      // position groups of the value phase
+    constexpr int U = (PB + groups - 1) / groups;  // positions per value thread
     __shared__ float qs[D];
-    __shared__ float ps[kAttnThreads];
-    __shared__ int64_t vofs[kAttnThreads];
+    __shared__ float ps[PB];
+    __shared__ int64_t vofs[PB];
     __shared__ float red[kAttnThreads / 64];
     __shared__ float osum[groups * D];
 
@@ -126,8 +129,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(const uint16_t *__restric
     float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
-    for (int tb = t0; tb < t1; tb += kAttnThreads) {
-        const int nb = min(kAttnThreads, t1 - tb);
+    for (int tb = t0; tb < t1; tb += PB) {
+        const int nb = min(PB, t1 - tb);
         // scores: one position per thread, its key row's loads all in flight;
         // the row's value offset goes to LDS for the value phase
         const int64_t koff = tid < nb ? cache_row(r, tb + tid, kvh) : -1;
@@ -150,13 +153,15 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(const uint16_t *__restric
             }
             sc = dot * scale;
         }
-        vofs[tid] = koff < 0 ? -1 : koff + kv_dist;
+        if (tid < PB)
+            vofs[tid] = koff < 0 ? -1 : koff + kv_dist;
         const float m_blk = block_reduce(sc, red, true);
         const float m_new = fmaxf(m_run, m_blk);
         // with no valid position yet there is nothing to rescale or add
         const float alpha = m_new == -INFINITY ? 1.f : expf(m_run - m_new);
         const float p = sc == -INFINITY ? 0.f : expf(sc - m_new);
-        ps[tid] = p;
+        if (tid < PB)
+            ps[tid] = p;
         const float l_blk = block_reduce(p, red, false);  // its barrier publishes ps, vofs
         l_run = l_run * alpha + l_blk;
         m_run = m_new;
@@ -170,9 +175,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(const uint16_t *__restric
             float pj[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int j = min(tg + u * groups, kAttnThreads - 1);
+                const int j = min(tg + u * groups, PB - 1);
                 const int64_t vo = vofs[j];
-                pj[u] = (tg + u * groups < kAttnThreads && vo >= 0) ? ps[j] : 0.f;
+                pj[u] = (tg + u * groups < PB && vo >= 0) ? ps[j] : 0.f;
                 vw[u] = reinterpret_cast<const uint4 *>(kv + (vo >= 0 ? vo : 0))[dc];
             }
 #pragma unroll
@@ -291,11 +296,21 @@ q4_status launch_attention(const uint16_t *q, const uint16_t *kv, const RopeArgs
         part = reinterpret_cast<float *>(ws + kWsHeader);
     }
     const dim3 grid(r.n_heads, NS);
+    // blocks of 64 positions where no split can be longer (the bound on the
+    // position count gives the longest split; the kernel loops over blocks
+    // either way)
+    const int64_t len = std::max<int64_t>(1, std::min<int64_t>(max_len, (int64_t)r.max_pages * r.page_size));
+    const int64_t pieces = (len + kSplitGrain - 1) / kSplitGrain;
+    const bool short_splits = kSplitGrain * ((pieces + NS - 1) / NS) <= 64;
     switch (r.head_dim / 8) {
 #define Q4_ATTN_CASE(nc)                                                                          \
     case nc:                                                                                      \
-        hipLaunchKernelGGL(k_attn<nc>, grid, dim3(kAttnThreads), 0, stream, q, kv, r, scale, part, \
-                           out);                                                                  \
+        if (short_splits)                                                                         \
+            hipLaunchKernelGGL((k_attn<nc, 64>), grid, dim3(kAttnThreads), 0, stream, q, kv, r,   \
+                               scale, part, out);                                                 \
+        else                                                                                      \
+            hipLaunchKernelGGL((k_attn<nc, kAttnThreads>), grid, dim3(kAttnThreads), 0, stream, q, \
+                               kv, r, scale, part, out);                                          \
         break;
         Q4_ATTN_CASE(1) Q4_ATTN_CASE(2) Q4_ATTN_CASE(4) Q4_ATTN_CASE(6) Q4_ATTN_CASE(8)
         Q4_ATTN_CASE(12) Q4_ATTN_CASE(16) Q4_ATTN_CASE(20) Q4_ATTN_CASE(24) Q4_ATTN_CASE(32)

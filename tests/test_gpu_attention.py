@@ -162,6 +162,21 @@ def test_attention_skips_pages_outside_the_table(o, q4):
     assert_within(host(over), o.attention(q, kc, vc, nh, nh, hd), "clamped position")
 
 
+def test_attention_walks_blocks_when_the_position_passes_its_bound(o, q4):
+    """max_len = 64 sizes one split of one 64-position block, but *pos + 1 =
+    300: the workgroup walks five blocks with the running softmax and still
+    attends over every cached position."""
+    g = PHI3
+    nh, hd = g["n_heads"], g["head_dim"]
+    d = desc_for(q4, g)
+    table = np.random.default_rng(64).permutation(257).astype(np.int32)
+    kv, kc, vc = fill_cache(q4, d, 970, 300, table)
+    q = datagen.activations(971, 1, nh * hd)[0]
+    out = q4.attention_decode(dev_tensor(q), kv, i32(table), i32([299]), 64, d)
+    sync()
+    assert_within(host(out), o.attention(q, kc, vc, nh, nh, hd), "300 positions, bound 64")
+
+
 def test_decode_loop_append_then_attend(o, q4):
     """Twenty decode steps on a small grouped geometry: each step appends its
     rotated K and V, then attends over everything cached so far. The oracle is
