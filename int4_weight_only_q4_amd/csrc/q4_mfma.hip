@@ -456,7 +456,8 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ part,
 // the whole launch. A unit of work is one 16-row tile times one of KP equal
 // parts of K (SK = 2 SK2 steps of four groups); wave w takes part w % KP of
 // the tiles blockIdx.x + gridDim.x * (w / KP + (kMmaWaves / KP) * round), one
-// unit per round. A wave issues all loads of a unit at once, in whole memory
+// unit per round (waves from (kMmaWaves / KP) * KP on, when KP does not
+// divide kMmaWaves, take none). A wave issues all loads of a unit at once, in whole memory
 // lines: the unit's scales as a row-major block (64 consecutive scales, or
 // pairs of them, per load), then its weights as 8 rows x 128 bytes per load
 // (a pair of steps per two loads). The scales go to a per-wave LDS block, each
@@ -532,6 +533,8 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
 
     const int KP = a.KP, rounds = a.rounds;
     const int kp = wave % KP, tslot = wave / KP, tpr = kMmaWaves / KP;
+    // waves past tpr * KP (KP not dividing kMmaWaves) take no tiles
+    const int my_rounds = tslot < tpr ? rounds : 0;
     const int ntiles = (N + 15) >> 4;
     const int gp0 = kp * GU;  // first group of this wave's part of K
     auto tile_of = [&](int r) { return (int)blockIdx.x + (int)gridDim.x * (tslot + tpr * r); };
@@ -762,7 +765,7 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
                 }
         }
     };
-    for (int r = 0; r < rounds; ++r) {
+    for (int r = 0; r < my_rounds; ++r) {
         if (!kEarly || r > 0)
             load_unit(r, ua);
         compute_unit(r, ua);
@@ -829,43 +832,53 @@ q4_status launch_mfma_rows(const uint32_t *W, const uint16_t *S, const uint16_t 
 
 namespace {
 // The launch of k_gemv_mma for an N x K matrix and mt <= 16 activation rows:
-// K parts per tile (enough units of work for most waves of the chip, at most
-// 12 steps and no part empty), the rounds, workgroups and LDS bytes.
+// the K parts per tile, the rounds, workgroups and LDS bytes. Among the part
+// counts KP = 1..12 whose part fits a unit (at most 2 max_pairs steps), whose
+// last part is not empty and whose LDS fits the CU, the plan takes the fewest
+// rounds (each round adds a wave's load latency and the meeting of the parts:
+// measured, more rounds of shorter units are slower), then the fewest
+// wave-steps per workgroup (working waves x rounds x steps per unit: a short
+// last part and tiles past the last one still cost their steps). lds is
+// SIZE_MAX when no part count fits.
 struct MmaPlan {
     int KP, SK2, rounds, blocks;
     size_t lds;
 };
+
+constexpr size_t kMmaLdsLimit = 160 * 1024;
 
 MmaPlan mma_plan(int N, int K, int mt)
 {
     MmaPlan pl;
     const int G = K / 32, ntiles = (N + 15) / 16;
     const int steps = (G + 3) / 4;  // steps of four groups over the whole of K
-    const int target = kMmaWaves * cu_count() * 3 / 4;
-    static const int kParts[] = {1, 2, 3, 4, 6, 12};  // divisors of kMmaWaves
     // (6 pairs with single scales, G odd, spill registers)
     const int max_pairs = G % 2 == 0 ? kMmaMaxPairs : kMmaMaxPairs - 1;
-    pl.KP = 0;
-    for (int c : kParts) {
-        if (c > steps && pl.KP)
-            break;
-        if ((steps + c - 1) / c > 2 * max_pairs)
-            continue;  // a unit of too many steps
-        pl.KP = c;
-        if ((int64_t)ntiles * c >= target)
-            break;
-    }
-    if (pl.KP == 0) {  // K too long for 12 parts of 16 steps
-        pl.lds = SIZE_MAX;
-        return pl;
-    }
-    pl.SK2 = ((steps + pl.KP - 1) / pl.KP + 1) / 2;
-    const int tpr = kMmaWaves / pl.KP;
     pl.blocks = std::min(cu_count(), ntiles);
-    pl.rounds = (ntiles + pl.blocks * tpr - 1) / (pl.blocks * tpr);
-    pl.lds = (size_t)kMmaWaves * mma_wave_lds(pl.SK2) + (size_t)2 * kMmaWaves * 256 * sizeof(float) +
-             (size_t)4 * kMmaWaves * sizeof(uint32_t) + (size_t)mt * (K + 8) * 2 +
-             (size_t)G * 16 * sizeof(float);
+    pl.KP = 0;
+    pl.lds = SIZE_MAX;
+    int64_t best_work = 0;
+    for (int c = 1; c <= kMmaWaves; ++c) {
+        const int sk2 = ((steps + c - 1) / c + 1) / 2;
+        if (sk2 > max_pairs || (int64_t)(c - 1) * 2 * sk2 >= steps + (c > 1 ? 0 : 1))
+            continue;  // a unit of too many steps, or an empty last part
+        const size_t lds = (size_t)kMmaWaves * mma_wave_lds(sk2) +
+                           (size_t)2 * kMmaWaves * 256 * sizeof(float) +
+                           (size_t)4 * kMmaWaves * sizeof(uint32_t) + (size_t)mt * (K + 8) * 2 +
+                           (size_t)G * 16 * sizeof(float);
+        if (lds > kMmaLdsLimit)
+            continue;
+        const int tpr = kMmaWaves / c;
+        const int rounds = (ntiles + pl.blocks * tpr - 1) / (pl.blocks * tpr);
+        const int64_t work = (int64_t)tpr * c * rounds * 2 * sk2;
+        if (!pl.KP || rounds < pl.rounds || (rounds == pl.rounds && work < best_work)) {
+            pl.KP = c;
+            pl.SK2 = sk2;
+            pl.rounds = rounds;
+            pl.lds = lds;
+            best_work = work;
+        }
+    }
     return pl;
 }
 
@@ -882,7 +895,7 @@ q4_status run_mma(const MmaArgs &args, const MmaPlan &pl, hipStream_t stream)
 }
 }  // namespace
 
-bool mma_fits(int N, int K, int M) { return mma_plan(N, K, std::min(M, kMTile)).lds <= 160 * 1024; }
+bool mma_fits(int N, int K, int M) { return mma_plan(N, K, std::min(M, kMTile)).lds <= kMmaLdsLimit; }
 
 int mma_blocks(int N) { return std::min(cu_count(), (N + 15) / 16); }
 
@@ -893,7 +906,7 @@ q4_status launch_gemv_mma(const uint32_t *W, const uint16_t *S, const uint16_t *
     for (int m0 = 0; m0 < M; m0 += kMTile) {
         const int mt = std::min(kMTile, M - m0);
         const MmaPlan pl = mma_plan(N, K, mt);
-        if (pl.lds > 160 * 1024)
+        if (pl.lds > kMmaLdsLimit)
             return fail(Q4_ERANGE, "internal: the batched matrix-core kernel does not fit K = %d", K);
         MmaArgs args;
         args.W = reinterpret_cast<const uint4 *>(W);
