@@ -467,8 +467,8 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ part,
 // without a barrier, so the waves of a CU drift apart and one wave's loads
 // overlap another's arithmetic: the last of the KP waves to arrive (an LDS
 // counter) adds the parts in K order, stores, and frees the slot for its use
-// two rounds later. Every wave of a tile runs the same number of rounds
-// (units past the last tile re-read valid data and are not stored).
+// two rounds later. A wave stops at its first tile past the last one; the KP
+// waves of a tile slot share their tiles, so they stop together.
 constexpr int kMmaWaves = 12;   // three waves per SIMD
 constexpr int kMmaMaxPairs = 6;  // steps per unit <= 12 (7 pairs spill registers)
 constexpr int kMmaXq = 8;       // activation chunks per thread held in registers
@@ -533,9 +533,9 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
 
     const int KP = a.KP, rounds = a.rounds;
     const int kp = wave % KP, tslot = wave / KP, tpr = kMmaWaves / KP;
-    // waves past tpr * KP (KP not dividing kMmaWaves) take no tiles
-    const int my_rounds = tslot < tpr ? rounds : 0;
     const int ntiles = (N + 15) >> 4;
+    // waves past tpr * KP (KP not dividing kMmaWaves) take no tiles
+    const bool working = tslot < tpr;
     const int gp0 = kp * GU;  // first group of this wave's part of K
     auto tile_of = [&](int r) { return (int)blockIdx.x + (int)gridDim.x * (tslot + tpr * r); };
 
@@ -765,7 +765,12 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
                 }
         }
     };
-    for (int r = 0; r < my_rounds; ++r) {
+    for (int r = 0; working && r < rounds; ++r) {
+        // tiles grow with the round: a wave stops at its first tile past the
+        // last, and every wave of its tile slot (the KP parts that meet in
+        // LDS) stops at the same round
+        if (tile_of(r) >= ntiles)
+            break;
         if (!kEarly || r > 0)
             load_unit(r, ua);
         compute_unit(r, ua);
