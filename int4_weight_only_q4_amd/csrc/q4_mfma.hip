@@ -457,8 +457,8 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ part,
 // parts of K (SK = 2 SK2 steps of four groups); wave w takes part w % KP of
 // the tiles blockIdx.x + gridDim.x * (w / KP + (kMmaWaves / KP) * round), one
 // unit per round (waves from (kMmaWaves / KP) * KP on, when KP does not
-// divide kMmaWaves, take none). A wave issues all loads of a unit at once, in whole memory
-// lines: the unit's scales as a row-major block (64 consecutive scales, or
+// divide kMmaWaves, take none). A wave issues all loads of a unit at once, in
+// whole memory lines: the unit's scales as a row-major block (64 consecutive scales, or
 // pairs of them, per load), then its weights as 8 rows x 128 bytes per load
 // (a pair of steps per two loads). The scales go to a per-wave LDS block, each
 // pair of steps' weights to a per-wave LDS tile from which every lane reads
@@ -841,10 +841,11 @@ namespace {
 // counts KP = 1..12 whose part fits a unit (at most 2 max_pairs steps), whose
 // last part is not empty and whose LDS fits the CU, the plan takes the fewest
 // rounds (each round adds a wave's load latency and the meeting of the parts:
-// measured, more rounds of shorter units are slower), then the fewest
-// wave-steps per workgroup (working waves x rounds x steps per unit: a short
-// last part and tiles past the last one still cost their steps). lds is
-// SIZE_MAX when no part count fits.
+// measured, more rounds of shorter units are slower), then the least
+// occupancy of the workgroup's waves (working waves x rounds x steps per unit,
+// the padding of a short last part included; counting only the steps of the
+// tiles that exist would favour long units on few waves). lds is SIZE_MAX
+// when no part count fits.
 struct MmaPlan {
     int KP, SK2, rounds, blocks;
     size_t lds;
@@ -865,7 +866,7 @@ MmaPlan mma_plan(int N, int K, int mt)
     int64_t best_work = 0;
     for (int c = 1; c <= kMmaWaves; ++c) {
         const int sk2 = ((steps + c - 1) / c + 1) / 2;
-        if (sk2 > max_pairs || (int64_t)(c - 1) * 2 * sk2 >= steps + (c > 1 ? 0 : 1))
+        if (sk2 > max_pairs || (c > 1 && (c - 1) * 2 * sk2 >= steps))
             continue;  // a unit of too many steps, or an empty last part
         const size_t lds = (size_t)kMmaWaves * mma_wave_lds(sk2) +
                            (size_t)2 * kMmaWaves * 256 * sizeof(float) +
