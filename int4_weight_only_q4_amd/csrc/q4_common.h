@@ -179,14 +179,16 @@ q4_status launch_gemv_mfma(const uint32_t *W, const uint16_t *S, const uint16_t 
                            hipStream_t stream, const uint16_t *bias = nullptr);
 // M >= 2 rows on the matrix cores with the subnormal nibble unpack and the K
 // quarters reduced inside the workgroup (no workspace), for K with
-// mma_fits(N, K, M); y f16 or yf f32 as launch_gemv_mfma. cand set: each
-// workgroup also leaves its largest argmax_key of every row's results in
-// cand[m * mma_blocks(N) + workgroup] (M * mma_blocks(N) keys).
-bool mma_fits(int N, int K, int M);
+// mma_fits(N, K, M, bias != nullptr); y f16 or yf f32 as launch_gemv_mfma.
+// cand set: each workgroup also leaves its largest argmax_key of every row's
+// results in cand[m * mma_blocks(N) + workgroup] (M * mma_blocks(N) keys).
+// bias set: the MLX affine format (scales and biases [N][K/64]).
+bool mma_fits(int N, int K, int M, bool aff = false);
 int mma_blocks(int N);
 q4_status launch_gemv_mma(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
                           uint16_t *y, float *yf, int64_t ldy, int N, int K, int M,
-                          hipStream_t stream, unsigned long long *cand = nullptr);
+                          hipStream_t stream, unsigned long long *cand = nullptr,
+                          const uint16_t *bias = nullptr);
 // One matrix-core launch for mt <= 16 activation rows. With mfma_splits(K) > 1
 // it leaves f32 partials part[ks][m][n] (mfma_part_bytes(N, K) bytes) and
 // writes neither y nor yf; otherwise the results go to yf (f32) when set, else

@@ -450,6 +450,10 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ part,
 // significant bits) and so is their difference: the result is (q - 7) * s
 // exactly, as with the other matvecs. A-operand rows m >= M repeat row M - 1
 // and are never stored.
+// AFF (the MLX affine format, w = s q + b per 64 values, scales and biases
+// [N][G/2]): the code part is the same with each 64-value group's scale on
+// both of its 32-value halves, and the second contraction takes the biases in
+// place of the scales: y = 2^24 * (code part) + (bias part).
 //
 // Work split. One workgroup of kMmaWaves waves per CU stages the activation
 // once in LDS (pair order, odd positions / 16, group sums) and keeps it for
@@ -486,6 +490,7 @@ __device__ __forceinline__ half8 codes_subnormal(uint32_t w)
 struct MmaArgs {
     const uint4 *W;
     const uint16_t *S;
+    const uint16_t *B;  // AFF: the biases [N][G/2]
     const uint16_t *x;
     int64_t ldx;
     uint16_t *y;  // f16 results, or
@@ -498,12 +503,17 @@ struct MmaArgs {
     int KP, rounds;  // K parts, rounds
 };
 
-// LDS bytes of one wave's scale block and weight tile
-constexpr int mma_wave_lds(int SK2) { return 16 * 8 * SK2 * 2 + 16 * kMmaTileStride * 16; }
+// LDS bytes of one wave's scale block (AFF: scale and bias per group, 4
+// bytes) and weight tile
+constexpr int mma_wave_lds(int SK2, bool AFF = false)
+{
+    return 16 * 8 * SK2 * (AFF ? 4 : 2) + 16 * kMmaTileStride * 16;
+}
 
-template <int SK2, bool SP>
+template <int SK2, bool SP, bool AFF>
 __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
 {
+    static_assert(!(AFF && SP), "affine scales are loaded one per group");
     constexpr int SK = 2 * SK2;  // steps per unit
     constexpr int GU = 4 * SK;   // groups per unit
     // short units: the first unit's loads go out before the activation is
@@ -521,11 +531,11 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
     // the waves' parts [2][kMmaWaves][64 lanes][4] f32; arrival counters and
     // use counts [2][kMmaWaves] u32 each; the staged rows [M][xstride]
     // binary16; the group sums [G][16] f32
-    char *wbase = reinterpret_cast<char *>(smem) + (size_t)wave * mma_wave_lds(SK2);
-    uint16_t *sblk = reinterpret_cast<uint16_t *>(wbase);
-    uint4 *wtile = reinterpret_cast<uint4 *>(wbase + 16 * GU * 2);
+    char *wbase = reinterpret_cast<char *>(smem) + (size_t)wave * mma_wave_lds(SK2, AFF);
+    uint16_t *sblk = reinterpret_cast<uint16_t *>(wbase);  // AFF: uint32 (scale | bias << 16)
+    uint4 *wtile = reinterpret_cast<uint4 *>(wbase + 16 * GU * (AFF ? 4 : 2));
     float *red = reinterpret_cast<float *>(reinterpret_cast<char *>(smem) +
-                                           (size_t)kMmaWaves * mma_wave_lds(SK2));
+                                           (size_t)kMmaWaves * mma_wave_lds(SK2, AFF));
     uint32_t *arrived = reinterpret_cast<uint32_t *>(red + 2 * kMmaWaves * 256);
     uint32_t *uses = arrived + 2 * kMmaWaves;
     _Float16 *xs = reinterpret_cast<_Float16 *>(uses + 2 * kMmaWaves);
@@ -546,7 +556,8 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
     // and half i as lane l reading group gp0 + 8 q + (l & 7) of row 8 i +
     // (l >> 3): 8 rows x 128 bytes per load
     // (SP, G even: the scales in pairs, elements 2 (64 j + l) and the next, one
-    // 4-byte load each: a pair never straddles a row and is 4-byte aligned)
+    // 4-byte load each: a pair never straddles a row and is 4-byte aligned;
+    // AFF: element e holds its 64-value group's scale and bias, s | b << 16)
     constexpr int NSL = SP ? SK2 : SK;  // scale loads per unit
     struct Unit {
         uint32_t sl[NSL];
@@ -558,6 +569,12 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
         for (int j = 0; j < NSL; ++j) {
             const int e = SP ? 2 * (64 * j + l) : 64 * j + l;
             const int rr = e / GU, cc = e - rr * GU;
+            if (AFF) {
+                const size_t off = (size_t)min(row0 + rr, N - 1) * (G >> 1) +
+                                   (min(gp0 + cc, G - 1) >> 1);
+                u.sl[j] = load_scale(a.S + off) | (load_scale(a.B + off) << 16);
+                continue;
+            }
             const size_t off = (size_t)min(row0 + rr, N - 1) * G + min(gp0 + cc, G - (SP ? 2 : 1));
             if (SP)
                 u.sl[j] = __builtin_nontemporal_load(
@@ -644,7 +661,7 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
         // order: the previous unit's reads are done)
 #pragma unroll
         for (int j = 0; j < NSL; ++j) {
-            if (SP)
+            if (SP || AFF)
                 reinterpret_cast<uint32_t *>(sblk)[64 * j + l] = u.sl[j];
             else
                 sblk[64 * j + l] = (uint16_t)u.sl[j];
@@ -672,15 +689,32 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
                 for (int tt = 0; tt < 4; ++tt)
                     w[tt] = reinterpret_cast<const uint32_t *>(
                         &wtile[n * kMmaTileStride + 4 * h + tt])[kb];
-                // the step's four scales of row n (zero past G)
-                const uint2 s4 = *reinterpret_cast<const uint2 *>(&sblk[n * GU + 4 * p]);
-                uint32_t sc[4] = {s4.x & 0xFFFFu, s4.x >> 16, s4.y & 0xFFFFu, s4.y >> 16};
+                // the step's four scales of row n (zero past G), and the
+                // second contraction's operand for group gb + kb: its scale
+                // (AFF: its bias)
+                uint32_t sc[4], sk;
+                if (AFF) {
+                    const uint4 sb = *reinterpret_cast<const uint4 *>(
+                        &reinterpret_cast<const uint32_t *>(sblk)[n * GU + 4 * p]);
+                    sc[0] = sb.x & 0xFFFFu;
+                    sc[1] = sb.y & 0xFFFFu;
+                    sc[2] = sb.z & 0xFFFFu;
+                    sc[3] = sb.w & 0xFFFFu;
+                    const uint32_t bk = (kb & 2) ? ((kb & 1) ? sb.w : sb.z) : ((kb & 1) ? sb.y : sb.x);
+                    sk = gb + kb < G ? bk >> 16 : 0u;
+                } else {
+                    const uint2 s4 = *reinterpret_cast<const uint2 *>(&sblk[n * GU + 4 * p]);
+                    sc[0] = s4.x & 0xFFFFu;
+                    sc[1] = s4.x >> 16;
+                    sc[2] = s4.y & 0xFFFFu;
+                    sc[3] = s4.y >> 16;
+                    const uint32_t hs = (kb & 2) ? s4.y : s4.x;
+                    sk = gb + kb < G ? ((kb & 1) ? hs >> 16 : hs & 0xFFFFu) : 0u;
+                }
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt)
                     if (gb + tt >= G)
                         sc[tt] = 0u;
-                const uint32_t hs = (kb & 2) ? s4.y : s4.x;
-                const uint32_t sk = gb + kb < G ? ((kb & 1) ? hs >> 16 : hs & 0xFFFFu) : 0u;
                 acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, h2f((uint16_t)sk), acc0, 0, 0, 0);
                 floatx4 d[4];
 #pragma unroll
@@ -701,10 +735,11 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
                 asm volatile("" : "+v"(acc));
             }
         }
-        // this wave's part: 2^24 * code part - 7 * zero-point part
+        // this wave's part: 2^24 * code part - 7 * zero-point part (AFF:
+        // + bias part)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            acc[e] = fmaf(-7.0f, acc0[e], acc[e] * 0x1p24f);
+            acc[e] = fmaf(AFF ? 1.0f : -7.0f, acc0[e], acc[e] * 0x1p24f);
         // the KP parts of the tile meet in LDS slot r & 1 without a barrier:
         // each wave waits until the slot's previous use (round r - 2) has
         // been read, writes its part, and counts itself in; the last to
@@ -853,13 +888,13 @@ struct MmaPlan {
 
 constexpr size_t kMmaLdsLimit = 160 * 1024;
 
-MmaPlan mma_plan(int N, int K, int mt)
+MmaPlan mma_plan(int N, int K, int mt, bool aff)
 {
     MmaPlan pl;
     const int G = K / 32, ntiles = (N + 15) / 16;
     const int steps = (G + 3) / 4;  // steps of four groups over the whole of K
-    // (6 pairs with single scales, G odd, spill registers)
-    const int max_pairs = G % 2 == 0 ? kMmaMaxPairs : kMmaMaxPairs - 1;
+    // (6 pairs with single scales, G odd or affine, spill registers)
+    const int max_pairs = G % 2 == 0 && !aff ? kMmaMaxPairs : kMmaMaxPairs - 1;
     pl.blocks = std::min(cu_count(), ntiles);
     pl.KP = 0;
     pl.lds = SIZE_MAX;
@@ -868,7 +903,7 @@ MmaPlan mma_plan(int N, int K, int mt)
         const int sk2 = ((steps + c - 1) / c + 1) / 2;
         if (sk2 > max_pairs || (c > 1 && (c - 1) * 2 * sk2 >= steps))
             continue;  // a unit of too many steps, or an empty last part
-        const size_t lds = (size_t)kMmaWaves * mma_wave_lds(sk2) +
+        const size_t lds = (size_t)kMmaWaves * mma_wave_lds(sk2, aff) +
                            (size_t)2 * kMmaWaves * 256 * sizeof(float) +
                            (size_t)4 * kMmaWaves * sizeof(uint32_t) + (size_t)mt * (K + 8) * 2 +
                            (size_t)G * 16 * sizeof(float);
@@ -891,32 +926,39 @@ MmaPlan mma_plan(int N, int K, int mt)
 template <int SK2>
 q4_status run_mma(const MmaArgs &args, const MmaPlan &pl, hipStream_t stream)
 {
-    if (args.G % 2 == 0 && (reinterpret_cast<uintptr_t>(args.S) & 3) == 0)
-        Q4_LAUNCH_MATVEC((k_gemv_mma<SK2, true>), dim3(pl.blocks), dim3(64 * kMmaWaves), pl.lds,
-                         stream, args);
+    if (args.B)
+        Q4_LAUNCH_MATVEC((k_gemv_mma<SK2, false, true>), dim3(pl.blocks), dim3(64 * kMmaWaves),
+                         pl.lds, stream, args);
+    else if (args.G % 2 == 0 && (reinterpret_cast<uintptr_t>(args.S) & 3) == 0)
+        Q4_LAUNCH_MATVEC((k_gemv_mma<SK2, true, false>), dim3(pl.blocks), dim3(64 * kMmaWaves),
+                         pl.lds, stream, args);
     else
-        Q4_LAUNCH_MATVEC((k_gemv_mma<SK2, false>), dim3(pl.blocks), dim3(64 * kMmaWaves), pl.lds,
-                         stream, args);
+        Q4_LAUNCH_MATVEC((k_gemv_mma<SK2, false, false>), dim3(pl.blocks), dim3(64 * kMmaWaves),
+                         pl.lds, stream, args);
     return check_launch("k_gemv_mma");
 }
 }  // namespace
 
-bool mma_fits(int N, int K, int M) { return mma_plan(N, K, std::min(M, kMTile)).lds <= kMmaLdsLimit; }
+bool mma_fits(int N, int K, int M, bool aff)
+{
+    return mma_plan(N, K, std::min(M, kMTile), aff).lds <= kMmaLdsLimit;
+}
 
 int mma_blocks(int N) { return std::min(cu_count(), (N + 15) / 16); }
 
 q4_status launch_gemv_mma(const uint32_t *W, const uint16_t *S, const uint16_t *x, int64_t ldx,
                           uint16_t *y, float *yf, int64_t ldy, int N, int K, int M,
-                          hipStream_t stream, unsigned long long *cand)
+                          hipStream_t stream, unsigned long long *cand, const uint16_t *bias)
 {
     for (int m0 = 0; m0 < M; m0 += kMTile) {
         const int mt = std::min(kMTile, M - m0);
-        const MmaPlan pl = mma_plan(N, K, mt);
+        const MmaPlan pl = mma_plan(N, K, mt, bias != nullptr);
         if (pl.lds > kMmaLdsLimit)
             return fail(Q4_ERANGE, "internal: the batched matrix-core kernel does not fit K = %d", K);
         MmaArgs args;
         args.W = reinterpret_cast<const uint4 *>(W);
         args.S = S;
+        args.B = bias;
         args.x = x + m0 * ldx;
         args.ldx = ldx;
         args.y = yf ? nullptr : y + m0 * ldy;
@@ -944,8 +986,12 @@ q4_status launch_gemv_mma(const uint32_t *W, const uint16_t *S, const uint16_t *
 
 size_t ws_rows(int N, int K, int M)
 {
-    if (M <= 1 || gemv_rows_fits(M, K, N) || mma_fits(N, K, M) || mfma_splits(K) <= 1)
-        return 0;  // single-row, few-row and workgroup-reduced kernels, or no K split
+    // single-row, few-row and workgroup-reduced kernels, or no K split, for
+    // both formats (the affine call checks the few-row kernel without N, and
+    // its workgroup-reduced kernel needs more LDS)
+    if (M <= 1 || mfma_splits(K) <= 1 || mma_fits(N, K, M, true) ||
+        (gemv_rows_fits(M, K, N) && gemv_rows_fits(M, K)))
+        return 0;
     return kWsHeader + mfma_part_bytes(N, K);
 }
 
@@ -953,8 +999,8 @@ q4_status launch_gemv_mfma(const uint32_t *W, const uint16_t *S, const uint16_t 
                            uint16_t *y, float *yf, int64_t ldy, int N, int K, int M,
                            hipStream_t stream, const uint16_t *bias)
 {
-    if (!bias && mma_fits(N, K, M))
-        return launch_gemv_mma(W, S, x, ldx, y, yf, ldy, N, K, M, stream);
+    if (mma_fits(N, K, M, bias != nullptr))
+        return launch_gemv_mma(W, S, x, ldx, y, yf, ldy, N, K, M, stream, nullptr, bias);
     const int KS = mfma_splits(K);
     float *part = nullptr;
     if (KS > 1) {

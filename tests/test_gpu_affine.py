@@ -55,7 +55,8 @@ SHAPES = [("qwen3_qkv", 6144, 2560, 1), ("qwen3_gate_up", 19456, 2560, 1),
           ("qwen3_down", 2560, 9728, 1), ("ragged", 333, 640, 1), ("one_group", 5, 64, 1),
           ("qwen3_qkv", 6144, 2560, 8), ("qwen3_down", 2560, 9728, 2), ("ragged", 333, 640, 2),
           ("ragged", 333, 640, 17), ("one_group", 5, 64, 8), ("qwen3_qkv", 6144, 2560, 4),
-          ("qwen3_gate_up", 19456, 2560, 3)]
+          ("qwen3_gate_up", 19456, 2560, 3), ("qwen3_gate_up", 19456, 2560, 8),
+          ("qwen3_o", 2560, 4096, 8), ("qwen3_down", 2560, 9728, 4)]
 
 
 @pytest.mark.parametrize("name,n,k,m", SHAPES, ids=["%s-M%d" % (s[0], s[3]) for s in SHAPES])
