@@ -501,6 +501,7 @@ struct MmaArgs {
     unsigned long long *cand;
     int N, G, M;
     int KP, rounds;  // K parts, rounds
+    int NPH, KPH;    // K phases and groups per phase (one phase: 1 and G)
 };
 
 // LDS bytes of one wave's scale block (AFF: scale and bias per group, 4
@@ -510,7 +511,7 @@ constexpr int mma_wave_lds(int SK2, bool AFF = false)
     return 16 * 8 * SK2 * (AFF ? 4 : 2) + 16 * kMmaTileStride * 16;
 }
 
-template <int SK2, bool SP, bool AFF>
+template <int SK2, bool SP, bool AFF, bool PH>
 __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
 {
     static_assert(!(AFF && SP), "affine scales are loaded one per group");
@@ -522,15 +523,18 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
     constexpr bool kEarly = SK2 <= 3;
     extern __shared__ uint4 smem[];
     __shared__ unsigned long long s_cand[16];  // (cand) each row's largest key so far
-    const int G = a.G, K = G * 32, M = a.M, N = a.N;
-    const int xstride = K + 8;  // staged row: 16 bytes of padding against bank conflicts
+    const int G = a.G, M = a.M, N = a.N;
+    // PH: K in NPH phases of KPH groups, the activation staged one phase at a
+    // time (one round: each wave's unit accumulates over the phases)
+    const int KPH = PH ? a.KPH : G, NPH = PH ? a.NPH : 1;
+    const int xstride = KPH * 32 + 8;  // staged row: 16 bytes of padding against bank conflicts
     const int t = threadIdx.x, l = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int n = l & 15, kb = l >> 4;
     // LDS: per wave a scale block [16][GU] and a weight tile [16][9] x 16 B;
     // the waves' parts [2][kMmaWaves][64 lanes][4] f32; arrival counters and
     // use counts [2][kMmaWaves] u32 each; the staged rows [M][xstride]
-    // binary16; the group sums [G][16] f32
+    // binary16; the group sums [KPH][16] f32
     char *wbase = reinterpret_cast<char *>(smem) + (size_t)wave * mma_wave_lds(SK2, AFF);
     uint16_t *sblk = reinterpret_cast<uint16_t *>(wbase);  // AFF: uint32 (scale | bias << 16)
     uint4 *wtile = reinterpret_cast<uint4 *>(wbase + 16 * GU * (AFF ? 4 : 2));
@@ -546,15 +550,15 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
     const int ntiles = (N + 15) >> 4;
     // waves past tpr * KP (KP not dividing kMmaWaves) take no tiles
     const bool working = tslot < tpr;
-    const int gp0 = kp * GU;  // first group of this wave's part of K
+    const int gp0 = kp * GU;  // first group of this wave's part of K (of the phase)
     auto tile_of = [&](int r) { return (int)blockIdx.x + (int)gridDim.x * (tslot + tpr * r); };
 
-    // the loads of unit r (branch-free: groups past G re-read group G - 1 and
-    // are zeroed at use; rows past N re-read row N - 1; units past the last
-    // tile re-read the last tile and are not stored): its scales as elements
-    // e = 64 j + l of the row-major block [16][GU], then its weights, pair q
-    // and half i as lane l reading group gp0 + 8 q + (l & 7) of row 8 i +
-    // (l >> 3): 8 rows x 128 bytes per load
+    // the loads of unit r over groups [gbase, gend) (branch-free: groups past
+    // gend re-read group gend - 1 and are zeroed at use; rows past N re-read
+    // row N - 1): its scales as elements e = 64 j + l of the row-major block
+    // [16][GU], then its weights, pair q and half i as lane l reading group
+    // gbase + gp0 + 8 q + (l & 7) of row 8 i + (l >> 3): 8 rows x 128 bytes
+    // per load
     // (SP, G even: the scales in pairs, elements 2 (64 j + l) and the next, one
     // 4-byte load each: a pair never straddles a row and is 4-byte aligned;
     // AFF: element e holds its 64-value group's scale and bias, s | b << 16)
@@ -563,7 +567,7 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
         uint32_t sl[NSL];
         uint4 wl[SK2][2];
     };
-    auto load_unit = [&](int r, Unit &u) __attribute__((always_inline)) {
+    auto load_unit = [&](int r, Unit &u, int gbase, int gend) __attribute__((always_inline)) {
         const int row0 = min(tile_of(r), ntiles - 1) * 16;
 #pragma unroll
         for (int j = 0; j < NSL; ++j) {
@@ -571,11 +575,12 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
             const int rr = e / GU, cc = e - rr * GU;
             if (AFF) {
                 const size_t off = (size_t)min(row0 + rr, N - 1) * (G >> 1) +
-                                   (min(gp0 + cc, G - 1) >> 1);
+                                   (min(gbase + gp0 + cc, gend - 1) >> 1);
                 u.sl[j] = load_scale(a.S + off) | (load_scale(a.B + off) << 16);
                 continue;
             }
-            const size_t off = (size_t)min(row0 + rr, N - 1) * G + min(gp0 + cc, G - (SP ? 2 : 1));
+            const size_t off = (size_t)min(row0 + rr, N - 1) * G +
+                               min(gbase + gp0 + cc, gend - (SP ? 2 : 1));
             if (SP)
                 u.sl[j] = __builtin_nontemporal_load(
                     (__attribute__((address_space(1))) const uint32_t *)(a.S + off));
@@ -587,18 +592,21 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int rr = min(row0 + 8 * i + (l >> 3), N - 1);
-                u.wl[q][i] = load_weights(a.W + (size_t)rr * G + min(gp0 + 8 * q + (l & 7), G - 1));
+                u.wl[q][i] = load_weights(a.W + (size_t)rr * G +
+                                          min(gbase + gp0 + 8 * q + (l & 7), gend - 1));
             }
     };
 
-    // 1. the activation's chunks (up to kMmaXq per thread) into registers,
-    //    then into LDS: the pair order, the odd positions x1 x3 x5 x7 (the high halves of the words,
-    //    which meet the 2^-20 pairs) divided by 16, and each group's sum of the
-    //    unscaled values (a quad of lanes holds the four chunks of a group: cpr
-    //    and the thread count are multiples of 4, so quads never mix rows)
+    // 1. the activation's chunks of groups [gbase, gend) (up to kMmaXq per
+    //    thread) into registers, then into LDS: the pair order, the odd
+    //    positions x1 x3 x5 x7 (the high halves of the words, which meet the
+    //    2^-20 pairs) divided by 16, and each group's sum of the unscaled
+    //    values (a quad of lanes holds the four chunks of a group: cpr and the
+    //    thread count are multiples of 4, so quads never mix rows). early: the
+    //    first unit's loads go out between the two.
     Unit ua;
-    {
-        const int cpr = K >> 3;
+    auto stage_x = [&](int gbase, int gend, bool early) __attribute__((always_inline)) {
+        const int cpr = (gend - gbase) * 4;
         const int total = M * cpr;  // a multiple of 4
         constexpr int kThreads = 64 * kMmaWaves;
         const half2v odd16 = {(_Float16)1.0f, (_Float16)0.0625f};
@@ -607,7 +615,7 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
             // a quad past the end re-reads the last group and stores nothing
             const int cc = c < total ? c : total - 4 + (c & 3);
             const int m = cc / cpr, j = cc - m * cpr;
-            return *reinterpret_cast<const u32x4 *>(a.x + m * a.ldx + 8 * j);
+            return *reinterpret_cast<const u32x4 *>(a.x + m * a.ldx + 8 * (4 * gbase + j));
         };
         auto stage = [&](int c, u32x4 v) __attribute__((always_inline)) {
             const bool live = c < total;
@@ -635,8 +643,8 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
         for (int i = 0; i < kMmaXq; ++i)
             if (i < xq)
                 xr[i] = chunk(i * kThreads + t);
-        if (kEarly)
-            load_unit(0, ua);
+        if (early)
+            load_unit(0, ua, gbase, gend);
 #pragma unroll
         for (int i = 0; i < kMmaXq; ++i)
             if (i < xq)
@@ -644,19 +652,26 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
         // more chunks than the registers hold: the rest one by one
         for (int c0 = kMmaXq * kThreads; c0 < total; c0 += kThreads)
             stage(c0 + t, chunk(c0 + t));
-    }
+    };
+    if (!PH)
+        stage_x(0, G, kEarly);
     if (t < 4 * kMmaWaves)
         arrived[t] = 0u;  // and uses[]
     if (t < 16)
         s_cand[t] = 0ull;
-    __syncthreads();
+    if (!PH)
+        __syncthreads();
 
     // 2. the rounds: each unit issues all of its loads, then computes
     unsigned long long best[4] = {0ull, 0ull, 0ull, 0ull};  // (cand) rows 4 kb + e
     const int mrow = min(n, M - 1);  // A row m = n
     const _Float16 *xrow = xs + mrow * xstride + 8 * kb;
     const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
-    auto compute_unit = [&](int r, const Unit &u) __attribute__((always_inline)) {
+    // the unit's products over groups [gbase, gend) (the staged activation's
+    // first group is gbase) added to acc (code part) and acc0 (second
+    // contraction)
+    auto accumulate = [&](const Unit &u, floatx4 &acc, floatx4 &acc0, int gbase, int gend)
+                          __attribute__((always_inline)) {
         // the scales into the wave's block (a wave's LDS accesses complete in
         // order: the previous unit's reads are done)
 #pragma unroll
@@ -666,7 +681,6 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
             else
                 sblk[64 * j + l] = (uint16_t)u.sl[j];
         }
-        floatx4 acc = zero, acc0 = zero;
 #pragma unroll
         for (int q = 0; q < SK2; ++q) {
             // the pair's weights into the wave's tile: row 8 i + (l >> 3), slot
@@ -677,12 +691,13 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int p = 2 * q + h;
-                const int gb = gp0 + 4 * p;  // the step's first group (uniform)
+                const int gb = gbase + gp0 + 4 * p;  // the step's first group (uniform)
                 half8 av[4];
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt)
-                    av[tt] = *reinterpret_cast<const half8 *>(xrow + min(gb + tt, G - 1) * 32);
-                const float a0 = xsum[min(gb + kb, G - 1) * 16 + mrow];
+                    av[tt] = *reinterpret_cast<const half8 *>(
+                        xrow + (min(gb + tt, gend - 1) - gbase) * 32);
+                const float a0 = xsum[(min(gb + kb, gend - 1) - gbase) * 16 + mrow];
                 // word kb of group 4 h + tt of row n
                 uint32_t w[4];
 #pragma unroll
@@ -701,7 +716,7 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
                     sc[2] = sb.z & 0xFFFFu;
                     sc[3] = sb.w & 0xFFFFu;
                     const uint32_t bk = (kb & 2) ? ((kb & 1) ? sb.w : sb.z) : ((kb & 1) ? sb.y : sb.x);
-                    sk = gb + kb < G ? bk >> 16 : 0u;
+                    sk = gb + kb < gend ? bk >> 16 : 0u;
                 } else {
                     const uint2 s4 = *reinterpret_cast<const uint2 *>(&sblk[n * GU + 4 * p]);
                     sc[0] = s4.x & 0xFFFFu;
@@ -709,11 +724,11 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
                     sc[2] = s4.y & 0xFFFFu;
                     sc[3] = s4.y >> 16;
                     const uint32_t hs = (kb & 2) ? s4.y : s4.x;
-                    sk = gb + kb < G ? ((kb & 1) ? hs >> 16 : hs & 0xFFFFu) : 0u;
+                    sk = gb + kb < gend ? ((kb & 1) ? hs >> 16 : hs & 0xFFFFu) : 0u;
                 }
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt)
-                    if (gb + tt >= G)
+                    if (gb + tt >= gend)
                         sc[tt] = 0u;
                 acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, h2f((uint16_t)sk), acc0, 0, 0, 0);
                 floatx4 d[4];
@@ -735,6 +750,9 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
                 asm volatile("" : "+v"(acc));
             }
         }
+    };
+    // the wave's part of tile_of(r) from its sums, then the meeting and store
+    auto finish = [&](int r, floatx4 acc, const floatx4 &acc0) __attribute__((always_inline)) {
         // this wave's part: 2^24 * code part - 7 * zero-point part (AFF:
         // + bias part)
 #pragma unroll
@@ -800,15 +818,37 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
                 }
         }
     };
-    for (int r = 0; working && r < rounds; ++r) {
-        // tiles grow with the round: a wave stops at its first tile past the
-        // last, and every wave of its tile slot (the KP parts that meet in
-        // LDS) stops at the same round
-        if (tile_of(r) >= ntiles)
-            break;
-        if (!kEarly || r > 0)
-            load_unit(r, ua);
-        compute_unit(r, ua);
+    if (!PH) {
+        for (int r = 0; working && r < rounds; ++r) {
+            // tiles grow with the round: a wave stops at its first tile past
+            // the last, and every wave of its tile slot (the KP parts that
+            // meet in LDS) stops at the same round
+            if (tile_of(r) >= ntiles)
+                break;
+            if (!kEarly || r > 0)
+                load_unit(r, ua, 0, G);
+            floatx4 acc = zero, acc0 = zero;
+            accumulate(ua, acc, acc0, 0, G);
+            finish(r, acc, acc0);
+        }
+    } else {
+        // one round; every wave takes part in each phase's staging and barriers
+        const bool mine = working && tile_of(0) < ntiles;
+        floatx4 acc = zero, acc0 = zero;
+        for (int ph = 0; ph < NPH; ++ph) {
+            const int gbase = ph * KPH, gend = min(G, gbase + KPH);
+            if (ph > 0)
+                __syncthreads();  // the previous phase's activation reads are done
+            stage_x(gbase, gend, kEarly && mine);
+            __syncthreads();
+            if (mine) {
+                if (!kEarly)
+                    load_unit(0, ua, gbase, gend);
+                accumulate(ua, acc, acc0, gbase, gend);
+            }
+        }
+        if (mine)
+            finish(0, acc, acc0);
     }
     if (a.cand) {
         // the lane row's largest keys over its 16 lanes (rows 4 kb + e), into
@@ -883,58 +923,72 @@ namespace {
 // when no part count fits.
 struct MmaPlan {
     int KP, SK2, rounds, blocks;
+    int NPH, KPH;  // K phases (the activation staged one phase at a time) and groups per phase
     size_t lds;
 };
 
 constexpr size_t kMmaLdsLimit = 160 * 1024;
+constexpr int kMmaMaxPhases = 4;
 
 MmaPlan mma_plan(int N, int K, int mt, bool aff)
 {
     MmaPlan pl;
     const int G = K / 32, ntiles = (N + 15) / 16;
-    const int steps = (G + 3) / 4;  // steps of four groups over the whole of K
     // (6 pairs with single scales, G odd or affine, spill registers)
     const int max_pairs = G % 2 == 0 && !aff ? kMmaMaxPairs : kMmaMaxPairs - 1;
     pl.blocks = std::min(cu_count(), ntiles);
     pl.KP = 0;
     pl.lds = SIZE_MAX;
-    int64_t best_work = 0;
-    for (int c = 1; c <= kMmaWaves; ++c) {
-        const int sk2 = ((steps + c - 1) / c + 1) / 2;
-        if (sk2 > max_pairs || (c > 1 && (c - 1) * 2 * sk2 >= steps))
-            continue;  // a unit of too many steps, or an empty last part
-        const size_t lds = (size_t)kMmaWaves * mma_wave_lds(sk2, aff) +
-                           (size_t)2 * kMmaWaves * 256 * sizeof(float) +
-                           (size_t)4 * kMmaWaves * sizeof(uint32_t) + (size_t)mt * (K + 8) * 2 +
-                           (size_t)G * 16 * sizeof(float);
-        if (lds > kMmaLdsLimit)
-            continue;
-        const int tpr = kMmaWaves / c;
-        const int rounds = (ntiles + pl.blocks * tpr - 1) / (pl.blocks * tpr);
-        const int64_t work = (int64_t)tpr * c * rounds * 2 * sk2;
-        if (!pl.KP || rounds < pl.rounds || (rounds == pl.rounds && work < best_work)) {
-            pl.KP = c;
-            pl.SK2 = sk2;
-            pl.rounds = rounds;
-            pl.lds = lds;
-            best_work = work;
+    // the fewest K phases that fit the CU's LDS (several phases only with one
+    // round: a wave's unit then accumulates over the phases)
+    for (int nph = 1; nph <= kMmaMaxPhases && !pl.KP; ++nph) {
+        int kph = (G + nph - 1) / nph;
+        kph += nph > 1 ? (kph & 1) : 0;  // even: pairs of scales stay in one phase
+        if (nph > 1 && (int64_t)kph * (nph - 1) >= G)
+            break;  // the last phase would be empty
+        const int steps = (kph + 3) / 4;  // steps of four groups over a phase
+        int64_t best_work = 0;
+        for (int c = 1; c <= kMmaWaves; ++c) {
+            const int sk2 = ((steps + c - 1) / c + 1) / 2;
+            if (sk2 > max_pairs || (c > 1 && (c - 1) * 2 * sk2 >= steps))
+                continue;  // a unit of too many steps, or an empty last part
+            const size_t lds = (size_t)kMmaWaves * mma_wave_lds(sk2, aff) +
+                               (size_t)2 * kMmaWaves * 256 * sizeof(float) +
+                               (size_t)4 * kMmaWaves * sizeof(uint32_t) +
+                               (size_t)mt * (kph * 32 + 8) * 2 + (size_t)kph * 16 * sizeof(float);
+            if (lds > kMmaLdsLimit)
+                continue;
+            const int tpr = kMmaWaves / c;
+            const int rounds = (ntiles + pl.blocks * tpr - 1) / (pl.blocks * tpr);
+            if (nph > 1 && rounds > 1)
+                continue;
+            const int64_t work = (int64_t)tpr * c * rounds * 2 * sk2;
+            if (!pl.KP || rounds < pl.rounds || (rounds == pl.rounds && work < best_work)) {
+                pl.KP = c;
+                pl.SK2 = sk2;
+                pl.rounds = rounds;
+                pl.NPH = nph;
+                pl.KPH = kph;
+                pl.lds = lds;
+                best_work = work;
+            }
         }
     }
     return pl;
 }
 
-template <int SK2>
+template <int SK2, bool PH>
 q4_status run_mma(const MmaArgs &args, const MmaPlan &pl, hipStream_t stream)
 {
     if (args.B)
-        Q4_LAUNCH_MATVEC((k_gemv_mma<SK2, false, true>), dim3(pl.blocks), dim3(64 * kMmaWaves),
-                         pl.lds, stream, args);
+        Q4_LAUNCH_MATVEC((k_gemv_mma<SK2, false, true, PH>), dim3(pl.blocks),
+                         dim3(64 * kMmaWaves), pl.lds, stream, args);
     else if (args.G % 2 == 0 && (reinterpret_cast<uintptr_t>(args.S) & 3) == 0)
-        Q4_LAUNCH_MATVEC((k_gemv_mma<SK2, true, false>), dim3(pl.blocks), dim3(64 * kMmaWaves),
-                         pl.lds, stream, args);
+        Q4_LAUNCH_MATVEC((k_gemv_mma<SK2, true, false, PH>), dim3(pl.blocks),
+                         dim3(64 * kMmaWaves), pl.lds, stream, args);
     else
-        Q4_LAUNCH_MATVEC((k_gemv_mma<SK2, false, false>), dim3(pl.blocks), dim3(64 * kMmaWaves),
-                         pl.lds, stream, args);
+        Q4_LAUNCH_MATVEC((k_gemv_mma<SK2, false, false, PH>), dim3(pl.blocks),
+                         dim3(64 * kMmaWaves), pl.lds, stream, args);
     return check_launch("k_gemv_mma");
 }
 }  // namespace
@@ -970,10 +1024,14 @@ q4_status launch_gemv_mma(const uint32_t *W, const uint16_t *S, const uint16_t *
         args.M = mt;
         args.KP = pl.KP;
         args.rounds = pl.rounds;
+        args.NPH = pl.NPH;
+        args.KPH = pl.KPH;
         q4_status st;
         switch (pl.SK2) {
 #define Q4_MMA_CASE(d)                                                                            \
-    case d: st = run_mma<d>(args, pl, stream); break;
+    case d:                                                                                       \
+        st = pl.NPH > 1 ? run_mma<d, true>(args, pl, stream) : run_mma<d, false>(args, pl, stream); \
+        break;
             Q4_MMA_CASE(1) Q4_MMA_CASE(2) Q4_MMA_CASE(3) Q4_MMA_CASE(4) Q4_MMA_CASE(5) Q4_MMA_CASE(6)
 #undef Q4_MMA_CASE
         default: return fail(Q4_ERANGE, "internal: %d step pairs for the batched matrix-core kernel", pl.SK2);
