@@ -462,8 +462,8 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ part,
 // the tiles blockIdx.x + gridDim.x * (w / KP + (kMmaWaves / KP) * round), one
 // unit per round (waves from (kMmaWaves / KP) * KP on, when KP does not
 // divide kMmaWaves, take none). A wave issues all loads of a unit at once, in
-// whole memory lines: the unit's scales as a row-major block (64 consecutive scales, or
-// pairs of them, per load), then its weights as 8 rows x 128 bytes per load
+// whole memory lines: the unit's scales as a row-major block (64 consecutive
+// scales, or pairs of them, per load), then its weights as 8 rows x 128 bytes per load
 // (a pair of steps per two loads). The scales go to a per-wave LDS block, each
 // pair of steps' weights to a per-wave LDS tile from which every lane reads
 // the words of its MFMA lane (word kb of each group of row n): no exchanges
@@ -472,7 +472,11 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ part,
 // overlap another's arithmetic: the last of the KP waves to arrive (an LDS
 // counter) adds the parts in K order, stores, and frees the slot for its use
 // two rounds later. A wave stops at its first tile past the last one; the KP
-// waves of a tile slot share their tiles, so they stop together.
+// waves of a tile slot share their tiles, so they stop together. Where the
+// staged rows of the whole of K exceed the LDS (PH), the launch has one round
+// and K runs in NPH phases of KPH groups: the workgroup stages one phase's
+// activation at a time (a barrier before each restaging), and each wave adds
+// its part of every phase into the same sums before the parts meet.
 constexpr int kMmaWaves = 12;   // three waves per SIMD
 constexpr int kMmaMaxPairs = 6;  // steps per unit <= 12 (7 pairs spill registers)
 constexpr int kMmaXq = 8;       // activation chunks per thread held in registers
