@@ -87,9 +87,9 @@ __device__ __forceinline__ void fma8(float (&o)[8], float p, uint4 w)
 }
 
 // Workgroup (head, split): partial softmax state of the split's positions,
-// in blocks of PB positions (256, or 64 where every split is at most 64
-// positions long: the value phase then loads and adds only a quarter of the
-// chunks; the positions dropped are those past the block, whose weight is 0).
+// in blocks of PB positions (256, or 64 or 128 where every split is at most
+// that long: the value phase then loads and adds only the chunks of those
+// positions; the ones it drops are past the block, with weight 0).
 // part layout: [n_heads][splits][2 + head_dim] = (max, sum, weighted values).
 // NC = head_dim / 8 (16-byte chunks of a cache row).
 template <int NC, int PB>
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(const uint16_t *__restric
                                                        uint16_t *__restrict__ out)
 {
     constexpr int D = 8 * NC;
-    static_assert(PB == 64 || PB == kAttnThreads, "positions per block");
+    static_assert(PB == 64 || PB == 128 || PB == kAttnThreads, "positions per block");
     constexpr int groups = kAttnThreads / NC;      // position groups of the value phase
     constexpr int U = (PB + groups - 1) / groups;  // positions per value thread
     __shared__ float qs[D];
@@ -296,17 +296,20 @@ q4_status launch_attention(const uint16_t *q, const uint16_t *kv, const RopeArgs
         part = reinterpret_cast<float *>(ws + kWsHeader);
     }
     const dim3 grid(r.n_heads, NS);
-    // blocks of 64 positions where no split can be longer (the bound on the
-    // position count gives the longest split; the kernel loops over blocks
+    // blocks of 64 or 128 positions where no split can be longer (the bound on
+    // the position count gives the longest split; the kernel loops over blocks
     // either way)
     const int64_t len = std::max<int64_t>(1, std::min<int64_t>(max_len, (int64_t)r.max_pages * r.page_size));
     const int64_t pieces = (len + kSplitGrain - 1) / kSplitGrain;
-    const bool short_splits = kSplitGrain * ((pieces + NS - 1) / NS) <= 64;
+    const int64_t longest = kSplitGrain * ((pieces + NS - 1) / NS);
     switch (r.head_dim / 8) {
 #define Q4_ATTN_CASE(nc)                                                                          \
     case nc:                                                                                      \
-        if (short_splits)                                                                         \
+        if (longest <= 64)                                                                        \
             hipLaunchKernelGGL((k_attn<nc, 64>), grid, dim3(kAttnThreads), 0, stream, q, kv, r,   \
+                               scale, part, out);                                                 \
+        else if (longest <= 128)                                                                  \
+            hipLaunchKernelGGL((k_attn<nc, 128>), grid, dim3(kAttnThreads), 0, stream, q, kv, r,  \
                                scale, part, out);                                                 \
         else                                                                                      \
             hipLaunchKernelGGL((k_attn<nc, kAttnThreads>), grid, dim3(kAttnThreads), 0, stream, q, \

@@ -126,8 +126,8 @@ def fill_cache(q4, d, seed, L, table):
 
 @pytest.mark.parametrize("geom,L,max_len", [
     ("phi3", 1, 1), ("phi3", 2, 2), ("phi3", 17, 17), ("phi3", 256, 256), ("phi3", 257, 257),
-    ("phi3", 1000, 1000), ("phi3", 4112, 4112), ("phi3", 10, 4112), ("gqa", 300, 300),
-    ("gqa", 2048, 2048)])
+    ("phi3", 1000, 1000), ("phi3", 2000, 2000), ("phi3", 4112, 4112), ("phi3", 10, 4112),
+    ("gqa", 300, 300), ("gqa", 2048, 2048)])
 def test_attention_vs_oracle(o, q4, geom, L, max_len):
     g = PHI3 if geom == "phi3" else GQA
     nh, nkv, hd = g["n_heads"], g["n_kv"], g["head_dim"]
@@ -162,19 +162,21 @@ def test_attention_skips_pages_outside_the_table(o, q4):
     assert_within(host(over), o.attention(q, kc, vc, nh, nh, hd), "clamped position")
 
 
-def test_attention_walks_blocks_when_the_position_passes_its_bound(o, q4):
-    """max_len = 64 sizes one split of one 64-position block, but *pos + 1 =
-    300: the workgroup walks five blocks with the running softmax and still
-    attends over every cached position."""
+@pytest.mark.parametrize("bound", [64, 128])
+def test_attention_walks_blocks_when_the_position_passes_its_bound(o, q4, bound):
+    """max_len = 64 (or 128) sizes one split of one 64-position (128-position)
+    block, but *pos + 1 = 300: the workgroup walks several blocks with the
+    running softmax and still attends over every cached position."""
     g = PHI3
     nh, hd = g["n_heads"], g["head_dim"]
     d = desc_for(q4, g)
     table = np.random.default_rng(64).permutation(257).astype(np.int32)
     kv, kc, vc = fill_cache(q4, d, 970, 300, table)
     q = datagen.activations(971, 1, nh * hd)[0]
-    out = q4.attention_decode(dev_tensor(q), kv, i32(table), i32([299]), 64, d)
+    out = q4.attention_decode(dev_tensor(q), kv, i32(table), i32([299]), bound, d)
     sync()
-    assert_within(host(out), o.attention(q, kc, vc, nh, nh, hd), "300 positions, bound 64")
+    assert_within(host(out), o.attention(q, kc, vc, nh, nh, hd),
+                  "300 positions, bound %d" % bound)
 
 
 def test_decode_loop_append_then_attend(o, q4):
