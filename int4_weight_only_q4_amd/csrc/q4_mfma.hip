@@ -601,72 +601,8 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
             }
     };
 
-    // 1. the activation's chunks of groups [gbase, gend) (up to kMmaXq per
-    //    thread) into registers, then into LDS: the pair order, the odd
-    //    positions x1 x3 x5 x7 (the high halves of the words, which meet the
-    //    2^-20 pairs) divided by 16, and each group's sum of the unscaled
-    //    values (a quad of lanes holds the four chunks of a group: cpr and the
-    //    thread count are multiples of 4, so quads never mix rows). early: the
-    //    first unit's loads go out between the two.
     Unit ua;
-    auto stage_x = [&](int gbase, int gend, bool early) __attribute__((always_inline)) {
-        const int cpr = (gend - gbase) * 4;
-        const int total = M * cpr;  // a multiple of 4
-        constexpr int kThreads = 64 * kMmaWaves;
-        const half2v odd16 = {(_Float16)1.0f, (_Float16)0.0625f};
-        const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
-        auto chunk = [&](int c) __attribute__((always_inline)) {
-            // a quad past the end re-reads the last group and stores nothing
-            const int cc = c < total ? c : total - 4 + (c & 3);
-            const int m = cc / cpr, j = cc - m * cpr;
-            return *reinterpret_cast<const u32x4 *>(a.x + m * a.ldx + 8 * (4 * gbase + j));
-        };
-        auto stage = [&](int c, u32x4 v) __attribute__((always_inline)) {
-            const bool live = c < total;
-            const int cc = live ? c : total - 4 + (c & 3);
-            const int m = cc / cpr, j = cc - m * cpr;
-            float sum = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                // through a scalar: this compiler's bit_cast of a vector
-                // element reads element 0
-                const uint32_t h = v[e];
-                sum = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, h), ones, sum, false);
-                v[e] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, h) * odd16);
-            }
-            sum = quad_sum(sum);
-            if (live) {
-                *reinterpret_cast<u32x4 *>(xs + m * xstride + 8 * j) = pair_order(v);
-                if ((j & 3) == 0)
-                    xsum[(j >> 2) * 16 + m] = sum;
-            }
-        };
-        const int xq = min((total + kThreads - 1) / kThreads, kMmaXq);  // uniform
-        u32x4 xr[kMmaXq];
-#pragma unroll
-        for (int i = 0; i < kMmaXq; ++i)
-            if (i < xq)
-                xr[i] = chunk(i * kThreads + t);
-        if (early)
-            load_unit(0, ua, gbase, gend);
-#pragma unroll
-        for (int i = 0; i < kMmaXq; ++i)
-            if (i < xq)
-                stage(i * kThreads + t, xr[i]);
-        // more chunks than the registers hold: the rest one by one
-        for (int c0 = kMmaXq * kThreads; c0 < total; c0 += kThreads)
-            stage(c0 + t, chunk(c0 + t));
-    };
-    if (!PH)
-        stage_x(0, G, kEarly);
-    if (t < 4 * kMmaWaves)
-        arrived[t] = 0u;  // and uses[]
-    if (t < 16)
-        s_cand[t] = 0ull;
-    if (!PH)
-        __syncthreads();
-
-    // 2. the rounds: each unit issues all of its loads, then computes
+    // 2. the units' arithmetic (the rounds follow the staging below)
     unsigned long long best[4] = {0ull, 0ull, 0ull, 0ull};  // (cand) rows 4 kb + e
     const int mrow = min(n, M - 1);  // A row m = n
     const _Float16 *xrow = xs + mrow * xstride + 8 * kb;
@@ -822,6 +758,85 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
                 }
         }
     };
+    // 3. the activation's chunks of groups [gbase, gend) (up to kMmaXq per
+    //    thread) into registers, then into LDS: the pair order, the odd
+    //    positions x1 x3 x5 x7 (the high halves of the words, which meet the
+    //    2^-20 pairs) divided by 16, and each group's sum of the unscaled
+    //    values (a quad of lanes holds the four chunks of a group: cpr and the
+    //    thread count are multiples of 4, so quads never mix rows). early: the
+    //    first unit's loads go out between the two.
+    //    Staged once (PH: phase by phase, each wave adding its unit's part of
+    //    the phase into pacc / pacc0), then the rounds.
+    const bool mine = PH && working && tile_of(0) < ntiles;  // PH: one round
+    floatx4 pacc = zero, pacc0 = zero;
+    for (int ph = 0; ph < NPH; ++ph) {
+        const int gbase = ph * KPH, gend = min(G, gbase + KPH);
+        if (ph > 0)
+            __syncthreads();  // the previous phase's activation reads are done
+        {
+            const int cpr = (gend - gbase) * 4;
+            const int total = M * cpr;  // a multiple of 4
+            constexpr int kThreads = 64 * kMmaWaves;
+            const half2v odd16 = {(_Float16)1.0f, (_Float16)0.0625f};
+            const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
+            auto chunk = [&](int c) __attribute__((always_inline)) {
+                // a quad past the end re-reads the last group and stores nothing
+                const int cc = c < total ? c : total - 4 + (c & 3);
+                const int m = cc / cpr, j = cc - m * cpr;
+                return *reinterpret_cast<const u32x4 *>(a.x + m * a.ldx + 8 * (4 * gbase + j));
+            };
+            auto stage = [&](int c, u32x4 v) __attribute__((always_inline)) {
+                const bool live = c < total;
+                const int cc = live ? c : total - 4 + (c & 3);
+                const int m = cc / cpr, j = cc - m * cpr;
+                float sum = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // through a scalar: this compiler's bit_cast of a vector
+                    // element reads element 0
+                    const uint32_t h = v[e];
+                    sum = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, h), ones, sum, false);
+                    v[e] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, h) * odd16);
+                }
+                sum = quad_sum(sum);
+                if (live) {
+                    *reinterpret_cast<u32x4 *>(xs + m * xstride + 8 * j) = pair_order(v);
+                    if ((j & 3) == 0)
+                        xsum[(j >> 2) * 16 + m] = sum;
+                }
+            };
+            const int xq = min((total + kThreads - 1) / kThreads, kMmaXq);  // uniform
+            u32x4 xr[kMmaXq];
+            // PH: every register chunk is loaded (those past the end re-read
+            // the last quad): loads under the uniform guard, in the phase
+            // loop, leave the compiler waiting on each before the next issues
+#pragma unroll
+            for (int i = 0; i < kMmaXq; ++i)
+                if (PH || i < xq)
+                    xr[i] = chunk(i * kThreads + t);
+            if (PH ? kEarly && mine : kEarly)
+                load_unit(0, ua, gbase, gend);
+#pragma unroll
+            for (int i = 0; i < kMmaXq; ++i)
+                if (i < xq)
+                    stage(i * kThreads + t, xr[i]);
+            // more chunks than the registers hold: the rest one by one
+            for (int c0 = kMmaXq * kThreads; c0 < total; c0 += kThreads)
+                stage(c0 + t, chunk(c0 + t));
+        }
+        if (ph == 0) {
+            if (t < 4 * kMmaWaves)
+                arrived[t] = 0u;  // and uses[]
+            if (t < 16)
+                s_cand[t] = 0ull;
+        }
+        __syncthreads();
+        if (mine) {
+            if (!kEarly)
+                load_unit(0, ua, gbase, gend);
+            accumulate(ua, pacc, pacc0, gbase, gend);
+        }
+    }
     if (!PH) {
         for (int r = 0; working && r < rounds; ++r) {
             // tiles grow with the round: a wave stops at its first tile past
@@ -835,24 +850,8 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
             accumulate(ua, acc, acc0, 0, G);
             finish(r, acc, acc0);
         }
-    } else {
-        // one round; every wave takes part in each phase's staging and barriers
-        const bool mine = working && tile_of(0) < ntiles;
-        floatx4 acc = zero, acc0 = zero;
-        for (int ph = 0; ph < NPH; ++ph) {
-            const int gbase = ph * KPH, gend = min(G, gbase + KPH);
-            if (ph > 0)
-                __syncthreads();  // the previous phase's activation reads are done
-            stage_x(gbase, gend, kEarly && mine);
-            __syncthreads();
-            if (mine) {
-                if (!kEarly)
-                    load_unit(0, ua, gbase, gend);
-                accumulate(ua, acc, acc0, gbase, gend);
-            }
-        }
-        if (mine)
-            finish(0, acc, acc0);
+    } else if (mine) {
+        finish(0, pacc, pacc0);
     }
     if (a.cand) {
         // the lane row's largest keys over its 16 lanes (rows 4 kb + e), into
