@@ -259,6 +259,138 @@ def committed_traffic():
     return None
 
 
+STACK_TRACE_PROFILE = os.path.join(ROOT, "profiles", "kernel_trace_phi3_stack_decode.md")
+DOMINANT_KERNEL = "k_gemv<32, 3, 2, 1, 1, false>"  # gate_up: RMSNorm prologue, SiLU epilogue
+DOMINANT_REPS = 3  # passes of time_dominant_kernel over the layers' gate_up weights
+STACK_KERNEL_ROLES = {
+    DOMINANT_KERNEL: "gate_up 16384x3072, RMSNorm prologue + SiLU-multiply epilogue",
+    "k_gemv<32, 3, 2, 0, 1, false>": "QKV 9216x3072, RMSNorm prologue (layers 1..31)",
+    "k_gemv<64, 4, 1, 2, 0, false>": "down 3072x8192, residual-add epilogue",
+    "k_gemv<32, 3, 1, 2, 0, false>": "O 3072x3072, residual-add epilogue",
+    "k_gemv<32, 3, 2, 0, 0, false>": "QKV 9216x3072 (layer 0, given h)",
+    "k_add_rmsnorm_vec<2>": "final RMSNorm (and the trace norms of the parity check)",
+}
+
+
+def summarize_trace(trace_csv, status):
+    """The per-kernel summary of a rocprofv3 kernel trace of `bench.py
+    --no-cpu-baseline`, and the dominant kernel's mean dispatch duration inside
+    the stack's tokens (every gate_up dispatch but the timing loop's last ones)
+    against the timing loop's, written to STACK_TRACE_PROFILE with the hash of
+    the kernel's sources."""
+    import csv
+    with open(trace_csv, newline="") as fh:
+        rows = sorted(csv.DictReader(fh), key=lambda r: int(r["Start_Timestamp"]))
+
+    def name(r):
+        return r["Kernel_Name"].replace("void ", "").replace(
+            "q4::(anonymous namespace)::", "").split("(")[0]
+
+    def dur(r):
+        return (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+
+    p = PHI3
+    per = {}
+    for r in rows:
+        per.setdefault(name(r), []).append(dur(r))
+    gu = per.get(DOMINANT_KERNEL, [])
+    loop_n = DOMINANT_REPS * p["layers"]
+    if len(gu) <= loop_n:
+        raise SystemExit("the trace holds %d dispatches of %s, not the stack's and the "
+                         "timing loop's" % (len(gu), DOMINANT_KERNEL))
+    bytes_per_launch = int(2 * p["f"] * p["d"] * BPW)
+
+    def gbs(us):
+        return bytes_per_launch / (us * 1e-6) / 1e9
+
+    stack_us = float(np.mean(gu[:-loop_n]))
+    loop_us = float(np.mean(gu[-loop_n:]))
+    rec = dict(source_hash=kernel_source_hash(), kernel=DOMINANT_KERNEL,
+               bytes_per_launch=bytes_per_launch,
+               in_stack_dispatches=len(gu) - loop_n, in_stack_us=round(stack_us, 3),
+               loop_dispatches=loop_n, loop_us=round(loop_us, 3), profiled_status=int(status))
+    text = [
+        "# Kernel trace: Phi-3-mini-shaped 32-layer int4 decode stack, batch 1 (bench.py)",
+        "",
+        "Commands (from the repository root, on one MI355X; OUT: an output directory; the "
+        "summary from the trace CSV):",
+        "",
+        "```",
+        "export REPO=$PWD && cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats "
+        "--output-format csv -d $OUT/prof_bench -o bench -- python3 $REPO/bench.py "
+        "--no-cpu-baseline; echo $?",
+        "python3 bench.py --summarize-trace $OUT/prof_bench/bench_kernel_trace.csv STATUS",
+        "```",
+        "",
+        "The profiled command exited with status %d%s." % (
+            int(status), " (no fault at the profiler's exit)" if int(status) == 0 else ""),
+        "Durations are the dispatch durations of the kernel trace over every dispatch of the "
+        "run: the parity check, the eager warm-up and graph-check tokens, the warm-up and timed "
+        "tokens replayed from the captured token graphs, and the dominant-kernel timing loop "
+        "(the library's kernels with the largest total time).",
+        "",
+        "| kernel | role | dispatches | mean us | min us | max us |",
+        "|---|---|---|---|---|---|",
+    ]
+    ours = {k: v for k, v in per.items() if k.startswith("k_")}  # the library's kernels
+    for k, v in sorted(ours.items(), key=lambda kv: -sum(kv[1]))[:8]:
+        text.append("| `%s` | %s | %d | %.3f | %.3f | %.3f |" % (
+            k, STACK_KERNEL_ROLES.get(k, ""), len(v), np.mean(v), min(v), max(v)))
+    text += [
+        "",
+        "Dominant kernel (the roofline line of bench.py): the gate_up matvec, %s B per launch."
+        % format(bytes_per_launch, ","),
+        "",
+        "| dispatches | mean us per launch | GB/s | % of 8 TB/s |",
+        "|---|---|---|---|",
+        "| inside the stack's tokens (the first %d) | %.3f | %.0f | %.1f |" % (
+            len(gu) - loop_n, stack_us, gbs(stack_us), 100 * gbs(stack_us) / HBM_PEAK_GBS),
+        "| the timing loop, launched back to back over the layers' weights (the last %d) "
+        "| %.3f | %.0f | %.1f |" % (loop_n, loop_us, gbs(loop_us), 100 * gbs(loop_us) / HBM_PEAK_GBS),
+        "",
+        "Under the kernel trace the whole stack runs slower than without it, so in-stack "
+        "durations here are upper bounds. bench.py reports the in-stack figure beside its "
+        "roofline line while the kernel's sources are unchanged (the hash below).",
+        "",
+        json.dumps(rec),
+        "",
+    ]
+    with open(STACK_TRACE_PROFILE, "w") as fh:
+        fh.write("\n".join(text))
+    print(json.dumps(rec))
+
+
+def in_stack_line(bytes_per_launch):
+    """The roofline line's kernel as it runs inside the stack: the mean of its
+    dispatches over the stack's tokens in the committed kernel trace (the line
+    itself times it back to back over the layers' weights), or None."""
+    rec = committed_in_stack()
+    if rec is None or rec.get("bytes_per_launch") != int(bytes_per_launch):
+        return None
+    us = rec["in_stack_us"]
+    achieved = bytes_per_launch / (us * 1e-6) / 1e9
+    return {"us_per_launch": us, "achieved": round(achieved, 1),
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "dispatches": rec["in_stack_dispatches"],
+            "source": "rocprofv3 kernel trace of this command (committed summary), "
+                      "upper bound: the profiler slows the stack"}
+
+
+def committed_in_stack():
+    """The dominant kernel's mean dispatch duration inside the stack from the
+    committed kernel-trace summary, or None if absent or taken on other kernel
+    sources."""
+    try:
+        with open(STACK_TRACE_PROFILE) as fh:
+            for line in fh:
+                if line.startswith("{"):
+                    rec = json.loads(line)
+                    if rec.get("source_hash") == kernel_source_hash():
+                        return rec
+    except (OSError, ValueError):
+        pass
+    return None
+
+
 GEMV_TABLE_PROFILE = os.path.join(ROOT, "profiles", "gemv_table_phi3_qwen3_moe.md")
 MOE_KERNELS = ("the gate_up stage one expert kernel; the down stage one kernel with the "
                "routing-weighted combine up to 32 (token, slot) pairs, else an expert kernel "
@@ -968,7 +1100,13 @@ def main():
                     help="run only the workload of the rocprofv3 counter passes")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic summary from two rocprofv3 --pmc CSV outputs")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "STATUS"),
+                    help="write the stack's kernel-trace summary from a rocprofv3 --kernel-trace "
+                         "CSV of this command and the profiled command's exit status")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
         return
@@ -1097,6 +1235,7 @@ def main():
             "measured_copy_gbs": round(copy_gbs, 1),
             "measured_copy_note": "1 GiB device-to-device copy, read + write bytes per "
                                   "second; informational, the peak is the nominal 8 TB/s",
+            "in_stack": in_stack_line(dom_bytes),
         },
     }
     rec["context"] = dict(BROWSER_CONTEXT)
