@@ -779,16 +779,30 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
             constexpr int kThreads = 64 * kMmaWaves;
             const half2v odd16 = {(_Float16)1.0f, (_Float16)0.0625f};
             const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
-            auto chunk = [&](int c) __attribute__((always_inline)) {
-                // a quad past the end re-reads the last group and stores nothing
-                const int cc = c < total ? c : total - 4 + (c & 3);
-                const int m = cc / cpr, j = cc - m * cpr;
-                return *reinterpret_cast<const u32x4 *>(a.x + m * a.ldx + 8 * (4 * gbase + j));
+            // chunk c = i * kThreads + t of the phase as (row m, chunk j of
+            // the row): one division per thread, then steps of kThreads chunks
+            // (c < total exactly when m < M; cpr and kThreads are multiples of
+            // 4, so j & 3 is the chunk's place in its quad)
+            struct Pos {
+                int m, j;
             };
-            auto stage = [&](int c, u32x4 v) __attribute__((always_inline)) {
-                const bool live = c < total;
-                const int cc = live ? c : total - 4 + (c & 3);
-                const int m = cc / cpr, j = cc - m * cpr;
+            const int dm = kThreads / cpr, dj = kThreads - dm * cpr;  // uniform
+            auto step = [&](Pos q) __attribute__((always_inline)) {
+                q.m += dm;
+                q.j += dj;
+                if (q.j >= cpr) {
+                    q.j -= cpr;
+                    ++q.m;
+                }
+                return q;
+            };
+            auto chunk = [&](Pos q) __attribute__((always_inline)) {
+                // a quad past the end re-reads the last group and stores nothing
+                if (q.m >= M)
+                    q = Pos{M - 1, cpr - 4 + (q.j & 3)};
+                return *reinterpret_cast<const u32x4 *>(a.x + q.m * a.ldx + 8 * (4 * gbase + q.j));
+            };
+            auto stage = [&](Pos q, u32x4 v) __attribute__((always_inline)) {
                 float sum = 0.f;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -799,30 +813,39 @@ __global__ __launch_bounds__(64 * kMmaWaves) void k_gemv_mma(MmaArgs a)
                     v[e] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, h) * odd16);
                 }
                 sum = quad_sum(sum);
-                if (live) {
-                    *reinterpret_cast<u32x4 *>(xs + m * xstride + 8 * j) = pair_order(v);
-                    if ((j & 3) == 0)
-                        xsum[(j >> 2) * 16 + m] = sum;
+                if (q.m < M) {
+                    *reinterpret_cast<u32x4 *>(xs + q.m * xstride + 8 * q.j) = pair_order(v);
+                    if ((q.j & 3) == 0)
+                        xsum[(q.j >> 2) * 16 + q.m] = sum;
                 }
             };
+            const Pos p0 = {t / cpr, t - (t / cpr) * cpr};
             const int xq = min((total + kThreads - 1) / kThreads, kMmaXq);  // uniform
             u32x4 xr[kMmaXq];
             // PH: every register chunk is loaded (those past the end re-read
             // the last quad): loads under the uniform guard, in the phase
             // loop, leave the compiler waiting on each before the next issues
+            Pos q = p0;
 #pragma unroll
-            for (int i = 0; i < kMmaXq; ++i)
+            for (int i = 0; i < kMmaXq; ++i) {
                 if (PH || i < xq)
-                    xr[i] = chunk(i * kThreads + t);
+                    xr[i] = chunk(q);
+                q = step(q);
+            }
             if (PH ? kEarly && mine : kEarly)
                 load_unit(0, ua, gbase, gend);
+            q = p0;
 #pragma unroll
-            for (int i = 0; i < kMmaXq; ++i)
+            for (int i = 0; i < kMmaXq; ++i) {
                 if (i < xq)
-                    stage(i * kThreads + t, xr[i]);
+                    stage(q, xr[i]);
+                q = step(q);
+            }
             // more chunks than the registers hold: the rest one by one
-            for (int c0 = kMmaXq * kThreads; c0 < total; c0 += kThreads)
-                stage(c0 + t, chunk(c0 + t));
+            for (int c0 = kMmaXq * kThreads; c0 < total; c0 += kThreads) {
+                stage(q, chunk(q));
+                q = step(q);
+            }
         }
         if (ph == 0) {
             if (t < 4 * kMmaWaves)
