@@ -148,6 +148,13 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams a)
                 sv[i][r] = load_scale(a.S + off);
             }
         }
+    // RESID: the residual rows behind the weights (consumed in the epilogue;
+    // loaded there, they would add a memory round trip after the sums)
+    uint16_t rin[EPI == EPI_RESID ? RPS : 1];
+    if (EPI == EPI_RESID)
+#pragma unroll
+        for (int r = 0; r < RPS; ++r)
+            rin[r] = a.res_in[row[r]];
 
     // 2. activation into LDS (after an RMSNorm of the residual for PRO_NORM)
     if (PRO == PRO_NORM) {
@@ -278,7 +285,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams a)
             for (int r = 0; r < RPS; ++r)
                 if (ok[r]) {
                     const float t = h2f(f2h(acc[r]));  // as stored by an unfused matvec
-                    a.res_out[row[r]] = f2h(t + h2f(a.res_in[row[r]]));
+                    a.res_out[row[r]] = f2h(t + h2f(rin[r]));
                 }
     }
 }
