@@ -432,41 +432,66 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long k)
 // angle pos * base^(-2i / head_dim) is taken in binary64 and reduced to
 // [-pi, pi] there; its cosine and sine are then taken in f32 (error ~1e-7),
 // the rotation in f32.
-__device__ __forceinline__ void rope_pair_store(const RopeArgs &r, int p, float x1, float x2)
+// The part of a pair's work that needs no matvec result, split off so that a
+// fused epilogue can take it (the position, the angle, the cache page) while
+// the weights stream: rope_pair_prepare with the step's position, then
+// rope_pair_finish with the pair's values.
+struct RopePair {
+    float c, s;
+    uint16_t *dst;  // the pair's first element (q_out or the cache slot); null: nothing stored
+    int half;
+    bool rotate;    // Q and K pairs; V pairs are copied
+};
+
+__device__ __forceinline__ RopePair rope_pair_prepare(const RopeArgs &r, int p, int pos)
 {
-    const int half = r.head_dim >> 1;
-    const int head = p / half, i = p - head * half;
-    const int pos = *r.pos;
-    float c = 1.f, s = 0.f;
-    if (head < r.n_heads + r.n_kv) {
+    RopePair o;
+    o.half = r.head_dim >> 1;
+    const int head = p / o.half, i = p - head * o.half;
+    o.c = 1.f;
+    o.s = 0.f;
+    o.dst = nullptr;
+    o.rotate = head < r.n_heads + r.n_kv;
+    if (o.rotate) {
         const double theta =
             (double)pos * exp2(-2.0 * (double)i / (double)r.head_dim * log2((double)r.base));
         const double two_pi = 6.283185307179586;
         const float red = (float)(theta - two_pi * rint(theta / two_pi));
-        sincosf(red, &s, &c);
+        sincosf(red, &o.s, &o.c);
     }
-    const float y1 = x1 * c - x2 * s;
-    const float y2 = x2 * c + x1 * s;
     if (head < r.n_heads) {
-        r.q_out[head * r.head_dim + i] = f2h(y1);
-        r.q_out[head * r.head_dim + i + half] = f2h(y2);
-        return;
+        o.dst = r.q_out + head * r.head_dim + i;
+        return o;
     }
     const bool is_v = head >= r.n_heads + r.n_kv;
     const int kvh = head - r.n_heads - (is_v ? r.n_kv : 0);
     if (pos < 0)
-        return;
+        return o;
     const int lp = pos / r.page_size, slot = pos - lp * r.page_size;
     if (lp >= r.max_pages)
-        return;
+        return o;
     const int pp = r.page_table[lp];
     if (pp < 0 || pp >= r.n_pages)
+        return o;
+    o.dst = r.kv + (((size_t)pp * 2 + (is_v ? 1 : 0)) * r.n_kv + kvh) *
+                       (size_t)r.page_size * r.head_dim +
+            (size_t)slot * r.head_dim + i;
+    return o;
+}
+
+__device__ __forceinline__ void rope_pair_finish(const RopePair &o, float x1, float x2)
+{
+    if (!o.dst)
         return;
-    uint16_t *dst = r.kv + (((size_t)pp * 2 + (is_v ? 1 : 0)) * r.n_kv + kvh) *
-                               (size_t)r.page_size * r.head_dim +
-                    (size_t)slot * r.head_dim;
-    dst[i] = f2h(is_v ? x1 : y1);
-    dst[i + half] = f2h(is_v ? x2 : y2);
+    const float y1 = x1 * o.c - x2 * o.s;
+    const float y2 = x2 * o.c + x1 * o.s;
+    o.dst[0] = f2h(o.rotate ? y1 : x1);
+    o.dst[o.half] = f2h(o.rotate ? y2 : x2);
+}
+
+__device__ __forceinline__ void rope_pair_store(const RopeArgs &r, int p, float x1, float x2)
+{
+    rope_pair_finish(rope_pair_prepare(r, p, *r.pos), x1, x2);
 }
 
 }  // namespace q4

@@ -126,6 +126,10 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams a)
         row[r] = ok[r] ? rr : 0;
     }
 
+    // ROPE: the step's position behind the activation (a wave-uniform load
+    // the epilogue's angle and cache page wait for)
+    const int rope_pos = EPI == EPI_ROPE ? *a.rope.pos : 0;
+
     // 1. weight and scale loads, in the order they are consumed (group-major)
     uint4 wv[NG][RPS];
     uint32_t sv[NG][RPS];
@@ -148,6 +152,13 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams a)
                 sv[i][r] = load_scale(a.S + off);
             }
         }
+    // ROPE: this thread's pair (threads RB / 2 .. repeat the last one), its
+    // angle and cache slot while the weights stream (in the epilogue they
+    // would add two memory round trips after the sums)
+    RopePair rp;
+    if (EPI == EPI_ROPE)
+        rp = rope_pair_prepare(a.rope, min(blockIdx.x * (RB / 2) + min(tid, RB / 2 - 1), half - 1),
+                               rope_pos);
     // RESID: the residual rows behind the weights (consumed in the epilogue;
     // loaded there, they would add a memory round trip after the sums)
     uint16_t rin[EPI == EPI_RESID ? RPS : 1];
@@ -249,7 +260,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams a)
         if (tid < RB / 2) {
             const int pi = blockIdx.x * (RB / 2) + tid;
             if (pi < half)
-                rope_pair_store(a.rope, pi, vals[tid], vals[tid + RB / 2]);
+                rope_pair_finish(rp, vals[tid], vals[tid + RB / 2]);
         }
     } else if (EPI == EPI_LOGITS) {  // f32 logits and this workgroup's argmax candidate
         unsigned long long key = 0;
